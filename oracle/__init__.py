@@ -1,0 +1,45 @@
+"""CPU oracle for chunkwise gated-delta linear attention (test infrastructure).
+
+This package is test infrastructure, not part of the product.  Only the test
+suite, the smoke check in ``__graft_entry__`` and the CPU-baseline leg of
+``bench.py`` may import it.  The GPU library never imports, links or calls
+anything in here, and nothing in here imports the GPU library: the two share
+no code.  Inputs reach both sides from the seeded generators in
+``workloads/``, which hold none of the method's arithmetic.
+
+Everything is float64 NumPy, written for a reader to check against the pages
+by eye rather than for speed.
+
+Sources (cited by title and section):
+
+* [HA-1]  "混合注意力学习(1): 线性注意力" (hybrid-attention notes, part 1:
+  linear attention), jsqmd.com.
+* [LA-OV] "LinearAttention 概述" (linear attention overview), razer666.cn.
+* [CS336] "【CS336】lecture4 线性注意力|Mamba|GDN|DSA" (lecture-4 notes),
+  wsisp.com.
+
+Modules:
+
+* ``recurrence`` -- the token-by-token recurrence (the definition of what the
+  method computes) and the single decode step.
+* ``chunkwise``  -- the chunkwise-parallel algebra in float64 (masked intra-
+  chunk products, WY/UT representation, decay folding); it is pinned to the
+  recurrence by the exactness of the chunkwise form and is used to pin
+  intermediates.
+
+Parity status of each function is stated in its module header.
+"""
+
+from .recurrence import (  # noqa: F401
+    MODES,
+    decode_steps,
+    recurrent_fwd,
+    recurrent_step,
+)
+from .chunkwise import (  # noqa: F401
+    chunkwise_fwd,
+    forward_substitution_inverse,
+    parallel_masked_linear,
+    ut_transform,
+    wy_transition,
+)

@@ -1,0 +1,345 @@
+"""Pins of the float64 oracle to facts the pages and the mathematics fix.
+
+Each test ties the oracle to something other than itself: an independent
+formula (the masked parallel form, a finite-difference gradient, an explicit
+product of dk x dk factors, a library triangular solve), a closed form, an
+exact-integer expansion, or an invariant.  Shapes use dk != dv so that a
+transposed operand cannot pass unnoticed.
+
+Sources: [HA-1] "混合注意力学习(1): 线性注意力" (jsqmd.com); [LA-OV]
+"LinearAttention 概述" (razer666.cn); [CS336] "【CS336】lecture4 线性注意力|
+Mamba|GDN|DSA" (wsisp.com).
+"""
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from oracle import (chunkwise_fwd, decode_steps, forward_substitution_inverse,
+                    parallel_masked_linear, recurrent_fwd, recurrent_step,
+                    ut_transform, wy_transition)
+
+
+def _rand(seed, B=2, H=3, L=13, dk=5, dv=3, unit_keys=True, s0=0.3):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, L, dk))
+    k = rng.standard_normal((B, H, L, dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, L, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, L))))
+    log_alpha = -np.log1p(np.exp(rng.standard_normal((B, H, L)))) / 4.0
+    S0 = s0 * rng.standard_normal((B, H, dk, dv))
+    return q, k, v, log_alpha, beta, S0
+
+
+def _rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ---------------------------------------------------------------- linear mode
+
+def test_linear_recurrence_equals_masked_parallel_form():
+    """[HA-1 "传统FWP形式的线性注意力并行"; LA-OV "快速预览"]: stacking the
+    rows, causal linear attention is (Q K^T * M) V; with a zero initial state
+    the final state is K^T V (the sum of all writes)."""
+    q, k, v, la, be, _ = _rand(1, L=17, dk=6, dv=4, unit_keys=False)
+    o, S = recurrent_fwd(q, k, v, la, be, None, "linear")
+    assert _rel(o, parallel_masked_linear(q, k, v)) < 1e-13
+    assert _rel(S, np.swapaxes(k, -1, -2) @ v) < 1e-13
+
+
+def test_linear_four_token_cumsum_example_exact_integers():
+    """[LA-OV "Lightning Attention"] expands the causal sum for four tokens:
+    output t is q_t times the running sum of k_j^T v_j over j <= t.  With
+    small integer inputs float64 is exact, so the oracle must match the
+    expansion evaluated in Python integers with equality."""
+    rng = np.random.default_rng(7)
+    d_k, d_v = 3, 2
+    qi = rng.integers(-4, 5, size=(4, d_k))
+    ki = rng.integers(-4, 5, size=(4, d_k))
+    vi = rng.integers(-4, 5, size=(4, d_v))
+    expect = []
+    for t in range(4):
+        row = []
+        for c in range(d_v):
+            # q_t (k_1^T v_1 + ... + k_t^T v_t), entry c
+            row.append(sum(int(qi[t, a]) * int(ki[j, a]) * int(vi[j, c])
+                           for j in range(t + 1) for a in range(d_k)))
+        expect.append(row)
+    o, _ = recurrent_fwd(qi[None, None].astype(float), ki[None, None].astype(float),
+                         vi[None, None].astype(float), None, None, None, "linear")
+    assert np.array_equal(o[0, 0], np.array(expect, dtype=float))
+
+
+def test_linear_never_forgets_same_key_twice():
+    """[HA-1 "Fast Weight Programmers与DeltaNet"]: the plain update only adds,
+    so writing the same unit key twice returns the sum of both values, while
+    the delta rule with beta = 1 returns the latest value."""
+    k1 = np.array([0.0, 1.0, 0.0, 0.0])
+    v1 = np.array([1.0, -2.0, 0.5])
+    v2 = np.array([3.0, 0.25, -1.0])
+    k = np.stack([k1, k1])[None, None]
+    v = np.stack([v1, v2])[None, None]
+    q = k.copy()
+    beta = np.ones((1, 1, 2))
+    o_lin, _ = recurrent_fwd(q, k, v, None, None, None, "linear")
+    o_del, _ = recurrent_fwd(q, k, v, None, beta, None, "delta")
+    assert np.allclose(o_lin[0, 0, 1], v1 + v2, rtol=0, atol=1e-15)
+    assert np.allclose(o_del[0, 0, 1], v2, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- delta rule
+
+def _fd_grad(S, k, v, h=1e-6):
+    """Central-difference gradient of 0.5 ||S^T k - v||^2 over S's entries."""
+    G = np.zeros_like(S)
+    for i in range(S.shape[0]):
+        for j in range(S.shape[1]):
+            Sp = S.copy()
+            Sm = S.copy()
+            Sp[i, j] += h
+            Sm[i, j] -= h
+            lp = 0.5 * np.sum((Sp.T @ k - v) ** 2)
+            lm = 0.5 * np.sum((Sm.T @ k - v) ** 2)
+            G[i, j] = (lp - lm) / (2 * h)
+    return G
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_delta_step_is_gradient_step_on_reconstruction_loss(seed):
+    """[HA-1 "Fast Weight Programmers与DeltaNet"]: the delta rule is one
+    gradient-descent step, with the learned rate beta, on the reconstruction
+    loss of the value from the key.  The gradient here comes from finite
+    differences, not from the update formula."""
+    rng = np.random.default_rng(seed)
+    dk, dv = 5, 3
+    S = rng.standard_normal((dk, dv))
+    k = rng.standard_normal(dk)          # any norm: the identity is exact
+    v = rng.standard_normal(dv)
+    q = rng.standard_normal(dk)
+    beta = 0.37
+    S_new, o = recurrent_step(S, q, k, v, None, beta, "delta")
+    expect = S - beta * _fd_grad(S, k, v)
+    assert np.max(np.abs(S_new - expect)) < 1e-7
+    assert np.max(np.abs(o - S_new.T @ q)) < 1e-14
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_gated_delta_step_is_decay_then_gradient_step(seed):
+    """[HA-1 "Gated DeltaNet"; CS336 "继续改进：GDN"]: the gated rule decays the
+    whole state by alpha (Mamba2-style weight decay) and then takes the delta
+    step; equivalently a gradient step on the loss evaluated at alpha S.
+    The decay therefore scales the erase term too, but not the new write."""
+    rng = np.random.default_rng(seed)
+    dk, dv = 4, 6
+    S = rng.standard_normal((dk, dv))
+    k = rng.standard_normal(dk)
+    k /= np.linalg.norm(k)
+    v = rng.standard_normal(dv)
+    q = rng.standard_normal(dk)
+    beta, log_alpha = 0.8, -0.3
+    a = np.exp(log_alpha)
+    S_new, _ = recurrent_step(S, q, k, v, log_alpha, beta, "gated_delta")
+    expect = a * S - beta * _fd_grad(a * S, k, v)
+    assert np.max(np.abs(S_new - expect)) < 1e-7
+
+
+def test_delta_blend_reading_matches_update():
+    """[HA-1 "Fast Weight Programmers与DeltaNet"] describes the rule as: read
+    the old value under k, blend it with the new one by beta, remove the old
+    association and write the blended one.  Written out step by step this
+    equals the oracle's update for any key norm."""
+    rng = np.random.default_rng(11)
+    dk, dv = 6, 2
+    S = rng.standard_normal((dk, dv))
+    k = 1.7 * rng.standard_normal(dk)
+    v = rng.standard_normal(dv)
+    beta = 0.61
+    v_old = S.T @ k
+    v_new = beta * v + (1.0 - beta) * v_old
+    S_blend = S - np.outer(k, v_old) + np.outer(k, v_new)
+    S_new, _ = recurrent_step(S, np.zeros(dk), k, v, None, beta, "delta")
+    assert np.max(np.abs(S_new - S_blend)) < 1e-13
+
+
+def test_delta_exact_retrieval_with_orthonormal_keys():
+    """With beta = 1 and orthonormal keys each write replaces exactly what is
+    stored under its key and leaves the other keys untouched, so querying
+    with an earlier key returns its value, whatever the initial state
+    (the delta rule's erase-then-write, [HA-1 "Fast Weight Programmers与
+    DeltaNet"]).  Plain linear attention fails this when S0 != 0."""
+    rng = np.random.default_rng(5)
+    dk, dv, n = 7, 3, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    keys = Qm[:, :n].T                                  # n orthonormal rows
+    vals = rng.standard_normal((n, dv))
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    # token t queries with key j(t) <= t
+    j_of_t = [0, 0, 1, 2, 1, 4]
+    q = keys[j_of_t][None, None]
+    k = keys[None, None]
+    v = vals[None, None]
+    beta = np.ones((1, 1, n))
+    o, _ = recurrent_fwd(q, k, v, None, beta, S0, "delta")
+    assert np.max(np.abs(o[0, 0] - vals[j_of_t])) < 1e-13
+    o_g, _ = recurrent_fwd(q, k, v, np.zeros((1, 1, n)), beta, S0, "gated_delta")
+    assert np.max(np.abs(o_g - o)) < 1e-15             # alpha = 1
+    o_lin, _ = recurrent_fwd(q, k, v, None, None, S0, "linear")
+    assert np.max(np.abs(o_lin[0, 0] - vals[j_of_t])) > 1e-3
+
+
+def test_householder_reflection_preserves_state_norm():
+    """[HA-1 "HouseHolder变换和WY表示"]: I - 2 k k^T / (k^T k) is a Householder
+    reflection, orthogonal.  With beta = 2, unit keys, alpha = 1 and zero
+    values every delta step applies one reflection, so the Frobenius norm of
+    every column of the state is preserved and a reflected key flips sign."""
+    rng = np.random.default_rng(9)
+    dk, dv, L = 6, 4, 11
+    k = rng.standard_normal((1, 1, L, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    zeros_v = np.zeros((1, 1, L, dv))
+    beta = 2.0 * np.ones((1, 1, L))
+    _, S = recurrent_fwd(np.zeros((1, 1, L, dk)), k, zeros_v, None, beta, S0, "delta")
+    assert np.allclose(np.linalg.norm(S, axis=-2), np.linalg.norm(S0, axis=-2),
+                       rtol=1e-13, atol=0)
+    kk = k[0, 0, 0]
+    S1, _ = recurrent_step(kk[:, None] * np.ones((1, dv)), np.zeros(dk), kk,
+                           np.zeros(dv), None, 2.0, "delta")
+    assert np.allclose(S1, -kk[:, None] * np.ones((1, dv)), atol=1e-15)
+
+
+def test_gate_closed_forms():
+    """Closed forms of the gated rule: with beta = 0 nothing is written or
+    erased, so o_t = gamma_t S0^T q_t with gamma_t the running product of the
+    decays; with alpha -> 0 all history is dropped and o_t = beta_t
+    (q_t . k_t) v_t."""
+    q, k, v, la, be, S0 = _rand(21, L=9, dk=4, dv=5)
+    o, S = recurrent_fwd(q, k, v, la, np.zeros_like(be), S0, "gated_delta")
+    gamma = np.exp(np.cumsum(la, axis=-1))
+    expect = gamma[..., None] * np.einsum("bhij,bhti->bhtj", S0, q)
+    assert _rel(o, expect) < 1e-13
+    assert _rel(S, gamma[..., -1, None, None] * S0) < 1e-13
+    la_zero = np.full_like(la, -1e30)                    # exp -> exactly 0
+    o2, _ = recurrent_fwd(q, k, v, la_zero, be, S0, "gated_delta")
+    expect2 = be[..., None] * np.sum(q * k, axis=-1)[..., None] * v
+    assert _rel(o2, expect2) < 1e-14
+
+
+def test_scalar_state_by_hand():
+    """dk = dv = 1: the gated rule reads s <- alpha (1 - beta k^2) s + beta k v
+    and o = s q; evaluated here with plain Python floats."""
+    rng = np.random.default_rng(13)
+    L = 8
+    q, k, v = (rng.standard_normal(L) for _ in range(3))
+    la = -np.abs(rng.standard_normal(L)) / 3
+    be = rng.uniform(0, 1, L)
+    s = 0.7
+    want = []
+    for t in range(L):
+        a = float(np.exp(la[t]))
+        s = a * (1.0 - be[t] * k[t] * k[t]) * s + be[t] * k[t] * v[t]
+        want.append(s * q[t])
+    o, S = recurrent_fwd(q[None, None, :, None], k[None, None, :, None],
+                         v[None, None, :, None], la[None, None], be[None, None],
+                         np.array([[[[0.7]]]]), "gated_delta")
+    assert np.allclose(o[0, 0, :, 0], want, rtol=1e-14, atol=0)
+    assert abs(S[0, 0, 0, 0] - s) < 1e-14
+
+
+# ---------------------------------------------------------------- chunkwise
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+@pytest.mark.parametrize("C", [1, 3, 7, 16, 32])
+def test_chunkwise_is_exact_for_every_chunk_size(mode, C):
+    """[LA-OV "FLASH"; HA-1 "FWP分块并行机制"]: the chunkwise form equals the
+    recurrent form for any chunk size (C = 1 is the recurrent form, C = L the
+    parallel one), including a ragged last chunk (C = 3, 7 do not divide 32).
+    Exact in exact arithmetic; float64 round-off here."""
+    q, k, v, la, be, S0 = _rand(100 + C, L=32, dk=6, dv=5)
+    o_ref, S_ref = recurrent_fwd(q, k, v, la, be, S0, mode)
+    o, S = chunkwise_fwd(q, k, v, la, be, S0, mode, C)
+    assert _rel(o, o_ref) < 1e-12
+    assert _rel(S, S_ref) < 1e-12
+
+
+def test_chunkwise_linear_single_chunk_is_parallel_form():
+    """C = L with a zero state is exactly the masked parallel form."""
+    q, k, v, la, be, _ = _rand(31, L=12, dk=4, dv=6, unit_keys=False)
+    o, _ = chunkwise_fwd(q, k, v, la, be, None, "linear", 12)
+    assert _rel(o, parallel_masked_linear(q, k, v)) < 1e-13
+
+
+def test_forward_substitution_matches_library_triangular_solve():
+    """T = (I + A)^{-1} for strictly lower A, checked against SciPy's
+    triangular solve (a textbook routine, independent of the loop)."""
+    rng = np.random.default_rng(17)
+    for C in (1, 5, 16, 64):
+        A = np.tril(rng.standard_normal((C, C)) * 0.2, k=-1)
+        T = forward_substitution_inverse(A)
+        ref = scipy.linalg.solve_triangular(np.eye(C) + A, np.eye(C), lower=True,
+                                            unit_diagonal=True)
+        assert np.max(np.abs(T - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("mode", ["delta", "gated_delta"])
+def test_wy_representation_equals_product_of_factors(mode):
+    """[HA-1 "HouseHolder变换和WY表示"]: a product of rank-1 corrections is
+    the identity minus a low-rank product.  For one chunk the WY/UT form
+    gamma_C I - (diag(gamma_C/gamma) K)^T W must equal the explicit product
+    of dk x dk factors alpha_r (I - beta_r k_r k_r^T), latest on the left.
+    dk = 9 > n = 6 so the product is a genuine rank-6 correction."""
+    rng = np.random.default_rng(23)
+    n, dk = 6, 9
+    k = rng.standard_normal((n, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = rng.uniform(0.1, 1.0, n)
+    la = -rng.uniform(0.0, 0.5, n) if mode == "gated_delta" else None
+    P = np.eye(dk)
+    for r in range(n):
+        a = 1.0 if la is None else np.exp(la[r])
+        P = a * (np.eye(dk) - beta[r] * np.outer(k[r], k[r])) @ P
+    assert np.max(np.abs(wy_transition(k, la, beta, mode) - P)) < 1e-13
+    # and T from the transform solves the unit lower-triangular system
+    ut = ut_transform(k, np.zeros((n, 1)), la, beta, mode)
+    assert np.max(np.abs((np.eye(n) + ut["A"]) @ ut["T"] - np.eye(n))) < 1e-13
+
+
+# ---------------------------------------------------------------- carry / decode
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_state_carry_and_decode_match_forward(mode):
+    """Only the fixed-size state is carried between calls [CS336 "朴素线性注意力"]:
+    a forward over L1 tokens followed by one over L2 tokens started from its
+    final state equals one forward over L1 + L2; L single decode steps equal
+    the forward over the same L tokens [HA-1 "Prefill、Decode与KVCache"]."""
+    q, k, v, la, be, S0 = _rand(41, L=20, dk=5, dv=4)
+    o_ref, S_ref = recurrent_fwd(q, k, v, la, be, S0, mode)
+    o1, S1 = chunkwise_fwd(q[:, :, :8], k[:, :, :8], v[:, :, :8], la[:, :, :8],
+                           be[:, :, :8], S0, mode, 4)
+    o2, S2 = chunkwise_fwd(q[:, :, 8:], k[:, :, 8:], v[:, :, 8:], la[:, :, 8:],
+                           be[:, :, 8:], S1, mode, 5)
+    assert _rel(np.concatenate([o1, o2], axis=2), o_ref) < 1e-12
+    assert _rel(S2, S_ref) < 1e-12
+    tq = np.moveaxis(q, 2, 0)
+    od, Sd = decode_steps(S0, tq, np.moveaxis(k, 2, 0), np.moveaxis(v, 2, 0),
+                          np.moveaxis(la, 2, 0), np.moveaxis(be, 2, 0), mode)
+    assert _rel(np.moveaxis(od, 0, 2), o_ref) < 1e-14
+    assert _rel(Sd, S_ref) < 1e-14
+
+
+def test_modes_ignore_unused_gates():
+    """linear ignores beta and alpha; delta ignores alpha."""
+    q, k, v, la, be, S0 = _rand(51, L=6)
+    a, _ = recurrent_fwd(q, k, v, la, be, S0, "linear")
+    b, _ = recurrent_fwd(q, k, v, None, None, S0, "linear")
+    assert np.array_equal(a, b)
+    c, _ = recurrent_fwd(q, k, v, la, be, S0, "delta")
+    d, _ = recurrent_fwd(q, k, v, np.zeros_like(la), be, S0, "gated_delta")
+    assert _rel(c, d) < 1e-15
+    with pytest.raises(ValueError):
+        recurrent_fwd(q, k, v, la, None, S0, "delta")
+    with pytest.raises(ValueError):
+        recurrent_fwd(q, k, v, la, be, S0, "softmax")
