@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated-delta forward and the decode step on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One JSON line on stdout.  A "step" is one call of the chunkwise forward
+(la_chunk_fwd) over the long-context gated-delta workload
+(B=1, H=32, L=65536, d=128, C=64, bf16 q/k/v/out, float32 gates and state,
+nonzero initial state); ``value`` is its throughput in tokens/s with the
+inputs already resident in HBM.  The same line carries the decode half of
+the metric (128 in-place decode steps over B=256, H=32, d=128 float32
+states: state GB/s and fraction of HBM peak), the per-kernel HIP-event
+timings, the roofline of the forward's dominant kernel and the float64 CPU
+oracle timed on a bounded sample of the same forward workload.
+
+Inputs are seeded synthetic tensors from ``workloads`` (the recipe is in
+that module's docstring); two copies of the forward inputs alternate so
+consecutive steps do not hit the 256 MB last-level cache.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("chunkwise gated-delta fwd tokens/s (% MFMA peak); "
+          "decode state GB/s (% HBM)")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, flop/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work model
+# Per (token, head) of the forward, d = dk = dv, chunk C, element size e:
+#   algorithmic work of the method (dense-block chunkwise):
+#     gated/delta: 10 C d + 6 d^2 flop;  linear: 4 C d + 4 d^2
+#   la_wy    moves q, k, v in (3 d e), beta and log_alpha (8 B), W, U out
+#            (2 d e), the masked C x C score row out (C e), g out (4 B);
+#            linear mode: q, k in, score row out
+#   la_state moves q, k, W, U, the score row and g in, o out;
+#            linear mode: q, k, v, the score row in, o out
+# Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,
+# o (2 dk e + 2 dv e), two float gates.
+
+def fwd_flops_per_token_head(w):
+    d, C = w.dk, w.C
+    if w.mode == "linear":
+        return 4 * C * d + 4 * d * d
+    return 10 * C * d + 6 * d * d
+
+
+def kernel_bytes_per_token_head(name, w):
+    d, C = w.dk, w.C
+    e = 2 if w.dtype == "bf16" else 4
+    if name == "la_wy":
+        if w.mode == "linear":
+            return 2 * d * e + C * e
+        return 3 * d * e + 8 + 2 * d * e + C * e + 4
+    if name == "la_state":
+        if w.mode == "linear":
+            return 3 * d * e + C * e + d * e
+        return 4 * d * e + C * e + 4 + d * e
+    raise KeyError(name)
+
+
+def decode_bytes_per_head(w):
+    e = 2 if w.dtype == "bf16" else 4
+    return 2 * w.dk * w.dv * 4 + 2 * w.dk * e + 2 * w.dv * e + 8
+
+
+def fwd_min_bytes_per_token_head(w):
+    """q, k, v, o and the two gates: what the op must read and write."""
+    e = 2 if w.dtype == "bf16" else 4
+    return (2 * w.dk + 2 * w.dv) * e + 8
+
+
+# ------------------------------------------------------------------ legs
+
+def bench_forward(w, steps, warmup):
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] forward workload {w.name}: generating inputs")
+    x = workloads.make_inputs(w)
+    copies = []
+    for _ in range(2):
+        copies.append({k: t.cuda() for k, t in x.items()})
+    out = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.torch_dtype, device="cuda")
+    S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        d = copies[i % 2]
+        la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                     d["S0"] if w.s0_std > 0 else None, mode=w.mode, C=w.C,
+                     out=out, S_final=S_final)
+
+    log(f"[bench] forward: {warmup} warmup steps")
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] forward: {steps} timed steps")
+    with la.kernel_timer() as kt:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sec = (t1 - t0) / steps
+    token_heads = w.B * w.H * w.L
+    kernels = {}
+    for name, (n, ms) in kt.stats.items():
+        avg_ms = ms / max(n, 1)
+        by = kernel_bytes_per_token_head(name, w) * token_heads
+        kernels[name] = {"launches": n, "avg_ms": round(avg_ms, 5),
+                         "algorithmic_bytes": by,
+                         "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+    flops = fwd_flops_per_token_head(w) * token_heads
+    min_bytes = fwd_min_bytes_per_token_head(w) * token_heads
+    res = {
+        "value": w.B * w.L / sec,
+        "ms_per_step": sec * 1e3,
+        "mfma_frac_of_bf16_peak": flops / sec / BF16_MFMA_PEAK,
+        "hbm_frac_of_min_bytes": min_bytes / sec / (HBM_PEAK_GBS * 1e9),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    del copies
+    torch.cuda.empty_cache()
+    return x, res
+
+
+def bench_decode(w, warmup=1):
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] decode workload {w.name}: generating inputs")
+    x = workloads.make_inputs(w)
+    d = {k: t.cuda() for k, t in x.items()}
+    S = d["S0"].clone()
+    outs = torch.empty((w.steps, w.B, w.H, w.dv), dtype=w.torch_dtype, device="cuda")
+
+    def run():
+        for n in range(w.steps):
+            la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["log_alpha"][n], d["beta"][n],
+                           S, mode=w.mode, out=outs[n])
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"[bench] decode: {w.steps} timed steps")
+    with la.kernel_timer() as kt:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    n, ms = kt.stats["la_decode"]
+    avg_ms = ms / n
+    by = decode_bytes_per_head(w) * w.B * w.H
+    gbs = by / (avg_ms * 1e-3) / 1e9
+    wall = (t1 - t0) / w.steps
+    return {
+        "workload": w.name, "steps": w.steps,
+        "tokens_per_s": w.B / wall,
+        "ms_per_step_wall": wall * 1e3,
+        "kernel_avg_ms": round(avg_ms, 5),
+        "state_GBs": round(gbs, 1),
+        "roofline": {"kernel": "la_decode", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+
+def cpu_baseline(w, x, tokens):
+    """The float64 oracle, as it stands, on the first `tokens` tokens of
+    every head of the forward workload, BLAS limited to one thread."""
+    import workloads
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    sub = {k: (t[:, :, :tokens] if k != "S0" else t) for k, t in x.items()}
+    y = workloads.to_f64(sub)
+    log(f"[bench] cpu baseline: oracle on {tokens} tokens x {w.B * w.H} heads")
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.recurrent_fwd(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
+                             y["S0"] if w.s0_std > 0 else None, w.mode)
+        sec = time.perf_counter() - t0
+    return {"value": w.B * tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {tokens} of {w.L} tokens of all {w.B}x{w.H} (batch, head) "
+                      f"sequences of {w.name}, float64 token recurrence, {sec:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="forward workload id in workloads.WORKLOADS (default 4)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens per head of the CPU oracle sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the forward shards over (batch, head) or over the sequence, "
+              "see the design notes, but no multi-GPU path is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[args.workload]
+    x, fwd = bench_forward(w, args.steps, args.warmup)
+    dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
+    cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
+    line = {
+        "metric": METRIC,
+        "value": fwd["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fwd["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "L": w.L,
+                   "dk": w.dk, "dv": w.dv, "C": w.C, "inputs": w.dtype + " q/k/v/out, "
+                   "float32 gates and state"},
+        "mfma_frac_of_bf16_peak": round(fwd["mfma_frac_of_bf16_peak"], 4),
+        "hbm_frac_of_min_bytes": round(fwd["hbm_frac_of_min_bytes"], 4),
+        "roofline": fwd["roofline"],
+        "kernels": fwd["kernels"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

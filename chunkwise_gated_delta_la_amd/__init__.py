@@ -1,0 +1,13 @@
+"""chunkwise_gated_delta_la_amd -- chunkwise gated-delta linear attention on
+AMD Instinct MI355X (gfx950).
+
+A thin Python binding over liblachunk.so, whose C ABI is declared in
+``include/la.h``.  Every step of the computation runs in the library's HIP
+kernels; this package only checks and marshals torch tensors (device
+memory) and passes torch's current HIP stream.
+
+    out, S_final = chunk_fwd(q, k, v, log_alpha, beta, S0, mode="gated_delta")
+    out = decode_step(q, k, v, log_alpha, beta, S, mode="gated_delta")  # S in place
+"""
+from ._lib import LAError, LIB_PATH  # noqa: F401
+from .api import MODES, chunk_fwd, decode_step, kernel_timer, version  # noqa: F401

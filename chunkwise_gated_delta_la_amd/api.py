@@ -1,0 +1,143 @@
+"""Tensor-level entry points with the same names as the C ABI calls.
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are
+checked here so that errors name the offending tensor; the library checks
+them again and does all the work.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+MODES = {"linear": 0, "delta": 1, "gated_delta": 2}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def version():
+    return _lib.get().la_version().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mode(mode):
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}, got {mode!r}")
+    return MODES[mode]
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta",
+              C=64, out=None, S_final=None, return_state=True):
+    """Chunkwise forward (``la_chunk_fwd``).
+
+    q, k ``[B, H, L, dk]``, v ``[B, H, L, dv]`` (float32 or bfloat16, on the
+    GPU); log_alpha, beta ``[B, H, L]`` float32; S0 ``[B, H, dk, dv]`` float32
+    or None.  Returns ``(out, S_final)`` (S_final None if not requested).
+    ``S_final`` may be the same tensor as ``S0`` for an in-place update.
+    """
+    m = _mode(mode)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    _need(k, "k", (B, H, L, dk), dt, dev)
+    _need(v, "v", (B, H, L, dv), dt, dev)
+    _need(q, "q", (B, H, L, dk), dt, dev)
+    _need(log_alpha if m == 2 else None, "log_alpha", (B, H, L), torch.float32, dev)
+    _need(beta if m >= 1 else None, "beta", (B, H, L), torch.float32, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
+    _need(out, "out", (B, H, L, dv), dt, dev)
+    if S_final is None and return_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v),
+                              _ptr(log_alpha if m == 2 else None),
+                              _ptr(beta if m >= 1 else None), _ptr(S0),
+                              _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
+                              _DTYPES[dt], _stream(dev))
+    _lib.check(rc)
+    return out, S_final
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None):
+    """One recurrent decode step (``la_decode_step``), updating ``S`` in place.
+
+    q, k ``[B, H, dk]``, v ``[B, H, dv]`` (float32 or bfloat16); log_alpha,
+    beta ``[B, H]`` float32; S ``[B, H, dk, dv]`` float32.  Returns ``out``
+    ``[B, H, dv]``.
+    """
+    m = _mode(mode)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    _need(k, "k", (B, H, dk), dt, dev)
+    _need(v, "v", (B, H, dv), dt, dev)
+    _need(log_alpha if m == 2 else None, "log_alpha", (B, H), torch.float32, dev)
+    _need(beta if m >= 1 else None, "beta", (B, H), torch.float32, dev)
+    _need(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(out, "out", (B, H, dv), dt, dev)
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v),
+                                _ptr(log_alpha if m == 2 else None),
+                                _ptr(beta if m >= 1 else None), _ptr(S), _ptr(out),
+                                B, H, dk, dv, m, _DTYPES[dt], _stream(dev))
+    _lib.check(rc)
+    return out
+
+
+class kernel_timer:
+    """Context manager timing the library's kernel launches with HIP events
+    (``la_profile_begin`` / ``la_profile_end``).  On exit, ``stats`` maps a
+    kernel name to ``(launches, total_ms)``; leaving the block waits for
+    the recorded events."""
+
+    def __enter__(self):
+        _lib.check(_lib.get().la_profile_begin())
+        self.stats = {}
+        return self
+
+    def __exit__(self, *exc):
+        lib = _lib.get()
+        buf = (_lib.KernelTime * 16)()
+        n = ctypes.c_int(0)
+        rc = lib.la_profile_end(buf, 16, ctypes.byref(n))
+        for i in range(min(n.value, 16)):
+            self.stats[buf[i].name.decode()] = (buf[i].launches, buf[i].total_ms)
+        if exc[0] is None:
+            _lib.check(rc)
+        return False

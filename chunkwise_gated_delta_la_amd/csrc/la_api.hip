@@ -1,0 +1,330 @@
+// C-ABI host layer of liblachunk: argument validation, dispatch to the
+// gfx950 kernels, stream-ordered workspace.  See include/la.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+#include <map>
+#include <cstring>
+#include <algorithm>
+
+#include "la.h"
+#include "la_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(const char* what, hipError_t e) {
+  return fail(LA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Half-open byte range of a tensor argument; empty when ptr is NULL.
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+  Range() = default;
+  Range(const void* p, size_t bytes)
+      : lo(reinterpret_cast<uintptr_t>(p)), hi(p ? lo + bytes : lo) {}
+  bool empty() const { return lo == hi; }
+  bool overlaps(const Range& o) const {
+    return !empty() && !o.empty() && lo < o.hi && o.lo < hi;
+  }
+};
+
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Element count of a product of positive sizes, or false on overflow.
+bool count(std::initializer_list<long> dims, size_t* out) {
+  size_t n = 1;
+  for (long d : dims)
+    if (!mul_ok(n, (size_t)d, &n)) return false;
+  *out = n;
+  return true;
+}
+
+int check_mode_dtype(int mode, int dtype) {
+  if (mode < LA_MODE_LINEAR || mode > LA_MODE_GATED_DELTA)
+    return fail(LA_ERR_UNSUPPORTED, "mode must be LA_MODE_LINEAR, LA_MODE_DELTA or "
+                                    "LA_MODE_GATED_DELTA, got " + std::to_string(mode));
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16)
+    return fail(LA_ERR_UNSUPPORTED,
+                "dtype must be LA_DTYPE_F32 or LA_DTYPE_BF16, got " + std::to_string(dtype));
+  return LA_OK;
+}
+
+int check_gates(int mode, const float* log_alpha, const float* beta) {
+  if (mode != LA_MODE_LINEAR && !beta)
+    return fail(LA_ERR_NULL, "beta is required for the delta modes");
+  if (mode == LA_MODE_GATED_DELTA && !log_alpha)
+    return fail(LA_ERR_NULL, "log_alpha is required for LA_MODE_GATED_DELTA");
+  return LA_OK;
+}
+
+// Per-device memory pool for transient workspace.  Its release threshold
+// is raised so that memory freed at the end of one call is reused by the
+// next call instead of being returned to the driver.
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[64] = {};
+
+hipError_t get_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t threshold = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return e;
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- kernel timing with HIP events (la_profile_begin / la_profile_end)
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<TimedLaunch> g_prof;
+
+// Records an event on `st` if profiling is on; returns it (or nullptr).
+hipEvent_t prof_mark(hipStream_t st) {
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return nullptr;
+  }
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+  if (hipEventRecord(ev, st) != hipSuccess) {
+    (void)hipEventDestroy(ev);
+    return nullptr;
+  }
+  return ev;
+}
+
+void prof_add(const char* name, hipEvent_t a, hipEvent_t b) {
+  if (!a || !b) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({name, a, b});
+}
+
+}  // namespace
+
+namespace la {
+
+WorkspaceSizes chunk_workspace_sizes(const ChunkArgs& a) {
+  const size_t esz = a.bf16 ? 2 : 4;
+  const size_t tokens = (size_t)a.B * a.H * a.L;
+  WorkspaceSizes s{};
+  s.Aqk = align_up(tokens * a.C * esz);  // (L / C) chunks of C x C per head
+  if (a.mode != kModeLinear) {
+    s.W = align_up(tokens * a.d * esz);
+    s.U = align_up(tokens * a.d * esz);
+    s.G = align_up(tokens * 4);
+  }
+  return s;
+}
+
+}  // namespace la
+
+extern "C" {
+
+const char* la_last_error(void) { return g_last_error.c_str(); }
+
+const char* la_version(void) { return "lachunk 0.1.0 gfx950"; }
+
+int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* S0, void* out, float* S_final, int B,
+                 int H, int L, int dk, int dv, int C, int mode, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || C <= 0)
+    return fail(LA_ERR_SHAPE, "B, H, L, dk, dv and C must be positive");
+  if (L % C != 0)
+    return fail(LA_ERR_SHAPE, "L (" + std::to_string(L) + ") must be a multiple of C (" +
+                                  std::to_string(C) + ")");
+  if (dk != dv || (dk != 64 && dk != 128))
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd supports dk == dv in {64, 128}, got dk=" +
+                                        std::to_string(dk) + " dv=" + std::to_string(dv));
+  if (C != 64)
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd supports C == 64, got " + std::to_string(C));
+  size_t n_qk, n_v, n_g, n_s;
+  if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
+      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s) || n_qk > (SIZE_MAX >> 3))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  if ((size_t)B * H * (L / C) > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "B * H * L / C exceeds the launch grid");
+  const size_t esz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
+  const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
+  const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
+  const Range rs0(S0, n_s * 4), ro(out, n_v * esz), rsf(S_final, n_s * 4);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0})
+    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro})
+    if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
+  if (rsf.overlaps(rs0) && (S0 != S_final))
+    return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
+
+  la::ChunkArgs a{q, k, v, log_alpha, beta, S0, out, S_final,
+                  B, H, L, dk, C, mode, dtype == LA_DTYPE_BF16};
+  const la::WorkspaceSizes sz = la::chunk_workspace_sizes(a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipMemPool_t pool = nullptr;
+  if (hipError_t e = get_pool(&pool)) return fail_hip("creating the workspace pool", e);
+  void* base = nullptr;
+  if (hipError_t e = hipMallocFromPoolAsync(&base, sz.total(), pool, st))
+    return fail_hip("allocating workspace", e);
+  char* p = static_cast<char*>(base);
+  la::ChunkWorkspace ws{};
+  ws.Aqk = p;
+  p += sz.Aqk;
+  if (sz.W) {
+    ws.W = p;
+    p += sz.W;
+    ws.U = p;
+    p += sz.U;
+    ws.G = reinterpret_cast<float*>(p);
+  }
+  hipEvent_t e0 = prof_mark(st);
+  hipError_t e = la::launch_wy(a, ws, st);
+  hipEvent_t e1 = prof_mark(st);
+  hipEvent_t e2 = nullptr;
+  if (e == hipSuccess) {
+    e = la::launch_state(a, ws, st);
+    e2 = prof_mark(st);
+  }
+  prof_add("la_wy", e0, e1);
+  prof_add("la_state", e1, e2);
+  hipError_t ef = hipFreeAsync(base, st);
+  if (e != hipSuccess) return fail_hip("launching the chunk kernels", e);
+  if (ef != hipSuccess) return fail_hip("releasing workspace", ef);
+  return LA_OK;
+}
+
+int la_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                   const float* beta, float* S, void* out, int B, int H, int dk, int dv,
+                   int mode, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !S || !out) return fail(LA_ERR_NULL, "q, k, v, S and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(LA_ERR_SHAPE, "B, H, dk and dv must be positive");
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(LA_ERR_UNSUPPORTED, "la_decode_step supports dk, dv in {64, 128}, got dk=" +
+                                        std::to_string(dk) + " dv=" + std::to_string(dv));
+  size_t n_k, n_v, n_g, n_s;
+  if (!count({B, H, dk}, &n_k) || !count({B, H, dv}, &n_v) || !count({B, H}, &n_g) ||
+      !count({B, H, dk, dv}, &n_s) || n_s > (SIZE_MAX >> 3))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  if (n_g > 0x7fffffffu) return fail(LA_ERR_SHAPE, "B * H exceeds the launch grid");
+  const size_t esz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const Range rq(q, n_k * esz), rk(k, n_k * esz), rv(v, n_v * esz);
+  const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
+  const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
+  const Range rs(S, n_s * 4), ro(out, n_v * esz);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
+    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
+    if (rs.overlaps(*in)) return fail(LA_ERR_ALIAS, "S overlaps an input");
+
+  la::DecodeArgs a{q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode,
+                   dtype == LA_DTYPE_BF16};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = prof_mark(st);
+  hipError_t e = la::launch_decode(a, st);
+  prof_add("la_decode", e0, prof_mark(st));
+  if (e != hipSuccess) return fail_hip("launching the decode kernel", e);
+  return LA_OK;
+}
+
+int la_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = true;
+  return LA_OK;
+}
+
+int la_profile_end(la_kernel_time_t* out, int capacity, int* count) {
+  g_last_error.clear();
+  if (!count) return fail(LA_ERR_NULL, "count is required");
+  std::vector<TimedLaunch> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    recs.swap(g_prof);
+  }
+  // Events shared by two records (one kernel's stop is the next one's
+  // start) are destroyed once.
+  std::map<std::string, std::pair<int, double>> agg;
+  std::vector<std::string> order;
+  hipError_t err = hipSuccess;
+  for (const TimedLaunch& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      order.push_back(r.name);
+      it = agg.emplace(r.name, std::make_pair(0, 0.0)).first;
+    }
+    it->second.first += 1;
+    it->second.second += ms;
+  }
+  std::vector<hipEvent_t> evs;
+  for (const TimedLaunch& r : recs) {
+    evs.push_back(r.start);
+    evs.push_back(r.stop);
+  }
+  std::sort(evs.begin(), evs.end());
+  evs.erase(std::unique(evs.begin(), evs.end()), evs.end());
+  for (hipEvent_t ev : evs) (void)hipEventDestroy(ev);
+  int n = 0;
+  for (const std::string& name : order) {
+    if (out && n < capacity) {
+      std::memset(out[n].name, 0, sizeof(out[n].name));
+      std::strncpy(out[n].name, name.c_str(), sizeof(out[n].name) - 1);
+      out[n].launches = agg[name].first;
+      out[n].total_ms = agg[name].second;
+    }
+    ++n;
+  }
+  *count = n;
+  if (err != hipSuccess) return fail_hip("reading kernel timing events", err);
+  return LA_OK;
+}
+
+}  // extern "C"

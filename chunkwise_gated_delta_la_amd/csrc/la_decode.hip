@@ -1,0 +1,163 @@
+// Decode step: one token of the gated delta recurrence for B*H independent
+// states, state read-modify-written in place in HBM.
+//
+// Per (b, h), with S the dk x dv float state:
+//     s = S^T k,  p = S^T q,  kq = k . q
+//     linear      : u = v,             S' = S + k u^T,          o = p + kq u
+//     delta       : u = beta (v - s),  S' = S + k u^T,          o = p + kq u
+//     gated_delta : u = beta (v - a s),S' = a S + k u^T,        o = a p + kq u
+// where a = exp(log_alpha).  o = S'^T q is expanded so that one read of S
+// yields both s and p; the erase term k (k^T S) is never formed as a
+// dk x dk matrix (the O(d^2) evaluation order of "继续改进：GDN" in the
+// lecture notes "【CS336】lecture4 线性注意力|Mamba|GDN|DSA").
+//
+// The step is pure streaming: 0.75 flop per byte of state, so it is bound by
+// HBM bandwidth.  One 256-thread workgroup owns one (b, h) state (64 KiB at
+// dk = dv = 128): every thread loads its rows x 4 columns with 16-byte
+// non-temporal loads (a wave covers whole contiguous rows), keeps them in
+// registers, reduces the two column dot products through LDS, and writes the
+// updated values back from the same registers with 16-byte non-temporal
+// stores.  S is read exactly once and written exactly once.
+#include "la_device.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+namespace {
+
+template <typename T, int DK, int DV, int MODE>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    float* __restrict__ S, T* __restrict__ out) {
+  constexpr int NQ = DV / 4;       // 16-byte column quads per state row
+  constexpr int RG = 256 / NQ;     // row groups
+  constexpr int RPT = DK / RG;     // rows per thread
+  static_assert(RPT * RG == DK && NQ * RG == 256, "tile shape");
+
+  __shared__ float sk[DK];
+  __shared__ float sq[DK];
+  __shared__ float sv[DV];
+  __shared__ float su[DV];
+  __shared__ float red[2][RG][DV];
+  __shared__ float skq;
+
+  const size_t bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int cq = t % NQ;
+  const int rg = t / NQ;
+
+  f32x4* Sp = reinterpret_cast<f32x4*>(S + bh * DK * DV);
+  f32x4 s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    s[m] = __builtin_nontemporal_load(Sp + (rg + RG * m) * NQ + cq);
+
+  for (int i = t; i < DK; i += 256) {
+    sk[i] = to_f32(k[bh * DK + i]);
+    sq[i] = to_f32(q[bh * DK + i]);
+  }
+  for (int j = t; j < DV; j += 256) sv[j] = to_f32(v[bh * DV + j]);
+  __syncthreads();
+
+  // Partial column dots over this thread's rows.
+  float pk[4] = {0.f, 0.f, 0.f, 0.f};
+  float pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = rg + RG * m;
+    const float kk = sk[i], qq = sq[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pk[c] = fmaf(s[m][c], kk, pk[c]);
+      pq[c] = fmaf(s[m][c], qq, pq[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    red[0][rg][4 * cq + c] = pk[c];
+    red[1][rg][4 * cq + c] = pq[c];
+  }
+  if (t < kWave) {
+    float d = 0.f;
+    for (int i = t; i < DK; i += kWave) d = fmaf(sk[i], sq[i], d);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (t == 0) skq = d;
+  }
+  __syncthreads();
+
+  float a = 1.f;
+  if (MODE == kModeGatedDelta) a = __expf(log_alpha[bh]);
+  if (t < DV) {
+    float sj = 0.f, pj = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      sj += red[0][r][t];
+      pj += red[1][r][t];
+    }
+    float u, o;
+    if (MODE == kModeLinear) {
+      u = sv[t];
+      o = pj + skq * u;
+    } else {
+      const float b = beta[bh];
+      u = b * (sv[t] - a * sj);
+      o = a * pj + skq * u;
+    }
+    su[t] = u;
+    out[bh * DV + t] = from_f32<T>(o);
+  }
+  __syncthreads();
+
+  float u4[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u4[c] = su[4 * cq + c];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const float kk = sk[rg + RG * m];
+    f32x4 w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = fmaf(a, s[m][c], kk * u4[c]);
+    __builtin_nontemporal_store(w, Sp + (rg + RG * m) * NQ + cq);
+  }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.B * a.H), block(256);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  T* o = static_cast<T*>(a.out);
+  switch (a.mode) {
+    case kModeLinear:
+      decode_kernel<T, DK, DV, kModeLinear><<<grid, block, 0, st>>>(
+          q, k, v, a.log_alpha, a.beta, a.S, o);
+      break;
+    case kModeDelta:
+      decode_kernel<T, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
+          q, k, v, a.log_alpha, a.beta, a.S, o);
+      break;
+    default:
+      decode_kernel<T, DK, DV, kModeGatedDelta><<<grid, block, 0, st>>>(
+          q, k, v, a.log_alpha, a.beta, a.S, o);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+  if (a.dk == 64 && a.dv == 64) return launch_dk_dv<T, 64, 64>(a, st);
+  if (a.dk == 64 && a.dv == 128) return launch_dk_dv<T, 64, 128>(a, st);
+  if (a.dk == 128 && a.dv == 64) return launch_dk_dv<T, 128, 64>(a, st);
+  return launch_dk_dv<T, 128, 128>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_t<__bf16>(a, st) : launch_t<float>(a, st);
+}
+
+}  // namespace la

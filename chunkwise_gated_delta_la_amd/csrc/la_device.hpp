@@ -1,0 +1,208 @@
+// Device-side helpers shared by the gfx950 kernels of liblachunk.
+//
+// Element types: q, k, v and outputs are either float or __bf16 (bfloat16,
+// round-to-nearest-even on conversion from float); everything is accumulated
+// in float.
+//
+// MFMA fragments.  The dense contractions use v_mfma_f32_16x16x32_bf16 (bf16
+// inputs) or eight v_mfma_f32_16x16x4_f32 (float inputs) per 32-deep block of
+// the contraction.  For a 16 x 16 output tile and a 32-deep block:
+//
+//   * lane l (0..63) holds, for the A operand, 8 values of row (l % 16) and,
+//     for the B operand, 8 values of column (l % 16); the 8 values are the
+//     contraction indices kidx(l / 16, j), j = 0..7, of the block;
+//   * the float accumulator holds, in lane l, column (l % 16) and rows
+//     4 * (l / 16) + i, i = 0..3.
+//
+// Because a contraction is a plain sum, any assignment of contraction
+// indices to (lane group, slot) works as long as A and B use the same one.
+// We use
+//
+//     kidx(g, j) = 4 g + j         for j < 4
+//     kidx(g, j) = 16 + 4 g + j - 4 for j >= 4
+//
+// which is exactly the set of rows an accumulator lane holds in two
+// vertically stacked 16 x 16 tiles.  A tile produced by one product can
+// therefore feed the next product as its B operand straight from registers
+// (convert and pack, no data movement), which keeps the carried state and
+// the per-chunk update vectors on chip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Contraction index held in slot j of lane group g (see the file comment).
+__device__ __forceinline__ constexpr int kidx(int g, int j) {
+  return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+}
+
+// Eight operand values of one lane for one 32-deep block.
+template <typename T>
+struct Frag;
+
+template <>
+struct Frag<__bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void set(int j, float x) { v[j] = (__bf16)x; }
+};
+
+template <>
+struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void set(int j, float x) { v[j] = x; }
+};
+
+// acc += A(16 x 32) * B(32 x 16) over one 32-deep block.
+__device__ __forceinline__ void mma(const Frag<__bf16>& a, const Frag<__bf16>& b,
+                                    f32x4& acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(const Frag<float>& a, const Frag<float>& b,
+                                    f32x4& acc) {
+  // Each 16x16x4 step consumes one value per lane: lane group g supplies
+  // contraction index kidx(g, j) in step j, so the 8 steps cover the block.
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// B operand built from two stacked accumulator tiles (rows 0-15 in `lo`,
+// rows 16-31 in `hi`), each scaled per row.  scale_lo[i] / scale_hi[i] apply
+// to the rows this lane holds (4 * g + i and 16 + 4 * g + i).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& lo, const f32x4& hi) {
+  Frag<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, lo[i]);
+    f.set(4 + i, hi[i]);
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_acc_scaled(const f32x4& lo, const f32x4& hi,
+                                                        const float* slo,
+                                                        const float* shi) {
+  Frag<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, lo[i] * slo[i]);
+    f.set(4 + i, hi[i] * shi[i]);
+  }
+  return f;
+}
+
+// Operand row of a row-major matrix in LDS or global memory: 8 values
+// m[row][k0 + kidx(g, j)], i.e. two runs of 4 contiguous elements.
+__device__ __forceinline__ Frag<__bf16> frag_row(const __bf16* p, int g) {
+  Frag<__bf16> f;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p + 4 * g);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16 + 4 * g);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_row(const float* p, int g) {
+  Frag<float> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = a[i];
+    f.v[4 + i] = b[i];
+  }
+  return f;
+}
+
+// Operand column of a row-major matrix with row pitch `ld` (elements):
+// 8 values m[k0 + kidx(g, j)][col], gathered one by one.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_col(const T* p, int ld, int g) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.set(j, to_f32(p[kidx(g, j) * ld]));
+  return f;
+}
+
+// Same, scaling element j by s[kidx(g, j)] before the conversion.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_col_scaled(const T* p, int ld, int g,
+                                                   const float* s) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.set(j, to_f32(p[kidx(g, j) * ld]) * s[kidx(g, j)]);
+  return f;
+}
+
+
+// Operand row read from a float matrix and converted to the MFMA input type:
+// 8 values p[kidx(g, j)].  Used for the float UT matrix T feeding bf16 MFMAs.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_row_cvt(const float* p, int g) {
+  Frag<T> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, a[i]);
+    f.set(4 + i, b[i]);
+  }
+  return f;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Cooperative copy of a ROWS x COLS tile from global memory (row pitch gld
+// elements) into LDS (row pitch LLD elements) with 16-byte vectors.
+template <typename T, int ROWS, int COLS, int LLD, int NTHREADS>
+__device__ __forceinline__ void stage_tile(T* lds, const T* __restrict__ src, size_t gld,
+                                           int tid) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int VPR = COLS / VE;
+  constexpr int NV = ROWS * VPR;
+  static_assert(COLS % VE == 0 && (LLD * sizeof(T)) % 16 == 0, "16-byte rows");
+#pragma unroll
+  for (int it = 0; it < (NV + NTHREADS - 1) / NTHREADS; ++it) {
+    const int p = tid + it * NTHREADS;
+    if (NV % NTHREADS == 0 || p < NV) {
+      const int r = p / VPR, cv = p % VPR;
+      *reinterpret_cast<u32x4*>(lds + r * LLD + cv * VE) =
+          *reinterpret_cast<const u32x4*>(src + r * gld + cv * VE);
+    }
+  }
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace la

@@ -1,0 +1,178 @@
+/*
+ * la.h -- C ABI of liblachunk: chunkwise gated-delta linear attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes causal linear attention generalised to the gated
+ * delta rule.  For one (batch b, head h) with a dk x dv state S:
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (state after token t's update)
+ *
+ * with alpha_t = exp(log_alpha_t).  The rule combines the delta rule's
+ * erase-then-write with a scalar decay of the whole state ("Gated DeltaNet"
+ * and "Fast Weight Programmers与DeltaNet" in the hybrid-attention notes
+ * "混合注意力学习(1): 线性注意力"; "继续改进：GDN" in the lecture notes
+ * "【CS336】lecture4 线性注意力|Mamba|GDN|DSA").  Three modes:
+ *
+ *   LA_MODE_LINEAR       S_t = S_{t-1} + k_t v_t^T   (no feature map, no
+ *                        normaliser -- the numerator-only form of "线性注意力"
+ *                        in the hybrid-attention notes and of "The Devil in
+ *                        Linear Transformer" in "LinearAttention 概述")
+ *   LA_MODE_DELTA        alpha_t = 1
+ *   LA_MODE_GATED_DELTA  the full rule
+ *
+ * No scaling, activation, feature map, denominator or output norm is applied
+ * inside the op; the caller prepares q, k, beta and log_alpha.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer into memory the caller owns;
+ *   tensors are dense, row-major (C order), with no padding, and at least
+ *   16-byte aligned.
+ * - Per-token tensors are laid out [B, H, L, d]; gates [B, H, L]; states
+ *   [B, H, dk, dv].  The decode step drops the L axis.
+ * - `dtype` selects the element type of q, k, v and out: LA_DTYPE_F32
+ *   (float) or LA_DTYPE_BF16 (bfloat16, round-to-nearest-even on output).
+ *   Gates and states are always float32; arithmetic accumulates in float32
+ *   and the state is carried in float32.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *   enqueued asynchronously; the call returns without synchronising.
+ * - Return value: LA_OK or an la_status_t error code.  Argument errors are
+ *   detected before anything is enqueued and leave all outputs untouched.
+ *   A failed launch or allocation returns LA_ERR_HIP.  Faults during
+ *   execution surface at the caller's next synchronisation.
+ *   la_last_error() returns a message for the last non-OK return on the
+ *   calling thread.
+ * - The library keeps no pointer after a call returns.  Transient workspace
+ *   is allocated and released stream-ordered on `stream` from a memory pool
+ *   owned by the library, so concurrent calls on different streams do not
+ *   share workspace.
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_MODE_LINEAR = 0,
+  LA_MODE_DELTA = 1,
+  LA_MODE_GATED_DELTA = 2
+} la_mode_t;
+
+typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  LA_ERR_SHAPE = 2,       /* non-positive size, or L not a multiple of C     */
+  LA_ERR_UNSUPPORTED = 3, /* (dk, dv, C, dtype, mode) outside the built set  */
+  LA_ERR_ALIAS = 4,       /* an output overlaps an input (see each call)     */
+  LA_ERR_HIP = 5          /* HIP launch or allocation failure                */
+} la_status_t;
+
+/*
+ * la_chunk_fwd -- chunkwise-parallel forward over whole sequences (prefill /
+ * training form).
+ *
+ * Computes o[b,h,t,:] = S_t^T q_t for t = 0..L-1 and the final state S_L for
+ * every (b, h), starting from S0.  The sequence is cut into chunks of C
+ * tokens; inside a chunk the masked products are used, across chunks the
+ * state is carried.  The chunkwise form is exact -- C changes rounding only,
+ * not the result ("FLASH" in "LinearAttention 概述"; "FWP分块并行机制" in
+ * the hybrid-attention notes).  The delta modes use the inductive
+ * redefinition of the per-token update vectors (WY/UT representation,
+ * "重新定义降低内存占用" and "HouseHolder变换和WY表示" in the hybrid-attention
+ * notes) so no intermediate state is stored per token.
+ *
+ *   q          [B, H, L, dk]  dtype          queries
+ *   k          [B, H, L, dk]  dtype          keys
+ *   v          [B, H, L, dv]  dtype          values
+ *   log_alpha  [B, H, L]      float32        log of the decay (<= 0);
+ *                                            required for GATED_DELTA,
+ *                                            ignored (may be NULL) otherwise
+ *   beta       [B, H, L]      float32        write strength; required for
+ *                                            DELTA and GATED_DELTA, ignored
+ *                                            (may be NULL) for LINEAR
+ *   S0         [B, H, dk, dv] float32        initial state; NULL = zeros
+ *   out        [B, H, L, dv]  dtype          output (written)
+ *   S_final    [B, H, dk, dv] float32        final state (written); may be
+ *                                            NULL; may equal S0 (in-place)
+ *   B, H, L, dk, dv, C        sizes; L must be a multiple of C
+ *   mode       la_mode_t;  dtype  la_dtype_t;  stream  hipStream_t
+ *
+ * Supported: dk = dv in {64, 128}, C = 64, both dtypes, all modes.
+ * Aliasing: S_final == S0 is allowed; any other overlap of out or S_final
+ * with an input, or of out with S_final, returns LA_ERR_ALIAS.
+ */
+int la_chunk_fwd(const void* q, const void* k, const void* v,
+                 const float* log_alpha, const float* beta, const float* S0,
+                 void* out, float* S_final, int B, int H, int L, int dk,
+                 int dv, int C, int mode, int dtype, void* stream);
+
+/*
+ * la_decode_step -- one token of the recurrence for B*H independent states
+ * (decode / inference form), updating the state in place.
+ *
+ * For every (b, h): reads S, applies the mode's update with this token's
+ * (q, k, v, beta, log_alpha) and writes S back, then o = S_new^T q.  The
+ * erase term is evaluated as k (k^T S) -- the read k^T S first -- so a step
+ * costs O(dk dv), not O(dk^2 dv) ("继续改进：GDN" in the lecture notes).  The
+ * recurrent form is the inference path of the same method ("朴素线性注意力"
+ * in the lecture notes; "Prefill、Decode与KVCache" in the hybrid-attention
+ * notes): S after la_chunk_fwd is the S of the first decode step.
+ *
+ *   q, k       [B, H, dk]     dtype
+ *   v          [B, H, dv]     dtype
+ *   log_alpha  [B, H]         float32  (GATED_DELTA only; else may be NULL)
+ *   beta       [B, H]         float32  (DELTA, GATED_DELTA; else may be NULL)
+ *   S          [B, H, dk, dv] float32  state, read and overwritten in place
+ *   out        [B, H, dv]     dtype    output (written)
+ *
+ * Supported: dk, dv in {64, 128} (independently), both dtypes, all modes.
+ * Aliasing: out must not overlap S or any input; S must not overlap q, k,
+ * v or the gates (LA_ERR_ALIAS).
+ */
+int la_decode_step(const void* q, const void* k, const void* v,
+                   const float* log_alpha, const float* beta, float* S,
+                   void* out, int B, int H, int dk, int dv, int mode,
+                   int dtype, void* stream);
+
+/*
+ * Kernel timing with HIP events (profiling aid).
+ *
+ * Between la_profile_begin() and la_profile_end(), every kernel the library
+ * launches (from any thread) is bracketed by two HIP events recorded on the
+ * stream it is launched on.  la_profile_end() waits for the recorded events,
+ * then reports, per kernel name ("la_wy", "la_state", "la_decode"), the
+ * number of launches and the summed event-to-event time in milliseconds,
+ * and stops recording.  `out` is a host array of `capacity` entries; the
+ * number of distinct kernels is written to *count (entries beyond capacity
+ * are dropped).  Returns LA_ERR_HIP if an event call fails, LA_ERR_NULL for
+ * a NULL count.  Timing adds one event record per launch and no host
+ * synchronisation until la_profile_end().
+ */
+typedef struct {
+  char name[32];
+  int launches;
+  double total_ms;
+} la_kernel_time_t;
+
+int la_profile_begin(void);
+int la_profile_end(la_kernel_time_t* out, int capacity, int* count);
+
+/* Message for the last non-OK return on the calling thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char* la_last_error(void);
+
+/* Library version string, e.g. "lachunk 0.1.0 gfx950". */
+const char* la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

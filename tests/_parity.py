@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU parity tests: tolerances and oracle runs.
+
+Tolerances (written into every comparison):
+
+* float32 inputs: max |err| / max |ref| <= 1e-4, for the outputs and,
+  separately, the final states;
+* bfloat16 inputs (float32 accumulation and state): max |err| <= 2e-2 *
+  RMS(ref), for the outputs and, separately, the final states.
+
+The oracle always consumes float64 copies of exactly the tensors handed to
+the GPU (after bfloat16 rounding).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+F32_REL = 1e-4
+BF16_RMS = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bound(ref, dtype):
+    ref = np.asarray(ref, dtype=np.float64)
+    if dtype == "f32":
+        return F32_REL * float(np.max(np.abs(ref)))
+    return BF16_RMS * float(np.sqrt(np.mean(ref * ref)))
+
+
+def assert_close(name, got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err = float(np.max(np.abs(got - ref)))
+    b = bound(ref, dtype)
+    log(f"  {name}: max|err| {err:.3e}  bound {b:.3e}  ({err / b if b else 0:.3f} of bound)")
+    assert err <= b, f"{name}: max|err| {err:.3e} exceeds bound {b:.3e}"
+    return err / b if b else 0.0
+
+
+def to_cuda(x):
+    return {k: t.cuda() for k, t in x.items()}
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def oracle_fwd(x, mode, heads=None):
+    """Oracle forward on all heads, or on a list of (b, h) pairs."""
+    y = workloads.to_f64(x)
+    s0 = y["S0"]
+    if heads is None:
+        return oracle.recurrent_fwd(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
+                                    s0, mode)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    sel = lambda a: a[bs, hs][None]          # noqa: E731  -> [1, n, ...]
+    o, S = oracle.recurrent_fwd(sel(y["q"]), sel(y["k"]), sel(y["v"]),
+                                sel(y["log_alpha"]), sel(y["beta"]), sel(s0), mode)
+    return o[0], S[0]
+
+
+def oracle_decode(x, mode, heads=None):
+    """Oracle decode run over all steps, on all or on sampled (b, h) pairs."""
+    y = workloads.to_f64(x)
+    if heads is None:
+        return oracle.decode_steps(y["S0"], y["q"], y["k"], y["v"], y["log_alpha"],
+                                   y["beta"], mode)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    o, S = oracle.decode_steps(y["S0"][bs, hs][None], y["q"][:, bs, hs][:, None],
+                               y["k"][:, bs, hs][:, None], y["v"][:, bs, hs][:, None],
+                               y["log_alpha"][:, bs, hs][:, None],
+                               y["beta"][:, bs, hs][:, None], mode)
+    return o[:, 0], S[0]

@@ -1,0 +1,113 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU.
+
+Only argument-validation paths are called here (NULL pointers, bad sizes,
+unsupported shapes, overlapping fake pointers): each returns its error code
+before any HIP call, so no GPU is needed and no device memory is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from _lib_build import ROOT, ensure_built
+
+ensure_built()
+from chunkwise_gated_delta_la_amd import _lib  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "la.h")
+OK, NULL, SHAPE, UNSUP, ALIAS = 0, 1, 2, 3, 4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.get()
+    names = _declared_functions()
+    assert {"la_chunk_fwd", "la_decode_step", "la_last_error", "la_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in la.h but not exported"
+
+
+def test_version_and_empty_error():
+    lib = _lib.get()
+    assert lib.la_version().decode().startswith("lachunk ")
+    assert lib.la_version().decode().endswith("gfx950")
+
+
+P = 1 << 20            # fake, never dereferenced, well-separated pointers
+
+
+def fake(i):
+    return ctypes.c_void_p(P * (i + 1))
+
+
+def chunk(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5),
+          out=fake(6), sf=fake(7), B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1):
+    return lib.la_chunk_fwd(q, k, v, la, be, s0, out, sf, B, H, L, dk, dv, C, mode, dtype,
+                            None)
+
+
+def decode(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), S=fake(5),
+           out=fake(6), B=1, H=1, dk=64, dv=64, mode=2, dtype=1):
+    return lib.la_decode_step(q, k, v, la, be, S, out, B, H, dk, dv, mode, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
+    (dict(be=None), NULL), (dict(la=None), NULL), (dict(be=None, mode=1), NULL),
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=0), SHAPE), (dict(C=0), SHAPE),
+    (dict(L=96), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(dk=96, dv=96), UNSUP),
+    (dict(C=32, L=64), UNSUP), (dict(mode=3), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(mode=-1), UNSUP),
+])
+def test_chunk_fwd_rejects(kw, code):
+    lib = _lib.get()
+    assert chunk(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_chunk_fwd_alias_rules():
+    lib = _lib.get()
+    # out overlapping q (q spans 64*64*2 bytes; out starts inside it)
+    assert chunk(lib, out=ctypes.c_void_p(P + 128)) == ALIAS
+    # S_final overlapping v
+    assert chunk(lib, sf=ctypes.c_void_p(3 * P + 64)) == ALIAS
+    # S_final partially overlapping S0 is rejected ...
+    assert chunk(lib, sf=ctypes.c_void_p(6 * P + 4)) == ALIAS
+    # ... out overlapping S_final too
+    assert chunk(lib, out=ctypes.c_void_p(8 * P + 4)) == ALIAS
+
+
+def test_chunk_fwd_unused_gates_may_alias_anything():
+    """Gates a mode ignores are not part of its inputs: in linear mode a
+    beta pointer equal to out is not an alias error (the call is only
+    validated, never launched, because q is NULL)."""
+    lib = _lib.get()
+    assert chunk(lib, mode=0, be=fake(6), la=fake(6), q=None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(S=None), NULL), (dict(out=None), NULL),
+    (dict(be=None), NULL), (dict(la=None), NULL),
+    (dict(B=0), SHAPE), (dict(dk=0), SHAPE), (dict(dk=32), UNSUP), (dict(dv=256), UNSUP),
+    (dict(mode=7), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(out=ctypes.c_void_p(6 * P - 8)), ALIAS),      # out overlaps S's start
+    (dict(S=ctypes.c_void_p(P + 64)), ALIAS),            # S overlaps q
+])
+def test_decode_rejects(kw, code):
+    lib = _lib.get()
+    assert decode(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.get()

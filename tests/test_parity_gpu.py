@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case prints its name, shapes and seed before touching the GPU.  Small
+cases compare every element; the full-size workloads run exactly as the
+bench launches them and compare sampled (batch, head) slices, which the
+oracle computes independently (heads do not interact).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_gated_delta_la_amd as la
+import workloads
+from _parity import assert_close, f64, log, oracle_decode, oracle_fwd, to_cuda
+from workloads import WORKLOADS, Workload
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("linear", "delta", "gated_delta")
+
+
+def recipe(mode, dtype, B, H, L, d, s0_std=0.0, seed=7):
+    """The workloads' recipe for `mode` at reduced sizes."""
+    lin = mode == "linear"
+    return Workload(f"{mode}_{dtype}_b{B}h{H}l{L}d{d}", mode, dtype, B=B, H=H, L=L, dk=d,
+                    dv=d, C=64, qk_norm=not lin,
+                    qkv_scale=1.0 / math.sqrt(d) if lin else 1.0, s0_std=s0_std, seed=seed)
+
+
+def run_chunk(w, x, mode=None, S_final=True):
+    mode = mode or w.mode
+    d = to_cuda(x)
+    s0 = d["S0"] if w.s0_std > 0 else None
+    out, S = la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s0, mode=mode,
+                          C=w.C, return_state=S_final)
+    torch.cuda.synchronize()
+    return out, S
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_decode_small(mode, dtype, dk, dv):
+    w = WORKLOADS[5].scaled(mode=mode, dtype=dtype, B=3, H=5, dk=dk, dv=dv, steps=4, seed=11)
+    log(f"decode small {w}")
+    x = workloads.make_inputs(w)
+    d = to_cuda(x)
+    S = d["S0"].clone()
+    outs = [la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["log_alpha"][n],
+                           d["beta"][n], S, mode=mode) for n in range(w.steps)]
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_decode(x, mode)
+    assert_close("o", np.stack([f64(o) for o in outs]), o_ref, dtype)
+    assert_close("S", f64(S), S_ref, dtype)
+
+
+def test_decode_full_size_sampled():
+    """B=256, H=32, d=128, 128 steps in place, as the bench runs it; the
+    oracle follows 12 sampled (b, h) states through all 128 steps."""
+    w = WORKLOADS[5]
+    log(f"decode full {w}")
+    x = workloads.make_inputs(w)
+    d = to_cuda(x)
+    S = d["S0"].clone()
+    outs = torch.empty((w.steps, w.B, w.H, w.dv), dtype=w.torch_dtype, device="cuda")
+    for n in range(w.steps):
+        la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["log_alpha"][n], d["beta"][n], S,
+                       mode=w.mode, out=outs[n])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(b), int(h)) for b, h in
+                                            zip(rng.integers(0, w.B, 10), rng.integers(0, w.H, 10))]
+    o_ref, S_ref = oracle_decode(x, w.mode, heads)
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    assert_close("o[sampled]", f64(outs[:, bs, hs]), o_ref, w.dtype)
+    assert_close("S[sampled]", f64(S[bs, hs]), S_ref, w.dtype)
+
+
+# ------------------------------------------------------------------ chunk forward
+
+@pytest.mark.parametrize("s0", [0.0, 0.3])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_small(mode, dtype, d, s0):
+    """B=2, H=3, L=320 (5 chunks): every output and state element."""
+    w = recipe(mode, dtype, B=2, H=3, L=320, d=d, s0_std=s0)
+    log(f"chunk small {w}")
+    x = workloads.make_inputs(w)
+    out, S = run_chunk(w, x)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    assert_close("o", f64(out), o_ref, dtype)
+    assert_close("S_final", f64(S), S_ref, dtype)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_single_chunk_single_head(mode):
+    w = recipe(mode, "bf16", B=1, H=1, L=64, d=128, s0_std=0.5, seed=3)
+    log(f"chunk one chunk {w}")
+    x = workloads.make_inputs(w)
+    out, S = run_chunk(w, x)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    assert_close("o", f64(out), o_ref, "bf16")
+    assert_close("S_final", f64(S), S_ref, "bf16")
+
+
+def test_chunk_workload1_full():
+    """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
+    w = WORKLOADS[1]
+    log(f"chunk full {w}")
+    x = workloads.make_inputs(w)
+    out, S = run_chunk(w, x)
+    o_ref, S_ref = oracle_fwd(x, w.mode)
+    assert_close("o", f64(out), o_ref, "f32")
+    assert_close("S_final", f64(S), S_ref, "f32")
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_chunk_full_size_sampled(wid):
+    """Workloads 2-4 at full size, launched as the bench launches them; the
+    oracle recomputes 2 sampled heads over the whole sequence."""
+    w = WORKLOADS[wid]
+    log(f"chunk full {w}")
+    x = workloads.make_inputs(w)
+    out, S = run_chunk(w, x)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
+    o_ref, S_ref = oracle_fwd(x, w.mode, heads)
+    assert_close("o[sampled]", f64(out[bs, hs]), o_ref, w.dtype)
+    assert_close("S_final[sampled]", f64(S[bs, hs]), S_ref, w.dtype)
+
+
+# ------------------------------------------------------------------ properties
+
+@pytest.mark.parametrize("mode", MODES)
+def test_state_carry_and_in_place(mode):
+    """fwd(L1) then fwd(L2, S0 = S_final) equals fwd(L1 + L2); the second
+    call updates its state in place (S_final is S0)."""
+    w = recipe(mode, "bf16", B=2, H=2, L=448, d=128, s0_std=0.2, seed=17)
+    log(f"carry {w}")
+    x = workloads.make_inputs(w)
+    d = to_cuda(x)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    L1 = 192
+    part = lambda t, a, b: t[:, :, a:b].contiguous()   # noqa: E731
+    S = d["S0"].clone()
+    o1, _ = la.chunk_fwd(part(d["q"], 0, L1), part(d["k"], 0, L1), part(d["v"], 0, L1),
+                         part(d["log_alpha"], 0, L1), part(d["beta"], 0, L1), S, mode=mode,
+                         S_final=S)
+    o2, _ = la.chunk_fwd(part(d["q"], L1, w.L), part(d["k"], L1, w.L), part(d["v"], L1, w.L),
+                         part(d["log_alpha"], L1, w.L), part(d["beta"], L1, w.L), S,
+                         mode=mode, S_final=S)
+    torch.cuda.synchronize()
+    assert_close("o", np.concatenate([f64(o1), f64(o2)], axis=2), o_ref, "bf16")
+    assert_close("S_final", f64(S), S_ref, "bf16")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_steps_match_chunk_forward(mode):
+    """L decode steps and one chunkwise forward over the same L tokens reach
+    the same outputs and state (train with the chunk form, infer with the
+    recurrent one)."""
+    w = recipe(mode, "f32", B=2, H=2, L=128, d=64, s0_std=0.3, seed=23)
+    log(f"decode vs chunk {w}")
+    x = workloads.make_inputs(w)
+    d = to_cuda(x)
+    out, S_chunk = la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                                mode=mode)
+    S = d["S0"].clone()
+    outs = [la.decode_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                           d["v"][:, :, t].contiguous(), d["log_alpha"][:, :, t].contiguous(),
+                           d["beta"][:, :, t].contiguous(), S, mode=mode)
+            for t in range(w.L)]
+    torch.cuda.synchronize()
+    o_dec = np.stack([f64(o) for o in outs], axis=2)
+    assert_close("decode vs chunk o", o_dec, f64(out), "f32")
+    assert_close("decode vs chunk S", f64(S), f64(S_chunk), "f32")
+
+
+def test_deterministic():
+    """No atomics and a fixed reduction order: repeated calls are bitwise equal."""
+    w = recipe("gated_delta", "bf16", B=2, H=4, L=256, d=128, s0_std=0.1, seed=29)
+    log(f"determinism {w}")
+    x = workloads.make_inputs(w)
+    a_o, a_S = run_chunk(w, x)
+    b_o, b_S = run_chunk(w, x)
+    assert torch.equal(a_o, b_o) and torch.equal(a_S, b_S)
+
+
+def test_gate_edge_cases():
+    """beta = 0: nothing is written or erased, o_t = gamma_t S0^T q_t.
+    alpha -> 0 (log_alpha = -1e4): history is dropped, o_t = beta_t (q_t . k_t) v_t."""
+    w = recipe("gated_delta", "f32", B=1, H=2, L=192, d=64, s0_std=0.5, seed=31)
+    log(f"gate edges {w}")
+    x = workloads.make_inputs(w)
+    x0 = dict(x, beta=torch.zeros_like(x["beta"]))
+    out, S = run_chunk(w, x0)
+    o_ref, S_ref = oracle_fwd(x0, "gated_delta")
+    assert_close("beta=0 o", f64(out), o_ref, "f32")
+    assert_close("beta=0 S", f64(S), S_ref, "f32")
+    x1 = dict(x, log_alpha=torch.full_like(x["log_alpha"], -1e4))
+    out, S = run_chunk(w, x1)
+    o_ref, S_ref = oracle_fwd(x1, "gated_delta")
+    assert_close("alpha->0 o", f64(out), o_ref, "f32")
+    assert_close("alpha->0 S", f64(S), S_ref, "f32")
+
+
+def test_errors_surface_as_exceptions():
+    w = recipe("delta", "bf16", B=1, H=1, L=96, d=128)
+    x = to_cuda(workloads.make_inputs(w))
+    with pytest.raises(la.LAError, match="LA_ERR_SHAPE"):
+        la.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, mode="delta")
