@@ -14,6 +14,16 @@ MODES = {"linear": 0, "delta": 1, "gated_delta": 2}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
+def _dtype_code(in_dtype, out_dtype):
+    if in_dtype == torch.float32 and out_dtype == torch.float32:
+        return 0
+    if in_dtype == torch.bfloat16 and out_dtype == torch.bfloat16:
+        return 1
+    if in_dtype == torch.bfloat16 and out_dtype == torch.float32:
+        return 2
+    raise TypeError(f"unsupported (input, output) dtypes ({in_dtype}, {out_dtype})")
+
+
 def version():
     return _lib.get().la_version().decode()
 
@@ -48,13 +58,14 @@ def _stream(device):
 
 
 def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta",
-              C=64, out=None, S_final=None, return_state=True):
+              C=64, out=None, S_final=None, return_state=True, out_dtype=None):
     """Chunkwise forward (``la_chunk_fwd``).
 
     q, k ``[B, H, L, dk]``, v ``[B, H, L, dv]`` (float32 or bfloat16, on the
     GPU); log_alpha, beta ``[B, H, L]`` float32; S0 ``[B, H, dk, dv]`` float32
     or None.  Returns ``(out, S_final)`` (S_final None if not requested).
     ``S_final`` may be the same tensor as ``S0`` for an in-place update.
+    ``out_dtype`` (default: the input dtype) may be float32 for bf16 inputs.
     """
     m = _mode(mode)
     if q.dim() != 4 or v.dim() != 4:
@@ -70,9 +81,11 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     _need(log_alpha if m == 2 else None, "log_alpha", (B, H, L), torch.float32, dev)
     _need(beta if m >= 1 else None, "beta", (B, H, L), torch.float32, dev)
     _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    odt = out_dtype or (out.dtype if out is not None else dt)
+    code = _dtype_code(dt, odt)
     if out is None:
-        out = torch.empty((B, H, L, dv), dtype=dt, device=dev)
-    _need(out, "out", (B, H, L, dv), dt, dev)
+        out = torch.empty((B, H, L, dv), dtype=odt, device=dev)
+    _need(out, "out", (B, H, L, dv), odt, dev)
     if S_final is None and return_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
@@ -82,12 +95,13 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
                               _ptr(log_alpha if m == 2 else None),
                               _ptr(beta if m >= 1 else None), _ptr(S0),
                               _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
-                              _DTYPES[dt], _stream(dev))
+                              code, _stream(dev))
     _lib.check(rc)
     return out, S_final
 
 
-def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None):
+def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
+                out_dtype=None):
     """One recurrent decode step (``la_decode_step``), updating ``S`` in place.
 
     q, k ``[B, H, dk]``, v ``[B, H, dv]`` (float32 or bfloat16); log_alpha,
@@ -107,15 +121,17 @@ def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None):
     _need(log_alpha if m == 2 else None, "log_alpha", (B, H), torch.float32, dev)
     _need(beta if m >= 1 else None, "beta", (B, H), torch.float32, dev)
     _need(S, "S", (B, H, dk, dv), torch.float32, dev)
+    odt = out_dtype or (out.dtype if out is not None else dt)
+    code = _dtype_code(dt, odt)
     if out is None:
-        out = torch.empty((B, H, dv), dtype=dt, device=dev)
-    _need(out, "out", (B, H, dv), dt, dev)
+        out = torch.empty((B, H, dv), dtype=odt, device=dev)
+    _need(out, "out", (B, H, dv), odt, dev)
     lib = _lib.get()
     with torch.cuda.device(dev):
         rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v),
                                 _ptr(log_alpha if m == 2 else None),
                                 _ptr(beta if m >= 1 else None), _ptr(S), _ptr(out),
-                                B, H, dk, dv, m, _DTYPES[dt], _stream(dev))
+                                B, H, dk, dv, m, code, _stream(dev))
     _lib.check(rc)
     return out
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -59,9 +60,9 @@ int check_mode_dtype(int mode, int dtype) {
   if (mode < LA_MODE_LINEAR || mode > LA_MODE_GATED_DELTA)
     return fail(LA_ERR_UNSUPPORTED, "mode must be LA_MODE_LINEAR, LA_MODE_DELTA or "
                                     "LA_MODE_GATED_DELTA, got " + std::to_string(mode));
-  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16)
-    return fail(LA_ERR_UNSUPPORTED,
-                "dtype must be LA_DTYPE_F32 or LA_DTYPE_BF16, got " + std::to_string(dtype));
+  if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16 && dtype != LA_DTYPE_BF16_F32OUT)
+    return fail(LA_ERR_UNSUPPORTED, "dtype must be LA_DTYPE_F32, LA_DTYPE_BF16 or "
+                                    "LA_DTYPE_BF16_F32OUT, got " + std::to_string(dtype));
   return LA_OK;
 }
 
@@ -108,6 +109,11 @@ hipError_t get_pool(hipMemPool_t* out) {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+bool canary_enabled() {
+  const char* v = std::getenv("LA_WORKSPACE_CANARY");
+  return v && v[0] == '1';
+}
+
 // ---- kernel timing with HIP events (la_profile_begin / la_profile_end)
 struct TimedLaunch {
   const char* name;
@@ -143,13 +149,14 @@ void prof_add(const char* name, hipEvent_t a, hipEvent_t b) {
 namespace la {
 
 WorkspaceSizes chunk_workspace_sizes(const ChunkArgs& a) {
-  const size_t esz = a.bf16 ? 2 : 4;
+  const size_t esz = a.in_bf16 ? 2 : 4;
+  const size_t planes = a.in_bf16 ? 2 : 1;
   const size_t tokens = (size_t)a.B * a.H * a.L;
   WorkspaceSizes s{};
-  s.Aqk = align_up(tokens * a.C * esz);  // (L / C) chunks of C x C per head
+  s.Aqk = align_up(tokens * a.C * esz * planes);  // (L / C) chunks of C x C
   if (a.mode != kModeLinear) {
     s.W = align_up(tokens * a.d * esz);
-    s.U = align_up(tokens * a.d * esz);
+    s.U = align_up(tokens * a.d * 4);
     s.G = align_up(tokens * 4);
   }
   return s;
@@ -186,11 +193,12 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   if ((size_t)B * H * (L / C) > 0x7fffffffu)
     return fail(LA_ERR_SHAPE, "B * H * L / C exceeds the launch grid");
-  const size_t esz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
   const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
   const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
-  const Range rs0(S0, n_s * 4), ro(out, n_v * esz), rsf(S_final, n_s * 4);
+  const Range rs0(S0, n_s * 4), ro(out, n_v * osz), rsf(S_final, n_s * 4);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro})
@@ -198,8 +206,8 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
   if (rsf.overlaps(rs0) && (S0 != S_final))
     return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
 
-  la::ChunkArgs a{q, k, v, log_alpha, beta, S0, out, S_final,
-                  B, H, L, dk, C, mode, dtype == LA_DTYPE_BF16};
+  la::ChunkArgs a{q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
+                  dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16};
   const la::WorkspaceSizes sz = la::chunk_workspace_sizes(a);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipMemPool_t pool = nullptr;
@@ -214,9 +222,18 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
   if (sz.W) {
     ws.W = p;
     p += sz.W;
-    ws.U = p;
+    ws.U = reinterpret_cast<float*>(p);
     p += sz.U;
     ws.G = reinterpret_cast<float*>(p);
+  }
+  // Debug aid: LA_WORKSPACE_CANARY=1 fills the workspace with all-ones bytes
+  // (NaN in float and bfloat16) before the kernels run, so that any read of
+  // a workspace element no kernel wrote shows up as NaN in the results.
+  if (canary_enabled()) {
+    if (hipError_t e = hipMemsetAsync(base, 0xff, sz.total(), st)) {
+      (void)hipFreeAsync(base, st);
+      return fail_hip("filling the workspace canary", e);
+    }
   }
   hipEvent_t e0 = prof_mark(st);
   hipError_t e = la::launch_wy(a, ws, st);
@@ -251,18 +268,19 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
       !count({B, H, dk, dv}, &n_s) || n_s > (SIZE_MAX >> 3))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   if (n_g > 0x7fffffffu) return fail(LA_ERR_SHAPE, "B * H exceeds the launch grid");
-  const size_t esz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_k * esz), rk(k, n_k * esz), rv(v, n_v * esz);
   const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
   const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
-  const Range rs(S, n_s * 4), ro(out, n_v * esz);
+  const Range rs(S, n_s * 4), ro(out, n_v * osz);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
     if (rs.overlaps(*in)) return fail(LA_ERR_ALIAS, "S overlaps an input");
 
   la::DecodeArgs a{q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode,
-                   dtype == LA_DTYPE_BF16};
+                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = prof_mark(st);
   hipError_t e = la::launch_decode(a, st);

@@ -24,11 +24,11 @@
 namespace la {
 namespace {
 
-template <typename T, int DK, int DV, int MODE>
+template <typename T, typename TO, int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    float* __restrict__ S, T* __restrict__ out) {
+    float* __restrict__ S, TO* __restrict__ out) {
   constexpr int NQ = DV / 4;       // 16-byte column quads per state row
   constexpr int RG = 256 / NQ;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
       o = a * pj + skq * u;
     }
     su[t] = u;
-    out[bh * DV + t] = from_f32<T>(o);
+    out[bh * DV + t] = from_f32<TO>(o);
   }
   __syncthreads();
 
@@ -122,42 +122,44 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, typename TO, int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.B * a.H), block(256);
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
-  T* o = static_cast<T*>(a.out);
+  TO* o = static_cast<TO*>(a.out);
   switch (a.mode) {
     case kModeLinear:
-      decode_kernel<T, DK, DV, kModeLinear><<<grid, block, 0, st>>>(
+      decode_kernel<T, TO, DK, DV, kModeLinear><<<grid, block, 0, st>>>(
           q, k, v, a.log_alpha, a.beta, a.S, o);
       break;
     case kModeDelta:
-      decode_kernel<T, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
+      decode_kernel<T, TO, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
           q, k, v, a.log_alpha, a.beta, a.S, o);
       break;
     default:
-      decode_kernel<T, DK, DV, kModeGatedDelta><<<grid, block, 0, st>>>(
+      decode_kernel<T, TO, DK, DV, kModeGatedDelta><<<grid, block, 0, st>>>(
           q, k, v, a.log_alpha, a.beta, a.S, o);
       break;
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename TO>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-  if (a.dk == 64 && a.dv == 64) return launch_dk_dv<T, 64, 64>(a, st);
-  if (a.dk == 64 && a.dv == 128) return launch_dk_dv<T, 64, 128>(a, st);
-  if (a.dk == 128 && a.dv == 64) return launch_dk_dv<T, 128, 64>(a, st);
-  return launch_dk_dv<T, 128, 128>(a, st);
+  if (a.dk == 64 && a.dv == 64) return launch_dk_dv<T, TO, 64, 64>(a, st);
+  if (a.dk == 64 && a.dv == 128) return launch_dk_dv<T, TO, 64, 128>(a, st);
+  if (a.dk == 128 && a.dv == 64) return launch_dk_dv<T, TO, 128, 64>(a, st);
+  return launch_dk_dv<T, TO, 128, 128>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  return a.bf16 ? launch_t<__bf16>(a, st) : launch_t<float>(a, st);
+  if (a.in_bf16)
+    return a.out_bf16 ? launch_t<__bf16, __bf16>(a, st) : launch_t<__bf16, float>(a, st);
+  return launch_t<float, float>(a, st);
 }
 
 }  // namespace la

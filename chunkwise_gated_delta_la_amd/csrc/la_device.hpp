@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace la {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -204,5 +206,95 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// Split operands.  A float value x feeding a bf16 MFMA is carried as
+// hi = bf16(x) and lo = bf16(x - hi); a product with an exact bf16 operand a
+// is then a*hi + a*lo, accurate to about 2^-16 relative instead of 2^-8.
+// Two split operands multiply as a.hi*b.hi + a.hi*b.lo + a.lo*b.hi (the
+// a.lo*b.lo term is below float rounding).  For float inputs the MFMA is
+// already float and nothing is split: `lo` is unused and all lo products
+// compile away.
+template <typename T>
+struct IsBf16 {
+  static constexpr bool value = false;
+};
+template <>
+struct IsBf16<__bf16> {
+  static constexpr bool value = true;
+};
+
+template <typename T>
+struct Frag2 {
+  Frag<T> hi, lo;
+  __device__ __forceinline__ void set(int j, float x) {
+    if constexpr (IsBf16<T>::value) {
+      const __bf16 h = (__bf16)x;
+      hi.v[j] = h;
+      lo.v[j] = (__bf16)(x - (float)h);
+    } else {
+      hi.set(j, x);
+    }
+  }
+};
+
+// acc += a * b with b split
+template <typename T>
+__device__ __forceinline__ void mma_ab2(const Frag<T>& a, const Frag2<T>& b, f32x4& acc) {
+  if constexpr (IsBf16<T>::value) mma(a, b.lo, acc);
+  mma(a, b.hi, acc);
+}
+
+// acc += a * b with both split
+template <typename T>
+__device__ __forceinline__ void mma_a2b2(const Frag2<T>& a, const Frag2<T>& b, f32x4& acc) {
+  if constexpr (IsBf16<T>::value) {
+    mma(a.lo, b.hi, acc);
+    mma(a.hi, b.lo, acc);
+  }
+  mma(a.hi, b.hi, acc);
+}
+
+// Split B operand from two stacked accumulator tiles (see frag_from_acc).
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_from_acc(const f32x4& lo, const f32x4& hi) {
+  Frag2<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, lo[i]);
+    f.set(4 + i, hi[i]);
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_from_acc_scaled(const f32x4& lo, const f32x4& hi,
+                                                          const float* slo,
+                                                          const float* shi) {
+  Frag2<T> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, lo[i] * slo[i]);
+    f.set(4 + i, hi[i] * shi[i]);
+  }
+  return f;
+}
+
+// Split A operand from a float row p[kidx(g, j)], each value scaled by
+// s[kidx(g, j)] first (a matrix times a diagonal on the right).
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_row_scaled(const float* p, int g, const float* s) {
+  Frag2<T> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
+  const f32x4 sa = *reinterpret_cast<const f32x4*>(s + 4 * g);
+  const f32x4 sb = *reinterpret_cast<const f32x4*>(s + 16 + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, a[i] * sa[i]);
+    f.set(4 + i, b[i] * sb[i]);
+  }
+  return f;
+}
 
 }  // namespace la

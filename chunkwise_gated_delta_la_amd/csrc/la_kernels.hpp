@@ -18,16 +18,22 @@ struct DecodeArgs {
   float* S;
   void* out;
   int B, H, dk, dv, mode;
-  bool bf16;
+  bool in_bf16;   // q, k, v are bf16 (else float)
+  bool out_bf16;  // out is bf16 (else float)
 };
 
 // Transient per-call workspace of the chunk forward (device memory).
-//   W, U  [B*H*L, d]      element type of the inputs   (delta modes only)
-//   Aqk   [B*H*L/C, C, C] element type of the inputs   lower triangle only
-//   G     [B*H*L]         float: in-chunk cumulative log-decay (delta modes)
+//   W    [B*H*L, d]              input element type   (delta modes only)
+//   U    [B*H*L, d]              float                (delta modes only)
+//   Aqk  [B*H*L/C, P, C, C]      input element type; P = 2 planes (hi, lo)
+//                                for bf16 inputs, 1 for float; only the
+//                                32-column blocks on or below the diagonal
+//                                are written
+//   G    [B*H*L]                 float: in-chunk cumulative log-decay
+//                                (delta modes only)
 struct ChunkWorkspace {
   void* W;
-  void* U;
+  float* U;
   void* Aqk;
   float* G;
 };
@@ -42,7 +48,8 @@ struct ChunkArgs {
   void* out;
   float* S_final;
   int B, H, L, d, C, mode;
-  bool bf16;
+  bool in_bf16;   // q, k, v are bf16 (else float)
+  bool out_bf16;  // out is bf16 (else float)
 };
 
 // Bytes of each workspace part for a call (0 when the mode does not use it).

@@ -31,10 +31,14 @@
  *   16-byte aligned.
  * - Per-token tensors are laid out [B, H, L, d]; gates [B, H, L]; states
  *   [B, H, dk, dv].  The decode step drops the L axis.
- * - `dtype` selects the element type of q, k, v and out: LA_DTYPE_F32
- *   (float) or LA_DTYPE_BF16 (bfloat16, round-to-nearest-even on output).
- *   Gates and states are always float32; arithmetic accumulates in float32
- *   and the state is carried in float32.
+ * - `dtype` selects the element types of q, k, v and out (la_dtype_t):
+ *   float32 throughout, bfloat16 throughout (output rounded to nearest
+ *   even), or bfloat16 inputs with a float32 output.  Gates and states are
+ *   always float32; products accumulate in float32 and the state is carried
+ *   in float32.  With bf16 inputs every float intermediate that feeds a
+ *   bf16 matrix product is split into two bf16 terms, so the only roundings
+ *   beyond float are the bf16 inputs themselves, one bf16 copy of the
+ *   chunk's W factor, and the output (when it is bf16).
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *   enqueued asynchronously; the call returns without synchronising.
  * - Return value: LA_OK or an la_status_t error code.  Argument errors are
@@ -63,7 +67,13 @@ typedef enum {
   LA_MODE_GATED_DELTA = 2
 } la_mode_t;
 
-typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+/* Element types of (q, k, v) and of out.  LA_DTYPE_BF16_F32OUT takes bf16
+ * inputs and writes a float32 output (no output rounding to bf16). */
+typedef enum {
+  LA_DTYPE_F32 = 0,         /* q, k, v float32; out float32 */
+  LA_DTYPE_BF16 = 1,        /* q, k, v bf16;    out bf16    */
+  LA_DTYPE_BF16_F32OUT = 2  /* q, k, v bf16;    out float32 */
+} la_dtype_t;
 
 typedef enum {
   LA_OK = 0,

@@ -5,7 +5,13 @@ Tolerances (written into every comparison):
 * float32 inputs: max |err| / max |ref| <= 1e-4, for the outputs and,
   separately, the final states;
 * bfloat16 inputs (float32 accumulation and state): max |err| <= 2e-2 *
-  RMS(ref), for the outputs and, separately, the final states.
+  RMS(ref), for the outputs and, separately, the final states;
+* bfloat16 outputs additionally carry their own rounding: an exact result
+  rounded to bfloat16 is off by up to half an ulp, at most 2^-8 |ref|, which
+  on the full-size workloads alone exceeds 2e-2 * RMS(ref) (the largest
+  outputs are 6-9 RMS).  A bf16 output therefore passes when every element
+  satisfies |err| <= 2e-2 * RMS(ref) * (1 + 2^-8) + 2^-8 |ref|; the same
+  kernels with a float32 output are held to the plain bound.
 
 The oracle always consumes float64 copies of exactly the tensors handed to
 the GPU (after bfloat16 rounding).
@@ -34,16 +40,30 @@ def bound(ref, dtype):
     return BF16_RMS * float(np.sqrt(np.mean(ref * ref)))
 
 
-def assert_close(name, got, ref, dtype):
+BF16_HALF_ULP = 2.0 ** -8
+
+
+def assert_close(name, got, ref, dtype, bf16_out=False):
+    """Compare against the oracle under the tolerance of `dtype` (the input
+    dtype); `bf16_out` adds the output's own rounding per element."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    err = float(np.max(np.abs(got - ref)))
+    diff = np.abs(got - ref)
+    err = float(np.max(diff))
     b = bound(ref, dtype)
-    log(f"  {name}: max|err| {err:.3e}  bound {b:.3e}  ({err / b if b else 0:.3f} of bound)")
-    assert err <= b, f"{name}: max|err| {err:.3e} exceeds bound {b:.3e}"
-    return err / b if b else 0.0
+    if not bf16_out:
+        log(f"  {name}: max|err| {err:.3e}  bound {b:.3e}  ({err / b if b else 0:.3f} of bound)")
+        assert err <= b, f"{name}: max|err| {err:.3e} exceeds bound {b:.3e}"
+        return err / b if b else 0.0
+    excess = float(np.max(diff - BF16_HALF_ULP * np.abs(ref)))
+    bb = b * (1.0 + BF16_HALF_ULP)
+    log(f"  {name} (bf16 out): max|err| {err:.3e} ({err / b:.3f} of plain bound); "
+        f"beyond output rounding {excess:.3e} ({excess / bb:.3f} of bound)")
+    assert excess <= bb, (f"{name}: error beyond the bf16 output rounding {excess:.3e} "
+                          f"exceeds {bb:.3e}")
+    return excess / bb
 
 
 def to_cuda(x):

@@ -63,8 +63,8 @@ def decode(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), S=fake(
     (dict(be=None), NULL), (dict(la=None), NULL), (dict(be=None, mode=1), NULL),
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=0), SHAPE), (dict(C=0), SHAPE),
     (dict(L=96), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(dk=96, dv=96), UNSUP),
-    (dict(C=32, L=64), UNSUP), (dict(mode=3), UNSUP), (dict(dtype=2), UNSUP),
-    (dict(mode=-1), UNSUP),
+    (dict(C=32, L=64), UNSUP), (dict(mode=3), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(mode=-1), UNSUP), (dict(dtype=3), UNSUP),
 ])
 def test_chunk_fwd_rejects(kw, code):
     lib = _lib.get()

@@ -29,14 +29,30 @@ def recipe(mode, dtype, B, H, L, d, s0_std=0.0, seed=7):
                     qkv_scale=1.0 / math.sqrt(d) if lin else 1.0, s0_std=s0_std, seed=seed)
 
 
-def run_chunk(w, x, mode=None, S_final=True):
+def run_chunk(w, x, mode=None, S_final=True, out_dtype=None):
     mode = mode or w.mode
     d = to_cuda(x)
     s0 = d["S0"] if w.s0_std > 0 else None
     out, S = la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s0, mode=mode,
-                          C=w.C, return_state=S_final)
+                          C=w.C, return_state=S_final, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out, S
+
+
+def check_fwd(w, x, o_ref, S_ref, mode=None, sel=None):
+    """Run the forward with the workload's output dtype and, for bf16
+    inputs, also with a float32 output; compare both with the oracle."""
+    sel = sel or (lambda t: t)
+    bf16 = w.dtype == "bf16"
+    out, S = run_chunk(w, x, mode)
+    assert_close("o", f64(sel(out)), o_ref, w.dtype, bf16_out=bf16)
+    assert_close("S_final", f64(sel(S)), S_ref, w.dtype)
+    if bf16:
+        out32, S32 = run_chunk(w, x, mode, out_dtype=torch.float32)
+        assert_close("o (f32 out)", f64(sel(out32)), o_ref, w.dtype)
+        assert torch.equal(S32, S), "the output dtype must not change the state"
+        # the bf16 output is the float output rounded to nearest even
+        assert torch.equal(out32.to(torch.bfloat16), out), "bf16 out != rne(f32 out)"
 
 
 # ------------------------------------------------------------------ decode
@@ -54,8 +70,16 @@ def test_decode_small(mode, dtype, dk, dv):
                            d["beta"][n], S, mode=mode) for n in range(w.steps)]
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_decode(x, mode)
-    assert_close("o", np.stack([f64(o) for o in outs]), o_ref, dtype)
+    assert_close("o", np.stack([f64(o) for o in outs]), o_ref, dtype, bf16_out=dtype == "bf16")
     assert_close("S", f64(S), S_ref, dtype)
+    if dtype == "bf16":
+        S2 = d["S0"].clone()
+        outs = [la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["log_alpha"][n],
+                               d["beta"][n], S2, mode=mode, out_dtype=torch.float32)
+                for n in range(w.steps)]
+        torch.cuda.synchronize()
+        assert_close("o (f32 out)", np.stack([f64(o) for o in outs]), o_ref, dtype)
+        assert torch.equal(S2, S)
 
 
 def test_decode_full_size_sampled():
@@ -77,7 +101,7 @@ def test_decode_full_size_sampled():
     o_ref, S_ref = oracle_decode(x, w.mode, heads)
     bs = [b for b, _ in heads]
     hs = [h for _, h in heads]
-    assert_close("o[sampled]", f64(outs[:, bs, hs]), o_ref, w.dtype)
+    assert_close("o[sampled]", f64(outs[:, bs, hs]), o_ref, w.dtype, bf16_out=True)
     assert_close("S[sampled]", f64(S[bs, hs]), S_ref, w.dtype)
 
 
@@ -92,10 +116,8 @@ def test_chunk_small(mode, dtype, d, s0):
     w = recipe(mode, dtype, B=2, H=3, L=320, d=d, s0_std=s0)
     log(f"chunk small {w}")
     x = workloads.make_inputs(w)
-    out, S = run_chunk(w, x)
     o_ref, S_ref = oracle_fwd(x, mode)
-    assert_close("o", f64(out), o_ref, dtype)
-    assert_close("S_final", f64(S), S_ref, dtype)
+    check_fwd(w, x, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -103,10 +125,8 @@ def test_chunk_single_chunk_single_head(mode):
     w = recipe(mode, "bf16", B=1, H=1, L=64, d=128, s0_std=0.5, seed=3)
     log(f"chunk one chunk {w}")
     x = workloads.make_inputs(w)
-    out, S = run_chunk(w, x)
     o_ref, S_ref = oracle_fwd(x, mode)
-    assert_close("o", f64(out), o_ref, "bf16")
-    assert_close("S_final", f64(S), S_ref, "bf16")
+    check_fwd(w, x, o_ref, S_ref)
 
 
 def test_chunk_workload1_full():
@@ -114,10 +134,8 @@ def test_chunk_workload1_full():
     w = WORKLOADS[1]
     log(f"chunk full {w}")
     x = workloads.make_inputs(w)
-    out, S = run_chunk(w, x)
     o_ref, S_ref = oracle_fwd(x, w.mode)
-    assert_close("o", f64(out), o_ref, "f32")
-    assert_close("S_final", f64(S), S_ref, "f32")
+    check_fwd(w, x, o_ref, S_ref)
 
 
 @pytest.mark.parametrize("wid", [2, 3, 4])
@@ -127,13 +145,11 @@ def test_chunk_full_size_sampled(wid):
     w = WORKLOADS[wid]
     log(f"chunk full {w}")
     x = workloads.make_inputs(w)
-    out, S = run_chunk(w, x)
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     bs = [b for b, _ in heads]
     hs = [h for _, h in heads]
     o_ref, S_ref = oracle_fwd(x, w.mode, heads)
-    assert_close("o[sampled]", f64(out[bs, hs]), o_ref, w.dtype)
-    assert_close("S_final[sampled]", f64(S[bs, hs]), S_ref, w.dtype)
+    check_fwd(w, x, o_ref, S_ref, sel=lambda t: t[bs, hs])
 
 
 # ------------------------------------------------------------------ properties
@@ -157,7 +173,7 @@ def test_state_carry_and_in_place(mode):
                          part(d["log_alpha"], L1, w.L), part(d["beta"], L1, w.L), S,
                          mode=mode, S_final=S)
     torch.cuda.synchronize()
-    assert_close("o", np.concatenate([f64(o1), f64(o2)], axis=2), o_ref, "bf16")
+    assert_close("o", np.concatenate([f64(o1), f64(o2)], axis=2), o_ref, "bf16", bf16_out=True)
     assert_close("S_final", f64(S), S_ref, "bf16")
 
 
@@ -216,3 +232,18 @@ def test_errors_surface_as_exceptions():
     x = to_cuda(workloads.make_inputs(w))
     with pytest.raises(la.LAError, match="LA_ERR_SHAPE"):
         la.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, mode="delta")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+def test_workspace_canary(mode, dtype, d, monkeypatch):
+    """With LA_WORKSPACE_CANARY=1 the library fills its workspace with NaN
+    before the kernels run: any element read but never written would turn
+    the results into NaN."""
+    monkeypatch.setenv("LA_WORKSPACE_CANARY", "1")
+    w = recipe(mode, dtype, B=1, H=2, L=192, d=d, s0_std=0.2, seed=37)
+    log(f"canary {w}")
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    check_fwd(w, x, o_ref, S_ref)
