@@ -41,11 +41,9 @@ def log(msg):
 # Per (token, head) of the forward, d = dk = dv, chunk C, element size e:
 #   algorithmic work of the method (dense-block chunkwise):
 #     gated/delta: 10 C d + 6 d^2 flop;  linear: 4 C d + 4 d^2
-#   la_wy    moves q, k, v in (3 d e), beta and log_alpha (8 B), W, U out
-#            (2 d e), the masked C x C score row out (C e), g out (4 B);
-#            linear mode: q, k in, score row out
-#   la_state moves q, k, W, U, the score row and g in, o out;
-#            linear mode: q, k, v, the score row in, o out
+#   la_chunk (the fused forward kernel) moves q, k, v in and o out (4 d e),
+#            plus beta (delta modes) and log_alpha (gated) at 4 B each;
+#            per (b, h): S0 in (when given) and S_final out at dk dv 4 B
 # Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,
 # o (2 dk e + 2 dv e), two float gates.
 
@@ -57,17 +55,20 @@ def fwd_flops_per_token_head(w):
 
 
 def kernel_bytes_per_token_head(name, w):
-    d, C = w.dk, w.C
-    e = 2 if w.dtype == "bf16" else 4
-    if name == "la_wy":
-        if w.mode == "linear":
-            return 2 * d * e + C * e
-        return 3 * d * e + 8 + 2 * d * e + C * e + 4
-    if name == "la_state":
-        if w.mode == "linear":
-            return 3 * d * e + C * e + d * e
-        return 4 * d * e + C * e + 4 + d * e
-    raise KeyError(name)
+    """Algorithmic HBM bytes per (token, head) of a forward kernel: the
+    fused chunk kernel reads q, k, v and the gates the mode uses once and
+    writes o once (initial and final states are added per head)."""
+    if name != "la_chunk":
+        raise KeyError(name)
+    return fwd_min_bytes_per_token_head(w)
+
+
+def kernel_bytes_per_head(name, w):
+    """Per-head state bytes of a forward call: S0 read (if given), S_final
+    written."""
+    if name != "la_chunk":
+        raise KeyError(name)
+    return (2 if w.s0_std > 0 else 1) * w.dk * w.dv * 4
 
 
 def decode_bytes_per_head(w):
@@ -76,9 +77,10 @@ def decode_bytes_per_head(w):
 
 
 def fwd_min_bytes_per_token_head(w):
-    """q, k, v, o and the two gates: what the op must read and write."""
+    """q, k, v, o and the gates the mode reads: what the op must move."""
     e = 2 if w.dtype == "bf16" else 4
-    return (2 * w.dk + 2 * w.dv) * e + 8
+    gates = {"linear": 0, "delta": 4, "gated_delta": 8}[w.mode]
+    return (2 * w.dk + 2 * w.dv) * e + gates
 
 
 # ------------------------------------------------------------------ legs
@@ -120,7 +122,8 @@ def bench_forward(w, steps, warmup):
     kernels = {}
     for name, (n, ms) in kt.stats.items():
         avg_ms = ms / max(n, 1)
-        by = kernel_bytes_per_token_head(name, w) * token_heads
+        by = (kernel_bytes_per_token_head(name, w) * token_heads
+              + kernel_bytes_per_head(name, w) * w.B * w.H)
         kernels[name] = {"launches": n, "avg_ms": round(avg_ms, 5),
                          "algorithmic_bytes": by,
                          "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1)}
@@ -130,7 +133,8 @@ def bench_forward(w, steps, warmup):
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
     flops = fwd_flops_per_token_head(w) * token_heads
-    min_bytes = fwd_min_bytes_per_token_head(w) * token_heads
+    min_bytes = (fwd_min_bytes_per_token_head(w) * token_heads
+                 + kernel_bytes_per_head("la_chunk", w) * w.B * w.H)
     res = {
         "value": w.B * w.L / sec,
         "ms_per_step": sec * 1e3,

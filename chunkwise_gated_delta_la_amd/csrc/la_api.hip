@@ -74,46 +74,6 @@ int check_gates(int mode, const float* log_alpha, const float* beta) {
   return LA_OK;
 }
 
-// Per-device memory pool for transient workspace.  Its release threshold
-// is raised so that memory freed at the end of one call is reused by the
-// next call instead of being returned to the driver.
-std::mutex g_pool_mu;
-hipMemPool_t g_pools[64] = {};
-
-hipError_t get_pool(hipMemPool_t* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lk(g_pool_mu);
-  if (!g_pools[dev]) {
-    hipMemPoolProps props = {};
-    props.allocType = hipMemAllocationTypePinned;
-    props.handleTypes = hipMemHandleTypeNone;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t pool = nullptr;
-    e = hipMemPoolCreate(&pool, &props);
-    if (e != hipSuccess) return e;
-    uint64_t threshold = UINT64_MAX;
-    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
-    if (e != hipSuccess) {
-      (void)hipMemPoolDestroy(pool);
-      return e;
-    }
-    g_pools[dev] = pool;
-  }
-  *out = g_pools[dev];
-  return hipSuccess;
-}
-
-size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
-
-bool canary_enabled() {
-  const char* v = std::getenv("LA_WORKSPACE_CANARY");
-  return v && v[0] == '1';
-}
-
 // ---- kernel timing with HIP events (la_profile_begin / la_profile_end)
 struct TimedLaunch {
   const char* name;
@@ -146,24 +106,6 @@ void prof_add(const char* name, hipEvent_t a, hipEvent_t b) {
 
 }  // namespace
 
-namespace la {
-
-WorkspaceSizes chunk_workspace_sizes(const ChunkArgs& a) {
-  const size_t esz = a.in_bf16 ? 2 : 4;
-  const size_t planes = a.in_bf16 ? 2 : 1;
-  const size_t tokens = (size_t)a.B * a.H * a.L;
-  WorkspaceSizes s{};
-  s.Aqk = align_up(tokens * a.C * esz * planes);  // (L / C) chunks of C x C
-  if (a.mode != kModeLinear) {
-    s.W = align_up(tokens * a.d * esz);
-    s.U = align_up(tokens * a.d * 4);
-    s.G = align_up(tokens * 4);
-  }
-  return s;
-}
-
-}  // namespace la
-
 extern "C" {
 
 const char* la_last_error(void) { return g_last_error.c_str(); }
@@ -191,8 +133,8 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
   if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
       !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s) || n_qk > (SIZE_MAX >> 3))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
-  if ((size_t)B * H * (L / C) > 0x7fffffffu)
-    return fail(LA_ERR_SHAPE, "B * H * L / C exceeds the launch grid");
+  if ((size_t)B * H * (dv / 16) > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "B * H * dv / 16 exceeds the launch grid");
   const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
   const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
@@ -208,46 +150,11 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
 
   la::ChunkArgs a{q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16};
-  const la::WorkspaceSizes sz = la::chunk_workspace_sizes(a);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipMemPool_t pool = nullptr;
-  if (hipError_t e = get_pool(&pool)) return fail_hip("creating the workspace pool", e);
-  void* base = nullptr;
-  if (hipError_t e = hipMallocFromPoolAsync(&base, sz.total(), pool, st))
-    return fail_hip("allocating workspace", e);
-  char* p = static_cast<char*>(base);
-  la::ChunkWorkspace ws{};
-  ws.Aqk = p;
-  p += sz.Aqk;
-  if (sz.W) {
-    ws.W = p;
-    p += sz.W;
-    ws.U = reinterpret_cast<float*>(p);
-    p += sz.U;
-    ws.G = reinterpret_cast<float*>(p);
-  }
-  // Debug aid: LA_WORKSPACE_CANARY=1 fills the workspace with all-ones bytes
-  // (NaN in float and bfloat16) before the kernels run, so that any read of
-  // a workspace element no kernel wrote shows up as NaN in the results.
-  if (canary_enabled()) {
-    if (hipError_t e = hipMemsetAsync(base, 0xff, sz.total(), st)) {
-      (void)hipFreeAsync(base, st);
-      return fail_hip("filling the workspace canary", e);
-    }
-  }
   hipEvent_t e0 = prof_mark(st);
-  hipError_t e = la::launch_wy(a, ws, st);
-  hipEvent_t e1 = prof_mark(st);
-  hipEvent_t e2 = nullptr;
-  if (e == hipSuccess) {
-    e = la::launch_state(a, ws, st);
-    e2 = prof_mark(st);
-  }
-  prof_add("la_wy", e0, e1);
-  prof_add("la_state", e1, e2);
-  hipError_t ef = hipFreeAsync(base, st);
-  if (e != hipSuccess) return fail_hip("launching the chunk kernels", e);
-  if (ef != hipSuccess) return fail_hip("releasing workspace", ef);
+  hipError_t e = la::launch_chunk(a, st);
+  prof_add("la_chunk", e0, prof_mark(st));
+  if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
   return LA_OK;
 }
 

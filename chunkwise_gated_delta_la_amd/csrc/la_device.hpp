@@ -280,6 +280,21 @@ __device__ __forceinline__ Frag2<T> frag2_from_acc_scaled(const f32x4& lo, const
   return f;
 }
 
+// Split operand from a float row p[kidx(g, j)] (a row of a float matrix
+// as the A operand, or a column stored contiguously as the B operand).
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_row(const float* p, int g) {
+  Frag2<T> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, a[i]);
+    f.set(4 + i, b[i]);
+  }
+  return f;
+}
+
 // Split A operand from a float row p[kidx(g, j)], each value scaled by
 // s[kidx(g, j)] first (a matrix times a diagonal on the right).
 template <typename T>

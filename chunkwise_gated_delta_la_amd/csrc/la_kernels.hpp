@@ -22,22 +22,6 @@ struct DecodeArgs {
   bool out_bf16;  // out is bf16 (else float)
 };
 
-// Transient per-call workspace of the chunk forward (device memory).
-//   W    [B*H*L, d]              input element type   (delta modes only)
-//   U    [B*H*L, d]              float                (delta modes only)
-//   Aqk  [B*H*L/C, P, C, C]      input element type; P = 2 planes (hi, lo)
-//                                for bf16 inputs, 1 for float; only the
-//                                32-column blocks on or below the diagonal
-//                                are written
-//   G    [B*H*L]                 float: in-chunk cumulative log-decay
-//                                (delta modes only)
-struct ChunkWorkspace {
-  void* W;
-  float* U;
-  void* Aqk;
-  float* G;
-};
-
 struct ChunkArgs {
   const void* q;
   const void* k;
@@ -52,15 +36,7 @@ struct ChunkArgs {
   bool out_bf16;  // out is bf16 (else float)
 };
 
-// Bytes of each workspace part for a call (0 when the mode does not use it).
-struct WorkspaceSizes {
-  size_t W, U, Aqk, G;
-  size_t total() const { return W + U + Aqk + G; }
-};
-WorkspaceSizes chunk_workspace_sizes(const ChunkArgs& a);
-
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_wy(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t st);
-hipError_t launch_state(const ChunkArgs& a, const ChunkWorkspace& ws, hipStream_t st);
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 
 }  // namespace la

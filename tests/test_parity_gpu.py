@@ -237,13 +237,19 @@ def test_errors_surface_as_exceptions():
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", MODES)
-def test_workspace_canary(mode, dtype, d, monkeypatch):
-    """With LA_WORKSPACE_CANARY=1 the library fills its workspace with NaN
-    before the kernels run: any element read but never written would turn
-    the results into NaN."""
-    monkeypatch.setenv("LA_WORKSPACE_CANARY", "1")
-    w = recipe(mode, dtype, B=1, H=2, L=192, d=d, s0_std=0.2, seed=37)
-    log(f"canary {w}")
+def test_outputs_fully_written(mode, dtype, d):
+    """out and S_final are pre-filled with NaN: every element must be
+    written by the kernel (a skipped row or column tile stays NaN).  B * H
+    = 8 exercises the head-to-XCD block numbering."""
+    w = recipe(mode, dtype, B=2, H=4, L=192, d=d, s0_std=0.2, seed=37)
+    log(f"outputs fully written {w}")
     x = workloads.make_inputs(w)
     o_ref, S_ref = oracle_fwd(x, mode)
-    check_fwd(w, x, o_ref, S_ref)
+    dev = to_cuda(x)
+    out = torch.full((w.B, w.H, w.L, w.dv), float("nan"), dtype=w.torch_dtype, device="cuda")
+    S = torch.full((w.B, w.H, w.dk, w.dv), float("nan"), dtype=torch.float32, device="cuda")
+    la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"],
+                 mode=mode, out=out, S_final=S)
+    torch.cuda.synchronize()
+    assert_close("o", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
+    assert_close("S_final", f64(S), S_ref, dtype)
