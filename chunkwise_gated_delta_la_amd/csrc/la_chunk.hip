@@ -38,7 +38,8 @@
 //                       columns), beta and g to LDS; issue the next
 //                       chunk's global loads
 //   scores   all waves  the 10 lower-triangular 16 x 16 tiles of Q K^T and
-//                       (delta modes) of K K^T on MFMA, with decay and mask
+//                       (delta modes) of K K^T on MFMA, with decay and mask;
+//                       each wave owns two row tiles of one product
 //   T        wave 0     the four 16 x 16 diagonal blocks of T by forward
 //                       substitution (one lane per column)
 //            waves 0-2  wave j: the blocks below the diagonal in column
@@ -48,6 +49,8 @@
 //                       state that wave 0 published in LDS
 //   output   waves 1-3  O = diag(gam) Q S + Aqk U_new; wave 0 publishes the
 //                       new state for the next chunk's Q S
+// With one wave per SIMD nothing hides LDS latency, so every phase loads
+// all of its operands into registers before its first product.
 //
 // Precision (bf16 inputs).  Q, K, V are exact bf16 MFMA operands.  Every
 // float quantity that feeds a bf16 MFMA -- the state S, R, U_new, the
@@ -65,13 +68,6 @@ constexpr int C = 64;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-// Rows of the f32x4 accumulator `a` this lane holds: 4 g + i.
-// Number of the lower-triangular tile job p (0..9) -> (ti, tj), ti >= tj.
-__device__ __forceinline__ void tri_tile(int p, int& ti, int& tj) {
-  ti = p >= 6 ? 3 : p >= 3 ? 2 : p >= 1 ? 1 : 0;
-  tj = p - ti * (ti + 1) / 2;
-}
-
 // 16-deep operand: values p[4 g + j] for j < 4 and zero in the upper four
 // slots (the second 16 of a 32-deep block), matching kidx().
 template <typename T>
@@ -84,6 +80,149 @@ __device__ __forceinline__ Frag2<T> frag2_row16(const float* p, int g) {
     f.set(4 + i, 0.f);
   }
   return f;
+}
+
+// The 16-bit element `half` (0 = low, 1 = high) of the dwords a and b,
+// packed as (a's, b's) into one dword: two rows of a column of a bf16 tile.
+__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int half) {
+  return half ? (a >> 16) | (b & 0xffff0000u) : (a & 0xffffu) | (b << 16);
+}
+
+// Column swizzle of the transposed K tile: the 16-byte units of row r are
+// permuted by XOR with ((r / 8) mod 8), which spreads both the transposing
+// writes (16 lanes writing one column of 16 different rows) and the row
+// reads over the LDS banks.  Returns the XOR in elements.
+template <typename T>
+__device__ __forceinline__ constexpr int tswz(int r) {
+  return ((r >> 3) & 7) * (16 / (int)sizeof(T));
+}
+
+// Operand row of the swizzled tile: 8 values rowp[(c0 + kidx(g, j)) ^ swz];
+// c0 is a multiple of 32 elements, swz a multiple of 16 bytes.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_row_swz(const T* rowp, int c0, int g, int swz) {
+  Frag<T> f;
+  const int a = (c0 + 4 * g) ^ swz, b = (c0 + 16 + 4 * g) ^ swz;
+  if constexpr (IsBf16<T>::value) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(rowp + a);
+    const bf16x4 y = *reinterpret_cast<const bf16x4*>(rowp + b);
+    f.v = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + a);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(rowp + b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.v[i] = x[i];
+      f.v[4 + i] = y[i];
+    }
+  }
+  return f;
+}
+
+// Scores of two row tiles R0 and R1 of X K^T.  X = Q: the masked, decayed
+// scores (Q K^T) * M * Gamma go to Aq as hi/lo planes; X = K:
+// A = strict_lower(diag(beta) (K K^T) * Gamma) goes to As.  All operands
+// are loaded before the first product; the 16 x 16 tiles strictly below the
+// diagonal need no mask.
+template <typename T, int D, bool GATED, bool QK, int R0, int R1, int LDQ, int LDT, int LDF>
+__device__ __forceinline__ void score_rows(const T* X, const T* Ks, const float* gs,
+                                           const float* bs, T* Aq, float* As, int g, int n,
+                                           int nq) {
+  constexpr int NKB = D / 32;
+  constexpr int NT = (R0 > R1 ? R0 : R1) + 1;
+  constexpr bool kSplit = IsBf16<T>::value;
+  Frag<T> a0[NKB], a1[NKB], b[NT][NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    a0[kb] = frag_row(X + 16 * LDQ * R0 + nq + 32 * kb, g);
+    a1[kb] = frag_row(X + 16 * LDQ * R1 + nq + 32 * kb, g);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) b[t][kb] = frag_row(Ks + 16 * LDQ * t + nq + 32 * kb, g);
+  // gates: rows 16 R + 4 g + i of this lane, column 16 t + n
+  f32x4 gr0 = zero4(), gr1 = zero4(), br0 = zero4(), br1 = zero4();
+  float gc[NT];
+  if constexpr (GATED) {
+    gr0 = *reinterpret_cast<const f32x4*>(gs + 16 * R0 + 4 * g);
+    gr1 = *reinterpret_cast<const f32x4*>(gs + 16 * R1 + 4 * g);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) gc[t] = gs[16 * t + n];
+  }
+  if constexpr (!QK) {
+    br0 = *reinterpret_cast<const f32x4*>(bs + 16 * R0 + 4 * g);
+    br1 = *reinterpret_cast<const f32x4*>(bs + 16 * R1 + 4 * g);
+  }
+  f32x4 acc0[R0 + 1], acc1[R1 + 1];
+#pragma unroll
+  for (int t = 0; t <= R0; ++t) acc0[t] = zero4();
+#pragma unroll
+  for (int t = 0; t <= R1; ++t) acc1[t] = zero4();
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int t = 0; t <= R0; ++t) mma(a0[kb], b[t][kb], acc0[t]);
+#pragma unroll
+    for (int t = 0; t <= R1; ++t) mma(a1[kb], b[t][kb], acc1[t]);
+  }
+  auto epilogue = [&](const f32x4& acc, int R, int t, const f32x4& gr, const f32x4& br) {
+    const int cc = 16 * t + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * R + 4 * g + i;
+      const bool keep = R > t || (QK ? r >= cc : r > cc);
+      float decay = 1.f;
+      if constexpr (GATED) decay = __expf(keep ? gr[i] - gc[t] : 0.f);
+      float x = acc[i] * decay;
+      if constexpr (!QK) x *= br[i];
+      x = keep ? x : 0.f;
+      if constexpr (QK) {
+        const T h = from_f32<T>(x);
+        Aq[r * LDT + cc] = h;
+        if constexpr (kSplit) Aq[C * LDT + r * LDT + cc] = from_f32<T>(x - to_f32(h));
+      } else {
+        As[r * LDF + cc] = x;
+      }
+    }
+  };
+#pragma unroll
+  for (int t = 0; t <= R0; ++t) epilogue(acc0[t], R0, t, gr0, br0);
+#pragma unroll
+  for (int t = 0; t <= R1; ++t) epilogue(acc1[t], R1, t, gr1, br1);
+}
+
+// The four 16 x 16 diagonal blocks of T, one wave: lane (g, n) solves
+// column n of block g by forward substitution,
+//   x_r = [r == n] - sum_{i < r} A[16 g + r][16 g + i] x_i,
+// with the block's rows loaded first and each sum split over two
+// accumulators to halve the dependent chain.
+template <typename T, int LDF, int LDT>
+__device__ __forceinline__ void tdiag_solve(const float* As, float* Tf, T* Tb, int g, int n) {
+  const float* Ab = As + (16 * g) * LDF + 16 * g;
+  f32x4 arow[16][4];
+#pragma unroll
+  for (int r = 1; r < 16; ++r)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      if (4 * i4 < r) arow[r][i4] = *reinterpret_cast<const f32x4*>(Ab + r * LDF + 4 * i4);
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float s0 = r == n ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < r; ++i) {
+      const float a = arow[r][i / 4][i % 4];
+      if (i % 2 == 0) s0 = fmaf(-a, x[i], s0);
+      else s1 = fmaf(-a, x[i], s1);
+    }
+    x[r] = s0 + s1;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    Tf[(16 * g + r) * LDF + 16 * g + n] = x[r];
+    if constexpr (IsBf16<T>::value) Tb[(16 * g + r) * LDT + 16 * g + n] = from_f32<T>(x[r]);
+  }
 }
 
 // Column block J of T = (I + A)^{-1} below the diagonal, given the
@@ -122,6 +261,99 @@ __device__ __forceinline__ void tcol_solve(const float* As, float* Tf, T* Tb, in
   }
 }
 
+// Q S for NTI row tiles (TI0, TI1) of the chunk, from the entry state that
+// wave 0 published in Sx as split B-operand fragments.
+template <typename T, int D, int NTI, int TI0, int TI1, int LDQ>
+__device__ __forceinline__ void qs_rows(const T* Qs, const Frag<T>* Sx, f32x4 (&qs)[2], int g,
+                                        int nq, int lane) {
+  constexpr int NKB = D / 32;
+  constexpr int kPlanes = IsBf16<T>::value ? 2 : 1;
+  Frag2<T> sx[NKB];
+  Frag<T> qf[NTI][NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    sx[kb].hi = Sx[(kPlanes * kb) * kWave + lane];
+    if constexpr (kPlanes == 2) sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      qf[u][kb] = frag_row(Qs + 16 * LDQ * (u == 0 ? TI0 : TI1) + nq + 32 * kb, g);
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    qs[u] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[u][kb], sx[kb], qs[u]);
+  }
+}
+
+// O = diag(gam) Q S + Aqk U_new for NTI row tiles (TI0, TI1); linear mode
+// uses V for U_new.  ob0 indexes (first row of the chunk, this lane's
+// column) of the output.
+template <typename T, int D, int MODE, int NTI, int TI0, int TI1, int LDT>
+__device__ __forceinline__ void out_rows(const T* Aq, const Frag<T>* Ux, const T* Vt,
+                                         const float* gs, const f32x4 (&qs)[2], void* out_,
+                                         size_t ob0, int out_bf16, int g, int nt, int lane) {
+  constexpr bool kDelta = MODE != kModeLinear;
+  constexpr bool kGated = MODE == kModeGatedDelta;
+  constexpr bool kSplit = IsBf16<T>::value;
+  constexpr int kPlanes = kSplit ? 2 : 1;
+  Frag2<T> uf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if constexpr (kDelta) {
+      uf[kb].hi = Ux[(kPlanes * kb) * kWave + lane];
+      if constexpr (kSplit) uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
+    } else {
+      uf[kb].hi = frag_row(Vt + nt + 32 * kb, g);
+    }
+  }
+  Frag2<T> af[NTI][2];
+  f32x4 gg[NTI];
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u == 0 ? TI0 : TI1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && ti < 2) continue;       // Aq is zero above the diagonal
+      af[u][kb].hi = frag_row(Aq + 16 * LDT * ti + nt + 32 * kb, g);
+      if constexpr (kSplit) af[u][kb].lo = frag_row(Aq + C * LDT + 16 * LDT * ti + nt + 32 * kb, g);
+    }
+    if constexpr (kGated) gg[u] = *reinterpret_cast<const f32x4*>(gs + 16 * ti + 4 * g);
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u == 0 ? TI0 : TI1;
+    f32x4 o = qs[u];
+    if constexpr (kGated) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= __expf(gg[u][i]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && ti < 2) continue;
+      if constexpr (kDelta) {
+        mma_a2b2(af[u][kb], uf[kb], o);
+      } else {
+        // linear: V is exact in the input type
+        if constexpr (kSplit) mma(af[u][kb].lo, uf[kb].hi, o);
+        mma(af[u][kb].hi, uf[kb].hi, o);
+      }
+    }
+    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
+    if (out_bf16) {
+      __bf16* out = static_cast<__bf16*>(out_);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = (__bf16)o[i];
+    } else {
+      float* out = static_cast<float*>(out_);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = o[i];
+    }
+  }
+}
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -142,9 +374,15 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
   // A transposed copy of K serves K^T U_new; without room for it (float,
   // D = 128) K^T's operand columns are gathered from K directly.
   constexpr bool kKt = sizeof(T) == 2 || D == 64;
+  // Prefetch layout: thread t holds 16-byte vector t % VPR of the rows
+  // 2 p and 2 p + 1, p = t / VPR + NRP * pass.
   constexpr int VPR = D / PE;                    // 16-byte vectors per row
-  constexpr int NVQ = C * VPR / kThreads;        // Q (and K) vectors per thread
-  static_assert(NVQ * kThreads == C * VPR, "tile split");
+  constexpr int NRP = kThreads / VPR;            // row pairs per pass
+  constexpr int NPASS = C / (2 * NRP);
+  constexpr int NVQ = 2 * NPASS;                 // Q (and K) vectors per thread
+  static_assert(NPASS * 2 * NRP == C, "tile split");
+  constexpr int VVR = 16 / PE;                   // V vectors per 16-column row
+  constexpr int NVV = C * VVR / kWave;           // V vectors per lane of wave 0
 
   __shared__ __attribute__((aligned(16))) T Qs[C * LDQ];
   __shared__ __attribute__((aligned(16))) T Ks[C * LDQ];
@@ -187,7 +425,9 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
   // tile address is this plus a wave-uniform or constant term, so the
   // vector address arithmetic there is additions only.
   const int nq = n * LDQ;       // row n of a Q / K tile
-  const int nt = n * LDT;       // row n of a K^T / V^T / T / Aqk tile
+  const int nt = n * LDT;       // row n of a V^T / T / Aqk tile
+  const int pcv = tid % VPR;    // prefetch: 16-byte vector within the row
+  const int prp = tid / VPR;    // prefetch: row pair within a pass
 
   const size_t hbase = (size_t)bh * L;          // first token row of the head
 
@@ -196,6 +436,31 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
   if constexpr (kDelta && kSplit) Top = Tb;
   else Top = reinterpret_cast<const T*>(Tf);
   constexpr int LDTop = kDelta && kSplit ? LDT : LDF;
+
+  // ---- blocks that stay zero for the whole sequence.  The output reads
+  // Aq, and U_new = T R reads T, in 32-column blocks: the upper 16 x 16
+  // blocks (0, 1) and (2, 3) that share such a block with a lower block are
+  // never written by the chunk loop and must read as zero.
+  if (wave == kWaves - 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p) {
+        Aq[p * C * LDT + r * LDT + 16 + n] = from_f32<T>(0.f);
+        Aq[p * C * LDT + (32 + r) * LDT + 48 + n] = from_f32<T>(0.f);
+      }
+      if constexpr (kDelta) {
+        if constexpr (kSplit) {
+          Tb[r * LDT + 16 + n] = from_f32<T>(0.f);
+          Tb[(32 + r) * LDT + 48 + n] = from_f32<T>(0.f);
+        } else {
+          Tf[r * LDF + 16 + n] = 0.f;
+          Tf[(32 + r) * LDF + 48 + n] = 0.f;
+        }
+      }
+    }
+  }
 
   // ---- state tile (wave 0): S[tj][i] = S[16 tj + 4 g + i][col]
   f32x4 S[NKT];
@@ -221,23 +486,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
 
   // ---- prefetch registers for one chunk
   u32x4 pq[NVQ], pk[NVQ];
-  u32x4 pv;                 // threads < 2 * C: one half-row (8 or 4 columns) of V
+  u32x4 pv[NVV];            // wave 0: this tile's 16 columns of V
   float pla = 0.f, pb = 0.f;
-  constexpr int VVR = 16 / PE;                   // V vectors per tile row
+  // V row of wave-0 prefetch vector m: bf16 lanes take row pairs
+  // (2 p, 2 p + 1), float lanes rows p + 16 m; the 16-byte unit is lane % VVR.
+  auto vrow = [&](int m) {
+    if constexpr (kSplit) return 2 * (lane / 2) + m;
+    else return lane / VVR + (C / NVV) * m;
+  };
   auto load_chunk = [&](int c) {
     const size_t row0 = hbase + (size_t)c * C;
 #pragma unroll
     for (int m = 0; m < NVQ; ++m) {
-      const int p = tid + kThreads * m;
-      const int r = p / VPR, cv = p % VPR;
-      pq[m] = *reinterpret_cast<const u32x4*>(q + (row0 + r) * D + cv * PE);
-      pk[m] = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + cv * PE);
-    }
-    if (tid < C * VVR) {
-      const int r = tid / VVR, h = tid % VVR;
-      pv = *reinterpret_cast<const u32x4*>(v + (row0 + r) * D + col0 + h * PE);
+      const int r = 2 * (prp + NRP * (m / 2)) + (m % 2);
+      pq[m] = *reinterpret_cast<const u32x4*>(q + (row0 + r) * D + pcv * PE);
+      pk[m] = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + pcv * PE);
     }
     if (wave == 0) {
+#pragma unroll
+      for (int m = 0; m < NVV; ++m)
+        pv[m] = *reinterpret_cast<const u32x4*>(v + (row0 + vrow(m)) * D + col0 +
+                                               (lane % VVR) * PE);
       if (kGated) pla = log_alpha[row0 + lane];
       if (kDelta) pb = beta[row0 + lane];
     }
@@ -252,23 +521,44 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
     // ---------------- stage: registers -> LDS, then prefetch the next chunk
 #pragma unroll
     for (int m = 0; m < NVQ; ++m) {
-      const int p = tid + kThreads * m;
-      const int r = p / VPR, cv = p % VPR;
-      *reinterpret_cast<u32x4*>(Qs + r * LDQ + cv * PE) = pq[m];
-      *reinterpret_cast<u32x4*>(Ks + r * LDQ + cv * PE) = pk[m];
-      if constexpr (kKt) {
-        const T* e = reinterpret_cast<const T*>(&pk[m]);
+      const int r = 2 * (prp + NRP * (m / 2)) + (m % 2);
+      *reinterpret_cast<u32x4*>(Qs + r * LDQ + pcv * PE) = pq[m];
+      *reinterpret_cast<u32x4*>(Ks + r * LDQ + pcv * PE) = pk[m];
+    }
+    if constexpr (kKt) {
+      // K^T[j][r] = K[r][j], swizzled; for bf16 rows r, r + 1 go as one dword
 #pragma unroll
-        for (int j = 0; j < PE; ++j) Kt[(cv * PE + j) * LDT + r] = e[j];
+      for (int m = 0; m < NVQ; m += 2) {
+        const int r = 2 * (prp + NRP * (m / 2));
+#pragma unroll
+        for (int j = 0; j < PE; ++j) {
+          const int row = pcv * PE + j;
+          const int sw = tswz<T>(row);
+          if constexpr (kSplit) {
+            *reinterpret_cast<uint32_t*>(Kt + row * LDT + (r ^ sw)) =
+                pack_halves(pk[m][j / 2], pk[m + 1][j / 2], j % 2);
+          } else {
+            reinterpret_cast<uint32_t*>(Kt)[row * LDT + (r ^ sw)] = pk[m][j];
+            reinterpret_cast<uint32_t*>(Kt)[row * LDT + ((r + 1) ^ sw)] = pk[m + 1][j];
+          }
+        }
       }
     }
-    if (tid < C * VVR) {
-      const int r = tid / VVR, h = tid % VVR;
-      const T* e = reinterpret_cast<const T*>(&pv);
-#pragma unroll
-      for (int j = 0; j < PE; ++j) Vt[(h * PE + j) * LDT + r] = e[j];
-    }
     if (wave == 0) {
+      // V^T[j][r] = V[r][col0 + j]
+      if constexpr (kSplit) {
+        const int r = 2 * (lane / 2), h = lane % 2;
+#pragma unroll
+        for (int j = 0; j < PE; ++j)
+          *reinterpret_cast<uint32_t*>(Vt + (h * PE + j) * LDT + r) =
+              pack_halves(pv[0][j / 2], pv[1][j / 2], j % 2);
+      } else {
+#pragma unroll
+        for (int m = 0; m < NVV; ++m)
+#pragma unroll
+          for (int j = 0; j < PE; ++j)
+            reinterpret_cast<uint32_t*>(Vt)[((lane % VVR) * PE + j) * LDT + vrow(m)] = pv[m][j];
+      }
       if constexpr (kGated) gs[lane] = wave_inclusive_scan(pla);
       else gs[lane] = 0.f;
       bs[lane] = pb;
@@ -277,136 +567,99 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
     __syncthreads();
 
     // ---------------- scores: lower tiles of Q K^T (-> Aq) and K K^T (-> As)
-    {
-      constexpr int kJobs = kDelta ? 20 : 10;
-      for (int job = wave; job < kJobs; job += kWaves) {
-        int ti, tj;
-        tri_tile(job % 10, ti, tj);
-        const T* X = job < 10 ? Qs : Ks;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          mma(frag_row(X + (16 * LDQ) * ti + nq + 32 * kb, g),
-              frag_row(Ks + (16 * LDQ) * tj + nq + 32 * kb, g), acc);
-        const int cc = 16 * tj + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * ti + 4 * g + i;
-          float decay = 1.f;
-          if constexpr (kGated) decay = __expf(r >= cc ? gs[r] - gs[cc] : 0.f);
-          if (job < 10) {
-            const float x = r >= cc ? acc[i] * decay : 0.f;
-            const T h = from_f32<T>(x);
-            Aq[r * LDT + cc] = h;
-            if constexpr (kSplit) Aq[C * LDT + r * LDT + cc] = from_f32<T>(x - to_f32(h));
-          } else {
-            As[r * LDF + cc] = r > cc ? bs[r] * acc[i] * decay : 0.f;
-          }
-        }
-      }
-      // The output reads Aq in 32-column blocks: the upper tiles (0, 1) and
-      // (2, 3) that share such a block with a lower tile must be zero.
-      if (wave == kWaves - 1) {
-#pragma unroll
-        for (int p = 0; p < kPlanes; ++p)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            Aq[p * C * LDT + r * LDT + 16 + n] = from_f32<T>(0.f);
-            Aq[p * C * LDT + (32 + r) * LDT + 48 + n] = from_f32<T>(0.f);
-          }
-      }
+    // wave 0: Q rows 0, 3; wave 1: Q rows 1, 2; wave 2: K rows 0, 3;
+    // wave 3: K rows 1, 2 -- five 16 x 16 tiles each.  Linear mode has no
+    // K K^T: waves 2 and 3 idle here.
+    if (wave == 0) {
+      score_rows<T, D, kGated, true, 0, 3, LDQ, LDT, LDF>(Qs, Ks, gs, bs, Aq, As, g, n, nq);
+    } else if (wave == 1) {
+      score_rows<T, D, kGated, true, 1, 2, LDQ, LDT, LDF>(Qs, Ks, gs, bs, Aq, As, g, n, nq);
+    } else if constexpr (kDelta) {
+      if (wave == 2)
+        score_rows<T, D, kGated, false, 0, 3, LDQ, LDT, LDF>(Ks, Ks, gs, bs, Aq, As, g, n, nq);
+      else
+        score_rows<T, D, kGated, false, 1, 2, LDQ, LDT, LDF>(Ks, Ks, gs, bs, Aq, As, g, n, nq);
     }
     __syncthreads();
 
     if constexpr (kDelta) {
       // ---------------- T = (I + A)^{-1}: diagonal blocks (wave 0)
-      // Lane (g, n) solves column n of diagonal block g:
-      //   x_r = [r == n] - sum_{i < r} A[16g + r][16g + i] x_i.
-      if (wave == 0) {
-        float x[16];
-        const float* Ab = As + (16 * g) * LDF + 16 * g;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = r == n ? 1.f : 0.f;
-#pragma unroll
-          for (int i4 = 0; i4 < r; i4 += 4) {
-            const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ab + r * LDF + i4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (i4 + j < r) s = fmaf(-a4[j], x[i4 + j], s);
-          }
-          x[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          Tf[(16 * g + r) * LDF + 16 * g + n] = x[r];
-          if constexpr (kSplit) Tb[(16 * g + r) * LDT + 16 * g + n] = from_f32<T>(x[r]);
-        }
-      }
+      if (wave == 0) tdiag_solve<T, LDF, LDT>(As, Tf, Tb, g, n);
       __syncthreads();
-
       // ---------------- T: blocks below the diagonal, column block j = wave
       //   T_ij = -T_ii (sum_{k=j}^{i-1} A_ik T_kj),  i = j+1 .. 3
-      if (wave < 3) {
-        if (wave == 0) tcol_solve<T, 0, LDF, LDT>(As, Tf, Tb, g, n);
-        else if (wave == 1) tcol_solve<T, 1, LDF, LDT>(As, Tf, Tb, g, n);
-        else tcol_solve<T, 2, LDF, LDT>(As, Tf, Tb, g, n);
-      } else {
-        // Zero the upper blocks (0, 1) and (2, 3) of T that U_new = T R
-        // reads as part of a 32-column block.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          if constexpr (kSplit) {
-            Tb[r * LDT + 16 + n] = from_f32<T>(0.f);
-            Tb[(32 + r) * LDT + 48 + n] = from_f32<T>(0.f);
-          } else {
-            Tf[r * LDF + 16 + n] = 0.f;
-            Tf[(32 + r) * LDF + 48 + n] = 0.f;
-          }
-        }
-      }
+      if (wave == 0) tcol_solve<T, 0, LDF, LDT>(As, Tf, Tb, g, n);
+      else if (wave == 1) tcol_solve<T, 1, LDF, LDT>(As, Tf, Tb, g, n);
+      else if (wave == 2) tcol_solve<T, 2, LDF, LDT>(As, Tf, Tb, g, n);
       __syncthreads();
     }
 
     // ---------------- chain (wave 0) and Q S (waves 1-3)
     f32x4 qs[2];
     if (wave == 0) {
-      f32x4 un[4];
+      // operands of the whole step, loaded before the first product
+      Frag<T> ktf[NKT][2];
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (kKt) {
+            const int row = 16 * tj + n;
+            ktf[tj][kb] = frag_row_swz(Kt + row * LDT, 32 * kb, g, tswz<T>(row));
+          } else {
+            ktf[tj][kb] = frag_col(Ks + 32 * kb * LDQ + 16 * tj + n, LDQ, g);
+          }
+        }
       if constexpr (kDelta) {
+        Frag<T> kf[4][NKB], tf[4][2];
+        f32x4 vv[4], bb[4], gg[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            kf[ti][kb] = frag_row(Ks + 16 * LDQ * ti + nq + 32 * kb, g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= ti / 2) tf[ti][kb] = frag_row(Top + (16 * LDTop) * ti + n * LDTop + 32 * kb, g);
+          const int r0 = 16 * ti + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[ti][i] = to_f32(Vt[nt + r0 + i]);
+          bb[ti] = *reinterpret_cast<const f32x4*>(bs + r0);
+          gg[ti] = *reinterpret_cast<const f32x4*>(gs + r0);
+        }
+        const float gC = gs[C - 1];
         Frag2<T> sf[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sf[kb] = frag2_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
         // R = diag(beta) (V - diag(gam) K S), rows 16 ti + 4 g + i
-        f32x4 rr[4];
+        f32x4 ks[4], rr[4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          f32x4 ks = zero4();
+        for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            mma_ab2(frag_row(Ks + (16 * LDQ) * ti + nq + 32 * kb, g), sf[kb], ks);
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ti + 4 * g + i;
-            const float gam = kGated ? __expf(gs[r]) : 1.f;
-            rr[ti][i] = bs[r] * (to_f32(Vt[nt + r]) - gam * ks[i]);
+            const float gam = kGated ? __expf(gg[ti][i]) : 1.f;
+            rr[ti][i] = bb[ti][i] * (vv[ti][i] - gam * ks[ti][i]);
           }
-        }
         // U_new = T R (T lower triangular: row tile ti needs blocks <= ti / 2)
         Frag2<T> rf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) rf[kb] = frag2_from_acc<T>(rr[2 * kb], rr[2 * kb + 1]);
+        f32x4 un[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           un[ti] = zero4();
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (kb == 1 && ti < 2) continue;
-            mma_ab2(frag_row(Top + (16 * LDTop) * ti + n * LDTop + 32 * kb, g), rf[kb], un[ti]);
-          }
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= ti / 2) mma_ab2(tf[ti][kb], rf[kb], un[ti]);
         }
-        // publish U_new for the output, then S' = gam_C S + K^T diag(gam_C / gam) U_new
+        // publish U_new for the output, then
+        // S' = gam_C S + K^T diag(gam_C / gam) U_new
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const Frag2<T> f = frag2_from_acc<T>(un[2 * kb], un[2 * kb + 1]);
@@ -415,14 +668,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
         }
         Frag2<T> ut[2];
         if constexpr (kGated) {
-          const float gC = gs[C - 1];
           float slo[2][4], shi[2][4];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              slo[kb][i] = __expf(gC - gs[32 * kb + 4 * g + i]);
-              shi[kb][i] = __expf(gC - gs[32 * kb + 16 + 4 * g + i]);
+              slo[kb][i] = __expf(gC - gg[2 * kb][i]);
+              shi[kb][i] = __expf(gC - gg[2 * kb + 1][i]);
             }
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
@@ -435,45 +687,25 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
           for (int kb = 0; kb < 2; ++kb) ut[kb] = frag2_from_acc<T>(un[2 * kb], un[2 * kb + 1]);
         }
 #pragma unroll
-        for (int tj = 0; tj < NKT; ++tj)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            Frag<T> kt;
-            if constexpr (kKt) kt = frag_row(Kt + (16 * LDT) * tj + nt + 32 * kb, g);
-            else kt = frag_col(Ks + 32 * kb * LDQ + 16 * tj + n, LDQ, g);
-            mma_ab2(kt, ut[kb], S[tj]);
-          }
+          for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
       } else {
         // linear: S' = S + K^T V
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const Frag<T> vf = frag_row(Vt + nt + 32 * kb, g);
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) {
-            Frag<T> kt;
-            if constexpr (kKt) kt = frag_row(Kt + (16 * LDT) * tj + nt + 32 * kb, g);
-            else kt = frag_col(Ks + 32 * kb * LDQ + 16 * tj + n, LDQ, g);
-            mma(kt, vf, S[tj]);
-          }
+          for (int tj = 0; tj < NKT; ++tj) mma(ktf[tj][kb], vf, S[tj]);
         }
       }
-    } else {
+    } else if (wave == 1) {
       // Q S for row tiles: wave 1 -> 0 and 3, wave 2 -> 1, wave 3 -> 2
-      Frag2<T> sx[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sx[kb].hi = Sx[(kPlanes * kb) * kWave + lane];
-        if constexpr (kSplit) sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ti = u == 0 ? wave - 1 : 3;
-        qs[u] = zero4();
-        if (u == 1 && wave != 1) continue;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          mma_ab2(frag_row(Qs + (16 * LDQ) * ti + nq + 32 * kb, g), sx[kb], qs[u]);
-      }
+      qs_rows<T, D, 2, 0, 3, LDQ>(Qs, Sx, qs, g, nq, lane);
+    } else if (wave == 2) {
+      qs_rows<T, D, 1, 1, 1, LDQ>(Qs, Sx, qs, g, nq, lane);
+    } else {
+      qs_rows<T, D, 1, 2, 2, LDQ>(Qs, Sx, qs, g, nq, lane);
     }
     __syncthreads();
 
@@ -486,49 +718,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
         if constexpr (kSplit) Sx[(2 * kb + 1) * kWave + lane] = f.lo;
       }
     } else {
-      Frag2<T> uf[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (kDelta) {
-          uf[kb].hi = Ux[(kPlanes * kb) * kWave + lane];
-          if constexpr (kSplit) uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
-        } else {
-          uf[kb].hi = frag_row(Vt + nt + 32 * kb, g);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u == 1 && wave != 1) continue;
-        const int ti = u == 0 ? wave - 1 : 3;
-        f32x4 o = qs[u];
-        if constexpr (kGated) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] *= __expf(gs[16 * ti + 4 * g + i]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (kb == 1 && ti < 2) continue;     // Aq is zero above the diagonal
-          Frag2<T> a;
-          a.hi = frag_row(Aq + (16 * LDT) * ti + nt + 32 * kb, g);
-          if constexpr (kSplit) a.lo = frag_row(Aq + C * LDT + (16 * LDT) * ti + nt + 32 * kb, g);
-          if constexpr (kDelta) {
-            mma_a2b2(a, uf[kb], o);
-          } else {
-            // linear: V is exact in the input type
-            if constexpr (kSplit) mma(a.lo, uf[kb].hi, o);
-            mma(a.hi, uf[kb].hi, o);
-          }
-        }
-        const size_t ob = (row0 + 16 * ti + 4 * g) * D + col;
-        if (out_bf16) {
-          __bf16* out = static_cast<__bf16*>(out_);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = (__bf16)o[i];
-        } else {
-          float* out = static_cast<float*>(out_);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = o[i];
-        }
+      const size_t ob0 = row0 * D + col;
+      if (wave == 1) {
+        out_rows<T, D, MODE, 2, 0, 3, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
+      } else if (wave == 2) {
+        out_rows<T, D, MODE, 1, 1, 1, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
+      } else {
+        out_rows<T, D, MODE, 1, 2, 2, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
       }
     }
     __syncthreads();
