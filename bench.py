@@ -31,6 +31,16 @@ METRIC = ("chunkwise gated-delta fwd tokens/s (% MFMA peak); "
           "decode state GB/s (% HBM)")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, flop/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "chunkwise_gated_delta_la_amd", "csrc")
+# Source files each kernel is built from: a traffic measurement is used
+# only while these are unchanged.
+KERNEL_SOURCES = {
+    "la_chunk": ["la_chunk.hip", "la_device.hpp", "la_kernels.hpp"],
+    "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
+}
+# rocprofv3 kernel names -> library kernel names
+KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "decode_kernel": "la_decode"}
 
 
 def log(msg):
@@ -83,6 +93,95 @@ def fwd_min_bytes_per_token_head(w):
     return (2 * w.dk + 2 * w.dv) * e + gates
 
 
+# ------------------------------------------------------------------ HBM traffic
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs recorded in profiles/traffic.json, scaled
+    by the copy-kernel calibration; None when absent or when the kernel's
+    sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or ent.get("workload") != workload or ent.get("source_hash") != source_hash(kernel):
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def calibrate_copy(mib, reps=5):
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the
+    reference kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the
+    traffic figures (it reads and writes exactly `mib` MiB per launch)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def _read_pmc(csv_dir, counter):
+    """{kernel: [per-dispatch counter value]} from rocprofv3 counter CSVs."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, command):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the
+    bench and of the copy calibration) into profiles/traffic.json."""
+    def copy_factor(d, counter):
+        vals = [v for k, vs in _read_pmc(d, counter).items() if "copy" in k.lower() for v in vs]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {d}")
+        kib = sorted(vals)[len(vals) // 2]          # median dispatch
+        return kib * 1024.0, (1 << 30)              # counted bytes, true bytes
+    cf, tf = copy_factor(cal_fetch_dir, "FETCH_SIZE")
+    cw, tw = copy_factor(cal_write_dir, "WRITE_SIZE")
+    sf, sw = tf / cf, tw / cw
+    fetch, write = _read_pmc(fetch_dir, "FETCH_SIZE"), _read_pmc(write_dir, "WRITE_SIZE")
+    kernels = {}
+    for sym, lib_name in KERNEL_SYMBOLS.items():
+        fv = [v for k, vs in fetch.items() if sym in k for v in vs]
+        wv = [v for k, vs in write.items() if sym in k for v in vs]
+        if not fv or not wv:
+            continue
+        f_b = sorted(fv)[len(fv) // 2] * 1024.0 * sf
+        w_b = sorted(wv)[len(wv) // 2] * 1024.0 * sw
+        kernels[lib_name] = {
+            "workload": workload[lib_name], "source_hash": source_hash(lib_name),
+            "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
+            "hbm_bytes_per_launch": round(f_b + w_b), "dispatches": len(fv)}
+    rec = {"calibration": {"copy_bytes": 1 << 30, "fetch_scale": sf, "write_scale": sw},
+           "command": command, "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 # ------------------------------------------------------------------ legs
 
 def bench_forward(w, steps, warmup):
@@ -129,9 +228,11 @@ def bench_forward(w, steps, warmup):
                          "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1)}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
     dk = kernels[dom]
+    traffic = measured_traffic(dom, w.name)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["achieved_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": dk["algorithmic_bytes"]}
     flops = fwd_flops_per_token_head(w) * token_heads
     min_bytes = (fwd_min_bytes_per_token_head(w) * token_heads
                  + kernel_bytes_per_head("la_chunk", w) * w.B * w.H)
@@ -188,7 +289,9 @@ def bench_decode(w, warmup=1):
         "state_GBs": round(gbs, 1),
         "roofline": {"kernel": "la_decode", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("la_decode", w.name),
+                     "algorithmic_bytes": by},
     }
 
 
@@ -220,9 +323,20 @@ def main():
     ap.add_argument("--workload", type=int, default=4,
                     help="forward workload id in workloads.WORKLOADS (default 4)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (traffic calibration)")
+    ap.add_argument("--ingest-pmc", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH",
+                                                      "CAL_WRITE", "COMMAND"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc CSV folders")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        import workloads
+        ingest_pmc(*args.ingest_pmc[:4],
+                   {"la_chunk": workloads.WORKLOADS[args.workload].name,
+                    "la_decode": workloads.WORKLOADS[5].name}, args.ingest_pmc[4])
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the forward shards over (batch, head) or over the sequence, "
@@ -235,6 +349,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     w = workloads.WORKLOADS[args.workload]
     x, fwd = bench_forward(w, args.steps, args.warmup)
     dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
