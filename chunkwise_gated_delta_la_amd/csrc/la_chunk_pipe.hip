@@ -1,0 +1,736 @@
+// Pipelined chunkwise forward for bf16 inputs: the same computation as the
+// float kernel in la_chunk.hip (see there for the formulas and their
+// sources), restructured so that the serial part -- the state carried from
+// chunk to chunk -- runs alone on one wave while the other waves prepare the
+// next chunks and finish the previous one.
+//
+// One 256-thread workgroup owns one 16-column tile of one (batch, head)
+// state.  Roles, per chunk c, in two barrier-separated segments:
+//
+//   wave 0 (chain)   A: K S, R = diag(beta)(V - diag(gam) K S),
+//                       U_new = T R, publish U_new
+//                    B: S <- gam_C S + K^T diag(gam_C / gam) U_new, publish S
+//   wave 1 (T)       A: diagonal 16 x 16 blocks of T(c+1) = (I + A)^-1
+//                    B: the blocks below the diagonal of T(c+1)
+//   waves 2, 3       A: DMA loads of chunk c+1 (Q, V) and c+2 (K, gates);
+//                       masked decayed scores and Q S of chunk c for their
+//                       row tiles, kept in registers
+//                    B: output O = diag(gam) Q S + Aqk U_new of chunk c;
+//                       A(c+2) = strict_lower(diag(beta) K K^T * Gamma)
+//
+// so T and A are ready one and two chunks ahead of the chain.  Inputs go
+// from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
+// bytes land at base + 16 l) without passing through registers; Q and K
+// tiles are stored row-major with the 16-byte units of row r XOR-permuted
+// by r, which makes both the operand-row reads and the transposed reads
+// conflict-free.  K^T and V^T operands are read transposed from the
+// row-major tiles with ds_read_b64_tr_b16 (within each 16-lane group, lane
+// i receives element i % 4 of the 4-element runs addressed by lanes
+// i / 4 + 4 j, j = 0..3), so no transposed copy is ever stored.
+//
+// The scores are computed transposed (K Q^T tiles): the accumulator layout
+// of K Q^T is exactly the A-operand layout of Aqk = Q K^T * M * Gamma for
+// O += Aqk U_new, so the scores never leave registers.
+//
+// Precision as in the float kernel's bf16 path: q, k, v exact, float
+// operands split into bf16 hi + lo, T a single bf16, float accumulation and
+// state.
+#include "la_device.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+namespace {
+
+constexpr int C = 64;
+constexpr int kThreads = 256;
+constexpr int LDT = C + 8;        // row pitch of the bf16 T tile
+constexpr int LDB = 20;           // row pitch of a float 16 x 16 block
+typedef __bf16 T16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---------------------------------------------------------------- LDS access
+
+// Element offset of (r, c) in a C x D bf16 tile whose 16-byte units are
+// permuted by XOR with (r mod D / 8).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int U = D / 8;
+  return r * D + ((((c >> 3) ^ (r & (U - 1)))) << 3) + (c & 7);
+}
+
+// Operand row R of the swizzled tile over columns c0 + kidx(g, j).
+template <int D>
+__device__ __forceinline__ Frag<T16> frag_row_sw(const T16* tile, int R, int c0, int g) {
+  Frag<T16> f;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(tile + swz<D>(R, c0 + 4 * g));
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(tile + swz<D>(R, c0 + 16 + 4 * g));
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+__device__ __forceinline__ bf16x4 read_tr(const T16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Transposed operand from the swizzled row-major tile: 8 values
+// tile[r0 + kidx(g, j)][c0 + n] for lane (g, n), i.e. column c0 + n of the
+// tile as an operand over the rows r0 .. r0 + 31.  Lane k of group g
+// addresses row r0 + 4 g + k / 4 (+ 16), columns c0 + 4 (k % 4) .. + 3.
+template <int D>
+__device__ __forceinline__ Frag<T16> frag_col_tr(const T16* tile, int r0, int c0, int g, int n) {
+  Frag<T16> f;
+  const int c = c0 + 4 * (n & 3);
+  const bf16x4 a = read_tr(tile + swz<D>(r0 + 4 * g + (n >> 2), c));
+  const bf16x4 b = read_tr(tile + swz<D>(r0 + 16 + 4 * g + (n >> 2), c));
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// The same over a plain C x 16 bf16 tile (this workgroup's V columns).
+__device__ __forceinline__ Frag<T16> frag_col_tr_v(const T16* tile, int r0, int g, int n) {
+  Frag<T16> f;
+  const int c = 4 * (n & 3);
+  const bf16x4 a = read_tr(tile + (r0 + 4 * g + (n >> 2)) * 16 + c);
+  const bf16x4 b = read_tr(tile + (r0 + 16 + 4 * g + (n >> 2)) * 16 + c);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// V in accumulator layout for rows 16 ti + 4 g + i, column n.
+__device__ __forceinline__ f32x4 v_acc(const T16* tile, int ti, int g, int n) {
+  const bf16x4 a = read_tr(tile + (16 * ti + 4 * g + (n >> 2)) * 16 + 4 * (n & 3));
+  return f32x4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
+}
+
+// A 16 x 16 float block (row pitch LDB) as a 16-deep split operand row:
+// p[4 g + j] in slots j < 4, zero above.
+__device__ __forceinline__ Frag2<T16> frag2_blk16(const float* p, int g) {
+  Frag2<T16> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, a[i]);
+    f.set(4 + i, 0.f);
+  }
+  return f;
+}
+
+// Two side-by-side 16 x 16 float blocks as one 32-deep split operand row.
+__device__ __forceinline__ Frag2<T16> frag2_blk32(const float* p0, const float* p1, int g) {
+  Frag2<T16> f;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p0 + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p1 + 4 * g);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.set(i, a[i]);
+    f.set(4 + i, b[i]);
+  }
+  return f;
+}
+
+// Index of the lower 16 x 16 block (i, j), i >= j, in the compact A store.
+__device__ __forceinline__ constexpr int bid(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// ---------------------------------------------------------------- DMA loads
+//
+// global_load_lds moves `size` bytes per lane from global memory straight
+// into LDS at M0 + lane * size.  It is issued through inline assembly so
+// that the compiler does not track it: the loading waves wait for it
+// explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes the
+// data.  Otherwise the compiler, unable to tell the ring slots apart, would
+// wait for the transfer before every later LDS read of the issuing wave.
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// DMA of one C x D tile into the swizzled layout: instructions m = part,
+// part + 2, ... (the two loading waves take alternate ones); each moves
+// 1 KiB = 512 elements.
+template <int D>
+__device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int part, int lane) {
+  constexpr int RB = 2 * D;                     // bytes per row
+  constexpr int NI = C * RB / 1024;             // instructions per tile
+  const uint32_t base = lds_addr(dst);
+#pragma unroll
+  for (int i = 0; i < NI / 2; ++i) {
+    const int m = part + 2 * i;
+    const int byte = 1024 * m + 16 * lane;
+    const int r = byte / RB, ul = (byte % RB) / 16;
+    const int ug = ul ^ (r & (D / 8 - 1));
+    dma16(src_rows + r * D + ug * 8, __builtin_amdgcn_readfirstlane(base + 1024 * m));
+  }
+}
+
+// ---------------------------------------------------------------- roles
+
+// Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
+// registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
+// Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
+// (Q S)[16 ti + 4 g + e][n].
+template <int D, bool GATED, int NTI, int TI0, int TI1>
+__device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
+                                          const Frag<T16>* Sx, f32x4 (&sc)[2][4],
+                                          f32x4 (&qs)[2], int g, int n, int lane) {
+  constexpr int NKB = D / 32;
+  constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
+  Frag<T16> qf[NTI][NKB], kf[NT][NKB];
+  Frag2<T16> sx[NKB];
+#pragma unroll
+  for (int u = 0; u < NTI; ++u)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_sw<D>(Qt, 16 * (u ? TI1 : TI0) + n, 32 * kb, g);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    sx[kb].hi = Sx[(2 * kb) * kWave + lane];
+    sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
+  }
+  float gq[NTI];
+  f32x4 gk[NT];
+  if constexpr (GATED) {
+#pragma unroll
+    for (int u = 0; u < NTI; ++u) gq[u] = gsc[16 * (u ? TI1 : TI0) + n];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gsc + 16 * t + 4 * g);
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u ? TI1 : TI0;
+    qs[u] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[u][kb], sx[kb], qs[u]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[u][t] = zero4();
+      if (t > ti) continue;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[u][kb], sc[u][t]);
+      // element (K row 16 t + 4 g + e, Q row 16 ti + n) = Aqk[r][cc]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = t < ti || 4 * g + e <= n;
+        float decay = 1.f;
+        if constexpr (GATED) decay = __expf(keep ? gq[u] - gk[t][e] : 0.f);
+        sc[u][t][e] = keep ? sc[u][t][e] * decay : 0.f;
+      }
+    }
+  }
+}
+
+// Output of chunk c for the row tiles of scores_qs.
+template <int D, int MODE, int NTI, int TI0, int TI1>
+__device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
+                                         const Frag<T16>* Ux, const T16* Vt, const float* gsc,
+                                         void* out_, size_t ob0, int out_bf16, int g, int n,
+                                         int lane) {
+  constexpr bool kDelta = MODE != kModeLinear;
+  constexpr bool kGated = MODE == kModeGatedDelta;
+  Frag2<T16> uf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if constexpr (kDelta) {
+      uf[kb].hi = Ux[(2 * kb) * kWave + lane];
+      uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
+    } else {
+      uf[kb].hi = frag_col_tr_v(Vt, 32 * kb, g, n);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u ? TI1 : TI0;
+    f32x4 o = qs[u];
+    if constexpr (kGated) {
+      const f32x4 gr = *reinterpret_cast<const f32x4*>(gsc + 16 * ti + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= __expf(gr[e]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb > ti) continue;
+      const Frag2<T16> a = frag2_from_acc<T16>(sc[u][2 * kb], sc[u][2 * kb + 1]);
+      if constexpr (kDelta) {
+        mma_a2b2(a, uf[kb], o);
+      } else {
+        mma(a.lo, uf[kb].hi, o);
+        mma(a.hi, uf[kb].hi, o);
+      }
+    }
+    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
+    if (out_bf16) {
+      T16* out = static_cast<T16*>(out_);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[e];
+    } else {
+      float* out = static_cast<float*>(out_);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[e];
+    }
+  }
+}
+
+// A = strict_lower(diag(beta) K K^T * Gamma) for row tiles R0, R1 into the
+// compact block store (block (i, j) at Ab + bid(i, j) * 16 * LDB).
+template <int D, bool GATED, int R0, int R1>
+__device__ __forceinline__ void kkt_rows(const T16* Kt, const float* gsc, const float* bsc,
+                                         float* Ab, int g, int n) {
+  constexpr int NKB = D / 32;
+  constexpr int NT = (R0 > R1 ? R0 : R1) + 1;
+  Frag<T16> kf[NT][NKB];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
+  f32x4 br[2], gr[2];
+  float gc[NT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int R = u ? R1 : R0;
+    br[u] = *reinterpret_cast<const f32x4*>(bsc + 16 * R + 4 * g);
+    if constexpr (GATED) gr[u] = *reinterpret_cast<const f32x4*>(gsc + 16 * R + 4 * g);
+  }
+  if constexpr (GATED) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) gc[t] = gsc[16 * t + n];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int R = u ? R1 : R0;
+#pragma unroll
+    for (int t = 0; t <= R; ++t) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma(kf[R][kb], kf[t][kb], acc);
+      float* blk = Ab + bid(R, t) * 16 * LDB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = R > t || 4 * g + e > n;
+        float decay = 1.f;
+        if constexpr (GATED) decay = __expf(keep ? gr[u][e] - gc[t] : 0.f);
+        blk[(4 * g + e) * LDB + n] = keep ? br[u][e] * acc[e] * decay : 0.f;
+      }
+    }
+  }
+}
+
+// Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
+// g by forward substitution; the block's rows are loaded first.
+__device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int g, int n) {
+  const float* A = Ab + bid(g, g) * 16 * LDB;
+  f32x4 arow[16][4];
+#pragma unroll
+  for (int r = 1; r < 16; ++r)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      if (4 * i4 < r) arow[r][i4] = *reinterpret_cast<const f32x4*>(A + r * LDB + 4 * i4);
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float s0 = r == n ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < r; ++i) {
+      const float a = arow[r][i / 4][i % 4];
+      if (i % 2 == 0) s0 = fmaf(-a, x[i], s0);
+      else s1 = fmaf(-a, x[i], s1);
+    }
+    x[r] = s0 + s1;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    Df[g * 16 * LDB + r * LDB + n] = x[r];
+    Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)x[r];
+  }
+}
+
+// Blocks of T below the diagonal from the diagonal blocks D_i (Df) and A:
+//   T10 = -D1 A10 D0,  T32 = -D3 A32 D2,
+//   [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
+// (block inverse of a 2 x 2 block lower-triangular matrix, applied twice),
+// four dependent product steps.  Products split both operands.
+__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, T16* Tb,
+                                      int g, int n) {
+  auto blkA = [&](int i, int j) { return Ab + bid(i, j) * 16 * LDB; };
+  auto blkD = [&](int i) { return Df + i * 16 * LDB; };
+  auto dacc = [&](int i) {     // D_i in accumulator layout
+    f32x4 d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = blkD(i)[(4 * g + e) * LDB + n];
+    return d;
+  };
+  const f32x4 D0 = dacc(0), D1 = dacc(1), D2 = dacc(2);
+  // level 1
+  f32x4 x10 = zero4(), x32 = zero4(), t10 = zero4(), t32 = zero4();
+  mma_a2b2(frag2_blk16(blkA(1, 0) + n * LDB, g), frag2_from_acc<T16>(D0, zero4()), x10);
+  mma_a2b2(frag2_blk16(blkA(3, 2) + n * LDB, g), frag2_from_acc<T16>(D2, zero4()), x32);
+  mma_a2b2(frag2_blk16(blkD(1) + n * LDB, g), frag2_from_acc<T16>(x10, zero4()), t10);
+  mma_a2b2(frag2_blk16(blkD(3) + n * LDB, g), frag2_from_acc<T16>(x32, zero4()), t32);
+  t10 = -t10;
+  t32 = -t32;
+  // T32 rows are needed as an A operand: through LDS (this wave only)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) T32f[(4 * g + e) * LDB + n] = t32[e];
+  // level 2: X = [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
+  f32x4 x00 = zero4(), x10b = zero4(), x01 = zero4(), x11 = zero4();
+  {
+    const Frag2<T16> b0 = frag2_from_acc<T16>(D0, t10);
+    const Frag2<T16> b1 = frag2_from_acc<T16>(D1, zero4());
+    mma_a2b2(frag2_blk32(blkA(2, 0) + n * LDB, blkA(2, 1) + n * LDB, g), b0, x00);
+    mma_a2b2(frag2_blk32(blkA(3, 0) + n * LDB, blkA(3, 1) + n * LDB, g), b0, x10b);
+    mma_a2b2(frag2_blk16(blkA(2, 1) + n * LDB, g), b1, x01);
+    mma_a2b2(frag2_blk16(blkA(3, 1) + n * LDB, g), b1, x11);
+  }
+  // Y = -[[D2, 0], [T32, D3]] X
+  f32x4 y00 = zero4(), y01 = zero4(), y10 = zero4(), y11 = zero4();
+  {
+    const Frag2<T16> d2 = frag2_blk16(blkD(2) + n * LDB, g);
+    mma_a2b2(d2, frag2_from_acc<T16>(x00, zero4()), y00);
+    mma_a2b2(d2, frag2_from_acc<T16>(x01, zero4()), y01);
+    const Frag2<T16> td = frag2_blk32(T32f + n * LDB, blkD(3) + n * LDB, g);
+    mma_a2b2(td, frag2_from_acc<T16>(x00, x10b), y10);
+    mma_a2b2(td, frag2_from_acc<T16>(x01, x11), y11);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g + e;
+    Tb[(16 + r) * LDT + n] = (T16)t10[e];
+    Tb[(48 + r) * LDT + 32 + n] = (T16)t32[e];
+    Tb[(32 + r) * LDT + n] = (T16)(-y00[e]);
+    Tb[(32 + r) * LDT + 16 + n] = (T16)(-y01[e]);
+    Tb[(48 + r) * LDT + n] = (T16)(-y10[e]);
+    Tb[(48 + r) * LDT + 16 + n] = (T16)(-y11[e]);
+  }
+}
+
+// In-chunk cumulative log-decay of the 64 values at p, one per lane.
+__device__ __forceinline__ float cumsum64(const float* p, int lane) {
+  return wave_inclusive_scan(p[lane]);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
+    const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const float* __restrict__ S0, void* __restrict__ out_, float* __restrict__ S_final,
+    int L, int BH, int out_bf16) {
+  constexpr bool kDelta = MODE != kModeLinear;
+  constexpr bool kGated = MODE == kModeGatedDelta;
+  constexpr int NKT = D / 16;                    // 16-row tiles of the state
+  constexpr int NKB = D / 32;                    // 32-deep blocks over dk
+  constexpr int NCT = D / 16;                    // column tiles per head
+  constexpr int TILE = C * D;                    // elements of a Q / K tile
+
+  __shared__ __attribute__((aligned(16))) T16 Qs[2][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Vs[2][C * 16];
+  __shared__ __attribute__((aligned(16))) float Ls[3][C];     // log alpha
+  __shared__ __attribute__((aligned(16))) float Bs[3][C];     // beta
+  __shared__ __attribute__((aligned(16))) float Gs[3][C];     // in-chunk cumsum
+  __shared__ __attribute__((aligned(16))) float Ab[kDelta ? 2 : 1][kDelta ? 10 * 16 * LDB : 4];
+  __shared__ __attribute__((aligned(16))) float Df[kDelta ? 4 * 16 * LDB : 4];
+  __shared__ __attribute__((aligned(16))) float T32f[kDelta ? 16 * LDB : 4];
+  __shared__ __attribute__((aligned(16))) T16 Tb[kDelta ? 2 : 1][kDelta ? C * LDT : 8];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2 * NKB * kWave];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Ux[4 * kWave];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int g = lane / 16;
+  const int n = lane % 16;
+
+  int bh, ct;
+  {
+    const int b = blockIdx.x;
+    if (BH % 8 == 0) {
+      const int x = b % 8, s = b / 8;
+      ct = s % NCT;
+      bh = (s / NCT) * 8 + x;
+    } else {
+      bh = b / NCT;
+      ct = b % NCT;
+    }
+  }
+  const int col0 = ct * 16;
+  const int col = col0 + n;
+  const size_t hbase = (size_t)bh * L;
+  const int NC = L / C;
+
+  // DMA issue for one chunk's pieces (waves 2 and 3 split the instructions)
+  const int dw = wave - 2;                       // 0 or 1 on the loading waves
+  auto load_qv = [&](int c) {                    // Q and this tile's V columns
+    const size_t row0 = hbase + (size_t)c * C;
+    dma_tile<D>(Qs[c % 2], q + row0 * D, dw, lane);
+    const int r = 32 * dw + lane / 2;
+    dma16(v + (row0 + r) * D + col0 + 8 * (lane % 2),
+          __builtin_amdgcn_readfirstlane(lds_addr(Vs[c % 2]) + 1024 * dw));
+  };
+  auto load_kg = [&](int c) {                    // K and the gates
+    const size_t row0 = hbase + (size_t)c * C;
+    dma_tile<D>(Ks[c % 3], k + row0 * D, dw, lane);
+    if (dw == 0) {
+      if constexpr (kGated) dma4(log_alpha + row0 + lane, lds_addr(Ls[c % 3]));
+    } else {
+      if constexpr (kDelta) dma4(beta + row0 + lane, lds_addr(Bs[c % 3]));
+    }
+  };
+
+  // ---- prologue
+  f32x4 S[NKT];
+  const size_t sbase = (size_t)bh * D * D;
+  if (wave == 0) {
+    if (S0) {
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[tj][i] = S0[sbase + (size_t)(16 * tj + 4 * g + i) * D + col];
+    } else {
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj) S[tj] = zero4();
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag2<T16> f = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+      Sx[(2 * kb) * kWave + lane] = f.hi;
+      Sx[(2 * kb + 1) * kWave + lane] = f.lo;
+    }
+  } else if (wave == 1) {
+    if constexpr (kDelta) {
+      // upper blocks (0, 1) and (2, 3) of both T slots stay zero
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Tb[s][(4 * g + e) * LDT + 16 + n] = (T16)0.f;
+          Tb[s][(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
+        }
+    }
+  } else {
+    load_qv(0);
+    load_kg(0);
+    if (NC > 1) load_kg(1);
+    dma_wait();
+  }
+  __syncthreads();
+  if (wave >= 2) {
+    // g of chunks 0 and 1; A of chunks 0 and 1
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s == 1 && NC < 2) break;
+      if constexpr (kGated) Gs[s][lane] = cumsum64(Ls[s], lane);
+      else Gs[s][lane] = 0.f;
+    }
+  }
+  __syncthreads();
+  if constexpr (kDelta) {
+    if (wave >= 2) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s == 1 && NC < 2) break;
+        if (wave == 2) kkt_rows<D, kGated, 0, 3>(Ks[s], Gs[s], Bs[s], Ab[s], g, n);
+        else kkt_rows<D, kGated, 1, 2>(Ks[s], Gs[s], Bs[s], Ab[s], g, n);
+      }
+    }
+    __syncthreads();
+    if (wave == 1) t_diag(Ab[0], Df, Tb[0], g, n);
+    __syncthreads();
+    if (wave == 1) t_col(Ab[0], Df, T32f, Tb[0], g, n);
+    __syncthreads();
+  }
+
+  // ---- chunk loop
+  f32x4 un[4];                 // wave 0: U_new of the current chunk
+  f32x4 sc[2][4], qs[2];       // waves 2, 3: scores and Q S of the current chunk
+  for (int c = 0; c < NC; ++c) {
+    const size_t row0 = hbase + (size_t)c * C;
+    const T16* Kc = Ks[c % 3];
+    const float* gc = Gs[c % 3];
+    const float* bc = Bs[c % 3];
+
+    // ================= segment A
+    if (wave == 0) {
+      if constexpr (kDelta) {
+        Frag<T16> kf[4][NKB], tf[4][2];
+        f32x4 vv[4], bb[4], gg[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kf[ti][kb] = frag_row_sw<D>(Kc, 16 * ti + n, 32 * kb, g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= ti / 2) tf[ti][kb] = frag_row(Tb[c % 2] + (16 * ti + n) * LDT + 32 * kb, g);
+          vv[ti] = v_acc(Vs[c % 2], ti, g, n);
+          bb[ti] = *reinterpret_cast<const f32x4*>(bc + 16 * ti + 4 * g);
+          if constexpr (kGated) gg[ti] = *reinterpret_cast<const f32x4*>(gc + 16 * ti + 4 * g);
+        }
+        Frag2<T16> sf[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+        f32x4 ks[4], rr[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gam = kGated ? __expf(gg[ti][i]) : 1.f;
+            rr[ti][i] = bb[ti][i] * (vv[ti][i] - gam * ks[ti][i]);
+          }
+        Frag2<T16> rf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) rf[kb] = frag2_from_acc<T16>(rr[2 * kb], rr[2 * kb + 1]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          un[ti] = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= ti / 2) mma_ab2(tf[ti][kb], rf[kb], un[ti]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag2<T16> f = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
+          Ux[(2 * kb) * kWave + lane] = f.hi;
+          Ux[(2 * kb + 1) * kWave + lane] = f.lo;
+        }
+      }
+    } else if (wave == 1) {
+      if constexpr (kDelta) {
+        if (c + 1 < NC) t_diag(Ab[(c + 1) % 2], Df, Tb[(c + 1) % 2], g, n);
+      }
+    } else {
+      if (c + 1 < NC) load_qv(c + 1);
+      if (c + 2 < NC) load_kg(c + 2);
+      if (wave == 2)
+        scores_qs<D, kGated, 2, 0, 3>(Qs[c % 2], Kc, gc, Sx, sc, qs, g, n, lane);
+      else
+        scores_qs<D, kGated, 2, 1, 2>(Qs[c % 2], Kc, gc, Sx, sc, qs, g, n, lane);
+      dma_wait();
+    }
+    __syncthreads();
+
+    // ================= segment B
+    if (wave == 0) {
+      Frag<T16> ktf[NKT][2];
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ktf[tj][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n);
+      if constexpr (kDelta) {
+        Frag2<T16> ut[2];
+        if constexpr (kGated) {
+          const float gC = gc[C - 1];
+          float slo[2][4], shi[2][4];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              slo[kb][i] = __expf(gC - gc[32 * kb + 4 * g + i]);
+              shi[kb][i] = __expf(gC - gc[32 * kb + 16 + 4 * g + i]);
+            }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo[kb], shi[kb]);
+          const float decC = __expf(gC);
+#pragma unroll
+          for (int tj = 0; tj < NKT; ++tj) S[tj] *= decC;
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag<T16> vf = frag_col_tr_v(Vs[c % 2], 32 * kb, g, n);
+#pragma unroll
+          for (int tj = 0; tj < NKT; ++tj) mma(ktf[tj][kb], vf, S[tj]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const Frag2<T16> f = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+        Sx[(2 * kb) * kWave + lane] = f.hi;
+        Sx[(2 * kb + 1) * kWave + lane] = f.lo;
+      }
+    } else if (wave == 1) {
+      if constexpr (kDelta) {
+        if (c + 1 < NC) t_col(Ab[(c + 1) % 2], Df, T32f, Tb[(c + 1) % 2], g, n);
+      }
+    } else {
+      const size_t ob0 = row0 * D + col;
+      if (wave == 2)
+        out_rows<D, MODE, 2, 0, 3>(sc, qs, Ux, Vs[c % 2], gc, out_, ob0, out_bf16, g, n, lane);
+      else
+        out_rows<D, MODE, 2, 1, 2>(sc, qs, Ux, Vs[c % 2], gc, out_, ob0, out_bf16, g, n, lane);
+      if (c + 2 < NC) {
+        const int s = (c + 2) % 3;
+        if constexpr (kGated) Gs[s][lane] = cumsum64(Ls[s], lane);
+        else Gs[s][lane] = 0.f;
+        if constexpr (kDelta) {
+          if (wave == 2) kkt_rows<D, kGated, 0, 3>(Ks[s], Gs[s], Bs[s], Ab[(c + 2) % 2], g, n);
+          else kkt_rows<D, kGated, 1, 2>(Ks[s], Gs[s], Bs[s], Ab[(c + 2) % 2], g, n);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wave == 0 && S_final) {
+#pragma unroll
+    for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+  }
+}
+
+template <int D, int MODE>
+hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
+  chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
+      static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
+      a.log_alpha, a.beta, a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
+  switch (a.mode) {
+    case kModeLinear: return launch_one<D, kModeLinear>(a, st);
+    case kModeDelta: return launch_one<D, kModeDelta>(a, st);
+    default: return launch_one<D, kModeGatedDelta>(a, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace la

@@ -37,6 +37,8 @@ struct ChunkArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);       // dispatcher
+hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st);   // la_chunk.hip
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st);  // la_chunk_pipe.hip (bf16)
 
 }  // namespace la
