@@ -36,11 +36,15 @@ CSRC = os.path.join(ROOT, "chunkwise_gated_delta_la_amd", "csrc")
 # Source files each kernel is built from: a traffic measurement is used
 # only while these are unchanged.
 KERNEL_SOURCES = {
-    "la_chunk": ["la_chunk.hip", "la_device.hpp", "la_kernels.hpp"],
+    "la_chunk": ["la_chunk.hip", "la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
+    "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
-# rocprofv3 kernel names -> library kernel names
-KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "decode_kernel": "la_decode"}
+# rocprofv3 kernel names -> library kernel names (chunk_kernel: float
+# inputs, chunk_pipe_kernel: bf16 inputs)
+KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
+                  "t_solve_kernel": "la_tsolve", "decode_kernel": "la_decode"}
+T_BYTES_PER_CHUNK = 6 * 1024   # T operand fragments of one (b, h, chunk)
 
 
 def log(msg):
@@ -51,9 +55,12 @@ def log(msg):
 # Per (token, head) of the forward, d = dk = dv, chunk C, element size e:
 #   algorithmic work of the method (dense-block chunkwise):
 #     gated/delta: 10 C d + 6 d^2 flop;  linear: 4 C d + 4 d^2
-#   la_chunk (the fused forward kernel) moves q, k, v in and o out (4 d e),
-#            plus beta (delta modes) and log_alpha (gated) at 4 B each;
-#            per (b, h): S0 in (when given) and S_final out at dk dv 4 B
+#   la_chunk (the chain kernel) moves q, k, v in and o out (4 d e), plus
+#            beta (delta modes) and log_alpha (gated) at 4 B each, plus,
+#            for bf16 inputs in the delta modes, the chunk's T factor
+#            (6 KiB per chunk: 96 B per token); per (b, h): S0 in (when
+#            given) and S_final out at dk dv 4 B
+#   la_tsolve (bf16 delta modes) reads k and the gates and writes T
 # Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,
 # o (2 dk e + 2 dv e), two float gates.
 
@@ -64,18 +71,31 @@ def fwd_flops_per_token_head(w):
     return 10 * C * d + 6 * d * d
 
 
+def t_bytes_per_token_head(w):
+    """Bytes of the T factor per (token, head): written by la_tsolve, read
+    by la_chunk (bf16 inputs in the delta modes only)."""
+    return T_BYTES_PER_CHUNK // w.C if (w.dtype == "bf16" and w.mode != "linear") else 0
+
+
 def kernel_bytes_per_token_head(name, w):
     """Algorithmic HBM bytes per (token, head) of a forward kernel: the
-    fused chunk kernel reads q, k, v and the gates the mode uses once and
-    writes o once (initial and final states are added per head)."""
-    if name != "la_chunk":
-        raise KeyError(name)
-    return fwd_min_bytes_per_token_head(w)
+    chain kernel reads q, k, v, the gates the mode uses and T once and
+    writes o once (initial and final states are added per head); the T
+    solve reads k and the gates and writes T."""
+    e = 2 if w.dtype == "bf16" else 4
+    gates = {"linear": 0, "delta": 4, "gated_delta": 8}[w.mode]
+    if name == "la_chunk":
+        return fwd_min_bytes_per_token_head(w) + t_bytes_per_token_head(w)
+    if name == "la_tsolve":
+        return w.dk * e + gates + t_bytes_per_token_head(w)
+    raise KeyError(name)
 
 
 def kernel_bytes_per_head(name, w):
     """Per-head state bytes of a forward call: S0 read (if given), S_final
-    written."""
+    written (chain kernel only)."""
+    if name == "la_tsolve":
+        return 0
     if name != "la_chunk":
         raise KeyError(name)
     return (2 if w.s0_std > 0 else 1) * w.dk * w.dv * 4
@@ -197,12 +217,15 @@ def bench_forward(w, steps, warmup):
         copies.append({k: t.cuda() for k, t in x.items()})
     out = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.torch_dtype, device="cuda")
     S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws_bytes = la.chunk_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C,
+                                        dtype=w.torch_dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def step(i):
         d = copies[i % 2]
         la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
                      d["S0"] if w.s0_std > 0 else None, mode=w.mode, C=w.C,
-                     out=out, S_final=S_final)
+                     out=out, S_final=S_final, workspace=ws)
 
     log(f"[bench] forward: {warmup} warmup steps")
     for i in range(warmup):
@@ -335,6 +358,7 @@ def main():
         import workloads
         ingest_pmc(*args.ingest_pmc[:4],
                    {"la_chunk": workloads.WORKLOADS[args.workload].name,
+                    "la_tsolve": workloads.WORKLOADS[args.workload].name,
                     "la_decode": workloads.WORKLOADS[5].name}, args.ingest_pmc[4])
         return
     if args.gpus != 1:

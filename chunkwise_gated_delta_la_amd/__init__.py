@@ -10,4 +10,5 @@ memory) and passes torch's current HIP stream.
     out = decode_step(q, k, v, log_alpha, beta, S, mode="gated_delta")  # S in place
 """
 from ._lib import LAError, LIB_PATH  # noqa: F401
-from .api import MODES, chunk_fwd, decode_step, kernel_timer, version  # noqa: F401
+from .api import (MODES, chunk_fwd, chunk_workspace_bytes, decode_step,  # noqa: F401
+                  kernel_timer, version)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblachunk.
 
 LA_OK = 0
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED",
-                4: "LA_ERR_ALIAS", 5: "LA_ERR_HIP"}
+                4: "LA_ERR_ALIAS", 5: "LA_ERR_HIP", 6: "LA_ERR_WORKSPACE"}
 
 _lock = threading.Lock()
 _lib = None
@@ -27,10 +27,12 @@ class LAError(RuntimeError):
 
 
 def _declare(lib):
-    vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.la_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
-                                 i, i, i, i, i, i, i, i, vp]
+                                 i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_chunk_fwd.restype = i
+    lib.la_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_workspace_bytes.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i

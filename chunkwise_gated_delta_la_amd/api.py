@@ -57,8 +57,20 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def chunk_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
+                          dtype=torch.bfloat16, out_dtype=None):
+    """Workspace bytes ``la_chunk_fwd`` needs for these sizes
+    (``la_chunk_workspace_bytes``)."""
+    code = _dtype_code(dtype, out_dtype or dtype)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.get().la_chunk_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
+                                                   ctypes.byref(n)))
+    return n.value
+
+
 def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta",
-              C=64, out=None, S_final=None, return_state=True, out_dtype=None):
+              C=64, out=None, S_final=None, return_state=True, out_dtype=None,
+              workspace=None):
     """Chunkwise forward (``la_chunk_fwd``).
 
     q, k ``[B, H, L, dk]``, v ``[B, H, L, dv]`` (float32 or bfloat16, on the
@@ -66,6 +78,9 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     or None.  Returns ``(out, S_final)`` (S_final None if not requested).
     ``S_final`` may be the same tensor as ``S0`` for an in-place update.
     ``out_dtype`` (default: the input dtype) may be float32 for bf16 inputs.
+    ``workspace`` is an optional uint8 device tensor of at least
+    ``chunk_workspace_bytes(...)`` bytes; without one, a buffer of that size
+    is taken from torch's allocator for the call.
     """
     m = _mode(mode)
     if q.dim() != 4 or v.dim() != 4:
@@ -90,12 +105,20 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     lib = _lib.get()
+    need = ctypes.c_size_t(0)
+    _lib.check(lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, m, code, ctypes.byref(need)))
+    if workspace is None and need.value > 0:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
         rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v),
                               _ptr(log_alpha if m == 2 else None),
                               _ptr(beta if m >= 1 else None), _ptr(S0),
                               _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
-                              code, _stream(dev))
+                              code, _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check(rc)
     return out, S_final
 

@@ -1,5 +1,5 @@
 // C-ABI host layer of liblachunk: argument validation, dispatch to the
-// gfx950 kernels, stream-ordered workspace.  See include/la.h for the
+// gfx950 kernels, caller-provided workspace.  See include/la.h for the
 // contract of every entry point.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -104,21 +104,10 @@ void prof_add(const char* name, hipEvent_t a, hipEvent_t b) {
   g_prof.push_back({name, a, b});
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* la_last_error(void) { return g_last_error.c_str(); }
-
-const char* la_version(void) { return "lachunk 0.1.0 gfx950"; }
-
-int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
-                 const float* beta, const float* S0, void* out, float* S_final, int B,
-                 int H, int L, int dk, int dv, int C, int mode, int dtype, void* stream) {
-  g_last_error.clear();
-  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+// Shape, mode and dtype checks shared by la_chunk_fwd and
+// la_chunk_workspace_bytes.
+int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int dtype) {
   if (int e = check_mode_dtype(mode, dtype)) return e;
-  if (int e = check_gates(mode, log_alpha, beta)) return e;
   if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || C <= 0)
     return fail(LA_ERR_SHAPE, "B, H, L, dk, dv and C must be positive");
   if (L % C != 0)
@@ -129,30 +118,92 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
                                         std::to_string(dk) + " dv=" + std::to_string(dv));
   if (C != 64)
     return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd supports C == 64, got " + std::to_string(C));
+  size_t n_qk;
+  if (!count({B, H, L, dk}, &n_qk) || n_qk > (SIZE_MAX >> 4))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  if ((size_t)B * H * (dv / 16) > 0x7fffffffu || (size_t)B * H * (L / C) > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "B * H * dv / 16 or B * H * L / C exceeds the launch grid");
+  return LA_OK;
+}
+
+la::ChunkArgs chunk_args(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, void* out, float* S_final, int B,
+                         int H, int L, int dk, int C, int mode, int dtype, void* workspace) {
+  return la::ChunkArgs{q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
+                       dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, workspace};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_last_error(void) { return g_last_error.c_str(); }
+
+const char* la_version(void) { return "lachunk 0.2.0 gfx950"; }
+
+int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode, int dtype,
+                             size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  *bytes = la::chunk_workspace_bytes(
+      chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, L,
+                 dk, C, mode, dtype, nullptr));
+  return LA_OK;
+}
+
+int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* S0, void* out, float* S_final, int B,
+                 int H, int L, int dk, int dv, int C, int mode, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
   size_t n_qk, n_v, n_g, n_s;
   if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
-      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s) || n_qk > (SIZE_MAX >> 3))
+      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
-  if ((size_t)B * H * (dv / 16) > 0x7fffffffu)
-    return fail(LA_ERR_SHAPE, "B * H * dv / 16 exceeds the launch grid");
+  const la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk,
+                                     C, mode, dtype, workspace);
+  const size_t need = la::chunk_workspace_bytes(a);
+  if (need > 0) {
+    if (!workspace)
+      return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
+                                        " bytes (la_chunk_workspace_bytes)");
+    if (workspace_bytes < need)
+      return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                        " bytes, this call needs " + std::to_string(need));
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
   const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
   const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
   const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
   const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
   const Range rs0(S0, n_s * 4), ro(out, n_v * osz), rsf(S_final, n_s * 4);
+  const Range rws(need > 0 ? workspace : nullptr, need);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro})
     if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
   if (rsf.overlaps(rs0) && (S0 != S_final))
     return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf})
+    if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
 
-  la::ChunkArgs a{q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
-                  dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = prof_mark(st);
-  hipError_t e = la::launch_chunk(a, st);
+  if (la::chunk_needs_tsolve(a)) {
+    const hipError_t e = la::launch_tsolve(a, st);
+    hipEvent_t e1 = prof_mark(st);
+    prof_add("la_tsolve", e0, e1);
+    if (e != hipSuccess) return fail_hip("launching the T-solve kernel", e);
+    e0 = e1;
+  }
+  const hipError_t e = la::launch_chunk(a, st);
   prof_add("la_chunk", e0, prof_mark(st));
   if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
   return LA_OK;

@@ -58,7 +58,6 @@
 // into bf16 hi + lo parts, so those products carry about 16 bits.  T itself
 // enters U_new = T R as a single bf16 (its rounding changes the result by a
 // small fraction of the tolerance).  The state is accumulated in float.
-#include <cstdlib>
 
 #include "la_device.hpp"
 #include "la_kernels.hpp"
@@ -763,22 +762,20 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st) {
-  if (a.in_bf16) return a.d == 64 ? launch_d<__bf16, 64>(a, st) : launch_d<__bf16, 128>(a, st);
   return a.d == 64 ? launch_d<float, 64>(a, st) : launch_d<float, 128>(a, st);
 }
 
-// bf16 inputs run the pipelined kernel (la_chunk_pipe.hip); float inputs,
+// bf16 inputs run the two-kernel path of la_chunk_pipe.hip; float inputs,
 // which have no transposed LDS reads, run the phase-sequential kernel
-// above.  LA_CHUNK_KERNEL=seq selects the sequential kernel for bf16 too.
+// above.
+bool chunk_needs_tsolve(const ChunkArgs& a) { return a.in_bf16 && a.mode != kModeLinear; }
+
+size_t chunk_workspace_bytes(const ChunkArgs& a) {
+  return a.in_bf16 ? chunk_pipe_workspace_bytes(a) : 0;
+}
+
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st) {
-  if (a.in_bf16) {
-    static const bool seq = [] {
-      const char* e = std::getenv("LA_CHUNK_KERNEL");
-      return e && e[0] == 's';
-    }();
-    if (!seq) return launch_chunk_pipe(a, st);
-  }
-  return launch_chunk_seq(a, st);
+  return a.in_bf16 ? launch_chunk_pipe(a, st) : launch_chunk_seq(a, st);
 }
 
 }  // namespace la

@@ -1,36 +1,41 @@
-// Pipelined chunkwise forward for bf16 inputs: the same computation as the
-// float kernel in la_chunk.hip (see there for the formulas and their
-// sources), restructured so that the serial part -- the state carried from
-// chunk to chunk -- runs alone on one wave while the other waves prepare the
-// next chunks and finish the previous one.
+// Chunkwise forward for bf16 inputs in two kernels: the same computation as
+// the float kernel in la_chunk.hip (see there for the formulas and their
+// sources), split along what does and does not depend on the carried state.
 //
-// One 256-thread workgroup owns one 16-column tile of one (batch, head)
-// state.  Roles, per chunk c, in two barrier-separated segments:
+// 1. t_solve_kernel, parallel over every (batch, head, chunk): the chunk's
+//    A = strict_lower(diag(beta) K K^T * Gamma) and T = (I + A)^-1.  T does
+//    not depend on the state, so all chunks are solved at once, at full
+//    occupancy, and written to a workspace as the exact MFMA operand
+//    fragments the second kernel feeds to U_new = T R (6 KiB per chunk).
 //
-//   wave 0 (chain)   A: K S, R = diag(beta)(V - diag(gam) K S),
-//                       U_new = T R, publish U_new
-//                    B: S <- gam_C S + K^T diag(gam_C / gam) U_new, publish S
-//   wave 1 (T)       A: diagonal 16 x 16 blocks of T(c+1) = (I + A)^-1
-//                    B: the blocks below the diagonal of T(c+1)
-//   waves 2, 3       A: DMA loads of chunk c+1 (Q, V) and c+2 (K, gates);
-//                       masked decayed scores and Q S of chunk c for their
-//                       row tiles, kept in registers
-//                    B: output O = diag(gam) Q S + Aqk U_new of chunk c;
-//                       A(c+2) = strict_lower(diag(beta) K K^T * Gamma)
+// 2. chunk_pipe_kernel, one 256-thread workgroup per 16-column tile of one
+//    (batch, head) state, walking the chunks in order.  Per chunk c, with a
+//    single barrier at the end:
 //
-// so T and A are ready one and two chunks ahead of the chain.  Inputs go
-// from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
-// bytes land at base + 16 l) without passing through registers; Q and K
-// tiles are stored row-major with the 16-byte units of row r XOR-permuted
-// by r, which makes both the operand-row reads and the transposed reads
-// conflict-free.  K^T and V^T operands are read transposed from the
-// row-major tiles with ds_read_b64_tr_b16 (within each 16-lane group, lane
-// i receives element i % 4 of the 4-element runs addressed by lanes
-// i / 4 + 4 j, j = 0..3), so no transposed copy is ever stored.
+//      wave 0 (chain)  K S, R = diag(beta)(V - diag(gam) K S), U_new = T R
+//                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
+//                      U_new (publish S)
+//      waves 1-3       output of chunk c-1 from the U_new published at the
+//                      last barrier; masked decayed scores and diag(gam) Q S
+//                      of chunk c for their row tiles (wave 1: tiles 0 and
+//                      1, wave 2: tile 2, wave 3: tile 3), kept in
+//                      registers until the next chunk; DMA of chunk c+2
+//                      (Q, K, V, T) and of the gates of chunk c+3; the
+//                      decay tables of chunk c+1
 //
-// The scores are computed transposed (K Q^T tiles): the accumulator layout
-// of K Q^T is exactly the A-operand layout of Aqk = Q K^T * M * Gamma for
-// O += Aqk U_new, so the scores never leave registers.
+//    so the serial chain only ever waits for its own products.  Inputs go
+//    from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
+//    bytes land at base + 16 l) without passing through registers, issued
+//    two chunks ahead and waited for one chunk later.  Q and K tiles are
+//    stored row-major with the 16-byte units of row r XOR-permuted by r,
+//    which makes both the operand-row reads and the transposed reads
+//    conflict-free.  K^T and V^T operands are read transposed from the
+//    row-major tiles with ds_read_b64_tr_b16 (within each 16-lane group,
+//    lane i receives element i % 4 of the 4-element runs addressed by lanes
+//    i / 4 + 4 j, j = 0..3), so no transposed copy is ever stored.  The
+//    scores are computed transposed (K Q^T tiles): the accumulator layout of
+//    K Q^T is exactly the A-operand layout of Aqk = Q K^T * M * Gamma for
+//    O += Aqk U_new, so the scores never leave registers.
 //
 // Precision as in the float kernel's bf16 path: q, k, v exact, float
 // operands split into bf16 hi + lo, T a single bf16, float accumulation and
@@ -134,14 +139,17 @@ __device__ __forceinline__ Frag2<T16> frag2_blk32(const float* p0, const float* 
 // Index of the lower 16 x 16 block (i, j), i >= j, in the compact A store.
 __device__ __forceinline__ constexpr int bid(int i, int j) { return i * (i + 1) / 2 + j; }
 
+
 // ---------------------------------------------------------------- DMA loads
 //
 // global_load_lds moves `size` bytes per lane from global memory straight
 // into LDS at M0 + lane * size.  It is issued through inline assembly so
 // that the compiler does not track it: the loading waves wait for it
-// explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes the
-// data.  Otherwise the compiler, unable to tell the ring slots apart, would
-// wait for the transfer before every later LDS read of the issuing wave.
+// explicitly (s_waitcnt vmcnt) before the barrier that publishes the data.
+// Otherwise the compiler, unable to tell the ring slots apart, would wait
+// for the transfer before every later LDS read of the issuing wave.  Vector
+// memory loads complete in issue order, so waiting until at most N are
+// outstanding retires everything but the last N issued.
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -157,19 +165,21 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
-// DMA of one C x D tile into the swizzled layout: instructions m = part,
-// part + 2, ... (the two loading waves take alternate ones); each moves
-// 1 KiB = 512 elements.
+// DMA of one C x D tile into the swizzled layout by one wave; each
+// instruction moves 1 KiB = 512 elements.
 template <int D>
-__device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int part, int lane) {
+__device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int lane) {
   constexpr int RB = 2 * D;                     // bytes per row
   constexpr int NI = C * RB / 1024;             // instructions per tile
   const uint32_t base = lds_addr(dst);
 #pragma unroll
-  for (int i = 0; i < NI / 2; ++i) {
-    const int m = part + 2 * i;
+  for (int m = 0; m < NI; ++m) {
     const int byte = 1024 * m + 16 * lane;
     const int r = byte / RB, ul = (byte % RB) / 16;
     const int ug = ul ^ (r & (D / 8 - 1));
@@ -177,159 +187,11 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int part
   }
 }
 
-// ---------------------------------------------------------------- roles
+// ---------------------------------------------------------------- T solve
 
-// Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
-// registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
-// Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
-// (Q S)[16 ti + 4 g + e][n].
-template <int D, bool GATED, int NTI, int TI0, int TI1>
-__device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
-                                          const Frag<T16>* Sx, f32x4 (&sc)[2][4],
-                                          f32x4 (&qs)[2], int g, int n, int lane) {
-  constexpr int NKB = D / 32;
-  constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
-  Frag<T16> qf[NTI][NKB], kf[NT][NKB];
-  Frag2<T16> sx[NKB];
-#pragma unroll
-  for (int u = 0; u < NTI; ++u)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_sw<D>(Qt, 16 * (u ? TI1 : TI0) + n, 32 * kb, g);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    sx[kb].hi = Sx[(2 * kb) * kWave + lane];
-    sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
-  }
-  float gq[NTI];
-  f32x4 gk[NT];
-  if constexpr (GATED) {
-#pragma unroll
-    for (int u = 0; u < NTI; ++u) gq[u] = gsc[16 * (u ? TI1 : TI0) + n];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gsc + 16 * t + 4 * g);
-  }
-#pragma unroll
-  for (int u = 0; u < NTI; ++u) {
-    const int ti = u ? TI1 : TI0;
-    qs[u] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[u][kb], sx[kb], qs[u]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sc[u][t] = zero4();
-      if (t > ti) continue;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[u][kb], sc[u][t]);
-      // element (K row 16 t + 4 g + e, Q row 16 ti + n) = Aqk[r][cc]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = t < ti || 4 * g + e <= n;
-        float decay = 1.f;
-        if constexpr (GATED) decay = __expf(keep ? gq[u] - gk[t][e] : 0.f);
-        sc[u][t][e] = keep ? sc[u][t][e] * decay : 0.f;
-      }
-    }
-  }
-}
-
-// Output of chunk c for the row tiles of scores_qs.
-template <int D, int MODE, int NTI, int TI0, int TI1>
-__device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
-                                         const Frag<T16>* Ux, const T16* Vt, const float* gsc,
-                                         void* out_, size_t ob0, int out_bf16, int g, int n,
-                                         int lane) {
-  constexpr bool kDelta = MODE != kModeLinear;
-  constexpr bool kGated = MODE == kModeGatedDelta;
-  Frag2<T16> uf[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    if constexpr (kDelta) {
-      uf[kb].hi = Ux[(2 * kb) * kWave + lane];
-      uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
-    } else {
-      uf[kb].hi = frag_col_tr_v(Vt, 32 * kb, g, n);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NTI; ++u) {
-    const int ti = u ? TI1 : TI0;
-    f32x4 o = qs[u];
-    if constexpr (kGated) {
-      const f32x4 gr = *reinterpret_cast<const f32x4*>(gsc + 16 * ti + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] *= __expf(gr[e]);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (2 * kb > ti) continue;
-      const Frag2<T16> a = frag2_from_acc<T16>(sc[u][2 * kb], sc[u][2 * kb + 1]);
-      if constexpr (kDelta) {
-        mma_a2b2(a, uf[kb], o);
-      } else {
-        mma(a.lo, uf[kb].hi, o);
-        mma(a.hi, uf[kb].hi, o);
-      }
-    }
-    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
-    if (out_bf16) {
-      T16* out = static_cast<T16*>(out_);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[e];
-    } else {
-      float* out = static_cast<float*>(out_);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[e];
-    }
-  }
-}
-
-// A = strict_lower(diag(beta) K K^T * Gamma) for row tiles R0, R1 into the
-// compact block store (block (i, j) at Ab + bid(i, j) * 16 * LDB).
-template <int D, bool GATED, int R0, int R1>
-__device__ __forceinline__ void kkt_rows(const T16* Kt, const float* gsc, const float* bsc,
-                                         float* Ab, int g, int n) {
-  constexpr int NKB = D / 32;
-  constexpr int NT = (R0 > R1 ? R0 : R1) + 1;
-  Frag<T16> kf[NT][NKB];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
-  f32x4 br[2], gr[2];
-  float gc[NT];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int R = u ? R1 : R0;
-    br[u] = *reinterpret_cast<const f32x4*>(bsc + 16 * R + 4 * g);
-    if constexpr (GATED) gr[u] = *reinterpret_cast<const f32x4*>(gsc + 16 * R + 4 * g);
-  }
-  if constexpr (GATED) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) gc[t] = gsc[16 * t + n];
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int R = u ? R1 : R0;
-#pragma unroll
-    for (int t = 0; t <= R; ++t) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(kf[R][kb], kf[t][kb], acc);
-      float* blk = Ab + bid(R, t) * 16 * LDB;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = R > t || 4 * g + e > n;
-        float decay = 1.f;
-        if constexpr (GATED) decay = __expf(keep ? gr[u][e] - gc[t] : 0.f);
-        blk[(4 * g + e) * LDB + n] = keep ? br[u][e] * acc[e] * decay : 0.f;
-      }
-    }
-  }
-}
+// Fragment index of the T operand (row tile ti, 32-deep block kb), kb <= ti / 2.
+__device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
+constexpr int kTFrags = 6;
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
@@ -384,9 +246,10 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
   mma_a2b2(frag2_blk16(blkD(3) + n * LDB, g), frag2_from_acc<T16>(x32, zero4()), t32);
   t10 = -t10;
   t32 = -t32;
-  // T32 rows are needed as an A operand: through LDS (this wave only)
+  // T32 rows are needed as an A operand: through LDS
 #pragma unroll
   for (int e = 0; e < 4; ++e) T32f[(4 * g + e) * LDB + n] = t32[e];
+  __syncthreads();
   // level 2: X = [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
   f32x4 x00 = zero4(), x10b = zero4(), x01 = zero4(), x11 = zero4();
   {
@@ -419,36 +282,232 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
   }
 }
 
+// One wave per (batch, head, chunk) (blocks numbered chunk-fastest): T of
+// the chunk into tws[item][f][lane], f = tfi(ti, kb), the operand fragment
+// T[16 ti + n][32 kb + kidx(g, j)] of lane (g, n).
+template <int D, bool GATED>
+__global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ k,
+                                                        const float* __restrict__ log_alpha,
+                                                        const float* __restrict__ beta,
+                                                        u32x4* __restrict__ tws, int L) {
+  constexpr int NKB = D / 32;
+  __shared__ __attribute__((aligned(16))) float Ab[10 * 16 * LDB];
+  __shared__ __attribute__((aligned(16))) float Df[4 * 16 * LDB];
+  __shared__ __attribute__((aligned(16))) float T32f[16 * LDB];
+  __shared__ __attribute__((aligned(16))) T16 Tb[C * LDT];
+  __shared__ __attribute__((aligned(16))) float gsh[C];
+  __shared__ __attribute__((aligned(16))) float bsh[C];
+
+  const int lane = threadIdx.x;
+  const int g = lane / 16, n = lane % 16;
+  const int NC = L / C;
+  const size_t item = blockIdx.x;
+  const size_t bh = item / NC;
+  const size_t row0 = bh * L + (item % NC) * C;
+
+  // K rows as operands of K K^T.  Both operands are rows of K, so any
+  // assignment of the contraction index to (group, slot) works; here slot j
+  // of group g is column 32 kb + 8 g + j, one 16-byte load per fragment.
+  Frag<T16> kf[4][NKB];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      kf[t][kb].v = *reinterpret_cast<const bf16x8*>(k + (row0 + 16 * t + n) * D + 32 * kb + 8 * g);
+  const float bv = beta[row0 + lane];
+  float gv = 0.f;
+  if constexpr (GATED) gv = wave_inclusive_scan(log_alpha[row0 + lane]);
+  gsh[lane] = gv;
+  bsh[lane] = bv;
+  // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
+    Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
+  }
+  __syncthreads();
+
+  // A blocks (R, t), t <= R: element (4 g + e, n) is row 16 R + 4 g + e,
+  // column 16 t + n
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    const f32x4 br = *reinterpret_cast<const f32x4*>(bsh + 16 * R + 4 * g);
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(gsh + 16 * R + 4 * g);
+#pragma unroll
+    for (int t = 0; t <= R; ++t) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma(kf[R][kb], kf[t][kb], acc);
+      const float gc = gsh[16 * t + n];
+      float* blk = Ab + bid(R, t) * 16 * LDB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = R > t || 4 * g + e > n;
+        float decay = 1.f;
+        if constexpr (GATED) decay = __expf(keep ? gr[e] - gc : 0.f);
+        blk[(4 * g + e) * LDB + n] = keep ? br[e] * acc[e] * decay : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  t_diag(Ab, Df, Tb, g, n);
+  __syncthreads();
+  t_col(Ab, Df, T32f, Tb, g, n);
+  __syncthreads();
+  u32x4* dst = tws + item * (kTFrags * kWave);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int kb = 0; kb <= ti / 2; ++kb) {
+      const Frag<T16> f = frag_row(Tb + (16 * ti + n) * LDT + 32 * kb, g);
+      dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.v);
+    }
+}
+
+// ---------------------------------------------------------------- side roles
+
+// Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
+// registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
+// Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
+// gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].
+template <int D, bool GATED, int NTI, int TI0, int TI1>
+__device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
+                                          const float* esc, const Frag<T16>* Sx,
+                                          f32x4 (&sc)[2][4], f32x4 (&qs)[2], int g, int n,
+                                          int lane) {
+  constexpr int NKB = D / 32;
+  constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
+  Frag<T16> qf[NTI][NKB], kf[NT][NKB];
+  Frag2<T16> sx[NKB];
+#pragma unroll
+  for (int u = 0; u < NTI; ++u)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_sw<D>(Qt, 16 * (u ? TI1 : TI0) + n, 32 * kb, g);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    sx[kb].hi = Sx[(2 * kb) * kWave + lane];
+    sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
+  }
+  float gq[NTI];
+  f32x4 gk[NT], eq[NTI];
+  if constexpr (GATED) {
+#pragma unroll
+    for (int u = 0; u < NTI; ++u) {
+      gq[u] = gsc[16 * (u ? TI1 : TI0) + n];
+      eq[u] = *reinterpret_cast<const f32x4*>(esc + 16 * (u ? TI1 : TI0) + 4 * g);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gsc + 16 * t + 4 * g);
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u ? TI1 : TI0;
+    qs[u] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[u][kb], sx[kb], qs[u]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[u][t] = zero4();
+      if (t > ti) continue;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[u][kb], sc[u][t]);
+      // element (K row 16 t + 4 g + e, Q row 16 ti + n) = Aqk[r][cc]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = t < ti || 4 * g + e <= n;
+        float decay = 1.f;
+        if constexpr (GATED) decay = __expf(keep ? gq[u] - gk[t][e] : 0.f);
+        sc[u][t][e] = keep ? sc[u][t][e] * decay : 0.f;
+      }
+    }
+    if constexpr (GATED) qs[u] *= eq[u];
+  }
+}
+
+// Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
+// (U_new = V in linear mode).
+template <int D, int MODE, int NTI, int TI0, int TI1>
+__device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
+                                         const Frag<T16>* Ux, const T16* Vt, void* out_,
+                                         size_t ob0, int out_bf16, int g, int n, int lane) {
+  constexpr bool kDelta = MODE != kModeLinear;
+  Frag2<T16> uf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if constexpr (kDelta) {
+      uf[kb].hi = Ux[(2 * kb) * kWave + lane];
+      uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
+    } else {
+      uf[kb].hi = frag_col_tr_v(Vt, 32 * kb, g, n);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u ? TI1 : TI0;
+    f32x4 o = qs[u];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb > ti) continue;
+      const Frag2<T16> a = frag2_from_acc<T16>(sc[u][2 * kb], sc[u][2 * kb + 1]);
+      if constexpr (kDelta) {
+        mma_a2b2(a, uf[kb], o);
+      } else {
+        mma(a.lo, uf[kb].hi, o);
+        mma(a.hi, uf[kb].hi, o);
+      }
+    }
+    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
+    if (out_bf16) {
+      T16* out = static_cast<T16*>(out_);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[e];
+    } else {
+      float* out = static_cast<float*>(out_);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[e];
+    }
+  }
+}
+
 // In-chunk cumulative log-decay of the 64 values at p, one per lane.
 __device__ __forceinline__ float cumsum64(const float* p, int lane) {
   return wave_inclusive_scan(p[lane]);
 }
 
+// ---------------------------------------------------------------- chain kernel
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const float* __restrict__ S0, void* __restrict__ out_, float* __restrict__ S_final,
-    int L, int BH, int out_bf16) {
+    const u32x4* __restrict__ tws, const float* __restrict__ S0, void* __restrict__ out_,
+    float* __restrict__ S_final, int L, int BH, int out_bf16) {
   constexpr bool kDelta = MODE != kModeLinear;
   constexpr bool kGated = MODE == kModeGatedDelta;
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
   constexpr int NCT = D / 16;                    // column tiles per head
   constexpr int TILE = C * D;                    // elements of a Q / K tile
+  constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
+  // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha
+  constexpr int NDMA3 = 2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0);
 
-  __shared__ __attribute__((aligned(16))) T16 Qs[2][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Qs[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
-  __shared__ __attribute__((aligned(16))) T16 Vs[2][C * 16];
-  __shared__ __attribute__((aligned(16))) float Ls[3][C];     // log alpha
-  __shared__ __attribute__((aligned(16))) float Bs[3][C];     // beta
-  __shared__ __attribute__((aligned(16))) float Gs[3][C];     // in-chunk cumsum
-  __shared__ __attribute__((aligned(16))) float Ab[kDelta ? 2 : 1][kDelta ? 10 * 16 * LDB : 4];
-  __shared__ __attribute__((aligned(16))) float Df[kDelta ? 4 * 16 * LDB : 4];
-  __shared__ __attribute__((aligned(16))) float T32f[kDelta ? 16 * LDB : 4];
-  __shared__ __attribute__((aligned(16))) T16 Tb[kDelta ? 2 : 1][kDelta ? C * LDT : 8];
-  __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2 * NKB * kWave];
-  __shared__ __attribute__((aligned(16))) Frag<T16> Ux[4 * kWave];
+  __shared__ __attribute__((aligned(16))) T16 Vs[4][C * 16];
+  __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTFrags * kWave : 1];
+  __shared__ __attribute__((aligned(16))) float Ls[kGated ? 4 : 1][C];   // log alpha
+  __shared__ __attribute__((aligned(16))) float Bs[kDelta ? 4 : 1][C];   // beta
+  __shared__ __attribute__((aligned(16))) float Gs[kGated ? 3 : 1][C];   // g (in-chunk cumsum)
+  __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
+  __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
+  __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
+  __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Ux[2][4 * kWave];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -472,28 +531,52 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int col = col0 + n;
   const size_t hbase = (size_t)bh * L;
   const int NC = L / C;
+  const u32x4* tw = tws + (size_t)bh * NC * (kTFrags * kWave);
 
-  // DMA issue for one chunk's pieces (waves 2 and 3 split the instructions)
-  const int dw = wave - 2;                       // 0 or 1 on the loading waves
-  auto load_qv = [&](int c) {                    // Q and this tile's V columns
-    const size_t row0 = hbase + (size_t)c * C;
-    dma_tile<D>(Qs[c % 2], q + row0 * D, dw, lane);
-    const int r = 32 * dw + lane / 2;
-    dma16(v + (row0 + r) * D + col0 + 8 * (lane % 2),
-          __builtin_amdgcn_readfirstlane(lds_addr(Vs[c % 2]) + 1024 * dw));
-  };
-  auto load_kg = [&](int c) {                    // K and the gates
-    const size_t row0 = hbase + (size_t)c * C;
-    dma_tile<D>(Ks[c % 3], k + row0 * D, dw, lane);
-    if (dw == 0) {
-      if constexpr (kGated) dma4(log_alpha + row0 + lane, lds_addr(Ls[c % 3]));
+  // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
+  auto issue_chunk = [&](int cc) {
+    const size_t r0 = hbase + (size_t)cc * C;
+    if (wave == 1) {
+      dma_tile<D>(Ks[cc % 3], k + r0 * D, lane);
+    } else if (wave == 2) {
+      dma_tile<D>(Qs[cc % 3], q + r0 * D, lane);
     } else {
-      if constexpr (kDelta) dma4(beta + row0 + lane, lds_addr(Bs[c % 3]));
+      const uint32_t vb = lds_addr(Vs[cc % 4]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        dma16(v + (r0 + 32 * m + lane / 2) * D + col0 + 8 * (lane % 2),
+              __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+      if constexpr (kDelta) {
+        const uint32_t tb = lds_addr(Ts[cc % 3]);
+        const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
+#pragma unroll
+        for (int f = 0; f < kTFrags; ++f)
+          dma16(src + f * kWave + lane, __builtin_amdgcn_readfirstlane(tb + 1024 * f));
+      }
+    }
+  };
+  // DMA of the gates of chunk cc (wave 3)
+  auto issue_gates = [&](int cc) {
+    const size_t r0 = hbase + (size_t)cc * C;
+    if constexpr (kDelta) dma4(beta + r0 + lane, lds_addr(Bs[cc % 4]));
+    if constexpr (kGated) dma4(log_alpha + r0 + lane, lds_addr(Ls[cc % 4]));
+  };
+  // Decay tables of chunk cc from its gates (wave 2, gated mode)
+  auto tables = [&](int cc) {
+    if constexpr (kGated) {
+      const float gv = cumsum64(Ls[cc % 4], lane);
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
+      const float e = __expf(gv);
+      Gs[cc % 3][lane] = gv;
+      Es[cc % 3][lane] = e;
+      Fs[cc % 3][lane] = __expf(gC - gv);
+      BGs[cc % 3][lane] = Bs[cc % 4][lane] * e;
     }
   };
 
-  // ---- prologue
+  // ---- prologue: state, chunks 0 and 1, gates of chunks 0..2
   f32x4 S[NKT];
+  Frag2<T16> sf[NKB];            // wave 0: bf16 split of S, as published in Sx
   const size_t sbase = (size_t)bh * D * D;
   if (wave == 0) {
     if (S0) {
@@ -507,95 +590,54 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const Frag2<T16> f = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-      Sx[(2 * kb) * kWave + lane] = f.hi;
-      Sx[(2 * kb + 1) * kWave + lane] = f.lo;
-    }
-  } else if (wave == 1) {
-    if constexpr (kDelta) {
-      // upper blocks (0, 1) and (2, 3) of both T slots stay zero
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Tb[s][(4 * g + e) * LDT + 16 + n] = (T16)0.f;
-          Tb[s][(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
-        }
+      sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+      Sx[0][(2 * kb) * kWave + lane] = sf[kb].hi;
+      Sx[0][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
     }
   } else {
-    load_qv(0);
-    load_kg(0);
-    if (NC > 1) load_kg(1);
-    dma_wait();
+    issue_chunk(0);
+    if (NC > 1) issue_chunk(1);
+    if (wave == 3)
+      for (int cc = 0; cc < 3 && cc < NC; ++cc) issue_gates(cc);
+    vm_wait<0>();
   }
   __syncthreads();
-  if (wave >= 2) {
-    // g of chunks 0 and 1; A of chunks 0 and 1
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s == 1 && NC < 2) break;
-      if constexpr (kGated) Gs[s][lane] = cumsum64(Ls[s], lane);
-      else Gs[s][lane] = 0.f;
-    }
-  }
+  if (wave == 2) tables(0);
   __syncthreads();
-  if constexpr (kDelta) {
-    if (wave >= 2) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s == 1 && NC < 2) break;
-        if (wave == 2) kkt_rows<D, kGated, 0, 3>(Ks[s], Gs[s], Bs[s], Ab[s], g, n);
-        else kkt_rows<D, kGated, 1, 2>(Ks[s], Gs[s], Bs[s], Ab[s], g, n);
-      }
-    }
-    __syncthreads();
-    if (wave == 1) t_diag(Ab[0], Df, Tb[0], g, n);
-    __syncthreads();
-    if (wave == 1) t_col(Ab[0], Df, T32f, Tb[0], g, n);
-    __syncthreads();
-  }
 
   // ---- chunk loop
-  f32x4 un[4];                 // wave 0: U_new of the current chunk
-  f32x4 sc[2][4], qs[2];       // waves 2, 3: scores and Q S of the current chunk
+  f32x4 sc[2][4], qs[2];       // waves 1-3: scores and Q S of the current chunk
   for (int c = 0; c < NC; ++c) {
-    const size_t row0 = hbase + (size_t)c * C;
     const T16* Kc = Ks[c % 3];
-    const float* gc = Gs[c % 3];
-    const float* bc = Bs[c % 3];
-
-    // ================= segment A
     if (wave == 0) {
+      // ================= chain
       if constexpr (kDelta) {
-        Frag<T16> kf[4][NKB], tf[4][2];
-        f32x4 vv[4], bb[4], gg[4];
+        Frag<T16> kf[4][NKB], tf[kTFrags];
+        f32x4 vv[4], bb[4], bg[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) kf[ti][kb] = frag_row_sw<D>(Kc, 16 * ti + n, 32 * kb, g);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            if (kb <= ti / 2) tf[ti][kb] = frag_row(Tb[c % 2] + (16 * ti + n) * LDT + 32 * kb, g);
-          vv[ti] = v_acc(Vs[c % 2], ti, g, n);
-          bb[ti] = *reinterpret_cast<const f32x4*>(bc + 16 * ti + 4 * g);
-          if constexpr (kGated) gg[ti] = *reinterpret_cast<const f32x4*>(gc + 16 * ti + 4 * g);
+          vv[ti] = v_acc(Vs[c % 4], ti, g, n);
+          bb[ti] = *reinterpret_cast<const f32x4*>(Bs[c % 4] + 16 * ti + 4 * g);
+          if constexpr (kGated) bg[ti] = *reinterpret_cast<const f32x4*>(BGs[c % 3] + 16 * ti + 4 * g);
         }
-        Frag2<T16> sf[NKB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-        f32x4 ks[4], rr[4];
+        for (int f = 0; f < kTFrags; ++f) tf[f].v = __builtin_bit_cast(bf16x8, Ts[c % 3][f * kWave + lane]);
+        f32x4 ks[4], rr[4], un[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
+        // R = diag(beta) V - diag(beta gam) K S
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float gam = kGated ? __expf(gg[ti][i]) : 1.f;
-            rr[ti][i] = bb[ti][i] * (vv[ti][i] - gam * ks[ti][i]);
+            if constexpr (kGated) rr[ti][i] = fmaf(-bg[ti][i], ks[ti][i], bb[ti][i] * vv[ti][i]);
+            else rr[ti][i] = bb[ti][i] * (vv[ti][i] - ks[ti][i]);
           }
         Frag2<T16> rf[2];
 #pragma unroll
@@ -605,116 +647,127 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
           un[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            if (kb <= ti / 2) mma_ab2(tf[ti][kb], rf[kb], un[ti]);
+            if (kb <= ti / 2) mma_ab2(tf[tfi(ti, kb)], rf[kb], un[ti]);
         }
+        Frag2<T16> ut[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const Frag2<T16> f = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
-          Ux[(2 * kb) * kWave + lane] = f.hi;
-          Ux[(2 * kb + 1) * kWave + lane] = f.lo;
+          Ux[c % 2][(2 * kb) * kWave + lane] = f.hi;
+          Ux[c % 2][(2 * kb + 1) * kWave + lane] = f.lo;
+          ut[kb] = f;
         }
-      }
-    } else if (wave == 1) {
-      if constexpr (kDelta) {
-        if (c + 1 < NC) t_diag(Ab[(c + 1) % 2], Df, Tb[(c + 1) % 2], g, n);
-      }
-    } else {
-      if (c + 1 < NC) load_qv(c + 1);
-      if (c + 2 < NC) load_kg(c + 2);
-      if (wave == 2)
-        scores_qs<D, kGated, 2, 0, 3>(Qs[c % 2], Kc, gc, Sx, sc, qs, g, n, lane);
-      else
-        scores_qs<D, kGated, 2, 1, 2>(Qs[c % 2], Kc, gc, Sx, sc, qs, g, n, lane);
-      dma_wait();
-    }
-    __syncthreads();
-
-    // ================= segment B
-    if (wave == 0) {
-      Frag<T16> ktf[NKT][2];
+        Frag<T16> ktf[NKT][2];
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
+        for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ktf[tj][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n);
-      if constexpr (kDelta) {
-        Frag2<T16> ut[2];
+          for (int kb = 0; kb < 2; ++kb) ktf[tj][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n);
         if constexpr (kGated) {
-          const float gC = gc[C - 1];
-          float slo[2][4], shi[2][4];
+          // S <- gam_C S + K^T diag(gam_C / gam) U_new
+          const float* fc = Fs[c % 3];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              slo[kb][i] = __expf(gC - gc[32 * kb + 4 * g + i]);
-              shi[kb][i] = __expf(gC - gc[32 * kb + 16 + 4 * g + i]);
-            }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo[kb], shi[kb]);
-          const float decC = __expf(gC);
+          for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 flo = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 4 * g);
+            const f32x4 fhi = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 16 + 4 * g);
+            const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
+            const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
+            ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo, shi);
+          }
+          const float decC = Es[c % 3][C - 1];
 #pragma unroll
           for (int tj = 0; tj < NKT; ++tj) S[tj] *= decC;
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
       } else {
+        // S <- S + K^T V
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const Frag<T16> vf = frag_col_tr_v(Vs[c % 2], 32 * kb, g, n);
+          const Frag<T16> vf = frag_col_tr_v(Vs[c % 4], 32 * kb, g, n);
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) mma(ktf[tj][kb], vf, S[tj]);
+          for (int tj = 0; tj < NKT; ++tj) mma(frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n), vf, S[tj]);
         }
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const Frag2<T16> f = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-        Sx[(2 * kb) * kWave + lane] = f.hi;
-        Sx[(2 * kb + 1) * kWave + lane] = f.lo;
-      }
-    } else if (wave == 1) {
-      if constexpr (kDelta) {
-        if (c + 1 < NC) t_col(Ab[(c + 1) % 2], Df, T32f, Tb[(c + 1) % 2], g, n);
+        sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+        Sx[(c + 1) % 2][(2 * kb) * kWave + lane] = sf[kb].hi;
+        Sx[(c + 1) % 2][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
       }
     } else {
-      const size_t ob0 = row0 * D + col;
-      if (wave == 2)
-        out_rows<D, MODE, 2, 0, 3>(sc, qs, Ux, Vs[c % 2], gc, out_, ob0, out_bf16, g, n, lane);
-      else
-        out_rows<D, MODE, 2, 1, 2>(sc, qs, Ux, Vs[c % 2], gc, out_, ob0, out_bf16, g, n, lane);
-      if (c + 2 < NC) {
-        const int s = (c + 2) % 3;
-        if constexpr (kGated) Gs[s][lane] = cumsum64(Ls[s], lane);
-        else Gs[s][lane] = 0.f;
-        if constexpr (kDelta) {
-          if (wave == 2) kkt_rows<D, kGated, 0, 3>(Ks[s], Gs[s], Bs[s], Ab[(c + 2) % 2], g, n);
-          else kkt_rows<D, kGated, 1, 2>(Ks[s], Gs[s], Bs[s], Ab[(c + 2) % 2], g, n);
-        }
+      // ================= side waves
+      const bool steady = c + 3 < NC;
+      if (c + 2 < NC) issue_chunk(c + 2);
+      if (wave == 3 && c + 3 < NC) issue_gates(c + 3);
+      if (c > 0) {
+        const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
+        const Frag<T16>* U = Ux[(c - 1) % 2];
+        const T16* Vp = Vs[(c - 1) % 4];
+        if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+        else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+        else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+      }
+      if (wave == 2 && c + 1 < NC) tables(c + 1);
+      {
+        const float* gc = Gs[kGated ? c % 3 : 0];
+        const float* ec = Es[kGated ? c % 3 : 0];
+        const Frag<T16>* Sc = Sx[c % 2];
+        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+      }
+      // everything issued before this chunk has landed (the newest
+      // transfers, chunk c+2 and the gates of c+3, may still be in flight)
+      if (steady) {
+        if (wave == 3) vm_wait<NDMA3>();
+        else vm_wait<NTILE>();
+      } else {
+        vm_wait<0>();
       }
     }
     __syncthreads();
   }
 
-  if (wave == 0 && S_final) {
+  if (wave == 0) {
+    if (S_final) {
 #pragma unroll
-    for (int tj = 0; tj < NKT; ++tj)
+      for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+        for (int i = 0; i < 4; ++i)
+          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+    }
+  } else {
+    const int c = NC - 1;
+    const size_t ob0 = (hbase + (size_t)c * C) * D + col;
+    const Frag<T16>* U = Ux[c % 2];
+    const T16* Vp = Vs[c % 4];
+    if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+    else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+    else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
   }
 }
 
 template <int D, int MODE>
 hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
+  const int NC = a.L / C;
+  const T16* k = static_cast<const T16*>(a.k);
+  u32x4* tws = static_cast<u32x4*>(a.workspace);
   const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
   chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
-      static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
-      a.log_alpha, a.beta, a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
+      static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v), a.log_alpha, a.beta, tws,
+      a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
+  (void)NC;
+  return hipGetLastError();
+}
+
+template <int D, bool GATED>
+hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
+  const size_t items = (size_t)a.B * a.H * (a.L / C);
+  t_solve_kernel<D, GATED><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
+      static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace), a.L);
   return hipGetLastError();
 }
 
@@ -728,6 +781,17 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
+  if (a.mode == kModeLinear) return 0;
+  return (size_t)a.B * a.H * (a.L / C) * kTFrags * kWave * sizeof(u32x4);
+}
+
+hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
+  const bool gated = a.mode == kModeGatedDelta;
+  if (a.d == 64) return gated ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
+  return gated ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
+}
 
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st) {
   return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);

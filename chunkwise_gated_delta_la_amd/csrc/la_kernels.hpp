@@ -34,11 +34,19 @@ struct ChunkArgs {
   int B, H, L, d, C, mode;
   bool in_bf16;   // q, k, v are bf16 (else float)
   bool out_bf16;  // out is bf16 (else float)
+  void* workspace;  // chunk_workspace_bytes(*this) bytes, 256-byte aligned
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);       // dispatcher
-hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st);   // la_chunk.hip
-hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st);  // la_chunk_pipe.hip (bf16)
+// Chunk forward: float inputs run one kernel (la_chunk.hip); bf16 inputs
+// in the delta modes first solve T for every chunk (launch_tsolve, into the
+// workspace), then run the chain kernel (la_chunk_pipe.hip).
+size_t chunk_workspace_bytes(const ChunkArgs& a);
+bool chunk_needs_tsolve(const ChunkArgs& a);
+hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st);       // la_chunk_pipe.hip
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);        // dispatcher
+hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st);    // la_chunk.hip
+hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st);   // la_chunk_pipe.hip
+size_t chunk_pipe_workspace_bytes(const ChunkArgs& a);               // la_chunk_pipe.hip
 
 }  // namespace la

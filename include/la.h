@@ -37,20 +37,21 @@
  *   always float32; products accumulate in float32 and the state is carried
  *   in float32.  With bf16 inputs every float intermediate that feeds a
  *   bf16 matrix product is split into two bf16 terms, so the only roundings
- *   beyond float are the bf16 inputs themselves, one bf16 copy of the
- *   chunk's W factor, and the output (when it is bf16).
+ *   beyond float are the bf16 inputs themselves, one bf16 copy of each
+ *   chunk's triangular factor T = (I + A)^-1, and the output (when it is
+ *   bf16).
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *   enqueued asynchronously; the call returns without synchronising.
  * - Return value: LA_OK or an la_status_t error code.  Argument errors are
  *   detected before anything is enqueued and leave all outputs untouched.
- *   A failed launch or allocation returns LA_ERR_HIP.  Faults during
+ *   A failed launch returns LA_ERR_HIP.  Faults during
  *   execution surface at the caller's next synchronisation.
  *   la_last_error() returns a message for the last non-OK return on the
  *   calling thread.
- * - The library keeps no pointer after a call returns.  Transient workspace
- *   is allocated and released stream-ordered on `stream` from a memory pool
- *   owned by the library, so concurrent calls on different streams do not
- *   share workspace.
+ * - The library allocates no memory and keeps no pointer after a call
+ *   returns.  Scratch space, where a call needs any, is a caller-provided
+ *   device workspace whose size la_chunk_workspace_bytes() reports; calls
+ *   that run concurrently need separate workspaces.
  */
 #ifndef LA_H_
 #define LA_H_
@@ -81,7 +82,8 @@ typedef enum {
   LA_ERR_SHAPE = 2,       /* non-positive size, or L not a multiple of C     */
   LA_ERR_UNSUPPORTED = 3, /* (dk, dv, C, dtype, mode) outside the built set  */
   LA_ERR_ALIAS = 4,       /* an output overlaps an input (see each call)     */
-  LA_ERR_HIP = 5          /* HIP launch or allocation failure                */
+  LA_ERR_HIP = 5,         /* HIP launch failure                              */
+  LA_ERR_WORKSPACE = 6    /* workspace missing, too small or misaligned      */
 } la_status_t;
 
 /*
@@ -112,16 +114,35 @@ typedef enum {
  *   S_final    [B, H, dk, dv] float32        final state (written); may be
  *                                            NULL; may equal S0 (in-place)
  *   B, H, L, dk, dv, C        sizes; L must be a multiple of C
- *   mode       la_mode_t;  dtype  la_dtype_t;  stream  hipStream_t
+ *   mode       la_mode_t;  dtype  la_dtype_t
+ *   workspace  device scratch of workspace_bytes bytes, 16-byte aligned,
+ *              at least what la_chunk_workspace_bytes() reports for the same
+ *              arguments; may be NULL when that is 0.  Its contents on entry
+ *              are ignored and on return are unspecified.  The bf16 delta
+ *              modes keep each chunk's T factor there (B*H*L/C * 6 KiB);
+ *              float inputs and LA_MODE_LINEAR need none.
+ *   stream     hipStream_t
  *
- * Supported: dk = dv in {64, 128}, C = 64, both dtypes, all modes.
+ * Supported: dk = dv in {64, 128}, C = 64, all dtypes, all modes.
  * Aliasing: S_final == S0 is allowed; any other overlap of out or S_final
- * with an input, or of out with S_final, returns LA_ERR_ALIAS.
+ * with an input, or of out with S_final, returns LA_ERR_ALIAS, as does a
+ * workspace that overlaps any tensor argument.  A missing, short or
+ * misaligned workspace returns LA_ERR_WORKSPACE.
  */
 int la_chunk_fwd(const void* q, const void* k, const void* v,
                  const float* log_alpha, const float* beta, const float* S0,
                  void* out, float* S_final, int B, int H, int L, int dk,
-                 int dv, int C, int mode, int dtype, void* stream);
+                 int dv, int C, int mode, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * la_chunk_workspace_bytes -- size of the workspace la_chunk_fwd needs for
+ * these sizes, mode and dtype, written to *bytes (0 if it needs none).
+ * Validates the same shape, mode and dtype rules as la_chunk_fwd and
+ * returns the same error codes; LA_ERR_NULL for a NULL bytes.
+ */
+int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
+                             int mode, int dtype, size_t* bytes);
 
 /*
  * la_decode_step -- one token of the recurrence for B*H independent states
@@ -157,7 +178,7 @@ int la_decode_step(const void* q, const void* k, const void* v,
  * Between la_profile_begin() and la_profile_end(), every kernel the library
  * launches (from any thread) is bracketed by two HIP events recorded on the
  * stream it is launched on.  la_profile_end() waits for the recorded events,
- * then reports, per kernel name ("la_wy", "la_state", "la_decode"), the
+ * then reports, per kernel name ("la_tsolve", "la_chunk", "la_decode"), the
  * number of launches and the summed event-to-event time in milliseconds,
  * and stops recording.  `out` is a host array of `capacity` entries; the
  * number of distinct kernels is written to *count (entries beyond capacity
@@ -178,7 +199,7 @@ int la_profile_end(la_kernel_time_t* out, int capacity, int* count);
  * The pointer stays valid until the next call on the same thread. */
 const char* la_last_error(void);
 
-/* Library version string, e.g. "lachunk 0.1.0 gfx950". */
+/* Library version string, e.g. "lachunk 0.2.0 gfx950". */
 const char* la_version(void);
 
 #ifdef __cplusplus

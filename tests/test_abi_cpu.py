@@ -17,7 +17,8 @@ ensure_built()
 from chunkwise_gated_delta_la_amd import _lib  # noqa: E402
 
 HEADER = os.path.join(ROOT, "include", "la.h")
-OK, NULL, SHAPE, UNSUP, ALIAS = 0, 1, 2, 3, 4
+OK, NULL, SHAPE, UNSUP, ALIAS, WS = 0, 1, 2, 3, 4, 6
+TSOLVE_BYTES = 6 * 1024     # T operand fragments per chunk (bf16 delta modes)
 
 
 def _declared_functions():
@@ -48,9 +49,16 @@ def fake(i):
 
 
 def chunk(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5),
-          out=fake(6), sf=fake(7), B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1):
+          out=fake(6), sf=fake(7), B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1,
+          ws=fake(8), wsb=P):
     return lib.la_chunk_fwd(q, k, v, la, be, s0, out, sf, B, H, L, dk, dv, C, mode, dtype,
-                            None)
+                            ws, wsb, None)
+
+
+def ws_bytes(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1):
+    n = ctypes.c_size_t(12345)
+    rc = lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, mode, dtype, ctypes.byref(n))
+    return rc, n.value
 
 
 def decode(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), S=fake(5),
@@ -82,6 +90,44 @@ def test_chunk_fwd_alias_rules():
     assert chunk(lib, sf=ctypes.c_void_p(6 * P + 4)) == ALIAS
     # ... out overlapping S_final too
     assert chunk(lib, out=ctypes.c_void_p(8 * P + 4)) == ALIAS
+
+
+def test_workspace_size():
+    """One T factor per chunk for bf16 inputs in the delta modes; nothing
+    for float inputs or linear attention."""
+    lib = _lib.get()
+    for mode in (1, 2):
+        for dtype in (1, 2):
+            for (B, H, L, d) in ((1, 1, 64, 64), (2, 3, 256, 128), (1, 32, 65536, 128)):
+                rc, n = ws_bytes(lib, B=B, H=H, L=L, dk=d, dv=d, mode=mode, dtype=dtype)
+                assert rc == OK and n == B * H * (L // 64) * TSOLVE_BYTES
+    assert ws_bytes(lib, mode=0) == (OK, 0)
+    assert ws_bytes(lib, dtype=0) == (OK, 0)
+    assert ws_bytes(lib, L=96)[0] == SHAPE
+    assert ws_bytes(lib, dk=96, dv=96)[0] == UNSUP
+    assert ws_bytes(lib, mode=5)[0] == UNSUP
+    assert lib.la_chunk_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ws=None), dict(wsb=TSOLVE_BYTES - 1), dict(ws=ctypes.c_void_p(9 * P + 8)),
+    dict(B=2, wsb=TSOLVE_BYTES), dict(ws=None, wsb=P),
+])
+def test_chunk_fwd_workspace_rejects(kw):
+    lib = _lib.get()
+    assert chunk(lib, **kw) == WS
+    assert "workspace" in lib.la_last_error().decode()
+
+
+def test_chunk_fwd_workspace_alias_and_optional():
+    lib = _lib.get()
+    # workspace overlapping k, or out
+    assert chunk(lib, ws=ctypes.c_void_p(2 * P - 1024)) == ALIAS
+    assert chunk(lib, ws=ctypes.c_void_p(7 * P - 4096)) == ALIAS
+    # float inputs and linear attention need none: a NULL workspace passes the
+    # workspace checks and the call fails on the NULL q it was given instead
+    assert chunk(lib, ws=None, wsb=0, dtype=0, q=None) == NULL
+    assert chunk(lib, ws=None, wsb=0, mode=0, out=ctypes.c_void_p(P + 128)) == ALIAS
 
 
 def test_chunk_fwd_unused_gates_may_alias_anything():

@@ -129,6 +129,18 @@ def test_chunk_single_chunk_single_head(mode):
     check_fwd(w, x, o_ref, S_ref)
 
 
+@pytest.mark.parametrize("L", [128, 192, 256])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_short_sequences(mode, L):
+    """2, 3 and 4 chunks: the load pipeline runs two chunks ahead, so these
+    are the lengths where its prologue and drain overlap."""
+    w = recipe(mode, "bf16", B=1, H=2, L=L, d=64, s0_std=0.3, seed=11)
+    log(f"chunk short {w}")
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    check_fwd(w, x, o_ref, S_ref)
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]
@@ -240,7 +252,8 @@ def test_errors_surface_as_exceptions():
 def test_outputs_fully_written(mode, dtype, d):
     """out and S_final are pre-filled with NaN: every element must be
     written by the kernel (a skipped row or column tile stays NaN).  B * H
-    = 8 exercises the head-to-XCD block numbering."""
+    = 8 exercises the head-to-XCD block numbering.  The workspace is passed
+    explicitly, pre-filled with NaN."""
     w = recipe(mode, dtype, B=2, H=4, L=192, d=d, s0_std=0.2, seed=37)
     log(f"outputs fully written {w}")
     x = workloads.make_inputs(w)
@@ -248,8 +261,13 @@ def test_outputs_fully_written(mode, dtype, d):
     dev = to_cuda(x)
     out = torch.full((w.B, w.H, w.L, w.dv), float("nan"), dtype=w.torch_dtype, device="cuda")
     S = torch.full((w.B, w.H, w.dk, w.dv), float("nan"), dtype=torch.float32, device="cuda")
+    # the workspace too starts as all-ones bytes (NaN in bf16 and float):
+    # nothing may be read from it before the call writes it
+    nws = la.chunk_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=mode,
+                                   dtype=w.torch_dtype)
+    ws = torch.full((max(nws, 1),), 255, dtype=torch.uint8, device="cuda")
     la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"],
-                 mode=mode, out=out, S_final=S)
+                 mode=mode, out=out, S_final=S, workspace=ws)
     torch.cuda.synchronize()
     assert_close("o", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
     assert_close("S_final", f64(S), S_ref, dtype)
