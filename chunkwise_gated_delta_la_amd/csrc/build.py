@@ -24,6 +24,10 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # packed FP32 instructions are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the chain kernel's accumulators feed
+    # VALU work (splits, scaling) every chunk, and AGPR-resident results
+    # would need a v_accvgpr_read per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", HERE,
 ]

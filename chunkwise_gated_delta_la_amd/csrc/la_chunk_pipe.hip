@@ -16,12 +16,12 @@
 //                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
 //                      U_new (publish S)
 //      waves 1-3       output of chunk c-1 from the U_new published at the
-//                      last barrier; masked decayed scores and diag(gam) Q S
-//                      of chunk c for their row tiles (wave 1: tiles 0 and
-//                      1, wave 2: tile 2, wave 3: tile 3), kept in
-//                      registers until the next chunk; DMA of chunk c+2
-//                      (Q, K, V, T) and of the gates of chunk c+3; the
-//                      decay tables of chunk c+1
+//                      last barrier; the decay tables of chunk c+1; masked
+//                      decayed scores and diag(gam) Q S of chunk c for their
+//                      row tiles (wave 1: tiles 0 and 1, wave 2: tile 2,
+//                      wave 3: tile 3), kept in registers until the next
+//                      chunk; then DMA of chunk c+2 (Q, K, V, T) and of the
+//                      gates of chunk c+3
 //
 //    so the serial chain only ever waits for its own products.  Inputs go
 //    from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
@@ -574,11 +574,14 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     }
   };
 
-  // ---- prologue: state, chunks 0 and 1, gates of chunks 0..2
-  f32x4 S[NKT];
-  Frag2<T16> sf[NKB];            // wave 0: bf16 split of S, as published in Sx
-  const size_t sbase = (size_t)bh * D * D;
+  // Each role runs its own loop with the same barriers (two in the
+  // prologue, one per chunk), so the registers one role carries from chunk
+  // to chunk are not live in the other's code.
   if (wave == 0) {
+    // ================= chain
+    f32x4 S[NKT];
+    Frag2<T16> sf[NKB];            // bf16 split of S, as published in Sx
+    const size_t sbase = (size_t)bh * D * D;
     if (S0) {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
@@ -594,23 +597,11 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       Sx[0][(2 * kb) * kWave + lane] = sf[kb].hi;
       Sx[0][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
     }
-  } else {
-    issue_chunk(0);
-    if (NC > 1) issue_chunk(1);
-    if (wave == 3)
-      for (int cc = 0; cc < 3 && cc < NC; ++cc) issue_gates(cc);
-    vm_wait<0>();
-  }
-  __syncthreads();
-  if (wave == 2) tables(0);
-  __syncthreads();
+    __syncthreads();
+    __syncthreads();
 
-  // ---- chunk loop
-  f32x4 sc[2][4], qs[2];       // waves 1-3: scores and Q S of the current chunk
-  for (int c = 0; c < NC; ++c) {
-    const T16* Kc = Ks[c % 3];
-    if (wave == 0) {
-      // ================= chain
+    for (int c = 0; c < NC; ++c) {
+      const T16* Kc = Ks[c % 3];
       if constexpr (kDelta) {
         Frag<T16> kf[4][NKB], tf[kTFrags];
         f32x4 vv[4], bb[4], bg[4];
@@ -696,11 +687,29 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         Sx[(c + 1) % 2][(2 * kb) * kWave + lane] = sf[kb].hi;
         Sx[(c + 1) % 2][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
       }
-    } else {
-      // ================= side waves
+      __syncthreads();
+    }
+    if (S_final) {
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+    }
+  } else {
+    // ================= side waves
+    issue_chunk(0);
+    if (NC > 1) issue_chunk(1);
+    if (wave == 3)
+      for (int cc = 0; cc < 3 && cc < NC; ++cc) issue_gates(cc);
+    vm_wait<0>();
+    __syncthreads();
+    if (wave == 2) tables(0);
+    __syncthreads();
+
+    f32x4 sc[2][4], qs[2];       // scores and Q S of the current chunk
+    for (int c = 0; c < NC; ++c) {
       const bool steady = c + 3 < NC;
-      if (c + 2 < NC) issue_chunk(c + 2);
-      if (wave == 3 && c + 3 < NC) issue_gates(c + 3);
       if (c > 0) {
         const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
         const Frag<T16>* U = Ux[(c - 1) % 2];
@@ -711,6 +720,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       }
       if (wave == 2 && c + 1 < NC) tables(c + 1);
       {
+        const T16* Kc = Ks[c % 3];
         const float* gc = Gs[kGated ? c % 3 : 0];
         const float* ec = Es[kGated ? c % 3 : 0];
         const Frag<T16>* Sc = Sx[c % 2];
@@ -718,6 +728,9 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
         else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
       }
+      // loads for later chunks, issued after this chunk's LDS reads
+      if (c + 2 < NC) issue_chunk(c + 2);
+      if (wave == 3 && c + 3 < NC) issue_gates(c + 3);
       // everything issued before this chunk has landed (the newest
       // transfers, chunk c+2 and the gates of c+3, may still be in flight)
       if (steady) {
@@ -726,19 +739,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       } else {
         vm_wait<0>();
       }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-
-  if (wave == 0) {
-    if (S_final) {
-#pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
-    }
-  } else {
     const int c = NC - 1;
     const size_t ob0 = (hbase + (size_t)c * C) * D + col;
     const Frag<T16>* U = Ux[c % 2];

@@ -280,6 +280,47 @@ __device__ __forceinline__ Frag2<T> frag2_from_acc_scaled(const f32x4& lo, const
   return f;
 }
 
+// bf16 specialisations: two values are rounded per instruction
+// (v_cvt_pk_bf16_f32) and the remainders x - hi are formed from the packed
+// pair, 3 instructions per value.  Same roundings as Frag2::set.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float h0 = __builtin_bit_cast(float, h << 16);
+  const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+  hi = h;
+}
+
+__device__ __forceinline__ Frag2<__bf16> frag2_pack(float a0, float a1, float a2, float a3,
+                                                    float b0, float b1, float b2, float b3) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split_pair(a0, a1, h0, l0);
+  split_pair(a2, a3, h1, l1);
+  split_pair(b0, b1, h2, l2);
+  split_pair(b2, b3, h3, l3);
+  Frag2<__bf16> f;
+  f.hi.v = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  f.lo.v = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
+  return f;
+}
+
+template <>
+__device__ __forceinline__ Frag2<__bf16> frag2_from_acc<__bf16>(const f32x4& lo, const f32x4& hi) {
+  return frag2_pack(lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]);
+}
+
+template <>
+__device__ __forceinline__ Frag2<__bf16> frag2_from_acc_scaled<__bf16>(const f32x4& lo,
+                                                                      const f32x4& hi,
+                                                                      const float* slo,
+                                                                      const float* shi) {
+  return frag2_pack(lo[0] * slo[0], lo[1] * slo[1], lo[2] * slo[2], lo[3] * slo[3],
+                    hi[0] * shi[0], hi[1] * shi[1], hi[2] * shi[2], hi[3] * shi[3]);
+}
+
 // Split operand from a float row p[kidx(g, j)] (a row of a float matrix
 // as the A operand, or a column stored contiguously as the B operand).
 template <typename T>
