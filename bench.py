@@ -37,16 +37,14 @@ CSRC = os.path.join(ROOT, "chunkwise_gated_delta_la_amd", "csrc")
 # only while these are unchanged.
 KERNEL_SOURCES = {
     "la_chunk": ["la_chunk.hip", "la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
-    "la_prep": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
+    "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
 # rocprofv3 kernel names -> library kernel names (chunk_kernel: float
 # inputs, chunk_pipe_kernel: bf16 inputs)
 KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
-                  "chunk_prep_kernel": "la_prep", "decode_kernel": "la_decode"}
-# Workspace record of one (b, h, chunk), bf16 inputs in the delta modes: T
-# and the gate tables.
-REC_BYTES = 8 * 1024
+                  "t_solve_kernel": "la_tsolve", "decode_kernel": "la_decode"}
+T_BYTES_PER_CHUNK = 6 * 1024   # T operand fragments of one (b, h, chunk)
 
 
 def log(msg):
@@ -57,13 +55,12 @@ def log(msg):
 # Per (token, head) of the forward, d = dk = dv, chunk C, element size e:
 #   algorithmic work of the method (dense-block chunkwise):
 #     gated/delta: 10 C d + 6 d^2 flop;  linear: 4 C d + 4 d^2
-#   la_chunk (the chain kernel) moves q, k, v in and o out (4 d e); for
-#            bf16 inputs in the delta modes it reads the chunk's workspace
-#            record (T and the gate tables, 8 KiB per chunk: 128 B per
-#            token) instead of the gates; float inputs read beta (delta
-#            modes) and log_alpha (gated) at 4 B each; per (b, h): S0 in
-#            (when given) and S_final out at dk dv 4 B
-#   la_prep (bf16 delta modes) reads k and the gates and writes the record
+#   la_chunk (the chain kernel) moves q, k, v in and o out (4 d e), plus
+#            beta (delta modes) and log_alpha (gated) at 4 B each, plus,
+#            for bf16 inputs in the delta modes, the chunk's T factor
+#            (6 KiB per chunk: 96 B per token); per (b, h): S0 in (when
+#            given) and S_final out at dk dv 4 B
+#   la_tsolve (bf16 delta modes) reads k and the gates and writes T
 # Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,
 # o (2 dk e + 2 dv e), two float gates.
 
@@ -74,12 +71,10 @@ def fwd_flops_per_token_head(w):
     return 10 * C * d + 6 * d * d
 
 
-def rec_bytes_per_token_head(w):
-    """Workspace record bytes per (token, head) that la_prep writes and
-    la_chunk reads (bf16 inputs only)."""
-    if w.dtype != "bf16" or w.mode == "linear":
-        return 0
-    return REC_BYTES // w.C
+def t_bytes_per_token_head(w):
+    """Bytes of the T factor per (token, head): written by la_tsolve, read
+    by la_chunk (bf16 inputs in the delta modes only)."""
+    return T_BYTES_PER_CHUNK // w.C if (w.dtype == "bf16" and w.mode != "linear") else 0
 
 
 def kernel_bytes_per_token_head(name, w):
@@ -90,17 +85,16 @@ def kernel_bytes_per_token_head(name, w):
     e = 2 if w.dtype == "bf16" else 4
     gates = {"linear": 0, "delta": 4, "gated_delta": 8}[w.mode]
     if name == "la_chunk":
-        rec = rec_bytes_per_token_head(w)
-        return fwd_min_bytes_per_token_head(w) + rec - (gates if rec else 0)
-    if name == "la_prep":
-        return w.dk * e + gates + rec_bytes_per_token_head(w)
+        return fwd_min_bytes_per_token_head(w) + t_bytes_per_token_head(w)
+    if name == "la_tsolve":
+        return w.dk * e + gates + t_bytes_per_token_head(w)
     raise KeyError(name)
 
 
 def kernel_bytes_per_head(name, w):
     """Per-head state bytes of a forward call: S0 read (if given), S_final
     written (chain kernel only)."""
-    if name == "la_prep":
+    if name == "la_tsolve":
         return 0
     if name != "la_chunk":
         raise KeyError(name)
@@ -352,7 +346,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4,
                     help="forward workload id in workloads.WORKLOADS (default 4)")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (traffic calibration)")
@@ -364,7 +358,7 @@ def main():
         import workloads
         ingest_pmc(*args.ingest_pmc[:4],
                    {"la_chunk": workloads.WORKLOADS[args.workload].name,
-                    "la_prep": workloads.WORKLOADS[args.workload].name,
+                    "la_tsolve": workloads.WORKLOADS[args.workload].name,
                     "la_decode": workloads.WORKLOADS[5].name}, args.ingest_pmc[4])
         return
     if args.gpus != 1:

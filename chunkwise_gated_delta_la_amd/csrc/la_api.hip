@@ -196,11 +196,11 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = prof_mark(st);
-  if (la::chunk_needs_prep(a)) {
-    const hipError_t e = la::launch_prep(a, st);
+  if (la::chunk_needs_tsolve(a)) {
+    const hipError_t e = la::launch_tsolve(a, st);
     hipEvent_t e1 = prof_mark(st);
-    prof_add("la_prep", e0, e1);
-    if (e != hipSuccess) return fail_hip("launching the chunk preparation kernel", e);
+    prof_add("la_tsolve", e0, e1);
+    if (e != hipSuccess) return fail_hip("launching the T-solve kernel", e);
     e0 = e1;
   }
   const hipError_t e = la::launch_chunk(a, st);

@@ -3,37 +3,30 @@
 // sources), split along what does and does not depend on the carried state.
 //
 // 1. t_solve_kernel, parallel over every (batch, head, chunk): the chunk's
-//    A = strict_lower(diag(beta) K K^T * Gamma) and T = (I + A)^-1, plus the
-//    per-row gate tables (g, exp(g), exp(g_C - g), beta, beta exp(g)).
-//    None of it depends on the carried state, so all chunks are solved at
-//    once, at full occupancy, and written to an 8 KiB workspace record per
-//    chunk; T is stored as the exact MFMA operand fragments the second
-//    kernel feeds to U_new = T R.
+//    A = strict_lower(diag(beta) K K^T * Gamma) and T = (I + A)^-1.  T does
+//    not depend on the state, so all chunks are solved at once, at full
+//    occupancy, and written to a workspace as the exact MFMA operand
+//    fragments the second kernel feeds to U_new = T R (6 KiB per chunk).
 //
 // 2. chunk_pipe_kernel, one 256-thread workgroup per 16-column tile of one
 //    (batch, head) state, walking the chunks in order.  Per chunk c, with a
 //    single barrier at the end:
 //
-//      waves 0, 1 (chain)  K S, R = diag(beta)(V - diag(gam) K S), U_new =
-//                          T R (both waves, from the split state published
-//                          at the last barrier; each publishes half of
-//                          U_new),
-//                          then each wave updates its half of the state's
-//                          rows, S <- gam_C S + K^T diag(gam_C/gam) U_new,
-//                          and publishes it split into bf16 hi + lo
-//      waves 2, 3          output of chunk c-1 from the U_new published at
-//                          the last barrier; masked decayed scores and
-//                          diag(gam) Q S of chunk c for their row tiles
-//                          (wave 2: tiles 0 and 3, wave 3: tiles 1 and 2),
-//                          kept in registers until the next chunk; then DMA
-//                          of chunk c+2 (Q, K, V and the workspace record)
+//      wave 0 (chain)  K S, R = diag(beta)(V - diag(gam) K S), U_new = T R
+//                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
+//                      U_new (publish S)
+//      waves 1-3       output of chunk c-1 from the U_new published at the
+//                      last barrier; the decay tables of chunk c+1; masked
+//                      decayed scores and diag(gam) Q S of chunk c for their
+//                      row tiles (wave 1: tiles 0 and 1, wave 2: tile 2,
+//                      wave 3: tile 3), kept in registers until the next
+//                      chunk; then DMA of chunk c+2 (Q, K, V, T) and of the
+//                      gates of chunk c+3
 //
-//    so the serial recurrence only waits for its own products.  Inputs go
+//    so the serial chain only ever waits for its own products.  Inputs go
 //    from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
 //    bytes land at base + 16 l) without passing through registers, issued
-//    two chunks ahead and complete one chunk ahead, so the chain waves load
-//    the next chunk's operands into registers while the current chunk's
-//    state update runs.  Q and K tiles are
+//    two chunks ahead and waited for one chunk later.  Q and K tiles are
 //    stored row-major with the 16-byte units of row r XOR-permuted by r,
 //    which makes both the operand-row reads and the transposed reads
 //    conflict-free.  K^T and V^T operands are read transposed from the
@@ -47,8 +40,6 @@
 // Precision as in the float kernel's bf16 path: q, k, v exact, float
 // operands split into bf16 hi + lo, T a single bf16, float accumulation and
 // state.
-#include <type_traits>
-
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
@@ -169,6 +160,11 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                :: "v"(src), "s"(lds) : "memory", "m0");
 }
 
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -196,17 +192,6 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int lane
 // Fragment index of the T operand (row tile ti, 32-deep block kb), kb <= ti / 2.
 __device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
 constexpr int kTFrags = 6;
-// Workspace record of one (batch, head, chunk): the T fragments, then
-// per-row tables (64 floats each) of the chunk's gates.
-constexpr int kRecBytes = 8192;
-constexpr int kTabOff = kTFrags * kWave * 16;        // 6144
-enum : int {
-  kTabG = 0,      // g, the in-chunk cumulative log decay (0 without gating)
-  kTabGam = 1,    // gam = exp(g)
-  kTabF = 2,      // exp(g_C - g): decay from each row to the chunk's end
-  kTabBeta = 3,   // beta
-  kTabBG = 4      // beta gam
-};
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
@@ -297,17 +282,14 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
   }
 }
 
-// One wave per (batch, head, chunk) (blocks numbered chunk-fastest): the
-// state-independent part of the chunk, into record `item` of the
-// workspace: T as fragments [f][lane] (f = tfi(ti, kb): lane (g, n) holds
-// T[16 ti + n][32 kb + kidx(g, j)]) and the gate tables.
-template <int D, int MODE>
-__global__ __launch_bounds__(kWave) void chunk_prep_kernel(const T16* __restrict__ k,
-                                                           const float* __restrict__ log_alpha,
-                                                           const float* __restrict__ beta,
-                                                           char* __restrict__ ws, int L) {
-  static_assert(MODE != kModeLinear, "linear attention needs no preparation");
-  constexpr bool kGated = MODE == kModeGatedDelta;
+// One wave per (batch, head, chunk) (blocks numbered chunk-fastest): T of
+// the chunk into tws[item][f][lane], f = tfi(ti, kb), the operand fragment
+// T[16 ti + n][32 kb + kidx(g, j)] of lane (g, n).
+template <int D, bool GATED>
+__global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ k,
+                                                        const float* __restrict__ log_alpha,
+                                                        const float* __restrict__ beta,
+                                                        u32x4* __restrict__ tws, int L) {
   constexpr int NKB = D / 32;
   __shared__ __attribute__((aligned(16))) float Ab[10 * 16 * LDB];
   __shared__ __attribute__((aligned(16))) float Df[4 * 16 * LDB];
@@ -322,41 +304,26 @@ __global__ __launch_bounds__(kWave) void chunk_prep_kernel(const T16* __restrict
   const size_t item = blockIdx.x;
   const size_t bh = item / NC;
   const size_t row0 = bh * L + (item % NC) * C;
-  char* rec = ws + item * kRecBytes;
 
   // K rows as operands of K K^T.  Both operands are rows of K, so any
-  // assignment of the contraction index to (group, slot) works; here slot
-  // j of group g is column 32 kb + 8 g + j, one 16-byte load per fragment.
+  // assignment of the contraction index to (group, slot) works; here slot j
+  // of group g is column 32 kb + 8 g + j, one 16-byte load per fragment.
   Frag<T16> kf[4][NKB];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       kf[t][kb].v = *reinterpret_cast<const bf16x8*>(k + (row0 + 16 * t + n) * D + 32 * kb + 8 * g);
+  const float bv = beta[row0 + lane];
   float gv = 0.f;
-  if constexpr (kGated) gv = wave_inclusive_scan(log_alpha[row0 + lane]);
+  if constexpr (GATED) gv = wave_inclusive_scan(log_alpha[row0 + lane]);
   gsh[lane] = gv;
-  {
-    const float bv = beta[row0 + lane];
-    bsh[lane] = bv;
-    float* tab = reinterpret_cast<float*>(rec + kTabOff);
-    float gam = 1.f, fc = 1.f;
-    if constexpr (kGated) {
-      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
-      gam = __expf(gv);
-      fc = __expf(gC - gv);
-    }
-    tab[kTabG * C + lane] = gv;
-    tab[kTabGam * C + lane] = gam;
-    tab[kTabF * C + lane] = fc;
-    tab[kTabBeta * C + lane] = bv;
-    tab[kTabBG * C + lane] = bv * gam;
-    // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
+  bsh[lane] = bv;
+  // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
-      Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
-    }
+  for (int e = 0; e < 4; ++e) {
+    Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
+    Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
   }
   __syncthreads();
 
@@ -377,7 +344,7 @@ __global__ __launch_bounds__(kWave) void chunk_prep_kernel(const T16* __restrict
       for (int e = 0; e < 4; ++e) {
         const bool keep = R > t || 4 * g + e > n;
         float decay = 1.f;
-        if constexpr (kGated) decay = __expf(keep ? gr[e] - gc : 0.f);
+        if constexpr (GATED) decay = __expf(keep ? gr[e] - gc : 0.f);
         blk[(4 * g + e) * LDB + n] = keep ? br[e] * acc[e] * decay : 0.f;
       }
     }
@@ -387,7 +354,7 @@ __global__ __launch_bounds__(kWave) void chunk_prep_kernel(const T16* __restrict
   __syncthreads();
   t_col(Ab, Df, T32f, Tb, g, n);
   __syncthreads();
-  u32x4* dst = reinterpret_cast<u32x4*>(rec);
+  u32x4* dst = tws + item * (kTFrags * kWave);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -399,17 +366,17 @@ __global__ __launch_bounds__(kWave) void chunk_prep_kernel(const T16* __restrict
 
 // ---------------------------------------------------------------- side roles
 
-// Scores and Q S of chunk c for row tiles TI0 and TI1, kept in registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
+// Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
+// registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
 // Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
 // gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].
-template <int D, bool GATED, int TI0, int TI1>
+template <int D, bool GATED, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
                                           const float* esc, const Frag<T16>* Sx,
                                           f32x4 (&sc)[2][4], f32x4 (&qs)[2], int g, int n,
                                           int lane) {
   constexpr int NKB = D / 32;
-  constexpr int NTI = 2;
-  constexpr int NT = (TI0 > TI1 ? TI0 : TI1) + 1;
+  constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
   Frag<T16> qf[NTI][NKB], kf[NT][NKB];
   Frag2<T16> sx[NKB];
 #pragma unroll
@@ -461,9 +428,9 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
   }
 }
 
-// Output of one chunk for row tiles TI0 and TI1: O = qs + Aqk U_new
-// (U_new = V in linear mode), from the registers scores_qs filled.
-template <int D, int MODE, int TI0, int TI1>
+// Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
+// (U_new = V in linear mode).
+template <int D, int MODE, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
                                          const Frag<T16>* Ux, const T16* Vt, void* out_,
                                          size_t ob0, int out_bf16, int g, int n, int lane) {
@@ -479,7 +446,7 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&
     }
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NTI; ++u) {
     const int ti = u ? TI1 : TI0;
     f32x4 o = qs[u];
 #pragma unroll
@@ -506,26 +473,39 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&
   }
 }
 
+// In-chunk cumulative log-decay of the 64 values at p, one per lane.
+__device__ __forceinline__ float cumsum64(const float* p, int lane) {
+  return wave_inclusive_scan(p[lane]);
+}
+
 // ---------------------------------------------------------------- chain kernel
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
-    const char* __restrict__ ws, const float* __restrict__ S0, void* __restrict__ out_,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const u32x4* __restrict__ tws, const float* __restrict__ S0, void* __restrict__ out_,
     float* __restrict__ S_final, int L, int BH, int out_bf16) {
   constexpr bool kDelta = MODE != kModeLinear;
   constexpr bool kGated = MODE == kModeGatedDelta;
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
-  constexpr int HKT = NKT / 2, HKB = NKB / 2;    // the same for half the rows
   constexpr int NCT = D / 16;                    // column tiles per head
   constexpr int TILE = C * D;                    // elements of a Q / K tile
   constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
+  // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha
+  constexpr int NDMA3 = 2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0);
 
   __shared__ __attribute__((aligned(16))) T16 Qs[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Vs[4][C * 16];
-  __shared__ __attribute__((aligned(16))) char Ws[kDelta ? 3 : 1][kDelta ? kRecBytes : 16];
+  __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTFrags * kWave : 1];
+  __shared__ __attribute__((aligned(16))) float Ls[kGated ? 4 : 1][C];   // log alpha
+  __shared__ __attribute__((aligned(16))) float Bs[kDelta ? 4 : 1][C];   // beta
+  __shared__ __attribute__((aligned(16))) float Gs[kGated ? 3 : 1][C];   // g (in-chunk cumsum)
+  __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
+  __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
+  __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
   __shared__ __attribute__((aligned(16))) Frag<T16> Ux[2][4 * kWave];
 
@@ -551,113 +531,97 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int col = col0 + n;
   const size_t hbase = (size_t)bh * L;
   const int NC = L / C;
-  const char* wrec = ws + (size_t)bh * NC * kRecBytes;
-  auto tab = [&](int slot, int row) {
-    return reinterpret_cast<const float*>(Ws[slot] + kTabOff) + row * C;
-  };
+  const u32x4* tw = tws + (size_t)bh * NC * (kTFrags * kWave);
 
-  // DMA of chunk cc: wave 2 K and this tile's V columns, wave 3 Q and the
-  // first part of the chunk's workspace record (T and the gate tables)
+  // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
   auto issue_chunk = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
-    if (wave == 2) {
+    if (wave == 1) {
       dma_tile<D>(Ks[cc % 3], k + r0 * D, lane);
+    } else if (wave == 2) {
+      dma_tile<D>(Qs[cc % 3], q + r0 * D, lane);
+    } else {
       const uint32_t vb = lds_addr(Vs[cc % 4]);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
         dma16(v + (r0 + 32 * m + lane / 2) * D + col0 + 8 * (lane % 2),
               __builtin_amdgcn_readfirstlane(vb + 1024 * m));
-    } else {
-      dma_tile<D>(Qs[cc % 3], q + r0 * D, lane);
       if constexpr (kDelta) {
-        const uint32_t wb = lds_addr(Ws[cc % 3]);
-        const char* src = wrec + (size_t)cc * kRecBytes;
+        const uint32_t tb = lds_addr(Ts[cc % 3]);
+        const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
 #pragma unroll
-        for (int m = 0; m < kRecBytes / 1024; ++m)
-          dma16(src + 1024 * m + 16 * lane, __builtin_amdgcn_readfirstlane(wb + 1024 * m));
+        for (int f = 0; f < kTFrags; ++f)
+          dma16(src + f * kWave + lane, __builtin_amdgcn_readfirstlane(tb + 1024 * f));
       }
     }
   };
+  // DMA of the gates of chunk cc (wave 3)
+  auto issue_gates = [&](int cc) {
+    const size_t r0 = hbase + (size_t)cc * C;
+    if constexpr (kDelta) dma4(beta + r0 + lane, lds_addr(Bs[cc % 4]));
+    if constexpr (kGated) dma4(log_alpha + r0 + lane, lds_addr(Ls[cc % 4]));
+  };
+  // Decay tables of chunk cc from its gates (wave 2, gated mode)
+  auto tables = [&](int cc) {
+    if constexpr (kGated) {
+      const float gv = cumsum64(Ls[cc % 4], lane);
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
+      const float e = __expf(gv);
+      Gs[cc % 3][lane] = gv;
+      Es[cc % 3][lane] = e;
+      Fs[cc % 3][lane] = __expf(gC - gv);
+      BGs[cc % 3][lane] = Bs[cc % 4][lane] * e;
+    }
+  };
 
-  // Waves 0 and 1 carry rows [64 h, 64 h + 64) of this tile's state (h =
-  // wave) and both evaluate the chunk's shared terms (K S, R, U_new) from
-  // the published split state, so neither waits for the other inside a
-  // chunk.  Each role runs its own loop with the same barriers (one in the
-  // prologue, one per chunk).
-  if (wave < 2) {
-    // ================= chain (one instantiation per wave, so that which
-    // rows are this wave's is known at compile time)
-    auto chain_loop = [&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    f32x4 S[HKT];
-    Frag2<T16> sf[HKB];            // bf16 split of this wave's rows of S
+  // Each role runs its own loop with the same barriers (two in the
+  // prologue, one per chunk), so the registers one role carries from chunk
+  // to chunk are not live in the other's code.
+  if (wave == 0) {
+    // ================= chain
+    f32x4 S[NKT];
+    Frag2<T16> sf[NKB];            // bf16 split of S, as published in Sx
     const size_t sbase = (size_t)bh * D * D;
+    if (S0) {
 #pragma unroll
-    for (int t = 0; t < HKT; ++t) {
-      const int tj = h * HKT + t;
-      if (S0) {
+      for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[t][i] = S0[sbase + (size_t)(16 * tj + 4 * g + i) * D + col];
-      } else {
-        S[t] = zero4();
-      }
+        for (int i = 0; i < 4; ++i) S[tj][i] = S0[sbase + (size_t)(16 * tj + 4 * g + i) * D + col];
+    } else {
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj) S[tj] = zero4();
     }
 #pragma unroll
-    for (int b = 0; b < HKB; ++b) {
-      const int kb = h * HKB + b;
-      sf[b] = frag2_from_acc<T16>(S[2 * b], S[2 * b + 1]);
-      Sx[0][(2 * kb) * kWave + lane] = sf[b].hi;
-      Sx[0][(2 * kb + 1) * kWave + lane] = sf[b].lo;
+    for (int kb = 0; kb < NKB; ++kb) {
+      sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+      Sx[0][(2 * kb) * kWave + lane] = sf[kb].hi;
+      Sx[0][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
     }
     __syncthreads();
-
-    // Operands of the next chunk's K S, R and T R, loaded during the
-    // current chunk's state update (its inputs landed one chunk earlier)
-    Frag<T16> kf[4][NKB], tf[kTFrags];
-    f32x4 vv[4], bb[4], bg[4];
-    auto prefetch = [&](int cc) {
-      const int s3 = cc % 3;
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kf[ti][kb] = frag_row_sw<D>(Ks[s3], 16 * ti + n, 32 * kb, g);
-        if constexpr (kDelta) {
-          vv[ti] = v_acc(Vs[cc % 4], ti, g, n);
-          bb[ti] = *reinterpret_cast<const f32x4*>(tab(s3, kTabBeta) + 16 * ti + 4 * g);
-          if constexpr (kGated) bg[ti] = *reinterpret_cast<const f32x4*>(tab(s3, kTabBG) + 16 * ti + 4 * g);
-        }
-      }
-      if constexpr (kDelta) {
-#pragma unroll
-        for (int f = 0; f < kTFrags; ++f)
-          tf[f].v = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(Ws[s3])[f * kWave + lane]);
-      }
-    };
-    if constexpr (kDelta) prefetch(0);
+    __syncthreads();
 
     for (int c = 0; c < NC; ++c) {
       const T16* Kc = Ks[c % 3];
       if constexpr (kDelta) {
-        const int ws_ = c % 3;
-        Frag2<T16> so[HKB];           // the other wave's rows of the split state
+        Frag<T16> kf[4][NKB], tf[kTFrags];
+        f32x4 vv[4], bb[4], bg[4];
 #pragma unroll
-        for (int b = 0; b < HKB; ++b) {
-          const int kb = (1 - h) * HKB + b;
-          so[b].hi = Sx[c % 2][(2 * kb) * kWave + lane];
-          so[b].lo = Sx[c % 2][(2 * kb + 1) * kWave + lane];
+        for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kf[ti][kb] = frag_row_sw<D>(Kc, 16 * ti + n, 32 * kb, g);
+          vv[ti] = v_acc(Vs[c % 4], ti, g, n);
+          bb[ti] = *reinterpret_cast<const f32x4*>(Bs[c % 4] + 16 * ti + 4 * g);
+          if constexpr (kGated) bg[ti] = *reinterpret_cast<const f32x4*>(BGs[c % 3] + 16 * ti + 4 * g);
         }
+#pragma unroll
+        for (int f = 0; f < kTFrags; ++f) tf[f].v = __builtin_bit_cast(bf16x8, Ts[c % 3][f * kWave + lane]);
         f32x4 ks[4], rr[4], un[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
-        // K S over all dk rows: this wave's split rows from registers, the
-        // other wave's from LDS
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bool mine = (kb / HKB) == h;
-          const Frag2<T16>& sk = mine ? sf[kb % HKB] : so[kb % HKB];
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sk, ks[ti]);
-        }
+          for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
         // R = diag(beta) V - diag(beta gam) K S
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -676,113 +640,114 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
           for (int kb = 0; kb < 2; ++kb)
             if (kb <= ti / 2) mma_ab2(tf[tfi(ti, kb)], rf[kb], un[ti]);
         }
-        // the next chunk's operands, now that this chunk's are consumed;
-        // unconditional (the last chunk reloads itself): a conditional load
-        // would be merged into the live registers right after issue, which
-        // waits for it
-        prefetch(c + 1 < NC ? c + 1 : c);
-        // U_new for the output: wave h publishes rows [32 h, 32 h + 32)
-        {
-          const Frag2<T16> f = frag2_from_acc<T16>(un[2 * h], un[2 * h + 1]);
-          Ux[c % 2][(2 * h) * kWave + lane] = f.hi;
-          Ux[c % 2][(2 * h + 1) * kWave + lane] = f.lo;
-        }
-        // diag(gam_C / gam) U_new for the state update
         Frag2<T16> ut[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if constexpr (kGated) {
-            const float* fc = tab(ws_, kTabF);
+          const Frag2<T16> f = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
+          Ux[c % 2][(2 * kb) * kWave + lane] = f.hi;
+          Ux[c % 2][(2 * kb + 1) * kWave + lane] = f.lo;
+          ut[kb] = f;
+        }
+        Frag<T16> ktf[NKT][2];
+#pragma unroll
+        for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) ktf[tj][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n);
+        if constexpr (kGated) {
+          // S <- gam_C S + K^T diag(gam_C / gam) U_new
+          const float* fc = Fs[c % 3];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
             const f32x4 flo = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 4 * g);
             const f32x4 fhi = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 16 + 4 * g);
             const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
             const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
             ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo, shi);
-          } else {
-            ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
           }
-        }
-        // S <- gam_C S + K^T diag(gam_C / gam) U_new, for this wave's rows
-        Frag<T16> ktf[HKT][2];
+          const float decC = Es[c % 3][C - 1];
 #pragma unroll
-        for (int t = 0; t < HKT; ++t)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ktf[t][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * (h * HKT + t), g, n);
-        if constexpr (kGated) {
-          const float decC = tab(ws_, kTabGam)[C - 1];
-#pragma unroll
-          for (int t = 0; t < HKT; ++t) S[t] *= decC;
+          for (int tj = 0; tj < NKT; ++tj) S[tj] *= decC;
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int t = 0; t < HKT; ++t) mma_ab2(ktf[t][kb], ut[kb], S[t]);
+          for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
       } else {
         // S <- S + K^T V
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const Frag<T16> vf = frag_col_tr_v(Vs[c % 4], 32 * kb, g, n);
 #pragma unroll
-          for (int t = 0; t < HKT; ++t)
-            mma(frag_col_tr<D>(Kc, 32 * kb, 16 * (h * HKT + t), g, n), vf, S[t]);
+          for (int tj = 0; tj < NKT; ++tj) mma(frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n), vf, S[tj]);
         }
       }
 #pragma unroll
-      for (int b = 0; b < HKB; ++b) {
-        const int kb = h * HKB + b;
-        sf[b] = frag2_from_acc<T16>(S[2 * b], S[2 * b + 1]);
-        Sx[(c + 1) % 2][(2 * kb) * kWave + lane] = sf[b].hi;
-        Sx[(c + 1) % 2][(2 * kb + 1) * kWave + lane] = sf[b].lo;
+      for (int kb = 0; kb < NKB; ++kb) {
+        sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+        Sx[(c + 1) % 2][(2 * kb) * kWave + lane] = sf[kb].hi;
+        Sx[(c + 1) % 2][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
       }
       __syncthreads();
     }
     if (S_final) {
 #pragma unroll
-      for (int t = 0; t < HKT; ++t) {
-        const int tj = h * HKT + t;
+      for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[t][i];
-      }
+          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
     }
-    };
-    if (wave == 0) chain_loop(std::integral_constant<int, 0>{});
-    else chain_loop(std::integral_constant<int, 1>{});
   } else {
-    // ================= side waves: wave 2 row tiles 0 and 3, wave 3 tiles 1 and 2
-    // Each wave runs its own instantiation of the loop: with one shared
-    // loop the compiler cannot tell that the two waves' loads into the same
-    // registers are on exclusive paths and waits for all memory traffic
-    // (including the DMA just issued) where the paths meet.
-    auto side_loop = [&](auto t0, auto t1) {
-      constexpr int TI0 = decltype(t0)::value, TI1 = decltype(t1)::value;
-      f32x4 sc[2][4], qs[2];       // scores and Q S of the current chunk
-      auto output = [&](int cc) {
-        out_rows<D, MODE, TI0, TI1>(sc, qs, Ux[cc % 2], Vs[cc % 4], out_,
-                                    (hbase + (size_t)cc * C) * D + col, out_bf16, g, n, lane);
-      };
-      issue_chunk(0);
-      if (NC > 1) issue_chunk(1);
-      vm_wait<0>();
-      __syncthreads();
+    // ================= side waves
+    issue_chunk(0);
+    if (NC > 1) issue_chunk(1);
+    if (wave == 3)
+      for (int cc = 0; cc < 3 && cc < NC; ++cc) issue_gates(cc);
+    vm_wait<0>();
+    __syncthreads();
+    if (wave == 2) tables(0);
+    __syncthreads();
 
-      for (int c = 0; c < NC; ++c) {
-        // loads for chunk c+2 (its ring slots held chunk c-1, whose readers
-        // finished before the last barrier); they land before this chunk's
-        // barrier, so the chain can read chunk c+2's operands during c+1
-        if (c + 2 < NC) issue_chunk(c + 2);
-        if (c > 0) output(c - 1);
-        const int s3 = c % 3;
-        scores_qs<D, kGated, TI0, TI1>(Qs[s3], Ks[s3], kGated ? tab(s3, kTabG) : nullptr,
-                                       kGated ? tab(s3, kTabGam) : nullptr, Sx[c % 2], sc, qs, g,
-                                       n, lane);
-        vm_wait<0>();
-        __syncthreads();
+    f32x4 sc[2][4], qs[2];       // scores and Q S of the current chunk
+    for (int c = 0; c < NC; ++c) {
+      const bool steady = c + 3 < NC;
+      if (c > 0) {
+        const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
+        const Frag<T16>* U = Ux[(c - 1) % 2];
+        const T16* Vp = Vs[(c - 1) % 4];
+        if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+        else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+        else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
       }
-      output(NC - 1);
-    };
-    if (wave == 2) side_loop(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
-    else side_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+      if (wave == 2 && c + 1 < NC) tables(c + 1);
+      {
+        const T16* Kc = Ks[c % 3];
+        const float* gc = Gs[kGated ? c % 3 : 0];
+        const float* ec = Es[kGated ? c % 3 : 0];
+        const Frag<T16>* Sc = Sx[c % 2];
+        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+      }
+      // loads for later chunks, issued after this chunk's LDS reads
+      if (c + 2 < NC) issue_chunk(c + 2);
+      if (wave == 3 && c + 3 < NC) issue_gates(c + 3);
+      // everything issued before this chunk has landed (the newest
+      // transfers, chunk c+2 and the gates of c+3, may still be in flight)
+      if (steady) {
+        if (wave == 3) vm_wait<NDMA3>();
+        else vm_wait<NTILE>();
+      } else {
+        vm_wait<0>();
+      }
+      __syncthreads();
+    }
+    const int c = NC - 1;
+    const size_t ob0 = (hbase + (size_t)c * C) * D + col;
+    const Frag<T16>* U = Ux[c % 2];
+    const T16* Vp = Vs[c % 4];
+    if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+    else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+    else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
   }
 }
 
@@ -791,27 +756,21 @@ hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int NC = a.L / C;
   const T16* k = static_cast<const T16*>(a.k);
+  u32x4* tws = static_cast<u32x4*>(a.workspace);
   const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
   chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
-      static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v),
-      static_cast<const char*>(a.workspace), a.S0, a.out, a.S_final, a.L, BH,
-      a.out_bf16 ? 1 : 0);
+      static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v), a.log_alpha, a.beta, tws,
+      a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
   (void)NC;
   return hipGetLastError();
 }
 
-template <int D, int MODE>
-hipError_t launch_prep(const ChunkArgs& a, hipStream_t st) {
+template <int D, bool GATED>
+hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   const size_t items = (size_t)a.B * a.H * (a.L / C);
-  chunk_prep_kernel<D, MODE><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
-      static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<char*>(a.workspace), a.L);
+  t_solve_kernel<D, GATED><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
+      static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace), a.L);
   return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_prep_d(const ChunkArgs& a, hipStream_t st) {
-  return a.mode == kModeDelta ? launch_prep<D, kModeDelta>(a, st)
-                               : launch_prep<D, kModeGatedDelta>(a, st);
 }
 
 template <int D>
@@ -827,11 +786,13 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
   if (a.mode == kModeLinear) return 0;
-  return (size_t)a.B * a.H * (a.L / C) * kRecBytes;
+  return (size_t)a.B * a.H * (a.L / C) * kTFrags * kWave * sizeof(u32x4);
 }
 
-hipError_t launch_prep(const ChunkArgs& a, hipStream_t st) {
-  return a.d == 64 ? launch_prep_d<64>(a, st) : launch_prep_d<128>(a, st);
+hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
+  const bool gated = a.mode == kModeGatedDelta;
+  if (a.d == 64) return gated ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
+  return gated ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
 }
 
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st) {

@@ -39,12 +39,11 @@ struct ChunkArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 // Chunk forward: float inputs run one kernel (la_chunk.hip); bf16 inputs
-// in the delta modes first run the parallel per-chunk preparation
-// (launch_prep: T and the gate tables, into the workspace), then the chain
-// kernel (la_chunk_pipe.hip).
+// in the delta modes first solve T for every chunk (launch_tsolve, into the
+// workspace), then run the chain kernel (la_chunk_pipe.hip).
 size_t chunk_workspace_bytes(const ChunkArgs& a);
-bool chunk_needs_prep(const ChunkArgs& a);
-hipError_t launch_prep(const ChunkArgs& a, hipStream_t st);         // la_chunk_pipe.hip
+bool chunk_needs_tsolve(const ChunkArgs& a);
+hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st);       // la_chunk_pipe.hip
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);        // dispatcher
 hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st);    // la_chunk.hip
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st);   // la_chunk_pipe.hip

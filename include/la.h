@@ -118,10 +118,9 @@ typedef enum {
  *   workspace  device scratch of workspace_bytes bytes, 16-byte aligned,
  *              at least what la_chunk_workspace_bytes() reports for the same
  *              arguments; may be NULL when that is 0.  Its contents on entry
- *              are ignored and on return are unspecified.  bf16 inputs
- *              in the delta modes keep an 8 KiB record per chunk there
- *              (B*H*L/C * 8 KiB): the chunk's triangular factor T and gate
- *              tables.  Float inputs and LA_MODE_LINEAR need none.
+ *              are ignored and on return are unspecified.  The bf16 delta
+ *              modes keep each chunk's T factor there (B*H*L/C * 6 KiB);
+ *              float inputs and LA_MODE_LINEAR need none.
  *   stream     hipStream_t
  *
  * Supported: dk = dv in {64, 128}, C = 64, all dtypes, all modes.
@@ -179,7 +178,7 @@ int la_decode_step(const void* q, const void* k, const void* v,
  * Between la_profile_begin() and la_profile_end(), every kernel the library
  * launches (from any thread) is bracketed by two HIP events recorded on the
  * stream it is launched on.  la_profile_end() waits for the recorded events,
- * then reports, per kernel name ("la_prep", "la_chunk", "la_decode"), the
+ * then reports, per kernel name ("la_tsolve", "la_chunk", "la_decode"), the
  * number of launches and the summed event-to-event time in milliseconds,
  * and stops recording.  `out` is a host array of `capacity` entries; the
  * number of distinct kernels is written to *count (entries beyond capacity

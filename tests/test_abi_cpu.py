@@ -18,7 +18,7 @@ from chunkwise_gated_delta_la_amd import _lib  # noqa: E402
 
 HEADER = os.path.join(ROOT, "include", "la.h")
 OK, NULL, SHAPE, UNSUP, ALIAS, WS = 0, 1, 2, 3, 4, 6
-REC_BYTES = 8 * 1024        # workspace record per chunk (bf16 delta modes)
+TSOLVE_BYTES = 6 * 1024     # T operand fragments per chunk (bf16 delta modes)
 
 
 def _declared_functions():
@@ -93,16 +93,16 @@ def test_chunk_fwd_alias_rules():
 
 
 def test_workspace_size():
-    """One record per chunk (T and the gate tables) for bf16 inputs in the
-    delta modes; nothing for float inputs or linear attention."""
+    """One T factor per chunk for bf16 inputs in the delta modes; nothing
+    for float inputs or linear attention."""
     lib = _lib.get()
     for mode in (1, 2):
         for dtype in (1, 2):
             for (B, H, L, d) in ((1, 1, 64, 64), (2, 3, 256, 128), (1, 32, 65536, 128)):
                 rc, n = ws_bytes(lib, B=B, H=H, L=L, dk=d, dv=d, mode=mode, dtype=dtype)
-                assert rc == OK and n == B * H * (L // 64) * REC_BYTES
-    assert ws_bytes(lib, dtype=0) == (OK, 0)
+                assert rc == OK and n == B * H * (L // 64) * TSOLVE_BYTES
     assert ws_bytes(lib, mode=0) == (OK, 0)
+    assert ws_bytes(lib, dtype=0) == (OK, 0)
     assert ws_bytes(lib, L=96)[0] == SHAPE
     assert ws_bytes(lib, dk=96, dv=96)[0] == UNSUP
     assert ws_bytes(lib, mode=5)[0] == UNSUP
@@ -110,8 +110,8 @@ def test_workspace_size():
 
 
 @pytest.mark.parametrize("kw", [
-    dict(ws=None), dict(wsb=REC_BYTES - 1), dict(ws=ctypes.c_void_p(9 * P + 8)),
-    dict(B=2, wsb=REC_BYTES), dict(ws=None, wsb=P),
+    dict(ws=None), dict(wsb=TSOLVE_BYTES - 1), dict(ws=ctypes.c_void_p(9 * P + 8)),
+    dict(B=2, wsb=TSOLVE_BYTES), dict(ws=None, wsb=P),
 ])
 def test_chunk_fwd_workspace_rejects(kw):
     lib = _lib.get()
@@ -124,9 +124,8 @@ def test_chunk_fwd_workspace_alias_and_optional():
     # workspace overlapping k, or out
     assert chunk(lib, ws=ctypes.c_void_p(2 * P - 1024)) == ALIAS
     assert chunk(lib, ws=ctypes.c_void_p(7 * P - 4096)) == ALIAS
-    # float inputs and linear attention need none: a NULL workspace passes
-    # the workspace checks and the call fails on the NULL q, or the overlap,
-    # it was given instead
+    # float inputs and linear attention need none: a NULL workspace passes the
+    # workspace checks and the call fails on the NULL q it was given instead
     assert chunk(lib, ws=None, wsb=0, dtype=0, q=None) == NULL
     assert chunk(lib, ws=None, wsb=0, mode=0, out=ctypes.c_void_p(P + 128)) == ALIAS
 
