@@ -14,28 +14,43 @@
 //
 //      wave 0 (chain)  K S, R = diag(beta)(V - diag(gam) K S), U_new = T R
 //                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
-//                      U_new (publish S)
+//                      U_new (publish S, already decayed for chunk c+1 in
+//                      the copy the chain keeps)
 //      waves 1-3       output of chunk c-1 from the U_new published at the
-//                      last barrier; the decay tables of chunk c+1; masked
+//                      last barrier; the decay tables of chunk c+2; masked
 //                      decayed scores and diag(gam) Q S of chunk c for their
 //                      row tiles (wave 1: tiles 0 and 1, wave 2: tile 2,
 //                      wave 3: tile 3), kept in registers until the next
 //                      chunk; then DMA of chunk c+2 (Q, K, V, T) and of the
-//                      gates of chunk c+3
+//                      gates of chunk c+4
 //
-//    so the serial chain only ever waits for its own products.  Inputs go
-//    from HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
+//    so the serial chain only ever waits for its own products, and does as
+//    little besides them as possible: every LDS address it uses is one add
+//    of a loop-invariant lane offset to the ring slot, and the float to
+//    bf16 splits it needs take two instructions per value.  Inputs go from
+//    HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
 //    bytes land at base + 16 l) without passing through registers, issued
-//    two chunks ahead and waited for one chunk later.  Q and K tiles are
-//    stored row-major with the 16-byte units of row r XOR-permuted by r,
-//    which makes both the operand-row reads and the transposed reads
-//    conflict-free.  K^T and V^T operands are read transposed from the
-//    row-major tiles with ds_read_b64_tr_b16 (within each 16-lane group,
-//    lane i receives element i % 4 of the 4-element runs addressed by lanes
-//    i / 4 + 4 j, j = 0..3), so no transposed copy is ever stored.  The
-//    scores are computed transposed (K Q^T tiles): the accumulator layout of
-//    K Q^T is exactly the A-operand layout of Aqk = Q K^T * M * Gamma for
-//    O += Aqk U_new, so the scores never leave registers.
+//    two chunks ahead and waited for one chunk later.
+//
+// State rows.  The rows of the state (the dk index) are kept in the
+// registers in a fixed permuted order: register row p = 32 kb + 16 h +
+// 4 g + j holds dk index 32 kb + 8 g + 4 h + j.  Any order works as long as
+// every product over dk uses the same one; this one makes the operand
+// fragment of a Q or K row over dk block kb for lane group g the 8
+// contiguous columns 32 kb + 8 g .. + 7, one 16-byte read, while the
+// accumulator tiles of S are still directly the B operand of K S and Q S.
+// Only loading S0 and storing S_final see the permutation.
+//
+// Q and K tiles are stored row-major with the 16-byte units of row r
+// permuted by XOR with key(r), a bit permutation of r's low bits chosen so
+// that both the operand-row reads and the transposed reads below are free
+// of bank conflicts.  K^T and V^T operands are read transposed from the
+// row-major tiles with ds_read_b64_tr_b16 (within each 16-lane group, lane i
+// receives element i % 4 of the 4-element runs addressed by lanes
+// i / 4 + 4 j, j = 0..3), so no transposed copy is ever stored.  The scores
+// are computed transposed (K Q^T tiles): the accumulator layout of K Q^T is
+// exactly the A-operand layout of Aqk = Q K^T * M * Gamma for O += Aqk
+// U_new, so the scores never leave registers.
 //
 // Precision as in the float kernel's bf16 path: q, k, v exact, float
 // operands split into bf16 hi + lo, T a single bf16, float accumulation and
@@ -52,61 +67,92 @@ constexpr int LDT = C + 8;        // row pitch of the bf16 T tile
 constexpr int LDB = 20;           // row pitch of a float 16 x 16 block
 typedef __bf16 T16;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
+#define LA_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------- LDS access
 
-// Element offset of (r, c) in a C x D bf16 tile whose 16-byte units are
-// permuted by XOR with (r mod D / 8).
-template <int D>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int U = D / 8;
-  return r * D + ((((c >> 3) ^ (r & (U - 1)))) << 3) + (c & 7);
+// Loads at a byte offset from an LDS array.
+template <typename V>
+__device__ __forceinline__ V lds_ld(const void* base, uint32_t off) {
+  return *(const LA_LDS V*)((const LA_LDS char*)base + off);
 }
 
-// Operand row R of the swizzled tile over columns c0 + kidx(g, j).
-template <int D>
-__device__ __forceinline__ Frag<T16> frag_row_sw(const T16* tile, int R, int c0, int g) {
-  Frag<T16> f;
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(tile + swz<D>(R, c0 + 4 * g));
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(tile + swz<D>(R, c0 + 16 + 4 * g));
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
+template <typename V>
+__device__ __forceinline__ void lds_st(void* base, uint32_t off, const V& x) {
+  *(LA_LDS V*)((LA_LDS char*)base + off) = x;
 }
 
-__device__ __forceinline__ bf16x4 read_tr(const T16* p) {
+__device__ __forceinline__ bf16x4 read_tr(const void* base, uint32_t off) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (s16x4 __attribute__((address_space(3)))*)(p));
+      (LA_LDS s16x4*)((const LA_LDS char*)base + off));
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Transposed operand from the swizzled row-major tile: 8 values
-// tile[r0 + kidx(g, j)][c0 + n] for lane (g, n), i.e. column c0 + n of the
-// tile as an operand over the rows r0 .. r0 + 31.  Lane k of group g
-// addresses row r0 + 4 g + k / 4 (+ 16), columns c0 + 4 (k % 4) .. + 3.
+// Unit key of row r of a C x D tile: logical 16-byte unit u of the row is
+// stored at position u ^ key(r).  Operand-row reads (16 lanes on 16
+// consecutive rows, one unit each) need key to be one-to-one on those rows;
+// transposed reads (16 lanes on 4 consecutive rows 4 g .. 4 g + 3, units
+// 4 kb + 0..3) need its bits above the unit's low two to follow r mod 4.
 template <int D>
-__device__ __forceinline__ Frag<T16> frag_col_tr(const T16* tile, int r0, int c0, int g, int n) {
+__device__ __forceinline__ constexpr int swz_key(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset of logical unit u of row r.
+template <int D>
+__device__ __forceinline__ constexpr uint32_t unit_off(int r, int u) {
+  return (uint32_t)(2 * r * D + ((u ^ swz_key<D>(r)) << 4));
+}
+
+// dk index held by register row p of the state.
+__device__ __forceinline__ constexpr int dk_of_row(int p) {
+  return (p & ~31) | ((p & 12) << 1) | ((p & 16) >> 2) | (p & 3);
+}
+
+// Operand row R over dk block kb: the unit 4 kb + g (the key depends only on
+// R's low four bits, so 16-row steps are a constant 32 D bytes).
+template <int D>
+__device__ __forceinline__ Frag<T16> frag_row_at(const void* tile, uint32_t off) {
   Frag<T16> f;
-  const int c = c0 + 4 * (n & 3);
-  const bf16x4 a = read_tr(tile + swz<D>(r0 + 4 * g + (n >> 2), c));
-  const bf16x4 b = read_tr(tile + swz<D>(r0 + 16 + 4 * g + (n >> 2), c));
+  f.v = lds_ld<bf16x8>(tile, off);
+  return f;
+}
+
+// Transposed K operand over token rows r0 + kidx(g, j) for state tile
+// tj = 2 kbs + h: lane (g, n) gets K[r0 + kidx(g, j)][dk_of_row(16 tj + n)].
+// Lane k of group g addresses row r0 + 4 g + k / 4 (+ 16) at the four
+// columns 32 kbs + 8 (k % 4) + 4 h .. + 3, so lane n receives element n % 4
+// of the runs of lanes n / 4 + 4 j: column 32 kbs + 8 (n / 4) + 4 h + n % 4.
+// tr_off gives the lane's offset for r0 = 0, h = 0; r0 adds 2 D r0 bytes,
+// h adds 8.
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(int g, int n, int kbs) {
+  return unit_off<D>(4 * g + (n >> 2), 4 * kbs + (n & 3));
+}
+
+__device__ __forceinline__ Frag<T16> frag_tr_at(const void* tile, uint32_t off, uint32_t half) {
+  Frag<T16> f;
+  const bf16x4 a = read_tr(tile, off);
+  const bf16x4 b = read_tr(tile, off + half);
   f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return f;
 }
 
-// The same over a plain C x 16 bf16 tile (this workgroup's V columns).
-__device__ __forceinline__ Frag<T16> frag_col_tr_v(const T16* tile, int r0, int g, int n) {
-  Frag<T16> f;
-  const int c = 4 * (n & 3);
-  const bf16x4 a = read_tr(tile + (r0 + 4 * g + (n >> 2)) * 16 + c);
-  const bf16x4 b = read_tr(tile + (r0 + 16 + 4 * g + (n >> 2)) * 16 + c);
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
+// Column n of a plain C x 16 bf16 tile (this workgroup's V columns) as an
+// operand over rows r0 .. r0 + 31.
+__device__ __forceinline__ Frag<T16> frag_col_tr_v(const void* tile, int r0, int g, int n) {
+  const uint32_t off = (uint32_t)(((r0 + 4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
+  return frag_tr_at(tile, off, 16 * 16 * 2);
 }
 
-// V in accumulator layout for rows 16 ti + 4 g + i, column n.
-__device__ __forceinline__ f32x4 v_acc(const T16* tile, int ti, int g, int n) {
-  const bf16x4 a = read_tr(tile + (16 * ti + 4 * g + (n >> 2)) * 16 + 4 * (n & 3));
+// V in accumulator layout for rows 16 ti + 4 g + i, column n: off is the
+// lane's byte offset for ti = 0 (vacc_off), ti adds 512 bytes.
+__device__ __forceinline__ uint32_t vacc_off(int g, int n) {
+  return (uint32_t)(((4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
+}
+__device__ __forceinline__ f32x4 v_acc_at(const void* tile, uint32_t off) {
+  const bf16x4 a = read_tr(tile, off);
   return f32x4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
 }
 
@@ -152,17 +198,19 @@ __device__ __forceinline__ constexpr int bid(int i, int j) { return i * (i + 1) 
 // outstanding retires everything but the last N issued.
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  return (uint32_t)(uintptr_t)(const LA_LDS void*)p;
 }
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
+// Issued from a wave-uniform base address plus a 32-bit lane offset
+// (scalar-base addressing: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 template <int N>
@@ -172,19 +220,27 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 // DMA of one C x D tile into the swizzled layout by one wave; each
-// instruction moves 1 KiB = 512 elements.
+// instruction moves 1 KiB = 512 elements.  Instruction m of lane l stores
+// LDS bytes 1024 m + 16 l: row r, position ul, i.e. logical unit
+// ul ^ key(r); off[m] is that unit's byte offset in the source rows.
 template <int D>
-__device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows, int lane) {
-  constexpr int RB = 2 * D;                     // bytes per row
-  constexpr int NI = C * RB / 1024;             // instructions per tile
-  const uint32_t base = lds_addr(dst);
+__device__ __forceinline__ void dma_tile_offsets(uint32_t (&off)[C * 2 * D / 1024], int lane) {
+  constexpr int RB = 2 * D;
 #pragma unroll
-  for (int m = 0; m < NI; ++m) {
+  for (int m = 0; m < C * RB / 1024; ++m) {
     const int byte = 1024 * m + 16 * lane;
     const int r = byte / RB, ul = (byte % RB) / 16;
-    const int ug = ul ^ (r & (D / 8 - 1));
-    dma16(src_rows + r * D + ug * 8, __builtin_amdgcn_readfirstlane(base + 1024 * m));
+    off[m] = (uint32_t)(r * RB + ((ul ^ swz_key<D>(r)) << 4));
   }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows,
+                                         const uint32_t (&off)[C * 2 * D / 1024]) {
+  const uint32_t base = lds_addr(dst);
+#pragma unroll
+  for (int m = 0; m < C * 2 * D / 1024; ++m)
+    dma16s(src_rows, off[m], __builtin_amdgcn_readfirstlane(base + 1024 * m));
 }
 
 // ---------------------------------------------------------------- T solve
@@ -364,29 +420,32 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
     }
 }
 
+
 // ---------------------------------------------------------------- side roles
 
 // Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
 // registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
 // Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
-// gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].
+// gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].  roff[kb] is the lane's
+// byte offset of operand row n over dk block kb in a Q or K tile.
 template <int D, bool GATED, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
                                           const float* esc, const Frag<T16>* Sx,
-                                          f32x4 (&sc)[2][4], f32x4 (&qs)[2], int g, int n,
-                                          int lane) {
+                                          const uint32_t (&roff)[D / 32], f32x4 (&sc)[2][4],
+                                          f32x4 (&qs)[2], int g, int n, int lane) {
   constexpr int NKB = D / 32;
   constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
+  constexpr uint32_t kRows16 = 32 * D;          // bytes of 16 tile rows
   Frag<T16> qf[NTI][NKB], kf[NT][NKB];
   Frag2<T16> sx[NKB];
 #pragma unroll
   for (int u = 0; u < NTI; ++u)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_sw<D>(Qt, 16 * (u ? TI1 : TI0) + n, 32 * kb, g);
+    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_at<D>(Qt, roff[kb] + kRows16 * (u ? TI1 : TI0));
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_sw<D>(Kt, 16 * t + n, 32 * kb, g);
+    for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_at<D>(Kt, roff[kb] + kRows16 * t);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     sx[kb].hi = Sx[(2 * kb) * kWave + lane];
@@ -429,18 +488,19 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
 }
 
 // Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
-// (U_new = V in linear mode).
+// (U_new = V in linear mode), into o[u] (row tile u ? TI1 : TI0, accumulator
+// layout).  U_new arrives in float (Uf, accumulator layout, tile ti at
+// ti * 64 + lane) and is split here.
 template <int D, int MODE, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
-                                         const Frag<T16>* Ux, const T16* Vt, void* out_,
-                                         size_t ob0, int out_bf16, int g, int n, int lane) {
+                                         const f32x4* Uf, const T16* Vt, f32x4 (&o)[2],
+                                         int g, int n, int lane) {
   constexpr bool kDelta = MODE != kModeLinear;
   Frag2<T16> uf[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     if constexpr (kDelta) {
-      uf[kb].hi = Ux[(2 * kb) * kWave + lane];
-      uf[kb].lo = Ux[(2 * kb + 1) * kWave + lane];
+      uf[kb] = frag2_from_acc<T16>(Uf[(2 * kb) * kWave + lane], Uf[(2 * kb + 1) * kWave + lane]);
     } else {
       uf[kb].hi = frag_col_tr_v(Vt, 32 * kb, g, n);
     }
@@ -448,27 +508,37 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&
 #pragma unroll
   for (int u = 0; u < NTI; ++u) {
     const int ti = u ? TI1 : TI0;
-    f32x4 o = qs[u];
+    o[u] = qs[u];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (2 * kb > ti) continue;
       const Frag2<T16> a = frag2_from_acc<T16>(sc[u][2 * kb], sc[u][2 * kb + 1]);
       if constexpr (kDelta) {
-        mma_a2b2(a, uf[kb], o);
+        mma_a2b2(a, uf[kb], o[u]);
       } else {
-        mma(a.lo, uf[kb].hi, o);
-        mma(a.hi, uf[kb].hi, o);
+        mma(a.lo, uf[kb].hi, o[u]);
+        mma(a.hi, uf[kb].hi, o[u]);
       }
     }
+  }
+}
+
+// Store of the rows out_rows produced.
+template <int D, int NTI, int TI0, int TI1>
+__device__ __forceinline__ void store_rows(const f32x4 (&o)[2], void* out_, size_t ob0,
+                                           int out_bf16, int g) {
+#pragma unroll
+  for (int u = 0; u < NTI; ++u) {
+    const int ti = u ? TI1 : TI0;
     const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
     if (out_bf16) {
       T16* out = static_cast<T16*>(out_);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[e];
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[u][e];
     } else {
       float* out = static_cast<float*>(out_);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[e];
+      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[u][e];
     }
   }
 }
@@ -492,7 +562,10 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
   constexpr int NCT = D / 16;                    // column tiles per head
   constexpr int TILE = C * D;                    // elements of a Q / K tile
+  constexpr uint32_t kTileB = 2 * TILE;          // bytes of a Q / K tile
+  constexpr uint32_t kRows16 = 32 * D;           // bytes of 16 tile rows
   constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
+  constexpr int NG = 5;                          // gate ring depth (DMA 4 ahead)
   // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha
   constexpr int NDMA3 = 2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0);
 
@@ -500,14 +573,14 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Vs[4][C * 16];
   __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTFrags * kWave : 1];
-  __shared__ __attribute__((aligned(16))) float Ls[kGated ? 4 : 1][C];   // log alpha
-  __shared__ __attribute__((aligned(16))) float Bs[kDelta ? 4 : 1][C];   // beta
+  __shared__ __attribute__((aligned(16))) float Ls[kGated ? NG : 1][C];  // log alpha
+  __shared__ __attribute__((aligned(16))) float Bs[kDelta ? NG : 1][C];  // beta
   __shared__ __attribute__((aligned(16))) float Gs[kGated ? 3 : 1][C];   // g (in-chunk cumsum)
   __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
-  __shared__ __attribute__((aligned(16))) Frag<T16> Ux[2][4 * kWave];
+  __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -533,44 +606,57 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int NC = L / C;
   const u32x4* tw = tws + (size_t)bh * NC * (kTFrags * kWave);
 
+  // lane offsets of operand row n over each dk block in a Q or K tile
+  uint32_t roff[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) roff[kb] = unit_off<D>(n, 4 * kb + g);
+
+  // Lane offsets of the DMA sources (loop-invariant): a Q or K tile for
+  // waves 1 and 2; for wave 3 the two V instructions (rows 32 m + l / 2,
+  // columns col0 + 8 (l % 2) ..) and the T fragments.
+  uint32_t doff[NTILE];
+  dma_tile_offsets<D>(doff, lane);
+  uint32_t voff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) voff[m] = (uint32_t)(((32 * m + lane / 2) * D + 8 * (lane % 2)) * 2);
+
   // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
   auto issue_chunk = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
     if (wave == 1) {
-      dma_tile<D>(Ks[cc % 3], k + r0 * D, lane);
+      dma_tile<D>(Ks[cc % 3], k + r0 * D, doff);
     } else if (wave == 2) {
-      dma_tile<D>(Qs[cc % 3], q + r0 * D, lane);
+      dma_tile<D>(Qs[cc % 3], q + r0 * D, doff);
     } else {
       const uint32_t vb = lds_addr(Vs[cc % 4]);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        dma16(v + (r0 + 32 * m + lane / 2) * D + col0 + 8 * (lane % 2),
-              __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+        dma16s(v + r0 * D + col0, voff[m], __builtin_amdgcn_readfirstlane(vb + 1024 * m));
       if constexpr (kDelta) {
         const uint32_t tb = lds_addr(Ts[cc % 3]);
         const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
 #pragma unroll
         for (int f = 0; f < kTFrags; ++f)
-          dma16(src + f * kWave + lane, __builtin_amdgcn_readfirstlane(tb + 1024 * f));
+          dma16s(src, (uint32_t)((f * kWave + lane) * 16), __builtin_amdgcn_readfirstlane(tb + 1024 * f));
       }
     }
   };
   // DMA of the gates of chunk cc (wave 3)
   auto issue_gates = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
-    if constexpr (kDelta) dma4(beta + r0 + lane, lds_addr(Bs[cc % 4]));
-    if constexpr (kGated) dma4(log_alpha + r0 + lane, lds_addr(Ls[cc % 4]));
+    if constexpr (kDelta) dma4s(beta + r0, (uint32_t)lane * 4, lds_addr(Bs[cc % NG]));
+    if constexpr (kGated) dma4s(log_alpha + r0, (uint32_t)lane * 4, lds_addr(Ls[cc % NG]));
   };
   // Decay tables of chunk cc from its gates (wave 2, gated mode)
   auto tables = [&](int cc) {
     if constexpr (kGated) {
-      const float gv = cumsum64(Ls[cc % 4], lane);
+      const float gv = cumsum64(Ls[cc % NG], lane);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
       const float e = __expf(gv);
       Gs[cc % 3][lane] = gv;
       Es[cc % 3][lane] = e;
       Fs[cc % 3][lane] = __expf(gC - gv);
-      BGs[cc % 3][lane] = Bs[cc % 4][lane] * e;
+      BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
     }
   };
 
@@ -586,7 +672,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[tj][i] = S0[sbase + (size_t)(16 * tj + 4 * g + i) * D + col];
+        for (int i = 0; i < 4; ++i)
+          S[tj][i] = S0[sbase + (size_t)dk_of_row(16 * tj + 4 * g + i) * D + col];
     } else {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj) S[tj] = zero4();
@@ -599,29 +686,105 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     }
     __syncthreads();
     __syncthreads();
+    // S is carried decayed by the coming chunk's gam_C: the accumulator of
+    // that chunk's update, while sf (and Sx) hold the undecayed state.
+    if constexpr (kGated) {
+      const float g0 = Es[0][C - 1];
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj) S[tj] *= g0;
+    }
 
+    // loop-invariant lane offsets
+    uint32_t ktr[NKT / 2];
+#pragma unroll
+    for (int kbs = 0; kbs < NKT / 2; ++kbs) ktr[kbs] = tr_off<D>(g, n, kbs);
+    const uint32_t voff = vacc_off(g, n);
+    const uint32_t toff = (uint32_t)lane * 16;
+    const uint32_t goff = (uint32_t)(4 * g) * 4;        // tables: row 16 ti + 4 g
+    const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf slots
+
+    // Ring slot offsets go through readfirstlane: opaque to the loop
+    // optimiser, which would otherwise turn each lane address into an
+    // induction variable of its own plus a wrap correction (two adds per
+    // address and a register each) instead of one add to a scalar.
+    auto slot = [](int c, int depth, uint32_t bytes) {
+      return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(c % depth) * bytes));
+    };
     for (int c = 0; c < NC; ++c) {
-      const T16* Kc = Ks[c % 3];
+      const uint32_t kslot = slot(c, 3, kTileB);
+      // gam_C of chunk c+1 (its tables are two chunks ahead), read first:
+      // the split at the end of the chunk waits for it.  The load is
+      // unconditional, from a clamped slot, so that no branch splits the
+      // loop body.
+      float gn = 1.f;
+      if constexpr (kGated) {
+        const float e = lds_ld<float>(Es, slot(c + 1 < NC ? c + 1 : c, 3, C * 4) + (C - 1) * 4);
+        gn = c + 1 < NC ? e : 1.f;
+      }
       if constexpr (kDelta) {
+        const uint32_t vslot = slot(c, 4, C * 16 * 2);
+        const uint32_t gslot = slot(c, NG, C * 4);
+        const uint32_t tslot = slot(c, 3, C * 4);
         Frag<T16> kf[4][NKB], tf[kTFrags];
         f32x4 vv[4], bb[4], bg[4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t a = kslot + roff[kb];
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) kf[ti][kb] = frag_row_sw<D>(Kc, 16 * ti + n, 32 * kb, g);
-          vv[ti] = v_acc(Vs[c % 4], ti, g, n);
-          bb[ti] = *reinterpret_cast<const f32x4*>(Bs[c % 4] + 16 * ti + 4 * g);
-          if constexpr (kGated) bg[ti] = *reinterpret_cast<const f32x4*>(BGs[c % 3] + 16 * ti + 4 * g);
+          for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = frag_row_at<D>(Ks, a + kRows16 * ti);
         }
+        {
+          const uint32_t a = vslot + voff;
 #pragma unroll
-        for (int f = 0; f < kTFrags; ++f) tf[f].v = __builtin_bit_cast(bf16x8, Ts[c % 3][f * kWave + lane]);
+          for (int ti = 0; ti < 4; ++ti) vv[ti] = v_acc_at(Vs, a + 512 * ti);
+        }
+        {
+          const uint32_t a = gslot + goff;
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) bb[ti] = lds_ld<f32x4>(Bs, a + 64 * ti);
+        }
+        if constexpr (kGated) {
+          const uint32_t a = tslot + goff;
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) bg[ti] = lds_ld<f32x4>(BGs, a + 64 * ti);
+        }
+        {
+          const uint32_t a = slot(c, 3, kTFrags * kWave * 16) + toff;
+#pragma unroll
+          for (int f = 0; f < kTFrags; ++f) tf[f].v = lds_ld<bf16x8>(Ts, a + f * kWave * 16);
+        }
+        // Everything above is read before any product starts; the operands
+        // of the state update (K^T, and the gate ratios) are read while the
+        // K S products run, one read per MFMA, so that no LDS latency is
+        // exposed after the first.
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 ks[4], rr[4], un[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
+        // row tile outer: each ks[ti] is final early, so R and its split for
+        // that tile can proceed under the remaining products
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
+          for (int kb = 0; kb < NKB; ++kb) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
+        Frag<T16> ktf[NKT][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int tj = 0; tj < NKT; ++tj)
+            ktf[tj][kb] = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
+        f32x4 fr[4];
+        if constexpr (kGated) {
+          const uint32_t a = tslot + goff;
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) fr[ti] = lds_ld<f32x4>(Fs, a + 64 * ti);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * NKB * 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // R = diag(beta) V - diag(beta gam) K S
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -640,52 +803,63 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
           for (int kb = 0; kb < 2; ++kb)
             if (kb <= ti / 2) mma_ab2(tf[tfi(ti, kb)], rf[kb], un[ti]);
         }
-        Frag2<T16> ut[2];
+        // U_new in float for the output waves
+        {
+          const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const Frag2<T16> f = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
-          Ux[c % 2][(2 * kb) * kWave + lane] = f.hi;
-          Ux[c % 2][(2 * kb + 1) * kWave + lane] = f.lo;
-          ut[kb] = f;
+          for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(Uf, a + ti * kWave * 16, un[ti]);
         }
-        Frag<T16> ktf[NKT][2];
-#pragma unroll
-        for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ktf[tj][kb] = frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n);
+        // operand of the state update: diag(gam_C / gam) U_new (gated), U_new
+        Frag2<T16> ut[2];
         if constexpr (kGated) {
-          // S <- gam_C S + K^T diag(gam_C / gam) U_new
-          const float* fc = Fs[c % 3];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const f32x4 flo = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 4 * g);
-            const f32x4 fhi = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 16 + 4 * g);
+            const f32x4 flo = fr[2 * kb], fhi = fr[2 * kb + 1];
             const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
             const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
             ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo, shi);
           }
-          const float decC = Es[c % 3][C - 1];
+        } else {
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) S[tj] *= decC;
+          for (int kb = 0; kb < 2; ++kb) ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
         }
+        // S += K^T ut (S is already decayed by gam_C); state tile outer, so
+        // the split of each finished pair of tiles overlaps the products of
+        // the next
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
+          for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
       } else {
         // S <- S + K^T V
+        const uint32_t vslot = slot(c, 4, C * 16 * 2);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const Frag<T16> vf = frag_col_tr_v(Vs[c % 4], 32 * kb, g, n);
+          const Frag<T16> vf = frag_col_tr_v((const char*)Vs + vslot, 32 * kb, g, n);
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) mma(frag_col_tr<D>(Kc, 32 * kb, 16 * tj, g, n), vf, S[tj]);
+          for (int tj = 0; tj < NKT; ++tj) {
+            const Frag<T16> kt = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
+            mma(kt, vf, S[tj]);
+          }
         }
       }
+      // publish the split of S_{c+1}; in gated mode the split consumes S and
+      // the state carried on is S_{c+1} decayed by gam_C of chunk c+1
+      {
+        const uint32_t a = slot(c + 1, 2, 2 * NKB * kWave * 16) + xoff;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-        Sx[(c + 1) % 2][(2 * kb) * kWave + lane] = sf[kb].hi;
-        Sx[(c + 1) % 2][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
+        for (int kb = 0; kb < NKB; ++kb) {
+          if constexpr (kGated) {
+            const f32x4 d0 = S[2 * kb] * gn, d1 = S[2 * kb + 1] * gn;
+            sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+            S[2 * kb] = d0;
+            S[2 * kb + 1] = d1;
+          } else {
+            sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+          }
+          lds_st<bf16x8>(Sx, a + (2 * kb) * kWave * 16, sf[kb].hi.v);
+          lds_st<bf16x8>(Sx, a + (2 * kb + 1) * kWave * 16, sf[kb].lo.v);
+        }
       }
       __syncthreads();
     }
@@ -694,45 +868,60 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S_final[sbase + (size_t)(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+          S_final[sbase + (size_t)dk_of_row(16 * tj + 4 * g + i) * D + col] = S[tj][i];
     }
   } else {
     // ================= side waves
     issue_chunk(0);
     if (NC > 1) issue_chunk(1);
     if (wave == 3)
-      for (int cc = 0; cc < 3 && cc < NC; ++cc) issue_gates(cc);
+      for (int cc = 0; cc < NG - 1 && cc < NC; ++cc) issue_gates(cc);
     vm_wait<0>();
     __syncthreads();
-    if (wave == 2) tables(0);
+    if (wave == 2) {
+      tables(0);
+      if (NC > 1) tables(1);
+    }
     __syncthreads();
 
     f32x4 sc[2][4], qs[2];       // scores and Q S of the current chunk
+    f32x4 ot[2];                 // output rows of the previous chunk
     for (int c = 0; c < NC; ++c) {
-      const bool steady = c + 3 < NC;
+      const bool steady = c + NG - 1 < NC;      // every DMA of this step issued
+      // Loads for later chunks first: the slots they fill held chunk c-1
+      // (Q, K, T, gates) or c-2 (V), all last read before the barrier that
+      // opened this chunk, so the transfers get two chunks' time to land.
+      if (c + 2 < NC) issue_chunk(c + 2);
+      if (wave == 3 && c + NG - 1 < NC) issue_gates(c + NG - 1);
       if (c > 0) {
-        const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
-        const Frag<T16>* U = Ux[(c - 1) % 2];
+        const f32x4* U = Uf[kDelta ? (c - 1) % 2 : 0];
         const T16* Vp = Vs[(c - 1) % 4];
-        if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
-        else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
-        else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+        const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
+        if (wave == 1) {
+          out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
+          store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g);
+        } else if (wave == 2) {
+          out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
+          store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g);
+        } else {
+          out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
+          store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g);
+        }
       }
-      if (wave == 2 && c + 1 < NC) tables(c + 1);
+      if (wave == 2 && c + 2 < NC) tables(c + 2);
       {
         const T16* Kc = Ks[c % 3];
         const float* gc = Gs[kGated ? c % 3 : 0];
         const float* ec = Es[kGated ? c % 3 : 0];
         const Frag<T16>* Sc = Sx[c % 2];
-        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
-        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
-        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, sc, qs, g, n, lane);
+        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
+        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
+        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
       }
-      // loads for later chunks, issued after this chunk's LDS reads
-      if (c + 2 < NC) issue_chunk(c + 2);
-      if (wave == 3 && c + 3 < NC) issue_gates(c + 3);
-      // everything issued before this chunk has landed (the newest
-      // transfers, chunk c+2 and the gates of c+3, may still be in flight)
+      // Everything issued before this chunk has landed.  Loads complete in
+      // issue order, so while any earlier transfer is outstanding all N of
+      // this chunk's are too: at most N outstanding (this chunk's output
+      // stores, issued later, included) means the earlier ones are done.
       if (steady) {
         if (wave == 3) vm_wait<NDMA3>();
         else vm_wait<NTILE>();
@@ -743,11 +932,18 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     }
     const int c = NC - 1;
     const size_t ob0 = (hbase + (size_t)c * C) * D + col;
-    const Frag<T16>* U = Ux[c % 2];
+    const f32x4* U = Uf[kDelta ? c % 2 : 0];
     const T16* Vp = Vs[c % 4];
-    if (wave == 1) out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
-    else if (wave == 2) out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
-    else out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, out_, ob0, out_bf16, g, n, lane);
+    if (wave == 1) {
+      out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
+      store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g);
+    } else if (wave == 2) {
+      out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
+      store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g);
+    } else {
+      out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
+      store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g);
+    }
   }
 }
 

@@ -194,14 +194,24 @@ __device__ __forceinline__ void stage_tile(T* lds, const T* __restrict__ src, si
   }
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Lanes of x moved by a DPP pattern; lanes without a source (or outside
+// row_mask) read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, in registers: a
+// Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2, 4, 8), then
+// lane 15 of rows 0 and 2 added to rows 1 and 3 (row_bcast:15) and lane 31
+// added to rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+  x += dpp_or_zero<0x111, 0xf>(x);
+  x += dpp_or_zero<0x112, 0xf>(x);
+  x += dpp_or_zero<0x114, 0xf>(x);
+  x += dpp_or_zero<0x118, 0xf>(x);
+  x += dpp_or_zero<0x142, 0xa>(x);
+  x += dpp_or_zero<0x143, 0xc>(x);
   return x;
 }
 
@@ -281,17 +291,33 @@ __device__ __forceinline__ Frag2<T> frag2_from_acc_scaled(const f32x4& lo, const
 }
 
 // bf16 specialisations: two values are rounded per instruction
-// (v_cvt_pk_bf16_f32) and the remainders x - hi are formed from the packed
-// pair, 3 instructions per value.  Same roundings as Frag2::set.
+// (v_cvt_pk_bf16_f32), and each remainder x - hi is one bf16 dot product
+// of the packed pair with (-1, 0) or (0, -1) accumulated onto x
+// (v_dot2c_f32_bf16): the product is exact and x - hi is representable, so
+// the remainder is exact, 2 instructions per value in all.  Same roundings
+// as Frag2::set.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// The two selector pairs, held in scalar registers.  Written as constants,
+// (-1, 0) would be folded into the inline constant -1.0, which the
+// instruction reads as the 32-bit pattern 0xbf800000, i.e. the pair (0, -1).
+struct SplitSel {
+  uint32_t lo_half, hi_half;
+};
+__device__ __forceinline__ SplitSel split_sel() {
+  uint32_t a = 0x0000bf80u, b = 0xbf800000u;
+  asm("" : "+s"(a), "+s"(b));
+  return SplitSel{a, b};
+}
+
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-  const float h0 = __builtin_bit_cast(float, h << 16);
-  const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
-  hi = h;
+  const SplitSel s = split_sel();
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, s.lo_half), h, x0, false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, s.hi_half), h, x1, false);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+  hi = __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ Frag2<__bf16> frag2_pack(float a0, float a1, float a2, float a3,
