@@ -31,6 +31,8 @@ Parity status of each function is stated in its module header.
 """
 
 from .recurrence import (  # noqa: F401
+    ERASE_MODES,
+    GATED_MODES,
     MODES,
     decode_steps,
     recurrent_fwd,

@@ -38,19 +38,25 @@ gives a unit lower-triangular system for the rows u_r:
     S' = gamma_C S + (diag(gamma_C / gamma) K)^T U_new
 
 With alpha = 1 (``delta``) every gamma is 1 and this is the UT/WY form; in
-``linear`` mode u_r = v_r and the system disappears.  The chunk's state map
+``linear`` and ``gated_linear`` mode u_r = v_r and the system disappears:
+
+    O = diag(gamma) Q S + (Q K^T * M * Gamma) V
+    S' = gamma_C S + (diag(gamma_C / gamma) K)^T V
+
+(``linear``: every gamma and Gamma entry is 1).  The chunk's state map
 for V = 0 is ``S' = P S`` with ``P = gamma_C I - (diag(gamma_C/gamma) K)^T W``,
 equal to the product of the per-token factors alpha_r (I - beta_r k_r k_r^T)
 (latest factor on the left).
 
 Parity status: pinned -- to the token recurrence for C = 1, C = L and ragged
-chunkings in every mode, T to a library triangular solve, P to the explicit
-product of dk x dk factors (tests/test_oracle_pins.py).
+chunkings in every mode (and through it to the pins of each mode), T to a
+library triangular solve, P to the explicit product of dk x dk factors
+(tests/test_oracle_pins.py).
 """
 
 import numpy as np
 
-from .recurrence import MODES
+from .recurrence import ERASE_MODES, GATED_MODES, MODES
 
 
 def parallel_masked_linear(q, k, v):
@@ -86,14 +92,14 @@ def forward_substitution_inverse(A):
 
 def _gates(log_alpha, beta, n, mode, lead_shape):
     """Per-row log-decay and write strength for one chunk of n rows."""
-    if mode == "gated_delta":
+    if mode in GATED_MODES:
         la = np.asarray(log_alpha, dtype=np.float64)
     else:
         la = np.zeros(lead_shape + (n,))
-    if mode == "linear":
-        be = np.ones(lead_shape + (n,))
-    else:
+    if mode in ERASE_MODES:
         be = np.asarray(beta, dtype=np.float64)
+    else:
+        be = np.ones(lead_shape + (n,))
     return la, be
 
 
@@ -168,11 +174,18 @@ def chunkwise_fwd(q, k, v, log_alpha, beta, S0, mode, C):
         e = min(s + C, L)
         Q, K, V = q[:, :, s:e], k[:, :, s:e], v[:, :, s:e]
         n = e - s
-        lower = np.tril(np.ones((n, n)))
         QKt = np.matmul(Q, np.swapaxes(K, -1, -2))
-        if mode == "linear":
-            o[:, :, s:e] = np.matmul(Q, S) + np.matmul(QKt * lower, V)
-            S = S + np.matmul(np.swapaxes(K, -1, -2), V)
+        if mode not in ERASE_MODES:
+            la, _ = _gates(None if log_alpha is None else log_alpha[:, :, s:e],
+                           None, n, mode, K.shape[:-2])
+            g = np.cumsum(la, axis=-1)
+            gamma, Gamma = _decay(g)
+            o[:, :, s:e] = (gamma[..., :, None] * np.matmul(Q, S)
+                            + np.matmul(QKt * Gamma, V))
+            gC = g[..., -1:]
+            Kt = np.exp(gC - g)[..., :, None] * K
+            S = (np.exp(gC)[..., None] * S
+                 + np.matmul(np.swapaxes(Kt, -1, -2), V))
             continue
         ut = ut_transform(K, V,
                           None if log_alpha is None else log_alpha[:, :, s:e],

@@ -10,7 +10,8 @@ query is ``S^T q`` (a length-dv vector).  [CS336 "朴素线性注意力"] descri
 [LA-OV "Lightning Attention"] writes the same sum as ``k_j^T v_j`` with row
 vectors.
 
-Update rules, one token at a time (all three are special cases of the last):
+Update rules, one token at a time (the first three are special cases of
+``gated_delta``, the first of ``gated_linear``):
 
 * ``linear``      S <- S + k v^T.  Plain causal linear attention without
   feature map or normaliser: [HA-1 "线性注意力"] drops the denominator as
@@ -30,6 +31,13 @@ Update rules, one token at a time (all three are special cases of the last):
   GDN"].  The decay multiplies the old state and the erase term, not the new
   write.  Evaluating ``k^T S`` first keeps the step O(dk dv) instead of
   forming the dk x dk matrix [CS336 "继续改进：GDN"].
+* ``gated_linear`` S <- alpha S + k v^T: plain linear attention whose state
+  is multiplied by a scalar gate before each write -- the weight decay by
+  which Mamba2 forgets the past [HA-1 "Gated DeltaNet"], a gate on the naive
+  linear attention's state update that costs a constant factor [CS336
+  "继续改进：Mamba"].  No erase and no beta.  Reading taken: the gate is per
+  token, alpha = exp(log_alpha) as in ``gated_delta`` (a constant gate is
+  the special case of equal log_alpha).
 
 Output.  ``o_t = S_t^T q_t`` with the state *after* token t's update, so a
 token sees itself: the causal mask of [LA-OV "快速预览"] includes the diagonal
@@ -40,7 +48,10 @@ Gates are scalars per (batch, head, token).  No scaling (1/sqrt(dk)), feature
 map, denominator or output norm is applied inside the op.
 
 Parity status: pinned.  ``linear`` is pinned to the masked parallel form
-(QK^T * M) V and to the pages' four-token example; ``delta`` and
+(QK^T * M) V and to the pages' four-token example; ``gated_linear`` to the
+same sum with each term weighted by the product of the gates after it
+(evaluated by explicit loops), to ``linear`` at alpha = 1, to its alpha -> 0
+closed form and to a hand-expanded scalar case; ``delta`` and
 ``gated_delta`` to a finite-difference gradient step on the reconstruction
 loss, exact retrieval with orthonormal keys, the Householder norm invariant,
 closed forms for beta = 0 and alpha -> 0, and a hand-expanded scalar case
@@ -49,7 +60,9 @@ closed forms for beta = 0 and alpha -> 0, and a hand-expanded scalar case
 
 import numpy as np
 
-MODES = ("linear", "delta", "gated_delta")
+MODES = ("linear", "delta", "gated_delta", "gated_linear")
+GATED_MODES = ("gated_delta", "gated_linear")    # use log_alpha
+ERASE_MODES = ("delta", "gated_delta")           # use beta (delta rule)
 
 
 def _check_mode(mode):
@@ -73,6 +86,9 @@ def recurrent_step(S, q, k, v, log_alpha, beta, mode):
     write = k[..., :, None] * v[..., None, :]          # k v^T
     if mode == "linear":
         S_new = S + write
+    elif mode == "gated_linear":
+        alpha = np.exp(np.asarray(log_alpha, dtype=np.float64))[..., None, None]
+        S_new = alpha * S + write
     else:
         beta = np.asarray(beta, dtype=np.float64)[..., None, None]
         if mode == "gated_delta":
@@ -102,10 +118,10 @@ def recurrent_fwd(q, k, v, log_alpha, beta, S0, mode):
     v = np.asarray(v, dtype=np.float64)
     B, H, L, dk = k.shape
     dv = v.shape[-1]
-    if mode != "linear" and beta is None:
+    if mode in ERASE_MODES and beta is None:
         raise ValueError("beta is required for the delta modes")
-    if mode == "gated_delta" and log_alpha is None:
-        raise ValueError("log_alpha is required for gated_delta")
+    if mode in GATED_MODES and log_alpha is None:
+        raise ValueError(f"log_alpha is required for {mode}")
     la = None if log_alpha is None else np.asarray(log_alpha, dtype=np.float64)
     be = None if beta is None else np.asarray(beta, dtype=np.float64)
     S = (np.zeros((B, H, dk, dv)) if S0 is None

@@ -4,7 +4,8 @@ The fixture freezes the oracle's outputs on a tiny fixed input for every
 mode, so that a later change to the oracle's arithmetic shows up as a failed
 comparison and has to be justified.  The values come from the token
 recurrence (o_t = S_t^T q_t after the gated-delta update of the
-hybrid-attention notes, section "Gated DeltaNet", and its special cases).
+hybrid-attention notes, section "Gated DeltaNet", its special cases, and
+the gated linear update of the same section).
 
 Run from the repository root:  python tests/golden/make_oracle_golden.py
 """
@@ -36,7 +37,7 @@ def main():
     x = tiny_inputs()
     out = {"source": "oracle.recurrent_fwd on tiny_inputs() of this script",
            "inputs": {n: a.tolist() for n, a in x.items()}, "modes": {}}
-    for mode in ("linear", "delta", "gated_delta"):
+    for mode in ("linear", "delta", "gated_delta", "gated_linear"):
         o, S = recurrent_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"],
                              x["S0"], mode)
         out["modes"][mode] = {"o": o.tolist(), "S_final": S.tolist()}

@@ -249,6 +249,91 @@ def test_scalar_state_by_hand():
     assert abs(S[0, 0, 0, 0] - s) < 1e-14
 
 
+# ---------------------------------------------------------------- gated linear
+
+def _gated_linear_by_loops(q, k, v, la, S0):
+    """o_t = (prod_{u<=t} alpha_u) S0^T q_t
+             + sum_{s<=t} (prod_{s<u<=t} alpha_u) (q_t . k_s) v_s
+    and the final state, evaluated with explicit loops over t and s and
+    running products of the gates (no cumulative sums, no exponent
+    differences)."""
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    alpha = np.exp(la)
+    o = np.zeros((B, H, L, dv))
+    S = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                w0 = 1.0
+                for u in range(t + 1):
+                    w0 *= alpha[b, h, u]
+                acc = w0 * (S0[b, h].T @ q[b, h, t])
+                for s_ in range(t + 1):
+                    w = 1.0
+                    for u in range(s_ + 1, t + 1):
+                        w *= alpha[b, h, u]
+                    acc = acc + w * float(q[b, h, t] @ k[b, h, s_]) * v[b, h, s_]
+                o[b, h, t] = acc
+            wL = 1.0
+            for u in range(L):
+                wL *= alpha[b, h, u]
+            Sbh = wL * S0[b, h]
+            for s_ in range(L):
+                w = 1.0
+                for u in range(s_ + 1, L):
+                    w *= alpha[b, h, u]
+                Sbh = Sbh + w * np.outer(k[b, h, s_], v[b, h, s_])
+            S[b, h] = Sbh
+    return o, S
+
+
+def test_gated_linear_equals_gate_weighted_sum():
+    """[HA-1 "Gated DeltaNet"; CS336 "继续改进：Mamba"]: multiplying the state
+    by alpha_t before each write makes output t the causal sum of the writes,
+    each weighted by the product of the gates applied after it, plus the
+    initial state decayed by all gates so far."""
+    q, k, v, la, be, S0 = _rand(61, B=1, H=2, L=11, dk=4, dv=3, unit_keys=False)
+    o, S = recurrent_fwd(q, k, v, la, be, S0, "gated_linear")
+    o_ref, S_ref = _gated_linear_by_loops(q, k, v, la, S0)
+    assert _rel(o, o_ref) < 1e-13
+    assert _rel(S, S_ref) < 1e-13
+
+
+def test_gated_linear_special_cases():
+    """alpha = 1 is plain linear attention; alpha -> 0 keeps only the token's
+    own write, o_t = (q_t . k_t) v_t; beta is ignored."""
+    q, k, v, la, be, S0 = _rand(62, L=9, dk=4, dv=5)
+    a, Sa = recurrent_fwd(q, k, v, np.zeros_like(la), be, S0, "gated_linear")
+    b, Sb = recurrent_fwd(q, k, v, None, None, S0, "linear")
+    assert _rel(a, b) < 1e-15 and _rel(Sa, Sb) < 1e-15
+    o0, _ = recurrent_fwd(q, k, v, np.full_like(la, -1e30), be, S0, "gated_linear")
+    assert _rel(o0, np.sum(q * k, axis=-1)[..., None] * v) < 1e-14
+    c, _ = recurrent_fwd(q, k, v, la, None, S0, "gated_linear")
+    d, _ = recurrent_fwd(q, k, v, la, be, S0, "gated_linear")
+    assert np.array_equal(c, d)
+    with pytest.raises(ValueError):
+        recurrent_fwd(q, k, v, None, be, S0, "gated_linear")
+
+
+def test_gated_linear_scalar_by_hand():
+    """dk = dv = 1: s <- alpha s + k v, o = s q, with plain Python floats."""
+    rng = np.random.default_rng(63)
+    L = 7
+    q, k, v = (rng.standard_normal(L) for _ in range(3))
+    la = -np.abs(rng.standard_normal(L)) / 2
+    s = -0.4
+    want = []
+    for t in range(L):
+        s = float(np.exp(la[t])) * s + k[t] * v[t]
+        want.append(s * q[t])
+    o, S = recurrent_fwd(q[None, None, :, None], k[None, None, :, None],
+                         v[None, None, :, None], la[None, None], None,
+                         np.array([[[[-0.4]]]]), "gated_linear")
+    assert np.allclose(o[0, 0, :, 0], want, rtol=1e-14, atol=0)
+    assert abs(S[0, 0, 0, 0] - s) < 1e-14
+
+
 # ---------------------------------------------------------------- chunkwise
 
 @pytest.mark.parametrize("mode", oracle.MODES)
@@ -331,7 +416,8 @@ def test_state_carry_and_decode_match_forward(mode):
 
 
 def test_modes_ignore_unused_gates():
-    """linear ignores beta and alpha; delta ignores alpha."""
+    """linear ignores beta and alpha; delta ignores alpha (gated_linear's
+    beta: test_gated_linear_special_cases)."""
     q, k, v, la, be, S0 = _rand(51, L=6)
     a, _ = recurrent_fwd(q, k, v, la, be, S0, "linear")
     b, _ = recurrent_fwd(q, k, v, None, None, S0, "linear")
