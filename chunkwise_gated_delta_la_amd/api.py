@@ -10,7 +10,9 @@ import torch
 
 from . import _lib
 
-MODES = {"linear": 0, "delta": 1, "gated_delta": 2}
+MODES = {"linear": 0, "delta": 1, "gated_delta": 2, "gated_linear": 3}
+_DECAY = (2, 3)      # modes that read log_alpha
+_ERASE = (1, 2)      # modes that read beta
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
@@ -93,8 +95,8 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     _need(k, "k", (B, H, L, dk), dt, dev)
     _need(v, "v", (B, H, L, dv), dt, dev)
     _need(q, "q", (B, H, L, dk), dt, dev)
-    _need(log_alpha if m == 2 else None, "log_alpha", (B, H, L), torch.float32, dev)
-    _need(beta if m >= 1 else None, "beta", (B, H, L), torch.float32, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (B, H, L), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (B, H, L), torch.float32, dev)
     _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
     odt = out_dtype or (out.dtype if out is not None else dt)
     code = _dtype_code(dt, odt)
@@ -115,8 +117,8 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
         rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v),
-                              _ptr(log_alpha if m == 2 else None),
-                              _ptr(beta if m >= 1 else None), _ptr(S0),
+                              _ptr(log_alpha if m in _DECAY else None),
+                              _ptr(beta if m in _ERASE else None), _ptr(S0),
                               _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
                               code, _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check(rc)
@@ -141,8 +143,8 @@ def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
         raise TypeError(f"q must be float32 or bfloat16, got {dt}")
     _need(k, "k", (B, H, dk), dt, dev)
     _need(v, "v", (B, H, dv), dt, dev)
-    _need(log_alpha if m == 2 else None, "log_alpha", (B, H), torch.float32, dev)
-    _need(beta if m >= 1 else None, "beta", (B, H), torch.float32, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (B, H), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (B, H), torch.float32, dev)
     _need(S, "S", (B, H, dk, dv), torch.float32, dev)
     odt = out_dtype or (out.dtype if out is not None else dt)
     code = _dtype_code(dt, odt)
@@ -152,8 +154,8 @@ def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
     lib = _lib.get()
     with torch.cuda.device(dev):
         rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v),
-                                _ptr(log_alpha if m == 2 else None),
-                                _ptr(beta if m >= 1 else None), _ptr(S), _ptr(out),
+                                _ptr(log_alpha if m in _DECAY else None),
+                                _ptr(beta if m in _ERASE else None), _ptr(S), _ptr(out),
                                 B, H, dk, dv, m, code, _stream(dev))
     _lib.check(rc)
     return out

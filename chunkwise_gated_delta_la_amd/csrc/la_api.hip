@@ -57,9 +57,10 @@ bool count(std::initializer_list<long> dims, size_t* out) {
 }
 
 int check_mode_dtype(int mode, int dtype) {
-  if (mode < LA_MODE_LINEAR || mode > LA_MODE_GATED_DELTA)
-    return fail(LA_ERR_UNSUPPORTED, "mode must be LA_MODE_LINEAR, LA_MODE_DELTA or "
-                                    "LA_MODE_GATED_DELTA, got " + std::to_string(mode));
+  if (mode < LA_MODE_LINEAR || mode > LA_MODE_GATED_LINEAR)
+    return fail(LA_ERR_UNSUPPORTED, "mode must be LA_MODE_LINEAR, LA_MODE_DELTA, "
+                                    "LA_MODE_GATED_DELTA or LA_MODE_GATED_LINEAR, got " +
+                                        std::to_string(mode));
   if (dtype != LA_DTYPE_F32 && dtype != LA_DTYPE_BF16 && dtype != LA_DTYPE_BF16_F32OUT)
     return fail(LA_ERR_UNSUPPORTED, "dtype must be LA_DTYPE_F32, LA_DTYPE_BF16 or "
                                     "LA_DTYPE_BF16_F32OUT, got " + std::to_string(dtype));
@@ -67,10 +68,10 @@ int check_mode_dtype(int mode, int dtype) {
 }
 
 int check_gates(int mode, const float* log_alpha, const float* beta) {
-  if (mode != LA_MODE_LINEAR && !beta)
+  if (la::mode_erase(mode) && !beta)
     return fail(LA_ERR_NULL, "beta is required for the delta modes");
-  if (mode == LA_MODE_GATED_DELTA && !log_alpha)
-    return fail(LA_ERR_NULL, "log_alpha is required for LA_MODE_GATED_DELTA");
+  if (la::mode_decay(mode) && !log_alpha)
+    return fail(LA_ERR_NULL, "log_alpha is required for the gated modes");
   return LA_OK;
 }
 
@@ -139,7 +140,7 @@ extern "C" {
 
 const char* la_last_error(void) { return g_last_error.c_str(); }
 
-const char* la_version(void) { return "lachunk 0.2.0 gfx950"; }
+const char* la_version(void) { return "lachunk 0.3.0 gfx950"; }
 
 int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode, int dtype,
                              size_t* bytes) {
@@ -181,8 +182,8 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
   const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
   const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
-  const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
-  const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
+  const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
+  const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
   const Range rs0(S0, n_s * 4), ro(out, n_v * osz), rsf(S_final, n_s * 4);
   const Range rws(need > 0 ? workspace : nullptr, need);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0})
@@ -229,8 +230,8 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
   const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
   const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
   const Range rq(q, n_k * esz), rk(k, n_k * esz), rv(v, n_v * esz);
-  const Range rla(mode == LA_MODE_GATED_DELTA ? log_alpha : nullptr, n_g * 4);
-  const Range rb(mode != LA_MODE_LINEAR ? beta : nullptr, n_g * 4);
+  const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
+  const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
   const Range rs(S, n_s * 4), ro(out, n_v * osz);
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");

@@ -289,15 +289,15 @@ __device__ __forceinline__ void qs_rows(const T* Qs, const Frag<T>* Sx, f32x4 (&
   }
 }
 
-// O = diag(gam) Q S + Aqk U_new for NTI row tiles (TI0, TI1); linear mode
-// uses V for U_new.  ob0 indexes (first row of the chunk, this lane's
+// O = diag(gam) Q S + Aqk U_new for NTI row tiles (TI0, TI1); the modes
+// without erase use V for U_new.  ob0 indexes (first row of the chunk, this lane's
 // column) of the output.
 template <typename T, int D, int MODE, int NTI, int TI0, int TI1, int LDT>
 __device__ __forceinline__ void out_rows(const T* Aq, const Frag<T>* Ux, const T* Vt,
                                          const float* gs, const f32x4 (&qs)[2], void* out_,
                                          size_t ob0, int out_bf16, int g, int nt, int lane) {
-  constexpr bool kDelta = MODE != kModeLinear;
-  constexpr bool kGated = MODE == kModeGatedDelta;
+  constexpr bool kDelta = mode_erase(MODE);
+  constexpr bool kGated = mode_decay(MODE);
   constexpr bool kSplit = IsBf16<T>::value;
   constexpr int kPlanes = kSplit ? 2 : 1;
   Frag2<T> uf[2];
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, void* __restrict__ out_, float* __restrict__ S_final,
     int L, int BH, int out_bf16) {
-  constexpr bool kDelta = MODE != kModeLinear;
-  constexpr bool kGated = MODE == kModeGatedDelta;
+  constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T
+  constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   constexpr bool kSplit = IsBf16<T>::value;
   constexpr int kPlanes = kSplit ? 2 : 1;
   constexpr int PE = 16 / sizeof(T);             // elements per 16 bytes
@@ -691,6 +691,25 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
+      } else if constexpr (kGated) {
+        // gated linear: S' = gam_C S + K^T diag(gam_C / gam) V; operand
+        // element j of block kb is token 32 kb + kidx(g, j)
+        const float gC = gs[C - 1];
+        Frag2<T> vf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag<T> raw = frag_row(Vt + nt + 32 * kb, g);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            vf[kb].set(j, to_f32(raw.v[j]) * __expf(gC - gs[32 * kb + kidx(g, j)]));
+        }
+        const float decC = __expf(gC);
+#pragma unroll
+        for (int tj = 0; tj < NKT; ++tj) S[tj] *= decC;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int tj = 0; tj < NKT; ++tj) mma_ab2(ktf[tj][kb], vf[kb], S[tj]);
       } else {
         // linear: S' = S + K^T V
 #pragma unroll
@@ -755,6 +774,7 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
   switch (a.mode) {
     case kModeLinear: return launch_one<T, D, kModeLinear>(a, st);
     case kModeDelta: return launch_one<T, D, kModeDelta>(a, st);
+    case kModeGatedLinear: return launch_one<T, D, kModeGatedLinear>(a, st);
     default: return launch_one<T, D, kModeGatedDelta>(a, st);
   }
 }
@@ -768,7 +788,7 @@ hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st) {
 // bf16 inputs run the two-kernel path of la_chunk_pipe.hip; float inputs,
 // which have no transposed LDS reads, run the phase-sequential kernel
 // above.
-bool chunk_needs_tsolve(const ChunkArgs& a) { return a.in_bf16 && a.mode != kModeLinear; }
+bool chunk_needs_tsolve(const ChunkArgs& a) { return a.in_bf16 && mode_erase(a.mode); }
 
 size_t chunk_workspace_bytes(const ChunkArgs& a) {
   return a.in_bf16 ? chunk_pipe_workspace_bytes(a) : 0;

@@ -488,14 +488,14 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
 }
 
 // Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
-// (U_new = V in linear mode), into o[u] (row tile u ? TI1 : TI0, accumulator
+// (U_new = V in the modes without erase), into o[u] (row tile u ? TI1 : TI0, accumulator
 // layout).  U_new arrives in float (Uf, accumulator layout, tile ti at
 // ti * 64 + lane) and is split here.
 template <int D, int MODE, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
                                          const f32x4* Uf, const T16* Vt, f32x4 (&o)[2],
                                          int g, int n, int lane) {
-  constexpr bool kDelta = MODE != kModeLinear;
+  constexpr bool kDelta = mode_erase(MODE);
   Frag2<T16> uf[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const u32x4* __restrict__ tws, const float* __restrict__ S0, void* __restrict__ out_,
     float* __restrict__ S_final, int L, int BH, int out_bf16) {
-  constexpr bool kDelta = MODE != kModeLinear;
-  constexpr bool kGated = MODE == kModeGatedDelta;
+  constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T, U_new
+  constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
   constexpr int NCT = D / 16;                    // column tiles per head
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       Gs[cc % 3][lane] = gv;
       Es[cc % 3][lane] = e;
       Fs[cc % 3][lane] = __expf(gC - gv);
-      BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
+      if constexpr (kDelta) BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
     }
   };
 
@@ -830,6 +830,32 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
+      } else if constexpr (kGated) {
+        // S += K^T diag(gam_C / gam) V (S is already decayed by gam_C): V in
+        // accumulator layout, scaled and split like U_new above
+        const uint32_t vslot = slot(c, 4, C * 16 * 2);
+        const uint32_t tslot = slot(c, 3, C * 4);
+        f32x4 vv[4], fr[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          vv[ti] = v_acc_at(Vs, vslot + voff + 512 * ti);
+          fr[ti] = lds_ld<f32x4>(Fs, tslot + goff + 64 * ti);
+        }
+        Frag2<T16> ut[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const f32x4 flo = fr[2 * kb], fhi = fr[2 * kb + 1];
+          const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
+          const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
+          ut[kb] = frag2_from_acc_scaled<T16>(vv[2 * kb], vv[2 * kb + 1], slo, shi);
+        }
+#pragma unroll
+        for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const Frag<T16> kt = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
+            mma_ab2(kt, ut[kb], S[tj]);
+          }
       } else {
         // S <- S + K^T V
         const uint32_t vslot = slot(c, 4, C * 16 * 2);
@@ -974,6 +1000,7 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
   switch (a.mode) {
     case kModeLinear: return launch_one<D, kModeLinear>(a, st);
     case kModeDelta: return launch_one<D, kModeDelta>(a, st);
+    case kModeGatedLinear: return launch_one<D, kModeGatedLinear>(a, st);
     default: return launch_one<D, kModeGatedDelta>(a, st);
   }
 }
@@ -981,12 +1008,12 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
-  if (a.mode == kModeLinear) return 0;
+  if (!mode_erase(a.mode)) return 0;
   return (size_t)a.B * a.H * (a.L / C) * kTFrags * kWave * sizeof(u32x4);
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
-  const bool gated = a.mode == kModeGatedDelta;
+  const bool gated = mode_decay(a.mode);
   if (a.d == 64) return gated ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
   return gated ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
 }

@@ -6,6 +6,7 @@
 //     linear      : u = v,             S' = S + k u^T,          o = p + kq u
 //     delta       : u = beta (v - s),  S' = S + k u^T,          o = p + kq u
 //     gated_delta : u = beta (v - a s),S' = a S + k u^T,        o = a p + kq u
+//     gated_linear: u = v,             S' = a S + k u^T,        o = a p + kq u
 // where a = exp(log_alpha).  o = S'^T q is expanded so that one read of S
 // yields both s and p; the erase term k (k^T S) is never formed as a
 // dk x dk matrix (the O(d^2) evaluation order of "继续改进：GDN" in the
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __syncthreads();
 
   float a = 1.f;
-  if (MODE == kModeGatedDelta) a = __expf(log_alpha[bh]);
+  if (mode_decay(MODE)) a = __expf(log_alpha[bh]);
   if (t < DV) {
     float sj = 0.f, pj = 0.f;
 #pragma unroll
@@ -96,9 +97,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
       pj += red[1][r][t];
     }
     float u, o;
-    if (MODE == kModeLinear) {
+    if (!mode_erase(MODE)) {
+      // S' = a S + k v^T:  o = a S^T q + (k . q) v
       u = sv[t];
-      o = pj + skq * u;
+      o = a * pj + skq * u;
     } else {
       const float b = beta[bh];
       u = b * (sv[t] - a * sj);
@@ -136,6 +138,10 @@ hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
       break;
     case kModeDelta:
       decode_kernel<T, TO, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
+          q, k, v, a.log_alpha, a.beta, a.S, o);
+      break;
+    case kModeGatedLinear:
+      decode_kernel<T, TO, DK, DV, kModeGatedLinear><<<grid, block, 0, st>>>(
           q, k, v, a.log_alpha, a.beta, a.S, o);
       break;
     default:

@@ -7,7 +7,12 @@
 
 namespace la {
 
-enum : int { kModeLinear = 0, kModeDelta = 1, kModeGatedDelta = 2 };
+enum : int { kModeLinear = 0, kModeDelta = 1, kModeGatedDelta = 2, kModeGatedLinear = 3 };
+
+// The delta rule (beta, erase, the T factor) and the scalar decay (log
+// alpha) are independent switches of the four modes.
+__host__ __device__ constexpr bool mode_erase(int m) { return m == kModeDelta || m == kModeGatedDelta; }
+__host__ __device__ constexpr bool mode_decay(int m) { return m == kModeGatedDelta || m == kModeGatedLinear; }
 
 struct DecodeArgs {
   const void* q;
@@ -39,8 +44,8 @@ struct ChunkArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 // Chunk forward: float inputs run one kernel (la_chunk.hip); bf16 inputs
-// in the delta modes first solve T for every chunk (launch_tsolve, into the
-// workspace), then run the chain kernel (la_chunk_pipe.hip).
+// in the delta (erase) modes first solve T for every chunk (launch_tsolve,
+// into the workspace), then run the chain kernel (la_chunk_pipe.hip).
 size_t chunk_workspace_bytes(const ChunkArgs& a);
 bool chunk_needs_tsolve(const ChunkArgs& a);
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st);       // la_chunk_pipe.hip

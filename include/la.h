@@ -12,14 +12,21 @@
  * erase-then-write with a scalar decay of the whole state ("Gated DeltaNet"
  * and "Fast Weight Programmers与DeltaNet" in the hybrid-attention notes
  * "混合注意力学习(1): 线性注意力"; "继续改进：GDN" in the lecture notes
- * "【CS336】lecture4 线性注意力|Mamba|GDN|DSA").  Three modes:
+ * "【CS336】lecture4 线性注意力|Mamba|GDN|DSA").  Four modes:
  *
- *   LA_MODE_LINEAR       S_t = S_{t-1} + k_t v_t^T   (no feature map, no
- *                        normaliser -- the numerator-only form of "线性注意力"
- *                        in the hybrid-attention notes and of "The Devil in
- *                        Linear Transformer" in "LinearAttention 概述")
- *   LA_MODE_DELTA        alpha_t = 1
- *   LA_MODE_GATED_DELTA  the full rule
+ *   LA_MODE_LINEAR        S_t = S_{t-1} + k_t v_t^T  (no feature map, no
+ *                         normaliser -- the numerator-only form of
+ *                         "线性注意力" in the hybrid-attention notes and of
+ *                         "The Devil in Linear Transformer" in
+ *                         "LinearAttention 概述")
+ *   LA_MODE_DELTA         alpha_t = 1
+ *   LA_MODE_GATED_DELTA   the full rule
+ *   LA_MODE_GATED_LINEAR  S_t = alpha_t S_{t-1} + k_t v_t^T: linear
+ *                         attention with the scalar state decay and no
+ *                         erase (the weight decay attributed to Mamba2 in
+ *                         "Gated DeltaNet" of the hybrid-attention notes;
+ *                         the gated state update of "继续改进：Mamba" in the
+ *                         lecture notes)
  *
  * No scaling, activation, feature map, denominator or output norm is applied
  * inside the op; the caller prepares q, k, beta and log_alpha.
@@ -65,7 +72,8 @@ extern "C" {
 typedef enum {
   LA_MODE_LINEAR = 0,
   LA_MODE_DELTA = 1,
-  LA_MODE_GATED_DELTA = 2
+  LA_MODE_GATED_DELTA = 2,
+  LA_MODE_GATED_LINEAR = 3
 } la_mode_t;
 
 /* Element types of (q, k, v) and of out.  LA_DTYPE_BF16_F32OUT takes bf16
@@ -104,11 +112,13 @@ typedef enum {
  *   k          [B, H, L, dk]  dtype          keys
  *   v          [B, H, L, dv]  dtype          values
  *   log_alpha  [B, H, L]      float32        log of the decay (<= 0);
- *                                            required for GATED_DELTA,
- *                                            ignored (may be NULL) otherwise
+ *                                            required for GATED_DELTA and
+ *                                            GATED_LINEAR, ignored (may be
+ *                                            NULL) otherwise
  *   beta       [B, H, L]      float32        write strength; required for
  *                                            DELTA and GATED_DELTA, ignored
- *                                            (may be NULL) for LINEAR
+ *                                            (may be NULL) for LINEAR and
+ *                                            GATED_LINEAR
  *   S0         [B, H, dk, dv] float32        initial state; NULL = zeros
  *   out        [B, H, L, dv]  dtype          output (written)
  *   S_final    [B, H, dk, dv] float32        final state (written); may be
@@ -120,7 +130,8 @@ typedef enum {
  *              arguments; may be NULL when that is 0.  Its contents on entry
  *              are ignored and on return are unspecified.  The bf16 delta
  *              modes keep each chunk's T factor there (B*H*L/C * 6 KiB);
- *              float inputs and LA_MODE_LINEAR need none.
+ *              float inputs and the modes without erase (LINEAR,
+ *              GATED_LINEAR) need none.
  *   stream     hipStream_t
  *
  * Supported: dk = dv in {64, 128}, C = 64, all dtypes, all modes.
@@ -158,7 +169,8 @@ int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
  *
  *   q, k       [B, H, dk]     dtype
  *   v          [B, H, dv]     dtype
- *   log_alpha  [B, H]         float32  (GATED_DELTA only; else may be NULL)
+ *   log_alpha  [B, H]         float32  (GATED_DELTA, GATED_LINEAR; else
+ *                                       may be NULL)
  *   beta       [B, H]         float32  (DELTA, GATED_DELTA; else may be NULL)
  *   S          [B, H, dk, dv] float32  state, read and overwritten in place
  *   out        [B, H, dv]     dtype    output (written)
@@ -199,7 +211,7 @@ int la_profile_end(la_kernel_time_t* out, int capacity, int* count);
  * The pointer stays valid until the next call on the same thread. */
 const char* la_last_error(void);
 
-/* Library version string, e.g. "lachunk 0.2.0 gfx950". */
+/* Library version string, e.g. "lachunk 0.3.0 gfx950". */
 const char* la_version(void);
 
 #ifdef __cplusplus

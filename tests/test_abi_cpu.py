@@ -71,7 +71,8 @@ def decode(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), S=fake(
     (dict(be=None), NULL), (dict(la=None), NULL), (dict(be=None, mode=1), NULL),
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=0), SHAPE), (dict(C=0), SHAPE),
     (dict(L=96), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(dk=96, dv=96), UNSUP),
-    (dict(C=32, L=64), UNSUP), (dict(mode=3), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(C=32, L=64), UNSUP), (dict(mode=4), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(la=None, mode=3), NULL),
     (dict(mode=-1), UNSUP), (dict(dtype=3), UNSUP),
 ])
 def test_chunk_fwd_rejects(kw, code):
@@ -102,6 +103,7 @@ def test_workspace_size():
                 rc, n = ws_bytes(lib, B=B, H=H, L=L, dk=d, dv=d, mode=mode, dtype=dtype)
                 assert rc == OK and n == B * H * (L // 64) * TSOLVE_BYTES
     assert ws_bytes(lib, mode=0) == (OK, 0)
+    assert ws_bytes(lib, mode=3) == (OK, 0)
     assert ws_bytes(lib, dtype=0) == (OK, 0)
     assert ws_bytes(lib, L=96)[0] == SHAPE
     assert ws_bytes(lib, dk=96, dv=96)[0] == UNSUP
@@ -136,6 +138,9 @@ def test_chunk_fwd_unused_gates_may_alias_anything():
     validated, never launched, because q is NULL)."""
     lib = _lib.get()
     assert chunk(lib, mode=0, be=fake(6), la=fake(6), q=None) == NULL
+    # gated linear reads log_alpha but not beta: a NULL beta passes the gate
+    # checks and the call stops at the alias check instead
+    assert chunk(lib, mode=3, be=None, ws=None, wsb=0, out=ctypes.c_void_p(P + 128)) == ALIAS
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -18,12 +18,13 @@ from workloads import WORKLOADS, Workload
 
 pytestmark = pytest.mark.gpu
 
-MODES = ("linear", "delta", "gated_delta")
+MODES = ("linear", "delta", "gated_delta", "gated_linear")
 
 
 def recipe(mode, dtype, B, H, L, d, s0_std=0.0, seed=7):
-    """The workloads' recipe for `mode` at reduced sizes."""
-    lin = mode == "linear"
+    """The workloads' recipe for `mode` at reduced sizes (the modes without
+    erase take the linear-attention recipe: raw scaled q, k)."""
+    lin = mode in ("linear", "gated_linear")
     return Workload(f"{mode}_{dtype}_b{B}h{H}l{L}d{d}", mode, dtype, B=B, H=H, L=L, dk=d,
                     dv=d, C=64, qk_norm=not lin,
                     qkv_scale=1.0 / math.sqrt(d) if lin else 1.0, s0_std=s0_std, seed=seed)

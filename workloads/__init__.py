@@ -35,7 +35,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    mode: str            # "linear" | "delta" | "gated_delta"
+    mode: str            # "linear" | "delta" | "gated_delta" | "gated_linear"
     dtype: str           # "f32" | "bf16": dtype of q, k, v and the output
     B: int
     H: int
