@@ -111,9 +111,6 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   if (int e = check_mode_dtype(mode, dtype)) return e;
   if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || C <= 0)
     return fail(LA_ERR_SHAPE, "B, H, L, dk, dv and C must be positive");
-  if (L % C != 0)
-    return fail(LA_ERR_SHAPE, "L (" + std::to_string(L) + ") must be a multiple of C (" +
-                                  std::to_string(C) + ")");
   if (dk != dv || (dk != 64 && dk != 128))
     return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd supports dk == dv in {64, 128}, got dk=" +
                                         std::to_string(dk) + " dv=" + std::to_string(dv));
@@ -122,8 +119,9 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   size_t n_qk;
   if (!count({B, H, L, dk}, &n_qk) || n_qk > (SIZE_MAX >> 4))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
-  if ((size_t)B * H * (dv / 16) > 0x7fffffffu || (size_t)B * H * (L / C) > 0x7fffffffu)
-    return fail(LA_ERR_SHAPE, "B * H * dv / 16 or B * H * L / C exceeds the launch grid");
+  const size_t nc = ((size_t)L + C - 1) / C;             // chunks, the last may be partial
+  if ((size_t)B * H * (dv / 16) > 0x7fffffffu || (size_t)B * H * nc > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "B * H * dv / 16 or B * H * ceil(L / C) exceeds the launch grid");
   return LA_OK;
 }
 

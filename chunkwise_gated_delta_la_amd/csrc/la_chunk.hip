@@ -295,7 +295,8 @@ __device__ __forceinline__ void qs_rows(const T* Qs, const Frag<T>* Sx, f32x4 (&
 template <typename T, int D, int MODE, int NTI, int TI0, int TI1, int LDT>
 __device__ __forceinline__ void out_rows(const T* Aq, const Frag<T>* Ux, const T* Vt,
                                          const float* gs, const f32x4 (&qs)[2], void* out_,
-                                         size_t ob0, int out_bf16, int g, int nt, int lane) {
+                                         size_t ob0, int out_bf16, int g, int nt, int lane,
+                                         int nrows) {
   constexpr bool kDelta = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr bool kSplit = IsBf16<T>::value;
@@ -342,15 +343,19 @@ __device__ __forceinline__ void out_rows(const T* Aq, const Frag<T>* Ux, const T
         mma(af[u][kb].hi, uf[kb].hi, o);
       }
     }
-    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
+    // rows at or past nrows lie past the end of the sequence
+    const int r0 = 16 * ti + 4 * g;
+    const size_t ob = ob0 + (size_t)r0 * D;
     if (out_bf16) {
       __bf16* out = static_cast<__bf16*>(out_);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = (__bf16)o[i];
+      for (int i = 0; i < 4; ++i)
+        if (r0 + i < nrows) out[ob + (size_t)i * D] = (__bf16)o[i];
     } else {
       float* out = static_cast<float*>(out_);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[ob + (size_t)i * D] = o[i];
+      for (int i = 0; i < 4; ++i)
+        if (r0 + i < nrows) out[ob + (size_t)i * D] = o[i];
     }
   }
 }
@@ -495,25 +500,36 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
     if constexpr (kSplit) return 2 * (lane / 2) + m;
     else return lane / VVR + (C / NVV) * m;
   };
+  // Chunks; the last may hold fewer than C rows.  Rows past the sequence
+  // act as tokens that change nothing: their Q and K reads are clamped to
+  // the last valid row, V, beta and log alpha are zero (no write, no erase,
+  // no decay; identity rows of T), and their outputs are not stored.  Valid
+  // rows never see them: every product inside a chunk is causal.
+  const int NC = (L + C - 1) / C;
+  auto rows_of = [&](int c) { return min(C, L - c * C); };
   auto load_chunk = [&](int c) {
     const size_t row0 = hbase + (size_t)c * C;
+    const int nv = rows_of(c);
 #pragma unroll
     for (int m = 0; m < NVQ; ++m) {
-      const int r = 2 * (prp + NRP * (m / 2)) + (m % 2);
+      const int r = min(2 * (prp + NRP * (m / 2)) + (m % 2), nv - 1);
       pq[m] = *reinterpret_cast<const u32x4*>(q + (row0 + r) * D + pcv * PE);
       pk[m] = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + pcv * PE);
     }
     if (wave == 0) {
 #pragma unroll
-      for (int m = 0; m < NVV; ++m)
-        pv[m] = *reinterpret_cast<const u32x4*>(v + (row0 + vrow(m)) * D + col0 +
+      for (int m = 0; m < NVV; ++m) {
+        const int r = vrow(m);
+        pv[m] = *reinterpret_cast<const u32x4*>(v + (row0 + min(r, nv - 1)) * D + col0 +
                                                (lane % VVR) * PE);
-      if (kGated) pla = log_alpha[row0 + lane];
-      if (kDelta) pb = beta[row0 + lane];
+        if (r >= nv) pv[m] = u32x4{0u, 0u, 0u, 0u};
+      }
+      const int lr = min(lane, nv - 1);
+      if (kGated) pla = lane < nv ? log_alpha[row0 + lr] : 0.f;
+      if (kDelta) pb = lane < nv ? beta[row0 + lr] : 0.f;
     }
   };
 
-  const int NC = L / C;
   load_chunk(0);
 
   for (int c = 0; c < NC; ++c) {
@@ -739,12 +755,13 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
       }
     } else {
       const size_t ob0 = row0 * D + col;
+      const int nv = rows_of(c);
       if (wave == 1) {
-        out_rows<T, D, MODE, 2, 0, 3, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
+        out_rows<T, D, MODE, 2, 0, 3, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane, nv);
       } else if (wave == 2) {
-        out_rows<T, D, MODE, 1, 1, 1, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
+        out_rows<T, D, MODE, 1, 1, 1, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane, nv);
       } else {
-        out_rows<T, D, MODE, 1, 2, 2, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane);
+        out_rows<T, D, MODE, 1, 2, 2, LDT>(Aq, Ux, Vt, gs, qs, out_, ob0, out_bf16, g, nt, lane, nv);
       }
     }
     __syncthreads();

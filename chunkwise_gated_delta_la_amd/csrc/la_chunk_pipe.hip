@@ -223,14 +223,18 @@ __device__ __forceinline__ void vm_wait() {
 // instruction moves 1 KiB = 512 elements.  Instruction m of lane l stores
 // LDS bytes 1024 m + 16 l: row r, position ul, i.e. logical unit
 // ul ^ key(r); off[m] is that unit's byte offset in the source rows.
+//
+// Rows at or past nrows (the end of the sequence in a partial last chunk)
+// read the last valid row instead, so no load leaves the tensor.
 template <int D>
-__device__ __forceinline__ void dma_tile_offsets(uint32_t (&off)[C * 2 * D / 1024], int lane) {
+__device__ __forceinline__ void dma_tile_offsets(uint32_t (&off)[C * 2 * D / 1024], int lane,
+                                                 int nrows) {
   constexpr int RB = 2 * D;
 #pragma unroll
   for (int m = 0; m < C * RB / 1024; ++m) {
     const int byte = 1024 * m + 16 * lane;
     const int r = byte / RB, ul = (byte % RB) / 16;
-    off[m] = (uint32_t)(r * RB + ((ul ^ swz_key<D>(r)) << 4));
+    off[m] = (uint32_t)(min(r, nrows - 1) * RB + ((ul ^ swz_key<D>(r)) << 4));
   }
 }
 
@@ -356,10 +360,15 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
 
   const int lane = threadIdx.x;
   const int g = lane / 16, n = lane % 16;
-  const int NC = L / C;
+  const int NC = (L + C - 1) / C;
   const size_t item = blockIdx.x;
   const size_t bh = item / NC;
-  const size_t row0 = bh * L + (item % NC) * C;
+  const int c = (int)(item % NC);
+  const size_t row0 = bh * L + (size_t)c * C;
+  // rows of this chunk inside the sequence (the last chunk may be partial):
+  // rows past it read the last valid row and carry beta = 0, log alpha = 0,
+  // which makes their rows of A zero and of T the identity
+  const int nv = min(C, L - c * C);
 
   // K rows as operands of K K^T.  Both operands are rows of K, so any
   // assignment of the contraction index to (group, slot) works; here slot j
@@ -369,10 +378,12 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
-      kf[t][kb].v = *reinterpret_cast<const bf16x8*>(k + (row0 + 16 * t + n) * D + 32 * kb + 8 * g);
-  const float bv = beta[row0 + lane];
+      kf[t][kb].v = *reinterpret_cast<const bf16x8*>(
+          k + (row0 + min(16 * t + n, nv - 1)) * D + 32 * kb + 8 * g);
+  const int lr = min(lane, nv - 1);
+  const float bv = lane < nv ? beta[row0 + lr] : 0.f;
   float gv = 0.f;
-  if constexpr (GATED) gv = wave_inclusive_scan(log_alpha[row0 + lane]);
+  if constexpr (GATED) gv = wave_inclusive_scan(lane < nv ? log_alpha[row0 + lr] : 0.f);
   gsh[lane] = gv;
   bsh[lane] = bv;
   // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
@@ -523,22 +534,26 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&
   }
 }
 
-// Store of the rows out_rows produced.
+// Store of the rows out_rows produced; rows at or past nrows (past the end
+// of the sequence in a partial last chunk) are not written.
 template <int D, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void store_rows(const f32x4 (&o)[2], void* out_, size_t ob0,
-                                           int out_bf16, int g) {
+                                           int out_bf16, int g, int nrows) {
 #pragma unroll
   for (int u = 0; u < NTI; ++u) {
     const int ti = u ? TI1 : TI0;
-    const size_t ob = ob0 + (size_t)(16 * ti + 4 * g) * D;
+    const int r0 = 16 * ti + 4 * g;
+    const size_t ob = ob0 + (size_t)r0 * D;
     if (out_bf16) {
       T16* out = static_cast<T16*>(out_);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = (T16)o[u][e];
+      for (int e = 0; e < 4; ++e)
+        if (r0 + e < nrows) out[ob + (size_t)e * D] = (T16)o[u][e];
     } else {
       float* out = static_cast<float*>(out_);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[ob + (size_t)e * D] = o[u][e];
+      for (int e = 0; e < 4; ++e)
+        if (r0 + e < nrows) out[ob + (size_t)e * D] = o[u][e];
     }
   }
 }
@@ -603,7 +618,15 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int col0 = ct * 16;
   const int col = col0 + n;
   const size_t hbase = (size_t)bh * L;
-  const int NC = L / C;
+  // Chunks; the last holds nlast rows (C unless L is not a multiple of C).
+  // Rows past the sequence act as tokens that change nothing: beta = 0 and
+  // log alpha = 0 (no erase, no write, no decay -- their rows of T are the
+  // identity rows), V = 0 (no write in the modes without beta); their Q, K
+  // and V reads are clamped to the last valid row and their outputs are not
+  // stored.  Valid rows never see them: every product inside a chunk is
+  // causal.
+  const int NC = (L + C - 1) / C;
+  const int nlast = L - (NC - 1) * C;
   const u32x4* tw = tws + (size_t)bh * NC * (kTFrags * kWave);
 
   // lane offsets of operand row n over each dk block in a Q or K tile
@@ -615,23 +638,34 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   // waves 1 and 2; for wave 3 the two V instructions (rows 32 m + l / 2,
   // columns col0 + 8 (l % 2) ..) and the T fragments.
   uint32_t doff[NTILE];
-  dma_tile_offsets<D>(doff, lane);
+  dma_tile_offsets<D>(doff, lane, C);
+  auto v_off = [&](int m, int nrows) {
+    return (uint32_t)((min(32 * m + lane / 2, nrows - 1) * D + 8 * (lane % 2)) * 2);
+  };
   uint32_t voff[2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) voff[m] = (uint32_t)(((32 * m + lane / 2) * D + 8 * (lane % 2)) * 2);
+  for (int m = 0; m < 2; ++m) voff[m] = v_off(m, C);
 
   // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
   auto issue_chunk = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
-    if (wave == 1) {
-      dma_tile<D>(Ks[cc % 3], k + r0 * D, doff);
-    } else if (wave == 2) {
-      dma_tile<D>(Qs[cc % 3], q + r0 * D, doff);
+    const bool part = cc == NC - 1 && nlast < C;     // partial last chunk
+    if (wave == 1 || wave == 2) {
+      T16* dst = wave == 1 ? Ks[cc % 3] : Qs[cc % 3];
+      const T16* src = (wave == 1 ? k : q) + r0 * D;
+      if (part) {
+        uint32_t po[NTILE];
+        dma_tile_offsets<D>(po, lane, nlast);
+        dma_tile<D>(dst, src, po);
+      } else {
+        dma_tile<D>(dst, src, doff);
+      }
     } else {
       const uint32_t vb = lds_addr(Vs[cc % 4]);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        dma16s(v + r0 * D + col0, voff[m], __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+        dma16s(v + r0 * D + col0, part ? v_off(m, nlast) : voff[m],
+               __builtin_amdgcn_readfirstlane(vb + 1024 * m));
       if constexpr (kDelta) {
         const uint32_t tb = lds_addr(Ts[cc % 3]);
         const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
@@ -641,14 +675,21 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       }
     }
   };
-  // DMA of the gates of chunk cc (wave 3)
+  // DMA of the gates of chunk cc (wave 3); lanes past the sequence read the
+  // last valid token's gates (tables() zeroes them)
   auto issue_gates = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
-    if constexpr (kDelta) dma4s(beta + r0, (uint32_t)lane * 4, lds_addr(Bs[cc % NG]));
-    if constexpr (kGated) dma4s(log_alpha + r0, (uint32_t)lane * 4, lds_addr(Ls[cc % NG]));
+    const uint32_t go = (uint32_t)(cc == NC - 1 ? min(lane, nlast - 1) : lane) * 4;
+    if constexpr (kDelta) dma4s(beta + r0, go, lds_addr(Bs[cc % NG]));
+    if constexpr (kGated) dma4s(log_alpha + r0, go, lds_addr(Ls[cc % NG]));
   };
-  // Decay tables of chunk cc from its gates (wave 2, gated mode)
+  // Gates of rows past the sequence set to zero, then the decay tables of
+  // chunk cc from its gates (wave 2, after the gates have landed)
   auto tables = [&](int cc) {
+    if (cc == NC - 1 && lane >= nlast) {
+      if constexpr (kDelta) Bs[cc % NG][lane] = 0.f;
+      if constexpr (kGated) Ls[cc % NG][lane] = 0.f;
+    }
     if constexpr (kGated) {
       const float gv = cumsum64(Ls[cc % NG], lane);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
@@ -903,6 +944,16 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     if (wave == 3)
       for (int cc = 0; cc < NG - 1 && cc < NC; ++cc) issue_gates(cc);
     vm_wait<0>();
+    // V rows past the sequence set to zero once the last chunk's V has
+    // landed: here for a single chunk, else at the end of chunk NC - 2
+    auto zero_v_tail = [&]() {
+      if (nlast < C && lane >= nlast) {
+        u32x4* row = reinterpret_cast<u32x4*>(Vs[(NC - 1) % 4] + lane * 16);
+        row[0] = u32x4{0u, 0u, 0u, 0u};
+        row[1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    if (wave == 3 && NC == 1) zero_v_tail();
     __syncthreads();
     if (wave == 2) {
       tables(0);
@@ -925,13 +976,13 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
         if (wave == 1) {
           out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
-          store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g);
+          store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, C);
         } else if (wave == 2) {
           out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
-          store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g);
+          store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, C);
         } else {
           out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
-          store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g);
+          store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, C);
         }
       }
       if (wave == 2 && c + 2 < NC) tables(c + 2);
@@ -954,6 +1005,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       } else {
         vm_wait<0>();
       }
+      if (wave == 3 && c == NC - 2) zero_v_tail();
       __syncthreads();
     }
     const int c = NC - 1;
@@ -962,13 +1014,13 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* Vp = Vs[c % 4];
     if (wave == 1) {
       out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g);
+      store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, nlast);
     } else if (wave == 2) {
       out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g);
+      store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, nlast);
     } else {
       out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g);
+      store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, nlast);
     }
   }
 }
@@ -976,20 +1028,18 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
 template <int D, int MODE>
 hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int NC = a.L / C;
   const T16* k = static_cast<const T16*>(a.k);
   u32x4* tws = static_cast<u32x4*>(a.workspace);
   const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
   chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
       static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v), a.log_alpha, a.beta, tws,
       a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
-  (void)NC;
   return hipGetLastError();
 }
 
 template <int D, bool GATED>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
-  const size_t items = (size_t)a.B * a.H * (a.L / C);
+  const size_t items = (size_t)a.B * a.H * ((a.L + C - 1) / C);
   t_solve_kernel<D, GATED><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
       static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace), a.L);
   return hipGetLastError();
@@ -1009,7 +1059,7 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
   if (!mode_erase(a.mode)) return 0;
-  return (size_t)a.B * a.H * (a.L / C) * kTFrags * kWave * sizeof(u32x4);
+  return (size_t)a.B * a.H * ((a.L + C - 1) / C) * kTFrags * kWave * sizeof(u32x4);
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {

@@ -87,7 +87,7 @@ typedef enum {
 typedef enum {
   LA_OK = 0,
   LA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  LA_ERR_SHAPE = 2,       /* non-positive size, or L not a multiple of C     */
+  LA_ERR_SHAPE = 2,       /* non-positive size, or sizes past the grid limit */
   LA_ERR_UNSUPPORTED = 3, /* (dk, dv, C, dtype, mode) outside the built set  */
   LA_ERR_ALIAS = 4,       /* an output overlaps an input (see each call)     */
   LA_ERR_HIP = 5,         /* HIP launch failure                              */
@@ -123,13 +123,15 @@ typedef enum {
  *   out        [B, H, L, dv]  dtype          output (written)
  *   S_final    [B, H, dk, dv] float32        final state (written); may be
  *                                            NULL; may equal S0 (in-place)
- *   B, H, L, dk, dv, C        sizes; L must be a multiple of C
+ *   B, H, L, dk, dv, C        sizes; L need not be a multiple of C: the
+ *                             last chunk then holds L mod C tokens
  *   mode       la_mode_t;  dtype  la_dtype_t
  *   workspace  device scratch of workspace_bytes bytes, 16-byte aligned,
  *              at least what la_chunk_workspace_bytes() reports for the same
  *              arguments; may be NULL when that is 0.  Its contents on entry
  *              are ignored and on return are unspecified.  The bf16 delta
- *              modes keep each chunk's T factor there (B*H*L/C * 6 KiB);
+ *              modes keep each chunk's T factor there (B*H*ceil(L/C) *
+ *              6 KiB);
  *              float inputs and the modes without erase (LINEAR,
  *              GATED_LINEAR) need none.
  *   stream     hipStream_t

@@ -70,7 +70,7 @@ def decode(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), S=fake(
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
     (dict(be=None), NULL), (dict(la=None), NULL), (dict(be=None, mode=1), NULL),
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=0), SHAPE), (dict(C=0), SHAPE),
-    (dict(L=96), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(dk=96, dv=96), UNSUP),
+    (dict(dk=64, dv=128), UNSUP), (dict(dk=96, dv=96), UNSUP),
     (dict(C=32, L=64), UNSUP), (dict(mode=4), UNSUP), (dict(dtype=7), UNSUP),
     (dict(la=None, mode=3), NULL),
     (dict(mode=-1), UNSUP), (dict(dtype=3), UNSUP),
@@ -105,7 +105,10 @@ def test_workspace_size():
     assert ws_bytes(lib, mode=0) == (OK, 0)
     assert ws_bytes(lib, mode=3) == (OK, 0)
     assert ws_bytes(lib, dtype=0) == (OK, 0)
-    assert ws_bytes(lib, L=96)[0] == SHAPE
+    # a partial last chunk gets its own T factor
+    assert ws_bytes(lib, L=96) == (OK, 2 * TSOLVE_BYTES)
+    assert ws_bytes(lib, L=1, B=3, H=2) == (OK, 6 * TSOLVE_BYTES)
+    assert ws_bytes(lib, L=65537, H=32, dk=128, dv=128) == (OK, 32 * 1025 * TSOLVE_BYTES)
     assert ws_bytes(lib, dk=96, dv=96)[0] == UNSUP
     assert ws_bytes(lib, mode=5)[0] == UNSUP
     assert lib.la_chunk_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL

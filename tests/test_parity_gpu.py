@@ -142,6 +142,31 @@ def test_chunk_short_sequences(mode, L):
     check_fwd(w, x, o_ref, S_ref)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("f32", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_ragged_lengths(mode, dtype, d):
+    """L not a multiple of C: one partial chunk (L = 1, 37), a full chunk
+    and a partial one (L = 69), and a partial chunk after the load pipeline
+    has reached its steady state (L = 389).  The output buffer is one row
+    longer than the call's out and pre-filled with NaN: the row past the end
+    must stay untouched, every row before it written."""
+    for L in (1, 37, 69, 389):
+        w = recipe(mode, dtype, B=1, H=3, L=L, d=d, s0_std=0.3, seed=41 + L)
+        log(f"chunk ragged {w}")
+        x = workloads.make_inputs(w)
+        o_ref, S_ref = oracle_fwd(x, mode)
+        check_fwd(w, x, o_ref, S_ref)
+        dev = to_cuda(x)
+        big = torch.full((w.B * w.H * w.L * w.dv + w.dv,), float("nan"), dtype=w.torch_dtype,
+                         device="cuda")
+        out = big[: w.B * w.H * w.L * w.dv].view(w.B, w.H, w.L, w.dv)
+        la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"],
+                     mode=mode, out=out)
+        torch.cuda.synchronize()
+        assert torch.isnan(big[w.B * w.H * w.L * w.dv:]).all(), "a store went past the end"
+        assert_close("o (guarded)", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]
@@ -241,10 +266,17 @@ def test_gate_edge_cases():
 
 
 def test_errors_surface_as_exceptions():
-    w = recipe("delta", "bf16", B=1, H=1, L=96, d=128)
+    """A library error code comes back as an exception naming it: an empty
+    sequence (L = 0) is a shape error, a head size outside the built set an
+    unsupported one; nothing is launched."""
+    w = recipe("delta", "bf16", B=1, H=1, L=64, d=128)
     x = to_cuda(workloads.make_inputs(w))
+    e = {n: t[:, :, :0] for n, t in x.items() if n != "S0"}
     with pytest.raises(la.LAError, match="LA_ERR_SHAPE"):
-        la.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], None, mode="delta")
+        la.chunk_fwd(e["q"], e["k"], e["v"], e["log_alpha"], e["beta"], None, mode="delta")
+    n = {n: t[..., :96].contiguous() for n, t in x.items() if n in ("q", "k", "v")}
+    with pytest.raises(la.LAError, match="LA_ERR_UNSUPPORTED"):
+        la.chunk_fwd(n["q"], n["k"], n["v"], x["log_alpha"], x["beta"], None, mode="delta")
 
 
 @pytest.mark.parametrize("d", [64, 128])
