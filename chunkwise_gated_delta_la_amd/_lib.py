@@ -33,6 +33,11 @@ def _declare(lib):
     lib.la_chunk_fwd.restype = i
     lib.la_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_workspace_bytes.restype = i
+    lib.la_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp,
+                                        i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_chunk_fwd_varlen.restype = i
+    lib.la_chunk_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_varlen_workspace_bytes.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i

@@ -125,6 +125,72 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     return out, S_final
 
 
+def chunk_varlen_workspace_bytes(N, H, T, dk, dv, *, mode="gated_delta", C=64,
+                                 dtype=torch.bfloat16, out_dtype=None):
+    """Workspace bytes ``la_chunk_fwd_varlen`` needs for these sizes
+    (``la_chunk_varlen_workspace_bytes``)."""
+    code = _dtype_code(dtype, out_dtype or dtype)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.get().la_chunk_varlen_workspace_bytes(N, H, T, dk, dv, C, _mode(mode), code,
+                                                          ctypes.byref(n)))
+    return n.value
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, S0, cu_seqlens, *, mode="gated_delta", C=64,
+                     out=None, S_final=None, return_state=True, out_dtype=None,
+                     workspace=None):
+    """Chunkwise forward over a packed batch (``la_chunk_fwd_varlen``).
+
+    q, k ``[H, T, dk]``, v ``[H, T, dv]``: the tokens of N sequences back to
+    back per head; log_alpha, beta ``[H, T]`` float32; cu_seqlens ``[N + 1]``
+    int32 on the GPU (sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1);
+    S0 ``[N, H, dk, dv]`` float32 or None.  Returns ``(out [H, T, dv],
+    S_final [N, H, dk, dv])``.
+    """
+    m = _mode(mode)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, T, d]")
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _need(k, "k", (H, T, dk), dt, dev)
+    _need(v, "v", (H, T, dv), dt, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (H, T), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (H, T), torch.float32, dev)
+    _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    odt = out_dtype or (out.dtype if out is not None else dt)
+    code = _dtype_code(dt, odt)
+    if out is None:
+        out = torch.empty((H, T, dv), dtype=odt, device=dev)
+    _need(out, "out", (H, T, dv), odt, dev)
+    if S_final is None and return_state:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(S_final, "S_final", (N, H, dk, dv), torch.float32, dev)
+    need = chunk_varlen_workspace_bytes(N, H, T, dk, dv, mode=mode, C=C, dtype=dt,
+                                        out_dtype=odt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        rc = lib.la_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(log_alpha if m in _DECAY else None),
+                                     _ptr(beta if m in _ERASE else None), _ptr(S0),
+                                     _ptr(out), _ptr(S_final), _ptr(cu_seqlens), N, H, T, dk, dv,
+                                     C, m, code, _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check(rc)
+    return out, S_final
+
+
 def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
                 out_dtype=None):
     """One recurrent decode step (``la_decode_step``), updating ``S`` in place.

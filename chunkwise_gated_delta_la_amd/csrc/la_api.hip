@@ -127,9 +127,78 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
 
 la::ChunkArgs chunk_args(const void* q, const void* k, const void* v, const float* log_alpha,
                          const float* beta, const float* S0, void* out, float* S_final, int B,
-                         int H, int L, int dk, int C, int mode, int dtype, void* workspace) {
+                         int H, int L, int dk, int C, int mode, int dtype, void* workspace,
+                         const int* cu = nullptr) {
   return la::ChunkArgs{q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
-                       dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, workspace};
+                       dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, workspace, cu};
+}
+
+// Shape checks of a packed batch: N sequences of H heads over T tokens.
+int check_varlen_shape(int N, int H, int T, int dk, int dv, int C, int mode, int dtype) {
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (N <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || C <= 0)
+    return fail(LA_ERR_SHAPE, "N, H, dk, dv and C must be positive and T non-negative");
+  if (dk != dv || (dk != 64 && dk != 128))
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd_varlen supports dk == dv in {64, 128}, got "
+                                    "dk=" + std::to_string(dk) + " dv=" + std::to_string(dv));
+  if (C != 64)
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd_varlen supports C == 64, got " +
+                                        std::to_string(C));
+  size_t n_qk;
+  if (!count({H, T, dk}, &n_qk) || n_qk > (SIZE_MAX >> 4) || !count({N, H, dk, dv}, &n_qk))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  const size_t slots = (size_t)H * (((size_t)T + C - 1) / C + (size_t)N);
+  if ((size_t)N * H * (dv / 16) > 0x7fffffffu || slots > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "N * H * dv / 16 or H * (ceil(T / C) + N) exceeds the launch grid");
+  return LA_OK;
+}
+
+// Workspace and alias checks, then the launches, shared by both forward
+// entry points.  n_* are element counts of the tensors; cu (packed batches)
+// is an input of cu_bytes bytes.
+int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_t n_s,
+              int dtype, size_t workspace_bytes, size_t cu_bytes, void* stream) {
+  const size_t need = la::chunk_workspace_bytes(a);
+  if (need > 0) {
+    if (!a.workspace)
+      return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
+                                        " bytes (la_chunk_workspace_bytes)");
+    if (workspace_bytes < need)
+      return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                        " bytes, this call needs " + std::to_string(need));
+    if (reinterpret_cast<uintptr_t>(a.workspace) % 16 != 0)
+      return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const Range rq(a.q, n_qk * esz), rk(a.k, n_qk * esz), rv(a.v, n_v * esz);
+  const Range rla(la::mode_decay(a.mode) ? a.log_alpha : nullptr, n_g * 4);
+  const Range rb(la::mode_erase(a.mode) ? a.beta : nullptr, n_g * 4);
+  const Range rs0(a.S0, n_s * 4), ro(a.out, n_v * osz), rsf(a.S_final, n_s * 4);
+  const Range rws(need > 0 ? a.workspace : nullptr, need);
+  const Range rcu(a.cu, cu_bytes);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &rcu})
+    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro, &rcu})
+    if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
+  if (rsf.overlaps(rs0) && (a.S0 != a.S_final))
+    return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf, &rcu})
+    if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = prof_mark(st);
+  if (la::chunk_needs_tsolve(a)) {
+    const hipError_t e = la::launch_tsolve(a, st);
+    hipEvent_t e1 = prof_mark(st);
+    prof_add("la_tsolve", e0, e1);
+    if (e != hipSuccess) return fail_hip("launching the T-solve kernel", e);
+    e0 = e1;
+  }
+  const hipError_t e = la::launch_chunk(a, st);
+  prof_add("la_chunk", e0, prof_mark(st));
+  if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
+  return LA_OK;
 }
 
 }  // namespace
@@ -166,46 +235,41 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   const la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk,
                                      C, mode, dtype, workspace);
-  const size_t need = la::chunk_workspace_bytes(a);
-  if (need > 0) {
-    if (!workspace)
-      return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
-                                        " bytes (la_chunk_workspace_bytes)");
-    if (workspace_bytes < need)
-      return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                        " bytes, this call needs " + std::to_string(need));
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-      return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  }
-  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
-  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
-  const Range rq(q, n_qk * esz), rk(k, n_qk * esz), rv(v, n_v * esz);
-  const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
-  const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
-  const Range rs0(S0, n_s * 4), ro(out, n_v * osz), rsf(S_final, n_s * 4);
-  const Range rws(need > 0 ? workspace : nullptr, need);
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0})
-    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro})
-    if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
-  if (rsf.overlaps(rs0) && (S0 != S_final))
-    return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf})
-    if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
+  return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipEvent_t e0 = prof_mark(st);
-  if (la::chunk_needs_tsolve(a)) {
-    const hipError_t e = la::launch_tsolve(a, st);
-    hipEvent_t e1 = prof_mark(st);
-    prof_add("la_tsolve", e0, e1);
-    if (e != hipSuccess) return fail_hip("launching the T-solve kernel", e);
-    e0 = e1;
-  }
-  const hipError_t e = la::launch_chunk(a, st);
-  prof_add("la_chunk", e0, prof_mark(st));
-  if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
+int la_chunk_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int C, int mode,
+                                    int dtype, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_varlen_shape(N, H, T, dk, dv, C, mode, dtype)) return e;
+  // the size depends on N, H, T only, not on the offsets themselves
+  static const int kAny = 0;
+  *bytes = la::chunk_workspace_bytes(
+      chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, N, H, T,
+                 dk, C, mode, dtype, nullptr, &kAny));
   return LA_OK;
+}
+
+int la_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* S0, void* out, float* S_final,
+                        const int* cu_seqlens, int N, int H, int T, int dk, int dv, int C,
+                        int mode, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out || !cu_seqlens)
+    return fail(LA_ERR_NULL, "q, k, v, out and cu_seqlens are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (int e = check_varlen_shape(N, H, T, dk, dv, C, mode, dtype)) return e;
+  size_t n_qk, n_v, n_g, n_s;
+  if (!count({H, T, dk}, &n_qk) || !count({H, T, dv}, &n_v) || !count({H, T}, &n_g) ||
+      !count({N, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  const la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, N, H, T, dk,
+                                     C, mode, dtype, workspace, cu_seqlens);
+  return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, (size_t)(N + 1) * 4,
+                   stream);
 }
 
 int la_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* __restrict__ S0, void* __restrict__ out_, float* __restrict__ S_final,
-    int L, int BH, int out_bf16) {
+    SeqMap sm, int BH, int out_bf16) {
   constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T
   constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   constexpr bool kSplit = IsBf16<T>::value;
@@ -435,7 +435,21 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(
   const int pcv = tid % VPR;    // prefetch: 16-byte vector within the row
   const int prp = tid / VPR;    // prefetch: row pair within a pass
 
-  const size_t hbase = (size_t)bh * L;          // first token row of the head
+  const SeqInfo si = seq_info(sm, bh);
+  const size_t hbase = si.row0;                 // first token row of the head
+  const int L = si.len;                         // tokens of this sequence
+  if (L == 0) {
+    // empty sequence: the state passes through
+    if (wave == 0 && S_final) {
+      const size_t sb = (size_t)bh * D * D;
+#pragma unroll
+      for (int r = 0; r < D / 4; ++r) {
+        const size_t e = sb + (size_t)(4 * r + g) * D + col;
+        S_final[e] = S0 ? S0[e] : 0.f;
+      }
+    }
+    return;
+  }
 
   // T as the A operand of U_new = T R: bf16 copy (split inputs) or Tf.
   const T* Top;
@@ -782,7 +796,7 @@ hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
   chunk_kernel<T, D, MODE><<<grid, block, 0, st>>>(
       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      a.log_alpha, a.beta, a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
+      a.log_alpha, a.beta, a.S0, a.out, a.S_final, seq_map(a), BH, a.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

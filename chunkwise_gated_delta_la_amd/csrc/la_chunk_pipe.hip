@@ -342,14 +342,18 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
   }
 }
 
-// One wave per (batch, head, chunk) (blocks numbered chunk-fastest): T of
-// the chunk into tws[item][f][lane], f = tfi(ti, kb), the operand fragment
-// T[16 ti + n][32 kb + kidx(g, j)] of lane (g, n).
+// One wave per T-factor slot (blocks numbered chunk-fastest within a head):
+// T of the slot's chunk into tws[slot][f][lane], f = tfi(ti, kb), the
+// operand fragment T[16 ti + n][32 kb + kidx(g, j)] of lane (g, n).  In the
+// fixed-length layout slot = (batch * H + head) * ceil(L / C) + chunk; in a
+// packed batch the slot of chunk j of sequence s is floor(cu[s] / C) + s + j
+// within its head (see SeqMap), found here by a binary search over s, and
+// slots no chunk maps to exit at once.
 template <int D, bool GATED>
 __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ k,
                                                         const float* __restrict__ log_alpha,
                                                         const float* __restrict__ beta,
-                                                        u32x4* __restrict__ tws, int L) {
+                                                        u32x4* __restrict__ tws, SeqMap sm) {
   constexpr int NKB = D / 32;
   __shared__ __attribute__((aligned(16))) float Ab[10 * 16 * LDB];
   __shared__ __attribute__((aligned(16))) float Df[4 * 16 * LDB];
@@ -360,15 +364,36 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
 
   const int lane = threadIdx.x;
   const int g = lane / 16, n = lane % 16;
-  const int NC = (L + C - 1) / C;
   const size_t item = blockIdx.x;
-  const size_t bh = item / NC;
-  const int c = (int)(item % NC);
-  const size_t row0 = bh * L + (size_t)c * C;
-  // rows of this chunk inside the sequence (the last chunk may be partial):
-  // rows past it read the last valid row and carry beta = 0, log alpha = 0,
-  // which makes their rows of A zero and of T the identity
-  const int nv = min(C, L - c * C);
+  size_t row0;
+  int nv;   // rows of this chunk inside its sequence
+  if (!sm.cu) {
+    const int NC = (sm.L + C - 1) / C;
+    const size_t bh = item / NC;
+    const int c = (int)(item % NC);
+    row0 = bh * sm.L + (size_t)c * C;
+    nv = min(C, sm.L - c * C);
+  } else {
+    const size_t sph = sm.slots_per_head();
+    const int h = (int)(item / sph), j = (int)(item % sph);
+    auto start = [&](int s) { return min(max(sm.cu[s], 0), sm.L); };
+    auto first_slot = [&](int s) { return start(s) / C + s; };
+    if (first_slot(0) > j) return;
+    int lo = 0, hi = sm.N - 1;      // largest s with first_slot(s) <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (first_slot(mid) <= j) lo = mid;
+      else hi = mid - 1;
+    }
+    const int a = start(lo), len = min(max(sm.cu[lo + 1], a), sm.L) - a;
+    const int c = j - first_slot(lo);
+    if (c * C >= len) return;       // no chunk in this slot
+    row0 = (size_t)h * sm.L + a + (size_t)c * C;
+    nv = min(C, len - c * C);
+  }
+  // rows past the sequence's end (a partial last chunk) read the last valid
+  // row and carry beta = 0, log alpha = 0, which makes their rows of A zero
+  // and of T the identity
 
   // K rows as operands of K K^T.  Both operands are rows of K, so any
   // assignment of the contraction index to (group, slot) works; here slot j
@@ -570,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const u32x4* __restrict__ tws, const float* __restrict__ S0, void* __restrict__ out_,
-    float* __restrict__ S_final, int L, int BH, int out_bf16) {
+    float* __restrict__ S_final, SeqMap sm, int BH, int out_bf16) {
   constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T, U_new
   constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
@@ -617,7 +642,21 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   }
   const int col0 = ct * 16;
   const int col = col0 + n;
-  const size_t hbase = (size_t)bh * L;
+  const SeqInfo si = seq_info(sm, bh);
+  const size_t hbase = si.row0;                 // first token row
+  const int L = si.len;                         // tokens of this sequence
+  const size_t sbase = (size_t)bh * D * D;      // its state
+  if (L == 0) {
+    // empty sequence: the state passes through
+    if (wave == 0 && S_final) {
+#pragma unroll
+      for (int r = 0; r < D / 4; ++r) {
+        const size_t e = sbase + (size_t)(4 * r + g) * D + col;
+        S_final[e] = S0 ? S0[e] : 0.f;
+      }
+    }
+    return;
+  }
   // Chunks; the last holds nlast rows (C unless L is not a multiple of C).
   // Rows past the sequence act as tokens that change nothing: beta = 0 and
   // log alpha = 0 (no erase, no write, no decay -- their rows of T are the
@@ -627,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   // causal.
   const int NC = (L + C - 1) / C;
   const int nlast = L - (NC - 1) * C;
-  const u32x4* tw = tws + (size_t)bh * NC * (kTFrags * kWave);
+  const u32x4* tw = tws + si.slot0 * (kTFrags * kWave);
 
   // lane offsets of operand row n over each dk block in a Q or K tile
   uint32_t roff[NKB];
@@ -708,7 +747,6 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     // ================= chain
     f32x4 S[NKT];
     Frag2<T16> sf[NKB];            // bf16 split of S, as published in Sx
-    const size_t sbase = (size_t)bh * D * D;
     if (S0) {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
@@ -1033,15 +1071,16 @@ hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
   chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
       static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v), a.log_alpha, a.beta, tws,
-      a.S0, a.out, a.S_final, a.L, BH, a.out_bf16 ? 1 : 0);
+      a.S0, a.out, a.S_final, seq_map(a), BH, a.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int D, bool GATED>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
-  const size_t items = (size_t)a.B * a.H * ((a.L + C - 1) / C);
+  const size_t items = chunk_slots(a);
   t_solve_kernel<D, GATED><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
-      static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace), a.L);
+      static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace),
+      seq_map(a));
   return hipGetLastError();
 }
 
@@ -1059,7 +1098,7 @@ hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
   if (!mode_erase(a.mode)) return 0;
-  return (size_t)a.B * a.H * ((a.L + C - 1) / C) * kTFrags * kWave * sizeof(u32x4);
+  return chunk_slots(a) * kTFrags * kWave * sizeof(u32x4);
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {

@@ -158,6 +158,55 @@ int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
                              int mode, int dtype, size_t* bytes);
 
 /*
+ * la_chunk_fwd_varlen -- la_chunk_fwd over a packed batch of N independent
+ * sequences of different lengths (the same method per sequence: each has its
+ * own initial and final state, and no token sees another sequence's).
+ *
+ * The sequences are concatenated along one token axis of T tokens;
+ * sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1.  Every
+ * sequence is cut into chunks of C from its own start, so its last chunk may
+ * be partial; an empty sequence leaves its state unchanged
+ * (S_final = S0).
+ *
+ *   q          [H, T, dk]     dtype          queries (per head, tokens of all
+ *                                            sequences back to back)
+ *   k          [H, T, dk]     dtype
+ *   v          [H, T, dv]     dtype
+ *   log_alpha  [H, T]         float32        as in la_chunk_fwd
+ *   beta       [H, T]         float32        as in la_chunk_fwd
+ *   S0         [N, H, dk, dv] float32        initial states; NULL = zeros
+ *   out        [H, T, dv]     dtype          output (written)
+ *   S_final    [N, H, dk, dv] float32        final states (written); may be
+ *                                            NULL; may equal S0
+ *   cu_seqlens [N + 1]        int32 DEVICE   offsets: 0 = cu_seqlens[0] <=
+ *                                            ... <= cu_seqlens[N] = T
+ *   N, H, T, dk, dv, C        N >= 1, T >= 0; sizes as in la_chunk_fwd
+ *   mode, dtype, workspace, workspace_bytes, stream   as in la_chunk_fwd;
+ *              the workspace size comes from la_chunk_varlen_workspace_bytes
+ *              (bf16 delta modes: H * (ceil(T/C) + N) * 6 KiB, whatever the
+ *              offsets)
+ *
+ * The offsets are read on the device and cannot be validated before the
+ * launch: offsets that are not nondecreasing within [0, T] give unspecified
+ * results, but every access stays inside the tensors (they are clamped).
+ * Aliasing: as in la_chunk_fwd, with cu_seqlens counted as an input.
+ */
+int la_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                        const float* log_alpha, const float* beta,
+                        const float* S0, void* out, float* S_final,
+                        const int* cu_seqlens, int N, int H, int T, int dk,
+                        int dv, int C, int mode, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * la_chunk_varlen_workspace_bytes -- workspace size for la_chunk_fwd_varlen
+ * with these sizes, mode and dtype, written to *bytes.  Same checks and
+ * error codes; LA_ERR_NULL for a NULL bytes.
+ */
+int la_chunk_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int C,
+                                    int mode, int dtype, size_t* bytes);
+
+/*
  * la_decode_step -- one token of the recurrence for B*H independent states
  * (decode / inference form), updating the state in place.
  *

@@ -55,6 +55,49 @@ def chunk(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(
                             ws, wsb, None)
 
 
+def varlen(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5),
+           out=fake(6), sf=fake(7), cu=fake(9), N=2, H=1, T=64, dk=64, dv=64, C=64, mode=2,
+           dtype=1, ws=fake(8), wsb=P):
+    return lib.la_chunk_fwd_varlen(q, k, v, la, be, s0, out, sf, cu, N, H, T, dk, dv, C, mode,
+                                   dtype, ws, wsb, None)
+
+
+def varlen_ws(lib, N=2, H=1, T=64, dk=64, dv=64, C=64, mode=2, dtype=1):
+    n = ctypes.c_size_t(0)
+    rc = lib.la_chunk_varlen_workspace_bytes(N, H, T, dk, dv, C, mode, dtype, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), NULL), (dict(q=None), NULL), (dict(la=None), NULL),
+    (dict(be=None, mode=1), NULL), (dict(N=0), SHAPE), (dict(T=-1), SHAPE), (dict(H=0), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(mode=4), UNSUP), (dict(C=32), UNSUP),
+    (dict(out=ctypes.c_void_p(10 * P - 64)), ALIAS),       # out overlaps cu_seqlens
+    (dict(ws=ctypes.c_void_p(10 * P - 1024)), ALIAS),      # workspace overlaps cu_seqlens
+    (dict(sf=ctypes.c_void_p(2 * P + 64)), ALIAS),         # S_final overlaps k
+    (dict(wsb=1), WS),
+])
+def test_chunk_fwd_varlen_rejects(kw, code):
+    lib = _lib.get()
+    assert varlen(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_varlen_workspace_size():
+    """One T slot per chunk a sequence can start, per head: ceil(T/C) + N,
+    whatever the offsets; nothing without erase or for float inputs."""
+    lib = _lib.get()
+    for (N, H, T) in ((1, 1, 1), (2, 3, 64), (5, 2, 1000), (100, 32, 65536)):
+        for mode in (1, 2):
+            assert varlen_ws(lib, N=N, H=H, T=T, mode=mode) == (
+                OK, H * (-(-T // 64) + N) * TSOLVE_BYTES)
+    assert varlen_ws(lib, mode=0) == (OK, 0)
+    assert varlen_ws(lib, mode=3) == (OK, 0)
+    assert varlen_ws(lib, dtype=0) == (OK, 0)
+    assert varlen_ws(lib, T=0, N=3, H=2) == (OK, 2 * 3 * TSOLVE_BYTES)
+    assert lib.la_chunk_varlen_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+
+
 def ws_bytes(lib, B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1):
     n = ctypes.c_size_t(12345)
     rc = lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, mode, dtype, ctypes.byref(n))

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import chunkwise_gated_delta_la_amd as la
+import oracle
 import workloads
 from _parity import assert_close, f64, log, oracle_decode, oracle_fwd, to_cuda
 from workloads import WORKLOADS, Workload
@@ -165,6 +166,78 @@ def test_chunk_ragged_lengths(mode, dtype, d):
         torch.cuda.synchronize()
         assert torch.isnan(big[w.B * w.H * w.L * w.dv:]).all(), "a store went past the end"
         assert_close("o (guarded)", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
+
+
+def _packed(lens, H, d, dtype, mode, seed):
+    """A packed batch of sequences of the given lengths: the workloads'
+    recipe drawn as one [1, H, T, d] sequence and cut at the offsets, plus
+    one initial state per sequence."""
+    T = int(sum(lens))
+    w = recipe(mode, dtype, B=1, H=H, L=max(T, 1), d=d, s0_std=0.3, seed=seed)
+    x = workloads.make_inputs(w)
+    gen = torch.Generator("cpu")
+    gen.manual_seed(seed + 1)
+    S0 = torch.randn((len(lens), H, d, d), generator=gen, dtype=torch.float32) * 0.3
+    x = {n: t[0, :, :T].contiguous() for n, t in x.items() if n != "S0"}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return w, x, S0, cu
+
+
+def _packed_oracle(x, S0, cu, mode):
+    """The oracle run on each sequence on its own."""
+    y = {n: t.to(torch.float64).numpy() for n, t in x.items()}
+    s0 = S0.to(torch.float64).numpy()
+    H, T, dv = y["v"].shape
+    o = np.zeros((H, T, dv))
+    S = np.empty_like(s0)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            S[s] = s0[s]
+            continue
+        sl = lambda t: t[None, :, a:b]   # noqa: E731  -> [1, H, len, ...]
+        os_, Ss = oracle.recurrent_fwd(sl(y["q"]), sl(y["k"]), sl(y["v"]), sl(y["log_alpha"]),
+                                       sl(y["beta"]), s0[s][None], mode)
+        o[:, a:b] = os_[0]
+        S[s] = Ss[0]
+    return o, S
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_varlen_packed(mode, dtype, d):
+    """A packed batch of 9 sequences: empty ones (first, middle, last), a
+    single token, partial and exact chunks, and several chunks; every token
+    and every final state against the oracle run per sequence.  out and
+    S_final start as NaN: all of out and every state must be written."""
+    lens = [0, 1, 63, 64, 0, 65, 200, 130, 0]
+    H = 3
+    w, x, S0, cu = _packed(lens, H, d, dtype, mode, seed=61)
+    log(f"chunk varlen {mode} {dtype} d{d} H{H} lens {lens}")
+    o_ref, S_ref = _packed_oracle(x, S0, cu, mode)
+    dev = {n: t.cuda() for n, t in x.items()}
+    T = int(cu[-1])
+    out = torch.full((H, T, d), float("nan"), dtype=w.torch_dtype, device="cuda")
+    S = torch.full((len(lens), H, d, d), float("nan"), dtype=torch.float32, device="cuda")
+    la.chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                        S0.cuda(), cu.cuda(), mode=mode, out=out, S_final=S)
+    torch.cuda.synchronize()
+    assert_close("o", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
+    assert_close("S_final", f64(S), S_ref, dtype)
+    # empty sequences pass their state through unchanged
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(S[s].cpu(), S0[s]), f"sequence {s} (empty) changed its state"
+    # and the packed call equals the fixed-length call on each sequence
+    for s in (2, 6):
+        a, b = int(cu[s]), int(cu[s + 1])
+        o1, S1 = la.chunk_fwd(*(dev[n][None, :, a:b].contiguous() for n in ("q", "k", "v")),
+                              dev["log_alpha"][None, :, a:b].contiguous(),
+                              dev["beta"][None, :, a:b].contiguous(), S0[s][None].cuda(),
+                              mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[:, a:b]) and torch.equal(S1[0], S[s]), (
+            f"sequence {s}: packed and fixed-length calls differ")
 
 
 def test_chunk_workload1_full():
