@@ -64,9 +64,13 @@ def log(msg):
 # Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,
 # o (2 dk e + 2 dv e), two float gates.
 
+ERASE_MODES = ("delta", "gated_delta")           # beta and the T factor
+GATE_BYTES = {"linear": 0, "delta": 4, "gated_delta": 8, "gated_linear": 4}
+
+
 def fwd_flops_per_token_head(w):
     d, C = w.dk, w.C
-    if w.mode == "linear":
+    if w.mode not in ERASE_MODES:
         return 4 * C * d + 4 * d * d
     return 10 * C * d + 6 * d * d
 
@@ -74,7 +78,7 @@ def fwd_flops_per_token_head(w):
 def t_bytes_per_token_head(w):
     """Bytes of the T factor per (token, head): written by la_tsolve, read
     by la_chunk (bf16 inputs in the delta modes only)."""
-    return T_BYTES_PER_CHUNK // w.C if (w.dtype == "bf16" and w.mode != "linear") else 0
+    return T_BYTES_PER_CHUNK // w.C if (w.dtype == "bf16" and w.mode in ERASE_MODES) else 0
 
 
 def kernel_bytes_per_token_head(name, w):
@@ -83,7 +87,7 @@ def kernel_bytes_per_token_head(name, w):
     writes o once (initial and final states are added per head); the T
     solve reads k and the gates and writes T."""
     e = 2 if w.dtype == "bf16" else 4
-    gates = {"linear": 0, "delta": 4, "gated_delta": 8}[w.mode]
+    gates = GATE_BYTES[w.mode]
     if name == "la_chunk":
         return fwd_min_bytes_per_token_head(w) + t_bytes_per_token_head(w)
     if name == "la_tsolve":
@@ -109,7 +113,7 @@ def decode_bytes_per_head(w):
 def fwd_min_bytes_per_token_head(w):
     """q, k, v, o and the gates the mode reads: what the op must move."""
     e = 2 if w.dtype == "bf16" else 4
-    gates = {"linear": 0, "delta": 4, "gated_delta": 8}[w.mode]
+    gates = GATE_BYTES[w.mode]
     return (2 * w.dk + 2 * w.dv) * e + gates
 
 
@@ -241,14 +245,7 @@ def bench_forward(w, steps, warmup):
         t1 = time.perf_counter()
     sec = (t1 - t0) / steps
     token_heads = w.B * w.H * w.L
-    kernels = {}
-    for name, (n, ms) in kt.stats.items():
-        avg_ms = ms / max(n, 1)
-        by = (kernel_bytes_per_token_head(name, w) * token_heads
-              + kernel_bytes_per_head(name, w) * w.B * w.H)
-        kernels[name] = {"launches": n, "avg_ms": round(avg_ms, 5),
-                         "algorithmic_bytes": by,
-                         "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1)}
+    kernels = _kernel_table(kt.stats, w, token_heads, w.B * w.H)
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
     dk = kernels[dom]
     traffic = measured_traffic(dom, w.name)
@@ -270,6 +267,87 @@ def bench_forward(w, steps, warmup):
     del copies
     torch.cuda.empty_cache()
     return x, res
+
+
+def _kernel_table(stats, w, token_heads, heads):
+    kernels = {}
+    for name, (n, ms) in stats.items():
+        avg_ms = ms / max(n, 1)
+        by = (kernel_bytes_per_token_head(name, w) * token_heads
+              + kernel_bytes_per_head(name, w) * heads)
+        kernels[name] = {"launches": n, "avg_ms": round(avg_ms, 5),
+                         "algorithmic_bytes": by,
+                         "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(by / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
+    return kernels
+
+
+def bench_mode(w, steps, warmup):
+    """Another mode at a forward workload's sizes (extra measurement)."""
+    _, res = bench_forward(w, steps, warmup)
+    return {"workload": w.name, "mode": w.mode, "tokens_per_s": round(res["value"], 1),
+            "ms_per_step": round(res["ms_per_step"], 4),
+            "mfma_frac_of_bf16_peak": round(res["mfma_frac_of_bf16_peak"], 4),
+            "hbm_frac_of_min_bytes": round(res["hbm_frac_of_min_bytes"], 4),
+            "kernels": res["kernels"]}
+
+
+def varlen_lengths(n, total, seed):
+    """Seeded length mix of a packed batch: n lengths summing to `total`,
+    log-uniform between 1 and 16 K tokens (short prompts next to long
+    documents), rescaled to the total."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    raw = np.exp(rng.uniform(0.0, np.log(16384.0), n))
+    lens = np.maximum(1, np.floor(raw / raw.sum() * total)).astype(np.int64)
+    lens[-1] += total - int(lens.sum())
+    return [int(v) for v in lens]
+
+
+def bench_varlen(base, n_seq, total, steps, warmup):
+    """Packed batch of n_seq sequences (total tokens) with the recipe of
+    `base` (mode, dtype, heads, d): la_chunk_fwd_varlen tokens/s."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    lens = varlen_lengths(n_seq, total, seed=base.seed + 7)
+    w = base.scaled(name=f"varlen_{base.mode}_{base.dtype}_n{n_seq}h{base.H}t{total}d{base.dk}",
+                    B=1, L=total, s0_std=0.0)
+    log(f"[bench] packed batch {w.name}: generating inputs")
+    x = workloads.make_inputs(w)
+    d = {k: t[0].contiguous().cuda() for k, t in x.items() if k != "S0"}
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32,
+                      device="cuda")
+    out = torch.empty((w.H, total, w.dv), dtype=w.torch_dtype, device="cuda")
+    S_final = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    nws = la.chunk_varlen_workspace_bytes(n_seq, w.H, total, w.dk, w.dv, mode=w.mode,
+                                          dtype=w.torch_dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        la.chunk_fwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None, cu,
+                            mode=w.mode, out=out, S_final=S_final, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with la.kernel_timer() as kt:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sec = (t1 - t0) / steps
+    token_heads = w.H * total
+    res = {"workload": w.name, "mode": w.mode, "sequences": n_seq, "tokens": total,
+           "length_min": min(lens), "length_max": max(lens),
+           "tokens_per_s": round(total / sec, 1), "ms_per_step": round(sec * 1e3, 4),
+           "kernels": _kernel_table(kt.stats, w, token_heads, n_seq * w.H)}
+    del d, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(w, warmup=1):
@@ -346,6 +424,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4,
                     help="forward workload id in workloads.WORKLOADS (default 4)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra measurements (other mode, packed batch)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -379,6 +459,13 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     x, fwd = bench_forward(w, args.steps, args.warmup)
     dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
+    extra = None
+    if not args.no_extra:
+        extra = {
+            "gated_linear": bench_mode(w.scaled(name=w.name.replace(w.mode, "gated_linear"),
+                                                mode="gated_linear"), args.steps, 1),
+            "varlen": bench_varlen(w, 64, w.L, args.steps, 1),
+        }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
         "metric": METRIC,
@@ -401,6 +488,7 @@ def main():
         "roofline": fwd["roofline"],
         "kernels": fwd["kernels"],
         "decode": dec,
+        "extra": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

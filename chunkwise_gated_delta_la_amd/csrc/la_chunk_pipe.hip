@@ -689,9 +689,9 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   auto issue_chunk = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
     const bool part = cc == NC - 1 && nlast < C;     // partial last chunk
-    if (wave == 1 || wave == 2) {
-      T16* dst = wave == 1 ? Ks[cc % 3] : Qs[cc % 3];
-      const T16* src = (wave == 1 ? k : q) + r0 * D;
+    // (one branch per wave, so that each LDS destination is a compile-time
+    // array and its address stays scalar)
+    auto tile = [&](T16* dst, const T16* src) {
       if (part) {
         uint32_t po[NTILE];
         dma_tile_offsets<D>(po, lane, nlast);
@@ -699,6 +699,11 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       } else {
         dma_tile<D>(dst, src, doff);
       }
+    };
+    if (wave == 1) {
+      tile(Ks[cc % 3], k + r0 * D);
+    } else if (wave == 2) {
+      tile(Qs[cc % 3], q + r0 * D);
     } else {
       const uint32_t vb = lds_addr(Vs[cc % 4]);
 #pragma unroll
