@@ -16,13 +16,13 @@
 //                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
 //                      U_new (publish S, already decayed for chunk c+1 in
 //                      the copy the chain keeps)
-//      waves 1-3       output of chunk c-1 from the U_new published at the
-//                      last barrier; the decay tables of chunk c+2; masked
-//                      decayed scores and diag(gam) Q S of chunk c for their
-//                      row tiles (wave 1: tiles 0 and 1, wave 2: tile 2,
-//                      wave 3: tile 3), kept in registers until the next
-//                      chunk; then DMA of chunk c+2 (Q, K, V, T) and of the
-//                      gates of chunk c+4
+//      waves 1-3       first the DMA of chunk c+2 (Q, K, V, T) and of the
+//                      gates of chunk c+4; then the output of chunk c-1 from
+//                      the U_new published at the last barrier; the decay
+//                      tables of chunk c+2; masked decayed scores and
+//                      diag(gam) Q S of chunk c for their row tiles (wave 1:
+//                      tiles 0 and 1, wave 2: tile 2, wave 3: tile 3), kept
+//                      in registers until the next chunk
 //
 //    so the serial chain only ever waits for its own products, and does as
 //    little besides them as possible: every LDS address it uses is one add
