@@ -81,28 +81,48 @@ def t_bytes_per_token_head(w):
     return T_BYTES_PER_CHUNK // w.C if (w.dtype == "bf16" and w.mode in ERASE_MODES) else 0
 
 
-def kernel_bytes_per_token_head(name, w):
+def kernel_bytes_per_token_head(name, w, P=1):
     """Algorithmic HBM bytes per (token, head) of a forward kernel: the
     chain kernel reads q, k, v, the gates the mode uses and T once and
     writes o once (initial and final states are added per head); the T
-    solve reads k and the gates and writes T."""
+    solve reads k and the gates and writes T.  With P > 1 segments the
+    state pass reads k, v, the gates and T of the first P - 1 segments and,
+    in the delta modes, k, the gates and T again for the P - 2 transitions;
+    the scan touches states only."""
     e = 2 if w.dtype == "bf16" else 4
     gates = GATE_BYTES[w.mode]
+    t = t_bytes_per_token_head(w)
     if name == "la_chunk":
-        return fwd_min_bytes_per_token_head(w) + t_bytes_per_token_head(w)
+        return fwd_min_bytes_per_token_head(w) + t
     if name == "la_tsolve":
-        return w.dk * e + gates + t_bytes_per_token_head(w)
+        return w.dk * e + gates + t
+    if name == "la_chunk_state":
+        s_part = (w.dk + w.dv) * e + gates + t
+        m_part = (w.dk * e + gates + t) if w.mode in ERASE_MODES else 0
+        return ((P - 1) * s_part + max(P - 2, 0) * m_part) / P
+    if name == "la_seg_scan":
+        return 0
     raise KeyError(name)
 
 
-def kernel_bytes_per_head(name, w):
-    """Per-head state bytes of a forward call: S0 read (if given), S_final
-    written (chain kernel only)."""
+def kernel_bytes_per_head(name, w, P=1):
+    """Per-head state bytes of a forward call.  Whole walk: S0 read (if
+    given), S_final written by the chain kernel.  P > 1 segments: the state
+    pass reads S0 and writes X (P - 1) and M (P - 2, delta modes); the scan
+    reads S0, X and M and writes S_in (P); the output pass reads S_in and
+    writes S_final."""
+    st = w.dk * w.dv * 4
+    erase = w.mode in ERASE_MODES
+    s0 = 1 if w.s0_std > 0 else 0
     if name == "la_tsolve":
         return 0
-    if name != "la_chunk":
-        raise KeyError(name)
-    return (2 if w.s0_std > 0 else 1) * w.dk * w.dv * 4
+    if name == "la_chunk":
+        return (s0 + 1) * st if P == 1 else (P + 1) * st
+    if name == "la_chunk_state":
+        return (s0 + (P - 1) + (P - 2 if erase else 0)) * st
+    if name == "la_seg_scan":
+        return (s0 + (P - 1) + (P - 2 if erase else 0) + P) * st
+    raise KeyError(name)
 
 
 def decode_bytes_per_head(w):
@@ -245,7 +265,8 @@ def bench_forward(w, steps, warmup):
         t1 = time.perf_counter()
     sec = (t1 - t0) / steps
     token_heads = w.B * w.H * w.L
-    kernels = _kernel_table(kt.stats, w, token_heads, w.B * w.H)
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C, dtype=w.torch_dtype)
+    kernels = _kernel_table(kt.stats, w, token_heads, w.B * w.H, P)
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
     dk = kernels[dom]
     traffic = measured_traffic(dom, w.name)
@@ -259,6 +280,7 @@ def bench_forward(w, steps, warmup):
     res = {
         "value": w.B * w.L / sec,
         "ms_per_step": sec * 1e3,
+        "segments": P,
         "mfma_frac_of_bf16_peak": flops / sec / BF16_MFMA_PEAK,
         "hbm_frac_of_min_bytes": min_bytes / sec / (HBM_PEAK_GBS * 1e9),
         "kernels": kernels,
@@ -269,12 +291,12 @@ def bench_forward(w, steps, warmup):
     return x, res
 
 
-def _kernel_table(stats, w, token_heads, heads):
+def _kernel_table(stats, w, token_heads, heads, P=1):
     kernels = {}
     for name, (n, ms) in stats.items():
         avg_ms = ms / max(n, 1)
-        by = (kernel_bytes_per_token_head(name, w) * token_heads
-              + kernel_bytes_per_head(name, w) * heads)
+        by = round(kernel_bytes_per_token_head(name, w, P) * token_heads
+                   + kernel_bytes_per_head(name, w, P) * heads)
         kernels[name] = {"launches": n, "avg_ms": round(avg_ms, 5),
                          "algorithmic_bytes": by,
                          "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1),
@@ -290,6 +312,54 @@ def bench_mode(w, steps, warmup):
             "mfma_frac_of_bf16_peak": round(res["mfma_frac_of_bf16_peak"], 4),
             "hbm_frac_of_min_bytes": round(res["hbm_frac_of_min_bytes"], 4),
             "kernels": res["kernels"]}
+
+
+def bench_segments(w, steps, warmup):
+    """Few long sequences (one GPU's share of a head-sharded workload): the
+    whole-sequence walk (segments = 1) against the sequence-parallel
+    forward with la_chunk_fwd's own segment plan, tokens/s of each."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C, dtype=w.torch_dtype)
+    log(f"[bench] segments {w.name} (plan P={P}): generating inputs")
+    x = workloads.make_inputs(w)
+    copies = [{k: t.cuda() for k, t in x.items()} for _ in range(2)]
+    out = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.torch_dtype, device="cuda")
+    S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    res = {"workload": w.name, "mode": w.mode, "segments": P}
+    for label, seg in (("whole", 1), ("segmented", P)):
+        nws = la.chunk_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C,
+                                       dtype=w.torch_dtype, segments=seg)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            d = copies[i % 2]
+            la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                         d["S0"] if w.s0_std > 0 else None, mode=w.mode, C=w.C, out=out,
+                         S_final=S_final, workspace=ws, segments=seg)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        with la.kernel_timer() as kt:
+            t0 = time.perf_counter()
+            for i in range(steps):
+                step(i)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        sec = (t1 - t0) / steps
+        res[label] = {"P": seg, "tokens_per_s": round(w.B * w.L / sec, 1),
+                      "ms_per_step": round(sec * 1e3, 4),
+                      "kernels": {k: {"launches": n, "avg_ms": round(ms / max(n, 1), 5)}
+                                  for k, (n, ms) in kt.stats.items()}}
+        del ws
+    res["speedup"] = round(res["segmented"]["tokens_per_s"] / res["whole"]["tokens_per_s"], 3)
+    del copies, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def varlen_lengths(n, total, seed):
@@ -423,6 +493,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4,
                     help="forward workload id in workloads.WORKLOADS (default 4)")
+    ap.add_argument("--shard", type=int, default=1, metavar="N",
+                    help="time one GPU's share of the forward workload when its heads are "
+                         "split over N GPUs (H / N heads on this GPU)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra measurements (other mode, packed batch)")
@@ -456,7 +529,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
-    w = workloads.WORKLOADS[args.workload]
+    w = workloads.head_shard(workloads.WORKLOADS[args.workload], args.shard)
     x, fwd = bench_forward(w, args.steps, args.warmup)
     dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
     extra = None
@@ -465,6 +538,7 @@ def main():
             "gated_linear": bench_mode(w.scaled(name=w.name.replace(w.mode, "gated_linear"),
                                                 mode="gated_linear"), args.steps, 1),
             "varlen": bench_varlen(w, 64, w.L, args.steps, 1),
+            "segments": bench_segments(workloads.WORKLOAD4_SHARD8, args.steps, 1),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
@@ -482,7 +556,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "B": w.B, "H": w.H, "L": w.L,
                    "dk": w.dk, "dv": w.dv, "C": w.C, "inputs": w.dtype + " q/k/v/out, "
-                   "float32 gates and state"},
+                   "float32 gates and state", "segments": fwd["segments"],
+                   "head_shard_of": args.shard},
         "mfma_frac_of_bf16_peak": round(fwd["mfma_frac_of_bf16_peak"], 4),
         "hbm_frac_of_min_bytes": round(fwd["hbm_frac_of_min_bytes"], 4),
         "roofline": fwd["roofline"],

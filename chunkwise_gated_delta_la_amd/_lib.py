@@ -38,6 +38,14 @@ def _declare(lib):
     lib.la_chunk_fwd_varlen.restype = i
     lib.la_chunk_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_varlen_workspace_bytes.restype = i
+    lib.la_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
+                                           i, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_chunk_fwd_segmented.restype = i
+    lib.la_chunk_segmented_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i,
+                                                       ctypes.POINTER(sz)]
+    lib.la_chunk_segmented_workspace_bytes.restype = i
+    lib.la_chunk_segments.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i)]
+    lib.la_chunk_segments.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i

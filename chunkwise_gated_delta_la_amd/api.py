@@ -60,20 +60,39 @@ def _stream(device):
 
 
 def chunk_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
-                          dtype=torch.bfloat16, out_dtype=None):
+                          dtype=torch.bfloat16, out_dtype=None, segments=None):
     """Workspace bytes ``la_chunk_fwd`` needs for these sizes
-    (``la_chunk_workspace_bytes``)."""
+    (``la_chunk_workspace_bytes``), or ``la_chunk_fwd_segmented`` with
+    ``segments`` segments (``la_chunk_segmented_workspace_bytes``)."""
     code = _dtype_code(dtype, out_dtype or dtype)
     n = ctypes.c_size_t(0)
-    _lib.check(_lib.get().la_chunk_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
-                                                   ctypes.byref(n)))
+    lib = _lib.get()
+    if segments is None:
+        rc = lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code, ctypes.byref(n))
+    else:
+        rc = lib.la_chunk_segmented_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
+                                                    int(segments), ctypes.byref(n))
+    _lib.check(rc)
+    return n.value
+
+
+def chunk_segments(B, H, L, dk, dv, *, mode="gated_delta", C=64, dtype=torch.bfloat16,
+                   out_dtype=None):
+    """Segments per sequence ``la_chunk_fwd`` runs in parallel for these
+    sizes (``la_chunk_segments``; 1 = the whole-sequence walk)."""
+    code = _dtype_code(dtype, out_dtype or dtype)
+    n = ctypes.c_int(0)
+    _lib.check(_lib.get().la_chunk_segments(B, H, L, dk, dv, C, _mode(mode), code,
+                                            ctypes.byref(n)))
     return n.value
 
 
 def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta",
               C=64, out=None, S_final=None, return_state=True, out_dtype=None,
-              workspace=None):
-    """Chunkwise forward (``la_chunk_fwd``).
+              workspace=None, segments=None):
+    """Chunkwise forward (``la_chunk_fwd``; ``la_chunk_fwd_segmented`` when
+    ``segments`` is given: each sequence cut into that many segments run in
+    parallel).
 
     q, k ``[B, H, L, dk]``, v ``[B, H, L, dv]`` (float32 or bfloat16, on the
     GPU); log_alpha, beta ``[B, H, L]`` float32; S0 ``[B, H, dk, dv]`` float32
@@ -107,20 +126,25 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     lib = _lib.get()
-    need = ctypes.c_size_t(0)
-    _lib.check(lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, m, code, ctypes.byref(need)))
-    if workspace is None and need.value > 0:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    need = chunk_workspace_bytes(B, H, L, dk, dv, mode=mode, C=C, dtype=dt, out_dtype=odt,
+                                 segments=segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
         if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
-        rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v),
-                              _ptr(log_alpha if m in _DECAY else None),
-                              _ptr(beta if m in _ERASE else None), _ptr(S0),
-                              _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
-                              code, _ptr(workspace), ws_bytes, _stream(dev))
+        la, be = _ptr(log_alpha if m in _DECAY else None), _ptr(beta if m in _ERASE else None)
+        if segments is None:
+            rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S0), _ptr(out),
+                                  _ptr(S_final), B, H, L, dk, dv, C, m, code, _ptr(workspace),
+                                  ws_bytes, _stream(dev))
+        else:
+            rc = lib.la_chunk_fwd_segmented(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S0),
+                                            _ptr(out), _ptr(S_final), B, H, L, dk, dv, C, m,
+                                            code, int(segments), _ptr(workspace), ws_bytes,
+                                            _stream(dev))
     _lib.check(rc)
     return out, S_final
 

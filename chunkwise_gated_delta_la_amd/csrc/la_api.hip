@@ -125,6 +125,18 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   return LA_OK;
 }
 
+// Segment count of la_chunk_fwd_segmented: 1 .. min(ceil(L / C), 1024);
+// above 1 only for bf16 inputs.
+int check_segments(int L, int C, int dtype, int segments) {
+  const long nc = ((long)L + C - 1) / C;
+  if (segments < 1 || segments > nc || segments > 1024)
+    return fail(LA_ERR_SHAPE, "segments must be in [1, min(ceil(L / C), 1024)], got " +
+                                  std::to_string(segments));
+  if (segments > 1 && dtype == LA_DTYPE_F32)
+    return fail(LA_ERR_UNSUPPORTED, "the sequence-parallel forward takes bf16 inputs");
+  return LA_OK;
+}
+
 la::ChunkArgs chunk_args(const void* q, const void* k, const void* v, const float* log_alpha,
                          const float* beta, const float* S0, void* out, float* S_final, int B,
                          int H, int L, int dk, int C, int mode, int dtype, void* workspace,
@@ -195,6 +207,16 @@ int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_
     if (e != hipSuccess) return fail_hip("launching the T-solve kernel", e);
     e0 = e1;
   }
+  if (a.P > 1) {
+    hipError_t e = la::launch_chunk_state(a, st);
+    hipEvent_t e1 = prof_mark(st);
+    prof_add("la_chunk_state", e0, e1);
+    if (e != hipSuccess) return fail_hip("launching the state pass", e);
+    e = la::launch_seg_scan(a, st);
+    e0 = prof_mark(st);
+    prof_add("la_seg_scan", e1, e0);
+    if (e != hipSuccess) return fail_hip("launching the segment scan", e);
+  }
   const hipError_t e = la::launch_chunk(a, st);
   prof_add("la_chunk", e0, prof_mark(st));
   if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
@@ -207,16 +229,41 @@ extern "C" {
 
 const char* la_last_error(void) { return g_last_error.c_str(); }
 
-const char* la_version(void) { return "lachunk 0.3.0 gfx950"; }
+const char* la_version(void) { return "lachunk 0.4.0 gfx950"; }
 
 int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode, int dtype,
                              size_t* bytes) {
   g_last_error.clear();
   if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
   if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
-  *bytes = la::chunk_workspace_bytes(
-      chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, L,
-                 dk, C, mode, dtype, nullptr));
+  la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, B, H, L, dk, C, mode, dtype, nullptr);
+  a.P = la::plan_segments(a);
+  *bytes = la::chunk_workspace_bytes(a);
+  return LA_OK;
+}
+
+int la_chunk_segments(int B, int H, int L, int dk, int dv, int C, int mode, int dtype,
+                      int* segments) {
+  g_last_error.clear();
+  if (!segments) return fail(LA_ERR_NULL, "segments is required");
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  *segments = la::plan_segments(chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                           nullptr, nullptr, B, H, L, dk, C, mode, dtype,
+                                           nullptr));
+  return LA_OK;
+}
+
+int la_chunk_segmented_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode,
+                                       int dtype, int segments, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  if (int e = check_segments(L, C, dtype, segments)) return e;
+  la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, B, H, L, dk, C, mode, dtype, nullptr);
+  a.P = segments;
+  *bytes = la::chunk_workspace_bytes(a);
   return LA_OK;
 }
 
@@ -233,8 +280,31 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
   if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
       !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
-  const la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk,
-                                     C, mode, dtype, workspace);
+  la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
+                               dtype, workspace);
+  a.P = la::plan_segments(a);
+  return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
+}
+
+int la_chunk_fwd_segmented(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* S0, void* out, float* S_final, int B,
+                           int H, int L, int dk, int dv, int C, int mode, int dtype, int segments,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  if (int e = check_segments(L, C, dtype, segments)) return e;
+  size_t n_qk, n_v, n_g, n_s;
+  if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
+      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  if ((size_t)B * H * (2 * (size_t)segments) * (dv / 16) > 0x7fffffffu)
+    return fail(LA_ERR_SHAPE, "B * H * segments exceeds the launch grid");
+  la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
+                               dtype, workspace);
+  a.P = segments;
   return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
 }
 

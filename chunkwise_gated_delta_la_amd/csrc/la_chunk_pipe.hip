@@ -590,12 +590,14 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 
 // ---------------------------------------------------------------- chain kernel
 
-template <int D, int MODE>
+// OUT = false is the state pass of the sequence-parallel forward: the chain
+// alone, with no Q and no outputs.
+template <int D, int MODE, bool OUT>
 __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    const u32x4* __restrict__ tws, const float* __restrict__ S0, void* __restrict__ out_,
-    float* __restrict__ S_final, SeqMap sm, int BH, int out_bf16) {
+    const u32x4* __restrict__ tws, void* __restrict__ out_, StreamMap smap, int NS,
+    int out_bf16) {
   constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T, U_new
   constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
@@ -628,31 +630,33 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int g = lane / 16;
   const int n = lane % 16;
 
-  int bh, ct;
+  // stream (sequence or segment) and column tile; the column tiles of one
+  // stream share an XCD (blocks go to XCDs round robin), so its Q, K and T
+  // reads are shared in that XCD's L2
+  int sidx, ct;
   {
     const int b = blockIdx.x;
-    if (BH % 8 == 0) {
+    if (NS % 8 == 0) {
       const int x = b % 8, s = b / 8;
       ct = s % NCT;
-      bh = (s / NCT) * 8 + x;
+      sidx = (s / NCT) * 8 + x;
     } else {
-      bh = b / NCT;
+      sidx = b / NCT;
       ct = b % NCT;
     }
   }
   const int col0 = ct * 16;
   const int col = col0 + n;
-  const SeqInfo si = seq_info(sm, bh);
+  const StreamInfo si = stream_info(smap, sidx);
   const size_t hbase = si.row0;                 // first token row
-  const int L = si.len;                         // tokens of this sequence
-  const size_t sbase = (size_t)bh * D * D;      // its state
+  const int L = si.len;                         // tokens of this stream
   if (L == 0) {
     // empty sequence: the state passes through
-    if (wave == 0 && S_final) {
+    if (wave == 0 && si.sf) {
 #pragma unroll
       for (int r = 0; r < D / 4; ++r) {
-        const size_t e = sbase + (size_t)(4 * r + g) * D + col;
-        S_final[e] = S0 ? S0[e] : 0.f;
+        const size_t e = (size_t)(4 * r + g) * D + col;
+        si.sf[e] = si.s0 ? si.s0[e] : 0.f;
       }
     }
     return;
@@ -686,6 +690,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   for (int m = 0; m < 2; ++m) voff[m] = v_off(m, C);
 
   // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
+  // (a transition stream reads no V: its ring holds zeros)
+  const bool vzero = si.eye;
   auto issue_chunk = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
     const bool part = cc == NC - 1 && nlast < C;     // partial last chunk
@@ -703,13 +709,15 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     if (wave == 1) {
       tile(Ks[cc % 3], k + r0 * D);
     } else if (wave == 2) {
-      tile(Qs[cc % 3], q + r0 * D);
+      if constexpr (OUT) tile(Qs[cc % 3], q + r0 * D);
     } else {
       const uint32_t vb = lds_addr(Vs[cc % 4]);
+      if (!vzero) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        dma16s(v + r0 * D + col0, part ? v_off(m, nlast) : voff[m],
-               __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+        for (int m = 0; m < 2; ++m)
+          dma16s(v + r0 * D + col0, part ? v_off(m, nlast) : voff[m],
+                 __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+      }
       if constexpr (kDelta) {
         const uint32_t tb = lds_addr(Ts[cc % 3]);
         const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
@@ -752,12 +760,17 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     // ================= chain
     f32x4 S[NKT];
     Frag2<T16> sf[NKB];            // bf16 split of S, as published in Sx
-    if (S0) {
+    if (si.eye) {
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[tj][i] = dk_of_row(16 * tj + 4 * g + i) == col ? 1.f : 0.f;
+    } else if (si.s0) {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S[tj][i] = S0[sbase + (size_t)dk_of_row(16 * tj + 4 * g + i) * D + col];
+          S[tj][i] = si.s0[(size_t)dk_of_row(16 * tj + 4 * g + i) * D + col];
     } else {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj) S[tj] = zero4();
@@ -973,15 +986,21 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       }
       __syncthreads();
     }
-    if (S_final) {
+    if (si.sf) {
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S_final[sbase + (size_t)dk_of_row(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+          si.sf[(size_t)dk_of_row(16 * tj + 4 * g + i) * D + col] = S[tj][i];
     }
   } else {
     // ================= side waves
+    if (vzero && wave == 3) {
+      // the V ring of a transition stream: zero once, never loaded
+      u32x4* vr = reinterpret_cast<u32x4*>(&Vs[0][0]);
+#pragma unroll
+      for (int i = 0; i < 4 * C * 16 * 2 / 16 / kWave; ++i) vr[i * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
+    }
     issue_chunk(0);
     if (NC > 1) issue_chunk(1);
     if (wave == 3)
@@ -1013,7 +1032,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       // opened this chunk, so the transfers get two chunks' time to land.
       if (c + 2 < NC) issue_chunk(c + 2);
       if (wave == 3 && c + NG - 1 < NC) issue_gates(c + NG - 1);
-      if (c > 0) {
+      if (OUT && c > 0) {
         const f32x4* U = Uf[kDelta ? (c - 1) % 2 : 0];
         const T16* Vp = Vs[(c - 1) % 4];
         const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
@@ -1029,7 +1048,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         }
       }
       if (wave == 2 && c + 2 < NC) tables(c + 2);
-      {
+      if constexpr (OUT) {
         const T16* Kc = Ks[c % 3];
         const float* gc = Gs[kGated ? c % 3 : 0];
         const float* ec = Es[kGated ? c % 3 : 0];
@@ -1051,32 +1070,205 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       if (wave == 3 && c == NC - 2) zero_v_tail();
       __syncthreads();
     }
-    const int c = NC - 1;
-    const size_t ob0 = (hbase + (size_t)c * C) * D + col;
-    const f32x4* U = Uf[kDelta ? c % 2 : 0];
-    const T16* Vp = Vs[c % 4];
-    if (wave == 1) {
-      out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, nlast);
-    } else if (wave == 2) {
-      out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, nlast);
-    } else {
-      out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
-      store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, nlast);
+    if constexpr (OUT) {
+      const int c = NC - 1;
+      const size_t ob0 = (hbase + (size_t)c * C) * D + col;
+      const f32x4* U = Uf[kDelta ? c % 2 : 0];
+      const T16* Vp = Vs[c % 4];
+      if (wave == 1) {
+        out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
+        store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, nlast);
+      } else if (wave == 2) {
+        out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
+        store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, nlast);
+      } else {
+        out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
+        store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, nlast);
+      }
     }
   }
 }
 
-template <int D, int MODE>
-hipError_t launch_one(const ChunkArgs& a, hipStream_t st) {
-  const int BH = a.B * a.H;
-  const T16* k = static_cast<const T16*>(a.k);
-  u32x4* tws = static_cast<u32x4*>(a.workspace);
-  const dim3 grid((unsigned)((size_t)BH * (D / 16))), block(kThreads);
-  chunk_pipe_kernel<D, MODE><<<grid, block, 0, st>>>(
-      static_cast<const T16*>(a.q), k, static_cast<const T16*>(a.v), a.log_alpha, a.beta, tws,
-      a.S0, a.out, a.S_final, seq_map(a), BH, a.out_bf16 ? 1 : 0);
+// ---------------------------------------------------------------- segment scan
+
+constexpr int kScanThreads = 512;
+constexpr int kScanCols = 8;         // state columns per workgroup
+constexpr int kScanGroup = 8;        // threads per segment of the log-alpha sums
+
+// States entering the segments of the sequence-parallel forward, from the
+// state pass's X_p and M_p: S_in(0) = S0, S_in(1) = X_0 and S_in(p+1) =
+// M_p S_in(p) + X_p, with M_p = exp(G_p) I, G_p the sum of log alpha over
+// segment p, in the modes without erase.  One workgroup per 8-column tile
+// of one sequence's state (M acts on the rows, so column tiles are
+// independent; narrow tiles shorten each step of the serial chain), float
+// FMA throughout, in a fixed order.
+//
+// Thread (r, u) (TPR threads per state row r) owns columns u CPT .. + CPT - 1
+// of the tile.  With erase, each step is an 8-column product over the D
+// rows of S_in(p) held in LDS: the thread sums the 4-row blocks b = u +
+// TPR j of its row of M_p (registers, loaded one step ahead), and the TPR
+// partial sums of a row are added across the adjacent lanes.  Without
+// erase there is no product: every segment's G_p is summed first, then each
+// thread runs the scalar recursion on its own elements.
+template <int D, bool ERASE, bool GATED>
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(
+    StreamMap m, const float* __restrict__ log_alpha) {
+  constexpr int SC = kScanCols;
+  constexpr int NCT = D / SC;
+  constexpr int TPR = kScanThreads / D;  // threads per state row: 4 or 8
+  constexpr int CPT = SC / TPR;          // columns per thread: 2 or 1
+  constexpr int NBT = D / 4 / TPR;       // 4-row blocks of the sums per thread
+  constexpr int LDS_P = 12;              // row pitch of the S_in tile (floats)
+  __shared__ __attribute__((aligned(16))) float Sc[ERASE ? D : 1][LDS_P];
+  __shared__ float G[GATED && !ERASE ? 1024 : 1];
+  const int bh = blockIdx.x / NCT, ct = blockIdx.x % NCT;
+  const int t = threadIdx.x, r = t / TPR, u = t % TPR;
+  const size_t e0 = (size_t)r * D + ct * SC + u * CPT;   // this thread's first element
+  const int nc = (m.sm.L + m.sm.C - 1) / m.sm.C;
+  const int P = m.P;
+  auto state = [&](const float* base, int p) { return base + ((size_t)bh * P + p) * m.dd; };
+
+  float cur[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) cur[j] = m.S0 ? m.S0[(size_t)bh * m.dd + e0 + j] : 0.f;
+  auto put = [&](int p) {
+    float* out = m.sin + ((size_t)bh * P + p) * m.dd + e0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) out[j] = cur[j];
+  };
+  put(0);
+  {
+    const float* X = state(m.xs, 0) + e0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) cur[j] = X[j];
+  }
+  put(1);
+
+  if constexpr (ERASE) {
+    f32x4 mv[NBT], mn[NBT];
+    float xv[CPT], xn[CPT];
+    auto fetch = [&](int p, f32x4 (&mr)[NBT], float (&xr)[CPT]) {
+      const float* M = state(m.ms, p) + (size_t)r * D;
+#pragma unroll
+      for (int j = 0; j < NBT; ++j) mr[j] = *reinterpret_cast<const f32x4*>(M + 4 * (u + TPR * j));
+      const float* X = state(m.xs, p) + e0;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) xr[j] = X[j];
+    };
+    if (P > 2) fetch(1, mv, xv);
+    for (int p = 2; p < P; ++p) {
+      __syncthreads();                   // the last step's reads of Sc are done
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) Sc[r][u * CPT + j] = cur[j];
+      __syncthreads();
+      if (p + 1 < P) fetch(p, mn, xn);   // next step's operands, in flight meanwhile
+      float a[SC];
+#pragma unroll
+      for (int c = 0; c < SC; ++c) a[c] = 0.f;
+#pragma unroll
+      for (int j = 0; j < NBT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float* row = Sc[4 * (u + TPR * j) + e];
+#pragma unroll
+          for (int c4 = 0; c4 < SC / 4; ++c4) {
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(row + 4 * c4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[4 * c4 + i] = fmaf(mv[j][e], sv[i], a[4 * c4 + i]);
+          }
+        }
+#pragma unroll
+      for (int o = 1; o < TPR; o *= 2)
+#pragma unroll
+        for (int c = 0; c < SC; ++c) a[c] += __shfl_xor(a[c], o);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) cur[j] = a[u * CPT + j] + xv[j];
+      put(p);
+#pragma unroll
+      for (int j = 0; j < NBT; ++j) mv[j] = mn[j];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) xv[j] = xn[j];
+    }
+  } else {
+    if constexpr (GATED) {
+      // G_p for p = 1 .. P - 2: kScanGroup threads per segment, a fixed
+      // strided order and a butterfly within the group
+      const float* la = log_alpha + (size_t)bh * m.sm.L;
+      constexpr int NSEG = kScanThreads / kScanGroup;
+      for (int p0 = 1; p0 < P - 1; p0 += NSEG) {
+        const int p = p0 + t / kScanGroup;
+        float sum = 0.f;
+        if (p < P - 1) {
+          const int t0 = seg_chunk0(p, P, nc) * m.sm.C;
+          const int t1 = min(seg_chunk0(p + 1, P, nc) * m.sm.C, m.sm.L);
+          for (int i = t0 + t % kScanGroup; i < t1; i += kScanGroup) sum += la[i];
+        }
+#pragma unroll
+        for (int o = 1; o < kScanGroup; o *= 2) sum += __shfl_xor(sum, o);
+        if (p < P - 1 && t % kScanGroup == 0) G[p] = sum;
+      }
+      __syncthreads();
+    }
+    // eight steps' X loads ahead of their stores (which the compiler must
+    // otherwise assume they depend on)
+    constexpr int kBatch = 8;
+    for (int p0 = 2; p0 < P; p0 += kBatch) {
+      float xb[kBatch][CPT];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (p0 + k < P) {
+          const float* X = state(m.xs, p0 + k - 1) + e0;
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) xb[k][j] = X[j];
+        }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (p0 + k < P) {
+          const float d = GATED ? __expf(G[p0 + k - 1]) : 1.f;
+#pragma unroll
+          for (int j = 0; j < CPT; ++j) cur[j] = fmaf(d, cur[j], xb[k][j]);
+          put(p0 + k);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launches
+
+constexpr int kComputeUnits = 256;   // gfx950 (MI355X)
+constexpr int kMinSegChunks = 4;     // shortest segment worth a pass
+constexpr int kMaxSegments = 64;
+
+// Workspace layout: the T fragments of every chunk (delta modes), then, for
+// P > 1, X, M and S_in, [BH, P, D, D] float each.
+size_t tsolve_bytes(const ChunkArgs& a) {
+  return mode_erase(a.mode) ? chunk_slots(a) * kTFrags * kWave * sizeof(u32x4) : 0;
+}
+
+size_t seg_states_offset(const ChunkArgs& a) { return (tsolve_bytes(a) + 255) & ~(size_t)255; }
+
+StreamMap stream_map(const ChunkArgs& a, int pass) {
+  StreamMap m{seq_map(a), a.S0, a.S_final, pass, a.P, mode_erase(a.mode),
+              (size_t)a.d * a.d, nullptr, nullptr, nullptr};
+  if (pass != kPassWhole) {
+    float* base = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + seg_states_offset(a));
+    const size_t n = (size_t)a.B * a.H * a.P * m.dd;
+    m.xs = base;
+    m.ms = base + n;
+    m.sin = base + 2 * n;
+  }
+  return m;
+}
+
+template <int D, int MODE, bool OUT>
+hipError_t launch_one(const ChunkArgs& a, int pass, hipStream_t st) {
+  const StreamMap m = stream_map(a, pass);
+  const size_t ns = (size_t)a.B * a.H * m.per_seq();
+  const dim3 grid((unsigned)(ns * (D / 16))), block(kThreads);
+  chunk_pipe_kernel<D, MODE, OUT><<<grid, block, 0, st>>>(
+      static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
+      a.log_alpha, a.beta, static_cast<const u32x4*>(a.workspace), a.out, m, (int)ns,
+      a.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1089,21 +1281,66 @@ hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const ChunkArgs& a, hipStream_t st) {
+template <int D, bool OUT>
+hipError_t launch_d(const ChunkArgs& a, int pass, hipStream_t st) {
   switch (a.mode) {
-    case kModeLinear: return launch_one<D, kModeLinear>(a, st);
-    case kModeDelta: return launch_one<D, kModeDelta>(a, st);
-    case kModeGatedLinear: return launch_one<D, kModeGatedLinear>(a, st);
-    default: return launch_one<D, kModeGatedDelta>(a, st);
+    case kModeLinear: return launch_one<D, kModeLinear, OUT>(a, pass, st);
+    case kModeDelta: return launch_one<D, kModeDelta, OUT>(a, pass, st);
+    case kModeGatedLinear: return launch_one<D, kModeGatedLinear, OUT>(a, pass, st);
+    default: return launch_one<D, kModeGatedDelta, OUT>(a, pass, st);
   }
+}
+
+template <int D>
+hipError_t launch_scan_d(const ChunkArgs& a, hipStream_t st) {
+  const StreamMap m = stream_map(a, kPassOut);
+  const dim3 grid((unsigned)((size_t)a.B * a.H * (D / kScanCols))), block(kScanThreads);
+  if (mode_erase(a.mode))
+    seg_scan_kernel<D, true, false><<<grid, block, 0, st>>>(m, a.log_alpha);
+  else if (mode_decay(a.mode))
+    seg_scan_kernel<D, false, true><<<grid, block, 0, st>>>(m, a.log_alpha);
+  else
+    seg_scan_kernel<D, false, false><<<grid, block, 0, st>>>(m, a.log_alpha);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
-  if (!mode_erase(a.mode)) return 0;
-  return chunk_slots(a) * kTFrags * kWave * sizeof(u32x4);
+  if (a.P <= 1) return tsolve_bytes(a);
+  return seg_states_offset(a) + 3 * (size_t)a.B * a.H * a.P * a.d * a.d * sizeof(float);
+}
+
+// Rough cost, in chunk steps of the whole-sequence walk, of P segments: the
+// state pass and the output pass, each in rounds of as many workgroups as
+// fit on the compute units at once (two state-pass workgroups share one: it
+// has no Q ring, at most 80 KiB of LDS), times their measured step costs
+// relative to a step of the walk (0.85 and 1.05), plus the scan (per
+// segment about 1.6 steps with erase, a dk x dk by dk x 8 product per
+// workgroup, and 0.3 without).
+int plan_segments(const ChunkArgs& a) {
+  if (!a.in_bf16 || a.cu) return 1;
+  const long chains = (long)a.B * a.H * (a.d / 16);
+  const int nc = (a.L + C - 1) / C;
+  auto rounds = [](long n, int per_cu) {
+    const long slots = (long)kComputeUnits * per_cu;
+    return (double)((n + slots - 1) / slots);
+  };
+  const double whole = rounds(chains, 1) * nc;
+  double best = whole;
+  int best_p = 1;
+  for (int P = 2; P <= nc / kMinSegChunks && P <= kMaxSegments; ++P) {
+    const long n1 = chains * ((P - 1) + (mode_erase(a.mode) ? P - 2 : 0));
+    const long n3 = chains * P;
+    const int seg = (nc + P - 1) / P;
+    const double scan = mode_erase(a.mode) ? 1.6 : 0.3;
+    const double cost = (0.85 * rounds(n1, 2) + 1.05 * rounds(n3, 1)) * seg + scan * P;
+    if (cost < best) {
+      best = cost;
+      best_p = P;
+    }
+  }
+  return best < 0.85 * whole ? best_p : 1;
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
@@ -1112,8 +1349,18 @@ hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
   return gated ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
 }
 
+hipError_t launch_chunk_state(const ChunkArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_d<64, false>(a, kPassState, st)
+                   : launch_d<128, false>(a, kPassState, st);
+}
+
+hipError_t launch_seg_scan(const ChunkArgs& a, hipStream_t st) {
+  return a.d == 64 ? launch_scan_d<64>(a, st) : launch_scan_d<128>(a, st);
+}
+
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st) {
-  return a.d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+  const int pass = a.P > 1 ? kPassOut : kPassWhole;
+  return a.d == 64 ? launch_d<64, true>(a, pass, st) : launch_d<128, true>(a, pass, st);
 }
 
 }  // namespace la

@@ -44,6 +44,9 @@ struct ChunkArgs {
   // laid out [H, L, d] (L = total tokens, B = number of sequences); NULL for
   // the fixed-length layout [B, H, L, d].
   const int* cu = nullptr;
+  // Segments per (b, h) sequence of the sequence-parallel forward (bf16,
+  // fixed-length layout only); 1 walks each sequence whole.
+  int P = 1;
 };
 
 // Where the tokens of one (sequence, head) pair bh = s * H + h live, shared
@@ -77,7 +80,7 @@ struct SeqInfo {
 
 // Offsets are clamped into [0, L] and made nondecreasing, so malformed
 // cu_seqlens can give wrong results but no out-of-bounds access.
-__device__ inline SeqInfo seq_info(const SeqMap& m, int bh) {
+__host__ __device__ inline SeqInfo seq_info(const SeqMap& m, int bh) {
   if (!m.cu) {
     const size_t nc = ((size_t)m.L + m.C - 1) / m.C;
     return SeqInfo{(size_t)bh * m.L, m.L, (size_t)bh * nc};
@@ -86,6 +89,92 @@ __device__ inline SeqInfo seq_info(const SeqMap& m, int bh) {
   const int a = min(max(m.cu[s], 0), m.L);
   const int b = min(max(m.cu[s + 1], a), m.L);
   return SeqInfo{(size_t)h * m.L + a, b - a, (size_t)h * m.slots_per_head() + a / m.C + s};
+}
+
+// ---- sequence-parallel forward
+//
+// The state after a run of chunks is affine in the state before it:
+// S_end = M S_start + X, where X is the end state from a zero start and M
+// (dk x dk) the product of the chunks' transitions (gam_C I - K^T diag(gam_C
+// / gam) W per chunk).  A (b, h) sequence cut into P chunk-aligned segments
+// is therefore run in three steps:
+//   state pass   every segment p < P - 1 from its local start (S0 for p = 0,
+//                else zero) to X_p; for p >= 1 also M_p, as the same chain
+//                with V = 0 started from the identity (erase modes only: the
+//                others have M_p = exp(sum of log alpha over p) I);
+//   scan         S_in(0) = S0, S_in(1) = X_0, S_in(p+1) = M_p S_in(p) + X_p;
+//   output pass  every segment from S_in(p), with its outputs; the last one
+//                writes S_final.
+// The passes have P times the parallelism of the whole-sequence walk for
+// 1/P of its serial depth; they pay when (b, h, column tile) chains alone
+// leave compute units idle.
+enum : int { kPassWhole = 0, kPassState = 1, kPassOut = 2 };
+
+// Chunk c0 of segment p of a sequence of nc chunks (balanced split; every
+// segment is non-empty for P <= nc).
+__host__ __device__ inline int seg_chunk0(int p, int P, int nc) {
+  return (int)(((long long)p * nc) / P);
+}
+
+// What one row of chain workgroups walks (one per column tile): a whole
+// (b, h) sequence, or one stream of a sequence-parallel pass.
+struct StreamMap {
+  SeqMap sm;
+  const float* S0;   // [BH, dk, dv] or NULL (zero)
+  float* S_final;    // [BH, dk, dv] or NULL
+  int pass;          // kPassWhole, kPassState or kPassOut
+  int P;             // segments per sequence (passes only)
+  bool erase;        // state pass also runs transition streams
+  size_t dd;         // elements of one state, dk * dv
+  float* xs;         // [BH, P, dk, dv]  X_p
+  float* ms;         // [BH, P, dk, dk]  M_p
+  float* sin;        // [BH, P, dk, dv]  S_in(p)
+  // streams per sequence
+  __host__ __device__ int per_seq() const {
+    if (pass == kPassWhole) return 1;
+    if (pass == kPassOut) return P;
+    return (P - 1) + (erase ? P - 2 : 0);
+  }
+};
+
+struct StreamInfo {
+  size_t row0;        // first token row
+  int len;            // tokens
+  size_t slot0;       // T-factor slot of the first chunk
+  const float* s0;    // start state, NULL: zero
+  float* sf;          // end state, NULL: not stored
+  bool eye;           // start from the identity, V read as zero
+};
+
+__host__ __device__ inline StreamInfo stream_info(const StreamMap& m, int s) {
+  if (m.pass == kPassWhole) {
+    const SeqInfo si = seq_info(m.sm, s);
+    return StreamInfo{si.row0, si.len, si.slot0, m.S0 ? m.S0 + (size_t)s * m.dd : nullptr,
+                      m.S_final ? m.S_final + (size_t)s * m.dd : nullptr, false};
+  }
+  const int n = m.per_seq();
+  const int bh = s / n, j = s % n;
+  const int nc = (m.sm.L + m.sm.C - 1) / m.sm.C;
+  int p = j;
+  bool eye = false;
+  if (m.pass == kPassState && j >= m.P - 1) {
+    p = j - (m.P - 1) + 1;       // transition stream of segment p >= 1
+    eye = true;
+  }
+  const int c0 = seg_chunk0(p, m.P, nc), c1 = seg_chunk0(p + 1, m.P, nc);
+  const int t0 = c0 * m.sm.C, t1 = min(c1 * m.sm.C, m.sm.L);
+  const size_t st = ((size_t)bh * m.P + p) * m.dd;
+  StreamInfo si{(size_t)bh * m.sm.L + t0, t1 - t0, (size_t)bh * nc + c0, nullptr, nullptr, eye};
+  if (m.pass == kPassOut) {
+    si.s0 = m.sin + st;
+    si.sf = (p == m.P - 1 && m.S_final) ? m.S_final + (size_t)bh * m.dd : nullptr;
+  } else if (eye) {
+    si.sf = m.ms + st;
+  } else {
+    si.s0 = (p == 0 && m.S0) ? m.S0 + (size_t)bh * m.dd : nullptr;
+    si.sf = m.xs + st;
+  }
+  return si;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
@@ -99,5 +188,12 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);        // dispatche
 hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st);    // la_chunk.hip
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st);   // la_chunk_pipe.hip
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a);               // la_chunk_pipe.hip
+// Segments per sequence the sequence-parallel forward uses for this call
+// (1: none), from the shapes alone (la_chunk_pipe.hip).
+int plan_segments(const ChunkArgs& a);
+// With P > 1: the state pass, then the scan, before launch_chunk runs the
+// output pass (la_chunk_pipe.hip).
+hipError_t launch_chunk_state(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_seg_scan(const ChunkArgs& a, hipStream_t st);
 
 }  // namespace la

@@ -131,10 +131,17 @@ typedef enum {
  *              arguments; may be NULL when that is 0.  Its contents on entry
  *              are ignored and on return are unspecified.  The bf16 delta
  *              modes keep each chunk's T factor there (B*H*ceil(L/C) *
- *              6 KiB);
- *              float inputs and the modes without erase (LINEAR,
- *              GATED_LINEAR) need none.
+ *              6 KiB); float inputs need none, nor do the modes without
+ *              erase (LINEAR, GATED_LINEAR) unless the call runs
+ *              sequence-parallel (below).
  *   stream     hipStream_t
+ *
+ * With bf16 inputs and few long sequences -- too few (b, h, 16-column)
+ * state tiles to occupy every compute unit -- the call runs each sequence
+ * as P segments in parallel (la_chunk_fwd_segmented), P chosen from the
+ * sizes alone (la_chunk_segments); the workspace then also holds three
+ * float arrays of B*H*P*dk*dv.  The result differs from the P = 1 walk by
+ * rounding only.
  *
  * Supported: dk = dv in {64, 128}, C = 64, all dtypes, all modes.
  * Aliasing: S_final == S0 is allowed; any other overlap of out or S_final
@@ -156,6 +163,66 @@ int la_chunk_fwd(const void* q, const void* k, const void* v,
  */
 int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
                              int mode, int dtype, size_t* bytes);
+
+/*
+ * la_chunk_fwd_segmented -- la_chunk_fwd with each (b, h) sequence cut into
+ * `segments` chunk-aligned pieces that run in parallel (sequence-parallel
+ * forward).
+ *
+ * The state after any run of chunks is an affine function of the state
+ * before it, S_end = M S_start + X, because every token's update is linear
+ * in the state; the chunkwise form is exact for any cut of the sequence
+ * ("FLASH" and "Lightning Attention" in "LinearAttention 概述": the output
+ * splits into an intra-block part and an inter-block part carried by the
+ * state).  The call therefore runs three steps on `stream`:
+ *   1. every segment but the last from its local start (S0 for the first,
+ *      zero otherwise) to its end state X_p, and, in the delta modes, every
+ *      inner segment's transition M_p (dk x dk, the same walk with V = 0
+ *      from the identity); without erase M_p is exp(sum of log_alpha over
+ *      the segment) times the identity;
+ *   2. a scan over the segments: S_in(0) = S0, S_in(1) = X_0, S_in(p+1) =
+ *      M_p S_in(p) + X_p, in float32;
+ *   3. every segment from S_in(p), writing its outputs; the last segment
+ *      writes S_final.
+ * The segments are balanced: segment p holds chunks floor(p n / P) ..
+ * floor((p+1) n / P) - 1 of the n = ceil(L/C) chunks.  The work grows (step
+ * 1 is extra), the serial depth shrinks from n to about 2 n / P chunk steps.
+ *
+ *   segments   P, 1 <= P <= min(ceil(L/C), 1024); P = 1 is la_chunk_fwd's
+ *              whole-sequence walk; P > 1 needs bf16 inputs (dtype
+ *              LA_DTYPE_BF16 or LA_DTYPE_BF16_F32OUT), else
+ *              LA_ERR_UNSUPPORTED; out of range: LA_ERR_SHAPE
+ *   workspace  at least la_chunk_segmented_workspace_bytes() for the same
+ *              arguments: the T factors as in la_chunk_fwd, then X, M and
+ *              S_in (3 * B*H*P*dk*dv float32) when P > 1
+ *   everything else as in la_chunk_fwd, including the aliasing rules
+ *              (S_final == S0 is allowed: S0 is read only by steps 1 and 2)
+ */
+int la_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta,
+                           const float* S0, void* out, float* S_final, int B,
+                           int H, int L, int dk, int dv, int C, int mode,
+                           int dtype, int segments, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * la_chunk_segmented_workspace_bytes -- workspace size for
+ * la_chunk_fwd_segmented with these arguments, written to *bytes.  Same
+ * checks and error codes; LA_ERR_NULL for a NULL bytes.
+ */
+int la_chunk_segmented_workspace_bytes(int B, int H, int L, int dk, int dv,
+                                       int C, int mode, int dtype,
+                                       int segments, size_t* bytes);
+
+/*
+ * la_chunk_segments -- the segment count la_chunk_fwd uses for these sizes,
+ * mode and dtype, written to *segments (1: the whole-sequence walk).  It
+ * depends on the arguments only, never on the data or the device.  Same
+ * checks and error codes as la_chunk_workspace_bytes; LA_ERR_NULL for a
+ * NULL segments.
+ */
+int la_chunk_segments(int B, int H, int L, int dk, int dv, int C, int mode,
+                      int dtype, int* segments);
 
 /*
  * la_chunk_fwd_varlen -- la_chunk_fwd over a packed batch of N independent
@@ -262,7 +329,7 @@ int la_profile_end(la_kernel_time_t* out, int capacity, int* count);
  * The pointer stays valid until the next call on the same thread. */
 const char* la_last_error(void);
 
-/* Library version string, e.g. "lachunk 0.3.0 gfx950". */
+/* Library version string, e.g. "lachunk 0.4.0 gfx950". */
 const char* la_version(void);
 
 #ifdef __cplusplus

@@ -42,6 +42,7 @@ def test_version_and_empty_error():
 
 
 P = 1 << 20            # fake, never dereferenced, well-separated pointers
+P_BIG = P
 
 
 def fake(i):
@@ -208,3 +209,80 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.get()
+
+
+def segmented(lib, P=2, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5),
+              out=fake(6), sf=fake(7), B=1, H=1, L=640, dk=64, dv=64, C=64, mode=2, dtype=1,
+              ws=fake(8), wsb=P_BIG):
+    return lib.la_chunk_fwd_segmented(q, k, v, la, be, s0, out, sf, B, H, L, dk, dv, C, mode,
+                                      dtype, P, ws, wsb, None)
+
+
+def seg_ws(lib, P, B=1, H=1, L=640, d=64, mode=2, dtype=1):
+    n = ctypes.c_size_t(0)
+    rc = lib.la_chunk_segmented_workspace_bytes(B, H, L, d, d, 64, mode, dtype, P,
+                                                ctypes.byref(n))
+    return rc, n.value
+
+
+def plan(lib, B, H, L, d=128, mode=2, dtype=1):
+    n = ctypes.c_int(0)
+    assert lib.la_chunk_segments(B, H, L, d, d, 64, mode, dtype, ctypes.byref(n)) == OK
+    return n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=0), SHAPE), (dict(P=-3), SHAPE), (dict(P=11), SHAPE),   # 10 chunks
+    (dict(P=2, dtype=0), UNSUP), (dict(q=None), NULL), (dict(be=None), NULL),
+    (dict(P=3, wsb=1), WS), (dict(sf=ctypes.c_void_p(2 * P + 64)), ALIAS),
+])
+def test_chunk_fwd_segmented_rejects(kw, code):
+    lib = _lib.get()
+    assert segmented(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_segmented_workspace_size():
+    """The T factors (delta modes), then X, M and S_in of every segment:
+    3 * B*H*P*d*d floats, placed at the next 256-byte boundary; P = 1 is
+    la_chunk_fwd's walk and needs only the T factors."""
+    lib = _lib.get()
+    for (B, H, L, d) in ((1, 1, 640, 64), (2, 3, 1000, 128), (1, 4, 65536, 128)):
+        nc = -(-L // 64)
+        for mode in (0, 1, 2, 3):
+            t = B * H * nc * TSOLVE_BYTES if mode in (1, 2) else 0
+            assert seg_ws(lib, 1, B, H, L, d, mode) == (OK, t)
+            for P in (2, 5, nc):
+                want = -(-t // 256) * 256 + 3 * B * H * P * d * d * 4
+                assert seg_ws(lib, P, B, H, L, d, mode) == (OK, want)
+    assert seg_ws(lib, 1, dtype=0) == (OK, 0)
+    assert seg_ws(lib, 2, dtype=0)[0] == UNSUP
+    assert seg_ws(lib, 11)[0] == SHAPE
+    assert lib.la_chunk_segmented_workspace_bytes(1, 1, 640, 64, 64, 64, 2, 1, 2, None) == NULL
+
+
+def test_segment_plan():
+    """The automatic plan: the whole-sequence walk wherever (b, h, column
+    tile) chains already occupy the 256 compute units or the sequence is
+    short; segments for few long sequences; and la_chunk_fwd's workspace
+    size follows the plan."""
+    lib = _lib.get()
+    assert plan(lib, 1, 32, 65536) == 1            # 256 chains: every CU busy
+    assert plan(lib, 8, 16, 4096, mode=0) == 1
+    assert plan(lib, 4, 16, 8192, mode=1) == 1
+    assert plan(lib, 1, 2, 256) == 1               # 4 chunks: too short to cut
+    assert plan(lib, 1, 2, 256, dtype=0) == 1      # float inputs: never
+    P = plan(lib, 1, 4, 65536)                     # one GPU's share of 32 heads over 8
+    assert 4 <= P <= 64
+    assert plan(lib, 1, 4, 65536) == P             # a function of the arguments only
+    rc, n = ws_bytes(lib, B=1, H=4, L=65536, dk=128, dv=128)
+    assert rc == OK and (OK, n) == seg_ws(lib, P, 1, 4, 65536, 128)
+    for mode in (0, 1, 2, 3):
+        for (B, H, L, d) in ((1, 1, 4096, 64), (1, 1, 100000, 128), (3, 1, 20000, 128)):
+            P = plan(lib, B, H, L, d, mode)
+            assert 1 <= P <= min(64, -(-L // 64))
+            rc, n = ws_bytes(lib, B=B, H=H, L=L, dk=d, dv=d, mode=mode)
+            assert (rc, n) == seg_ws(lib, P, B, H, L, d, mode)
+    n = ctypes.c_int(0)
+    assert lib.la_chunk_segments(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+    assert lib.la_chunk_segments(1, 1, 64, 96, 96, 64, 2, 1, ctypes.byref(n)) == UNSUP

@@ -415,6 +415,43 @@ def test_state_carry_and_decode_match_forward(mode):
     assert _rel(Sd, S_ref) < 1e-14
 
 
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_segment_state_is_affine_in_start_state(mode):
+    """Every token's update is affine in the state, so a run of tokens maps
+    its start state to M S_start + X: X the end state from a zero start, M
+    (dk x dk) the end state of the same run with V = 0 from the identity --
+    a scalar exp(sum of log alpha) times the identity when nothing is erased.
+    Cutting a sequence into segments, computing X and M of each from the
+    tokens alone and chaining S_in(p+1) = M_p S_in(p) + X_p gives every
+    segment's true start state; running the segments from those reproduces
+    the whole forward.  This is the decomposition behind the
+    sequence-parallel forward (the chunkwise form holds for any cut of the
+    sequence [LA-OV "FLASH"]; the inter-block part is carried by the state
+    alone [LA-OV "Lightning Attention"])."""
+    dk = dv = 4
+    q, k, v, la, be, S0 = _rand(43, B=1, H=2, L=23, dk=dk, dv=dv)
+    o_ref, S_ref = recurrent_fwd(q, k, v, la, be, S0, mode)
+    cuts = [0, 6, 7, 15, 23]
+    eye = np.broadcast_to(np.eye(dk), (1, 2, dk, dk))
+    S_in, outs = S0, []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        seg = lambda t: t[:, :, a:b]          # noqa: E731
+        _, X = recurrent_fwd(seg(q), seg(k), seg(v), seg(la), seg(be),
+                             np.zeros_like(S0), mode)
+        _, M = recurrent_fwd(seg(q), seg(k), np.zeros((1, 2, b - a, dk)), seg(la), seg(be),
+                             eye, mode)
+        if mode not in oracle.ERASE_MODES:
+            g = la[:, :, a:b].sum(-1) if mode in oracle.GATED_MODES else np.zeros((1, 2))
+            assert _rel(M, np.exp(g)[..., None, None] * eye) < 1e-14
+        # the true run from S_in: outputs and M S_in + X
+        o, S_end = recurrent_fwd(seg(q), seg(k), seg(v), seg(la), seg(be), S_in, mode)
+        assert _rel(np.einsum("bhij,bhjc->bhic", M, S_in) + X, S_end) < 1e-13
+        outs.append(o)
+        S_in = np.einsum("bhij,bhjc->bhic", M, S_in) + X
+    assert _rel(np.concatenate(outs, axis=2), o_ref) < 1e-13
+    assert _rel(S_in, S_ref) < 1e-13
+
+
 def test_modes_ignore_unused_gates():
     """linear ignores beta and alpha; delta ignores alpha (gated_linear's
     beta: test_gated_linear_special_cases)."""

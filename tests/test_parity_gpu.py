@@ -240,6 +240,86 @@ def test_chunk_varlen_packed(mode, dtype, d):
             f"sequence {s}: packed and fixed-length calls differ")
 
 
+# ------------------------------------------------------------------ sequence-parallel
+
+def _seg_call(d, mode, P, S0=None, S_final=None, out_dtype=None):
+    out, S = la.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0, mode=mode,
+                          segments=P, S_final=S_final, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, S
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_segmented(mode, d):
+    """Each sequence cut into P parallel segments (state pass, scan, output
+    pass) over 9 full chunks and a partial one: P = 2 (no transition), 3,
+    7 and 10 (one chunk per segment, the partial one last), every element
+    against the oracle; the bf16 output is the float one rounded; the
+    in-place state update (S_final is S0) works as in the whole walk."""
+    w = recipe(mode, "bf16", B=2, H=1, L=64 * 9 + 23, d=d, s0_std=0.3, seed=53)
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    dev = to_cuda(x)
+    for P in (2, 3, 7, 10):
+        log(f"chunk segmented P={P} {w}")
+        out, S = _seg_call(dev, mode, P, dev["S0"])
+        assert_close(f"o P={P}", f64(out), o_ref, "bf16", bf16_out=True)
+        assert_close(f"S_final P={P}", f64(S), S_ref, "bf16")
+    out32, S32 = _seg_call(dev, mode, 3, dev["S0"], out_dtype=torch.float32)
+    out, S = _seg_call(dev, mode, 3, dev["S0"])
+    assert torch.equal(out32.to(torch.bfloat16), out) and torch.equal(S32, S)
+    S_io = dev["S0"].clone()
+    _seg_call(dev, mode, 7, S_io, S_final=S_io)
+    assert_close("S in place P=7", f64(S_io), S_ref, "bf16")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_segmented_zero_state_and_single(mode):
+    """No S0 (the scan starts from zeros), and P = 1 through the segmented
+    entry point is the whole-sequence walk, bit for bit."""
+    w = recipe(mode, "bf16", B=1, H=3, L=64 * 6, d=128, s0_std=0.0, seed=59)
+    log(f"chunk segmented zero state {w}")
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    dev = to_cuda(x)
+    out, S = _seg_call(dev, mode, 4)
+    assert_close("o P=4", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final P=4", f64(S), S_ref, "bf16")
+    a_o, a_S = _seg_call(dev, mode, 1)
+    b_o, b_S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], None,
+                            mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(a_o, b_o) and torch.equal(a_S, b_S)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_auto_segments(mode):
+    """One long sequence: la_chunk_fwd cuts it by itself (the plan says
+    P > 1), every element against the oracle."""
+    w = recipe(mode, "bf16", B=1, H=1, L=4096 + 40, d=128, s0_std=0.2, seed=61)
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=mode)
+    log(f"chunk auto segments P={P} {w}")
+    assert P > 1
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    check_fwd(w, x, o_ref, S_ref)
+
+
+def test_chunk_shard_sampled():
+    """One GPU's share of workload 4 over 8 GPUs (B=1 H=4 L=65536 d=128) as
+    the bench runs it: sequence-parallel by the plan; the oracle recomputes
+    2 heads over the whole sequence."""
+    w = workloads.WORKLOAD4_SHARD8
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode)
+    log(f"chunk shard P={P} {w}")
+    assert P > 1
+    x = workloads.make_inputs(w)
+    heads = [(0, 0), (0, w.H - 1)]
+    o_ref, S_ref = oracle_fwd(x, w.mode, heads)
+    check_fwd(w, x, o_ref, S_ref, sel=lambda t: t[[0, 0], [0, w.H - 1]])
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]

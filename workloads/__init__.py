@@ -82,6 +82,23 @@ WORKLOADS = {
 }
 
 
+def head_shard(w, n):
+    """One GPU's share of forward workload ``w`` when its heads are split
+    over ``n`` GPUs: the same recipe with H / n heads (its own seed)."""
+    if n < 1 or w.H % n:
+        raise ValueError(f"{w.name}: {w.H} heads do not split over {n} GPUs")
+    if n == 1:
+        return w
+    return replace(w, name=w.name.replace(f"h{w.H}", f"h{w.H // n}"), H=w.H // n,
+                   seed=w.seed + 2)
+
+
+# One GPU's share of workload 4 when its 32 heads are split over 8 GPUs:
+# few (b, h) sequences, each long -- the shape the sequence-parallel forward
+# is for.
+WORKLOAD4_SHARD8 = head_shard(WORKLOADS[4], 8)
+
+
 def _normal(gen, shape):
     return torch.randn(shape, generator=gen, dtype=torch.float32)
 
