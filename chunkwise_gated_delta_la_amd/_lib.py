@@ -46,6 +46,15 @@ def _declare(lib):
     lib.la_chunk_segmented_workspace_bytes.restype = i
     lib.la_chunk_segments.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.la_chunk_segments.restype = i
+    lib.la_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
+                                       i, i, i, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+    lib.la_chunk_fwd_fused.restype = i
+    lib.la_chunk_fused_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i,
+                                                   ctypes.POINTER(sz)]
+    lib.la_chunk_fused_workspace_bytes.restype = i
+    lib.la_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp,
+                                         i, i, i, i, i, i, i, ctypes.c_float, vp]
+    lib.la_decode_step_fused.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i

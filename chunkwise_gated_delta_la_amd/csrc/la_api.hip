@@ -125,6 +125,22 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   return LA_OK;
 }
 
+// Prologue flags of the fused entry points, reduced to what the mode uses
+// (gate activations mean nothing in LINEAR mode).  Writes the effective
+// flags to *eff.
+int check_pro(int flags, float gate_scale, int mode, int* eff) {
+  if (flags < 0 || flags > (LA_PRO_GATES | LA_PRO_QK_L2NORM))
+    return fail(LA_ERR_UNSUPPORTED, "prologue flags must combine LA_PRO_GATES and "
+                                    "LA_PRO_QK_L2NORM, got " + std::to_string(flags));
+  const bool gates = la::mode_erase(mode) || la::mode_decay(mode);
+  int f = gates ? flags : (flags & ~LA_PRO_GATES);
+  if ((f & LA_PRO_GATES) && la::mode_decay(mode) &&
+      !(gate_scale > 0.f && gate_scale < 3.0e38f))
+    return fail(LA_ERR_UNSUPPORTED, "gate_scale must be positive and finite");
+  *eff = f;
+  return LA_OK;
+}
+
 // Segment count of la_chunk_fwd_segmented: 1 .. min(ceil(L / C), 1024);
 // above 1 only for bf16 inputs.
 int check_segments(int L, int C, int dtype, int segments) {
@@ -223,6 +239,46 @@ int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_
   return LA_OK;
 }
 
+// la_decode_step and la_decode_step_fused (flags 0: the inputs as given).
+int decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                const float* beta, float* S, void* out, int B, int H, int dk, int dv, int mode,
+                int dtype, int flags, float gate_scale, void* stream) {
+  if (!q || !k || !v || !S || !out) return fail(LA_ERR_NULL, "q, k, v, S and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  int pro = 0;
+  if (int e = check_pro(flags, gate_scale, mode, &pro)) return e;
+  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
+    return fail(LA_ERR_SHAPE, "B, H, dk and dv must be positive");
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    return fail(LA_ERR_UNSUPPORTED, "la_decode_step supports dk, dv in {64, 128}, got dk=" +
+                                        std::to_string(dk) + " dv=" + std::to_string(dv));
+  size_t n_k, n_v, n_g, n_s;
+  if (!count({B, H, dk}, &n_k) || !count({B, H, dv}, &n_v) || !count({B, H}, &n_g) ||
+      !count({B, H, dk, dv}, &n_s) || n_s > (SIZE_MAX >> 3))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  if (n_g > 0x7fffffffu) return fail(LA_ERR_SHAPE, "B * H exceeds the launch grid");
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const Range rq(q, n_k * esz), rk(k, n_k * esz), rv(v, n_v * esz);
+  const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
+  const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
+  const Range rs(S, n_s * 4), ro(out, n_v * osz);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
+    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
+    if (rs.overlaps(*in)) return fail(LA_ERR_ALIAS, "S overlaps an input");
+
+  la::DecodeArgs a{q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode,
+                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, pro, gate_scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = prof_mark(st);
+  hipError_t e = la::launch_decode(a, st);
+  prof_add("la_decode", e0, prof_mark(st));
+  if (e != hipSuccess) return fail_hip("launching the decode kernel", e);
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +294,23 @@ int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mod
   if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
   la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr, B, H, L, dk, C, mode, dtype, nullptr);
+  a.P = la::plan_segments(a);
+  *bytes = la::chunk_workspace_bytes(a);
+  return LA_OK;
+}
+
+int la_chunk_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode,
+                                   int dtype, int flags, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  int pro = 0;
+  if (int e = check_pro(flags, 1.f, mode, &pro)) return e;
+  if (pro && dtype == LA_DTYPE_F32)
+    return fail(LA_ERR_UNSUPPORTED, "the fused prologue takes bf16 inputs");
+  la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, B, H, L, dk, C, mode, dtype, nullptr);
+  a.pro = pro;
   a.P = la::plan_segments(a);
   *bytes = la::chunk_workspace_bytes(a);
   return LA_OK;
@@ -282,6 +355,31 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
                                dtype, workspace);
+  a.P = la::plan_segments(a);
+  return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
+}
+
+int la_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* a_raw,
+                       const float* b_raw, const float* S0, void* out, float* S_final, int B,
+                       int H, int L, int dk, int dv, int C, int mode, int dtype, int flags,
+                       float gate_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, a_raw, b_raw)) return e;
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  int pro = 0;
+  if (int e = check_pro(flags, gate_scale, mode, &pro)) return e;
+  if (pro && dtype == LA_DTYPE_F32)
+    return fail(LA_ERR_UNSUPPORTED, "the fused prologue takes bf16 inputs");
+  size_t n_qk, n_v, n_g, n_s;
+  if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
+      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  la::ChunkArgs a = chunk_args(q, k, v, a_raw, b_raw, S0, out, S_final, B, H, L, dk, C, mode,
+                               dtype, workspace);
+  a.pro = pro;
+  a.gate_scale = gate_scale;
   a.P = la::plan_segments(a);
   return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
 }
@@ -346,38 +444,16 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
                    const float* beta, float* S, void* out, int B, int H, int dk, int dv,
                    int mode, int dtype, void* stream) {
   g_last_error.clear();
-  if (!q || !k || !v || !S || !out) return fail(LA_ERR_NULL, "q, k, v, S and out are required");
-  if (int e = check_mode_dtype(mode, dtype)) return e;
-  if (int e = check_gates(mode, log_alpha, beta)) return e;
-  if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
-    return fail(LA_ERR_SHAPE, "B, H, dk and dv must be positive");
-  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-    return fail(LA_ERR_UNSUPPORTED, "la_decode_step supports dk, dv in {64, 128}, got dk=" +
-                                        std::to_string(dk) + " dv=" + std::to_string(dv));
-  size_t n_k, n_v, n_g, n_s;
-  if (!count({B, H, dk}, &n_k) || !count({B, H, dv}, &n_v) || !count({B, H}, &n_g) ||
-      !count({B, H, dk, dv}, &n_s) || n_s > (SIZE_MAX >> 3))
-    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
-  if (n_g > 0x7fffffffu) return fail(LA_ERR_SHAPE, "B * H exceeds the launch grid");
-  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
-  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
-  const Range rq(q, n_k * esz), rk(k, n_k * esz), rv(v, n_v * esz);
-  const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
-  const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
-  const Range rs(S, n_s * 4), ro(out, n_v * osz);
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
-    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
-    if (rs.overlaps(*in)) return fail(LA_ERR_ALIAS, "S overlaps an input");
+  return decode_step(q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode, dtype, 0, 0.f,
+                     stream);
+}
 
-  la::DecodeArgs a{q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode,
-                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipEvent_t e0 = prof_mark(st);
-  hipError_t e = la::launch_decode(a, st);
-  prof_add("la_decode", e0, prof_mark(st));
-  if (e != hipSuccess) return fail_hip("launching the decode kernel", e);
-  return LA_OK;
+int la_decode_step_fused(const void* q, const void* k, const void* v, const float* a_raw,
+                         const float* b_raw, float* S, void* out, int B, int H, int dk, int dv,
+                         int mode, int dtype, int flags, float gate_scale, void* stream) {
+  g_last_error.clear();
+  return decode_step(q, k, v, a_raw, b_raw, S, out, B, H, dk, dv, mode, dtype, flags,
+                     gate_scale, stream);
 }
 
 int la_profile_begin(void) {

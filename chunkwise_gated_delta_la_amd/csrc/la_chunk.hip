@@ -819,7 +819,9 @@ hipError_t launch_chunk_seq(const ChunkArgs& a, hipStream_t st) {
 // bf16 inputs run the two-kernel path of la_chunk_pipe.hip; float inputs,
 // which have no transposed LDS reads, run the phase-sequential kernel
 // above.
-bool chunk_needs_tsolve(const ChunkArgs& a) { return a.in_bf16 && mode_erase(a.mode); }
+bool chunk_needs_tsolve(const ChunkArgs& a) {
+  return a.in_bf16 && (mode_erase(a.mode) || a.pro != 0);
+}
 
 size_t chunk_workspace_bytes(const ChunkArgs& a) {
   return a.in_bf16 ? chunk_pipe_workspace_bytes(a) : 0;

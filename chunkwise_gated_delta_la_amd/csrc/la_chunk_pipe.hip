@@ -342,6 +342,47 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
   }
 }
 
+// Gate activations of the fused prologue, from their definitions: the
+// logistic function, and softplus(x) = log(1 + e^x) written as max(x, 0) +
+// log(1 + e^-|x|) so that no exponential overflows.
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+
+// What the fused prologue reads and writes besides k and the gates.
+struct ProIn {
+  const T16* q;      // queries (their norms)
+  ProArrays out;     // per-token gates and log inverse norms
+  int flags;         // kProGates | kProQKNorm
+  float gate_scale;
+  bool erase, decay; // the call's mode reads beta / log alpha
+};
+
+// Sum over each 16-lane group's four copies (lane groups g = 0..3 hold the
+// same rows): the row sums of squares of a chunk's fragments, then the one
+// for the lane's own row 16 g + n (selected without indexing a register
+// array by a lane-dependent value).
+template <int NKB>
+__device__ __forceinline__ float row_sumsq(const Frag<T16> (&f)[4][NKB], int g) {
+  float ss[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float a = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (float)f[t][kb].v[j];
+        a = fmaf(x, x, a);
+      }
+    a += __shfl_xor(a, 16);
+    a += __shfl_xor(a, 32);
+    ss[t] = a;
+  }
+  return g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3];
+}
+
 // One wave per T-factor slot (blocks numbered chunk-fastest within a head):
 // T of the slot's chunk into tws[slot][f][lane], f = tfi(ti, kb), the
 // operand fragment T[16 ti + n][32 kb + kidx(g, j)] of lane (g, n).  In the
@@ -349,17 +390,27 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
 // packed batch the slot of chunk j of sequence s is floor(cu[s] / C) + s + j
 // within its head (see SeqMap), found here by a binary search over s, and
 // slots no chunk maps to exit at once.
-template <int D, bool GATED>
+//
+// PRO: the fused prologue of the chunk's tokens first -- the gates the op
+// uses (raw scores through sigmoid / -gate_scale softplus when asked) and
+// log(1 / |q_t|), log(1 / |k_t|) (q and k normalised as x / sqrt(|x|^2 +
+// eps)), written per token for the chain kernels.  Normalised keys enter A
+// as diag(r) K K^T diag(r): the logs of r are folded into the decay
+// exponents (row g_r + log r_r, column g_i - log r_i).  TS = false: the
+// prologue alone (modes without erase have no T).
+template <int D, bool GATED, bool PRO, bool TS>
 __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ k,
                                                         const float* __restrict__ log_alpha,
                                                         const float* __restrict__ beta,
-                                                        u32x4* __restrict__ tws, SeqMap sm) {
+                                                        u32x4* __restrict__ tws, SeqMap sm,
+                                                        ProIn pro) {
   constexpr int NKB = D / 32;
-  __shared__ __attribute__((aligned(16))) float Ab[10 * 16 * LDB];
-  __shared__ __attribute__((aligned(16))) float Df[4 * 16 * LDB];
-  __shared__ __attribute__((aligned(16))) float T32f[16 * LDB];
-  __shared__ __attribute__((aligned(16))) T16 Tb[C * LDT];
-  __shared__ __attribute__((aligned(16))) float gsh[C];
+  __shared__ __attribute__((aligned(16))) float Ab[TS ? 10 * 16 * LDB : 1];
+  __shared__ __attribute__((aligned(16))) float Df[TS ? 4 * 16 * LDB : 1];
+  __shared__ __attribute__((aligned(16))) float T32f[TS ? 16 * LDB : 1];
+  __shared__ __attribute__((aligned(16))) T16 Tb[TS ? C * LDT : 1];
+  __shared__ __attribute__((aligned(16))) float gsh[C];               // row exponents
+  __shared__ __attribute__((aligned(16))) float gcsh[PRO ? C : 1];    // column exponents
   __shared__ __attribute__((aligned(16))) float bsh[C];
 
   const int lane = threadIdx.x;
@@ -406,54 +457,89 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
       kf[t][kb].v = *reinterpret_cast<const bf16x8*>(
           k + (row0 + min(16 * t + n, nv - 1)) * D + 32 * kb + 8 * g);
   const int lr = min(lane, nv - 1);
-  const float bv = lane < nv ? beta[row0 + lr] : 0.f;
-  float gv = 0.f;
-  if constexpr (GATED) gv = wave_inclusive_scan(lane < nv ? log_alpha[row0 + lr] : 0.f);
-  gsh[lane] = gv;
-  bsh[lane] = bv;
-  // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
+  float bv = 0.f, av = 0.f, lkv = 0.f;
+  if constexpr (PRO) {
+    const bool act = pro.flags & kProGates;
+    if (pro.erase && lane < nv) {
+      const float b = beta[row0 + lr];
+      bv = act ? sigmoid_f(b) : b;
+    }
+    if (pro.decay && lane < nv) {
+      const float a = log_alpha[row0 + lr];
+      av = act ? -pro.gate_scale * softplus_f(a) : a;
+    }
+    float lqv = 0.f;
+    if (pro.flags & kProQKNorm) {
+      Frag<T16> qf[4][NKB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
-    Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          qf[t][kb].v = *reinterpret_cast<const bf16x8*>(
+              pro.q + (row0 + min(16 * t + n, nv - 1)) * D + 32 * kb + 8 * g);
+      lkv = -0.5f * __logf(row_sumsq<NKB>(kf, g) + kQKNormEps);
+      lqv = -0.5f * __logf(row_sumsq<NKB>(qf, g) + kQKNormEps);
+    }
+    if (lane < nv) {
+      pro.out.beta[row0 + lane] = bv;
+      pro.out.log_alpha[row0 + lane] = av;
+      pro.out.lq[row0 + lane] = lqv;
+      pro.out.lk[row0 + lane] = lkv;
+    }
+  } else {
+    bv = lane < nv ? beta[row0 + lr] : 0.f;
+    if constexpr (GATED) av = lane < nv ? log_alpha[row0 + lr] : 0.f;
   }
-  __syncthreads();
+  if constexpr (TS) {
+    float gv = 0.f;
+    if constexpr (GATED) gv = wave_inclusive_scan(av);
+    gsh[lane] = gv + lkv;
+    if constexpr (PRO) gcsh[lane] = gv - lkv;
+    bsh[lane] = bv;
+    // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
+      Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
+    }
+    __syncthreads();
 
-  // A blocks (R, t), t <= R: element (4 g + e, n) is row 16 R + 4 g + e,
-  // column 16 t + n
+    // A blocks (R, t), t <= R: element (4 g + e, n) is row 16 R + 4 g + e,
+    // column 16 t + n
 #pragma unroll
-  for (int R = 0; R < 4; ++R) {
-    const f32x4 br = *reinterpret_cast<const f32x4*>(bsh + 16 * R + 4 * g);
-    const f32x4 gr = *reinterpret_cast<const f32x4*>(gsh + 16 * R + 4 * g);
+    for (int R = 0; R < 4; ++R) {
+      const f32x4 br = *reinterpret_cast<const f32x4*>(bsh + 16 * R + 4 * g);
+      const f32x4 gr = *reinterpret_cast<const f32x4*>(gsh + 16 * R + 4 * g);
 #pragma unroll
-    for (int t = 0; t <= R; ++t) {
-      f32x4 acc = zero4();
+      for (int t = 0; t <= R; ++t) {
+        f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(kf[R][kb], kf[t][kb], acc);
-      const float gc = gsh[16 * t + n];
-      float* blk = Ab + bid(R, t) * 16 * LDB;
+        for (int kb = 0; kb < NKB; ++kb) mma(kf[R][kb], kf[t][kb], acc);
+        const float gc = (PRO ? gcsh : gsh)[16 * t + n];
+        float* blk = Ab + bid(R, t) * 16 * LDB;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = R > t || 4 * g + e > n;
-        float decay = 1.f;
-        if constexpr (GATED) decay = __expf(keep ? gr[e] - gc : 0.f);
-        blk[(4 * g + e) * LDB + n] = keep ? br[e] * acc[e] * decay : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = R > t || 4 * g + e > n;
+          float decay = 1.f;
+          if constexpr (GATED) decay = __expf(keep ? gr[e] - gc : 0.f);
+          blk[(4 * g + e) * LDB + n] = keep ? br[e] * acc[e] * decay : 0.f;
+        }
       }
     }
+    __syncthreads();
+    t_diag(Ab, Df, Tb, g, n);
+    __syncthreads();
+    t_col(Ab, Df, T32f, Tb, g, n);
+    __syncthreads();
+    u32x4* dst = tws + item * (kTFrags * kWave);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int kb = 0; kb <= ti / 2; ++kb) {
+        const Frag<T16> f = frag_row(Tb + (16 * ti + n) * LDT + 32 * kb, g);
+        dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.v);
+      }
   }
-  __syncthreads();
-  t_diag(Ab, Df, Tb, g, n);
-  __syncthreads();
-  t_col(Ab, Df, T32f, Tb, g, n);
-  __syncthreads();
-  u32x4* dst = tws + item * (kTFrags * kWave);
-#pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-    for (int kb = 0; kb <= ti / 2; ++kb) {
-      const Frag<T16> f = frag_row(Tb + (16 * ti + n) * LDT + 32 * kb, g);
-      dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.v);
-    }
 }
 
 
@@ -463,10 +549,14 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
 // registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
 // Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
 // gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].  roff[kb] is the lane's
-// byte offset of operand row n over dk block kb in a Q or K tile.
+// byte offset of operand row n over dk block kb in a Q or K tile.  The decay
+// of score (r, i) is exp(gsc[r] - gkc[i]) and Q S row r is scaled by
+// esc[r]: the exponents g and the factors exp(g), or with normalised q and
+// k the same with the logs of the inverse norms folded in.
 template <int D, bool GATED, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
-                                          const float* esc, const Frag<T16>* Sx,
+                                          const float* gkc, const float* esc,
+                                          const Frag<T16>* Sx,
                                           const uint32_t (&roff)[D / 32], f32x4 (&sc)[2][4],
                                           f32x4 (&qs)[2], int g, int n, int lane) {
   constexpr int NKB = D / 32;
@@ -496,7 +586,7 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
       eq[u] = *reinterpret_cast<const f32x4*>(esc + 16 * (u ? TI1 : TI0) + 4 * g);
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gsc + 16 * t + 4 * g);
+    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gkc + 16 * t + 4 * g);
   }
 #pragma unroll
   for (int u = 0; u < NTI; ++u) {
@@ -591,15 +681,23 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 // ---------------------------------------------------------------- chain kernel
 
 // OUT = false is the state pass of the sequence-parallel forward: the chain
-// alone, with no Q and no outputs.
-template <int D, int MODE, bool OUT>
+// alone, with no Q and no outputs.  FUSED: q and k are normalised inside the
+// op -- with r_t = 1 / |x_t| per token, every product of the method sees
+// diag(r) K and diag(r) Q only through per-row factors that the decay tables
+// already apply, so the inverse norms (their logs lq, lk, from the prologue)
+// are folded into the tables and no product changes:
+//   scores  exp((g_r + lq_r) - (g_i - lk_i)),  Q S rows  exp(g + lq),
+//   update  exp(g_C - g + lk),  erase  beta exp(g + lk)
+// (MODE is then one of the decayed modes; log alpha = 0 stands for none).
+template <int D, int MODE, bool OUT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const u32x4* __restrict__ tws, void* __restrict__ out_, StreamMap smap, int NS,
-    int out_bf16) {
+    int out_bf16, ProArrays pro) {
   constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T, U_new
   constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
+  static_assert(!FUSED || kGated, "normalised q, k ride in the decay tables");
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
   constexpr int NCT = D / 16;                    // column tiles per head
@@ -608,8 +706,9 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   constexpr uint32_t kRows16 = 32 * D;           // bytes of 16 tile rows
   constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
   constexpr int NG = 5;                          // gate ring depth (DMA 4 ahead)
-  // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha
-  constexpr int NDMA3 = 2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0);
+  // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha, lk, lq
+  constexpr int NDMA3 =
+      2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0) + (FUSED ? 1 : 0) + (FUSED && OUT ? 1 : 0);
 
   __shared__ __attribute__((aligned(16))) T16 Qs[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
@@ -621,6 +720,12 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
+  // (the state pass has no Q side: only lk)
+  constexpr bool kQSide = FUSED && OUT;
+  __shared__ __attribute__((aligned(16))) float LQs[kQSide ? NG : 1][C];  // log(1 / |q|)
+  __shared__ __attribute__((aligned(16))) float LKs[FUSED ? NG : 1][C];   // log(1 / |k|)
+  __shared__ __attribute__((aligned(16))) float Gk[kQSide ? 3 : 1][C];    // g - lk (score columns)
+  __shared__ __attribute__((aligned(16))) float Eq[kQSide ? 3 : 1][C];    // exp(g + lq) (Q S rows)
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
   __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
 
@@ -734,6 +839,8 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const uint32_t go = (uint32_t)(cc == NC - 1 ? min(lane, nlast - 1) : lane) * 4;
     if constexpr (kDelta) dma4s(beta + r0, go, lds_addr(Bs[cc % NG]));
     if constexpr (kGated) dma4s(log_alpha + r0, go, lds_addr(Ls[cc % NG]));
+    if constexpr (FUSED) dma4s(pro.lk + r0, go, lds_addr(LKs[cc % NG]));
+    if constexpr (FUSED && OUT) dma4s(pro.lq + r0, go, lds_addr(LQs[cc % NG]));
   };
   // Gates of rows past the sequence set to zero, then the decay tables of
   // chunk cc from its gates (wave 2, after the gates have landed)
@@ -742,7 +849,20 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       if constexpr (kDelta) Bs[cc % NG][lane] = 0.f;
       if constexpr (kGated) Ls[cc % NG][lane] = 0.f;
     }
-    if constexpr (kGated) {
+    if constexpr (FUSED) {
+      const float gv = cumsum64(Ls[cc % NG], lane);
+      const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
+      const float lk = LKs[cc % NG][lane];
+      if constexpr (OUT) {
+        const float lq = LQs[cc % NG][lane];
+        Gs[cc % 3][lane] = gv + lq;
+        Gk[cc % 3][lane] = gv - lk;
+        Eq[cc % 3][lane] = __expf(gv + lq);
+      }
+      Es[cc % 3][lane] = __expf(gv);
+      Fs[cc % 3][lane] = __expf(gC - gv + lk);
+      if constexpr (kDelta) BGs[cc % 3][lane] = Bs[cc % NG][lane] * __expf(gv + lk);
+    } else if constexpr (kGated) {
       const float gv = cumsum64(Ls[cc % NG], lane);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
       const float e = __expf(gv);
@@ -1051,11 +1171,12 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       if constexpr (OUT) {
         const T16* Kc = Ks[c % 3];
         const float* gc = Gs[kGated ? c % 3 : 0];
-        const float* ec = Es[kGated ? c % 3 : 0];
+        const float* gk = kQSide ? Gk[c % 3] : gc;
+        const float* ec = kQSide ? Eq[c % 3] : Es[kGated ? c % 3 : 0];
         const Frag<T16>* Sc = Sx[c % 2];
-        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
-        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
-        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, ec, Sc, roff, sc, qs, g, n, lane);
+        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
+        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
+        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
       }
       // Everything issued before this chunk has landed.  Loads complete in
       // issue order, so while any earlier transfer is outstanding all N of
@@ -1239,13 +1360,39 @@ constexpr int kComputeUnits = 256;   // gfx950 (MI355X)
 constexpr int kMinSegChunks = 4;     // shortest segment worth a pass
 constexpr int kMaxSegments = 64;
 
-// Workspace layout: the T fragments of every chunk (delta modes), then, for
-// P > 1, X, M and S_in, [BH, P, D, D] float each.
+// Workspace layout: the T fragments of every chunk (delta modes); then, for
+// P > 1, X, M and S_in, [BH, P, D, D] float each; then, with the fused
+// prologue, its four per-token arrays (beta, log alpha, lq, lk), each on a
+// 256-byte boundary.
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 size_t tsolve_bytes(const ChunkArgs& a) {
   return mode_erase(a.mode) ? chunk_slots(a) * kTFrags * kWave * sizeof(u32x4) : 0;
 }
 
-size_t seg_states_offset(const ChunkArgs& a) { return (tsolve_bytes(a) + 255) & ~(size_t)255; }
+size_t seg_states_offset(const ChunkArgs& a) { return align256(tsolve_bytes(a)); }
+
+size_t seg_states_end(const ChunkArgs& a) {
+  if (a.P <= 1) return tsolve_bytes(a);
+  return seg_states_offset(a) + 3 * (size_t)a.B * a.H * a.P * a.d * a.d * sizeof(float);
+}
+
+size_t token_rows(const ChunkArgs& a) { return (a.cu ? (size_t)a.H : (size_t)a.B * a.H) * a.L; }
+
+size_t pro_stride(const ChunkArgs& a) { return align256(token_rows(a) * sizeof(float)); }
+
+// The arguments the chain kernels run with: with the fused prologue, its
+// gates and, for normalised q and k, the decayed kernel of the mode.
+ChunkArgs kernel_args(const ChunkArgs& a) {
+  ChunkArgs k = a;
+  if (a.pro) {
+    const ProArrays p = pro_arrays(a);
+    k.mode = kernel_mode(a);
+    k.log_alpha = p.log_alpha;
+    k.beta = p.beta;
+  }
+  return k;
+}
 
 StreamMap stream_map(const ChunkArgs& a, int pass) {
   StreamMap m{seq_map(a), a.S0, a.S_final, pass, a.P, mode_erase(a.mode),
@@ -1260,39 +1407,53 @@ StreamMap stream_map(const ChunkArgs& a, int pass) {
   return m;
 }
 
-template <int D, int MODE, bool OUT>
+// a: the kernel arguments (kernel_args of the call)
+template <int D, int MODE, bool OUT, bool FUSED>
 hipError_t launch_one(const ChunkArgs& a, int pass, hipStream_t st) {
   const StreamMap m = stream_map(a, pass);
   const size_t ns = (size_t)a.B * a.H * m.per_seq();
   const dim3 grid((unsigned)(ns * (D / 16))), block(kThreads);
-  chunk_pipe_kernel<D, MODE, OUT><<<grid, block, 0, st>>>(
+  const ProArrays pro = FUSED ? pro_arrays(a) : ProArrays{};
+  chunk_pipe_kernel<D, MODE, OUT, FUSED><<<grid, block, 0, st>>>(
       static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
       a.log_alpha, a.beta, static_cast<const u32x4*>(a.workspace), a.out, m, (int)ns,
-      a.out_bf16 ? 1 : 0);
+      a.out_bf16 ? 1 : 0, pro);
   return hipGetLastError();
 }
 
-template <int D, bool GATED>
+// a: the call's arguments (raw gates when the prologue activates them)
+template <int D, bool GATED, bool PRO, bool TS>
 hipError_t launch_t(const ChunkArgs& a, hipStream_t st) {
   const size_t items = chunk_slots(a);
-  t_solve_kernel<D, GATED><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
+  ProIn pro{};
+  if (PRO)
+    pro = ProIn{static_cast<const T16*>(a.q), pro_arrays(a), a.pro, a.gate_scale,
+                mode_erase(a.mode), mode_decay(a.mode)};
+  t_solve_kernel<D, GATED, PRO, TS><<<dim3((unsigned)items), dim3(kWave), 0, st>>>(
       static_cast<const T16*>(a.k), a.log_alpha, a.beta, static_cast<u32x4*>(a.workspace),
-      seq_map(a));
+      seq_map(a), pro);
   return hipGetLastError();
 }
 
 template <int D, bool OUT>
-hipError_t launch_d(const ChunkArgs& a, int pass, hipStream_t st) {
+hipError_t launch_d(const ChunkArgs& call, int pass, hipStream_t st) {
+  const ChunkArgs a = kernel_args(call);
+  const bool fused = call.pro & kProQKNorm;
   switch (a.mode) {
-    case kModeLinear: return launch_one<D, kModeLinear, OUT>(a, pass, st);
-    case kModeDelta: return launch_one<D, kModeDelta, OUT>(a, pass, st);
-    case kModeGatedLinear: return launch_one<D, kModeGatedLinear, OUT>(a, pass, st);
-    default: return launch_one<D, kModeGatedDelta, OUT>(a, pass, st);
+    case kModeLinear: return launch_one<D, kModeLinear, OUT, false>(a, pass, st);
+    case kModeDelta: return launch_one<D, kModeDelta, OUT, false>(a, pass, st);
+    case kModeGatedLinear:
+      return fused ? launch_one<D, kModeGatedLinear, OUT, true>(a, pass, st)
+                   : launch_one<D, kModeGatedLinear, OUT, false>(a, pass, st);
+    default:
+      return fused ? launch_one<D, kModeGatedDelta, OUT, true>(a, pass, st)
+                   : launch_one<D, kModeGatedDelta, OUT, false>(a, pass, st);
   }
 }
 
 template <int D>
-hipError_t launch_scan_d(const ChunkArgs& a, hipStream_t st) {
+hipError_t launch_scan_d(const ChunkArgs& call, hipStream_t st) {
+  const ChunkArgs a = kernel_args(call);
   const StreamMap m = stream_map(a, kPassOut);
   const dim3 grid((unsigned)((size_t)a.B * a.H * (D / kScanCols))), block(kScanThreads);
   if (mode_erase(a.mode))
@@ -1307,8 +1468,15 @@ hipError_t launch_scan_d(const ChunkArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
-  if (a.P <= 1) return tsolve_bytes(a);
-  return seg_states_offset(a) + 3 * (size_t)a.B * a.H * a.P * a.d * a.d * sizeof(float);
+  if (!a.pro) return seg_states_end(a);
+  return align256(seg_states_end(a)) + 4 * pro_stride(a);
+}
+
+ProArrays pro_arrays(const ChunkArgs& a) {
+  char* base = static_cast<char*>(a.workspace) + align256(seg_states_end(a));
+  const size_t s = pro_stride(a);
+  return ProArrays{reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + s),
+                   reinterpret_cast<float*>(base + 2 * s), reinterpret_cast<float*>(base + 3 * s)};
 }
 
 // Rough cost, in chunk steps of the whole-sequence walk, of P segments: the
@@ -1344,9 +1512,17 @@ int plan_segments(const ChunkArgs& a) {
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
+  if (a.pro) {
+    // the prologue, and T in the delta modes (with the decay exponents of
+    // the prologue's gates, zero where the mode has none)
+    if (mode_erase(a.mode))
+      return a.d == 64 ? launch_t<64, true, true, true>(a, st) : launch_t<128, true, true, true>(a, st);
+    return a.d == 64 ? launch_t<64, true, true, false>(a, st) : launch_t<128, true, true, false>(a, st);
+  }
   const bool gated = mode_decay(a.mode);
-  if (a.d == 64) return gated ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
-  return gated ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
+  if (a.d == 64)
+    return gated ? launch_t<64, true, false, true>(a, st) : launch_t<64, false, false, true>(a, st);
+  return gated ? launch_t<128, true, false, true>(a, st) : launch_t<128, false, false, true>(a, st);
 }
 
 hipError_t launch_chunk_state(const ChunkArgs& a, hipStream_t st) {

@@ -19,17 +19,29 @@
 // registers, reduces the two column dot products through LDS, and writes the
 // updated values back from the same registers with 16-byte non-temporal
 // stores.  S is read exactly once and written exactly once.
+//
+// Fused prologue (pro flags): kProGates -- beta = sigmoid(b), log alpha =
+// -gate_scale softplus(a) from the raw scores passed as beta and log_alpha;
+// kProQKNorm -- q and k are used as x / sqrt(|x|^2 + eps).  The inverse
+// norms r_q, r_k are computed with k . q and folded into the products (s
+// and k . q carry r_k, p and k . q carry r_q, the update's k carries r_k),
+// so the state pass is unchanged.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
 namespace la {
 namespace {
 
+__device__ __forceinline__ float sigmoid_d(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplus_d(float x) {
+  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));   // log(1 + e^x), no overflow
+}
+
 template <typename T, typename TO, int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    float* __restrict__ S, TO* __restrict__ out) {
+    float* __restrict__ S, TO* __restrict__ out, int pro, float gate_scale) {
   constexpr int NQ = DV / 4;       // 16-byte column quads per state row
   constexpr int RG = 256 / NQ;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -40,7 +52,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __shared__ float sv[DV];
   __shared__ float su[DV];
   __shared__ float red[2][RG][DV];
-  __shared__ float skq;
+  __shared__ float skq, srk, srq;
 
   const size_t bh = blockIdx.x;
   const int t = threadIdx.x;
@@ -78,17 +90,41 @@ __global__ __launch_bounds__(256) void decode_kernel(
     red[0][rg][4 * cq + c] = pk[c];
     red[1][rg][4 * cq + c] = pq[c];
   }
+  const bool qkn = pro & kProQKNorm;
   if (t < kWave) {
-    float d = 0.f;
-    for (int i = t; i < DK; i += kWave) d = fmaf(sk[i], sq[i], d);
+    float d = 0.f, nk = 0.f, nq = 0.f;
+    for (int i = t; i < DK; i += kWave) {
+      d = fmaf(sk[i], sq[i], d);
+      if (qkn) {
+        nk = fmaf(sk[i], sk[i], nk);
+        nq = fmaf(sq[i], sq[i], nq);
+      }
+    }
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) d += __shfl_xor(d, off);
-    if (t == 0) skq = d;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      d += __shfl_xor(d, off);
+      if (qkn) {
+        nk += __shfl_xor(nk, off);
+        nq += __shfl_xor(nq, off);
+      }
+    }
+    if (t == 0) {
+      const float rk = qkn ? rsqrtf(nk + kQKNormEps) : 1.f;
+      const float rq = qkn ? rsqrtf(nq + kQKNormEps) : 1.f;
+      skq = d * rk * rq;
+      srk = rk;
+      srq = rq;
+    }
   }
   __syncthreads();
 
+  const bool act = pro & kProGates;
   float a = 1.f;
-  if (mode_decay(MODE)) a = __expf(log_alpha[bh]);
+  if (mode_decay(MODE)) {
+    const float la = act ? -gate_scale * softplus_d(log_alpha[bh]) : log_alpha[bh];
+    a = __expf(la);
+  }
+  const float rk = srk;
   if (t < DV) {
     float sj = 0.f, pj = 0.f;
 #pragma unroll
@@ -96,13 +132,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
       sj += red[0][r][t];
       pj += red[1][r][t];
     }
+    sj *= rk;
+    pj *= srq;
     float u, o;
     if (!mode_erase(MODE)) {
       // S' = a S + k v^T:  o = a S^T q + (k . q) v
       u = sv[t];
       o = a * pj + skq * u;
     } else {
-      const float b = beta[bh];
+      const float b = act ? sigmoid_d(beta[bh]) : beta[bh];
       u = b * (sv[t] - a * sj);
       o = a * pj + skq * u;
     }
@@ -116,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int c = 0; c < 4; ++c) u4[c] = su[4 * cq + c];
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
-    const float kk = sk[rg + RG * m];
+    const float kk = sk[rg + RG * m] * rk;
     f32x4 w;
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[c] = fmaf(a, s[m][c], kk * u4[c]);
@@ -134,19 +172,19 @@ hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   switch (a.mode) {
     case kModeLinear:
       decode_kernel<T, TO, DK, DV, kModeLinear><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
       break;
     case kModeDelta:
       decode_kernel<T, TO, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
       break;
     case kModeGatedLinear:
       decode_kernel<T, TO, DK, DV, kModeGatedLinear><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
       break;
     default:
       decode_kernel<T, TO, DK, DV, kModeGatedDelta><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
       break;
   }
   return hipGetLastError();

@@ -25,6 +25,8 @@ struct DecodeArgs {
   int B, H, dk, dv, mode;
   bool in_bf16;   // q, k, v are bf16 (else float)
   bool out_bf16;  // out is bf16 (else float)
+  int pro = 0;            // fused prologue flags (kProGates, kProQKNorm)
+  float gate_scale = 0.f;
 };
 
 struct ChunkArgs {
@@ -47,7 +49,34 @@ struct ChunkArgs {
   // Segments per (b, h) sequence of the sequence-parallel forward (bf16,
   // fixed-length layout only); 1 walks each sequence whole.
   int P = 1;
+  // Fused prologue (bf16 inputs): kProGates -- log_alpha and beta hold raw
+  // scores a, b, and the op uses beta = sigmoid(b), log alpha =
+  // -gate_scale softplus(a); kProQKNorm -- q and k are L2-normalised per
+  // token inside the op.  0: the inputs are used as given.
+  int pro = 0;
+  float gate_scale = 0.f;
 };
+
+enum : int { kProGates = 1, kProQKNorm = 2 };
+constexpr float kQKNormEps = 1e-6f;   // x / sqrt(sum x^2 + eps)
+
+// Per-token values the fused prologue writes for the chain kernels, token
+// rows laid out like the gates ([B, H, L] or [H, T]): the gates the op uses
+// and the logs of the inverse norms of q and k (zero without kProQKNorm).
+struct ProArrays {
+  float* beta;
+  float* log_alpha;
+  float* lq;   // log(1 / |q_t|)
+  float* lk;   // log(1 / |k_t|)
+};
+
+// Mode the chain kernels run: with q, k normalisation the per-token norms
+// ride in the decay tables, so the modes without decay use their decayed
+// kernel with log alpha = 0.
+inline int kernel_mode(const ChunkArgs& a) {
+  if (!(a.pro & kProQKNorm)) return a.mode;
+  return mode_erase(a.mode) ? kModeGatedDelta : kModeGatedLinear;
+}
 
 // Where the tokens of one (sequence, head) pair bh = s * H + h live, shared
 // by the host (sizes) and the kernels (indexing).
@@ -191,6 +220,9 @@ size_t chunk_pipe_workspace_bytes(const ChunkArgs& a);               // la_chunk
 // Segments per sequence the sequence-parallel forward uses for this call
 // (1: none), from the shapes alone (la_chunk_pipe.hip).
 int plan_segments(const ChunkArgs& a);
+// The fused prologue's per-token arrays inside the workspace (valid when
+// a.pro != 0; la_chunk_pipe.hip).
+ProArrays pro_arrays(const ChunkArgs& a);
 // With P > 1: the state pass, then the scan, before launch_chunk runs the
 // output pass (la_chunk_pipe.hip).
 hipError_t launch_chunk_state(const ChunkArgs& a, hipStream_t st);

@@ -26,6 +26,8 @@ Modules:
   chunk products, WY/UT representation, decay folding); it is pinned to the
   recurrence by the exactness of the chunkwise form and is used to pin
   intermediates.
+* ``prologue``   -- the steps in front of the op that the fused entry points
+  take inside (q, k L2 normalisation, gate activations).
 
 Parity status of each function is stated in its module header.
 """
@@ -38,6 +40,7 @@ from .recurrence import (  # noqa: F401
     recurrent_fwd,
     recurrent_step,
 )
+from .prologue import l2_normalise, prepare, sigmoid, softplus  # noqa: F401
 from .chunkwise import (  # noqa: F401
     chunkwise_fwd,
     forward_substitution_inverse,

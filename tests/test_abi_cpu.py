@@ -286,3 +286,73 @@ def test_segment_plan():
     n = ctypes.c_int(0)
     assert lib.la_chunk_segments(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
     assert lib.la_chunk_segments(1, 1, 64, 96, 96, 64, 2, 1, ctypes.byref(n)) == UNSUP
+
+
+def fused(lib, flags=3, scale=0.0625, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4),
+          s0=fake(5), out=fake(6), sf=fake(7), B=1, H=1, L=640, dk=64, dv=64, C=64, mode=2,
+          dtype=1, ws=fake(8), wsb=P_BIG):
+    return lib.la_chunk_fwd_fused(q, k, v, la, be, s0, out, sf, B, H, L, dk, dv, C, mode, dtype,
+                                  flags, ctypes.c_float(scale), ws, wsb, None)
+
+
+def fused_ws(lib, flags, B=1, H=1, L=640, d=64, mode=2, dtype=1):
+    n = ctypes.c_size_t(0)
+    rc = lib.la_chunk_fused_workspace_bytes(B, H, L, d, d, 64, mode, dtype, flags, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), UNSUP), (dict(flags=-1), UNSUP), (dict(flags=1, scale=0.0), UNSUP),
+    (dict(flags=3, scale=float("inf")), UNSUP), (dict(flags=2, dtype=0), UNSUP),
+    (dict(la=None), NULL), (dict(be=None, mode=1), NULL), (dict(wsb=1), WS),
+    (dict(out=ctypes.c_void_p(P + 128)), ALIAS),
+])
+def test_chunk_fwd_fused_rejects(kw, code):
+    lib = _lib.get()
+    assert fused(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_fused_flag_rules():
+    """A zero scale only matters where a decay is activated; gate flags in
+    LINEAR mode (no gates) reduce to no prologue -- float inputs then pass
+    the flag check and stop at the NULL q they were given."""
+    lib = _lib.get()
+    assert fused(lib, flags=1, scale=0.0, mode=1, q=None) == NULL        # delta: no decay
+    assert fused(lib, flags=1, scale=0.0, mode=0, dtype=0, q=None) == NULL
+    assert fused(lib, flags=2, mode=0, dtype=0) == UNSUP                 # norm needs bf16
+
+
+def test_fused_workspace_size():
+    """la_chunk_fwd's workspace, then four float arrays of B*H*L tokens on
+    256-byte boundaries; no prologue (flags 0, or gates in LINEAR mode) is
+    la_chunk_fwd's size."""
+    lib = _lib.get()
+    for (B, H, L, d) in ((1, 1, 640, 64), (2, 3, 1000, 128), (1, 32, 65536, 128),
+                         (1, 4, 65536, 128)):
+        for mode in (0, 1, 2, 3):
+            rc, base = ws_bytes(lib, B=B, H=H, L=L, dk=d, dv=d, mode=mode)
+            assert rc == OK
+            arr = -(-(B * H * L * 4) // 256) * 256
+            for flags in (1, 2, 3):
+                want = base if (flags == 1 and mode == 0) else (-(-base // 256) * 256 + 4 * arr)
+                assert fused_ws(lib, flags, B, H, L, d, mode) == (OK, want)
+            assert fused_ws(lib, 0, B, H, L, d, mode) == (OK, base)
+    assert fused_ws(lib, 2, dtype=0)[0] == UNSUP
+    assert fused_ws(lib, 0, dtype=0) == (OK, 0)
+    assert lib.la_chunk_fused_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, 3, None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=8), UNSUP), (dict(flags=1, scale=-1.0), UNSUP), (dict(q=None), NULL),
+    (dict(la=None), NULL), (dict(S=ctypes.c_void_p(P + 64)), ALIAS),
+])
+def test_decode_fused_rejects(kw, code):
+    lib = _lib.get()
+    a = dict(flags=3, scale=0.0625, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4),
+             S=fake(5), out=fake(6))
+    a.update(kw)
+    rc = lib.la_decode_step_fused(a["q"], a["k"], a["v"], a["la"], a["be"], a["S"], a["out"],
+                                  1, 1, 64, 64, 2, 1, a["flags"], ctypes.c_float(a["scale"]), None)
+    assert rc == code
+    assert lib.la_last_error().decode() != ""

@@ -466,3 +466,74 @@ def test_modes_ignore_unused_gates():
         recurrent_fwd(q, k, v, la, None, S0, "delta")
     with pytest.raises(ValueError):
         recurrent_fwd(q, k, v, la, be, S0, "softmax")
+
+
+# ---------------------------------------------------------------- fused prologue
+
+def test_gate_activations_closed_forms():
+    """sigmoid and softplus against values fixed by their definitions:
+    sigmoid(0) = 1/2, sigmoid(log 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1;
+    softplus(0) = log 2, softplus(log(e - 1)) = 1, softplus(a) - softplus(-a)
+    = a; far from 0 they saturate (0 and 1; 0 and a) without overflow."""
+    from oracle.prologue import sigmoid, softplus
+    assert sigmoid(0.0) == 0.5
+    assert abs(sigmoid(np.log(3.0)) - 0.75) < 1e-15
+    x = np.linspace(-30, 30, 121)
+    assert np.max(np.abs(sigmoid(x) + sigmoid(-x) - 1.0)) < 1e-15
+    assert abs(softplus(0.0) - np.log(2.0)) < 1e-16
+    assert abs(softplus(np.log(np.e - 1.0)) - 1.0) < 1e-15
+    assert np.max(np.abs(softplus(x) - softplus(-x) - x)) < 1e-13
+    assert sigmoid(-800.0) == 0.0 and sigmoid(800.0) == 1.0
+    assert softplus(-800.0) == 0.0 and softplus(800.0) == 800.0
+
+
+def test_l2_normalise_closed_form():
+    """|x / sqrt(|x|^2 + eps)|^2 = |x|^2 / (|x|^2 + eps) exactly, per token
+    (last axis only); the zero vector stays zero."""
+    from oracle.prologue import QK_NORM_EPS, l2_normalise
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 4, 7, 6)) * rng.uniform(0.01, 10.0, (3, 4, 7, 1))
+    y = l2_normalise(x)
+    n2 = np.sum(x * x, axis=-1)
+    assert _rel(np.sum(y * y, axis=-1), n2 / (n2 + QK_NORM_EPS)) < 1e-14
+    # the direction is kept: y is a positive multiple of x, token by token
+    ratio = y / x
+    assert np.max(np.abs(ratio - ratio[..., :1])) < 1e-12 and np.all(ratio > 0)
+    assert np.all(l2_normalise(np.zeros((2, 5))) == 0.0)
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_prologue_makes_op_scale_invariant(mode):
+    """With q and k normalised inside, scaling any token's q or k by a
+    positive factor leaves the outputs and the state unchanged (up to the
+    eps inside the root): a normalisation over the wrong axis, or by the
+    sum instead of the norm, fails this.  The activated gates are a decay in
+    (0, 1] and a write strength in (0, 1)."""
+    from oracle.prologue import GATES, QK_L2NORM, prepare
+    q, k, v, _, _, S0 = _rand(47, B=1, H=2, L=17, dk=6, dv=5, unit_keys=False)
+    rng = np.random.default_rng(48)
+    a, b = rng.standard_normal((2, 1, 2, 17))
+    flags = GATES | QK_L2NORM
+    o1, S1 = recurrent_fwd(*_prepared(q, k, v, a, b, mode, flags), S0, mode)
+    sq = rng.uniform(0.2, 5.0, (1, 2, 17, 1))
+    sk = rng.uniform(0.2, 5.0, (1, 2, 17, 1))
+    o2, S2 = recurrent_fwd(*_prepared(q * sq, k * sk, v, a, b, mode, flags), S0, mode)
+    # each normalised vector moves by at most about eps / |x|^2 relative
+    n2 = min(np.min(np.sum(x * x, -1)) for x in (q, k, q * sq, k * sk))
+    tol = 50 * 1e-6 / n2
+    assert _rel(o2, o1) < tol and _rel(S2, S1) < tol
+    # without the normalisation the same scaling changes the result
+    o3, _ = recurrent_fwd(*_prepared(q * sq, k * sk, v, a, b, mode, GATES), S0, mode)
+    o4, _ = recurrent_fwd(*_prepared(q, k, v, a, b, mode, GATES), S0, mode)
+    assert _rel(o3, o4) > 1e-2
+    _, _, la, be = prepare(q, k, a, b, mode, flags, 0.25)
+    if mode in oracle.GATED_MODES:
+        assert np.all(la <= 0.0) and np.all(la >= -0.25 * (np.abs(a) + 1.0))
+    if mode in oracle.ERASE_MODES:
+        assert np.all((be > 0.0) & (be < 1.0))
+
+
+def _prepared(q, k, v, a, b, mode, flags):
+    from oracle.prologue import prepare
+    qq, kk, la, be = prepare(q, k, a, b, mode, flags, 1.0 / 16.0)
+    return qq, kk, v, la, be

@@ -320,6 +320,145 @@ def test_chunk_shard_sampled():
     check_fwd(w, x, o_ref, S_ref, sel=lambda t: t[[0, 0], [0, w.H - 1]])
 
 
+# ------------------------------------------------------------------ fused prologue
+
+PRO = {"gates": 1, "norm": 2, "both": 3}
+GATE_SCALE = 1.0 / 16.0
+
+
+def _raw(w, flags):
+    """Raw inputs and the gates to pass: q, k not normalised when the
+    prologue normalises them (else the recipe's prepared q, k, as a caller
+    without that step passes them), raw gate scores next to the activated
+    values (float32, computed here in front of the op)."""
+    r = workloads.make_raw_inputs(w)
+    if not flags & 2:
+        x = workloads.make_inputs(w)
+        r["q"], r["k"] = x["q"], x["k"]
+    r["log_alpha"] = -torch.nn.functional.softplus(r["a_raw"]) * GATE_SCALE
+    r["beta"] = torch.sigmoid(r["b_raw"])
+    return r
+
+
+def _fused_oracle(r, mode, flags, heads=None):
+    """The oracle's prologue (oracle.prepare) on the raw float64 inputs,
+    then its recurrence; gates not activated by the prologue are the float32
+    values the device received."""
+    y = {key: t.to(torch.float64).numpy() for key, t in r.items()}
+    a = y["a_raw"] if flags & 1 else y["log_alpha"]
+    b = y["b_raw"] if flags & 1 else y["beta"]
+    q, k, la, be = oracle.prepare(y["q"], y["k"], a, b, mode, flags, GATE_SCALE)
+    v, S0 = y["v"], y["S0"]
+    if heads is not None:
+        bs, hs = [b_ for b_, _ in heads], [h for _, h in heads]
+        sel = lambda t: t[bs, hs][None]       # noqa: E731
+        o, S = oracle.recurrent_fwd(sel(q), sel(k), sel(v), sel(la), sel(be), sel(S0), mode)
+        return o[0], S[0]
+    return oracle.recurrent_fwd(q, k, v, la, be, S0, mode)
+
+
+def _fused_call(d, mode, flags, out_dtype=None):
+    a = d["a_raw"] if flags & 1 else d["log_alpha"]
+    b = d["b_raw"] if flags & 1 else d["beta"]
+    out, S = la.chunk_fwd(d["q"], d["k"], d["v"], a, b, d["S0"], mode=mode,
+                          qk_l2norm=bool(flags & 2), gate_act=bool(flags & 1),
+                          gate_scale=GATE_SCALE, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, S
+
+
+@pytest.mark.parametrize("flags", ["gates", "norm", "both"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_fused_prologue(mode, d, flags):
+    """Raw q, k (N(0, 1), not normalised) and raw gate scores: the T-solve
+    kernel activates the gates and folds the inverse norms of q and k into
+    the decay tables; every element against the oracle's prologue and
+    recurrence, over 5 full chunks and a partial one, with S0.  The bf16
+    output is the float one rounded."""
+    f = PRO[flags]
+    w = recipe(mode, "bf16", B=2, H=2, L=64 * 5 + 13, d=d, s0_std=0.3, seed=67)
+    log(f"chunk fused prologue {flags} {w}")
+    r = _raw(w, f)
+    o_ref, S_ref = _fused_oracle(r, mode, f)
+    dev = to_cuda(r)
+    out, S = _fused_call(dev, mode, f)
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final", f64(S), S_ref, "bf16")
+    out32, S32 = _fused_call(dev, mode, f, out_dtype=torch.float32)
+    assert torch.equal(out32.to(torch.bfloat16), out) and torch.equal(S32, S)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_fused_prologue_segmented(mode):
+    """The fused prologue on one long sequence, which the plan runs
+    sequence-parallel (state pass, scan and output pass with the folded
+    tables)."""
+    w = recipe(mode, "bf16", B=1, H=1, L=4096 + 40, d=128, s0_std=0.2, seed=71)
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=mode)
+    log(f"chunk fused prologue segmented P={P} {w}")
+    assert P > 1
+    r = _raw(w, 3)
+    o_ref, S_ref = _fused_oracle(r, mode, 3)
+    out, S = _fused_call(to_cuda(r), mode, 3)
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final", f64(S), S_ref, "bf16")
+
+
+def test_chunk_fused_no_flags_is_plain_forward():
+    """flags = 0 is la_chunk_fwd, bit for bit."""
+    w = recipe("gated_delta", "bf16", B=1, H=2, L=300, d=128, s0_std=0.2, seed=73)
+    log(f"chunk fused flags 0 {w}")
+    dev = to_cuda(_raw(w, 0))
+    a = _fused_call(dev, "gated_delta", 0)
+    b = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"],
+                     mode="gated_delta")
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_chunk_fused_shard_sampled():
+    """One GPU's share of workload 4 from raw inputs with the whole prologue
+    fused, as a model layer would call it; 2 heads against the oracle."""
+    w = workloads.WORKLOAD4_SHARD8
+    log(f"chunk fused shard {w}")
+    r = _raw(w, 3)
+    heads = [(0, 0), (0, w.H - 1)]
+    o_ref, S_ref = _fused_oracle(r, w.mode, 3, heads)
+    out, S = _fused_call(to_cuda(r), w.mode, 3)
+    sel = lambda t: t[[0, 0], [0, w.H - 1]]   # noqa: E731
+    assert_close("o", f64(sel(out)), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final", f64(sel(S)), S_ref, "bf16")
+
+
+@pytest.mark.parametrize("flags", ["gates", "norm", "both"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_fused_prologue(mode, dtype, flags):
+    """Decode steps from raw inputs: 12 steps of B=3 H=2 d=128 against the
+    oracle's prologue and decode."""
+    f = PRO[flags]
+    w = Workload(f"decode_{mode}_{dtype}", mode, dtype, B=3, H=2, L=1, dk=128, dv=128, C=1,
+                 qk_norm=True, qkv_scale=1.0, s0_std=0.3, steps=12, seed=79)
+    log(f"decode fused prologue {flags} {w}")
+    r = _raw(w, f)
+    y = {key: t.to(torch.float64).numpy() for key, t in r.items()}
+    a = y["a_raw"] if f & 1 else y["log_alpha"]
+    b = y["b_raw"] if f & 1 else y["beta"]
+    q, k, lg, be = oracle.prepare(y["q"], y["k"], a, b, mode, f, GATE_SCALE)
+    o_ref, S_ref = oracle.decode_steps(y["S0"], q, k, y["v"], lg, be, mode)
+    d = to_cuda(r)
+    S = d["S0"].clone()
+    ga = d["a_raw"] if f & 1 else d["log_alpha"]
+    gb = d["b_raw"] if f & 1 else d["beta"]
+    outs = [la.decode_step(d["q"][n], d["k"][n], d["v"][n], ga[n], gb[n], S, mode=mode,
+                           qk_l2norm=bool(f & 2), gate_act=bool(f & 1), gate_scale=GATE_SCALE)
+            for n in range(w.steps)]
+    torch.cuda.synchronize()
+    assert_close("o", np.stack([f64(o) for o in outs]), o_ref, dtype, bf16_out=dtype == "bf16")
+    assert_close("S", f64(S), S_ref, dtype)
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]

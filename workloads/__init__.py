@@ -107,6 +107,28 @@ def _l2norm(x):
     return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
 
 
+def make_raw_inputs(w: Workload, seed=None):
+    """The draws of ``make_inputs`` before the preparation in front of the
+    op: q, k, v times ``qkv_scale`` (q and k not normalised) in the device
+    dtype, the raw gate scores ``a_raw`` (alpha) and ``b_raw`` (beta)
+    float32, and S0 -- the inputs of the fused entry points."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    lead = (w.steps, w.B, w.H) if w.is_decode else (w.B, w.H, w.L)
+    q = _normal(gen, lead + (w.dk,)) * w.qkv_scale
+    k = _normal(gen, lead + (w.dk,)) * w.qkv_scale
+    v = _normal(gen, lead + (w.dv,)) * w.qkv_scale
+    beta_raw = _normal(gen, lead)
+    alpha_raw = _normal(gen, lead)
+    if w.s0_std > 0:
+        S0 = _normal(gen, (w.B, w.H, w.dk, w.dv)) * w.s0_std
+    else:
+        S0 = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32)
+    dt = w.torch_dtype
+    return dict(q=q.to(dt).contiguous(), k=k.to(dt).contiguous(), v=v.to(dt).contiguous(),
+                a_raw=alpha_raw.contiguous(), b_raw=beta_raw.contiguous(), S0=S0.contiguous())
+
+
 def make_inputs(w: Workload, seed=None):
     """Draw the inputs of workload ``w`` on the CPU.
 
