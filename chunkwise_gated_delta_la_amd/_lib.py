@@ -26,6 +26,13 @@ class LAError(RuntimeError):
         super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
 
 
+class FusedOpts(ctypes.Structure):
+    """la_fused_opts_t of include/la.h."""
+    _fields_ = [("flags", ctypes.c_int), ("gate_scale", ctypes.c_float),
+                ("dskip", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
 def _declare(lib):
     vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.la_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
@@ -46,14 +53,15 @@ def _declare(lib):
     lib.la_chunk_segmented_workspace_bytes.restype = i
     lib.la_chunk_segments.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.la_chunk_segments.restype = i
+    op = ctypes.POINTER(FusedOpts)
     lib.la_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
-                                       i, i, i, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+                                       i, i, i, i, i, i, i, i, op, vp, sz, vp]
     lib.la_chunk_fwd_fused.restype = i
-    lib.la_chunk_fused_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i,
+    lib.la_chunk_fused_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, op,
                                                    ctypes.POINTER(sz)]
     lib.la_chunk_fused_workspace_bytes.restype = i
     lib.la_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp,
-                                         i, i, i, i, i, i, i, ctypes.c_float, vp]
+                                         i, i, i, i, i, i, op, vp]
     lib.la_decode_step_fused.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]

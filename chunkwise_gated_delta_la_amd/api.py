@@ -59,16 +59,24 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-PRO_GATES, PRO_QK_L2NORM = 1, 2     # la_prologue_t
+PRO_GATES, PRO_QK_L2NORM, EPI_DSKIP, EPI_OUT_NORM = 1, 2, 4, 8     # la_fused_flag_t
 
 
-def _pro_flags(qk_l2norm, gate_act):
-    return (PRO_QK_L2NORM if qk_l2norm else 0) | (PRO_GATES if gate_act else 0)
+def _fused_opts(qk_l2norm=False, gate_act=False, gate_scale=1.0 / 16.0, dskip=None,
+                out_norm=False, norm_weight=None, norm_eps=1e-6):
+    """la_fused_opts_t for these steps, or None when none is asked for."""
+    flags = ((PRO_QK_L2NORM if qk_l2norm else 0) | (PRO_GATES if gate_act else 0)
+             | (EPI_DSKIP if dskip is not None else 0) | (EPI_OUT_NORM if out_norm else 0))
+    if not flags:
+        return None
+    return _lib.FusedOpts(flags, float(gate_scale), _ptr(dskip).value if dskip is not None
+                          else None, _ptr(norm_weight).value if norm_weight is not None
+                          else None, float(norm_eps))
 
 
 def chunk_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
                           dtype=torch.bfloat16, out_dtype=None, segments=None,
-                          qk_l2norm=False, gate_act=False):
+                          qk_l2norm=False, gate_act=False, fused=None):
     """Workspace bytes ``la_chunk_fwd`` needs for these sizes
     (``la_chunk_workspace_bytes``), or ``la_chunk_fwd_segmented`` with
     ``segments`` segments (``la_chunk_segmented_workspace_bytes``), or
@@ -76,12 +84,12 @@ def chunk_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
     code = _dtype_code(dtype, out_dtype or dtype)
     n = ctypes.c_size_t(0)
     lib = _lib.get()
-    flags = _pro_flags(qk_l2norm, gate_act)
-    if flags:
+    opts = fused if fused is not None else _fused_opts(qk_l2norm, gate_act)
+    if opts is not None:
         if segments is not None:
-            raise ValueError("the fused prologue runs with the automatic segment plan")
-        rc = lib.la_chunk_fused_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code, flags,
-                                                ctypes.byref(n))
+            raise ValueError("the fused forward runs with the automatic segment plan")
+        rc = lib.la_chunk_fused_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
+                                                ctypes.byref(opts), ctypes.byref(n))
     elif segments is None:
         rc = lib.la_chunk_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code, ctypes.byref(n))
     else:
@@ -105,12 +113,16 @@ def chunk_segments(B, H, L, dk, dv, *, mode="gated_delta", C=64, dtype=torch.bfl
 def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta",
               C=64, out=None, S_final=None, return_state=True, out_dtype=None,
               workspace=None, segments=None, qk_l2norm=False, gate_act=False,
-              gate_scale=1.0 / 16.0):
+              gate_scale=1.0 / 16.0, dskip=None, out_norm=False, norm_weight=None,
+              norm_eps=1e-6):
     """Chunkwise forward (``la_chunk_fwd``; ``la_chunk_fwd_segmented`` when
     ``segments`` is given: each sequence cut into that many segments run in
-    parallel; ``la_chunk_fwd_fused`` when ``qk_l2norm`` -- q and k
-    normalised inside -- or ``gate_act`` -- log_alpha and beta are raw
-    scores a, b, used as -gate_scale softplus(a) and sigmoid(b) -- is set).
+    parallel; ``la_chunk_fwd_fused`` when a fused step is asked for:
+    ``qk_l2norm`` -- q and k normalised inside; ``gate_act`` -- log_alpha
+    and beta are raw scores a, b, used as -gate_scale softplus(a) and
+    sigmoid(b); ``dskip`` -- a float32 ``[H, dv]`` tensor D, o += D v;
+    ``out_norm`` -- o / sqrt(mean(o^2) + norm_eps) * norm_weight ``[H, dv]``
+    (ones when None)).
 
     q, k ``[B, H, L, dk]``, v ``[B, H, L, dv]`` (float32 or bfloat16, on the
     GPU); log_alpha, beta ``[B, H, L]`` float32; S0 ``[B, H, dk, dv]`` float32
@@ -144,9 +156,11 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     lib = _lib.get()
-    flags = _pro_flags(qk_l2norm, gate_act)
+    for t, name in ((dskip, "dskip"), (norm_weight, "norm_weight")):
+        _need(t, name, (H, dv), torch.float32, dev)
+    opts = _fused_opts(qk_l2norm, gate_act, gate_scale, dskip, out_norm, norm_weight, norm_eps)
     need = chunk_workspace_bytes(B, H, L, dk, dv, mode=mode, C=C, dtype=dt, out_dtype=odt,
-                                 segments=segments, qk_l2norm=qk_l2norm, gate_act=gate_act)
+                                 segments=segments, fused=opts)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
@@ -155,10 +169,10 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     ws_bytes = 0 if workspace is None else workspace.numel()
     with torch.cuda.device(dev):
         la, be = _ptr(log_alpha if m in _DECAY else None), _ptr(beta if m in _ERASE else None)
-        if flags:
+        if opts is not None:
             rc = lib.la_chunk_fwd_fused(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S0), _ptr(out),
-                                        _ptr(S_final), B, H, L, dk, dv, C, m, code, flags,
-                                        float(gate_scale), _ptr(workspace), ws_bytes,
+                                        _ptr(S_final), B, H, L, dk, dv, C, m, code,
+                                        ctypes.byref(opts), _ptr(workspace), ws_bytes,
                                         _stream(dev))
         elif segments is None:
             rc = lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S0), _ptr(out),
@@ -240,13 +254,15 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, S0, cu_seqlens, *, mode="gated_de
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
-                out_dtype=None, qk_l2norm=False, gate_act=False, gate_scale=1.0 / 16.0):
+                out_dtype=None, qk_l2norm=False, gate_act=False, gate_scale=1.0 / 16.0,
+                dskip=None, out_norm=False, norm_weight=None, norm_eps=1e-6):
     """One recurrent decode step (``la_decode_step``), updating ``S`` in place.
 
     q, k ``[B, H, dk]``, v ``[B, H, dv]`` (float32 or bfloat16); log_alpha,
     beta ``[B, H]`` float32; S ``[B, H, dk, dv]`` float32.  Returns ``out``
-    ``[B, H, dv]``.  ``qk_l2norm`` / ``gate_act`` / ``gate_scale``: the
-    fused prologue as in ``chunk_fwd`` (``la_decode_step_fused``).
+    ``[B, H, dv]``.  The fused steps (``qk_l2norm``, ``gate_act``,
+    ``gate_scale``, ``dskip``, ``out_norm``, ``norm_weight``, ``norm_eps``)
+    as in ``chunk_fwd`` (``la_decode_step_fused``).
     """
     m = _mode(mode)
     if q.dim() != 3 or v.dim() != 3:
@@ -267,12 +283,14 @@ def decode_step(q, k, v, log_alpha, beta, S, *, mode="gated_delta", out=None,
         out = torch.empty((B, H, dv), dtype=odt, device=dev)
     _need(out, "out", (B, H, dv), odt, dev)
     lib = _lib.get()
-    flags = _pro_flags(qk_l2norm, gate_act)
+    for t, name in ((dskip, "dskip"), (norm_weight, "norm_weight")):
+        _need(t, name, (H, dv), torch.float32, dev)
+    opts = _fused_opts(qk_l2norm, gate_act, gate_scale, dskip, out_norm, norm_weight, norm_eps)
     la, be = _ptr(log_alpha if m in _DECAY else None), _ptr(beta if m in _ERASE else None)
     with torch.cuda.device(dev):
-        if flags:
+        if opts is not None:
             rc = lib.la_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S), _ptr(out),
-                                          B, H, dk, dv, m, code, flags, float(gate_scale),
+                                          B, H, dk, dv, m, code, ctypes.byref(opts),
                                           _stream(dev))
         else:
             rc = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S), _ptr(out),

@@ -125,20 +125,51 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   return LA_OK;
 }
 
-// Prologue flags of the fused entry points, reduced to what the mode uses
-// (gate activations mean nothing in LINEAR mode).  Writes the effective
-// flags to *eff.
-int check_pro(int flags, float gate_scale, int mode, int* eff) {
-  if (flags < 0 || flags > (LA_PRO_GATES | LA_PRO_QK_L2NORM))
-    return fail(LA_ERR_UNSUPPORTED, "prologue flags must combine LA_PRO_GATES and "
-                                    "LA_PRO_QK_L2NORM, got " + std::to_string(flags));
+// Options of the fused entry points (NULL: none), reduced to what the mode
+// uses (gate activations mean nothing in LINEAR mode): the effective flags.
+struct Fused {
+  int flags = 0;
+  float gate_scale = 0.f;
+  const float* dskip = nullptr;
+  const float* norm_w = nullptr;
+  float norm_eps = 0.f;
+  int pro() const { return flags & (LA_PRO_GATES | LA_PRO_QK_L2NORM); }
+};
+
+int check_fused(const la_fused_opts_t* o, int mode, Fused* f) {
+  *f = Fused{};
+  if (!o) return LA_OK;
+  const int all = LA_PRO_GATES | LA_PRO_QK_L2NORM | LA_EPI_DSKIP | LA_EPI_OUT_NORM;
+  if (o->flags < 0 || (o->flags & ~all))
+    return fail(LA_ERR_UNSUPPORTED, "fused flags must combine la_fused_flag_t values, got " +
+                                        std::to_string(o->flags));
   const bool gates = la::mode_erase(mode) || la::mode_decay(mode);
-  int f = gates ? flags : (flags & ~LA_PRO_GATES);
-  if ((f & LA_PRO_GATES) && la::mode_decay(mode) &&
-      !(gate_scale > 0.f && gate_scale < 3.0e38f))
-    return fail(LA_ERR_UNSUPPORTED, "gate_scale must be positive and finite");
-  *eff = f;
+  f->flags = gates ? o->flags : (o->flags & ~LA_PRO_GATES);
+  if ((f->flags & LA_PRO_GATES) && la::mode_decay(mode)) {
+    if (!(o->gate_scale > 0.f && o->gate_scale < 3.0e38f))
+      return fail(LA_ERR_UNSUPPORTED, "gate_scale must be positive and finite");
+    f->gate_scale = o->gate_scale;
+  }
+  if (f->flags & LA_EPI_DSKIP) {
+    if (!o->dskip) return fail(LA_ERR_NULL, "LA_EPI_DSKIP needs dskip [H, dv]");
+    f->dskip = o->dskip;
+  }
+  if (f->flags & LA_EPI_OUT_NORM) {
+    if (!(o->norm_eps > 0.f && o->norm_eps < 3.0e38f))
+      return fail(LA_ERR_UNSUPPORTED, "norm_eps must be positive and finite");
+    f->norm_w = o->norm_weight;
+    f->norm_eps = o->norm_eps;
+  }
   return LA_OK;
+}
+
+void apply_fused(const Fused& f, la::ChunkArgs* a) {
+  a->pro = f.pro();
+  a->gate_scale = f.gate_scale;
+  a->dskip = f.dskip;
+  a->out_norm = (f.flags & LA_EPI_OUT_NORM) != 0;
+  a->norm_w = f.norm_w;
+  a->norm_eps = f.norm_eps;
 }
 
 // Segment count of la_chunk_fwd_segmented: 1 .. min(ceil(L / C), 1024);
@@ -205,13 +236,15 @@ int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_
   const Range rs0(a.S0, n_s * 4), ro(a.out, n_v * osz), rsf(a.S_final, n_s * 4);
   const Range rws(need > 0 ? a.workspace : nullptr, need);
   const Range rcu(a.cu, cu_bytes);
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &rcu})
+  const size_t n_hd = (size_t)a.H * a.d * 4;             // an [H, dv] float parameter
+  const Range rds(a.dskip, n_hd), rnw(a.out_norm ? a.norm_w : nullptr, n_hd);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &rcu, &rds, &rnw})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro, &rcu})
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &ro, &rcu, &rds, &rnw})
     if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
   if (rsf.overlaps(rs0) && (a.S0 != a.S_final))
     return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf, &rcu})
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf, &rcu, &rds, &rnw})
     if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -233,21 +266,27 @@ int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_
     prof_add("la_seg_scan", e1, e0);
     if (e != hipSuccess) return fail_hip("launching the segment scan", e);
   }
-  const hipError_t e = la::launch_chunk(a, st);
-  prof_add("la_chunk", e0, prof_mark(st));
+  hipError_t e = la::launch_chunk(a, st);
+  hipEvent_t e1 = prof_mark(st);
+  prof_add("la_chunk", e0, e1);
   if (e != hipSuccess) return fail_hip("launching the chunk kernel", e);
+  if (a.out_norm) {
+    e = la::launch_out_norm(a, st);
+    prof_add("la_out_norm", e1, prof_mark(st));
+    if (e != hipSuccess) return fail_hip("launching the output norm", e);
+  }
   return LA_OK;
 }
 
 // la_decode_step and la_decode_step_fused (flags 0: the inputs as given).
 int decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                 const float* beta, float* S, void* out, int B, int H, int dk, int dv, int mode,
-                int dtype, int flags, float gate_scale, void* stream) {
+                int dtype, const la_fused_opts_t* opts, void* stream) {
   if (!q || !k || !v || !S || !out) return fail(LA_ERR_NULL, "q, k, v, S and out are required");
   if (int e = check_mode_dtype(mode, dtype)) return e;
   if (int e = check_gates(mode, log_alpha, beta)) return e;
-  int pro = 0;
-  if (int e = check_pro(flags, gate_scale, mode, &pro)) return e;
+  Fused f;
+  if (int e = check_fused(opts, mode, &f)) return e;
   if (B <= 0 || H <= 0 || dk <= 0 || dv <= 0)
     return fail(LA_ERR_SHAPE, "B, H, dk and dv must be positive");
   if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
@@ -264,13 +303,19 @@ int decode_step(const void* q, const void* k, const void* v, const float* log_al
   const Range rla(la::mode_decay(mode) ? log_alpha : nullptr, n_g * 4);
   const Range rb(la::mode_erase(mode) ? beta : nullptr, n_g * 4);
   const Range rs(S, n_s * 4), ro(out, n_v * osz);
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs})
+  const Range rds(f.dskip, (size_t)H * dv * 4);
+  const Range rnw((f.flags & LA_EPI_OUT_NORM) ? f.norm_w : nullptr, (size_t)H * dv * 4);
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs, &rds, &rnw})
     if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps S or an input");
-  for (const Range* in : {&rq, &rk, &rv, &rla, &rb})
+  for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rds, &rnw})
     if (rs.overlaps(*in)) return fail(LA_ERR_ALIAS, "S overlaps an input");
 
   la::DecodeArgs a{q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode,
-                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, pro, gate_scale};
+                   dtype != LA_DTYPE_F32, dtype == LA_DTYPE_BF16, f.pro(), f.gate_scale};
+  a.dskip = f.dskip;
+  a.out_norm = (f.flags & LA_EPI_OUT_NORM) != 0;
+  a.norm_w = f.norm_w;
+  a.norm_eps = f.norm_eps;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = prof_mark(st);
   hipError_t e = la::launch_decode(a, st);
@@ -300,17 +345,17 @@ int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mod
 }
 
 int la_chunk_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode,
-                                   int dtype, int flags, size_t* bytes) {
+                                   int dtype, const la_fused_opts_t* opts, size_t* bytes) {
   g_last_error.clear();
   if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
   if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
-  int pro = 0;
-  if (int e = check_pro(flags, 1.f, mode, &pro)) return e;
-  if (pro && dtype == LA_DTYPE_F32)
-    return fail(LA_ERR_UNSUPPORTED, "the fused prologue takes bf16 inputs");
+  Fused f;
+  if (int e = check_fused(opts, mode, &f)) return e;
+  if (f.flags && dtype == LA_DTYPE_F32)
+    return fail(LA_ERR_UNSUPPORTED, "the fused forward takes bf16 inputs");
   la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                nullptr, B, H, L, dk, C, mode, dtype, nullptr);
-  a.pro = pro;
+  apply_fused(f, &a);
   a.P = la::plan_segments(a);
   *bytes = la::chunk_workspace_bytes(a);
   return LA_OK;
@@ -361,25 +406,25 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
 
 int la_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* a_raw,
                        const float* b_raw, const float* S0, void* out, float* S_final, int B,
-                       int H, int L, int dk, int dv, int C, int mode, int dtype, int flags,
-                       float gate_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                       int H, int L, int dk, int dv, int C, int mode, int dtype,
+                       const la_fused_opts_t* opts, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   g_last_error.clear();
   if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
   if (int e = check_mode_dtype(mode, dtype)) return e;
   if (int e = check_gates(mode, a_raw, b_raw)) return e;
   if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
-  int pro = 0;
-  if (int e = check_pro(flags, gate_scale, mode, &pro)) return e;
-  if (pro && dtype == LA_DTYPE_F32)
-    return fail(LA_ERR_UNSUPPORTED, "the fused prologue takes bf16 inputs");
+  Fused f;
+  if (int e = check_fused(opts, mode, &f)) return e;
+  if (f.flags && dtype == LA_DTYPE_F32)
+    return fail(LA_ERR_UNSUPPORTED, "the fused forward takes bf16 inputs");
   size_t n_qk, n_v, n_g, n_s;
   if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
       !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   la::ChunkArgs a = chunk_args(q, k, v, a_raw, b_raw, S0, out, S_final, B, H, L, dk, C, mode,
                                dtype, workspace);
-  a.pro = pro;
-  a.gate_scale = gate_scale;
+  apply_fused(f, &a);
   a.P = la::plan_segments(a);
   return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
 }
@@ -444,16 +489,15 @@ int la_decode_step(const void* q, const void* k, const void* v, const float* log
                    const float* beta, float* S, void* out, int B, int H, int dk, int dv,
                    int mode, int dtype, void* stream) {
   g_last_error.clear();
-  return decode_step(q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode, dtype, 0, 0.f,
+  return decode_step(q, k, v, log_alpha, beta, S, out, B, H, dk, dv, mode, dtype, nullptr,
                      stream);
 }
 
 int la_decode_step_fused(const void* q, const void* k, const void* v, const float* a_raw,
                          const float* b_raw, float* S, void* out, int B, int H, int dk, int dv,
-                         int mode, int dtype, int flags, float gate_scale, void* stream) {
+                         int mode, int dtype, const la_fused_opts_t* opts, void* stream) {
   g_last_error.clear();
-  return decode_step(q, k, v, a_raw, b_raw, S, out, B, H, dk, dv, mode, dtype, flags,
-                     gate_scale, stream);
+  return decode_step(q, k, v, a_raw, b_raw, S, out, B, H, dk, dv, mode, dtype, opts, stream);
 }
 
 int la_profile_begin(void) {

@@ -616,11 +616,12 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
 // Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
 // (U_new = V in the modes without erase), into o[u] (row tile u ? TI1 : TI0, accumulator
 // layout).  U_new arrives in float (Uf, accumulator layout, tile ti at
-// ti * 64 + lane) and is split here.
-template <int D, int MODE, int NTI, int TI0, int TI1>
+// ti * 64 + lane) and is split here.  DSKIP: plus the residual dcol * V of
+// the lane's column (the value tile read in the same accumulator layout).
+template <int D, int MODE, bool DSKIP, int NTI, int TI0, int TI1>
 __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
                                          const f32x4* Uf, const T16* Vt, f32x4 (&o)[2],
-                                         int g, int n, int lane) {
+                                         int g, int n, int lane, float dcol) {
   constexpr bool kDelta = mode_erase(MODE);
   Frag2<T16> uf[2];
 #pragma unroll
@@ -646,6 +647,7 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&
         mma(a.hi, uf[kb].hi, o[u]);
       }
     }
+    if constexpr (DSKIP) o[u] += dcol * v_acc_at(Vt, vacc_off(g, n) + 512 * ti);
   }
 }
 
@@ -689,15 +691,17 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 //   scores  exp((g_r + lq_r) - (g_i - lk_i)),  Q S rows  exp(g + lq),
 //   update  exp(g_C - g + lk),  erase  beta exp(g + lk)
 // (MODE is then one of the decayed modes; log alpha = 0 stands for none).
-template <int D, int MODE, bool OUT, bool FUSED>
+// DSKIP: the output gains the residual D * v (Mamba's term in v), D [H, dv].
+template <int D, int MODE, bool OUT, bool FUSED, bool DSKIP>
 __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const u32x4* __restrict__ tws, void* __restrict__ out_, StreamMap smap, int NS,
-    int out_bf16, ProArrays pro) {
+    int out_bf16, ProArrays pro, const float* __restrict__ dskip) {
   constexpr bool kDelta = mode_erase(MODE);      // delta rule: beta, T, U_new
   constexpr bool kGated = mode_decay(MODE);      // scalar decay: log alpha
   static_assert(!FUSED || kGated, "normalised q, k ride in the decay tables");
+  static_assert(!DSKIP || OUT, "the residual is part of the output");
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
   constexpr int NCT = D / 16;                    // column tiles per head
@@ -753,6 +757,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int col0 = ct * 16;
   const int col = col0 + n;
   const StreamInfo si = stream_info(smap, sidx);
+  const float dcol = DSKIP ? dskip[(size_t)si.head * D + col] : 0.f;
   const size_t hbase = si.row0;                 // first token row
   const int L = si.len;                         // tokens of this stream
   if (L == 0) {
@@ -1157,13 +1162,13 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         const T16* Vp = Vs[(c - 1) % 4];
         const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
         if (wave == 1) {
-          out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
+          out_rows<D, MODE, DSKIP, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane, dcol);
           store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, C);
         } else if (wave == 2) {
-          out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
+          out_rows<D, MODE, DSKIP, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane, dcol);
           store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, C);
         } else {
-          out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
+          out_rows<D, MODE, DSKIP, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane, dcol);
           store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, C);
         }
       }
@@ -1197,13 +1202,13 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       const f32x4* U = Uf[kDelta ? c % 2 : 0];
       const T16* Vp = Vs[c % 4];
       if (wave == 1) {
-        out_rows<D, MODE, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane);
+        out_rows<D, MODE, DSKIP, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane, dcol);
         store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, nlast);
       } else if (wave == 2) {
-        out_rows<D, MODE, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane);
+        out_rows<D, MODE, DSKIP, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane, dcol);
         store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, nlast);
       } else {
-        out_rows<D, MODE, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane);
+        out_rows<D, MODE, DSKIP, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane, dcol);
         store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, nlast);
       }
     }
@@ -1354,6 +1359,38 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(
   }
 }
 
+// ---------------------------------------------------------------- output norm
+
+// Output normalisation of the fused epilogue: each (token, head) row of out
+// becomes o / sqrt(mean(o^2) + eps) times w[h] (ones without w) -- the norm
+// that takes the place of linear attention's dropped denominator ("The
+// Devil in Linear Transformer" in "LinearAttention 概述").  One wave per
+// row, float arithmetic, in place; rows are token rows of [B, H, L, dv] or
+// [H, T, dv], so row / L names (b, h) and its head.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, size_t rows, int L,
+                                                       int H, const float* __restrict__ w,
+                                                       float eps) {
+  constexpr int PER = D / kWave;
+  const size_t row = (size_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;              // whole waves
+  const int lane = threadIdx.x % kWave;
+  TO* o = out + row * D;
+  float x[PER], ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    x[j] = to_f32(o[lane + kWave * j]);
+    ss = fmaf(x[j], x[j], ss);
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float r = rsqrtf(ss / D + eps);
+  const float* wh = w ? w + (size_t)((row / L) % H) * D : nullptr;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    o[lane + kWave * j] = from_f32<TO>(x[j] * r * (wh ? wh[lane + kWave * j] : 1.f));
+}
+
 // ---------------------------------------------------------------- launches
 
 constexpr int kComputeUnits = 256;   // gfx950 (MI355X)
@@ -1408,17 +1445,25 @@ StreamMap stream_map(const ChunkArgs& a, int pass) {
 }
 
 // a: the kernel arguments (kernel_args of the call)
-template <int D, int MODE, bool OUT, bool FUSED>
+template <int D, int MODE, bool OUT, bool FUSED, bool DSKIP>
 hipError_t launch_one(const ChunkArgs& a, int pass, hipStream_t st) {
   const StreamMap m = stream_map(a, pass);
   const size_t ns = (size_t)a.B * a.H * m.per_seq();
   const dim3 grid((unsigned)(ns * (D / 16))), block(kThreads);
   const ProArrays pro = FUSED ? pro_arrays(a) : ProArrays{};
-  chunk_pipe_kernel<D, MODE, OUT, FUSED><<<grid, block, 0, st>>>(
+  chunk_pipe_kernel<D, MODE, OUT, FUSED, DSKIP><<<grid, block, 0, st>>>(
       static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
       a.log_alpha, a.beta, static_cast<const u32x4*>(a.workspace), a.out, m, (int)ns,
-      a.out_bf16 ? 1 : 0, pro);
+      a.out_bf16 ? 1 : 0, pro, a.dskip);
   return hipGetLastError();
+}
+
+// the residual in v only where outputs are written
+template <int D, int MODE, bool OUT, bool FUSED>
+hipError_t launch_ep(const ChunkArgs& a, int pass, hipStream_t st) {
+  if constexpr (OUT)
+    if (a.dskip) return launch_one<D, MODE, OUT, FUSED, true>(a, pass, st);
+  return launch_one<D, MODE, OUT, FUSED, false>(a, pass, st);
 }
 
 // a: the call's arguments (raw gates when the prologue activates them)
@@ -1440,14 +1485,14 @@ hipError_t launch_d(const ChunkArgs& call, int pass, hipStream_t st) {
   const ChunkArgs a = kernel_args(call);
   const bool fused = call.pro & kProQKNorm;
   switch (a.mode) {
-    case kModeLinear: return launch_one<D, kModeLinear, OUT, false>(a, pass, st);
-    case kModeDelta: return launch_one<D, kModeDelta, OUT, false>(a, pass, st);
+    case kModeLinear: return launch_ep<D, kModeLinear, OUT, false>(a, pass, st);
+    case kModeDelta: return launch_ep<D, kModeDelta, OUT, false>(a, pass, st);
     case kModeGatedLinear:
-      return fused ? launch_one<D, kModeGatedLinear, OUT, true>(a, pass, st)
-                   : launch_one<D, kModeGatedLinear, OUT, false>(a, pass, st);
+      return fused ? launch_ep<D, kModeGatedLinear, OUT, true>(a, pass, st)
+                   : launch_ep<D, kModeGatedLinear, OUT, false>(a, pass, st);
     default:
-      return fused ? launch_one<D, kModeGatedDelta, OUT, true>(a, pass, st)
-                   : launch_one<D, kModeGatedDelta, OUT, false>(a, pass, st);
+      return fused ? launch_ep<D, kModeGatedDelta, OUT, true>(a, pass, st)
+                   : launch_ep<D, kModeGatedDelta, OUT, false>(a, pass, st);
   }
 }
 
@@ -1523,6 +1568,27 @@ hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
   if (a.d == 64)
     return gated ? launch_t<64, true, false, true>(a, st) : launch_t<64, false, false, true>(a, st);
   return gated ? launch_t<128, true, false, true>(a, st) : launch_t<128, false, false, true>(a, st);
+}
+
+hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st) {
+  const size_t rows = token_rows(a);
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (a.out_bf16) {
+    if (a.d == 64)
+      out_norm_kernel<T16, 64><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), rows, a.L, a.H,
+                                                        a.norm_w, a.norm_eps);
+    else
+      out_norm_kernel<T16, 128><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), rows, a.L,
+                                                         a.H, a.norm_w, a.norm_eps);
+  } else {
+    if (a.d == 64)
+      out_norm_kernel<float, 64><<<grid, block, 0, st>>>(static_cast<float*>(a.out), rows, a.L,
+                                                          a.H, a.norm_w, a.norm_eps);
+    else
+      out_norm_kernel<float, 128><<<grid, block, 0, st>>>(static_cast<float*>(a.out), rows, a.L,
+                                                           a.H, a.norm_w, a.norm_eps);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_state(const ChunkArgs& a, hipStream_t st) {

@@ -26,6 +26,10 @@
 // norms r_q, r_k are computed with k . q and folded into the products (s
 // and k . q carry r_k, p and k . q carry r_q, the update's k carries r_k),
 // so the state pass is unchanged.
+//
+// Fused epilogue: o += D * v per channel (dskip [H, dv]), then with out_norm
+// o / sqrt(mean(o^2) + norm_eps) times norm_w [H, dv] (ones when NULL), the
+// sum of squares over dv reduced through LDS.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
@@ -37,11 +41,19 @@ __device__ __forceinline__ float softplus_d(float x) {
   return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));   // log(1 + e^x), no overflow
 }
 
+struct DecodeEpi {
+  const float* dskip;    // [H, dv] or NULL
+  const float* norm_w;   // [H, dv] or NULL (ones)
+  float norm_eps;
+  int H;
+  bool norm;
+};
+
 template <typename T, typename TO, int DK, int DV, int MODE>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
-    float* __restrict__ S, TO* __restrict__ out, int pro, float gate_scale) {
+    float* __restrict__ S, TO* __restrict__ out, int pro, float gate_scale, DecodeEpi epi) {
   constexpr int NQ = DV / 4;       // 16-byte column quads per state row
   constexpr int RG = 256 / NQ;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -52,7 +64,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __shared__ float sv[DV];
   __shared__ float su[DV];
   __shared__ float red[2][RG][DV];
-  __shared__ float skq, srk, srq;
+  __shared__ float skq, srk, srq, sno;
+  __shared__ float so[DV];
 
   const size_t bh = blockIdx.x;
   const int t = threadIdx.x;
@@ -145,9 +158,25 @@ __global__ __launch_bounds__(256) void decode_kernel(
       o = a * pj + skq * u;
     }
     su[t] = u;
-    out[bh * DV + t] = from_f32<TO>(o);
+    if (epi.dskip) o = fmaf(epi.dskip[(bh % epi.H) * DV + t], sv[t], o);
+    if (epi.norm) so[t] = o;
+    else out[bh * DV + t] = from_f32<TO>(o);
   }
   __syncthreads();
+  if (epi.norm) {
+    if (t < kWave) {
+      float ss = 0.f;
+      for (int j = t; j < DV; j += kWave) ss = fmaf(so[j], so[j], ss);
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      if (t == 0) sno = rsqrtf(ss / DV + epi.norm_eps);
+    }
+    __syncthreads();
+    if (t < DV) {
+      const float wv = epi.norm_w ? epi.norm_w[(bh % epi.H) * DV + t] : 1.f;
+      out[bh * DV + t] = from_f32<TO>(so[t] * sno * wv);
+    }
+  }
 
   float u4[4];
 #pragma unroll
@@ -169,22 +198,23 @@ hipError_t launch_dk_dv(const DecodeArgs& a, hipStream_t st) {
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   TO* o = static_cast<TO*>(a.out);
+  const DecodeEpi epi{a.dskip, a.norm_w, a.norm_eps, a.H, a.out_norm};
   switch (a.mode) {
     case kModeLinear:
       decode_kernel<T, TO, DK, DV, kModeLinear><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale, epi);
       break;
     case kModeDelta:
       decode_kernel<T, TO, DK, DV, kModeDelta><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale, epi);
       break;
     case kModeGatedLinear:
       decode_kernel<T, TO, DK, DV, kModeGatedLinear><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale, epi);
       break;
     default:
       decode_kernel<T, TO, DK, DV, kModeGatedDelta><<<grid, block, 0, st>>>(
-          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale);
+          q, k, v, a.log_alpha, a.beta, a.S, o, a.pro, a.gate_scale, epi);
       break;
   }
   return hipGetLastError();

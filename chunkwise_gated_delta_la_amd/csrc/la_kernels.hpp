@@ -27,6 +27,13 @@ struct DecodeArgs {
   bool out_bf16;  // out is bf16 (else float)
   int pro = 0;            // fused prologue flags (kProGates, kProQKNorm)
   float gate_scale = 0.f;
+  // Fused epilogue: o += D * v (D [H, dv], NULL: none), then with
+  // out_norm the output normalised over dv: o / sqrt(mean(o^2) + norm_eps)
+  // times norm_w [H, dv] (NULL: ones).
+  const float* dskip = nullptr;
+  bool out_norm = false;
+  const float* norm_w = nullptr;
+  float norm_eps = 0.f;
 };
 
 struct ChunkArgs {
@@ -55,6 +62,14 @@ struct ChunkArgs {
   // token inside the op.  0: the inputs are used as given.
   int pro = 0;
   float gate_scale = 0.f;
+  // Fused epilogue: o += D * v per channel (D [H, dv], NULL: none); with
+  // out_norm the output normalised over dv per token and head, o /
+  // sqrt(mean(o^2) + norm_eps) times norm_w [H, dv] (NULL: ones), by a
+  // separate pass over out (the chain kernels own 16 columns each).
+  const float* dskip = nullptr;
+  bool out_norm = false;
+  const float* norm_w = nullptr;
+  float norm_eps = 0.f;
 };
 
 enum : int { kProGates = 1, kProQKNorm = 2 };
@@ -170,6 +185,7 @@ struct StreamInfo {
   size_t row0;        // first token row
   int len;            // tokens
   size_t slot0;       // T-factor slot of the first chunk
+  int head;           // h of the stream's (b, h) or (sequence, h)
   const float* s0;    // start state, NULL: zero
   float* sf;          // end state, NULL: not stored
   bool eye;           // start from the identity, V read as zero
@@ -178,7 +194,8 @@ struct StreamInfo {
 __host__ __device__ inline StreamInfo stream_info(const StreamMap& m, int s) {
   if (m.pass == kPassWhole) {
     const SeqInfo si = seq_info(m.sm, s);
-    return StreamInfo{si.row0, si.len, si.slot0, m.S0 ? m.S0 + (size_t)s * m.dd : nullptr,
+    return StreamInfo{si.row0, si.len, si.slot0, s % m.sm.H,
+                      m.S0 ? m.S0 + (size_t)s * m.dd : nullptr,
                       m.S_final ? m.S_final + (size_t)s * m.dd : nullptr, false};
   }
   const int n = m.per_seq();
@@ -193,7 +210,8 @@ __host__ __device__ inline StreamInfo stream_info(const StreamMap& m, int s) {
   const int c0 = seg_chunk0(p, m.P, nc), c1 = seg_chunk0(p + 1, m.P, nc);
   const int t0 = c0 * m.sm.C, t1 = min(c1 * m.sm.C, m.sm.L);
   const size_t st = ((size_t)bh * m.P + p) * m.dd;
-  StreamInfo si{(size_t)bh * m.sm.L + t0, t1 - t0, (size_t)bh * nc + c0, nullptr, nullptr, eye};
+  StreamInfo si{(size_t)bh * m.sm.L + t0, t1 - t0, (size_t)bh * nc + c0, bh % m.sm.H, nullptr,
+                nullptr, eye};
   if (m.pass == kPassOut) {
     si.s0 = m.sin + st;
     si.sf = (p == m.P - 1 && m.S_final) ? m.S_final + (size_t)bh * m.dd : nullptr;
@@ -207,6 +225,9 @@ __host__ __device__ inline StreamInfo stream_info(const StreamMap& m, int s) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// The output normalisation of the fused epilogue over out [rows, dv]
+// (la_chunk_pipe.hip).
+hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st);
 // Chunk forward: float inputs run one kernel (la_chunk.hip); bf16 inputs
 // in the delta (erase) modes first solve T for every chunk (launch_tsolve,
 // into the workspace), then run the chain kernel (la_chunk_pipe.hip).

@@ -84,7 +84,8 @@ typedef enum {
   LA_DTYPE_BF16_F32OUT = 2  /* q, k, v bf16;    out float32 */
 } la_dtype_t;
 
-/* Fused prologue of la_chunk_fwd_fused / la_decode_step_fused (flags, OR-ed).
+/* Steps in front of and behind the op that the fused entry points
+ * (la_chunk_fwd_fused, la_decode_step_fused) take inside; flags, OR-ed.
  * LA_PRO_GATES: the gate arguments are raw scores a, b and the op uses
  *   beta = sigmoid(b) and log_alpha = -gate_scale * softplus(a), with
  *   softplus(a) = log(1 + e^a) -- a write strength in (0, 1) from an
@@ -94,11 +95,31 @@ typedef enum {
  *   there; "继续改进：Mamba" in the lecture notes).
  * LA_PRO_QK_L2NORM: q and k are used as x / sqrt(|x|^2 + 1e-6) per token:
  *   the delta rule replaces a stored value exactly only for unit keys
- *   ("Fast Weight Programmers与DeltaNet"). */
+ *   ("Fast Weight Programmers与DeltaNet").
+ * LA_EPI_DSKIP: o_t += D * v_t per channel, D [H, dv] float32 -- the term in
+ *   v that Mamba adds to the output next to the state's read-out, a
+ *   residual path around the state ("继续改进：Mamba" in the lecture notes).
+ * LA_EPI_OUT_NORM: then o_t = o_t / sqrt(mean over dv of o_t^2 + norm_eps)
+ *   * w per (token, head), w [H, dv] float32 (NULL: ones) -- the output
+ *   normalisation that replaces linear attention's denominator ("The Devil
+ *   in Linear Transformer" in "LinearAttention 概述").  In the chunkwise
+ *   forward it is a second pass over out (the chain kernels own 16 columns
+ *   of a row each); a bf16 out is normalised from its rounded values. */
 typedef enum {
   LA_PRO_GATES = 1,
-  LA_PRO_QK_L2NORM = 2
-} la_prologue_t;
+  LA_PRO_QK_L2NORM = 2,
+  LA_EPI_DSKIP = 4,
+  LA_EPI_OUT_NORM = 8
+} la_fused_flag_t;
+
+/* Options of the fused entry points; a NULL pointer to it means none. */
+typedef struct {
+  int flags;                 /* la_fused_flag_t bits                       */
+  float gate_scale;          /* LA_PRO_GATES in a decayed mode: > 0        */
+  const float* dskip;        /* LA_EPI_DSKIP: D [H, dv], DEVICE            */
+  const float* norm_weight;  /* LA_EPI_OUT_NORM: w [H, dv], DEVICE, or NULL */
+  float norm_eps;            /* LA_EPI_OUT_NORM: > 0                       */
+} la_fused_opts_t;
 
 typedef enum {
   LA_OK = 0,
@@ -181,47 +202,49 @@ int la_chunk_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
                              int mode, int dtype, size_t* bytes);
 
 /*
- * la_chunk_fwd_fused -- la_chunk_fwd with the steps in front of the op done
- * inside it (fused prologue, la_prologue_t `flags`): from raw gate scores
- * (LA_PRO_GATES) and / or unnormalised q and k (LA_PRO_QK_L2NORM).  The
- * result is la_chunk_fwd's on the prepared inputs, except that q and k are
- * normalised in float32 and never rounded to bf16 after normalisation.
+ * la_chunk_fwd_fused -- la_chunk_fwd with the steps in front of and behind
+ * the op done inside it (la_fused_flag_t in opts->flags): raw gate scores
+ * (LA_PRO_GATES), unnormalised q and k (LA_PRO_QK_L2NORM), the residual in
+ * v (LA_EPI_DSKIP) and the output norm (LA_EPI_OUT_NORM).  The result is
+ * la_chunk_fwd's on the prepared inputs followed by the epilogue, except
+ * that q and k are normalised in float32 and never rounded to bf16 after
+ * normalisation.
  *
  *   a_raw      [B, H, L] float32  log_alpha as in la_chunk_fwd, or with
  *                                 LA_PRO_GATES the raw decay score a
  *   b_raw      [B, H, L] float32  beta, or with LA_PRO_GATES the raw score b
- *   flags      la_prologue_t bits; LA_PRO_GATES is ignored in LINEAR mode
- *              (no gates); flags = 0 is exactly la_chunk_fwd
- *   gate_scale positive, finite (LA_PRO_GATES with a decayed mode), else
- *              ignored
+ *   opts       la_fused_opts_t or NULL; LA_PRO_GATES is ignored in LINEAR
+ *              mode (no gates); NULL or flags = 0 is exactly la_chunk_fwd
  *   workspace  at least la_chunk_fused_workspace_bytes() for the same
- *              arguments: la_chunk_fwd's, then four float32 arrays of
- *              B*H*L (the gates and the logs of the inverse norms of q and
- *              k, written by the T-solve kernel and read by the chain)
- *   everything else as in la_chunk_fwd (sequence-parallel plan included)
+ *              arguments: la_chunk_fwd's, then with a prologue flag four
+ *              float32 arrays of B*H*L (the gates and the logs of the
+ *              inverse norms of q and k, written by the T-solve kernel and
+ *              read by the chain)
+ *   everything else as in la_chunk_fwd (sequence-parallel plan included);
+ *              dskip and norm_weight count as inputs for the alias rules
  *
- * Supported: bf16 inputs (LA_DTYPE_BF16, LA_DTYPE_BF16_F32OUT) for flags !=
- * 0, else LA_ERR_UNSUPPORTED; flags outside la_prologue_t or a bad
- * gate_scale: LA_ERR_UNSUPPORTED.  With LA_PRO_QK_L2NORM the inverse norms
- * ride in the decay tables of the chain kernels (LINEAR and DELTA run their
- * decayed kernels with log alpha = 0): no extra pass over q, k or the
- * output.
+ * Supported: bf16 inputs (LA_DTYPE_BF16, LA_DTYPE_BF16_F32OUT) when any
+ * flag is set, else LA_ERR_UNSUPPORTED; unknown flags, a bad gate_scale or
+ * norm_eps: LA_ERR_UNSUPPORTED; LA_EPI_DSKIP with a NULL dskip:
+ * LA_ERR_NULL.  With LA_PRO_QK_L2NORM the inverse norms ride in the decay
+ * tables of the chain kernels (LINEAR and DELTA run their decayed kernels
+ * with log alpha = 0): no extra pass over q or k.
  */
 int la_chunk_fwd_fused(const void* q, const void* k, const void* v,
                        const float* a_raw, const float* b_raw, const float* S0,
                        void* out, float* S_final, int B, int H, int L, int dk,
-                       int dv, int C, int mode, int dtype, int flags,
-                       float gate_scale, void* workspace,
+                       int dv, int C, int mode, int dtype,
+                       const la_fused_opts_t* opts, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /*
  * la_chunk_fused_workspace_bytes -- workspace size for la_chunk_fwd_fused
- * with these sizes, mode, dtype and flags, written to *bytes.  Same checks
+ * with these sizes, mode, dtype and options, written to *bytes.  Same checks
  * and error codes; LA_ERR_NULL for a NULL bytes.
  */
 int la_chunk_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
-                                   int mode, int dtype, int flags,
-                                   size_t* bytes);
+                                   int mode, int dtype,
+                                   const la_fused_opts_t* opts, size_t* bytes);
 
 /*
  * la_chunk_fwd_segmented -- la_chunk_fwd with each (b, h) sequence cut into
@@ -362,18 +385,18 @@ int la_decode_step(const void* q, const void* k, const void* v,
                    int dtype, void* stream);
 
 /*
- * la_decode_step_fused -- la_decode_step with the fused prologue
- * (la_prologue_t `flags`, `gate_scale` as in la_chunk_fwd_fused): a_raw and
- * b_raw [B, H] are the raw gate scores with LA_PRO_GATES, and q, k are
- * normalised inside with LA_PRO_QK_L2NORM (their inverse norms folded into
- * the step's dot products and update).  Both dtypes; flags = 0 is exactly
- * la_decode_step.  Errors as la_decode_step, plus LA_ERR_UNSUPPORTED for
- * bad flags or gate_scale.
+ * la_decode_step_fused -- la_decode_step with the fused steps of
+ * la_chunk_fwd_fused (opts as there): a_raw and b_raw [B, H] are the raw
+ * gate scores with LA_PRO_GATES; q, k are normalised inside with
+ * LA_PRO_QK_L2NORM (their inverse norms folded into the step's dot products
+ * and update); LA_EPI_DSKIP and LA_EPI_OUT_NORM act on the step's output
+ * inside the kernel.  Both dtypes; NULL opts or flags = 0 is exactly
+ * la_decode_step.  Errors as la_decode_step, plus those of the options.
  */
 int la_decode_step_fused(const void* q, const void* k, const void* v,
                          const float* a_raw, const float* b_raw, float* S,
                          void* out, int B, int H, int dk, int dv, int mode,
-                         int dtype, int flags, float gate_scale,
+                         int dtype, const la_fused_opts_t* opts,
                          void* stream);
 
 /*

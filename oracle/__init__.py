@@ -28,6 +28,8 @@ Modules:
   intermediates.
 * ``prologue``   -- the steps in front of the op that the fused entry points
   take inside (q, k L2 normalisation, gate activations).
+* ``epilogue``   -- the steps behind it (the residual in v, the output
+  normalisation).
 
 Parity status of each function is stated in its module header.
 """
@@ -41,6 +43,7 @@ from .recurrence import (  # noqa: F401
     recurrent_step,
 )
 from .prologue import l2_normalise, prepare, sigmoid, softplus  # noqa: F401
+from .epilogue import add_dskip, out_norm  # noqa: F401
 from .chunkwise import (  # noqa: F401
     chunkwise_fwd,
     forward_substitution_inverse,

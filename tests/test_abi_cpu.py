@@ -288,24 +288,35 @@ def test_segment_plan():
     assert lib.la_chunk_segments(1, 1, 64, 96, 96, 64, 2, 1, ctypes.byref(n)) == UNSUP
 
 
+def opts(flags=3, scale=0.0625, dskip=None, norm_w=None, eps=1e-6):
+    return _lib.FusedOpts(flags, scale, dskip, norm_w, eps)
+
+
 def fused(lib, flags=3, scale=0.0625, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4),
           s0=fake(5), out=fake(6), sf=fake(7), B=1, H=1, L=640, dk=64, dv=64, C=64, mode=2,
-          dtype=1, ws=fake(8), wsb=P_BIG):
+          dtype=1, ws=fake(8), wsb=P_BIG, dskip=None, norm_w=None, eps=1e-6):
+    o = opts(flags, scale, dskip, norm_w, eps)
     return lib.la_chunk_fwd_fused(q, k, v, la, be, s0, out, sf, B, H, L, dk, dv, C, mode, dtype,
-                                  flags, ctypes.c_float(scale), ws, wsb, None)
+                                  ctypes.byref(o), ws, wsb, None)
 
 
 def fused_ws(lib, flags, B=1, H=1, L=640, d=64, mode=2, dtype=1):
     n = ctypes.c_size_t(0)
-    rc = lib.la_chunk_fused_workspace_bytes(B, H, L, d, d, 64, mode, dtype, flags, ctypes.byref(n))
+    o = opts(flags, dskip=P if flags & 4 else None)
+    rc = lib.la_chunk_fused_workspace_bytes(B, H, L, d, d, 64, mode, dtype, ctypes.byref(o),
+                                            ctypes.byref(n))
     return rc, n.value
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(flags=4), UNSUP), (dict(flags=-1), UNSUP), (dict(flags=1, scale=0.0), UNSUP),
+    (dict(flags=16), UNSUP), (dict(flags=-1), UNSUP), (dict(flags=1, scale=0.0), UNSUP),
     (dict(flags=3, scale=float("inf")), UNSUP), (dict(flags=2, dtype=0), UNSUP),
+    (dict(flags=4, dtype=0, dskip=9 * P), UNSUP), (dict(flags=4), NULL),
+    (dict(flags=8, eps=0.0), UNSUP), (dict(flags=8, eps=float("nan")), UNSUP),
     (dict(la=None), NULL), (dict(be=None, mode=1), NULL), (dict(wsb=1), WS),
     (dict(out=ctypes.c_void_p(P + 128)), ALIAS),
+    (dict(flags=4, dskip=7 * P + 64), ALIAS),                # out overlaps D
+    (dict(flags=8, norm_w=8 * P + 64), ALIAS),               # S_final overlaps the weight
 ])
 def test_chunk_fwd_fused_rejects(kw, code):
     lib = _lib.get()
@@ -321,6 +332,12 @@ def test_fused_flag_rules():
     assert fused(lib, flags=1, scale=0.0, mode=1, q=None) == NULL        # delta: no decay
     assert fused(lib, flags=1, scale=0.0, mode=0, dtype=0, q=None) == NULL
     assert fused(lib, flags=2, mode=0, dtype=0) == UNSUP                 # norm needs bf16
+    # the norm weight is optional, and only counted when the norm is asked for
+    assert fused(lib, flags=8, q=None) == NULL
+    assert fused(lib, flags=4, dskip=9 * P, norm_w=6 * P, q=None) == NULL
+    assert lib.la_chunk_fwd_fused(fake(0), fake(1), fake(2), fake(3), fake(4), None, fake(6),
+                                  None, 1, 1, 64, 64, 64, 64, 2, 1, None, fake(8), P,
+                                  None) != UNSUP
 
 
 def test_fused_workspace_size():
@@ -337,22 +354,29 @@ def test_fused_workspace_size():
             for flags in (1, 2, 3):
                 want = base if (flags == 1 and mode == 0) else (-(-base // 256) * 256 + 4 * arr)
                 assert fused_ws(lib, flags, B, H, L, d, mode) == (OK, want)
+                assert fused_ws(lib, flags | 12, B, H, L, d, mode) == (OK, want)
+            assert fused_ws(lib, 4, B, H, L, d, mode) == (OK, base)       # epilogue only
+            assert fused_ws(lib, 8, B, H, L, d, mode) == (OK, base)
             assert fused_ws(lib, 0, B, H, L, d, mode) == (OK, base)
     assert fused_ws(lib, 2, dtype=0)[0] == UNSUP
     assert fused_ws(lib, 0, dtype=0) == (OK, 0)
-    assert lib.la_chunk_fused_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, 3, None) == NULL
+    o = opts(3)
+    assert lib.la_chunk_fused_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o),
+                                              None) == NULL
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(flags=8), UNSUP), (dict(flags=1, scale=-1.0), UNSUP), (dict(q=None), NULL),
-    (dict(la=None), NULL), (dict(S=ctypes.c_void_p(P + 64)), ALIAS),
+    (dict(flags=32), UNSUP), (dict(flags=1, scale=-1.0), UNSUP), (dict(q=None), NULL),
+    (dict(la=None), NULL), (dict(S=ctypes.c_void_p(P + 64)), ALIAS), (dict(flags=4), NULL),
+    (dict(flags=8, eps=-1.0), UNSUP), (dict(flags=4, dskip=6 * P + 8), ALIAS),
 ])
 def test_decode_fused_rejects(kw, code):
     lib = _lib.get()
     a = dict(flags=3, scale=0.0625, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4),
-             S=fake(5), out=fake(6))
+             S=fake(5), out=fake(6), dskip=None, eps=1e-6)
     a.update(kw)
+    o = opts(a["flags"], a["scale"], a["dskip"], None, a["eps"])
     rc = lib.la_decode_step_fused(a["q"], a["k"], a["v"], a["la"], a["be"], a["S"], a["out"],
-                                  1, 1, 64, 64, 2, 1, a["flags"], ctypes.c_float(a["scale"]), None)
+                                  1, 1, 64, 64, 2, 1, ctypes.byref(o), None)
     assert rc == code
     assert lib.la_last_error().decode() != ""

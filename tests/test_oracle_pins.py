@@ -537,3 +537,39 @@ def _prepared(q, k, v, a, b, mode, flags):
     from oracle.prologue import prepare
     qq, kk, la, be = prepare(q, k, a, b, mode, flags, 1.0 / 16.0)
     return qq, kk, v, la, be
+
+
+# ---------------------------------------------------------------- fused epilogue
+
+def test_dskip_worked_example():
+    """o + D v per (head, channel): a hand-computed case with two heads, so a
+    D applied per token, per batch or transposed fails."""
+    from oracle.epilogue import add_dskip
+    o = np.array([[[[1.0, 2.0]], [[0.0, -1.0]]]])       # [B=1, H=2, L=1, dv=2]
+    v = np.array([[[[3.0, 4.0]], [[2.0, 5.0]]]])
+    D = np.array([[0.5, -1.0], [2.0, 0.25]])            # [H, dv]
+    want = np.array([[[[2.5, -2.0]], [[4.0, 0.25]]]])
+    assert np.array_equal(add_dskip(o, v, D), want)
+
+
+def test_out_norm_closed_form():
+    """With unit weights the normalised row has mean square m / (m + eps),
+    m the row's mean square, and keeps each element's sign and ratio; a
+    weight multiplies channel by channel, per head; the norm is taken over
+    the value channels only (scaling one token's row leaves the others)."""
+    from oracle.epilogue import out_norm
+    rng = np.random.default_rng(9)
+    o = rng.standard_normal((2, 3, 5, 8)) * rng.uniform(0.01, 10.0, (2, 3, 5, 1))
+    eps = 1e-3
+    y = out_norm(o, eps=eps)
+    m = np.mean(o * o, axis=-1)
+    assert _rel(np.mean(y * y, axis=-1), m / (m + eps)) < 1e-14
+    assert np.all(np.sign(y) == np.sign(o))
+    w = rng.uniform(0.5, 2.0, (3, 8))
+    assert _rel(out_norm(o, w, eps), y * w[None, :, None, :]) < 1e-15
+    o2 = o.copy()
+    o2[1, 2, 3] *= 7.0
+    y2 = out_norm(o2, eps=eps)
+    mask = np.ones(o.shape[:3], bool)
+    mask[1, 2, 3] = False
+    assert np.array_equal(y2[mask], y[mask])

@@ -459,6 +459,99 @@ def test_decode_fused_prologue(mode, dtype, flags):
     assert_close("S", f64(S), S_ref, dtype)
 
 
+def _epi_params(w, seed):
+    gen = torch.Generator("cpu").manual_seed(seed)
+    D = torch.randn((w.H, w.dv), generator=gen) * 0.5
+    nw = 1.0 + 0.1 * torch.randn((w.H, w.dv), generator=gen)
+    return D, nw
+
+
+def _epi_oracle(o, v, D, nw, dskip, norm, eps):
+    if dskip:
+        o = oracle.add_dskip(o, v, D.double().numpy())
+    if norm:
+        o = oracle.out_norm(o, nw.double().numpy(), eps)
+    return o
+
+
+@pytest.mark.parametrize("steps", ["dskip", "norm", "all"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_fused_epilogue(mode, d, steps):
+    """The residual D v added by the output waves and the output norm (its
+    own pass over out), alone and after the whole prologue; every element
+    against the oracle's prologue, recurrence and epilogue, over 5 full
+    chunks and a partial one."""
+    dskip, norm = steps in ("dskip", "all"), steps in ("norm", "all")
+    f = 3 if steps == "all" else 0
+    w = recipe(mode, "bf16", B=2, H=2, L=64 * 5 + 13, d=d, s0_std=0.3, seed=83)
+    log(f"chunk fused epilogue {steps} {w}")
+    r = _raw(w, f)
+    D, nw = _epi_params(w, 84)
+    o_ref, S_ref = _fused_oracle(r, mode, f)
+    o_ref = _epi_oracle(o_ref, r["v"].double().numpy(), D, nw, dskip, norm, 1e-5)
+    dev = to_cuda(r)
+    a = dev["a_raw"] if f & 1 else dev["log_alpha"]
+    b = dev["b_raw"] if f & 1 else dev["beta"]
+    for odt in (None, torch.float32):
+        out, S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], a, b, dev["S0"], mode=mode,
+                              qk_l2norm=bool(f & 2), gate_act=bool(f & 1), gate_scale=GATE_SCALE,
+                              dskip=D.cuda() if dskip else None, out_norm=norm,
+                              norm_weight=nw.cuda() if norm else None, norm_eps=1e-5,
+                              out_dtype=odt)
+        torch.cuda.synchronize()
+        assert_close(f"o ({odt})", f64(out), o_ref, "bf16", bf16_out=odt is None)
+        assert_close("S_final", f64(S), S_ref, "bf16")
+
+
+def test_chunk_fused_all_segmented():
+    """Every fused step on one long gated-delta sequence, which the plan
+    runs sequence-parallel."""
+    mode = "gated_delta"
+    w = recipe(mode, "bf16", B=1, H=1, L=4096 + 40, d=128, s0_std=0.2, seed=89)
+    P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=mode)
+    log(f"chunk fused all segmented P={P} {w}")
+    assert P > 1
+    r = _raw(w, 3)
+    D, nw = _epi_params(w, 90)
+    o_ref, S_ref = _fused_oracle(r, mode, 3)
+    o_ref = _epi_oracle(o_ref, r["v"].double().numpy(), D, nw, True, True, 1e-6)
+    dev = to_cuda(r)
+    out, S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["a_raw"], dev["b_raw"], dev["S0"],
+                          mode=mode, qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE,
+                          dskip=D.cuda(), out_norm=True, norm_weight=nw.cuda())
+    torch.cuda.synchronize()
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final", f64(S), S_ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_fused_epilogue(mode, dtype):
+    """Decode steps with every fused step (the norm over dv reduced inside
+    the kernel): 12 steps of B=3 H=2 d=128 against the oracle."""
+    w = Workload(f"decode_{mode}_{dtype}", mode, dtype, B=3, H=2, L=1, dk=128, dv=128, C=1,
+                 qk_norm=True, qkv_scale=1.0, s0_std=0.3, steps=12, seed=97)
+    log(f"decode fused epilogue {w}")
+    r = _raw(w, 3)
+    D, nw = _epi_params(w, 98)
+    y = {key: t.to(torch.float64).numpy() for key, t in r.items()}
+    q, k, lg, be = oracle.prepare(y["q"], y["k"], y["a_raw"], y["b_raw"], mode, 3, GATE_SCALE)
+    o_ref, S_ref = oracle.decode_steps(y["S0"], q, k, y["v"], lg, be, mode)
+    # [N, B, H, dv] -> [B, H, N, dv] for the epilogue, and back
+    o_ref = np.moveaxis(_epi_oracle(np.moveaxis(o_ref, 0, 2), np.moveaxis(y["v"], 0, 2), D, nw,
+                                    True, True, 1e-6), 2, 0)
+    d = to_cuda(r)
+    S = d["S0"].clone()
+    outs = [la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["a_raw"][n], d["b_raw"][n], S,
+                           mode=mode, qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE,
+                           dskip=D.cuda(), out_norm=True, norm_weight=nw.cuda())
+            for n in range(w.steps)]
+    torch.cuda.synchronize()
+    assert_close("o", np.stack([f64(o) for o in outs]), o_ref, dtype, bf16_out=dtype == "bf16")
+    assert_close("S", f64(S), S_ref, dtype)
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]
