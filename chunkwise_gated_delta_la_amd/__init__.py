@@ -10,8 +10,9 @@ memory) and passes torch's current HIP stream.
     out, S_final = chunk_fwd_varlen(q, k, v, log_alpha, beta, S0, cu_seqlens)  # packed
     out, S_final = chunk_fwd(q, k, v, log_alpha, beta, S0, segments=8)  # sequence-parallel
     out = decode_step(q, k, v, log_alpha, beta, S, mode="gated_delta")  # S in place
+    out, S = noncausal_fwd(q, k, v, S0)                                   # O = Q (S0 + K^T V)
 """
 from ._lib import LAError, LIB_PATH  # noqa: F401
 from .api import (MODES, chunk_fwd, chunk_fwd_varlen, chunk_segments,  # noqa: F401
                   chunk_varlen_workspace_bytes, chunk_workspace_bytes, decode_step,
-                  kernel_timer, version)
+                  kernel_timer, noncausal_fwd, version)

@@ -53,6 +53,10 @@ def _declare(lib):
     lib.la_chunk_segmented_workspace_bytes.restype = i
     lib.la_chunk_segments.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.la_chunk_segments.restype = i
+    lib.la_noncausal_fwd.argtypes = [vp, vp, vp, fp, vp, fp, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_noncausal_fwd.restype = i
+    lib.la_noncausal_workspace_bytes.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_noncausal_workspace_bytes.restype = i
     op = ctypes.POINTER(FusedOpts)
     lib.la_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
                                        i, i, i, i, i, i, i, i, op, vp, sz, vp]

@@ -187,6 +187,43 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     return out, S_final
 
 
+def noncausal_fwd(q, k, v, S0=None, *, out=None, S_final=None, return_state=True,
+                  out_dtype=None, workspace=None):
+    """Bidirectional linear attention (``la_noncausal_fwd``): S = S0 + K^T V
+    over the whole sequence and o_t = S^T q_t for every token.  q, k, v
+    ``[B, H, L, d]`` bfloat16; S0 ``[B, H, d, d]`` float32 or None.  Returns
+    ``(out, S_final)``."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt != torch.bfloat16:
+        raise TypeError(f"noncausal_fwd takes bfloat16 q, k, v, got {dt}")
+    _need(k, "k", (B, H, L, dk), dt, dev)
+    _need(v, "v", (B, H, L, dv), dt, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    odt = out_dtype or (out.dtype if out is not None else dt)
+    code = _dtype_code(dt, odt)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=odt, device=dev)
+    _need(out, "out", (B, H, L, dv), odt, dev)
+    if S_final is None and return_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    lib = _lib.get()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib.la_noncausal_workspace_bytes(B, H, L, dk, dv, code, ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib.la_noncausal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(out), _ptr(S_final),
+                                  B, H, L, dk, dv, code, _ptr(workspace), workspace.numel(),
+                                  _stream(dev))
+    _lib.check(rc)
+    return out, S_final
+
+
 def chunk_varlen_workspace_bytes(N, H, T, dk, dv, *, mode="gated_delta", C=64,
                                  dtype=torch.bfloat16, out_dtype=None):
     """Workspace bytes ``la_chunk_fwd_varlen`` needs for these sizes

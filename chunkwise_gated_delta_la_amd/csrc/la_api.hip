@@ -172,6 +172,14 @@ void apply_fused(const Fused& f, la::ChunkArgs* a) {
   a->norm_eps = f.norm_eps;
 }
 
+// Shapes of the non-causal form: bf16 inputs, dk = dv in {64, 128}.
+int check_noncausal(int B, int H, int L, int dk, int dv, int dtype) {
+  if (dtype != LA_DTYPE_BF16 && dtype != LA_DTYPE_BF16_F32OUT)
+    return fail(LA_ERR_UNSUPPORTED, "la_noncausal_fwd takes bf16 inputs (LA_DTYPE_BF16 or "
+                                    "LA_DTYPE_BF16_F32OUT), got " + std::to_string(dtype));
+  return check_chunk_shape(B, H, L, dk, dv, 64, LA_MODE_LINEAR, dtype);
+}
+
 // Segment count of la_chunk_fwd_segmented: 1 .. min(ceil(L / C), 1024);
 // above 1 only for bf16 inputs.
 int check_segments(int L, int C, int dtype, int segments) {
@@ -358,6 +366,58 @@ int la_chunk_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C, i
   apply_fused(f, &a);
   a.P = la::plan_segments(a);
   *bytes = la::chunk_workspace_bytes(a);
+  return LA_OK;
+}
+
+int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv, int dtype,
+                                 size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_noncausal(B, H, L, dk, dv, dtype)) return e;
+  la::ChunkArgs a = chunk_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, B, H, L, dk, 64, LA_MODE_LINEAR, dtype, nullptr);
+  a.P = la::plan_sum_segments(a);
+  *bytes = la::noncausal_workspace_bytes(a);
+  return LA_OK;
+}
+
+int la_noncausal_fwd(const void* q, const void* k, const void* v, const float* S0, void* out,
+                     float* S_final, int B, int H, int L, int dk, int dv, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_noncausal(B, H, L, dk, dv, dtype)) return e;
+  size_t n_qk, n_s;
+  if (!count({B, H, L, dk}, &n_qk) || !count({B, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  la::ChunkArgs a = chunk_args(q, k, v, nullptr, nullptr, S0, out, S_final, B, H, L, dk, 64,
+                               LA_MODE_LINEAR, dtype, workspace);
+  a.P = la::plan_sum_segments(a);
+  const size_t need = la::noncausal_workspace_bytes(a);
+  if (!workspace)
+    return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
+                                      " bytes (la_noncausal_workspace_bytes)");
+  if (workspace_bytes < need)
+    return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, this call needs " + std::to_string(need));
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t osz = dtype == LA_DTYPE_BF16 ? 2 : 4;
+  const Range rq(q, n_qk * 2), rk(k, n_qk * 2), rv(v, n_qk * 2), rs0(S0, n_s * 4);
+  const Range ro(out, n_qk * osz), rsf(S_final, n_s * 4), rws(workspace, need);
+  for (const Range* in : {&rq, &rk, &rv, &rs0})
+    if (ro.overlaps(*in)) return fail(LA_ERR_ALIAS, "out overlaps an input");
+  for (const Range* in : {&rq, &rk, &rv, &ro})
+    if (rsf.overlaps(*in)) return fail(LA_ERR_ALIAS, "S_final overlaps an input or out");
+  if (rsf.overlaps(rs0) && S0 != S_final)
+    return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
+  for (const Range* in : {&rq, &rk, &rv, &rs0, &ro, &rsf})
+    if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = prof_mark(st);
+  const hipError_t e = la::launch_noncausal(a, st);
+  prof_add("la_noncausal", e0, prof_mark(st));
+  if (e != hipSuccess) return fail_hip("launching the non-causal kernels", e);
   return LA_OK;
 }
 

@@ -1391,6 +1391,90 @@ __global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, siz
     o[lane + kWave * j] = from_f32<TO>(x[j] * r * (wh ? wh[lane + kWave * j] : 1.f));
 }
 
+// ---------------------------------------------------------------- non-causal form
+
+// S = sum of the X_p of the sum pass (S0 + K^T V over the whole sequence),
+// in a fixed order: one thread per state element.  Written to the
+// workspace's S slot and, if given, to S_final.
+__global__ __launch_bounds__(256) void seg_sum_kernel(const float* __restrict__ xs,
+                                                      float* __restrict__ S,
+                                                      float* __restrict__ S_final, int P,
+                                                      size_t dd, size_t n) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const size_t bh = e / dd, i = e % dd;
+  const float* x = xs + bh * P * dd + i;
+  float a = 0.f;
+  for (int p = 0; p < P; ++p) a += x[(size_t)p * dd];
+  S[e] = a;
+  if (S_final) S_final[e] = a;
+}
+
+// O = Q S for every token of a (b, h) sequence (the bidirectional form:
+// each token reads the state after the whole sequence).  One workgroup per
+// (b, h) and 256 tokens; S (float) is split once into bf16 hi + lo operand
+// fragments in LDS, wave w computes token rows 16 w .. + 15 of each 64-token
+// block, all column tiles: per tile sum over dk of Q (exact bf16) times
+// S_hi and S_lo.  Q fragments are 16-byte loads straight from HBM (token
+// row n, columns 32 kb + 8 g ..), the same contraction order as S's.
+template <int D>
+__global__ __launch_bounds__(kThreads) void qs_kernel(const T16* __restrict__ q,
+                                                      const float* __restrict__ S,
+                                                      void* __restrict__ out_, int L,
+                                                      int out_bf16) {
+  constexpr int NKB = D / 32, NCT = D / 16;
+  constexpr int kRowsPerWg = 256;
+  __shared__ __attribute__((aligned(16))) Frag2<T16> Sf[NKB][NCT][kWave];
+  const int nblk = (L + kRowsPerWg - 1) / kRowsPerWg;
+  const size_t bh = blockIdx.x / nblk;
+  const int r0 = (blockIdx.x % nblk) * kRowsPerWg;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, n = lane % 16;
+  const float* Sb = S + bh * D * D;
+  for (int f = wave; f < NKB * NCT; f += kThreads / kWave) {
+    const int kb = f / NCT, ct = f % NCT;
+    Frag2<T16> x;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float a0 = Sb[(size_t)(32 * kb + 8 * g + j) * D + 16 * ct + n];
+      const float a1 = Sb[(size_t)(32 * kb + 8 * g + j + 1) * D + 16 * ct + n];
+      uint32_t hi, lo;
+      split_pair(a0, a1, hi, lo);
+      const bf16x2 h = __builtin_bit_cast(bf16x2, hi), l = __builtin_bit_cast(bf16x2, lo);
+      x.hi.v[j] = h[0];
+      x.hi.v[j + 1] = h[1];
+      x.lo.v[j] = l[0];
+      x.lo.v[j + 1] = l[1];
+    }
+    Sf[kb][ct][lane] = x;
+  }
+  __syncthreads();
+  const T16* qb = q + bh * (size_t)L * D;
+  for (int blk = 0; blk < kRowsPerWg / 64; ++blk) {
+    const int rt = r0 + 64 * blk + 16 * wave;      // first token row of this wave's tile
+    if (rt >= L) break;
+    Frag<T16> qf[NKB];
+    const int rr = min(rt + n, L - 1);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      qf[kb].v = *reinterpret_cast<const bf16x8*>(qb + (size_t)rr * D + 32 * kb + 8 * g);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[kb], Sf[kb][ct][lane], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt + 4 * g + e;
+        if (r >= L) continue;
+        const size_t o = (bh * (size_t)L + r) * D + 16 * ct + n;
+        if (out_bf16) static_cast<T16*>(out_)[o] = (T16)acc[e];
+        else static_cast<float*>(out_)[o] = acc[e];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launches
 
 constexpr int kComputeUnits = 256;   // gfx950 (MI355X)
@@ -1517,6 +1601,32 @@ size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
   return align256(seg_states_end(a)) + 4 * pro_stride(a);
 }
 
+// Segments of the non-causal sum pass: state-only LINEAR chains, two
+// workgroups per compute unit, about 0.85 of a walk step each; the sum costs
+// a read of every partial state.
+int plan_sum_segments(const ChunkArgs& a) {
+  const long chains = (long)a.B * a.H * (a.d / 16);
+  const int nc = (a.L + C - 1) / C;
+  const long slots = 2L * kComputeUnits;
+  double best = 1e300;
+  int best_p = 1;
+  for (int P = 1; P <= nc && P <= kMaxSegments; ++P) {
+    const double rounds = (double)((chains * P + slots - 1) / slots);
+    const double cost = 0.85 * rounds * ((nc + P - 1) / P) + 0.05 * P;
+    if (cost < best) {
+      best = cost;
+      best_p = P;
+    }
+  }
+  return best_p;
+}
+
+// X (P per sequence), an unused M block and S (slot 0 of S_in): the state
+// layout of the sequence-parallel passes.
+size_t noncausal_workspace_bytes(const ChunkArgs& a) {
+  return 3 * (size_t)a.B * a.H * a.P * a.d * a.d * sizeof(float);
+}
+
 ProArrays pro_arrays(const ChunkArgs& a) {
   char* base = static_cast<char*>(a.workspace) + align256(seg_states_end(a));
   const size_t s = pro_stride(a);
@@ -1588,6 +1698,29 @@ hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st) {
       out_norm_kernel<float, 128><<<grid, block, 0, st>>>(static_cast<float*>(a.out), rows, a.L,
                                                            a.H, a.norm_w, a.norm_eps);
   }
+  return hipGetLastError();
+}
+
+// Non-causal form: the sum pass (LINEAR chain kernel, state only, over P
+// segments), the sum of their end states, then O = Q S.  a.mode is LINEAR;
+// the workspace holds X (P per sequence) and S.
+hipError_t launch_noncausal(const ChunkArgs& a, hipStream_t st) {
+  const StreamMap m = stream_map(a, kPassSum);
+  const size_t n = (size_t)a.B * a.H * m.dd;
+  float* S = m.sin;                       // slot 0 of S_in holds S
+  hipError_t e = a.d == 64 ? launch_one<64, kModeLinear, false, false, false>(a, kPassSum, st)
+                           : launch_one<128, kModeLinear, false, false, false>(a, kPassSum, st);
+  if (e != hipSuccess) return e;
+  seg_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(m.xs, S, a.S_final,
+                                                                         a.P, m.dd, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t wgs = (size_t)a.B * a.H * ((a.L + 255) / 256);
+  if (a.d == 64)
+    qs_kernel<64><<<dim3((unsigned)wgs), dim3(kThreads), 0, st>>>(
+        static_cast<const T16*>(a.q), S, a.out, a.L, a.out_bf16 ? 1 : 0);
+  else
+    qs_kernel<128><<<dim3((unsigned)wgs), dim3(kThreads), 0, st>>>(
+        static_cast<const T16*>(a.q), S, a.out, a.L, a.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

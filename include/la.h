@@ -356,6 +356,36 @@ int la_chunk_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int C,
                                     int mode, int dtype, size_t* bytes);
 
 /*
+ * la_noncausal_fwd -- the bidirectional (non-causal) form of linear
+ * attention: every token reads the state after the whole sequence,
+ *     S = S0 + sum_t k_t v_t^T,   o_t = S^T q_t   (O = Q (K^T V)),
+ * by the associativity of the matrix products: two products in linear time
+ * with no causal mask ("快速预览" in "LinearAttention 概述": enough for
+ * bidirectional models, no kernel needed).  S is accumulated by the LINEAR-mode chain kernel
+ * over parallel segments of the sequence, the segments' partial states are
+ * summed in a fixed order, then O = Q S on MFMA with S split into bf16
+ * hi + lo operands.
+ *
+ *   q, k, v    [B, H, L, d]   bf16 (dtype LA_DTYPE_BF16 or _BF16_F32OUT)
+ *   S0         [B, H, d, d]   float32 or NULL (zeros)
+ *   out        [B, H, L, d]   bf16 / float32 (written)
+ *   S_final    [B, H, d, d]   float32 (written: S) or NULL; may equal S0
+ *   B, H, L, dk, dv  dk = dv in {64, 128}, L >= 1
+ *   workspace  at least la_noncausal_workspace_bytes() bytes, 16-byte
+ *              aligned (the segments' partial states and S)
+ * Errors as la_chunk_fwd; float inputs return LA_ERR_UNSUPPORTED.
+ */
+int la_noncausal_fwd(const void* q, const void* k, const void* v,
+                     const float* S0, void* out, float* S_final, int B, int H,
+                     int L, int dk, int dv, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* la_noncausal_workspace_bytes -- workspace size for la_noncausal_fwd with
+ * these sizes and dtype, written to *bytes; same checks. */
+int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv,
+                                 int dtype, size_t* bytes);
+
+/*
  * la_decode_step -- one token of the recurrence for B*H independent states
  * (decode / inference form), updating the state in place.
  *

@@ -30,6 +30,7 @@ Modules:
   take inside (q, k L2 normalisation, gate activations).
 * ``epilogue``   -- the steps behind it (the residual in v, the output
   normalisation).
+* ``noncausal``  -- the bidirectional form O = Q (S0 + K^T V).
 
 Parity status of each function is stated in its module header.
 """
@@ -44,6 +45,7 @@ from .recurrence import (  # noqa: F401
 )
 from .prologue import l2_normalise, prepare, sigmoid, softplus  # noqa: F401
 from .epilogue import add_dskip, out_norm  # noqa: F401
+from .noncausal import noncausal_fwd  # noqa: F401
 from .chunkwise import (  # noqa: F401
     chunkwise_fwd,
     forward_substitution_inverse,

@@ -380,3 +380,37 @@ def test_decode_fused_rejects(kw, code):
                                   1, 1, 64, 64, 2, 1, ctypes.byref(o), None)
     assert rc == code
     assert lib.la_last_error().decode() != ""
+
+
+def nc(lib, q=fake(0), k=fake(1), v=fake(2), s0=fake(5), out=fake(6), sf=fake(7), B=1, H=1,
+       L=640, d=64, dtype=1, ws=fake(8), wsb=P_BIG):
+    return lib.la_noncausal_fwd(q, k, v, s0, out, sf, B, H, L, d, d, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(dtype=0), UNSUP), (dict(d=96), UNSUP),
+    (dict(L=0), SHAPE), (dict(ws=None), WS), (dict(wsb=16), WS),
+    (dict(out=ctypes.c_void_p(P + 128)), ALIAS), (dict(sf=ctypes.c_void_p(6 * P + 4)), ALIAS),
+    (dict(ws=ctypes.c_void_p(2 * P - 64)), ALIAS),
+])
+def test_noncausal_rejects(kw, code):
+    lib = _lib.get()
+    assert nc(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_noncausal_workspace_size():
+    """Three state blocks per segment of the sum pass (the partial states, an
+    unused block and S), the segment count a function of the sizes only:
+    many heads walk whole, few long sequences are cut."""
+    lib = _lib.get()
+    def ws(B, H, L, d):
+        n = ctypes.c_size_t(0)
+        assert lib.la_noncausal_workspace_bytes(B, H, L, d, d, 1, ctypes.byref(n)) == OK
+        return n.value
+    assert ws(8, 16, 4096, 128) == 3 * 8 * 16 * 128 * 128 * 4          # 1024 chains: P = 1
+    n = ws(1, 1, 65536, 128)
+    P = n // (3 * 128 * 128 * 4)
+    assert n == 3 * P * 128 * 128 * 4 and 8 <= P <= 64
+    assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 0, ctypes.byref(ctypes.c_size_t())) == UNSUP
+    assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 1, None) == NULL

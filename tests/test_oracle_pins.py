@@ -573,3 +573,21 @@ def test_out_norm_closed_form():
     mask = np.ones(o.shape[:3], bool)
     mask[1, 2, 3] = False
     assert np.array_equal(y2[mask], y[mask])
+
+
+# ---------------------------------------------------------------- non-causal form
+
+def test_noncausal_orders_and_causal_last_token():
+    """O = Q (S0 + K^T V) equals the other evaluation order (Q K^T) V + Q S0
+    [LA-OV "快速预览"]; its state is the causal LINEAR recurrence's final
+    state, and its last token's output the causal last output (both see the
+    whole sequence) -- while earlier tokens differ (they see the future)."""
+    from oracle.noncausal import noncausal_fwd
+    q, k, v, _, _, S0 = _rand(53, B=2, H=2, L=11, dk=4, dv=3, unit_keys=False)
+    o, S = noncausal_fwd(q, k, v, S0)
+    qk = np.einsum("bhtd,bhsd->bhts", q, k)
+    assert _rel(o, np.einsum("bhts,bhsv->bhtv", qk, v) + np.einsum("bhtd,bhdv->bhtv", q, S0)) < 1e-13
+    o_c, S_c = recurrent_fwd(q, k, v, None, None, S0, "linear")
+    assert _rel(S, S_c) < 1e-13
+    assert _rel(o[:, :, -1], o_c[:, :, -1]) < 1e-13
+    assert _rel(o[:, :, 0], o_c[:, :, 0]) > 1e-3

@@ -552,6 +552,66 @@ def test_decode_fused_epilogue(mode, dtype):
     assert_close("S", f64(S), S_ref, dtype)
 
 
+# ------------------------------------------------------------------ non-causal form
+
+def _nc_oracle(x, heads=None):
+    y = workloads.to_f64(x)
+    if heads is not None:
+        bs, hs = [b for b, _ in heads], [h for _, h in heads]
+        sel = lambda t: t[bs, hs][None]      # noqa: E731
+        o, S = oracle.noncausal_fwd(sel(y["q"]), sel(y["k"]), sel(y["v"]), sel(y["S0"]))
+        return o[0], S[0]
+    return oracle.noncausal_fwd(y["q"], y["k"], y["v"], y["S0"])
+
+
+@pytest.mark.parametrize("L", [1, 64 * 5 + 13])
+@pytest.mark.parametrize("d", [64, 128])
+def test_noncausal_small(d, L):
+    """O = Q (S0 + K^T V): every element against the oracle, bf16 and float
+    outputs, with S0, one token and a ragged length; S_final == S0 in place."""
+    w = recipe("linear", "bf16", B=2, H=3, L=L, d=d, s0_std=0.3, seed=101)
+    log(f"noncausal small {w}")
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = _nc_oracle(x)
+    dev = to_cuda(x)
+    out, S = la.noncausal_fwd(dev["q"], dev["k"], dev["v"], dev["S0"])
+    out32, S32 = la.noncausal_fwd(dev["q"], dev["k"], dev["v"], dev["S0"],
+                                  out_dtype=torch.float32)
+    S_io = dev["S0"].clone()
+    la.noncausal_fwd(dev["q"], dev["k"], dev["v"], S_io, S_final=S_io)
+    torch.cuda.synchronize()
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("o (f32 out)", f64(out32), o_ref, "bf16")
+    assert_close("S", f64(S), S_ref, "bf16")
+    assert torch.equal(S32, S) and torch.equal(out32.to(torch.bfloat16), out)
+    assert_close("S in place", f64(S_io), S_ref, "bf16")
+
+
+def test_noncausal_long_few_heads():
+    """One long sequence per head (the sum pass cut into parallel segments)
+    and the linear workload's shape, sampled heads against the oracle."""
+    w = recipe("linear", "bf16", B=1, H=2, L=20000, d=128, s0_std=0.1, seed=103)
+    log(f"noncausal long {w}")
+    x = workloads.make_inputs(w)
+    o_ref, S_ref = _nc_oracle(x)
+    dev = to_cuda(x)
+    out, S = la.noncausal_fwd(dev["q"], dev["k"], dev["v"], dev["S0"])
+    torch.cuda.synchronize()
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S", f64(S), S_ref, "bf16")
+    w = WORKLOADS[2]
+    log(f"noncausal full {w}")
+    x = workloads.make_inputs(w)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    o_ref, S_ref = _nc_oracle(x, heads)
+    dev = to_cuda(x)
+    out, S = la.noncausal_fwd(dev["q"], dev["k"], dev["v"], None)
+    torch.cuda.synchronize()
+    sel = lambda t: t[[0, w.B - 1], [0, w.H - 1]]   # noqa: E731
+    assert_close("o", f64(sel(out)), o_ref, "bf16", bf16_out=True)
+    assert_close("S", f64(sel(S)), S_ref, "bf16")
+
+
 def test_chunk_workload1_full():
     """Gated delta, float32, B=1 H=2 L=256 d=64: all elements, rel 1e-4."""
     w = WORKLOADS[1]
