@@ -362,6 +362,99 @@ def bench_segments(w, steps, warmup):
     return res
 
 
+def _timed(step, steps, warmup):
+    """ms per call of step() (host clock around synchronised runs) and the
+    library's per-kernel HIP-event times over the same calls."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with la.kernel_timer() as kt:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    kernels = {k: {"launches": n, "avg_ms": round(ms / max(n, 1), 5)}
+               for k, (n, ms) in kt.stats.items()}
+    return (t1 - t0) / steps * 1e3, kernels
+
+
+def bench_fused(w, steps, warmup):
+    """The forward from raw inputs with every step in front of and behind
+    the op fused (q, k normalisation, gate activations, residual D v, output
+    norm), against the same steps as separate torch operations around
+    la_chunk_fwd (context: what the fusion saves)."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] fused steps {w.name}: generating inputs")
+    r = {k: t.cuda() for k, t in workloads.make_raw_inputs(w).items()}
+    gen = torch.Generator("cpu").manual_seed(w.seed + 11)
+    D = (torch.randn((w.H, w.dv), generator=gen) * 0.5).cuda()
+    nw = (1.0 + 0.1 * torch.randn((w.H, w.dv), generator=gen)).cuda()
+    out = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.torch_dtype, device="cuda")
+    S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    scale = 1.0 / 16.0
+    nws = la.chunk_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, dtype=w.torch_dtype,
+                                   qk_l2norm=True, gate_act=True)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        la.chunk_fwd(r["q"], r["k"], r["v"], r["a_raw"], r["b_raw"], r["S0"], mode=w.mode,
+                     out=out, S_final=S_final, workspace=ws, qk_l2norm=True, gate_act=True,
+                     gate_scale=scale, dskip=D, out_norm=True, norm_weight=nw, norm_eps=1e-6)
+
+    def unfused():
+        qf, kf = r["q"].float(), r["k"].float()
+        qn = (qf * torch.rsqrt((qf * qf).sum(-1, keepdim=True) + 1e-6)).to(w.torch_dtype)
+        kn = (kf * torch.rsqrt((kf * kf).sum(-1, keepdim=True) + 1e-6)).to(w.torch_dtype)
+        lg = -scale * torch.nn.functional.softplus(r["a_raw"])
+        be = torch.sigmoid(r["b_raw"])
+        o, _ = la.chunk_fwd(qn, kn, r["v"], lg, be, r["S0"], mode=w.mode, S_final=S_final,
+                            out_dtype=torch.float32)
+        o = o + D[None, :, None, :] * r["v"].float()
+        o = o * torch.rsqrt((o * o).mean(-1, keepdim=True) + 1e-6) * nw[None, :, None, :]
+        out.copy_(o)
+
+    f_ms, f_k = _timed(fused, steps, warmup)
+    u_ms, _ = _timed(unfused, steps, warmup)
+    del ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "steps_fused": "qk_l2norm, gate_act, dskip, out_norm",
+            "ms_per_step": round(f_ms, 4), "tokens_per_s": round(w.B * w.L / f_ms * 1e3, 1),
+            "kernels": f_k, "torch_composed_ms_per_step": round(u_ms, 4)}
+
+
+def bench_noncausal(w, steps, warmup):
+    """The bidirectional form O = Q (S0 + K^T V) at a forward workload's
+    sizes: tokens/s and the fraction of HBM peak of its algorithmic bytes
+    (q, k, v read and o written once, states per head)."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] non-causal {w.name}: generating inputs")
+    x = {k: t.cuda() for k, t in workloads.make_inputs(w).items()}
+    out = torch.empty((w.B, w.H, w.L, w.dv), dtype=torch.bfloat16, device="cuda")
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    s0 = x["S0"] if w.s0_std > 0 else None
+    ms, kernels = _timed(lambda: la.noncausal_fwd(x["q"], x["k"], x["v"], s0, out=out,
+                                                 S_final=S), steps, warmup)
+    by = w.B * w.H * (w.L * (w.dk * 2 + w.dv * 2 * 2) + (2 if s0 is not None else 1) * w.dk
+                      * w.dv * 4)
+    del x, out
+    torch.cuda.empty_cache()
+    return {"workload": "noncausal_" + w.name, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.B * w.L / ms * 1e3, 1), "algorithmic_bytes": by,
+            "hbm_frac": round(by / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4), "kernels": kernels}
+
+
 def varlen_lengths(n, total, seed):
     """Seeded length mix of a packed batch: n lengths summing to `total`,
     log-uniform between 1 and 16 K tokens (short prompts next to long
@@ -539,6 +632,8 @@ def main():
                                                 mode="gated_linear"), args.steps, 1),
             "varlen": bench_varlen(w, 64, w.L, args.steps, 1),
             "segments": bench_segments(workloads.WORKLOAD4_SHARD8, args.steps, 1),
+            "fused": bench_fused(w, args.steps, 1),
+            "noncausal": bench_noncausal(workloads.WORKLOADS[2], args.steps, 1),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {

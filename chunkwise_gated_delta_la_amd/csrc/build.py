@@ -71,8 +71,9 @@ def build(jobs=None, verbose=False):
     if failed:
         raise RuntimeError("liblachunk: compilation failed")
     tmp = LIB + ".tmp"
-    rc, msg = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
-                   verbose)
+    # -z defs: a symbol left undefined fails the link instead of the load
+    rc, msg = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp]
+                   + objs, verbose)
     if rc != 0:
         raise RuntimeError("liblachunk: link failed\n" + msg)
     os.replace(tmp, LIB)

@@ -1364,31 +1364,66 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(
 // Output normalisation of the fused epilogue: each (token, head) row of out
 // becomes o / sqrt(mean(o^2) + eps) times w[h] (ones without w) -- the norm
 // that takes the place of linear attention's dropped denominator ("The
-// Devil in Linear Transformer" in "LinearAttention 概述").  One wave per
-// row, float arithmetic, in place; rows are token rows of [B, H, L, dv] or
-// [H, T, dv], so row / L names (b, h) and its head.
+// Devil in Linear Transformer" in "LinearAttention 概述").  HBM-bound, in
+// place.  Grid y walks the (b, h) sequences (L token rows of [B, H, L, dv],
+// or the H heads of [H, T, dv]), so a workgroup knows its head without any
+// per-row division and keeps its lanes' weights in registers; grid x walks
+// a sequence's rows.  Every lane moves 16 bytes (EPL elements) per access,
+// D / EPL adjacent lanes hold one row and reduce its sum of squares among
+// themselves, two row groups' loads are in flight per wave.
 template <typename TO, int D>
-__global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, size_t rows, int L,
-                                                       int H, const float* __restrict__ w,
+__global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, int L, int H,
+                                                       unsigned nseq, const float* __restrict__ w,
                                                        float eps) {
-  constexpr int PER = D / kWave;
-  const size_t row = (size_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-  if (row >= rows) return;              // whole waves
+  constexpr int EPL = 16 / (int)sizeof(TO);        // elements per lane
+  constexpr int LPR = D / EPL;                     // lanes per row
+  constexpr int RPW = kWave / LPR;                 // rows per wave and group
+  typedef TO vec __attribute__((ext_vector_type(EPL)));
   const int lane = threadIdx.x % kWave;
-  TO* o = out + row * D;
-  float x[PER], ss = 0.f;
+  const int c0 = (lane % LPR) * EPL;
+  for (unsigned sq = blockIdx.y; sq < nseq; sq += gridDim.y) {
+  float wv[EPL];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    x[j] = to_f32(o[lane + kWave * j]);
-    ss = fmaf(x[j], x[j], ss);
+  for (int j = 0; j < EPL; ++j) wv[j] = 1.f;
+  if (w) {
+    const f32x4* wp = reinterpret_cast<const f32x4*>(w + (size_t)(sq % H) * D + c0);
+#pragma unroll
+    for (int j = 0; j < EPL / 4; ++j) {
+      const f32x4 t = wp[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[4 * j + i] = t[i];
+    }
   }
+  TO* seq = out + (size_t)sq * L * D;
+  const int groups = (L + RPW - 1) / RPW;
+  const int nwaves = gridDim.x * (256 / kWave);
+  for (int gi = blockIdx.x * (256 / kWave) + threadIdx.x / kWave; gi < groups;
+       gi += 2 * nwaves) {
+    int row[2];
+    bool live[2];
+    vec x[2];
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  const float r = rsqrtf(ss / D + eps);
-  const float* wh = w ? w + (size_t)((row / L) % H) * D : nullptr;
+    for (int u = 0; u < 2; ++u) {
+      row[u] = (gi + u * nwaves) * RPW + lane / LPR;
+      live[u] = gi + u * nwaves < groups && row[u] < L;
+      x[u] = live[u] ? *reinterpret_cast<const vec*>(seq + (size_t)row[u] * D + c0) : vec{};
+    }
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    o[lane + kWave * j] = from_f32<TO>(x[j] * r * (wh ? wh[lane + kWave * j] : 1.f));
+    for (int u = 0; u < 2; ++u) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) ss = fmaf((float)x[u][j], (float)x[u][j], ss);
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      if (!live[u]) continue;
+      const float r = rsqrtf(ss / D + eps);
+      vec y;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) y[j] = (TO)((float)x[u][j] * r * wv[j]);
+      *reinterpret_cast<vec*>(seq + (size_t)row[u] * D + c0) = y;
+    }
+  }
+  }
 }
 
 // ---------------------------------------------------------------- non-causal form
@@ -1681,22 +1716,27 @@ hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st) {
-  const size_t rows = token_rows(a);
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const unsigned nseq = (unsigned)(a.cu ? a.H : a.B * a.H);
+  // rows per workgroup pass: 4 waves of kWave * EPL / D rows, two passes in
+  // flight; about 8 workgroups per compute unit in all
+  const int per = 8 * kWave * (a.out_bf16 ? 8 : 4) / a.d;
+  const unsigned gx = (unsigned)std::max<long>(
+      1, std::min<long>((a.L + per - 1) / per, (8L * kComputeUnits + nseq - 1) / nseq));
+  const dim3 grid(gx, std::min(nseq, 65535u)), block(256);
   if (a.out_bf16) {
     if (a.d == 64)
-      out_norm_kernel<T16, 64><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), rows, a.L, a.H,
-                                                        a.norm_w, a.norm_eps);
+      out_norm_kernel<T16, 64><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), a.L, a.H,
+                                                        nseq, a.norm_w, a.norm_eps);
     else
-      out_norm_kernel<T16, 128><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), rows, a.L,
-                                                         a.H, a.norm_w, a.norm_eps);
+      out_norm_kernel<T16, 128><<<grid, block, 0, st>>>(static_cast<T16*>(a.out), a.L, a.H,
+                                                         nseq, a.norm_w, a.norm_eps);
   } else {
     if (a.d == 64)
-      out_norm_kernel<float, 64><<<grid, block, 0, st>>>(static_cast<float*>(a.out), rows, a.L,
-                                                          a.H, a.norm_w, a.norm_eps);
+      out_norm_kernel<float, 64><<<grid, block, 0, st>>>(static_cast<float*>(a.out), a.L, a.H,
+                                                          nseq, a.norm_w, a.norm_eps);
     else
-      out_norm_kernel<float, 128><<<grid, block, 0, st>>>(static_cast<float*>(a.out), rows, a.L,
-                                                           a.H, a.norm_w, a.norm_eps);
+      out_norm_kernel<float, 128><<<grid, block, 0, st>>>(static_cast<float*>(a.out), a.L, a.H,
+                                                           nseq, a.norm_w, a.norm_eps);
   }
   return hipGetLastError();
 }

@@ -414,3 +414,10 @@ def test_noncausal_workspace_size():
     assert n == 3 * P * 128 * 128 * 4 and 8 <= P <= 64
     assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 0, ctypes.byref(ctypes.c_size_t())) == UNSUP
     assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 1, None) == NULL
+
+
+def test_library_resolves_every_symbol_at_load():
+    """Loading with immediate binding fails on any undefined symbol (a lazy
+    load only fails when the missing function is first called, on a GPU)."""
+    import ctypes as ct
+    ct.CDLL(_lib.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
