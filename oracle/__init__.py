@@ -31,6 +31,8 @@ Modules:
 * ``epilogue``   -- the steps behind it (the residual in v, the output
   normalisation).
 * ``noncausal``  -- the bidirectional form O = Q (S0 + K^T V).
+* ``backward``   -- the gradients of every input, by the reverse of the token
+  recurrence.
 
 Parity status of each function is stated in its module header.
 """
@@ -46,6 +48,7 @@ from .recurrence import (  # noqa: F401
 from .prologue import l2_normalise, prepare, sigmoid, softplus  # noqa: F401
 from .epilogue import add_dskip, out_norm  # noqa: F401
 from .noncausal import noncausal_fwd  # noqa: F401
+from .backward import recurrent_bwd  # noqa: F401
 from .chunkwise import (  # noqa: F401
     chunkwise_fwd,
     forward_substitution_inverse,

@@ -591,3 +591,63 @@ def test_noncausal_orders_and_causal_last_token():
     assert _rel(S, S_c) < 1e-13
     assert _rel(o[:, :, -1], o_c[:, :, -1]) < 1e-13
     assert _rel(o[:, :, 0], o_c[:, :, 0]) > 1e-3
+
+
+# ---------------------------------------------------------------- backward
+
+def _loss(q, k, v, la, be, S0, mode, dO, dSf):
+    o, S = recurrent_fwd(q, k, v, la, be, S0, mode)
+    return float(np.sum(o * dO) + np.sum(S * dSf))
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_backward_matches_finite_differences(mode):
+    """Every gradient of sum(dO * O) + sum(dS_final * S_final) against
+    central finite differences of the forward, element by element, on a
+    tiny case (non-unit keys, beta and alpha away from their limits)."""
+    from oracle.backward import recurrent_bwd
+    q, k, v, la, be, S0 = _rand(61, B=1, H=2, L=6, dk=3, dv=2, unit_keys=False)
+    rng = np.random.default_rng(62)
+    dO = rng.standard_normal((1, 2, 6, 2))
+    dSf = rng.standard_normal((1, 2, 3, 2))
+    g = recurrent_bwd(q, k, v, la, be, S0, mode, dO, dSf)
+    args = dict(q=q, k=k, v=v, la=la, be=be, S0=S0)
+    names = dict(q="dq", k="dk", v="dv", S0="dS0")
+    if mode in oracle.GATED_MODES:
+        names["la"] = "dlog_alpha"
+    if mode in oracle.ERASE_MODES:
+        names["be"] = "dbeta"
+    h = 1e-6
+    for name, gname in names.items():
+        x = args[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            lp = _loss(**{**args, name: xp}, mode=mode, dO=dO, dSf=dSf)
+            lm = _loss(**{**args, name: xm}, mode=mode, dO=dO, dSf=dSf)
+            num[idx] = (lp - lm) / (2 * h)
+        assert _rel(g[gname], num) < 1e-7, (name, _rel(g[gname], num))
+    if mode not in oracle.GATED_MODES:
+        assert g["dlog_alpha"] is None
+    if mode not in oracle.ERASE_MODES:
+        assert g["dbeta"] is None
+
+
+def test_backward_linear_closed_forms():
+    """Causal linear attention O = (Q K^T * M) V + Q S0 has dV = (Q K^T *
+    M)^T dO, dQ = (dO V^T * M) K + dO S0^T, dK = (dO V^T * M)^T Q and dS0 =
+    Q^T dO (S0 reaches every output through o_t += S0^T q_t)."""
+    from oracle.backward import recurrent_bwd
+    q, k, v, _, _, S0 = _rand(63, B=2, H=1, L=9, dk=4, dv=3, unit_keys=False)
+    dO = np.random.default_rng(64).standard_normal((2, 1, 9, 3))
+    g = recurrent_bwd(q, k, v, None, None, S0, "linear", dO)
+    M = np.tril(np.ones((9, 9)))
+    A = np.einsum("bhtd,bhsd->bhts", q, k) * M
+    dA = np.einsum("bhtv,bhsv->bhts", dO, v) * M
+    assert _rel(g["dv"], np.einsum("bhts,bhtv->bhsv", A, dO)) < 1e-13
+    dq = np.einsum("bhts,bhsd->bhtd", dA, k) + np.einsum("bhtv,bhdv->bhtd", dO, S0)
+    assert _rel(g["dq"], dq) < 1e-13
+    assert _rel(g["dk"], np.einsum("bhts,bhtd->bhsd", dA, q)) < 1e-13
+    assert _rel(g["dS0"], np.einsum("bhtd,bhtv->bhdv", q, dO)) < 1e-13
