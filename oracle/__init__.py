@@ -50,6 +50,7 @@ from .epilogue import add_dskip, out_norm  # noqa: F401
 from .noncausal import noncausal_fwd  # noqa: F401
 from .backward import recurrent_bwd  # noqa: F401
 from .chunkwise import (  # noqa: F401
+    chunkwise_bwd,
     chunkwise_fwd,
     forward_substitution_inverse,
     parallel_masked_linear,

@@ -50,7 +50,9 @@ equal to the product of the per-token factors alpha_r (I - beta_r k_r k_r^T)
 
 Parity status: pinned -- to the token recurrence for C = 1, C = L and ragged
 chunkings in every mode (and through it to the pins of each mode), T to a
-library triangular solve, P to the explicit product of dk x dk factors
+library triangular solve, P to the explicit product of dk x dk factors;
+``chunkwise_bwd`` to the reverse of the token recurrence (``backward``,
+itself pinned by finite differences) for every mode and chunking
 (tests/test_oracle_pins.py).
 """
 
@@ -199,3 +201,114 @@ def chunkwise_fwd(q, k, v, log_alpha, beta, S0, mode, C):
         S = (np.exp(gC)[..., None] * S
              + np.matmul(np.swapaxes(Kt, -1, -2), U_new))
     return o, S
+
+
+def chunkwise_bwd(q, k, v, log_alpha, beta, S0, mode, C, dO, dS_final=None):
+    """Gradients by the chunkwise form: the same result as
+    ``backward.recurrent_bwd``, organised as a GPU backward would be.
+
+    The forward keeps the state entering every chunk (the per-chunk states a
+    training run saves [HA-1 "FWP分块并行机制"]).  Then, chunk by chunk in
+    reverse, with dS' the gradient of the state leaving the chunk and the
+    chunk's quantities as in ``chunkwise_fwd`` (f = gamma_C / gamma, P =
+    Q K^T * M * Gamma):
+
+        dU = P^T dO + diag(f) K dS'              (U = U_new; V without erase)
+        dR = T^T dU                              (U = T R, R = diag(beta)(V -
+                                                  diag(gamma) K S))
+        dS = gamma_C dS' + Q^T diag(gamma) dO - K^T diag(beta gamma) dR
+
+    is the only serial part -- the same shape as the forward's chain with T
+    transposed and two terms that do not depend on dS.  Every other gradient
+    of the chunk follows from S, dS', dO and the chunk's own inputs, in
+    parallel over chunks:
+
+        dQ = diag(gamma) dO S^T + (dO U^T * Gamma) K
+        dK = diag(f) U dS'^T - diag(beta gamma) dR S^T + (dO U^T * Gamma)^T Q
+             + H K + H^T K,   H = dA * beta_r * Gamma,  dA = strict_lower(-dR U^T)
+        dV = diag(beta) dR        (dU without erase)
+        dbeta_r = sum_j dR (V - diag(gamma) K S) + sum_i dA (K K^T) Gamma
+        dg = the decay's gradient through gamma, gamma_C, f and Gamma
+             (Gamma_ri = exp(g_r - g_i): +row sums, -column sums), and
+        dlog_alpha_i = sum over r >= i of dg_r   (g is the in-chunk cumsum).
+
+    The T factor's gradient uses d(I + A)^-1 = -T dA T, which with U = T R
+    collapses to dA = -dR U^T on the strictly lower triangle A occupies.
+    """
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {MODES}, got {mode!r}")
+    q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
+    B, H, L, dk = k.shape
+    dv = v.shape[-1]
+    erase, gated = mode in ERASE_MODES, mode in GATED_MODES
+    bounds = [(s, min(s + C, L)) for s in range(0, L, C)]
+    # forward: the state entering each chunk
+    entry = []
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    for s, e in bounds:
+        entry.append(S)
+        _, S = chunkwise_fwd(q[:, :, s:e], k[:, :, s:e], v[:, :, s:e],
+                             None if log_alpha is None else log_alpha[:, :, s:e],
+                             None if beta is None else beta[:, :, s:e], S, mode, e - s)
+    dq, dk_, dv_ = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dla, dbe = np.zeros((B, H, L)), np.zeros((B, H, L))
+    dS = np.zeros((B, H, dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
+    tr = lambda x: np.swapaxes(x, -1, -2)     # noqa: E731
+    for (s, e), S in zip(reversed(bounds), reversed(entry)):
+        n = e - s
+        Q, K, V, dOc = q[:, :, s:e], k[:, :, s:e], v[:, :, s:e], dO[:, :, s:e]
+        la, be = _gates(None if log_alpha is None else log_alpha[:, :, s:e],
+                        None if beta is None else beta[:, :, s:e], n, mode, K.shape[:-2])
+        g = np.cumsum(la, axis=-1)
+        gamma, Gamma = _decay(g)
+        gC = g[..., -1:]
+        f = np.exp(gC - g)
+        QKt = np.matmul(Q, tr(K))
+        P = QKt * Gamma
+        KS = np.matmul(K, S)
+        if erase:
+            KKt = np.matmul(K, tr(K))
+            A = np.tril(be[..., :, None] * KKt * Gamma, k=-1)
+            T = forward_substitution_inverse(A)
+            R = be[..., :, None] * (V - gamma[..., :, None] * KS)
+            U = np.matmul(T, R)
+        else:
+            U = V
+        # the output's and the carried state's direct terms
+        QS = np.matmul(Q, S)
+        dQ = gamma[..., :, None] * np.matmul(dOc, tr(S))
+        dS_in = np.matmul(tr(Q), gamma[..., :, None] * dOc) + np.exp(gC)[..., None] * dS
+        dgamma = np.sum(dOc * QS, axis=-1)
+        dgC = np.sum(dS * S, axis=(-2, -1))
+        dP = np.matmul(dOc, tr(U))
+        KdS = np.matmul(K, dS)
+        dU = np.matmul(tr(P), dOc) + f[..., :, None] * KdS
+        dK = f[..., :, None] * np.matmul(U, tr(dS))
+        df = np.sum(KdS * U, axis=-1)
+        dGamma = dP * QKt
+        if erase:
+            dR = np.matmul(tr(T), dU)
+            dA = np.tril(-np.matmul(dR, tr(U)), k=-1)
+            dV = be[..., :, None] * dR
+            dbe[:, :, s:e] = (np.sum(dR * (V - gamma[..., :, None] * KS), axis=-1)
+                              + np.sum(dA * KKt * Gamma, axis=-1))
+            bg = (be * gamma)[..., :, None]
+            dS_in = dS_in - np.matmul(tr(K), bg * dR)
+            dK = dK - bg * np.matmul(dR, tr(S))
+            dgamma = dgamma - be * np.sum(dR * KS, axis=-1)
+            Hm = dA * be[..., :, None] * Gamma
+            dK = dK + np.matmul(Hm, K) + np.matmul(tr(Hm), K)
+            dGamma = dGamma + dA * be[..., :, None] * KKt
+        else:
+            dV = dU
+        E = dP * Gamma
+        dQ = dQ + np.matmul(E, K)
+        dK = dK + np.matmul(tr(E), Q)
+        GG = dGamma * Gamma
+        dg = GG.sum(-1) - GG.sum(-2) + dgamma * gamma - df * f
+        dg[..., -1] += dgC * np.exp(gC[..., 0]) + np.sum(df * f, axis=-1)
+        dla[:, :, s:e] = np.flip(np.cumsum(np.flip(dg, -1), axis=-1), -1)
+        dq[:, :, s:e], dk_[:, :, s:e], dv_[:, :, s:e] = dQ, dK, dV
+        dS = dS_in
+    return dict(dq=dq, dk=dk_, dv=dv_, dlog_alpha=dla if gated else None,
+                dbeta=dbe if erase else None, dS0=dS)

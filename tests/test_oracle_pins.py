@@ -651,3 +651,25 @@ def test_backward_linear_closed_forms():
     assert _rel(g["dq"], dq) < 1e-13
     assert _rel(g["dk"], np.einsum("bhts,bhtd->bhsd", dA, q)) < 1e-13
     assert _rel(g["dS0"], np.einsum("bhtd,bhtv->bhdv", q, dO)) < 1e-13
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+@pytest.mark.parametrize("C", [1, 3, 7, 16, 29])
+def test_chunkwise_backward_equals_token_backward(mode, C):
+    """The chunkwise backward (per-chunk entry states, a reverse chain over
+    chunks with T transposed, parallel per-chunk gradients, dA = -dR U^T
+    through the triangular inverse, decay gradients summed back through the
+    in-chunk cumsum) gives the token backward's gradients for every chunk
+    size, ragged last chunk included."""
+    from oracle.backward import recurrent_bwd
+    q, k, v, la, be, S0 = _rand(71, B=2, H=1, L=29, dk=4, dv=3, unit_keys=True)
+    rng = np.random.default_rng(72)
+    dO = rng.standard_normal((2, 1, 29, 3))
+    dSf = rng.standard_normal((2, 1, 4, 3))
+    ref = recurrent_bwd(q, k, v, la, be, S0, mode, dO, dSf)
+    got = oracle.chunkwise_bwd(q, k, v, la, be, S0, mode, C, dO, dSf)
+    for name in ("dq", "dk", "dv", "dS0", "dlog_alpha", "dbeta"):
+        if ref[name] is None:
+            assert got[name] is None
+            continue
+        assert _rel(got[name], ref[name]) < 1e-11, (name, _rel(got[name], ref[name]))
