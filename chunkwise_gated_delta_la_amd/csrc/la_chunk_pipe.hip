@@ -1428,10 +1428,109 @@ __global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, int
 
 // ---------------------------------------------------------------- non-causal form
 
-// S = sum of the X_p of the sum pass (S0 + K^T V over the whole sequence),
-// in a fixed order: one thread per state element.  Written to the
-// workspace's S slot and, if given, to S_final.
+// Partial K^T V of one block of tokens of one (b, h) sequence: the sum over
+// its tokens of k_t v_t^T, a dk x dv float tile per workgroup.  The chunks
+// of a sum are independent, so token blocks run in parallel and the partial
+// states are added afterwards.  K and V chunks are DMA'd into LDS (double
+// buffered, the chain kernel's swizzled tile layout); both MFMA operands
+// are transposed reads of those tiles -- a K^T fragment (dk rows, token
+// contraction) and a V fragment (token contraction, dv columns) have the
+// same shape -- so the result arrives in the permuted state-row order on
+// both sides, undone at the store.  Wave w owns output row tiles w * TMW ..;
+// rows past the sequence's end read the last token and their V rows are
+// zeroed, so they add nothing.
+template <int D>
+__global__ __launch_bounds__(kThreads) void kv_kernel(const T16* __restrict__ k,
+                                                      const T16* __restrict__ v,
+                                                      float* __restrict__ partial, int L,
+                                                      int TB, int NB) {
+  constexpr int NT = D / 16;                 // 16-wide tiles per side
+  constexpr int TMW = NT / 4;                // output row tiles per wave
+  constexpr int NTILE = C * 2 * D / 1024;    // DMA instructions per tile
+  constexpr uint32_t kRows16 = 32 * D;
+  __shared__ __attribute__((aligned(16))) T16 Ks[2][C * D];
+  __shared__ __attribute__((aligned(16))) T16 Vs[2][C * D];
+  const size_t bh = blockIdx.x / NB;
+  const int t0 = (blockIdx.x % NB) * TB, t1 = min(t0 + TB, L);
+  const int nch = (t1 - t0 + C - 1) / C;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int g = lane / 16, n = lane % 16;
+  const T16* kb0 = k + (bh * L + t0) * D;
+  const T16* vb0 = v + (bh * L + t0) * D;
+  auto rows_of = [&](int c) { return min(C, t1 - t0 - c * C); };
+  // each wave moves half of the K or the V tile of a chunk
+  constexpr int NH = NTILE / 2;
+  auto issue = [&](int c) {
+    uint32_t off[NTILE];
+    dma_tile_offsets<D>(off, lane, rows_of(c));
+    const T16* src = (wave < 2 ? kb0 : vb0) + (size_t)c * C * D;
+    const uint32_t base = lds_addr(wave < 2 ? Ks[c % 2] : Vs[c % 2]);
+    const int m0 = (wave % 2) * NH;
+#pragma unroll
+    for (int m = 0; m < NH; ++m)
+      dma16s(src, off[m0 + m], __builtin_amdgcn_readfirstlane(base + 1024 * (m0 + m)));
+  };
+  f32x4 acc[TMW][NT];
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = zero4();
+  issue(0);
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) {
+      issue(c + 1);
+      vm_wait<NH>();                 // this wave's part of chunk c has landed
+    } else {
+      vm_wait<0>();
+    }
+    __syncthreads();
+    const int nr = rows_of(c);
+    if (nr < C) {
+      // V rows past the end of the block's tokens (the sequence's end) add
+      // nothing: zeroed once the whole tile has landed
+      if (wave == 2)
+        for (int r = nr; r < C; ++r) {
+          T16* row = Vs[c % 2] + r * D;
+          for (int j = lane; j < D; j += kWave) row[j] = (T16)0.f;
+        }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<T16> a[TMW];
+#pragma unroll
+      for (int i = 0; i < TMW; ++i) {
+        const int tm = wave * TMW + i;
+        a[i] = frag_tr_at(Ks[c % 2], tr_off<D>(g, n, tm / 2) + 8 * (tm % 2) + 64 * D * kb,
+                          kRows16);
+      }
+#pragma unroll
+      for (int tn = 0; tn < NT; ++tn) {
+        const Frag<T16> b = frag_tr_at(Vs[c % 2],
+                                       tr_off<D>(g, n, tn / 2) + 8 * (tn % 2) + 64 * D * kb,
+                                       kRows16);
+#pragma unroll
+        for (int i = 0; i < TMW; ++i) mma(a[i], b, acc[i][tn]);
+      }
+    }
+    __syncthreads();                 // buffer c % 2 is free for chunk c + 2
+  }
+  float* out = partial + (size_t)blockIdx.x * D * D;
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+#pragma unroll
+    for (int tn = 0; tn < NT; ++tn)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[(size_t)dk_of_row(16 * (wave * TMW + i) + 4 * g + e) * D + dk_of_row(16 * tn + n)] =
+            acc[i][tn][e];
+}
+
+// S = S0 + the sum of the partial states (fixed order): one thread per state
+// element.  Written to the workspace's S slot and, if given, to S_final.
 __global__ __launch_bounds__(256) void seg_sum_kernel(const float* __restrict__ xs,
+                                                      const float* __restrict__ S0,
                                                       float* __restrict__ S,
                                                       float* __restrict__ S_final, int P,
                                                       size_t dd, size_t n) {
@@ -1439,7 +1538,7 @@ __global__ __launch_bounds__(256) void seg_sum_kernel(const float* __restrict__ 
   if (e >= n) return;
   const size_t bh = e / dd, i = e % dd;
   const float* x = xs + bh * P * dd + i;
-  float a = 0.f;
+  float a = S0 ? S0[e] : 0.f;
   for (int p = 0; p < P; ++p) a += x[(size_t)p * dd];
   S[e] = a;
   if (S_final) S_final[e] = a;
@@ -1447,26 +1546,33 @@ __global__ __launch_bounds__(256) void seg_sum_kernel(const float* __restrict__ 
 
 // O = Q S for every token of a (b, h) sequence (the bidirectional form:
 // each token reads the state after the whole sequence).  One workgroup per
-// (b, h) and 256 tokens; S (float) is split once into bf16 hi + lo operand
-// fragments in LDS, wave w computes token rows 16 w .. + 15 of each 64-token
-// block, all column tiles: per tile sum over dk of Q (exact bf16) times
-// S_hi and S_lo.  Q fragments are 16-byte loads straight from HBM (token
-// row n, columns 32 kb + 8 g ..), the same contraction order as S's.
+// (b, h) and kQsRows tokens; S (float) is split once into bf16 hi + lo
+// operand fragments in LDS.  The product is computed transposed, O^T = S^T
+// Q^T, whose fragments are the same per-lane values as those of Q S (a
+// 16 x 32 operand holds row n, contraction 8 g ..): the accumulator then
+// gives each lane 4 consecutive columns of one token, stored in one 8- or
+// 16-byte write.  Wave w of 4 computes token rows 16 w .. + 15 of each
+// 64-token block, all column tiles, the next block's Q fragments loaded
+// (16-byte reads straight from HBM) before this block's products.
+constexpr int kQsRows = 1024;
+
+constexpr int kQsThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void qs_kernel(const T16* __restrict__ q,
+__global__ __launch_bounds__(kQsThreads) void qs_kernel(const T16* __restrict__ q,
                                                       const float* __restrict__ S,
                                                       void* __restrict__ out_, int L,
                                                       int out_bf16) {
   constexpr int NKB = D / 32, NCT = D / 16;
-  constexpr int kRowsPerWg = 256;
   __shared__ __attribute__((aligned(16))) Frag2<T16> Sf[NKB][NCT][kWave];
-  const int nblk = (L + kRowsPerWg - 1) / kRowsPerWg;
+  const int nblk = (L + kQsRows - 1) / kQsRows;
   const size_t bh = blockIdx.x / nblk;
-  const int r0 = (blockIdx.x % nblk) * kRowsPerWg;
+  const int r0 = (blockIdx.x % nblk) * kQsRows;
+  const int r1 = min(r0 + kQsRows, L);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = lane / 16, n = lane % 16;
   const float* Sb = S + bh * D * D;
-  for (int f = wave; f < NKB * NCT; f += kThreads / kWave) {
+  for (int f = wave; f < NKB * NCT; f += kQsThreads / kWave) {
     const int kb = f / NCT, ct = f % NCT;
     Frag2<T16> x;
 #pragma unroll
@@ -1484,29 +1590,39 @@ __global__ __launch_bounds__(kThreads) void qs_kernel(const T16* __restrict__ q,
     Sf[kb][ct][lane] = x;
   }
   __syncthreads();
+  constexpr int kStep = 16 * kQsThreads / kWave;     // token rows per block
   const T16* qb = q + bh * (size_t)L * D;
-  for (int blk = 0; blk < kRowsPerWg / 64; ++blk) {
-    const int rt = r0 + 64 * blk + 16 * wave;      // first token row of this wave's tile
-    if (rt >= L) break;
-    Frag<T16> qf[NKB];
+  auto load_q = [&](int rt, Frag<T16> (&qf)[NKB]) {
     const int rr = min(rt + n, L - 1);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
       qf[kb].v = *reinterpret_cast<const bf16x8*>(qb + (size_t)rr * D + 32 * kb + 8 * g);
+  };
+  Frag<T16> qf[NKB], qn[NKB];
+  int rt = r0 + 16 * wave;                       // this wave's first token row
+  if (rt < r1) load_q(rt, qf);
+  for (; rt < r1; rt += kStep) {
+    if (rt + kStep < r1) load_q(rt + kStep, qn);
+    const int tok = rt + n;                      // this lane's token
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[kb], Sf[kb][ct][lane], acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rt + 4 * g + e;
-        if (r >= L) continue;
-        const size_t o = (bh * (size_t)L + r) * D + 16 * ct + n;
-        if (out_bf16) static_cast<T16*>(out_)[o] = (T16)acc[e];
-        else static_cast<float*>(out_)[o] = acc[e];
+      for (int kb = 0; kb < NKB; ++kb) {
+        mma(Sf[kb][ct][lane].hi, qf[kb], acc);
+        mma(Sf[kb][ct][lane].lo, qf[kb], acc);
+      }
+      if (tok < r1) {
+        const size_t o = (bh * (size_t)L + tok) * D + 16 * ct + 4 * g;
+        if (out_bf16)
+          *reinterpret_cast<bf16x4*>(static_cast<T16*>(out_) + o) =
+              __builtin_convertvector(acc, bf16x4);
+        else
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + o) = acc;
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = qn[kb];
   }
 }
 
@@ -1636,24 +1752,18 @@ size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
   return align256(seg_states_end(a)) + 4 * pro_stride(a);
 }
 
-// Segments of the non-causal sum pass: state-only LINEAR chains, two
-// workgroups per compute unit, about 0.85 of a walk step each; the sum costs
-// a read of every partial state.
+// Token blocks per sequence of the non-causal K^T V: about four workgroups
+// per compute unit in all (each streams its block's K and V once), each
+// block whole chunks and non-empty; every block adds one partial state to
+// write and sum.
 int plan_sum_segments(const ChunkArgs& a) {
-  const long chains = (long)a.B * a.H * (a.d / 16);
+  const long seqs = (long)a.B * a.H;
   const int nc = (a.L + C - 1) / C;
-  const long slots = 2L * kComputeUnits;
-  double best = 1e300;
-  int best_p = 1;
-  for (int P = 1; P <= nc && P <= kMaxSegments; ++P) {
-    const double rounds = (double)((chains * P + slots - 1) / slots);
-    const double cost = 0.85 * rounds * ((nc + P - 1) / P) + 0.05 * P;
-    if (cost < best) {
-      best = cost;
-      best_p = P;
-    }
-  }
-  return best_p;
+  long P = (4L * kComputeUnits + seqs - 1) / seqs;
+  P = std::max(1L, std::min({P, (long)nc, (long)kMaxSegments}));
+  // the balanced block size, then the blocks it takes (none empty)
+  const int per = (int)((nc + P - 1) / P);
+  return (nc + per - 1) / per;
 }
 
 // X (P per sequence), an unused M block and S (slot 0 of S_in): the state
@@ -1741,25 +1851,33 @@ hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Non-causal form: the sum pass (LINEAR chain kernel, state only, over P
-// segments), the sum of their end states, then O = Q S.  a.mode is LINEAR;
-// the workspace holds X (P per sequence) and S.
+// Non-causal form: partial K^T V of a.P token blocks per sequence (chunk-
+// aligned, kv_kernel), S = S0 + their sum, then O = Q S.  a.mode is LINEAR;
+// the workspace holds the partials (P per sequence) and S.
 hipError_t launch_noncausal(const ChunkArgs& a, hipStream_t st) {
-  const StreamMap m = stream_map(a, kPassSum);
+  const StreamMap m = stream_map(a, kPassOut);    // the state arrays' layout
   const size_t n = (size_t)a.B * a.H * m.dd;
   float* S = m.sin;                       // slot 0 of S_in holds S
-  hipError_t e = a.d == 64 ? launch_one<64, kModeLinear, false, false, false>(a, kPassSum, st)
-                           : launch_one<128, kModeLinear, false, false, false>(a, kPassSum, st);
-  if (e != hipSuccess) return e;
-  seg_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(m.xs, S, a.S_final,
-                                                                         a.P, m.dd, n);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t wgs = (size_t)a.B * a.H * ((a.L + 255) / 256);
+  const int nc = (a.L + C - 1) / C;
+  const int TB = (nc + a.P - 1) / a.P * C;  // tokens per block; every block is non-empty
+  const dim3 kvgrid((unsigned)((size_t)a.B * a.H * a.P)), block(kThreads);
   if (a.d == 64)
-    qs_kernel<64><<<dim3((unsigned)wgs), dim3(kThreads), 0, st>>>(
+    kv_kernel<64><<<kvgrid, block, 0, st>>>(static_cast<const T16*>(a.k),
+                                            static_cast<const T16*>(a.v), m.xs, a.L, TB, a.P);
+  else
+    kv_kernel<128><<<kvgrid, block, 0, st>>>(static_cast<const T16*>(a.k),
+                                             static_cast<const T16*>(a.v), m.xs, a.L, TB, a.P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seg_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(m.xs, a.S0, S,
+                                                                         a.S_final, a.P, m.dd, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t wgs = (size_t)a.B * a.H * ((a.L + kQsRows - 1) / kQsRows);
+  if (a.d == 64)
+    qs_kernel<64><<<dim3((unsigned)wgs), dim3(kQsThreads), 0, st>>>(
         static_cast<const T16*>(a.q), S, a.out, a.L, a.out_bf16 ? 1 : 0);
   else
-    qs_kernel<128><<<dim3((unsigned)wgs), dim3(kThreads), 0, st>>>(
+    qs_kernel<128><<<dim3((unsigned)wgs), dim3(kQsThreads), 0, st>>>(
         static_cast<const T16*>(a.q), S, a.out, a.L, a.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }

@@ -152,10 +152,7 @@ __host__ __device__ inline SeqInfo seq_info(const SeqMap& m, int bh) {
 // The passes have P times the parallelism of the whole-sequence walk for
 // 1/P of its serial depth; they pay when (b, h, column tile) chains alone
 // leave compute units idle.
-enum : int { kPassWhole = 0, kPassState = 1, kPassOut = 2, kPassSum = 3 };
-// kPassSum (non-causal form, LINEAR mode): every segment p from a zero start
-// (S0 for p = 0) to X_p, all P of them; the sum of the X_p is then the
-// state after the whole sequence.
+enum : int { kPassWhole = 0, kPassState = 1, kPassOut = 2 };
 
 // Chunk c0 of segment p of a sequence of nc chunks (balanced split; every
 // segment is non-empty for P <= nc).
@@ -179,7 +176,7 @@ struct StreamMap {
   // streams per sequence
   __host__ __device__ int per_seq() const {
     if (pass == kPassWhole) return 1;
-    if (pass == kPassOut || pass == kPassSum) return P;
+    if (pass == kPassOut) return P;
     return (P - 1) + (erase ? P - 2 : 0);
   }
 };
@@ -248,7 +245,7 @@ int plan_segments(const ChunkArgs& a);
 // a.pro != 0; la_chunk_pipe.hip).
 ProArrays pro_arrays(const ChunkArgs& a);
 // Non-causal form O = Q (S0 + K^T V), bf16, a.mode LINEAR (la_chunk_pipe.hip):
-// the segments of its state sum pass, its workspace, its launches.
+// its token blocks per sequence (a.P), its workspace, its launches.
 int plan_sum_segments(const ChunkArgs& a);
 size_t noncausal_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_noncausal(const ChunkArgs& a, hipStream_t st);

@@ -1,10 +1,10 @@
 // Host-side check of the chain kernel's stream decode (stream_info in
 // la_kernels.hpp, compiled here for the CPU): for every pass of the
-// sequence-parallel forward and of the non-causal sum pass, over many
-// (sequences, length, segments) shapes, every stream's token rows, T-factor
-// slots and state pointers lie inside the tensors they index, segments start
-// on chunk boundaries, the state pass runs the streams the scan reads, and
-// the output and sum passes cover every token row exactly once.  Pointers are fake bases: only offsets are
+// sequence-parallel forward, over many (sequences, length, segments)
+// shapes, every stream's token rows, T-factor slots and state pointers lie
+// inside the tensors they index, segments start on chunk boundaries, the
+// state pass runs the streams the scan reads, and the output pass covers
+// every token row exactly once.  Pointers are fake bases: only offsets are
 // compared, nothing is dereferenced.  Prints "ok <n> streams" or the first
 // failure and exits non-zero.
 #include "la_kernels.hpp"
@@ -36,7 +36,7 @@ int main() {
         const float* S0 = reinterpret_cast<const float*>(size_t(1) << 40);
         float* Sf = reinterpret_cast<float*>(size_t(1) << 41);
         for (int erase = 0; erase < 2; ++erase)
-          for (int pass : {kPassState, kPassOut, kPassSum}) {
+          for (int pass : {kPassState, kPassOut}) {
             const SeqMap sm{nullptr, BH, 1, L, C};
             const StreamMap m{sm, S0, Sf, pass, P, erase != 0, dd, xs,
                               xs + (size_t)BH * P * dd, xs + 2 * (size_t)BH * P * dd};
@@ -61,14 +61,7 @@ int main() {
                 return (off >= 0 && off % (long)dd == 0 && off / (long)dd < P) ? off / (long)dd
                                                                                  : -1;
               };
-              if (pass == kPassSum) {
-                const long p = index(si.sf, m.xs);
-                if (si.eye || p < 0) return fail("sum X_p", BH, L, P, pass, s);
-                if ((p == 0) != (si.s0 != nullptr) || (si.s0 && si.s0 != S0 + (size_t)bh * dd))
-                  return fail("sum start state", BH, L, P, pass, s);
-                x_seen[(size_t)bh * P + p]++;
-                for (int t = 0; t < si.len; ++t) cover[si.row0 + t]++;
-              } else if (pass == kPassOut) {
+              if (pass == kPassOut) {
                 if (si.eye || index(si.s0, m.sin) < 0) return fail("S_in", BH, L, P, pass, s);
                 const bool last = si.row0 + si.len == lo + L;
                 if (last != (si.sf != nullptr) || (si.sf && si.sf != Sf + (size_t)bh * dd))
@@ -87,12 +80,9 @@ int main() {
               }
               ++checked;
             }
-            if (pass == kPassOut || pass == kPassSum) {
+            if (pass == kPassOut) {
               for (int c : cover)
                 if (c != 1) return fail("token coverage", BH, L, P, pass, -1);
-              if (pass == kPassSum)
-                for (int c : x_seen)
-                  if (c != 1) return fail("sum X_p coverage", BH, L, P, pass, -1);
             } else {
               for (int bh = 0; bh < BH; ++bh)
                 for (int p = 0; p < P; ++p) {

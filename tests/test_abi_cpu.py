@@ -400,18 +400,22 @@ def test_noncausal_rejects(kw, code):
 
 
 def test_noncausal_workspace_size():
-    """Three state blocks per segment of the sum pass (the partial states, an
-    unused block and S), the segment count a function of the sizes only:
-    many heads walk whole, few long sequences are cut."""
+    """Three state blocks per token block of K^T V (the partial states, an
+    unused block and S); the block count, a function of the sizes only,
+    gives about four workgroups per compute unit, at most one per chunk and
+    64 per sequence."""
     lib = _lib.get()
-    def ws(B, H, L, d):
+    def blocks(B, H, L, d):
         n = ctypes.c_size_t(0)
         assert lib.la_noncausal_workspace_bytes(B, H, L, d, d, 1, ctypes.byref(n)) == OK
-        return n.value
-    assert ws(8, 16, 4096, 128) == 3 * 8 * 16 * 128 * 128 * 4          # 1024 chains: P = 1
-    n = ws(1, 1, 65536, 128)
-    P = n // (3 * 128 * 128 * 4)
-    assert n == 3 * P * 128 * 128 * 4 and 8 <= P <= 64
+        unit = 3 * B * H * d * d * 4
+        assert n.value % unit == 0
+        return n.value // unit
+    assert blocks(8, 16, 4096, 128) == 8
+    assert blocks(1, 1, 65536, 128) == 64
+    assert blocks(1, 2, 64, 64) == 1
+    assert blocks(1, 1, 64 * 5 + 13, 128) == 6
+    assert blocks(300, 16, 4096, 128) == 1
     assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 0, ctypes.byref(ctypes.c_size_t())) == UNSUP
     assert lib.la_noncausal_workspace_bytes(1, 1, 64, 64, 64, 1, None) == NULL
 
