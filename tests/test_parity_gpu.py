@@ -431,6 +431,54 @@ def test_chunk_fused_shard_sampled():
     assert_close("S_final", f64(sel(S)), S_ref, "bf16")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_fused_extreme_inputs(mode):
+    """Raw gate scores of +-40 (softplus and sigmoid must not overflow: alpha
+    -> 0, beta -> 0 or 1), an all-zero q row and an all-zero k row (the eps
+    inside the norm keeps them zero), and a zero-valued token (its output
+    row may be all zero: the output norm's eps keeps it finite) -- forward
+    and decode against the oracle, every value finite."""
+    w = recipe(mode, "bf16", B=1, H=2, L=64 * 2 + 9, d=128, s0_std=0.3, seed=107)
+    log(f"fused extreme inputs {w}")
+    r = _raw(w, 3)
+    r["a_raw"][0, 0, 5:9] = torch.tensor([40.0, -40.0, 40.0, -40.0])
+    r["b_raw"][0, 0, 5:9] = torch.tensor([-40.0, 40.0, 40.0, -40.0])
+    r["q"][0, 1, 3] = 0
+    r["k"][0, 1, 7] = 0
+    r["v"][0, 1, 0] = 0
+    r["q"][0, 1, 0] = 0
+    D, nw = _epi_params(w, 108)
+    o_ref, S_ref = _fused_oracle(r, mode, 3)
+    o_ref = _epi_oracle(o_ref, r["v"].double().numpy(), D, nw, True, True, 1e-6)
+    dev = to_cuda(r)
+    out, S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["a_raw"], dev["b_raw"], dev["S0"],
+                          mode=mode, qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE,
+                          dskip=D.cuda(), out_norm=True, norm_weight=nw.cuda())
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(S).all()
+    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    assert_close("S_final", f64(S), S_ref, "bf16")
+    # the same tokens one by one through the fused decode step
+    y = {key: t.to(torch.float64).numpy() for key, t in r.items()}
+    q, k, lg, be = oracle.prepare(y["q"], y["k"], y["a_raw"], y["b_raw"], mode, 3, GATE_SCALE)
+    steps = 12
+    mv = lambda t: np.moveaxis(t, 2, 0)[:steps]      # noqa: E731
+    o_d, S_d = oracle.decode_steps(y["S0"], mv(q), mv(k), mv(y["v"]), mv(lg), mv(be), mode)
+    o_d = np.moveaxis(_epi_oracle(np.moveaxis(o_d, 0, 2), y["v"][:, :, :steps], D, nw, True,
+                                  True, 1e-6), 2, 0)
+    Sg = dev["S0"].clone()
+    col = lambda t, n: t[:, :, n].contiguous()       # noqa: E731
+    outs = [la.decode_step(col(dev["q"], n), col(dev["k"], n), col(dev["v"], n),
+                           col(dev["a_raw"], n), col(dev["b_raw"], n), Sg, mode=mode,
+                           qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE, dskip=D.cuda(),
+                           out_norm=True, norm_weight=nw.cuda()) for n in range(steps)]
+    torch.cuda.synchronize()
+    od = np.stack([f64(o) for o in outs])
+    assert np.all(np.isfinite(od)) and torch.isfinite(Sg).all()
+    assert_close("decode o", od, o_d, "bf16", bf16_out=True)
+    assert_close("decode S", f64(Sg), S_d, "bf16")
+
+
 @pytest.mark.parametrize("flags", ["gates", "norm", "both"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", MODES)
