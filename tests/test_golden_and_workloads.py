@@ -25,6 +25,29 @@ def test_oracle_matches_frozen_golden():
         assert np.max(np.abs(S - np.array(ref["S_final"]))) < 1e-14
 
 
+def test_oracle_extras_match_frozen_golden():
+    """The same fixture's "extra" block: the backward, the fused prologue and
+    epilogue, and the non-causal form on the frozen input."""
+    import oracle
+    with open(os.path.join(HERE, "golden", "oracle_small.json")) as f:
+        g = json.load(f)
+    x = {n: np.array(a) for n, a in g["inputs"].items()}
+    e = {n: np.array(a) for n, a in g["extra"]["inputs"].items()}
+    close = lambda a, b: np.max(np.abs(np.asarray(a) - np.asarray(b))) < 1e-12   # noqa: E731
+    for mode, ref in g["extra"]["modes"].items():
+        gr = oracle.recurrent_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"],
+                                  mode, e["dO"], e["dS"])
+        for n, a in ref["grads"].items():
+            assert (a is None) == (gr[n] is None), (mode, n)
+            assert a is None or close(gr[n], a), (mode, n)
+        q, k, la, be = oracle.prepare(x["q"], x["k"], e["a"], e["b"], mode, 3, 1.0 / 16.0)
+        o, _ = recurrent_fwd(q, k, x["v"], la, be, x["S0"], mode)
+        o = oracle.out_norm(oracle.add_dskip(o, x["v"], e["D"]), e["w"], 1e-6)
+        assert close(o, ref["fused_o"]), mode
+    o, S = oracle.noncausal_fwd(x["q"], x["k"], x["v"], x["S0"])
+    assert close(o, g["extra"]["noncausal"]["o"]) and close(S, g["extra"]["noncausal"]["S"])
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3])
 def test_workload_recipe_small_sizes(wid):
     w = workloads.WORKLOADS[wid].scaled(B=1, H=2, L=64)
