@@ -14,11 +14,13 @@
 //
 // The step is pure streaming: 0.75 flop per byte of state, so it is bound by
 // HBM bandwidth.  One 256-thread workgroup owns one (b, h) state (64 KiB at
-// dk = dv = 128): every thread loads its rows x 4 columns with 16-byte
-// non-temporal loads (a wave covers whole contiguous rows), keeps them in
-// registers, reduces the two column dot products through LDS, and writes the
-// updated values back from the same registers with 16-byte non-temporal
-// stores.  S is read exactly once and written exactly once.
+// dk = dv = 128): every thread loads its rows x 4 columns with 16-byte loads
+// (a wave covers whole contiguous rows), keeps them in registers, reduces the
+// two column dot products through LDS, and writes the updated values back
+// from the same registers with 16-byte non-temporal stores.  S is read
+// exactly once and written exactly once.  Plain loads stream faster here than
+// non-temporal ones (measured 0.162 ms against 0.193 ms per step on 1 GiB of
+// state); the stores stay non-temporal, plain stores measured slower still.
 //
 // Fused prologue (pro flags): kProGates -- beta = sigmoid(b), log alpha =
 // -gate_scale softplus(a) from the raw scores passed as beta and log_alpha;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   f32x4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
-    s[m] = __builtin_nontemporal_load(Sp + (rg + RG * m) * NQ + cq);
+    s[m] = Sp[(rg + RG * m) * NQ + cq];
 
   for (int i = t; i < DK; i += 256) {
     sk[i] = to_f32(k[bh * DK + i]);
