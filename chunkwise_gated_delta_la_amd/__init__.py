@@ -15,4 +15,5 @@ memory) and passes torch's current HIP stream.
 from ._lib import LAError, LIB_PATH  # noqa: F401
 from .api import (MODES, chunk_fwd, chunk_fwd_varlen, chunk_segments,  # noqa: F401
                   chunk_varlen_workspace_bytes, chunk_workspace_bytes, decode_step,
-                  kernel_timer, noncausal_fwd, version)
+                  kernel_timer, noncausal_fwd, version, chunk_bwd,
+                  chunk_bwd_workspace_bytes)

@@ -70,6 +70,11 @@ def _declare(lib):
     lib.la_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, vp,
                                    i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i
+    lib.la_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                 i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_chunk_bwd.restype = i
+    lib.la_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_bwd_workspace_bytes.restype = i
     lib.la_last_error.argtypes = []
     lib.la_last_error.restype = ctypes.c_char_p
     lib.la_version.argtypes = []

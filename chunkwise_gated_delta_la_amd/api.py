@@ -357,3 +357,65 @@ class kernel_timer:
         if exc[0] is None:
             _lib.check(rc)
         return False
+
+
+def chunk_bwd_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
+                              dtype=torch.bfloat16):
+    """Workspace bytes ``la_chunk_bwd`` needs for these sizes
+    (``la_chunk_bwd_workspace_bytes``)."""
+    code = _dtype_code(dtype, dtype)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.get().la_chunk_bwd_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
+                                                       ctypes.byref(n)))
+    return n.value
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, S0, dout, dS_final=None, *, mode="gated_delta",
+              C=64, workspace=None, want_dS0=True):
+    """Gradients of ``chunk_fwd`` (``la_chunk_bwd``) for upstream gradients
+    ``dout [B, H, L, dv]`` (the inputs' dtype) and ``dS_final [B, H, dk, dv]``
+    float32 (or None: zero).
+
+    Returns a dict of float32 tensors ``dq, dk, dv [B, H, L, d]``,
+    ``dlog_alpha, dbeta [B, H, L]`` (None where the mode does not read the
+    gate) and ``dS0 [B, H, dk, dv]`` (None unless ``want_dS0``).
+    ``workspace`` is an optional uint8 device tensor of at least
+    ``chunk_bwd_workspace_bytes(...)`` bytes.
+    """
+    m = _mode(mode)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    _need(k, "k", (B, H, L, dk), dt, dev)
+    _need(v, "v", (B, H, L, dv), dt, dev)
+    _need(dout, "dout", (B, H, L, dv), dt, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (B, H, L), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (B, H, L), torch.float32, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    _need(dS_final, "dS_final", (B, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty((B, H, L, dk), **f32), "dk": torch.empty((B, H, L, dk), **f32),
+           "dv": torch.empty((B, H, L, dv), **f32),
+           "dlog_alpha": torch.empty((B, H, L), **f32) if m in _DECAY else None,
+           "dbeta": torch.empty((B, H, L), **f32) if m in _ERASE else None,
+           "dS0": torch.empty((B, H, dk, dv), **f32) if want_dS0 else None}
+    need = chunk_bwd_workspace_bytes(B, H, L, dk, dv, mode=mode, C=C, dtype=dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        rc = lib.la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v),
+                              _ptr(log_alpha if m in _DECAY else None),
+                              _ptr(beta if m in _ERASE else None), _ptr(S0), _ptr(dout),
+                              _ptr(dS_final), _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]),
+                              _ptr(res["dlog_alpha"]), _ptr(res["dbeta"]), _ptr(res["dS0"]),
+                              B, H, L, dk, dv, C, m, _DTYPES[dt], _ptr(workspace),
+                              workspace.numel(), _stream(dev))
+    _lib.check(rc)
+    return res

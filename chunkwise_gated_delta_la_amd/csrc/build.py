@@ -17,7 +17,7 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OBJ_DIR = os.path.join(ROOT, "_build", "lachunk")
 LIB = os.path.join(PKG, "liblachunk.so")
-SOURCES = ["la_api.hip", "la_decode.hip", "la_chunk.hip", "la_chunk_pipe.hip"]
+SOURCES = ["la_api.hip", "la_decode.hip", "la_chunk.hip", "la_chunk_pipe.hip", "la_bwd.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

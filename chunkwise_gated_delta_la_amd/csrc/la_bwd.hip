@@ -1,0 +1,942 @@
+// Backward of the chunkwise forward: the gradients of every input for a
+// scalar loss with upstream gradients dO (of the outputs) and dS_final (of
+// the final state).
+//
+// The pages print no gradient formulas; they say that training runs the
+// chunked form and keeps the state of every chunk for it ("FWP分块并行机制"
+// in the hybrid-attention notes "混合注意力学习(1): 线性注意力"; train with
+// the parallel form, infer with the recurrent one: "朴素线性注意力" in
+// "【CS336】lecture4 线性注意力|Mamba|GDN|DSA").  The formulas below are the
+// derivative of the forward's chunk step (the WY/UT form of
+// "HouseHolder变换和WY表示" with the scalar decay of "Gated DeltaNet", same
+// notes).  Per chunk, with S the state entering it, g the in-chunk cumsum of
+// log alpha, gam = exp(g), f = exp(g_C - g), Gamma_ri = exp(g_r - g_i) for
+// i <= r, P = (Q K^T) * M * Gamma, A = strict_lower(diag(beta) K K^T *
+// Gamma), T = (I + A)^-1, R = diag(beta)(V - diag(gam) K S), U = T R (U = V
+// without erase), O = diag(gam) Q S + P U, S' = gam_C S + K^T diag(f) U, and
+// dS' the gradient of S':
+//
+//   dU  = P^T dO + diag(f) K dS'
+//   dR  = T^T dU                          (erase modes; dV = diag(beta) dR,
+//                                          else dV = dU)
+//   dS  = gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR
+//
+// is the only serial part (a reverse walk over chunks); everything else
+// follows per chunk from S, dS', dO and the chunk's own inputs:
+//
+//   E   = (dO U^T) * M * Gamma,  dA = strict_lower(-dR U^T),
+//   H   = dA * beta_r Gamma,     G  = H + H^T
+//   dQ  = diag(gam) dO S^T + E K
+//   dK  = diag(f) U dS'^T - diag(beta gam) dR S^T + E^T Q + G K
+//   dbeta_r = V_r . dR_r - gam_r K_r . (dR S^T)_r + sum_i dA_ri (K K^T *
+//             Gamma)_ri
+//   dg  = rowsum(GG) - colsum(GG) + gam * (Q . dO S^T - beta K . dR S^T)
+//         - f * (K . U dS'^T), GG = (dO U^T) * P + dA * A, plus at the last
+//         row gam_C <dS', S> + sum_r f_r (K . U dS'^T)_r
+//   dlog_alpha_i = sum over rows r >= i of the chunk of dg_r.
+//
+// Kernels (one call runs all four on one stream):
+//   bwd_prep     per (b, h, chunk): g, T by forward substitution, P^T
+//   bwd_states   per (b, h, 16 state columns): the forward walk, storing
+//                the state entering each chunk and U
+//   bwd_rev      per (b, h, 16 state columns): the reverse walk, storing dS'
+//                of each chunk and dR, writing dv and dS0
+//   bwd_grads    per (b, h, chunk): dq, dk, dbeta, dlog_alpha
+// The walks keep their 16-column state (or state-gradient) tile in the MFMA
+// accumulators of wave 0; waves 1-3 stage the next chunk's operands into the
+// other half of a double buffer (and, in the reverse walk, form its
+// P^T dO and Q^T diag(gam) dO), so each chunk step has one barrier.
+//
+// A ragged last chunk is padded with rows that change nothing: q, k, v, dO
+// and beta read as zero and log alpha as zero, so the padded rows of T are
+// identity rows, their U, dU and dR are zero, and the last row's g is the
+// chunk's total decay.  Their gradients are not stored.
+//
+// Precision: float inputs run float MFMAs throughout; bf16 inputs are exact
+// bf16 MFMA operands, and every float operand (states, U, dR, scores, T) is
+// split into bf16 hi + lo parts (about 16 bits).  Gradients are float32.
+#include "la_device.hpp"
+#include "la_kernels.hpp"
+
+#include <type_traits>
+
+namespace la {
+namespace {
+
+constexpr int C = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int LDC = C + 4;     // row pitch of float C x C tiles in LDS
+constexpr int LDX = 20;        // row pitch of float 16-column tiles in LDS
+
+struct BwdWs {
+  float* g;     // [BH, NC * C]     in-chunk cumsum of log alpha (padded rows: the total)
+  float* T;     // [BH, NC, C, C]   (I + A)^-1, row-major (erase modes)
+  float* Pt;    // [BH, NC, C, C]   P^T
+  float* Sent;  // [BH, NC, D, D]   state entering each chunk
+  float* U;     // [BH, NC * C, D]  T R (erase modes)
+  float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
+  float* dR;    // [BH, NC * C, D]  T^T dU (erase modes)
+  int NC;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Bytes of the workspace; with ws != NULL also its arrays in a.workspace.
+size_t carve(const BwdArgs& a, BwdWs* ws) {
+  const size_t BH = (size_t)a.B * a.H, NC = ((size_t)a.L + C - 1) / C, D = a.d;
+  const bool erase = mode_erase(a.mode);
+  const size_t n[7] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * C * C,
+                       BH * NC * D * D, erase ? BH * NC * C * D : 0, BH * NC * D * D,
+                       erase ? BH * NC * C * D : 0};
+  float* p[7];
+  size_t off = 0;
+  char* base = static_cast<char*>(a.workspace);
+  for (int i = 0; i < 7; ++i) {
+    p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
+    off += align256(n[i] * sizeof(float));
+  }
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], (int)NC};
+  return off;
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_zero() {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.set(j, 0.f);
+  return f;
+}
+
+// Operand row `r` of a chunk's token rows (row pitch D) in global memory;
+// rows at or past nrows read as zero.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> chunk_row(const T* base, int r, int nrows, int c0, int g) {
+  const Frag<T> f = frag_row(base + (size_t)min(r, nrows - 1) * D + c0, g);
+  return r < nrows ? f : frag_zero<T>();
+}
+
+// Operand column `col` of a chunk's token rows over the 32-deep block at
+// row k0: 8 values base[(k0 + kidx(g, j)) * D + col], zero past nrows.
+template <typename T, int D>
+__device__ __forceinline__ Frag<T> chunk_col(const T* base, int k0, int col, int nrows, int g) {
+  Frag<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = k0 + kidx(g, j);
+    const float x = to_f32(base[(size_t)min(r, nrows - 1) * D + col]);
+    f.set(j, r < nrows ? x : 0.f);
+  }
+  return f;
+}
+
+// Split operand gathered from a float column: p[kidx(g, j) * ld].
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_col(const float* p, int ld, int g) {
+  Frag2<T> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.set(j, p[kidx(g, j) * ld]);
+  return f;
+}
+
+// acc += a * b with a split and b exact
+template <typename T>
+__device__ __forceinline__ void mma_a2b(const Frag2<T>& a, const Frag<T>& b, f32x4& acc) {
+  if constexpr (IsBf16<T>::value) mma(a.lo, b, acc);
+  mma(a.hi, b, acc);
+}
+
+// Sum over the 16 lanes of a lane group (lanes with the same l / 16).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 1);
+  return x;
+}
+
+__device__ __forceinline__ float sum64(float x) {
+  x += __shfl_xor(x, 32);
+  x += __shfl_xor(x, 16);
+  return sum16(x);
+}
+
+// Block -> (head, 16-column tile), the tiles of one head on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin) when the head count
+// allows it, so they share the head's rows through that XCD's L2.
+__device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, int& ct) {
+  if (BH % 8 == 0) {
+    const int x = b % 8, s = b / 8;
+    ct = s % NCT;
+    bh = (s / NCT) * 8 + x;
+  } else {
+    bh = b / NCT;
+    ct = b % NCT;
+  }
+}
+
+// ---------------------------------------------------------------- prep
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ log_alpha,
+    const float* __restrict__ beta, BwdWs ws, int L) {
+  constexpr bool kErase = mode_erase(MODE);
+  constexpr bool kGated = mode_decay(MODE);
+  constexpr int NKB = D / 32;
+  const int NC = ws.NC;
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
+  const int nrows = min(C, L - c * C);
+  const size_t row0 = (size_t)bh * L + (size_t)c * C;
+  const size_t cid = (size_t)bh * NC + c;
+  const T* qc = q + row0 * D;
+  const T* kc = k + row0 * D;
+
+  __shared__ __attribute__((aligned(16))) float gs[C];
+  __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float As[kErase ? C * LDC : 4];
+
+  if (wave == 0) {
+    float la = 0.f, b = 0.f;
+    if (lane < nrows) {
+      if constexpr (kGated) la = log_alpha[row0 + lane];
+      if constexpr (kErase) b = beta[row0 + lane];
+    }
+    const float gg = kGated ? wave_inclusive_scan(la) : 0.f;
+    gs[lane] = gg;
+    bs[lane] = b;
+    ws.g[cid * C + lane] = gg;
+  }
+  __syncthreads();
+
+  for (int t = wave; t < 16; t += kWaves) {
+    const int ti = t / 4, tj = t % 4;
+    // P^T tile: rows i = 16 ti + 4 g + e (keys), columns r = 16 tj + n
+    // (queries), nonzero for r >= i
+    f32x4 acc = zero4();
+    if (tj >= ti) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        mma(chunk_row<T, D>(kc, 16 * ti + n, nrows, 32 * kb, g),
+            chunk_row<T, D>(qc, 16 * tj + n, nrows, 32 * kb, g), acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * ti + 4 * g + e, r = 16 * tj + n;
+      float x = 0.f;
+      if (r >= i) x = acc[e] * (kGated ? __expf(gs[r] - gs[i]) : 1.f);
+      ws.Pt[(cid * C + i) * C + r] = x;
+    }
+    if constexpr (kErase) {
+      // A tile: rows r = 16 ti + 4 g + e, columns i = 16 tj + n, i < r
+      f32x4 a2 = zero4();
+      if (ti >= tj) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          mma(chunk_row<T, D>(kc, 16 * ti + n, nrows, 32 * kb, g),
+              chunk_row<T, D>(kc, 16 * tj + n, nrows, 32 * kb, g), a2);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * ti + 4 * g + e, i = 16 * tj + n;
+        float x = 0.f;
+        if (r > i) x = bs[r] * a2[e] * (kGated ? __expf(gs[r] - gs[i]) : 1.f);
+        As[r * LDC + i] = x;
+      }
+    }
+  }
+  if constexpr (kErase) {
+    __syncthreads();
+    if (wave == 0) {
+      // T = (I + A)^-1: lane j solves column j,
+      //   x_r = [r == j] - sum_{i < r} A_ri x_i
+      float x[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) {
+        float s0 = r == lane ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i4 = 0; 4 * i4 < r; ++i4) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(As + r * LDC + 4 * i4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            if (i < r) {
+              if (i % 2 == 0) s0 = fmaf(-av[e], x[i], s0);
+              else s1 = fmaf(-av[e], x[i], s1);
+            }
+          }
+        }
+        x[r] = s0 + s1;
+      }
+#pragma unroll
+      for (int r = 0; r < C; ++r) ws.T[(cid * C + r) * C + lane] = x[r];
+    }
+  }
+}
+
+// ------------------------------------------------------- forward walk
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_states_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ S0, BwdWs ws, int BH, int L) {
+  constexpr bool kErase = mode_erase(MODE);
+  constexpr bool kGated = mode_decay(MODE);
+  constexpr int PE = 16 / sizeof(T);
+  constexpr int LDK = D + PE;
+  constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
+  constexpr int VPR = D / PE;   // 16-byte vectors per token row
+
+  __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
+  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
+  __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
+  __shared__ __attribute__((aligned(16))) float gsb[2][C];
+  __shared__ __attribute__((aligned(16))) float bsb[2][C];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
+  int bh, ct;
+  tile_of_block(blockIdx.x, BH, NCT, bh, ct);
+  const int col0 = 16 * ct;
+  const int NC = ws.NC;
+  const size_t NCC = (size_t)NC * C;
+
+  // chunk c's operands into buffer b by threads t, t + nt, ...
+  auto stage = [&](int c, int b, int t, int nt) {
+    const int nrows = min(C, L - c * C);
+    const size_t row0 = (size_t)bh * L + (size_t)c * C;
+    for (int p = t; p < C * VPR; p += nt) {
+      const int r = p / VPR, cv = p % VPR;
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (r < nrows) x = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + cv * PE);
+      *reinterpret_cast<u32x4*>(&Kb[b][r * LDK + cv * PE]) = x;
+    }
+    if constexpr (kErase) {
+      const float* Tg = ws.T + ((size_t)bh * NC + c) * C * C;
+      for (int p = t; p < C * C / 4; p += nt) {
+        const int r = p / (C / 4), cv = p % (C / 4);
+        *reinterpret_cast<f32x4*>(&Tb[b][r * LDC + 4 * cv]) =
+            *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
+      }
+    }
+    for (int p = t; p < C * 16; p += nt) {
+      const int r = p / 16, cc = p % 16;
+      Vb[b][r * LDX + cc] = r < nrows ? to_f32(v[(row0 + r) * D + col0 + cc]) : 0.f;
+    }
+    for (int p = t; p < C; p += nt) {
+      gsb[b][p] = ws.g[((size_t)bh * NC + c) * C + p];
+      bsb[b][p] = (kErase && p < nrows) ? beta[row0 + p] : 0.f;
+    }
+  };
+
+  f32x4 S[NKT];
+  if (wave == 0) {
+    const size_t sb = (size_t)bh * D * D;
+#pragma unroll
+    for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[tj][e] = S0 ? S0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
+  }
+  stage(0, 0, tid, kThreads);
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    const int b = c & 1;
+    if (wave == 0) {
+      float* Se = ws.Sent + ((size_t)bh * NC + c) * D * D;
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Se[(size_t)(16 * tj + 4 * g + e) * D + col0 + n] = S[tj][e];
+      const float* gsc = gsb[b];
+      const float gC = gsc[C - 1];
+      const float gamC = kGated ? __expf(gC) : 1.f;
+      // decay factors f of the rows 32 kb + 4 g + e (lo) and 32 kb + 16 + 4 g + e (hi)
+      float flo[2][4], fhi[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          flo[kb][e] = kGated ? __expf(gC - gsc[32 * kb + 4 * g + e]) : 1.f;
+          fhi[kb][e] = kGated ? __expf(gC - gsc[32 * kb + 16 + 4 * g + e]) : 1.f;
+        }
+      Frag2<T> bX[2];
+      if constexpr (kErase) {
+        Frag2<T> bS[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) bS[kb] = frag2_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
+        f32x4 R[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          f32x4 ks = zero4();
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            mma_ab2(frag_row(&Kb[b][(16 * ti + n) * LDK + 32 * kb], g), bS[kb], ks);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti + 4 * g + e;
+            const float gam = kGated ? __expf(gsc[r]) : 1.f;
+            R[ti][e] = bsb[b][r] * (Vb[b][r * LDX + n] - gam * ks[e]);
+          }
+        }
+        const Frag2<T> bR[2] = {frag2_from_acc<T>(R[0], R[1]), frag2_from_acc<T>(R[2], R[3])};
+        f32x4 U[4];
+        float* Ug = ws.U + ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          U[ti] = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            mma_a2b2(frag2_row<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g), bR[kb], U[ti]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Ug[(size_t)(16 * ti + 4 * g + e) * D] = U[ti][e];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          bX[kb] = frag2_from_acc_scaled<T>(U[2 * kb], U[2 * kb + 1], flo[kb], fhi[kb]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x4 vlo, vhi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vlo[e] = Vb[b][(32 * kb + 4 * g + e) * LDX + n];
+            vhi[e] = Vb[b][(32 * kb + 16 + 4 * g + e) * LDX + n];
+          }
+          bX[kb] = frag2_from_acc_scaled<T>(vlo, vhi, flo[kb], fhi[kb]);
+        }
+      }
+      // S <- gam_C S + K^T diag(f) U
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[tj][e] *= gamC;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bX[kb], S[tj]);
+      }
+    } else if (c + 1 < NC) {
+      stage(c + 1, b ^ 1, tid - kWave, kThreads - kWave);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- reverse walk
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ beta,
+    const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dv_out,
+    float* __restrict__ dS0, BwdWs ws, int BH, int L) {
+  constexpr bool kErase = mode_erase(MODE);
+  constexpr bool kGated = mode_decay(MODE);
+  constexpr int PE = 16 / sizeof(T);
+  constexpr int LDK = D + PE;
+  constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
+  constexpr int VPR = D / PE;
+
+  __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
+  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
+  __shared__ __attribute__((aligned(16))) float X1[2][C * LDX];   // P^T dO (16 columns)
+  __shared__ __attribute__((aligned(16))) float X2[2][D * LDX];   // Q^T diag(gam) dO
+  __shared__ __attribute__((aligned(16))) float gsb[2][C];
+  __shared__ __attribute__((aligned(16))) float bsb[2][C];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
+  int bh, ct;
+  tile_of_block(blockIdx.x, BH, NCT, bh, ct);
+  const int col0 = 16 * ct;
+  const int NC = ws.NC;
+  const size_t NCC = (size_t)NC * C;
+
+  // chunk c's operands and its two dS-independent products into buffer b,
+  // by waves w0, w0 + 1, ..., w0 + nw - 1
+  auto side = [&](int c, int b, int w0, int nw) {
+    const int nrows = min(C, L - c * C);
+    const size_t row0 = (size_t)bh * L + (size_t)c * C;
+    const size_t cid = (size_t)bh * NC + c;
+    const int t = tid - w0 * kWave, nt = nw * kWave;
+    for (int p = t; p < C * VPR; p += nt) {
+      const int r = p / VPR, cv = p % VPR;
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (r < nrows) x = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + cv * PE);
+      *reinterpret_cast<u32x4*>(&Kb[b][r * LDK + cv * PE]) = x;
+    }
+    if constexpr (kErase) {
+      const float* Tg = ws.T + cid * C * C;
+      for (int p = t; p < C * C / 4; p += nt) {
+        const int r = p / (C / 4), cv = p % (C / 4);
+        *reinterpret_cast<f32x4*>(&Tb[b][r * LDC + 4 * cv]) =
+            *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
+      }
+    }
+    for (int p = t; p < C; p += nt) {
+      gsb[b][p] = ws.g[cid * C + p];
+      bsb[b][p] = (kErase && p < nrows) ? beta[row0 + p] : 0.f;
+    }
+    // dO columns col0 .. col0 + 15 as B operands: raw, and scaled by gam
+    const T* dOc = dout + row0 * D;
+    Frag<T> dof[2];
+    Frag2<T> dog[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dof[kb] = chunk_col<T, D>(dOc, 32 * kb, col0 + n, nrows, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 32 * kb + kidx(g, j);
+        const float gam = kGated ? __expf(ws.g[cid * C + r]) : 1.f;
+        dog[kb].set(j, to_f32(dof[kb].v[j]) * gam);
+      }
+    }
+    const int wv = wave - w0;
+    for (int tt = wv; tt < 4 + NKT; tt += nw) {
+      f32x4 acc = zero4();
+      if (tt < 4) {
+        // X1 rows i = 16 tt + 4 g + e: sum_r P^T_ir dO_r
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma_a2b(frag2_row<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g), dof[kb], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X1[b][(16 * tt + 4 * g + e) * LDX + n] = acc[e];
+      } else {
+        // X2 rows 16 tj + 4 g + e (key dimension): sum_r Q_r gam_r dO_r
+        const int tj = tt - 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          mma_ab2(chunk_col<T, D>(q + row0 * D, 32 * kb, 16 * tj + n, nrows, g), dog[kb], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X2[b][(16 * tj + 4 * g + e) * LDX + n] = acc[e];
+      }
+    }
+  };
+
+  f32x4 dS[NKT];
+  if (wave == 0) {
+    const size_t sb = (size_t)bh * D * D;
+#pragma unroll
+    for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dS[tj][e] = dS_final ? dS_final[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
+  }
+  side(NC - 1, 0, 0, kWaves);
+  __syncthreads();
+
+  for (int s = 0; s < NC; ++s) {
+    const int c = NC - 1 - s, b = s & 1;
+    if (wave == 0) {
+      float* dSe = ws.dSx + ((size_t)bh * NC + c) * D * D;
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dSe[(size_t)(16 * tj + 4 * g + e) * D + col0 + n] = dS[tj][e];
+      const float* gsc = gsb[b];
+      const float gC = gsc[C - 1];
+      const float gamC = kGated ? __expf(gC) : 1.f;
+      const int nrows = min(C, L - c * C);
+      const size_t row0 = (size_t)bh * L + (size_t)c * C;
+      Frag2<T> bS[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) bS[kb] = frag2_from_acc<T>(dS[2 * kb], dS[2 * kb + 1]);
+      // dU = P^T dO + diag(f) K dS'
+      f32x4 dU[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          mma_ab2(frag_row(&Kb[b][(16 * ti + n) * LDK + 32 * kb], g), bS[kb], y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * ti + 4 * g + e;
+          const float f = kGated ? __expf(gC - gsc[r]) : 1.f;
+          dU[ti][e] = X1[b][r * LDX + n] + f * y[e];
+        }
+      }
+      float* dvo = dv_out + row0 * D + col0 + n;
+      if constexpr (kErase) {
+        const Frag2<T> bU[2] = {frag2_from_acc<T>(dU[0], dU[1]), frag2_from_acc<T>(dU[2], dU[3])};
+        f32x4 dR[4];
+        float* dRg = ws.dR + ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          dR[ti] = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            mma_a2b2(frag2_col<T>(&Tb[b][32 * kb * LDC + 16 * ti + n], LDC, g), bU[kb], dR[ti]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti + 4 * g + e;
+            dRg[(size_t)r * D] = dR[ti][e];
+            if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
+          }
+        }
+        // dS <- gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR
+        Frag2<T> bR[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float slo[4], shi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rl = 32 * kb + 4 * g + e, rh = rl + 16;
+            slo[e] = -bsb[b][rl] * (kGated ? __expf(gsc[rl]) : 1.f);
+            shi[e] = -bsb[b][rh] * (kGated ? __expf(gsc[rh]) : 1.f);
+          }
+          bR[kb] = frag2_from_acc_scaled<T>(dR[2 * kb], dR[2 * kb + 1], slo, shi);
+        }
+#pragma unroll
+        for (int tj = 0; tj < NKT; ++tj) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bR[kb], dS[tj]);
+        }
+      } else {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti + 4 * g + e;
+            if (r < nrows) dvo[(size_t)r * D] = dU[ti][e];
+          }
+#pragma unroll
+        for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
+      }
+    } else if (c > 0) {
+      side(c - 1, b ^ 1, 1, kWaves - 1);
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && dS0) {
+    const size_t sb = (size_t)bh * D * D;
+#pragma unroll
+    for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dS0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] = dS[tj][e];
+  }
+}
+
+// ------------------------------------------------------ per-chunk grads
+// The 10 lower-triangular 16 x 16 tiles of a C x C matrix.
+__device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
+  ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+  tj = t - ti * (ti + 1) / 2;
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ beta, const T* __restrict__ dout, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dla, float* __restrict__ dbeta, BwdWs ws,
+    int L) {
+  constexpr bool kErase = mode_erase(MODE);
+  constexpr bool kGated = mode_decay(MODE);
+  constexpr int NKB = D / 32, NCT = D / 16;
+  const int NC = ws.NC;
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
+  const int nrows = min(C, L - c * C);
+  const size_t row0 = (size_t)bh * L + (size_t)c * C;
+  const size_t cid = (size_t)bh * NC + c;
+  const size_t urow0 = (size_t)bh * NC * C + (size_t)c * C;   // row of U, dR
+  const T* qc = q + row0 * D;
+  const T* kc = k + row0 * D;
+  const T* vc = v + row0 * D;
+  const T* dOc = dout + row0 * D;
+  const float* Uc = kErase ? ws.U + urow0 * D : nullptr;
+  const float* dRc = kErase ? ws.dR + urow0 * D : nullptr;
+  const float* Se = ws.Sent + cid * D * D;
+  const float* dSe = ws.dSx + cid * D * D;
+
+  __shared__ __attribute__((aligned(16))) float gs[C];
+  __shared__ __attribute__((aligned(16))) float gam[C];
+  __shared__ __attribute__((aligned(16))) float fs[C];
+  __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float Em[C * LDC];
+  __shared__ __attribute__((aligned(16))) float Hm[kErase ? C * LDC : 4];
+  __shared__ __attribute__((aligned(16))) float GG[C * LDC];
+  __shared__ float dgam[C], dfv[C], dbe[C], rsum[C], csum[C];
+  __shared__ float red[kWaves];
+
+  for (int p = tid; p < C * LDC; p += kThreads) {
+    Em[p] = 0.f;
+    GG[p] = 0.f;
+    if constexpr (kErase) Hm[p] = 0.f;
+  }
+  if (tid < C) {
+    const float gg = ws.g[cid * C + tid];
+    gs[tid] = gg;
+    gam[tid] = kGated ? __expf(gg) : 1.f;
+    bs[tid] = (kErase && tid < nrows) ? beta[row0 + tid] : 0.f;
+    dbe[tid] = 0.f;
+  }
+  __syncthreads();
+  if (tid < C) fs[tid] = kGated ? __expf(gs[C - 1] - gs[tid]) : 1.f;
+
+  // C x C products on the lower tiles: scores, dO U^T, and (erase) K K^T, dR U^T
+  for (int t = wave; t < 10; t += kWaves) {
+    int ti, tj;
+    lower_tile(t, ti, tj);
+    const int ra = 16 * ti + n, rb = 16 * tj + n;
+    f32x4 qk = zero4(), dp = zero4(), kk = zero4(), dru = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag<T> bk = chunk_row<T, D>(kc, rb, nrows, 32 * kb, g);
+      const Frag<T> ado = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
+      mma(chunk_row<T, D>(qc, ra, nrows, 32 * kb, g), bk, qk);
+      if constexpr (kErase) {
+        mma(chunk_row<T, D>(kc, ra, nrows, 32 * kb, g), bk, kk);
+        const Frag2<T> bu = frag2_row<T>(Uc + (size_t)rb * D + 32 * kb, g);
+        mma_ab2(ado, bu, dp);
+        mma_a2b2(frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g), bu, dru);
+      } else {
+        mma(ado, chunk_row<T, D>(vc, rb, nrows, 32 * kb, g), dp);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ti + 4 * g + e, i = 16 * tj + n;
+      const float Gm = r >= i ? (kGated ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
+      const float P = qk[e] * Gm;
+      float gg = dp[e] * P;
+      Em[r * LDC + i] = dp[e] * Gm;
+      if constexpr (kErase) {
+        const float Kg = r > i ? kk[e] * Gm : 0.f;
+        const float dA = r > i ? -dru[e] : 0.f;
+        Hm[r * LDC + i] = dA * bs[r] * Gm;
+        gg += dA * bs[r] * Kg;
+        const float part = sum16(dA * Kg);
+        if (n == 0) atomicAdd(&dbe[r], part);
+      }
+      GG[r * LDC + i] = gg;
+    }
+  }
+  __syncthreads();
+
+  // C x D products: wave w owns the rows 16 w .. 16 w + 15
+  {
+    const int ti = wave, ra = 16 * ti + n;
+    Frag2<T> aE[2], aEt[2], aG[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      aE[kb] = frag2_row<T>(Em + ra * LDC + 32 * kb, g);
+      aEt[kb] = frag2_col<T>(Em + 32 * kb * LDC + ra, LDC, g);
+      if constexpr (kErase) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 32 * kb + kidx(g, j);
+          aG[kb].set(j, Hm[ra * LDC + i] + Hm[i * LDC + ra]);
+        }
+      }
+    }
+    Frag<T> aDO[NKB], aV[NKB];
+    Frag2<T> aDR[NKB], aU[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
+      if constexpr (kErase) {
+        aDR[kb] = frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g);
+        aU[kb] = frag2_row<T>(Uc + (size_t)ra * D + 32 * kb, g);
+      } else {
+        aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
+      }
+    }
+    float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
+          rdb[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int cj = 0; cj < NCT; ++cj) {
+      const int cb = 16 * cj + n;
+      f32x4 m1 = zero4(), m2 = zero4(), m3 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const Frag2<T> bS = frag2_row<T>(Se + (size_t)cb * D + 32 * kb, g);
+        const Frag2<T> bdS = frag2_row<T>(dSe + (size_t)cb * D + 32 * kb, g);
+        mma_ab2(aDO[kb], bS, m1);
+        if constexpr (kErase) {
+          mma_a2b2(aDR[kb], bS, m2);
+          mma_a2b2(aU[kb], bdS, m3);
+        } else {
+          mma_ab2(aV[kb], bdS, m3);
+        }
+      }
+      f32x4 ek = zero4(), etq = zero4(), gk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<T> bK = chunk_col<T, D>(kc, 32 * kb, cb, nrows, g);
+        mma_a2b(aE[kb], bK, ek);
+        mma_a2b(aEt[kb], chunk_col<T, D>(qc, 32 * kb, cb, nrows, g), etq);
+        if constexpr (kErase) mma_a2b(aG[kb], bK, gk);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * ti + 4 * g + e;
+        const int rr = min(r, nrows - 1);
+        const bool ok = r < nrows;
+        const float qv = ok ? to_f32(qc[(size_t)rr * D + cb]) : 0.f;
+        const float kv = ok ? to_f32(kc[(size_t)rr * D + cb]) : 0.f;
+        float dQ = gam[r] * m1[e] + ek[e];
+        float dK = fs[r] * m3[e] + etq[e];
+        rdg[e] += qv * m1[e];
+        rdf[e] += kv * m3[e];
+        if constexpr (kErase) {
+          dK += gk[e] - bs[r] * gam[r] * m2[e];
+          rdg[e] -= bs[r] * kv * m2[e];
+          const float vv = ok ? to_f32(vc[(size_t)rr * D + cb]) : 0.f;
+          rdb[e] += vv * dRc[(size_t)r * D + cb] - gam[r] * kv * m2[e];
+        }
+        if (ok) {
+          dq[(row0 + r) * D + cb] = dQ;
+          dk[(row0 + r) * D + cb] = dK;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ti + 4 * g + e;
+      const float a = sum16(rdg[e]), b = sum16(rdf[e]), cc = sum16(rdb[e]);
+      if (n == 0) {
+        dgam[r] = a;
+        dfv[r] = b;
+        dbe[r] += cc;
+      }
+    }
+  }
+
+  // gam_C <dS', S>
+  {
+    float acc = 0.f;
+    const f32x4* a4 = reinterpret_cast<const f32x4*>(dSe);
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(Se);
+    for (int p = tid; p < D * D / 4; p += kThreads) {
+      const f32x4 x = a4[p], y = s4[p];
+      acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+    }
+    acc = sum64(acc);
+    if (lane == 0) red[wave] = acc;
+  }
+  __syncthreads();
+  if (tid < C) {
+    float s = 0.f;
+    for (int i = 0; i < C; ++i) s += GG[tid * LDC + i];
+    rsum[tid] = s;
+  } else if (tid < 2 * C) {
+    const int i = tid - C;
+    float s = 0.f;
+    for (int r = 0; r < C; ++r) s += GG[r * LDC + i];
+    csum[i] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int r = lane;
+    const float dgC = red[0] + red[1] + red[2] + red[3];
+    float dg = rsum[r] - csum[r] + dgam[r] * gam[r] - dfv[r] * fs[r];
+    const float dff = sum64(dfv[r] * fs[r]);
+    if (r == C - 1) dg += dgC * gam[C - 1] + dff;
+    const float inc = wave_inclusive_scan(dg);
+    const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), C - 1));
+    if (r < nrows) {
+      if constexpr (kGated) dla[row0 + r] = tot - inc + dg;
+      if constexpr (kErase) dbeta[row0 + r] = dbe[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <typename X>
+struct Type {
+  using type = X;
+};
+
+template <typename F>
+hipError_t dispatch(const BwdArgs& a, F&& f) {
+  auto by_mode = [&](auto t, auto d) -> hipError_t {
+    switch (a.mode) {
+      case kModeLinear: return f(t, d, std::integral_constant<int, kModeLinear>{});
+      case kModeDelta: return f(t, d, std::integral_constant<int, kModeDelta>{});
+      case kModeGatedDelta: return f(t, d, std::integral_constant<int, kModeGatedDelta>{});
+      case kModeGatedLinear: return f(t, d, std::integral_constant<int, kModeGatedLinear>{});
+      default: return hipErrorInvalidValue;
+    }
+  };
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  if (a.in_bf16)
+    return a.d == 64 ? by_mode(Type<__bf16>{}, std::integral_constant<int, 64>{})
+                     : by_mode(Type<__bf16>{}, std::integral_constant<int, 128>{});
+  return a.d == 64 ? by_mode(Type<float>{}, std::integral_constant<int, 64>{})
+                   : by_mode(Type<float>{}, std::integral_constant<int, 128>{});
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const BwdArgs& a) { return carve(a, nullptr); }
+
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
+  BwdWs ws;
+  carve(a, &ws);
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
+  return dispatch(a, [&](auto t, auto d, auto m) {
+    using T = typename decltype(t)::type;
+    hipLaunchKernelGGL((bwd_prep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
+                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), a.log_alpha, a.beta, ws, a.L);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
+  BwdWs ws;
+  carve(a, &ws);
+  const int BH = a.B * a.H;
+  const unsigned grid = (unsigned)((size_t)BH * (a.d / 16));
+  return dispatch(a, [&](auto t, auto d, auto m) {
+    using T = typename decltype(t)::type;
+    hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
+                       dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.beta, a.S0, ws, BH, a.L);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
+  BwdWs ws;
+  carve(a, &ws);
+  const int BH = a.B * a.H;
+  const unsigned grid = (unsigned)((size_t)BH * (a.d / 16));
+  return dispatch(a, [&](auto t, auto d, auto m) {
+    using T = typename decltype(t)::type;
+    hipLaunchKernelGGL((bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
+                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), a.beta, static_cast<const T*>(a.dout),
+                       a.dS_final, a.dv, a.dS0, ws, BH, a.L);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st) {
+  BwdWs ws;
+  carve(a, &ws);
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
+  return dispatch(a, [&](auto t, auto d, auto m) {
+    using T = typename decltype(t)::type;
+    hipLaunchKernelGGL((bwd_grads_kernel<T, decltype(d)::value, decltype(m)::value>),
+                       dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.beta,
+                       static_cast<const T*>(a.dout), a.dq, a.dk, a.dlog_alpha, a.dbeta, ws,
+                       a.L);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace la

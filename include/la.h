@@ -386,6 +386,60 @@ int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv,
                                  int dtype, size_t* bytes);
 
 /*
+ * la_chunk_bwd -- gradients of la_chunk_fwd (training): for upstream
+ * gradients grad_out of the outputs and grad_S_final of the final state,
+ * the gradients of sum(grad_out * out) + sum(grad_S_final * S_final) with
+ * respect to q, k, v, log_alpha, beta and S0.
+ *
+ * The pages print no gradient formulas; training runs the chunked form and
+ * keeps the state entering every chunk for the backward ("FWP分块并行机制"
+ * in the hybrid-attention notes; train with the parallel form: "朴素线性注意力"
+ * in the lecture notes).  The call differentiates the forward's chunk step
+ * (WY/UT form, "HouseHolder变换和WY表示"; scalar decay, "Gated DeltaNet"):
+ * a per-chunk prep kernel (decays, T, transposed scores), a forward walk
+ * storing each chunk's entry state and U = T R, a reverse walk over chunks
+ * carrying the state gradient (dU = P^T dO + diag(f) K dS', dR = T^T dU,
+ * dS = gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR), and a
+ * parallel per-chunk kernel for dq, dk, dbeta and dlog_alpha.
+ *
+ *   q, k, v         [B, H, L, d]   dtype (LA_DTYPE_F32 or LA_DTYPE_BF16)
+ *   log_alpha, beta [B, H, L]      float32, as in la_chunk_fwd (NULL where
+ *                                  the mode does not read them)
+ *   S0              [B, H, d, d]   float32 or NULL (zeros)
+ *   grad_out        [B, H, L, d]   dtype (the type of la_chunk_fwd's out)
+ *   grad_S_final    [B, H, d, d]   float32 or NULL (zeros)
+ *   grad_q, grad_k, grad_v [B, H, L, d]  float32 (written)
+ *   grad_log_alpha  [B, H, L]      float32 (written; required in the gated
+ *                                  modes, else ignored and may be NULL)
+ *   grad_beta       [B, H, L]      float32 (written; required in the delta
+ *                                  modes, else ignored and may be NULL)
+ *   grad_S0         [B, H, d, d]   float32 (written) or NULL
+ *   B, H, L, dk, dv, C   dk = dv in {64, 128}, C = 64, any L >= 1 (the
+ *                        last chunk may be partial)
+ *   workspace       at least la_chunk_bwd_workspace_bytes() bytes, 16-byte
+ *                   aligned: per chunk the entry state and the gradient of
+ *                   the leaving state (2 d^2 floats), T and P^T (2 C^2
+ *                   floats), per token U and dR (2 d floats) and g
+ * Errors as la_chunk_fwd: missing required pointers LA_ERR_NULL; shapes
+ * LA_ERR_SHAPE / LA_ERR_UNSUPPORTED (also LA_DTYPE_BF16_F32OUT); any overlap
+ * between an output and an input, another output or the workspace
+ * LA_ERR_ALIAS.  Gradients of bf16 inputs are accumulated in float32 with
+ * float operands split into bf16 hi + lo parts.
+ */
+int la_chunk_bwd(const void* q, const void* k, const void* v,
+                 const float* log_alpha, const float* beta, const float* S0,
+                 const void* grad_out, const float* grad_S_final, float* grad_q,
+                 float* grad_k, float* grad_v, float* grad_log_alpha,
+                 float* grad_beta, float* grad_S0, int B, int H, int L, int dk,
+                 int dv, int C, int mode, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* la_chunk_bwd_workspace_bytes -- workspace size for la_chunk_bwd with these
+ * sizes, mode and dtype, written to *bytes; same shape checks. */
+int la_chunk_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
+                                 int mode, int dtype, size_t* bytes);
+
+/*
  * la_decode_step -- one token of the recurrence for B*H independent states
  * (decode / inference form), updating the state in place.
  *

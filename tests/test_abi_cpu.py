@@ -425,3 +425,72 @@ def test_library_resolves_every_symbol_at_load():
     load only fails when the missing function is first called, on a GPU)."""
     import ctypes as ct
     ct.CDLL(_lib.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
+# ------------------------------------------------------------- backward
+def bwd(lib, q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5), do=fake(6),
+        dsf=fake(7), gq=fake(8), gk=fake(9), gv=fake(10), gla=fake(11), gbe=fake(12),
+        gs0=fake(13), B=1, H=1, L=64, dk=64, dv=64, C=64, mode=2, dtype=1, ws=fake(14),
+        wsb=P):
+    return lib.la_chunk_bwd(q, k, v, la, be, s0, do, dsf, gq, gk, gv, gla, gbe, gs0,
+                            B, H, L, dk, dv, C, mode, dtype, ws, wsb, None)
+
+
+def bwd_ws_bytes(lib, B=1, H=1, L=64, d=64, mode=2, dtype=1):
+    n = ctypes.c_size_t(12345)
+    rc = lib.la_chunk_bwd_workspace_bytes(B, H, L, d, d, 64, mode, dtype, ctypes.byref(n))
+    return rc, n.value
+
+
+def expected_bwd_ws(B, H, L, d, erase):
+    """Per chunk the entry state and the gradient of the leaving state
+    (d^2 floats each) and P^T (C^2); T (C^2) with erase; per padded token
+    g, and U and dR (d floats each) with erase; each array 256-byte aligned."""
+    nc = -(-L // 64)
+    pad = lambda n: -(-n * 4 // 256) * 256     # noqa: E731
+    bh = B * H
+    arrays = [bh * nc * 64, bh * nc * 64 * 64, bh * nc * d * d, bh * nc * d * d]
+    if erase:
+        arrays += [bh * nc * 64 * 64, bh * nc * 64 * d, bh * nc * 64 * d]
+    return sum(pad(n) for n in arrays)
+
+
+def test_bwd_workspace_size():
+    lib = _lib.get()
+    for mode in range(4):
+        for (B, H, L, d) in ((1, 1, 64, 64), (2, 3, 200, 128), (1, 32, 65536, 128), (3, 1, 1, 64)):
+            for dtype in (0, 1):
+                rc, n = bwd_ws_bytes(lib, B, H, L, d, mode, dtype)
+                assert rc == OK and n == expected_bwd_ws(B, H, L, d, mode in (1, 2))
+    assert bwd_ws_bytes(lib, dtype=2)[0] == UNSUP
+    assert bwd_ws_bytes(lib, d=96)[0] == UNSUP
+    assert lib.la_chunk_bwd_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(do=None), NULL), (dict(gq=None), NULL), (dict(gk=None), NULL),
+    (dict(gv=None), NULL), (dict(be=None), NULL), (dict(la=None), NULL),
+    (dict(gla=None), NULL), (dict(gbe=None), NULL), (dict(gbe=None, mode=1), NULL),
+    (dict(gla=None, mode=3), NULL),
+    (dict(B=0), SHAPE), (dict(L=0), SHAPE), (dict(dk=64, dv=128), UNSUP), (dict(C=32), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(mode=4), UNSUP),
+    (dict(ws=None), WS), (dict(wsb=1000), WS), (dict(ws=ctypes.c_void_p(15 * P + 8)), WS),
+    (dict(gq=ctypes.c_void_p(P + 64)), ALIAS),          # grad_q overlaps q
+    (dict(gk=ctypes.c_void_p(9 * P + 64)), ALIAS),      # grad_k overlaps grad_q
+    (dict(gs0=ctypes.c_void_p(7 * P)), ALIAS),          # grad_S0 is dS_final
+    (dict(ws=ctypes.c_void_p(11 * P - 4096)), ALIAS),   # workspace overlaps grad_v
+])
+def test_chunk_bwd_rejects(kw, code):
+    lib = _lib.get()
+    assert bwd(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""
+
+
+def test_chunk_bwd_unused_gradients_and_gates():
+    """Gradients and gates a mode does not have may be NULL (or anything):
+    linear mode with every gate pointer NULL passes validation and stops at
+    the alias of grad_q with q."""
+    lib = _lib.get()
+    assert bwd(lib, mode=0, la=None, be=None, gla=None, gbe=None,
+               gq=ctypes.c_void_p(P + 64)) == ALIAS
+    assert bwd(lib, mode=3, be=None, gbe=None, gq=ctypes.c_void_p(P + 64)) == ALIAS

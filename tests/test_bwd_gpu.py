@@ -1,0 +1,134 @@
+"""GPU parity of the backward (la_chunk_bwd) against the float64 oracle.
+
+The reference is ``oracle.recurrent_bwd`` -- the reverse of the token
+recurrence, pinned on the CPU by finite differences -- on small cases, and
+``oracle.chunkwise_bwd`` (pinned on the CPU to the token backward) on the
+longer ones.  Both consume float64 copies of exactly the tensors handed to
+the GPU.  Tolerances per gradient as for the forward: float32 inputs
+max|err| <= 1e-4 max|ref|; bf16 inputs max|err| <= 2e-2 RMS(ref) (the
+gradients are float32, so no output rounding is added).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_gated_delta_la_amd as la
+import oracle
+import workloads
+from _parity import assert_close, f64, log, to_cuda
+from test_parity_gpu import recipe
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("linear", "delta", "gated_delta", "gated_linear")
+GATED = ("gated_delta", "gated_linear")
+ERASE = ("delta", "gated_delta")
+
+
+def run_bwd(w, x, gr, mode, with_s0=True, with_dsf=True):
+    d = to_cuda(x)
+    g = to_cuda(gr)
+    res = la.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                       d["S0"] if with_s0 else None, g["dout"],
+                       g["dS_final"] if with_dsf else None, mode=mode)
+    torch.cuda.synchronize()
+    return res
+
+
+def reference(x, gr, mode, with_s0=True, with_dsf=True, chunked=False):
+    y = workloads.to_f64(x)
+    gy = workloads.to_f64(gr)
+    args = (y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
+            y["S0"] if with_s0 else None, mode)
+    dsf = gy["dS_final"] if with_dsf else None
+    if chunked:
+        return oracle.chunkwise_bwd(*args, 64, gy["dout"], dsf)
+    return oracle.recurrent_bwd(*args, gy["dout"], dsf)
+
+
+def compare(res, ref, mode, dtype):
+    for name in ("dq", "dk", "dv", "dS0"):
+        assert_close(name, f64(res[name]), ref[name], dtype)
+    if mode in GATED:
+        assert_close("dlog_alpha", f64(res["dlog_alpha"]), ref["dlog_alpha"], dtype)
+    else:
+        assert res["dlog_alpha"] is None
+    if mode in ERASE:
+        assert_close("dbeta", f64(res["dbeta"]), ref["dbeta"], dtype)
+    else:
+        assert res["dbeta"] is None
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", ("f32", "bf16"))
+@pytest.mark.parametrize("d,L", [(64, 64), (64, 200), (128, 131), (128, 1)])
+def test_chunk_bwd_small(mode, dtype, d, L):
+    """Every gradient, every element, against the token backward: one
+    chunk, several chunks with a ragged tail, a single token; nonzero S0
+    and dS_final."""
+    w = recipe(mode, dtype, B=2, H=1, L=L, d=d, s0_std=0.05, seed=31 + L + d)
+    log(f"case chunk_bwd {w.name} mode={mode} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w, ds_std=0.1)
+    res = run_bwd(w, x, gr, mode)
+    ref = reference(x, gr, mode)
+    compare(res, ref, mode, dtype)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_zero_state_and_no_state_gradient(mode):
+    """S0 = NULL and dS_final = NULL read as zeros."""
+    w = recipe(mode, "bf16", B=1, H=2, L=130, d=64, seed=5)
+    log(f"case chunk_bwd_nulls {w.name} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w)
+    res = run_bwd(w, x, gr, mode, with_s0=False, with_dsf=False)
+    ref = reference(x, gr, mode, with_s0=False, with_dsf=False)
+    compare(res, ref, mode, "bf16")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_long(mode):
+    """A long bf16 sequence at d = 128 (64 chunks) against the chunkwise
+    float64 backward; the walks carry the state gradient over every chunk."""
+    w = recipe(mode, "bf16", B=1, H=2, L=4096 - 17, d=128, s0_std=0.02, seed=77)
+    log(f"case chunk_bwd_long {w.name} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w, ds_std=0.05)
+    res = run_bwd(w, x, gr, mode)
+    ref = reference(x, gr, mode, chunked=True)
+    compare(res, ref, mode, "bf16")
+
+
+def test_chunk_bwd_state_gradient_chains_over_a_split():
+    """The state gradient chains: the backward of two halves, the second
+    half's dS0 fed to the first as dS_final, equals the backward of the
+    whole (the chunk boundary at 128 lies on a chunk boundary)."""
+    mode = "gated_delta"
+    w = recipe(mode, "f32", B=1, H=2, L=256, d=64, s0_std=0.05, seed=91)
+    log(f"case chunk_bwd_split {w.name} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w, ds_std=0.1)
+    whole = run_bwd(w, x, gr, mode)
+    d = to_cuda(x)
+    g = to_cuda(gr)
+    # forward of the first half gives the second half's S0
+    _, S_mid = la.chunk_fwd(d["q"][:, :, :128].contiguous(), d["k"][:, :, :128].contiguous(),
+                            d["v"][:, :, :128].contiguous(),
+                            d["log_alpha"][:, :, :128].contiguous(),
+                            d["beta"][:, :, :128].contiguous(), d["S0"], mode=mode)
+    half = lambda t, s: t[:, :, s].contiguous()     # noqa: E731
+    second = la.chunk_bwd(*(half(d[n], slice(128, 256)) for n in ("q", "k", "v", "log_alpha",
+                                                                   "beta")),
+                          S_mid, half(g["dout"], slice(128, 256)), g["dS_final"], mode=mode)
+    first = la.chunk_bwd(*(half(d[n], slice(0, 128)) for n in ("q", "k", "v", "log_alpha",
+                                                                "beta")),
+                         d["S0"], half(g["dout"], slice(0, 128)), second["dS0"], mode=mode)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+        got = torch.cat([first[name], second[name]], dim=2)
+        ref = f64(whole[name])
+        err = float(np.max(np.abs(f64(got) - ref)))
+        log(f"  {name}: split vs whole max|err| {err:.3e}")
+        assert err <= 1e-4 * float(np.max(np.abs(ref)))
+    assert_close("dS0", f64(first["dS0"]), f64(whole["dS0"]), "f32")

@@ -168,3 +168,17 @@ def make_inputs(w: Workload, seed=None):
 def to_f64(inputs):
     """float64 NumPy copies of exactly the values handed to the device."""
     return {key: t.to(torch.float64).numpy() for key, t in inputs.items()}
+
+
+def make_upstream_grads(w: Workload, seed=None, ds_std=1.0):
+    """Upstream gradients for a backward of workload ``w``: ``dout`` drawn
+    N(0, 1) in the device dtype with the output's shape ``[B, H, L, dv]``,
+    and ``dS_final`` N(0, ds_std^2) float32 ``[B, H, dk, dv]`` (zeros when
+    ds_std == 0).  Seeded on its own (default: the workload's seed + 7919),
+    so the forward inputs are unchanged."""
+    gen = torch.Generator("cpu")
+    gen.manual_seed((w.seed + 7919) if seed is None else seed)
+    dout = _normal(gen, (w.B, w.H, w.L, w.dv))
+    dS = _normal(gen, (w.B, w.H, w.dk, w.dv)) * ds_std if ds_std > 0 else \
+        torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32)
+    return dict(dout=dout.to(w.torch_dtype).contiguous(), dS_final=dS.contiguous())
