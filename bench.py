@@ -455,6 +455,56 @@ def bench_noncausal(w, steps, warmup):
             "hbm_frac": round(by / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4), "kernels": kernels}
 
 
+def bwd_flops_per_token_head(w):
+    """Dense chunkwise backward flops per token-head as built (the forward
+    walk recomputes U and the states): 12 C x C x d products per chunk in
+    the delta modes (scores twice, K K^T twice, T R, P^T dO, T^T dU, dO U^T,
+    dR U^T, E K, E^T Q, G K; 7 without erase) and 8 C x d x d (K S, K^T U,
+    Q^T dO, K dS', K^T dR, dO S^T, dR S^T, U dS'^T; 5 without erase), plus
+    the T solve, C^3 / 3 per chunk."""
+    erase = w.mode in ("delta", "gated_delta")
+    d, C = w.dk, w.C
+    n_ccd = 12 if erase else 7
+    n_cdd = 8 if erase else 5
+    return n_ccd * 2 * C * d + n_cdd * 2 * d * d + (C * C / 3 if erase else 0)
+
+
+def bench_backward(w, steps, warmup):
+    """la_chunk_bwd at a forward workload's sizes (upstream gradients drawn
+    N(0, 1), dS_final N(0, 0.02^2)): tokens/s, the per-kernel HIP-event
+    times, the fraction of bf16 MFMA peak of the dense backward flops and of
+    HBM peak of the minimal bytes (q, k, v, dO read and dq, dk, dv written
+    as float32 once, gates and their gradients, states per head)."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] backward {w.name}: generating inputs")
+    x = {k: t.cuda() for k, t in workloads.make_inputs(w).items()}
+    gr = {k: t.cuda() for k, t in workloads.make_upstream_grads(w, ds_std=0.02).items()}
+    nws = la.chunk_bwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode,
+                                       dtype=w.torch_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    s0 = x["S0"] if w.s0_std > 0 else None
+    ms, kernels = _timed(lambda: la.chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"],
+                                              x["beta"], s0, gr["dout"], gr["dS_final"],
+                                              mode=w.mode, workspace=ws), steps, warmup)
+    th = w.B * w.H * w.L
+    esz = 2 if w.dtype == "bf16" else 4
+    by = th * (4 * w.dk * esz + 3 * w.dk * 4 + 4 * 4) + w.B * w.H * 3 * w.dk * w.dv * 4
+    fl = th * bwd_flops_per_token_head(w)
+    del x, gr, ws
+    torch.cuda.empty_cache()
+    return {"workload": "backward_" + w.name, "mode": w.mode, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.B * w.L / ms * 1e3, 1),
+            "flops_per_token_head": bwd_flops_per_token_head(w),
+            "mfma_frac_of_bf16_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4),
+            "min_bytes": by, "hbm_frac_of_min_bytes": round(by / (ms * 1e-3) /
+                                                             (HBM_PEAK_GBS * 1e9), 4),
+            "workspace_bytes": nws, "kernels": kernels}
+
+
 def varlen_lengths(n, total, seed):
     """Seeded length mix of a packed batch: n lengths summing to `total`,
     log-uniform between 1 and 16 K tokens (short prompts next to long
@@ -592,6 +642,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra measurements (other mode, packed batch)")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="only time la_chunk_bwd at the forward workload's sizes and print "
+                         "that measurement (for profiling runs)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -623,6 +676,9 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     w = workloads.head_shard(workloads.WORKLOADS[args.workload], args.shard)
+    if args.only_backward:
+        print(json.dumps({"backward": bench_backward(w, args.steps, args.warmup)}), flush=True)
+        return
     x, fwd = bench_forward(w, args.steps, args.warmup)
     dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
     extra = None
@@ -634,6 +690,7 @@ def main():
             "segments": bench_segments(workloads.WORKLOAD4_SHARD8, args.steps, 1),
             "fused": bench_fused(w, args.steps, 1),
             "noncausal": bench_noncausal(workloads.WORKLOADS[2], args.steps, 1),
+            "backward": bench_backward(w, args.steps, 1),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {

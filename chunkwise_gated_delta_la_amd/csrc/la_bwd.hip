@@ -175,6 +175,102 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
   }
 }
 
+// The chain operands of one chunk -- K rows, T (erase modes), 16 columns of
+// V (forward walk), the decays and beta -- read by the 192 threads of the
+// three staging waves in one batch (every load issued, at clamped indices,
+// before the first LDS write), then written to one half of the walk's
+// double buffer.  Rows past the end of the sequence read as zero.
+template <typename T, int D, bool ERASE, bool WITH_V>
+struct ChunkStage {
+  static constexpr int NT = kThreads - kWave;
+  static constexpr int PE = 16 / sizeof(T);
+  static constexpr int LDK = D + PE;
+  static constexpr int VPR = D / PE;
+  static constexpr int NK = C * VPR;
+  static constexpr int IK = (NK + NT - 1) / NT;
+  static constexpr int NTV = C * C / 4;
+  static constexpr int IT = ERASE ? (NTV + NT - 1) / NT : 1;
+  static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
+  static constexpr int NV = C * VV;
+  static constexpr int IV = WITH_V ? (NV + NT - 1) / NT : 1;
+  u32x4 kx[IK];
+  f32x4 tx[IT];
+  u32x4 vx[IV];
+  float gx, bx;
+
+  __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
+                                       const float* __restrict__ beta, const float* Tg,
+                                       const float* gg, size_t row0, int nrows, int col0,
+                                       int t) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
+      kx[i] = r < nrows ? x : z;
+    }
+    if constexpr (ERASE) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int p = min(t + i * NT, NTV - 1), r = p / (C / 4), cv = p % (C / 4);
+        tx[i] = *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
+      }
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const int p = min(t + i * NT, NV - 1), r = p / VV, cv = p % VV;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(
+            v + (row0 + min(r, nrows - 1)) * D + col0 + cv * PE);
+        vx[i] = r < nrows ? x : z;
+      }
+    }
+    const int tr = min(t, C - 1);
+    gx = gg[tr];
+    float b = 0.f;
+    if constexpr (ERASE) b = beta[row0 + min(tr, nrows - 1)];
+    bx = tr < nrows ? b : 0.f;
+  }
+
+  __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* bsb,
+                                        int t) const {
+#pragma unroll
+    for (int i = 0; i < IK; ++i) {
+      const int p = t + i * NT;
+      if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
+    }
+    if constexpr (ERASE) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int p = t + i * NT;
+        if (p < NTV) *reinterpret_cast<f32x4*>(Tb + (p / (C / 4)) * LDC + 4 * (p % (C / 4))) = tx[i];
+      }
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const int p = t + i * NT;
+        if (p < NV) {
+          float* dst = Vb + (p / VV) * LDX + (p % VV) * PE;
+          if constexpr (IsBf16<T>::value) {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, vx[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = (float)x[j];
+          } else {
+            const f32x4 x = __builtin_bit_cast(f32x4, vx[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[j] = x[j];
+          }
+        }
+      }
+    }
+    if (t < C) {
+      gsb[t] = gx;
+      bsb[t] = bx;
+    }
+  }
+};
+
 // ---------------------------------------------------------------- prep
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
@@ -286,7 +382,6 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   constexpr int PE = 16 / sizeof(T);
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
-  constexpr int VPR = D / PE;   // 16-byte vectors per token row
 
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
@@ -303,32 +398,15 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   const int NC = ws.NC;
   const size_t NCC = (size_t)NC * C;
 
-  // chunk c's operands into buffer b by threads t, t + nt, ...
-  auto stage = [&](int c, int b, int t, int nt) {
+  // chunk c's operands into buffer b (waves 1-3)
+  auto stage = [&](int c, int b) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = (size_t)bh * L + (size_t)c * C;
-    for (int p = t; p < C * VPR; p += nt) {
-      const int r = p / VPR, cv = p % VPR;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (r < nrows) x = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + cv * PE);
-      *reinterpret_cast<u32x4*>(&Kb[b][r * LDK + cv * PE]) = x;
-    }
-    if constexpr (kErase) {
-      const float* Tg = ws.T + ((size_t)bh * NC + c) * C * C;
-      for (int p = t; p < C * C / 4; p += nt) {
-        const int r = p / (C / 4), cv = p % (C / 4);
-        *reinterpret_cast<f32x4*>(&Tb[b][r * LDC + 4 * cv]) =
-            *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
-      }
-    }
-    for (int p = t; p < C * 16; p += nt) {
-      const int r = p / 16, cc = p % 16;
-      Vb[b][r * LDX + cc] = r < nrows ? to_f32(v[(row0 + r) * D + col0 + cc]) : 0.f;
-    }
-    for (int p = t; p < C; p += nt) {
-      gsb[b][p] = ws.g[((size_t)bh * NC + c) * C + p];
-      bsb[b][p] = (kErase && p < nrows) ? beta[row0 + p] : 0.f;
-    }
+    const size_t cid = (size_t)bh * NC + c;
+    ChunkStage<T, D, kErase, true> st;
+    st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
+            tid - kWave);
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], bsb[b], tid - kWave);
   };
 
   f32x4 S[NKT];
@@ -340,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
       for (int e = 0; e < 4; ++e)
         S[tj][e] = S0 ? S0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
   }
-  stage(0, 0, tid, kThreads);
+  if (wave != 0) stage(0, 0);
   __syncthreads();
 
   for (int c = 0; c < NC; ++c) {
@@ -419,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
           mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bX[kb], S[tj]);
       }
     } else if (c + 1 < NC) {
-      stage(c + 1, b ^ 1, tid - kWave, kThreads - kWave);
+      stage(c + 1, b ^ 1);
     }
     __syncthreads();
   }
@@ -436,7 +514,6 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   constexpr int PE = 16 / sizeof(T);
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
-  constexpr int VPR = D / PE;
 
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
@@ -454,63 +531,66 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   const int NC = ws.NC;
   const size_t NCC = (size_t)NC * C;
 
-  // chunk c's operands and its two dS-independent products into buffer b,
-  // by waves w0, w0 + 1, ..., w0 + nw - 1
-  auto side = [&](int c, int b, int w0, int nw) {
+  // chunk c's operands and its two dS-independent products into buffer b
+  // (waves 1-3): wave 1 forms X1 = P^T dO, waves 2 and 3 half of X2 = Q^T
+  // diag(gam) dO each, for this tile's 16 columns of dO.  Every global load
+  // of the step is issued before the first LDS write.
+  auto side = [&](int c, int b) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = (size_t)bh * L + (size_t)c * C;
     const size_t cid = (size_t)bh * NC + c;
-    const int t = tid - w0 * kWave, nt = nw * kWave;
-    for (int p = t; p < C * VPR; p += nt) {
-      const int r = p / VPR, cv = p % VPR;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (r < nrows) x = *reinterpret_cast<const u32x4*>(k + (row0 + r) * D + cv * PE);
-      *reinterpret_cast<u32x4*>(&Kb[b][r * LDK + cv * PE]) = x;
-    }
-    if constexpr (kErase) {
-      const float* Tg = ws.T + cid * C * C;
-      for (int p = t; p < C * C / 4; p += nt) {
-        const int r = p / (C / 4), cv = p % (C / 4);
-        *reinterpret_cast<f32x4*>(&Tb[b][r * LDC + 4 * cv]) =
-            *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
-      }
-    }
-    for (int p = t; p < C; p += nt) {
-      gsb[b][p] = ws.g[cid * C + p];
-      bsb[b][p] = (kErase && p < nrows) ? beta[row0 + p] : 0.f;
-    }
-    // dO columns col0 .. col0 + 15 as B operands: raw, and scaled by gam
-    const T* dOc = dout + row0 * D;
+    const int t = tid - kWave, wv = wave - 1;
+    ChunkStage<T, D, kErase, false> st;
+    st.load(k, nullptr, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0,
+            nrows, 0, t);
+    // dO columns col0 .. col0 + 15 as B operands (rows 32 kb + kidx(g, j))
     Frag<T> dof[2];
-    Frag2<T> dog[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      dof[kb] = chunk_col<T, D>(dOc, 32 * kb, col0 + n, nrows, g);
+    for (int kb = 0; kb < 2; ++kb) dof[kb] = chunk_col<T, D>(dout + row0 * D, 32 * kb, col0 + n, nrows, g);
+    if (wv == 0) {
+      Frag2<T> ap[4][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 32 * kb + kidx(g, j);
-        const float gam = kGated ? __expf(ws.g[cid * C + r]) : 1.f;
-        dog[kb].set(j, to_f32(dof[kb].v[j]) * gam);
-      }
-    }
-    const int wv = wave - w0;
-    for (int tt = wv; tt < 4 + NKT; tt += nw) {
-      f32x4 acc = zero4();
-      if (tt < 4) {
-        // X1 rows i = 16 tt + 4 g + e: sum_r P^T_ir dO_r
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mma_a2b(frag2_row<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g), dof[kb], acc);
+          ap[tt][kb] = frag2_row<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g);
+      st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma_a2b(ap[tt][kb], dof[kb], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) X1[b][(16 * tt + 4 * g + e) * LDX + n] = acc[e];
-      } else {
-        // X2 rows 16 tj + 4 g + e (key dimension): sum_r Q_r gam_r dO_r
-        const int tj = tt - 4;
+      }
+    } else {
+      constexpr int NX = NKT / 2;
+      const int tj0 = (wv - 1) * NX;
+      float gm[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gm[kb][j] = ws.g[cid * C + 32 * kb + kidx(g, j)];
+      Frag<T> aq[NX][2];
+#pragma unroll
+      for (int u = 0; u < NX; ++u)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mma_ab2(chunk_col<T, D>(q + row0 * D, 32 * kb, 16 * tj + n, nrows, g), dog[kb], acc);
+          aq[u][kb] = chunk_col<T, D>(q + row0 * D, 32 * kb, 16 * (tj0 + u) + n, nrows, g);
+      st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
+      Frag2<T> dog[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X2[b][(16 * tj + 4 * g + e) * LDX + n] = acc[e];
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          dog[kb].set(j, to_f32(dof[kb].v[j]) * (kGated ? __expf(gm[kb][j]) : 1.f));
+#pragma unroll
+      for (int u = 0; u < NX; ++u) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) mma_ab2(aq[u][kb], dog[kb], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X2[b][(16 * (tj0 + u) + 4 * g + e) * LDX + n] = acc[e];
       }
     }
   };
@@ -524,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       for (int e = 0; e < 4; ++e)
         dS[tj][e] = dS_final ? dS_final[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
   }
-  side(NC - 1, 0, 0, kWaves);
+  if (wave != 0) side(NC - 1, 0);
   __syncthreads();
 
   for (int s = 0; s < NC; ++s) {
@@ -614,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
       }
     } else if (c > 0) {
-      side(c - 1, b ^ 1, 1, kWaves - 1);
+      side(c - 1, b ^ 1);
     }
     __syncthreads();
   }
@@ -671,6 +751,23 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ float dgam[C], dfv[C], dbe[C], rsum[C], csum[C];
   __shared__ float red[kWaves];
 
+  // <dS', S> (this thread's share), every load issued before the sum
+  float dgc_part = 0.f;
+  {
+    constexpr int NV4 = D * D / 4 / kThreads;
+    const f32x4* a4 = reinterpret_cast<const f32x4*>(dSe);
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(Se);
+    f32x4 xa[NV4], xs[NV4];
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      xa[i] = a4[tid + i * kThreads];
+      xs[i] = s4[tid + i * kThreads];
+    }
+#pragma unroll
+    for (int i = 0; i < NV4; ++i)
+      dgc_part += xa[i][0] * xs[i][0] + xa[i][1] * xs[i][1] + xa[i][2] * xs[i][2] +
+                  xa[i][3] * xs[i][3];
+  }
   for (int p = tid; p < C * LDC; p += kThreads) {
     Em[p] = 0.f;
     GG[p] = 0.f;
@@ -743,16 +840,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
       }
     }
     Frag<T> aDO[NKB], aV[NKB];
-    Frag2<T> aDR[NKB], aU[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
-      if constexpr (kErase) {
-        aDR[kb] = frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g);
-        aU[kb] = frag2_row<T>(Uc + (size_t)ra * D + 32 * kb, g);
-      } else {
-        aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
-      }
+      if constexpr (!kErase) aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
     }
     float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
           rdb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -765,8 +856,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
         const Frag2<T> bdS = frag2_row<T>(dSe + (size_t)cb * D + 32 * kb, g);
         mma_ab2(aDO[kb], bS, m1);
         if constexpr (kErase) {
-          mma_a2b2(aDR[kb], bS, m2);
-          mma_a2b2(aU[kb], bdS, m3);
+          // dR and U rows re-read per column tile (cache hits): fewer live registers
+          mma_a2b2(frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g), bS, m2);
+          mma_a2b2(frag2_row<T>(Uc + (size_t)ra * D + 32 * kb, g), bdS, m3);
         } else {
           mma_ab2(aV[kb], bdS, m3);
         }
@@ -814,16 +906,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     }
   }
 
-  // gam_C <dS', S>
   {
-    float acc = 0.f;
-    const f32x4* a4 = reinterpret_cast<const f32x4*>(dSe);
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(Se);
-    for (int p = tid; p < D * D / 4; p += kThreads) {
-      const f32x4 x = a4[p], y = s4[p];
-      acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-    }
-    acc = sum64(acc);
+    const float acc = sum64(dgc_part);
     if (lane == 0) red[wave] = acc;
   }
   __syncthreads();
