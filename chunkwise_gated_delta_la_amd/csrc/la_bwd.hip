@@ -78,6 +78,8 @@ struct BwdWs {
   float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
   float* dR;    // [BH, NC * C, D]  T^T dU (erase modes)
   int NC;
+  size_t nS;    // elements of Sent and dSx
+  size_t nU;    // elements of U and dR
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -96,7 +98,7 @@ size_t carve(const BwdArgs& a, BwdWs* ws) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], (int)NC};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], (int)NC, n[3], n[4]};
   return off;
 }
 
@@ -124,26 +126,109 @@ __device__ __forceinline__ Frag<T> chunk_col(const T* base, int k0, int col, int
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = k0 + kidx(g, j);
-    const float x = to_f32(base[(size_t)min(r, nrows - 1) * D + col]);
-    f.set(j, r < nrows ? x : 0.f);
+    const T x = base[(size_t)min(r, nrows - 1) * D + col];
+    f.v[j] = r < nrows ? x : T(0.f);
   }
   return f;
+}
+
+// Split operand from 8 float values (slot order), two instructions per
+// value for bf16 (frag2_pack).
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_of(const float (&x)[8]) {
+  if constexpr (IsBf16<T>::value) {
+    return frag2_pack(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+  } else {
+    Frag2<T> f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.set(j, x[j]);
+    return f;
+  }
+}
+
+// Split operand from a float row p[kidx(g, j)].
+template <typename T>
+__device__ __forceinline__ Frag2<T> frag2_rowx(const float* p, int g) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16 + 4 * g);
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return frag2_of<T>(x);
 }
 
 // Split operand gathered from a float column: p[kidx(g, j) * ld].
 template <typename T>
 __device__ __forceinline__ Frag2<T> frag2_col(const float* p, int ld, int g) {
-  Frag2<T> f;
+  float x[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f.set(j, p[kidx(g, j) * ld]);
-  return f;
+  for (int j = 0; j < 8; ++j) x[j] = p[kidx(g, j) * ld];
+  return frag2_of<T>(x);
 }
+
+// A float matrix the walks hand to the gradient kernel, in the form that
+// kernel's MFMAs take it: float32 for float inputs; for bf16 inputs two
+// bf16 planes, hi = bf16(x) and lo = bf16(x - hi) (x to about 16 bits), so
+// the gradient kernel loads split operands without converting.  Either form
+// fills the same bytes of the workspace.
+template <typename T>
+struct SplitMat;
+
+template <>
+struct SplitMat<float> {
+  float* p;
+  __device__ static SplitMat make(float* region, size_t) { return SplitMat{region}; }
+  __device__ __forceinline__ void put(size_t i, float x) const { p[i] = x; }
+  __device__ __forceinline__ float get(size_t i) const { return p[i]; }
+  __device__ __forceinline__ Frag2<float> row(size_t i, int g) const {
+    Frag2<float> f;
+    f.hi = frag_row(p + i, g);
+    return f;
+  }
+};
+
+template <>
+struct SplitMat<__bf16> {
+  __bf16* p;
+  size_t plane;   // the lo plane starts plane elements after the hi plane
+  __device__ static SplitMat make(float* region, size_t n) {
+    return SplitMat{reinterpret_cast<__bf16*>(region), n};
+  }
+  __device__ __forceinline__ void put(size_t i, float x) const {
+    const __bf16 h = (__bf16)x;
+    p[i] = h;
+    p[plane + i] = (__bf16)(x - (float)h);
+  }
+  __device__ __forceinline__ float get(size_t i) const {
+    return (float)p[i] + (float)p[plane + i];
+  }
+  __device__ __forceinline__ Frag2<__bf16> row(size_t i, int g) const {
+    Frag2<__bf16> f;
+    f.hi = frag_row(p + i, g);
+    f.lo = frag_row(p + plane + i, g);
+    return f;
+  }
+};
 
 // acc += a * b with a split and b exact
 template <typename T>
 __device__ __forceinline__ void mma_a2b(const Frag2<T>& a, const Frag<T>& b, f32x4& acc) {
   if constexpr (IsBf16<T>::value) mma(a.lo, b, acc);
   mma(a.hi, b, acc);
+}
+
+// sum_j a_j b_j of two split operands (hi + lo each)
+template <typename T>
+__device__ __forceinline__ float frag_dot(const Frag2<T>& a, const Frag2<T>& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float x = to_f32(a.hi.v[j]), y = to_f32(b.hi.v[j]);
+    if constexpr (IsBf16<T>::value) {
+      x += to_f32(a.lo.v[j]);
+      y += to_f32(b.lo.v[j]);
+    }
+    s = fmaf(x, y, s);
+  }
+  return s;
 }
 
 // Sum over the 16 lanes of a lane group (lanes with the same l / 16).
@@ -424,11 +509,12 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
     if (wave == 0) {
-      float* Se = ws.Sent + ((size_t)bh * NC + c) * D * D;
+      const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
+      const size_t se0 = ((size_t)bh * NC + c) * D * D + col0 + n;
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Se[(size_t)(16 * tj + 4 * g + e) * D + col0 + n] = S[tj][e];
+        for (int e = 0; e < 4; ++e) Se.put(se0 + (size_t)(16 * tj + 4 * g + e) * D, S[tj][e]);
       const float* gsc = gsb[b];
       const float gC = gsc[C - 1];
       const float gamC = kGated ? __expf(gC) : 1.f;
@@ -462,15 +548,16 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
         }
         const Frag2<T> bR[2] = {frag2_from_acc<T>(R[0], R[1]), frag2_from_acc<T>(R[2], R[3])};
         f32x4 U[4];
-        float* Ug = ws.U + ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
+        const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
+        const size_t u0 = ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           U[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma_a2b2(frag2_row<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g), bR[kb], U[ti]);
+            mma_a2b2(frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g), bR[kb], U[ti]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Ug[(size_t)(16 * ti + 4 * g + e) * D] = U[ti][e];
+          for (int e = 0; e < 4; ++e) Um.put(u0 + (size_t)(16 * ti + 4 * g + e) * D, U[ti][e]);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -553,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          ap[tt][kb] = frag2_row<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g);
+          ap[tt][kb] = frag2_rowx<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g);
       st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -580,10 +667,13 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
       Frag2<T> dog[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          dog[kb].set(j, to_f32(dof[kb].v[j]) * (kGated ? __expf(gm[kb][j]) : 1.f));
+          x[j] = to_f32(dof[kb].v[j]) * (kGated ? __expf(gm[kb][j]) : 1.f);
+        dog[kb] = frag2_of<T>(x);
+      }
 #pragma unroll
       for (int u = 0; u < NX; ++u) {
         f32x4 acc = zero4();
@@ -610,12 +700,12 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   for (int s = 0; s < NC; ++s) {
     const int c = NC - 1 - s, b = s & 1;
     if (wave == 0) {
-      float* dSe = ws.dSx + ((size_t)bh * NC + c) * D * D;
+      const SplitMat<T> dSe = SplitMat<T>::make(ws.dSx, ws.nS);
+      const size_t se0 = ((size_t)bh * NC + c) * D * D + col0 + n;
 #pragma unroll
       for (int tj = 0; tj < NKT; ++tj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dSe[(size_t)(16 * tj + 4 * g + e) * D + col0 + n] = dS[tj][e];
+        for (int e = 0; e < 4; ++e) dSe.put(se0 + (size_t)(16 * tj + 4 * g + e) * D, dS[tj][e]);
       const float* gsc = gsb[b];
       const float gC = gsc[C - 1];
       const float gamC = kGated ? __expf(gC) : 1.f;
@@ -643,7 +733,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       if constexpr (kErase) {
         const Frag2<T> bU[2] = {frag2_from_acc<T>(dU[0], dU[1]), frag2_from_acc<T>(dU[2], dU[3])};
         f32x4 dR[4];
-        float* dRg = ws.dR + ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
+        const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
+        const size_t r0 = ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           dR[ti] = zero4();
@@ -653,7 +744,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti + 4 * g + e;
-            dRg[(size_t)r * D] = dR[ti][e];
+            dRm.put(r0 + (size_t)r * D, dR[ti][e]);
             if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
           }
         }
@@ -714,6 +805,73 @@ __device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
   tj = t - ti * (ti + 1) / 2;
 }
 
+// One column tile of the C x D phase, staged in LDS by all waves: the 16
+// rows of S and dS' (B^T operands: hi and lo planes for bf16 inputs) and
+// the 16 columns of K and Q (B operands of the products over the chunk, and
+// the row dots).  Loaded into registers one tile ahead, stored after the
+// barrier that ends the previous tile.
+template <typename T, int D>
+struct ColStage {
+  static constexpr bool kSplit = IsBf16<T>::value;
+  static constexpr int PE = 16 / sizeof(T);
+  static constexpr int NP = kSplit ? 4 : 2;       // S hi, (S lo), dS hi, (dS lo)
+  static constexpr int LDB = D + PE;              // row pitch of the S / dS' planes
+  static constexpr int LDQ = 16 + PE;             // row pitch of the K / Q columns
+  static constexpr int VPRD = D / PE;             // 16-byte vectors per state row
+  static constexpr int NS = NP * 16 * VPRD;       // state vectors (1024)
+  static constexpr int IS = NS / kThreads;
+  static constexpr int VV = 16 / PE;              // vectors per 16-column token row
+  static constexpr int NQ = 2 * C * VV;
+  static constexpr int IQ = (NQ + kThreads - 1) / kThreads;
+  u32x4 sx[IS], qx[IQ];
+
+  __device__ __forceinline__ void load(const SplitMat<T>& Sm, const SplitMat<T>& dSm, size_t s0,
+                                       const T* kc, const T* qc, int nrows, int cb0, int t) {
+#pragma unroll
+    for (int i = 0; i < IS; ++i) {
+      const int p = t + i * kThreads;
+      const int pl = p / (16 * VPRD), rem = p % (16 * VPRD);
+      const size_t o = s0 + (size_t)(cb0 + rem / VPRD) * D + (rem % VPRD) * PE;
+      const T* src;
+      if constexpr (kSplit) {
+        const SplitMat<T>& m = pl < 2 ? Sm : dSm;
+        src = m.p + (pl & 1 ? m.plane : 0) + o;
+      } else {
+        src = (pl == 0 ? Sm.p : dSm.p) + o;
+      }
+      sx[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < IQ; ++i) {
+      const int p = min(t + i * kThreads, NQ - 1);
+      const int m = p / (C * VV), rem = p % (C * VV), r = rem / VV;
+      const T* base = m == 0 ? kc : qc;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(base + (size_t)min(r, nrows - 1) * D +
+                                                      cb0 + (rem % VV) * PE);
+      qx[i] = r < nrows ? x : z;
+    }
+  }
+
+  __device__ __forceinline__ void store(T* Sb, T* Kc, T* Qc, int t) const {
+#pragma unroll
+    for (int i = 0; i < IS; ++i) {
+      const int p = t + i * kThreads;
+      const int pl = p / (16 * VPRD), rem = p % (16 * VPRD);
+      *reinterpret_cast<u32x4*>(Sb + (pl * 16 + rem / VPRD) * LDB + (rem % VPRD) * PE) = sx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < IQ; ++i) {
+      const int p = t + i * kThreads;
+      if (p < NQ) {
+        const int m = p / (C * VV), rem = p % (C * VV);
+        T* dst = m == 0 ? Kc : Qc;
+        *reinterpret_cast<u32x4*>(dst + (rem / VV) * LDQ + (rem % VV) * PE) = qx[i];
+      }
+    }
+  }
+};
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -722,7 +880,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     int L) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
+  constexpr bool kSplit = IsBf16<T>::value;
   constexpr int NKB = D / 32, NCT = D / 16;
+  using CS = ColStage<T, D>;
   const int NC = ws.NC;
   const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const int tid = threadIdx.x;
@@ -736,10 +896,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   const T* kc = k + row0 * D;
   const T* vc = v + row0 * D;
   const T* dOc = dout + row0 * D;
-  const float* Uc = kErase ? ws.U + urow0 * D : nullptr;
-  const float* dRc = kErase ? ws.dR + urow0 * D : nullptr;
-  const float* Se = ws.Sent + cid * D * D;
-  const float* dSe = ws.dSx + cid * D * D;
+  const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
+  const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
+  const SplitMat<T> Sm = SplitMat<T>::make(ws.Sent, ws.nS);
+  const SplitMat<T> dSm = SplitMat<T>::make(ws.dSx, ws.nS);
+  const size_t u0 = urow0 * D, s0 = cid * D * D;
 
   __shared__ __attribute__((aligned(16))) float gs[C];
   __shared__ __attribute__((aligned(16))) float gam[C];
@@ -747,30 +908,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ __attribute__((aligned(16))) float bs[C];
   __shared__ __attribute__((aligned(16))) float Em[C * LDC];
   __shared__ __attribute__((aligned(16))) float Hm[kErase ? C * LDC : 4];
-  __shared__ __attribute__((aligned(16))) float GG[C * LDC];
-  __shared__ float dgam[C], dfv[C], dbe[C], rsum[C], csum[C];
+  __shared__ __attribute__((aligned(16))) T Sb[CS::NP * 16 * CS::LDB];
+  __shared__ __attribute__((aligned(16))) T Kcs[C * CS::LDQ];
+  __shared__ __attribute__((aligned(16))) T Qcs[C * CS::LDQ];
+  __shared__ float dgam[C], dfv[C], dbe[C], rsum[C], csum[C], vdr[C];
   __shared__ float red[kWaves];
 
-  // <dS', S> (this thread's share), every load issued before the sum
-  float dgc_part = 0.f;
-  {
-    constexpr int NV4 = D * D / 4 / kThreads;
-    const f32x4* a4 = reinterpret_cast<const f32x4*>(dSe);
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(Se);
-    f32x4 xa[NV4], xs[NV4];
-#pragma unroll
-    for (int i = 0; i < NV4; ++i) {
-      xa[i] = a4[tid + i * kThreads];
-      xs[i] = s4[tid + i * kThreads];
-    }
-#pragma unroll
-    for (int i = 0; i < NV4; ++i)
-      dgc_part += xa[i][0] * xs[i][0] + xa[i][1] * xs[i][1] + xa[i][2] * xs[i][2] +
-                  xa[i][3] * xs[i][3];
-  }
+  // the first column tile's loads go out first
+  CS st;
+  st.load(Sm, dSm, s0, kc, qc, nrows, 0, tid);
+
   for (int p = tid; p < C * LDC; p += kThreads) {
     Em[p] = 0.f;
-    GG[p] = 0.f;
     if constexpr (kErase) Hm[p] = 0.f;
   }
   if (tid < C) {
@@ -779,11 +928,32 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     gam[tid] = kGated ? __expf(gg) : 1.f;
     bs[tid] = (kErase && tid < nrows) ? beta[row0 + tid] : 0.f;
     dbe[tid] = 0.f;
+    rsum[tid] = 0.f;
+    csum[tid] = 0.f;
+  }
+  if constexpr (kErase) {
+    // V_r . dR_r: four threads per row
+    const int r = tid / 4, q4 = tid % 4;
+    constexpr int W = D / 4;
+    float x = 0.f;
+    if (r < nrows) {
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const int cc = q4 * W + j;
+        x += to_f32(vc[(size_t)r * D + cc]) * dRm.get(u0 + (size_t)r * D + cc);
+      }
+    }
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    if (q4 == 0) vdr[r] = x;
   }
   __syncthreads();
   if (tid < C) fs[tid] = kGated ? __expf(gs[C - 1] - gs[tid]) : 1.f;
 
-  // C x C products on the lower tiles: scores, dO U^T, and (erase) K K^T, dR U^T
+  // C x C products on the lower tiles: scores, dO U^T, and (erase) K K^T,
+  // dR U^T; GG = (dO U^T) * P + dA * A goes straight into its row and
+  // column sums
+#pragma unroll 1
   for (int t = wave; t < 10; t += kWaves) {
     int ti, tj;
     lower_tile(t, ti, tj);
@@ -796,19 +966,19 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
       mma(chunk_row<T, D>(qc, ra, nrows, 32 * kb, g), bk, qk);
       if constexpr (kErase) {
         mma(chunk_row<T, D>(kc, ra, nrows, 32 * kb, g), bk, kk);
-        const Frag2<T> bu = frag2_row<T>(Uc + (size_t)rb * D + 32 * kb, g);
+        const Frag2<T> bu = Um.row(u0 + (size_t)rb * D + 32 * kb, g);
         mma_ab2(ado, bu, dp);
-        mma_a2b2(frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g), bu, dru);
+        mma_a2b2(dRm.row(u0 + (size_t)ra * D + 32 * kb, g), bu, dru);
       } else {
         mma(ado, chunk_row<T, D>(vc, rb, nrows, 32 * kb, g), dp);
       }
     }
+    float csp = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ti + 4 * g + e, i = 16 * tj + n;
       const float Gm = r >= i ? (kGated ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
-      const float P = qk[e] * Gm;
-      float gg = dp[e] * P;
+      float gg = dp[e] * qk[e] * Gm;
       Em[r * LDC + i] = dp[e] * Gm;
       if constexpr (kErase) {
         const float Kg = r > i ? kk[e] * Gm : 0.f;
@@ -818,108 +988,122 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
         const float part = sum16(dA * Kg);
         if (n == 0) atomicAdd(&dbe[r], part);
       }
-      GG[r * LDC + i] = gg;
+      const float rs = sum16(gg);
+      if (n == 0) atomicAdd(&rsum[r], rs);
+      csp += gg;
     }
+    csp += __shfl_xor(csp, 16);
+    csp += __shfl_xor(csp, 32);
+    if (g == 0) atomicAdd(&csum[16 * tj + n], csp);
   }
   __syncthreads();
 
-  // C x D products: wave w owns the rows 16 w .. 16 w + 15
-  {
-    const int ti = wave, ra = 16 * ti + n;
-    Frag2<T> aE[2], aEt[2], aG[2];
+  // C x D products: wave w owns the rows 16 w .. 16 w + 15; the column
+  // tiles go by in order, staged in LDS for all four waves
+  const int ti = wave, ra = 16 * ti + n;
+  Frag2<T> aE[2], aEt[2], aG[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      aE[kb] = frag2_row<T>(Em + ra * LDC + 32 * kb, g);
-      aEt[kb] = frag2_col<T>(Em + 32 * kb * LDC + ra, LDC, g);
-      if constexpr (kErase) {
+  for (int kb = 0; kb < 2; ++kb) {
+    aE[kb] = frag2_rowx<T>(Em + ra * LDC + 32 * kb, g);
+    aEt[kb] = frag2_col<T>(Em + 32 * kb * LDC + ra, LDC, g);
+    if constexpr (kErase) {
+      float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 32 * kb + kidx(g, j);
-          aG[kb].set(j, Hm[ra * LDC + i] + Hm[i * LDC + ra]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * kb + kidx(g, j);
+        x[j] = Hm[ra * LDC + i] + Hm[i * LDC + ra];
       }
+      aG[kb] = frag2_of<T>(x);
     }
-    Frag<T> aDO[NKB], aV[NKB];
+  }
+  Frag<T> aDO[NKB], aV[NKB];
+  Frag2<T> aDR[NKB], aU[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
+    if constexpr (kErase) {
+      aDR[kb] = dRm.row(u0 + (size_t)ra * D + 32 * kb, g);
+      aU[kb] = Um.row(u0 + (size_t)ra * D + 32 * kb, g);
+    } else {
+      aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
+    }
+  }
+  float dgc_part = 0.f;
+  float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
+        rdb[4] = {0.f, 0.f, 0.f, 0.f};
+  const T* Sp[CS::NP];
+#pragma unroll
+  for (int pl = 0; pl < CS::NP; ++pl) Sp[pl] = Sb + (pl * 16 + n) * CS::LDB;
+#pragma unroll 1
+  for (int cj = 0; cj < NCT; ++cj) {
+    const int cb = 16 * cj + n;
+    if (cj > 0) __syncthreads();          // the previous tile's LDS reads are done
+    st.store(Sb, Kcs, Qcs, tid);
+    __syncthreads();
+    if (cj + 1 < NCT) st.load(Sm, dSm, s0, kc, qc, nrows, 16 * (cj + 1), tid);
+    f32x4 m1 = zero4(), m2 = zero4(), m3 = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
-      if constexpr (!kErase) aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
+      Frag2<T> bS, bdS;
+      bS.hi = frag_row(Sp[0] + 32 * kb, g);
+      if constexpr (kSplit) {
+        bS.lo = frag_row(Sp[1] + 32 * kb, g);
+        bdS.hi = frag_row(Sp[2] + 32 * kb, g);
+        bdS.lo = frag_row(Sp[3] + 32 * kb, g);
+      } else {
+        bdS.hi = frag_row(Sp[1] + 32 * kb, g);
+      }
+      // <dS', S>, each column tile by one wave
+      if ((cj & 3) == wave) dgc_part += frag_dot(bS, bdS);
+      mma_ab2(aDO[kb], bS, m1);
+      if constexpr (kErase) {
+        mma_a2b2(aDR[kb], bS, m2);
+        mma_a2b2(aU[kb], bdS, m3);
+      } else {
+        mma_ab2(aV[kb], bdS, m3);
+      }
     }
-    float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
-          rdb[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int cj = 0; cj < NCT; ++cj) {
-      const int cb = 16 * cj + n;
-      f32x4 m1 = zero4(), m2 = zero4(), m3 = zero4();
+    f32x4 ek = zero4(), etq = zero4(), gk = zero4();
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const Frag2<T> bS = frag2_row<T>(Se + (size_t)cb * D + 32 * kb, g);
-        const Frag2<T> bdS = frag2_row<T>(dSe + (size_t)cb * D + 32 * kb, g);
-        mma_ab2(aDO[kb], bS, m1);
-        if constexpr (kErase) {
-          // dR and U rows re-read per column tile (cache hits): fewer live registers
-          mma_a2b2(frag2_row<T>(dRc + (size_t)ra * D + 32 * kb, g), bS, m2);
-          mma_a2b2(frag2_row<T>(Uc + (size_t)ra * D + 32 * kb, g), bdS, m3);
-        } else {
-          mma_ab2(aV[kb], bdS, m3);
-        }
-      }
-      f32x4 ek = zero4(), etq = zero4(), gk = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const Frag<T> bK = chunk_col<T, D>(kc, 32 * kb, cb, nrows, g);
-        mma_a2b(aE[kb], bK, ek);
-        mma_a2b(aEt[kb], chunk_col<T, D>(qc, 32 * kb, cb, nrows, g), etq);
-        if constexpr (kErase) mma_a2b(aG[kb], bK, gk);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * ti + 4 * g + e;
-        const int rr = min(r, nrows - 1);
-        const bool ok = r < nrows;
-        const float qv = ok ? to_f32(qc[(size_t)rr * D + cb]) : 0.f;
-        const float kv = ok ? to_f32(kc[(size_t)rr * D + cb]) : 0.f;
-        float dQ = gam[r] * m1[e] + ek[e];
-        float dK = fs[r] * m3[e] + etq[e];
-        rdg[e] += qv * m1[e];
-        rdf[e] += kv * m3[e];
-        if constexpr (kErase) {
-          dK += gk[e] - bs[r] * gam[r] * m2[e];
-          rdg[e] -= bs[r] * kv * m2[e];
-          const float vv = ok ? to_f32(vc[(size_t)rr * D + cb]) : 0.f;
-          rdb[e] += vv * dRc[(size_t)r * D + cb] - gam[r] * kv * m2[e];
-        }
-        if (ok) {
-          dq[(row0 + r) * D + cb] = dQ;
-          dk[(row0 + r) * D + cb] = dK;
-        }
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const Frag<T> bK = frag_col(Kcs + 32 * kb * CS::LDQ + n, CS::LDQ, g);
+      mma_a2b(aE[kb], bK, ek);
+      mma_a2b(aEt[kb], frag_col(Qcs + 32 * kb * CS::LDQ + n, CS::LDQ, g), etq);
+      if constexpr (kErase) mma_a2b(aG[kb], bK, gk);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ti + 4 * g + e;
-      const float a = sum16(rdg[e]), b = sum16(rdf[e]), cc = sum16(rdb[e]);
-      if (n == 0) {
-        dgam[r] = a;
-        dfv[r] = b;
-        dbe[r] += cc;
+      const float qv = to_f32(Qcs[r * CS::LDQ + n]);
+      const float kv = to_f32(Kcs[r * CS::LDQ + n]);
+      float dQ = gam[r] * m1[e] + ek[e];
+      float dK = fs[r] * m3[e] + etq[e];
+      rdg[e] += qv * m1[e];
+      rdf[e] += kv * m3[e];
+      if constexpr (kErase) {
+        dK += gk[e] - bs[r] * gam[r] * m2[e];
+        rdg[e] -= bs[r] * kv * m2[e];
+        rdb[e] -= gam[r] * kv * m2[e];
+      }
+      if (r < nrows) {
+        dq[(row0 + r) * D + cb] = dQ;
+        dk[(row0 + r) * D + cb] = dK;
       }
     }
   }
-
   {
     const float acc = sum64(dgc_part);
     if (lane == 0) red[wave] = acc;
   }
-  __syncthreads();
-  if (tid < C) {
-    float s = 0.f;
-    for (int i = 0; i < C; ++i) s += GG[tid * LDC + i];
-    rsum[tid] = s;
-  } else if (tid < 2 * C) {
-    const int i = tid - C;
-    float s = 0.f;
-    for (int r = 0; r < C; ++r) s += GG[r * LDC + i];
-    csum[i] = s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 16 * ti + 4 * g + e;
+    const float a = sum16(rdg[e]), b = sum16(rdf[e]), cc = sum16(rdb[e]);
+    if (n == 0) {
+      dgam[r] = a;
+      dfv[r] = b;
+      dbe[r] += cc + (kErase ? vdr[r] : 0.f);
+    }
   }
   __syncthreads();
   if (wave == 0) {
