@@ -77,6 +77,8 @@ struct BwdWs {
   float* U;     // [BH, NC * C, D]  T R (erase modes)
   float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
   float* dR;    // [BH, NC * C, D]  T^T dU (erase modes)
+  float* X1;    // [BH, NC * C, D]  P^T dO
+  float* X2;    // [BH, NC, D, D]   Q^T diag(gam) dO
   int NC;
   size_t nS;    // elements of Sent and dSx
   size_t nU;    // elements of U and dR
@@ -88,17 +90,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const BwdArgs& a, BwdWs* ws) {
   const size_t BH = (size_t)a.B * a.H, NC = ((size_t)a.L + C - 1) / C, D = a.d;
   const bool erase = mode_erase(a.mode);
-  const size_t n[7] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * C * C,
+  const size_t n[9] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * C * C,
                        BH * NC * D * D, erase ? BH * NC * C * D : 0, BH * NC * D * D,
-                       erase ? BH * NC * C * D : 0};
-  float* p[7];
+                       erase ? BH * NC * C * D : 0, BH * NC * C * D, BH * NC * D * D};
+  float* p[9];
   size_t off = 0;
   char* base = static_cast<char*>(a.workspace);
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 9; ++i) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], (int)NC, n[3], n[4]};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], (int)NC, n[3], n[4]};
   return off;
 }
 
@@ -183,6 +185,11 @@ struct SplitMat<float> {
     f.hi = frag_row(p + i, g);
     return f;
   }
+  // x[0..7] to elements i .. i + 7 (i a multiple of 8)
+  __device__ __forceinline__ void put8(size_t i, const float (&x)[8]) const {
+    *reinterpret_cast<f32x4*>(p + i) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + i + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
 };
 
 template <>
@@ -206,6 +213,11 @@ struct SplitMat<__bf16> {
     f.lo = frag_row(p + plane + i, g);
     return f;
   }
+  __device__ __forceinline__ void put8(size_t i, const float (&x)[8]) const {
+    const Frag2<__bf16> f = frag2_pack(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    *reinterpret_cast<u32x4*>(p + i) = __builtin_bit_cast(u32x4, f.hi.v);
+    *reinterpret_cast<u32x4*>(p + plane + i) = __builtin_bit_cast(u32x4, f.lo.v);
+  }
 };
 
 // acc += a * b with a split and b exact
@@ -213,6 +225,30 @@ template <typename T>
 __device__ __forceinline__ void mma_a2b(const Frag2<T>& a, const Frag<T>& b, f32x4& acc) {
   if constexpr (IsBf16<T>::value) mma(a.lo, b, acc);
   mma(a.hi, b, acc);
+}
+
+// A float tile of R rows x 16 columns handed from a walk's chain wave to
+// its staging waves through LDS, kept transposed ([16][R + 4]) so that a
+// chain lane writes its four rows of one accumulator tile with one 16-byte
+// write; the staging waves then store it to a workspace matrix (row pitch D,
+// the tile's 16 columns) in that matrix's form, 8 columns per thread.
+template <int R>
+__device__ __forceinline__ void tile_put(float* X, const f32x4* acc, int g, int n) {
+#pragma unroll
+  for (int t = 0; t < R / 16; ++t)
+    *reinterpret_cast<f32x4*>(X + n * (R + 4) + 16 * t + 4 * g) = acc[t];
+}
+
+template <typename T, int D, int R>
+__device__ __forceinline__ void tile_flush(const float* X, const SplitMat<T>& M, size_t base,
+                                           int t, int nt) {
+  for (int p = t; p < 2 * R; p += nt) {
+    const int r = p / 2, c0 = 8 * (p % 2);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = X[(c0 + j) * (R + 4) + r];
+    M.put8(base + (size_t)r * D + c0, x);
+  }
 }
 
 // sum_j a_j b_j of two split operands (hi + lo each)
@@ -265,7 +301,7 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 // three staging waves in one batch (every load issued, at clamped indices,
 // before the first LDS write), then written to one half of the walk's
 // double buffer.  Rows past the end of the sequence read as zero.
-template <typename T, int D, bool ERASE, bool WITH_V>
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false>
 struct ChunkStage {
   static constexpr int NT = kThreads - kWave;
   static constexpr int PE = 16 / sizeof(T);
@@ -278,16 +314,34 @@ struct ChunkStage {
   static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
   static constexpr int NV = C * VV;
   static constexpr int IV = WITH_V ? (NV + NT - 1) / NT : 1;
+  static constexpr int NX1 = C * 4, NX2 = D * 4;  // 16-float rows of X1, X2: 4 vectors
+  static constexpr int IX1 = WITH_X ? (NX1 + NT - 1) / NT : 1;
+  static constexpr int IX2 = WITH_X ? (NX2 + NT - 1) / NT : 1;
   u32x4 kx[IK];
   f32x4 tx[IT];
   u32x4 vx[IV];
+  f32x4 x1[IX1], x2[IX2];
   float gx, bx;
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        const float* __restrict__ beta, const float* Tg,
                                        const float* gg, size_t row0, int nrows, int col0,
-                                       int t) {
+                                       int t, const float* X1g = nullptr,
+                                       const float* X2g = nullptr) {
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (WITH_X) {
+      // 16 columns (col0 ..) of the chunk's X1 [C, D] and X2 [D, D]
+#pragma unroll
+      for (int i = 0; i < IX1; ++i) {
+        const int p = min(t + i * NT, NX1 - 1);
+        x1[i] = *reinterpret_cast<const f32x4*>(X1g + (size_t)(p / 4) * D + col0 + 4 * (p % 4));
+      }
+#pragma unroll
+      for (int i = 0; i < IX2; ++i) {
+        const int p = min(t + i * NT, NX2 - 1);
+        x2[i] = *reinterpret_cast<const f32x4*>(X2g + (size_t)(p / 4) * D + col0 + 4 * (p % 4));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
@@ -318,7 +372,20 @@ struct ChunkStage {
   }
 
   __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* bsb,
-                                        int t) const {
+                                        int t, float* X1b = nullptr,
+                                        float* X2b = nullptr) const {
+    if constexpr (WITH_X) {
+#pragma unroll
+      for (int i = 0; i < IX1; ++i) {
+        const int p = t + i * NT;
+        if (p < NX1) *reinterpret_cast<f32x4*>(X1b + (p / 4) * LDX + 4 * (p % 4)) = x1[i];
+      }
+#pragma unroll
+      for (int i = 0; i < IX2; ++i) {
+        const int p = t + i * NT;
+        if (p < NX2) *reinterpret_cast<f32x4*>(X2b + (p / 4) * LDX + 4 * (p % 4)) = x2[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int p = t + i * NT;
@@ -471,6 +538,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
   __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
+  __shared__ __attribute__((aligned(16))) float SxT[2][16 * (D + 4)];            // S entering
+  __shared__ __attribute__((aligned(16))) float UxT[2][kErase ? 16 * (C + 4) : 4];  // U
   __shared__ __attribute__((aligned(16))) float gsb[2][C];
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
 
@@ -483,16 +552,18 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   const int NC = ws.NC;
   const size_t NCC = (size_t)NC * C;
 
-  // chunk c's operands into buffer b (waves 1-3)
-  auto stage = [&](int c, int b) {
+  // Waves 1-3 stage the chain's operands: chunk c's loads go out during the
+  // step two before its use and land in LDS during the step before it (the
+  // barriers wait for LDS traffic only, so the loads stay in flight).
+  ChunkStage<T, D, kErase, true> st;
+  auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = (size_t)bh * L + (size_t)c * C;
     const size_t cid = (size_t)bh * NC + c;
-    ChunkStage<T, D, kErase, true> st;
     st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
             tid - kWave);
-    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], bsb[b], tid - kWave);
   };
+  auto store = [&](int b) { st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], bsb[b], tid - kWave); };
 
   f32x4 S[NKT];
   if (wave == 0) {
@@ -503,18 +574,41 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
       for (int e = 0; e < 4; ++e)
         S[tj][e] = S0 ? S0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
   }
-  if (wave != 0) stage(0, 0);
+  if (wave != 0) {
+    load(0);
+    store(0);
+    load(min(1, NC - 1));
+  }
   __syncthreads();
 
+  // each role runs its own loop (one barrier per chunk in both), so the
+  // staging loads meet no other role's registers and are not waited for early
+  if (wave != 0) {
+    // the state and U tiles of chunk c, handed over by the chain, go to the
+    // workspace during the next step
+    const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
+    const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
+    auto flush = [&](int c) {
+      const int b = c & 1;
+      tile_flush<T, D, D>(SxT[b], Se, ((size_t)bh * NC + c) * D * D + col0, tid - kWave,
+                          kThreads - kWave);
+      if constexpr (kErase)
+        tile_flush<T, D, C>(UxT[b], Um, ((size_t)bh * NCC + (size_t)c * C) * D + col0,
+                            tid - kWave, kThreads - kWave);
+    };
+    for (int c = 0; c < NC; ++c) {
+      if (c >= 1) flush(c - 1);
+      if (c + 1 < NC) store((c & 1) ^ 1);
+      load(min(c + 2, NC - 1));
+      __syncthreads();
+    }
+    flush(NC - 1);
+    return;
+  }
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
-    if (wave == 0) {
-      const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
-      const size_t se0 = ((size_t)bh * NC + c) * D * D + col0 + n;
-#pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Se.put(se0 + (size_t)(16 * tj + 4 * g + e) * D, S[tj][e]);
+    {
+      tile_put<D>(SxT[b], S, g, n);
       const float* gsc = gsb[b];
       const float gC = gsc[C - 1];
       const float gamC = kGated ? __expf(gC) : 1.f;
@@ -548,17 +642,14 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
         }
         const Frag2<T> bR[2] = {frag2_from_acc<T>(R[0], R[1]), frag2_from_acc<T>(R[2], R[3])};
         f32x4 U[4];
-        const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
-        const size_t u0 = ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           U[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
             mma_a2b2(frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g), bR[kb], U[ti]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Um.put(u0 + (size_t)(16 * ti + 4 * g + e) * D, U[ti][e]);
         }
+        tile_put<C>(UxT[b], U, g, n);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           bX[kb] = frag2_from_acc_scaled<T>(U[2 * kb], U[2 * kb + 1], flo[kb], fhi[kb]);
@@ -583,10 +674,80 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
         for (int kb = 0; kb < 2; ++kb)
           mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bX[kb], S[tj]);
       }
-    } else if (c + 1 < NC) {
-      stage(c + 1, b ^ 1);
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------- dS-independent products
+// Per chunk-head (parallel): X1 = P^T dO [C, dv] and X2 = Q^T diag(gam) dO
+// [dk, dv], the two terms of the reverse walk that do not depend on the
+// state gradient.  Q^T and dO^T are staged transposed in LDS so that every
+// operand is read along its contraction index.
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kThreads) void bwd_dprep_kernel(const T* __restrict__ q,
+                                                             const T* __restrict__ dout,
+                                                             BwdWs ws, int L) {
+  constexpr bool kGated = mode_decay(MODE);
+  constexpr int PE = 16 / sizeof(T);
+  constexpr int LDT = C + PE;         // row pitch of the transposed tiles
+  constexpr int VPR = D / PE;
+  constexpr int NT16 = D / 16;        // 16-wide tiles over d
+  const int NC = ws.NC;
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
+  const int nrows = min(C, L - c * C);
+  const size_t row0 = (size_t)bh * L + (size_t)c * C;
+  const size_t cid = (size_t)bh * NC + c;
+
+  __shared__ __attribute__((aligned(16))) T QT[D * LDT];
+  __shared__ __attribute__((aligned(16))) T OT[D * LDT];
+  __shared__ __attribute__((aligned(16))) float gam[C];
+
+  // Q and dO rows, transposed into LDS (rows past the end as zero)
+  for (int p = tid; p < 2 * C * VPR; p += kThreads) {
+    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem / VPR, c0 = (rem % VPR) * PE;
+    const T* src = (m == 0 ? q : dout) + (row0 + min(r, nrows - 1)) * D + c0;
+    T* dst = m == 0 ? QT : OT;
+#pragma unroll
+    for (int j = 0; j < PE; ++j) dst[(c0 + j) * LDT + r] = r < nrows ? src[j] : T(0.f);
+  }
+  if (tid < C) gam[tid] = kGated ? __expf(ws.g[cid * C + tid]) : 1.f;
+  __syncthreads();
+
+  // X1 tiles (rows i of P^T, columns j of dO): NT16 x 4; X2 tiles: NT16 x NT16
+  constexpr int N1 = 4 * NT16, N2 = NT16 * NT16;
+  for (int t = wave; t < N1 + N2; t += kWaves) {
+    f32x4 acc = zero4();
+    int r0, c0;
+    float* out;
+    if (t < N1) {
+      const int ti = t / NT16, tj = t % NT16;
+      r0 = 16 * ti;
+      c0 = 16 * tj;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma_a2b(frag2_rowx<T>(ws.Pt + (cid * C + r0 + n) * C + 32 * kb, g),
+                frag_row(OT + (c0 + n) * LDT + 32 * kb, g), acc);
+      out = ws.X1 + (cid * C + r0) * D + c0;
+    } else {
+      const int ti = (t - N1) / NT16, tj = (t - N1) % NT16;
+      r0 = 16 * ti;
+      c0 = 16 * tj;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<T> o = frag_row(OT + (c0 + n) * LDT + 32 * kb, g);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = to_f32(o.v[j]) * gam[32 * kb + kidx(g, j)];
+        mma_ab2(frag_row(QT + (r0 + n) * LDT + 32 * kb, g), frag2_of<T>(x), acc);
+      }
+      out = ws.X2 + (cid * D + r0) * D + c0;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(size_t)(4 * g + e) * D + n] = acc[e];
   }
 }
 
@@ -606,6 +767,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
   __shared__ __attribute__((aligned(16))) float X1[2][C * LDX];   // P^T dO (16 columns)
   __shared__ __attribute__((aligned(16))) float X2[2][D * LDX];   // Q^T diag(gam) dO
+  __shared__ __attribute__((aligned(16))) float dSxT[2][16 * (D + 4)];             // dS'
+  __shared__ __attribute__((aligned(16))) float dRxT[2][kErase ? 16 * (C + 4) : 4];  // dR
   __shared__ __attribute__((aligned(16))) float gsb[2][C];
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
 
@@ -618,71 +781,19 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   const int NC = ws.NC;
   const size_t NCC = (size_t)NC * C;
 
-  // chunk c's operands and its two dS-independent products into buffer b
-  // (waves 1-3): wave 1 forms X1 = P^T dO, waves 2 and 3 half of X2 = Q^T
-  // diag(gam) dO each, for this tile's 16 columns of dO.  Every global load
-  // of the step is issued before the first LDS write.
-  auto side = [&](int c, int b) {
+  // Waves 1-3 stage the chain's operands of each chunk -- K, T, the gates and
+  // the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO (formed
+  // in parallel beforehand) -- two chunks ahead, as in the forward walk.
+  ChunkStage<T, D, kErase, false, true> st;
+  auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = (size_t)bh * L + (size_t)c * C;
     const size_t cid = (size_t)bh * NC + c;
-    const int t = tid - kWave, wv = wave - 1;
-    ChunkStage<T, D, kErase, false> st;
     st.load(k, nullptr, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0,
-            nrows, 0, t);
-    // dO columns col0 .. col0 + 15 as B operands (rows 32 kb + kidx(g, j))
-    Frag<T> dof[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dof[kb] = chunk_col<T, D>(dout + row0 * D, 32 * kb, col0 + n, nrows, g);
-    if (wv == 0) {
-      Frag2<T> ap[4][2];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          ap[tt][kb] = frag2_rowx<T>(ws.Pt + (cid * C + 16 * tt + n) * C + 32 * kb, g);
-      st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma_a2b(ap[tt][kb], dof[kb], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X1[b][(16 * tt + 4 * g + e) * LDX + n] = acc[e];
-      }
-    } else {
-      constexpr int NX = NKT / 2;
-      const int tj0 = (wv - 1) * NX;
-      float gm[2][8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) gm[kb][j] = ws.g[cid * C + 32 * kb + kidx(g, j)];
-      Frag<T> aq[NX][2];
-#pragma unroll
-      for (int u = 0; u < NX; ++u)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          aq[u][kb] = chunk_col<T, D>(q + row0 * D, 32 * kb, 16 * (tj0 + u) + n, nrows, g);
-      st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], t);
-      Frag2<T> dog[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = to_f32(dof[kb].v[j]) * (kGated ? __expf(gm[kb][j]) : 1.f);
-        dog[kb] = frag2_of<T>(x);
-      }
-#pragma unroll
-      for (int u = 0; u < NX; ++u) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) mma_ab2(aq[u][kb], dog[kb], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X2[b][(16 * (tj0 + u) + 4 * g + e) * LDX + n] = acc[e];
-      }
-    }
+            nrows, col0, tid - kWave, ws.X1 + cid * C * D, ws.X2 + cid * D * D);
+  };
+  auto store = [&](int b) {
+    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], tid - kWave, X1[b], X2[b]);
   };
 
   f32x4 dS[NKT];
@@ -694,18 +805,39 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       for (int e = 0; e < 4; ++e)
         dS[tj][e] = dS_final ? dS_final[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
   }
-  if (wave != 0) side(NC - 1, 0);
+  if (wave != 0) {
+    load(NC - 1);
+    store(0);
+    load(max(NC - 2, 0));
+  }
   __syncthreads();
+  if (wave != 0) {
+    // dS' and dR of the chunk of step s, handed over by the chain, go to the
+    // workspace during step s + 1
+    const SplitMat<T> dSe = SplitMat<T>::make(ws.dSx, ws.nS);
+    const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
+    auto flush = [&](int s) {
+      const int c = NC - 1 - s, b = s & 1;
+      tile_flush<T, D, D>(dSxT[b], dSe, ((size_t)bh * NC + c) * D * D + col0, tid - kWave,
+                          kThreads - kWave);
+      if constexpr (kErase)
+        tile_flush<T, D, C>(dRxT[b], dRm, ((size_t)bh * NCC + (size_t)c * C) * D + col0,
+                            tid - kWave, kThreads - kWave);
+    };
+    for (int s = 0; s < NC; ++s) {
+      if (s >= 1) flush(s - 1);
+      if (s + 1 < NC) store((s & 1) ^ 1);
+      load(max(NC - 3 - s, 0));
+      __syncthreads();
+    }
+    flush(NC - 1);
+    return;
+  }
 
   for (int s = 0; s < NC; ++s) {
     const int c = NC - 1 - s, b = s & 1;
-    if (wave == 0) {
-      const SplitMat<T> dSe = SplitMat<T>::make(ws.dSx, ws.nS);
-      const size_t se0 = ((size_t)bh * NC + c) * D * D + col0 + n;
-#pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dSe.put(se0 + (size_t)(16 * tj + 4 * g + e) * D, dS[tj][e]);
+    {
+      tile_put<D>(dSxT[b], dS, g, n);
       const float* gsc = gsb[b];
       const float gC = gsc[C - 1];
       const float gamC = kGated ? __expf(gC) : 1.f;
@@ -733,8 +865,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       if constexpr (kErase) {
         const Frag2<T> bU[2] = {frag2_from_acc<T>(dU[0], dU[1]), frag2_from_acc<T>(dU[2], dU[3])};
         f32x4 dR[4];
-        const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
-        const size_t r0 = ((size_t)bh * NCC + (size_t)c * C) * D + col0 + n;
+
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           dR[ti] = zero4();
@@ -744,10 +875,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti + 4 * g + e;
-            dRm.put(r0 + (size_t)r * D, dR[ti][e]);
             if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
           }
         }
+        tile_put<C>(dRxT[b], dR, g, n);
         // dS <- gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR
         Frag2<T> bR[2];
 #pragma unroll
@@ -784,12 +915,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
           for (int e = 0; e < 4; ++e)
             dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
       }
-    } else if (c > 0) {
-      side(c - 1, b ^ 1);
     }
     __syncthreads();
   }
-  if (wave == 0 && dS0) {
+  if (dS0) {
     const size_t sb = (size_t)bh * D * D;
 #pragma unroll
     for (int tj = 0; tj < NKT; ++tj)
@@ -1173,6 +1302,19 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
                        dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.beta, a.S0, ws, BH, a.L);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_bwd_dprep(const BwdArgs& a, hipStream_t st) {
+  BwdWs ws;
+  carve(a, &ws);
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
+  return dispatch(a, [&](auto t, auto d, auto m) {
+    using T = typename decltype(t)::type;
+    hipLaunchKernelGGL((bwd_dprep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
+                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+                       static_cast<const T*>(a.dout), ws, a.L);
     return hipGetLastError();
   });
 }

@@ -132,3 +132,20 @@ def test_chunk_bwd_state_gradient_chains_over_a_split():
         log(f"  {name}: split vs whole max|err| {err:.3e}")
         assert err <= 1e-4 * float(np.max(np.abs(ref)))
     assert_close("dS0", f64(first["dS0"]), f64(whole["dS0"]), "f32")
+
+
+def test_chunk_bwd_full_size_sampled():
+    """The long-context workload at full size (B=1, H=32, L=65536, d=128,
+    bf16), launched as the bench launches it; the float64 chunkwise backward
+    recomputes two sampled heads over the whole sequence (heads do not
+    interact)."""
+    w = workloads.WORKLOADS[4]
+    log(f"case chunk_bwd_full {w.name} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w, ds_std=0.02)
+    res = run_bwd(w, x, gr, w.mode)
+    hs = [0, w.H - 1]
+    sub = lambda d: {k: t[:, hs].contiguous() for k, t in d.items()}   # noqa: E731
+    ref = reference(sub(x), sub(gr), w.mode, chunked=True)
+    got = {k: (t[:, hs] if t is not None else None) for k, t in res.items()}
+    compare(got, ref, w.mode, "bf16")
