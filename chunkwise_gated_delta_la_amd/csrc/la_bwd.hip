@@ -297,7 +297,8 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 }
 
 // The chain operands of one chunk -- K rows, T (erase modes), 16 columns of
-// V (forward walk), the decays and beta -- read by the 192 threads of the
+// V (forward walk), the decays (as exp(g) and exp(g_C - g)) and beta -- read
+// by the 192 threads of the
 // three staging waves in one batch (every load issued, at clamped indices,
 // before the first LDS write), then written to one half of the walk's
 // double buffer.  Rows past the end of the sequence read as zero.
@@ -321,7 +322,7 @@ struct ChunkStage {
   f32x4 tx[IT];
   u32x4 vx[IV];
   f32x4 x1[IX1], x2[IX2];
-  float gx, bx;
+  float gx, gcx, bx;
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        const float* __restrict__ beta, const float* Tg,
@@ -366,13 +367,14 @@ struct ChunkStage {
     }
     const int tr = min(t, C - 1);
     gx = gg[tr];
+    gcx = gg[C - 1];
     float b = 0.f;
     if constexpr (ERASE) b = beta[row0 + min(tr, nrows - 1)];
     bx = tr < nrows ? b : 0.f;
   }
 
-  __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* bsb,
-                                        int t, float* X1b = nullptr,
+  __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* fsb,
+                                        float* bsb, int t, float* X1b = nullptr,
                                         float* X2b = nullptr) const {
     if constexpr (WITH_X) {
 #pragma unroll
@@ -417,7 +419,9 @@ struct ChunkStage {
       }
     }
     if (t < C) {
-      gsb[t] = gx;
+      // the decays the chain needs per row: gam = exp(g) and f = exp(g_C - g)
+      gsb[t] = __expf(gx);
+      fsb[t] = __expf(gcx - gx);
       bsb[t] = bx;
     }
   }
@@ -540,7 +544,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
   __shared__ __attribute__((aligned(16))) float SxT[2][16 * (D + 4)];            // S entering
   __shared__ __attribute__((aligned(16))) float UxT[2][kErase ? 16 * (C + 4) : 4];  // U
-  __shared__ __attribute__((aligned(16))) float gsb[2][C];
+  __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
+  __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
 
   const int tid = threadIdx.x;
@@ -563,7 +568,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
     st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
             tid - kWave);
   };
-  auto store = [&](int b) { st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], bsb[b], tid - kWave); };
+  auto store = [&](int b) {
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tid - kWave);
+  };
 
   f32x4 S[NKT];
   if (wave == 0) {
@@ -609,18 +616,21 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
     const int b = c & 1;
     {
       tile_put<D>(SxT[b], S, g, n);
-      const float* gsc = gsb[b];
-      const float gC = gsc[C - 1];
-      const float gamC = kGated ? __expf(gC) : 1.f;
+      const float* gmc = gsb[b];     // exp(g)
+      const float* fc = fsb[b];      // exp(g_C - g)
+      const float gamC = kGated ? gmc[C - 1] : 1.f;
       // decay factors f of the rows 32 kb + 4 g + e (lo) and 32 kb + 16 + 4 g + e (hi)
       float flo[2][4], fhi[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 4 * g);
+        const f32x4 c2 = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 16 + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          flo[kb][e] = kGated ? __expf(gC - gsc[32 * kb + 4 * g + e]) : 1.f;
-          fhi[kb][e] = kGated ? __expf(gC - gsc[32 * kb + 16 + 4 * g + e]) : 1.f;
+          flo[kb][e] = kGated ? a[e] : 1.f;
+          fhi[kb][e] = kGated ? c2[e] : 1.f;
         }
+      }
       Frag2<T> bX[2];
       if constexpr (kErase) {
         Frag2<T> bS[NKB];
@@ -636,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti + 4 * g + e;
-            const float gam = kGated ? __expf(gsc[r]) : 1.f;
+            const float gam = kGated ? gmc[r] : 1.f;
             R[ti][e] = bsb[b][r] * (Vb[b][r * LDX + n] - gam * ks[e]);
           }
         }
@@ -769,7 +779,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   __shared__ __attribute__((aligned(16))) float X2[2][D * LDX];   // Q^T diag(gam) dO
   __shared__ __attribute__((aligned(16))) float dSxT[2][16 * (D + 4)];             // dS'
   __shared__ __attribute__((aligned(16))) float dRxT[2][kErase ? 16 * (C + 4) : 4];  // dR
-  __shared__ __attribute__((aligned(16))) float gsb[2][C];
+  __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
+  __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
 
   const int tid = threadIdx.x;
@@ -793,7 +804,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             nrows, col0, tid - kWave, ws.X1 + cid * C * D, ws.X2 + cid * D * D);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], bsb[b], tid - kWave, X1[b], X2[b]);
+    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tid - kWave, X1[b],
+             X2[b]);
   };
 
   f32x4 dS[NKT];
@@ -838,9 +850,9 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
     const int c = NC - 1 - s, b = s & 1;
     {
       tile_put<D>(dSxT[b], dS, g, n);
-      const float* gsc = gsb[b];
-      const float gC = gsc[C - 1];
-      const float gamC = kGated ? __expf(gC) : 1.f;
+      const float* gmc = gsb[b];     // exp(g)
+      const float* fc = fsb[b];      // exp(g_C - g)
+      const float gamC = kGated ? gmc[C - 1] : 1.f;
       const int nrows = min(C, L - c * C);
       const size_t row0 = (size_t)bh * L + (size_t)c * C;
       Frag2<T> bS[NKB];
@@ -857,7 +869,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * ti + 4 * g + e;
-          const float f = kGated ? __expf(gC - gsc[r]) : 1.f;
+          const float f = kGated ? fc[r] : 1.f;
           dU[ti][e] = X1[b][r * LDX + n] + f * y[e];
         }
       }
@@ -887,8 +899,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int rl = 32 * kb + 4 * g + e, rh = rl + 16;
-            slo[e] = -bsb[b][rl] * (kGated ? __expf(gsc[rl]) : 1.f);
-            shi[e] = -bsb[b][rh] * (kGated ? __expf(gsc[rh]) : 1.f);
+            slo[e] = -bsb[b][rl] * (kGated ? gmc[rl] : 1.f);
+            shi[e] = -bsb[b][rh] * (kGated ? gmc[rh] : 1.f);
           }
           bR[kb] = frag2_from_acc_scaled<T>(dR[2 * kb], dR[2 * kb + 1], slo, shi);
         }
