@@ -40,10 +40,15 @@ KERNEL_SOURCES = {
     "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
+for _k in ("la_bwd_prep", "la_bwd_states", "la_bwd_dprep", "la_bwd_rev", "la_bwd_grads"):
+    KERNEL_SOURCES[_k] = ["la_bwd.hip", "la_device.hpp", "la_kernels.hpp"]
 # rocprofv3 kernel names -> library kernel names (chunk_kernel: float
 # inputs, chunk_pipe_kernel: bf16 inputs)
 KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
-                  "t_solve_kernel": "la_tsolve", "decode_kernel": "la_decode"}
+                  "t_solve_kernel": "la_tsolve", "decode_kernel": "la_decode",
+                  "bwd_prep_kernel": "la_bwd_prep", "bwd_states_kernel": "la_bwd_states",
+                  "bwd_dprep_kernel": "la_bwd_dprep", "bwd_rev_kernel": "la_bwd_rev",
+                  "bwd_grads_kernel": "la_bwd_grads"}
 T_BYTES_PER_CHUNK = 6 * 1024   # T operand fragments of one (b, h, chunk)
 
 
@@ -210,7 +215,7 @@ def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, com
     for sym, lib_name in KERNEL_SYMBOLS.items():
         fv = [v for k, vs in fetch.items() if sym in k for v in vs]
         wv = [v for k, vs in write.items() if sym in k for v in vs]
-        if not fv or not wv:
+        if not fv or not wv or lib_name not in workload:
             continue
         f_b = sorted(fv)[len(fv) // 2] * 1024.0 * sf
         w_b = sorted(wv)[len(wv) // 2] * 1024.0 * sw
@@ -218,8 +223,15 @@ def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, com
             "workload": workload[lib_name], "source_hash": source_hash(lib_name),
             "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
             "hbm_bytes_per_launch": round(f_b + w_b), "dispatches": len(fv)}
+    # kernels not in these runs keep their earlier records
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            old = json.load(fh).get("kernels", {})
+    except (OSError, ValueError):
+        old = {}
+    old.update(kernels)
     rec = {"calibration": {"copy_bytes": 1 << 30, "fetch_scale": sf, "write_scale": sw},
-           "command": command, "kernels": kernels}
+           "command": command, "kernels": old}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -469,7 +481,7 @@ def bwd_flops_per_token_head(w):
     return n_ccd * 2 * C * d + n_cdd * 2 * d * d + (C * C / 3 if erase else 0)
 
 
-def bench_backward(w, steps, warmup):
+def bench_backward(w, steps, warmup, cpu_tokens=0):
     """la_chunk_bwd at a forward workload's sizes (upstream gradients drawn
     N(0, 1), dS_final N(0, 0.02^2)): tokens/s, the per-kernel HIP-event
     times, the fraction of bf16 MFMA peak of the dense backward flops and of
@@ -481,8 +493,10 @@ def bench_backward(w, steps, warmup):
     import workloads
 
     log(f"[bench] backward {w.name}: generating inputs")
-    x = {k: t.cuda() for k, t in workloads.make_inputs(w).items()}
-    gr = {k: t.cuda() for k, t in workloads.make_upstream_grads(w, ds_std=0.02).items()}
+    xc = workloads.make_inputs(w)
+    grc = workloads.make_upstream_grads(w, ds_std=0.02)
+    x = {k: t.cuda() for k, t in xc.items()}
+    gr = {k: t.cuda() for k, t in grc.items()}
     nws = la.chunk_bwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode,
                                        dtype=w.torch_dtype)
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
@@ -494,7 +508,26 @@ def bench_backward(w, steps, warmup):
     esz = 2 if w.dtype == "bf16" else 4
     by = th * (4 * w.dk * esz + 3 * w.dk * 4 + 4 * 4) + w.B * w.H * 3 * w.dk * w.dv * 4
     fl = th * bwd_flops_per_token_head(w)
-    del x, gr, ws
+    for name, k in kernels.items():
+        kb = bwd_kernel_bytes(name, w)
+        if kb:
+            k["algorithmic_bytes"] = kb
+            k["achieved_GBs"] = round(kb / (k["avg_ms"] * 1e-3) / 1e9, 1)
+            k["hbm_frac"] = round(k["achieved_GBs"] / HBM_PEAK_GBS, 4)
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] if n != "la_bwd_rev" and
+              n != "la_bwd_states" else 0.0)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom].get("achieved_GBs"),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom].get("hbm_frac"),
+            "traffic": measured_traffic(dom, "backward_" + w.name),
+            "algorithmic_bytes": kernels[dom].get("algorithmic_bytes"),
+            "note": "largest of the parallel kernels; the walks (la_bwd_states, la_bwd_rev) "
+                    "are bound by their serial chunk chain"}
+    del ws
+    torch.cuda.empty_cache()
+    cpu = None
+    if cpu_tokens > 0:
+        cpu = bwd_cpu_baseline(w, xc, grc, cpu_tokens)
+    del x, gr
     torch.cuda.empty_cache()
     return {"workload": "backward_" + w.name, "mode": w.mode, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(w.B * w.L / ms * 1e3, 1),
@@ -502,7 +535,55 @@ def bench_backward(w, steps, warmup):
             "mfma_frac_of_bf16_peak": round(fl / (ms * 1e-3) / BF16_MFMA_PEAK, 4),
             "min_bytes": by, "hbm_frac_of_min_bytes": round(by / (ms * 1e-3) /
                                                              (HBM_PEAK_GBS * 1e9), 4),
-            "workspace_bytes": nws, "kernels": kernels}
+            "workspace_bytes": nws, "roofline": roof, "kernels": kernels, "cpu_baseline": cpu}
+
+
+def bwd_kernel_bytes(name, w):
+    """Algorithmic bytes per launch of each backward kernel: its own inputs
+    and outputs read or written once (workspace arrays as the kernels hold
+    them: float32, or bf16 hi + lo planes of the same size)."""
+    erase = w.mode in ("delta", "gated_delta")
+    d, C = w.dk, w.C
+    nc = -(-w.L // C)
+    bh = w.B * w.H
+    tok = bh * w.L                 # real tokens
+    ptok = bh * nc * C             # padded rows of the workspace arrays
+    esz = 2 if w.dtype == "bf16" else 4
+    cc = bh * nc * C * C * 4       # one C x C float record per chunk-head
+    st = bh * nc * d * d * 4       # one state per chunk-head
+    S = bh * d * d * 4             # one state per head
+    return {
+        "la_bwd_prep": tok * (2 * d * esz + 8) + ptok * 4 + cc * (2 if erase else 1),
+        "la_bwd_states": tok * (2 * d * esz + 8) + ptok * 4 + (cc if erase else 0) + S + st
+                         + (ptok * d * 4 if erase else 0),
+        "la_bwd_dprep": tok * 2 * d * esz + ptok * 4 + cc + ptok * d * 4 + st,
+        "la_bwd_rev": tok * (d * esz + 4 + d * 4) + ptok * 4 + (cc if erase else 0)
+                      + ptok * d * 4 + 2 * st + 2 * S + (ptok * d * 4 if erase else 0),
+        "la_bwd_grads": tok * (4 * d * esz + 4 + 2 * d * 4 + 8) + ptok * 4 + 2 * st
+                        + (2 * ptok * d * 4 if erase else 0),
+    }.get(name)
+
+
+def bwd_cpu_baseline(w, x, gr, tokens):
+    """The float64 chunkwise backward oracle, as it stands, on the first
+    `tokens` tokens of every head, BLAS limited to one thread."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+
+    sub = {k: (t[:, :, :tokens] if k != "S0" else t) for k, t in x.items()}
+    y = workloads.to_f64(sub)
+    g = workloads.to_f64({"dout": gr["dout"][:, :, :tokens], "dS_final": gr["dS_final"]})
+    log(f"[bench] cpu baseline (backward): oracle on {tokens} tokens x {w.B * w.H} heads")
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.chunkwise_bwd(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
+                             y["S0"] if w.s0_std > 0 else None, w.mode, w.C, g["dout"],
+                             g["dS_final"])
+        sec = time.perf_counter() - t0
+    return {"value": w.B * tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {tokens} of {w.L} tokens of all {w.B}x{w.H} (batch, head) "
+                      f"sequences of {w.name}, float64 chunkwise backward, {sec:.1f} s"}
 
 
 def varlen_lengths(n, total, seed):
@@ -645,6 +726,8 @@ def main():
     ap.add_argument("--only-backward", action="store_true",
                     help="only time la_chunk_bwd at the forward workload's sizes and print "
                          "that measurement (for profiling runs)")
+    ap.add_argument("--bwd-cpu-tokens", type=int, default=8192,
+                    help="tokens per head of the backward's CPU oracle sample (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -655,10 +738,12 @@ def main():
     args = ap.parse_args()
     if args.ingest_pmc:
         import workloads
-        ingest_pmc(*args.ingest_pmc[:4],
-                   {"la_chunk": workloads.WORKLOADS[args.workload].name,
-                    "la_tsolve": workloads.WORKLOADS[args.workload].name,
-                    "la_decode": workloads.WORKLOADS[5].name}, args.ingest_pmc[4])
+        wname = workloads.WORKLOADS[args.workload].name
+        if args.only_backward:
+            wl = {k: "backward_" + wname for k in KERNEL_SOURCES if k.startswith("la_bwd")}
+        else:
+            wl = {"la_chunk": wname, "la_tsolve": wname, "la_decode": workloads.WORKLOADS[5].name}
+        ingest_pmc(*args.ingest_pmc[:4], wl, args.ingest_pmc[4])
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -677,7 +762,8 @@ def main():
         return
     w = workloads.head_shard(workloads.WORKLOADS[args.workload], args.shard)
     if args.only_backward:
-        print(json.dumps({"backward": bench_backward(w, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"backward": bench_backward(w, args.steps, args.warmup,
+                                                     args.bwd_cpu_tokens)}), flush=True)
         return
     x, fwd = bench_forward(w, args.steps, args.warmup)
     dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
@@ -690,7 +776,7 @@ def main():
             "segments": bench_segments(workloads.WORKLOAD4_SHARD8, args.steps, 1),
             "fused": bench_fused(w, args.steps, 1),
             "noncausal": bench_noncausal(workloads.WORKLOADS[2], args.steps, 1),
-            "backward": bench_backward(w, args.steps, 1),
+            "backward": bench_backward(w, args.steps, 1, args.bwd_cpu_tokens),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
