@@ -41,7 +41,7 @@ KERNEL_SOURCES = {
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
 for _k in ("la_bwd_prep", "la_bwd_states", "la_bwd_dprep", "la_bwd_rev", "la_bwd_grads"):
-    KERNEL_SOURCES[_k] = ["la_bwd.hip", "la_device.hpp", "la_kernels.hpp"]
+    KERNEL_SOURCES[_k] = ["la_bwd.hip", "la_bwd.hpp", "la_device.hpp", "la_kernels.hpp"]
 # rocprofv3 kernel names -> library kernel names (chunk_kernel: float
 # inputs, chunk_pipe_kernel: bf16 inputs)
 KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
@@ -726,7 +726,7 @@ def main():
     ap.add_argument("--only-backward", action="store_true",
                     help="only time la_chunk_bwd at the forward workload's sizes and print "
                          "that measurement (for profiling runs)")
-    ap.add_argument("--bwd-cpu-tokens", type=int, default=8192,
+    ap.add_argument("--bwd-cpu-tokens", type=int, default=32768,
                     help="tokens per head of the backward's CPU oracle sample (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")

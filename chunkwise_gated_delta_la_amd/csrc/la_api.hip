@@ -15,6 +15,7 @@
 
 #include "la.h"
 #include "la_kernels.hpp"
+#include "la_bwd.hpp"
 
 namespace {
 

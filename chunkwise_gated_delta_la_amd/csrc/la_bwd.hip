@@ -57,6 +57,7 @@
 // split into bf16 hi + lo parts (about 16 bits).  Gradients are float32.
 #include "la_device.hpp"
 #include "la_kernels.hpp"
+#include "la_bwd.hpp"
 
 #include <type_traits>
 

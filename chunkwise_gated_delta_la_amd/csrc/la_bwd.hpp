@@ -1,0 +1,47 @@
+// Internal interface of the backward (la_bwd.hip) for the C-ABI host layer.
+// Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+// Backward of the chunkwise forward.
+//
+// Gradients of sum(dO * O) + sum(dS_final * S_final) with respect to q, k,
+// v, log alpha, beta and S0, fixed-length layout [B, H, L, d], any L.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_alpha;
+  const float* beta;
+  const float* S0;        // NULL: zero
+  const void* dout;       // [B, H, L, dv], the input type
+  const float* dS_final;  // NULL: zero
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlog_alpha;      // gated modes
+  float* dbeta;           // erase modes
+  float* dS0;             // NULL: not written
+  int B, H, L, d, mode;
+  bool in_bf16;
+  void* workspace;        // bwd_workspace_bytes(*this) bytes, 16-byte aligned
+};
+
+size_t bwd_workspace_bytes(const BwdArgs& a);
+// The five launches in order: per-chunk prep (decays, T, transposed
+// scores), the forward walk (chunk entry states, U), the per-chunk
+// dS-independent products (P^T dO, Q^T diag(gam) dO), the reverse walk
+// (state gradients, dR, dv), the per-chunk gradients (dq, dk, dbeta,
+// dlog alpha).
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dprep(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st);
+
+
+}  // namespace la
