@@ -40,14 +40,14 @@ KERNEL_SOURCES = {
     "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
-for _k in ("la_bwd_prep", "la_bwd_states", "la_bwd_dprep", "la_bwd_rev", "la_bwd_grads"):
+for _k in ("la_bwd_prep", "la_bwd_states", "la_bwd_rev", "la_bwd_grads"):
     KERNEL_SOURCES[_k] = ["la_bwd.hip", "la_bwd.hpp", "la_device.hpp", "la_kernels.hpp"]
 # rocprofv3 kernel names -> library kernel names (chunk_kernel: float
 # inputs, chunk_pipe_kernel: bf16 inputs)
 KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
                   "t_solve_kernel": "la_tsolve", "decode_kernel": "la_decode",
                   "bwd_prep_kernel": "la_bwd_prep", "bwd_states_kernel": "la_bwd_states",
-                  "bwd_dprep_kernel": "la_bwd_dprep", "bwd_rev_kernel": "la_bwd_rev",
+                  "bwd_rev_kernel": "la_bwd_rev",
                   "bwd_grads_kernel": "la_bwd_grads"}
 T_BYTES_PER_CHUNK = 6 * 1024   # T operand fragments of one (b, h, chunk)
 
@@ -553,10 +553,10 @@ def bwd_kernel_bytes(name, w):
     st = bh * nc * d * d * 4       # one state per chunk-head
     S = bh * d * d * 4             # one state per head
     return {
-        "la_bwd_prep": tok * (2 * d * esz + 8) + ptok * 4 + cc * (2 if erase else 1),
+        "la_bwd_prep": tok * (3 * d * esz + 8) + ptok * 4 + (cc if erase else 0)
+                       + ptok * d * 4 + st,
         "la_bwd_states": tok * (2 * d * esz + 8) + ptok * 4 + (cc if erase else 0) + S + st
                          + (ptok * d * 4 if erase else 0),
-        "la_bwd_dprep": tok * 2 * d * esz + ptok * 4 + cc + ptok * d * 4 + st,
         "la_bwd_rev": tok * (d * esz + 4 + d * 4) + ptok * 4 + (cc if erase else 0)
                       + ptok * d * 4 + 2 * st + 2 * S + (ptok * d * 4 if erase else 0),
         "la_bwd_grads": tok * (4 * d * esz + 4 + 2 * d * 4 + 8) + ptok * 4 + 2 * st

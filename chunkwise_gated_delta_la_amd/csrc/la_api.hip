@@ -471,7 +471,6 @@ int la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_a
   };
   const Step steps[] = {{"la_bwd_prep", la::launch_bwd_prep},
                         {"la_bwd_states", la::launch_bwd_states},
-                        {"la_bwd_dprep", la::launch_bwd_dprep},
                         {"la_bwd_rev", la::launch_bwd_rev},
                         {"la_bwd_grads", la::launch_bwd_grads}};
   hipEvent_t e0 = prof_mark(st);

@@ -36,16 +36,17 @@
 //   dlog_alpha_i = sum over rows r >= i of the chunk of dg_r.
 //
 // Kernels (one call runs all four on one stream):
-//   bwd_prep     per (b, h, chunk): g, T by forward substitution, P^T
+//   bwd_prep     per (b, h, chunk): g, T by forward substitution, and the
+//                two dS-independent terms P^T dO and Q^T diag(gam) dO
 //   bwd_states   per (b, h, 16 state columns): the forward walk, storing
 //                the state entering each chunk and U
 //   bwd_rev      per (b, h, 16 state columns): the reverse walk, storing dS'
 //                of each chunk and dR, writing dv and dS0
 //   bwd_grads    per (b, h, chunk): dq, dk, dbeta, dlog_alpha
 // The walks keep their 16-column state (or state-gradient) tile in the MFMA
-// accumulators of wave 0; waves 1-3 stage the next chunk's operands into the
-// other half of a double buffer (and, in the reverse walk, form its
-// P^T dO and Q^T diag(gam) dO), so each chunk step has one barrier.
+// accumulators of wave 0; waves 1-3 stage the chain's operands two chunks
+// ahead into a double buffer and write out what the chain hands them
+// through LDS, so each chunk step has one barrier.
 //
 // A ragged last chunk is padded with rows that change nothing: q, k, v, dO
 // and beta read as zero and log alpha as zero, so the padded rows of T are
@@ -73,7 +74,6 @@ constexpr int LDX = 20;        // row pitch of float 16-column tiles in LDS
 struct BwdWs {
   float* g;     // [BH, NC * C]     in-chunk cumsum of log alpha (padded rows: the total)
   float* T;     // [BH, NC, C, C]   (I + A)^-1, row-major (erase modes)
-  float* Pt;    // [BH, NC, C, C]   P^T
   float* Sent;  // [BH, NC, D, D]   state entering each chunk
   float* U;     // [BH, NC * C, D]  T R (erase modes)
   float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
@@ -91,17 +91,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const BwdArgs& a, BwdWs* ws) {
   const size_t BH = (size_t)a.B * a.H, NC = ((size_t)a.L + C - 1) / C, D = a.d;
   const bool erase = mode_erase(a.mode);
-  const size_t n[9] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * C * C,
-                       BH * NC * D * D, erase ? BH * NC * C * D : 0, BH * NC * D * D,
+  const size_t n[8] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * D * D,
+                       erase ? BH * NC * C * D : 0, BH * NC * D * D,
                        erase ? BH * NC * C * D : 0, BH * NC * C * D, BH * NC * D * D};
-  float* p[9];
+  float* p[8];
   size_t off = 0;
   char* base = static_cast<char*>(a.workspace);
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 8; ++i) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], (int)NC, n[3], n[4]};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], (int)NC, n[2], n[3]};
   return off;
 }
 
@@ -429,13 +429,22 @@ struct ChunkStage {
 };
 
 // ---------------------------------------------------------------- prep
+// Per chunk-head (parallel): g, T = (I + A)^-1 (erase modes) and the two
+// terms of the reverse walk that do not depend on the state gradient,
+// X1 = P^T dO [C, d] and X2 = Q^T diag(gam) dO [d, d].  P^T stays in LDS;
+// Q and dO are staged transposed so that every operand is read along its
+// contraction index.
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ log_alpha,
-    const float* __restrict__ beta, BwdWs ws, int L) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ dout,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta, BwdWs ws, int L) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int NKB = D / 32;
+  constexpr int PE = 16 / sizeof(T);
+  constexpr int LDT = C + PE;         // row pitch of the transposed tiles
+  constexpr int VPR = D / PE;
+  constexpr int NT16 = D / 16;
   const int NC = ws.NC;
   const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const int tid = threadIdx.x;
@@ -448,9 +457,21 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   const T* kc = k + row0 * D;
 
   __shared__ __attribute__((aligned(16))) float gs[C];
+  __shared__ __attribute__((aligned(16))) float gam[C];
   __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float Pt[C * LDC];
   __shared__ __attribute__((aligned(16))) float As[kErase ? C * LDC : 4];
+  __shared__ __attribute__((aligned(16))) T QT[D * LDT];
+  __shared__ __attribute__((aligned(16))) T OT[D * LDT];
 
+  // Q and dO rows, transposed into LDS (rows past the end as zero)
+  for (int p = tid; p < 2 * C * VPR; p += kThreads) {
+    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem / VPR, c0 = (rem % VPR) * PE;
+    const T* src = (m == 0 ? q : dout) + (row0 + min(r, nrows - 1)) * D + c0;
+    T* dst = m == 0 ? QT : OT;
+#pragma unroll
+    for (int j = 0; j < PE; ++j) dst[(c0 + j) * LDT + r] = r < nrows ? src[j] : T(0.f);
+  }
   if (wave == 0) {
     float la = 0.f, b = 0.f;
     if (lane < nrows) {
@@ -459,6 +480,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     }
     const float gg = kGated ? wave_inclusive_scan(la) : 0.f;
     gs[lane] = gg;
+    gam[lane] = kGated ? __expf(gg) : 1.f;
     bs[lane] = b;
     ws.g[cid * C + lane] = gg;
   }
@@ -480,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       const int i = 16 * ti + 4 * g + e, r = 16 * tj + n;
       float x = 0.f;
       if (r >= i) x = acc[e] * (kGated ? __expf(gs[r] - gs[i]) : 1.f);
-      ws.Pt[(cid * C + i) * C + r] = x;
+      Pt[i * LDC + r] = x;
     }
     if constexpr (kErase) {
       // A tile: rows r = 16 ti + 4 g + e, columns i = 16 tj + n, i < r
@@ -500,32 +522,62 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       }
     }
   }
-  if constexpr (kErase) {
-    __syncthreads();
-    if (wave == 0) {
-      // T = (I + A)^-1: lane j solves column j,
-      //   x_r = [r == j] - sum_{i < r} A_ri x_i
-      float x[C];
+  __syncthreads();
+
+  if (kErase && wave == 0) {
+    // T = (I + A)^-1: lane j solves column j,
+    //   x_r = [r == j] - sum_{i < r} A_ri x_i
+    float x[C];
 #pragma unroll
-      for (int r = 0; r < C; ++r) {
-        float s0 = r == lane ? 1.f : 0.f, s1 = 0.f;
+    for (int r = 0; r < C; ++r) {
+      float s0 = r == lane ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i4 = 0; 4 * i4 < r; ++i4) {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(As + r * LDC + 4 * i4);
+      for (int i4 = 0; 4 * i4 < r; ++i4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(As + r * LDC + 4 * i4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            if (i < r) {
-              if (i % 2 == 0) s0 = fmaf(-av[e], x[i], s0);
-              else s1 = fmaf(-av[e], x[i], s1);
-            }
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          if (i < r) {
+            if (i % 2 == 0) s0 = fmaf(-av[e], x[i], s0);
+            else s1 = fmaf(-av[e], x[i], s1);
           }
         }
-        x[r] = s0 + s1;
       }
-#pragma unroll
-      for (int r = 0; r < C; ++r) ws.T[(cid * C + r) * C + lane] = x[r];
+      x[r] = s0 + s1;
     }
+#pragma unroll
+    for (int r = 0; r < C; ++r) ws.T[(cid * C + r) * C + lane] = x[r];
+    return;
+  }
+
+  // X1 tiles (rows i of P^T, columns j of dO): 4 x NT16; X2 tiles: NT16 x NT16,
+  // over the waves not solving T
+  constexpr int N1 = 4 * NT16, N2 = NT16 * NT16;
+  const int w0 = kErase ? 1 : 0, nw = kWaves - w0;
+  for (int t = wave - w0; t < N1 + N2; t += nw) {
+    f32x4 acc = zero4();
+    float* out;
+    if (t < N1) {
+      const int r0 = 16 * (t / NT16), c0 = 16 * (t % NT16);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma_a2b(frag2_rowx<T>(Pt + (r0 + n) * LDC + 32 * kb, g),
+                frag_row(OT + (c0 + n) * LDT + 32 * kb, g), acc);
+      out = ws.X1 + (cid * C + r0) * D + c0;
+    } else {
+      const int r0 = 16 * ((t - N1) / NT16), c0 = 16 * ((t - N1) % NT16);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const Frag<T> o = frag_row(OT + (c0 + n) * LDT + 32 * kb, g);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = to_f32(o.v[j]) * gam[32 * kb + kidx(g, j)];
+        mma_ab2(frag_row(QT + (r0 + n) * LDT + 32 * kb, g), frag2_of<T>(x), acc);
+      }
+      out = ws.X2 + (cid * D + r0) * D + c0;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(size_t)(4 * g + e) * D + n] = acc[e];
   }
 }
 
@@ -687,78 +739,6 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
       }
     }
     __syncthreads();
-  }
-}
-
-// ------------------------------------------- dS-independent products
-// Per chunk-head (parallel): X1 = P^T dO [C, dv] and X2 = Q^T diag(gam) dO
-// [dk, dv], the two terms of the reverse walk that do not depend on the
-// state gradient.  Q^T and dO^T are staged transposed in LDS so that every
-// operand is read along its contraction index.
-template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_dprep_kernel(const T* __restrict__ q,
-                                                             const T* __restrict__ dout,
-                                                             BwdWs ws, int L) {
-  constexpr bool kGated = mode_decay(MODE);
-  constexpr int PE = 16 / sizeof(T);
-  constexpr int LDT = C + PE;         // row pitch of the transposed tiles
-  constexpr int VPR = D / PE;
-  constexpr int NT16 = D / 16;        // 16-wide tiles over d
-  const int NC = ws.NC;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid % kWave, g = lane / 16, n = lane % 16;
-  const int nrows = min(C, L - c * C);
-  const size_t row0 = (size_t)bh * L + (size_t)c * C;
-  const size_t cid = (size_t)bh * NC + c;
-
-  __shared__ __attribute__((aligned(16))) T QT[D * LDT];
-  __shared__ __attribute__((aligned(16))) T OT[D * LDT];
-  __shared__ __attribute__((aligned(16))) float gam[C];
-
-  // Q and dO rows, transposed into LDS (rows past the end as zero)
-  for (int p = tid; p < 2 * C * VPR; p += kThreads) {
-    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem / VPR, c0 = (rem % VPR) * PE;
-    const T* src = (m == 0 ? q : dout) + (row0 + min(r, nrows - 1)) * D + c0;
-    T* dst = m == 0 ? QT : OT;
-#pragma unroll
-    for (int j = 0; j < PE; ++j) dst[(c0 + j) * LDT + r] = r < nrows ? src[j] : T(0.f);
-  }
-  if (tid < C) gam[tid] = kGated ? __expf(ws.g[cid * C + tid]) : 1.f;
-  __syncthreads();
-
-  // X1 tiles (rows i of P^T, columns j of dO): NT16 x 4; X2 tiles: NT16 x NT16
-  constexpr int N1 = 4 * NT16, N2 = NT16 * NT16;
-  for (int t = wave; t < N1 + N2; t += kWaves) {
-    f32x4 acc = zero4();
-    int r0, c0;
-    float* out;
-    if (t < N1) {
-      const int ti = t / NT16, tj = t % NT16;
-      r0 = 16 * ti;
-      c0 = 16 * tj;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        mma_a2b(frag2_rowx<T>(ws.Pt + (cid * C + r0 + n) * C + 32 * kb, g),
-                frag_row(OT + (c0 + n) * LDT + 32 * kb, g), acc);
-      out = ws.X1 + (cid * C + r0) * D + c0;
-    } else {
-      const int ti = (t - N1) / NT16, tj = (t - N1) % NT16;
-      r0 = 16 * ti;
-      c0 = 16 * tj;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const Frag<T> o = frag_row(OT + (c0 + n) * LDT + 32 * kb, g);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = to_f32(o.v[j]) * gam[32 * kb + kidx(g, j)];
-        mma_ab2(frag_row(QT + (r0 + n) * LDT + 32 * kb, g), frag2_of<T>(x), acc);
-      }
-      out = ws.X2 + (cid * D + r0) * D + c0;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[(size_t)(4 * g + e) * D + n] = acc[e];
   }
 }
 
@@ -1300,7 +1280,8 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_prep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
                        dim3(kThreads), 0, st, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), a.log_alpha, a.beta, ws, a.L);
+                       static_cast<const T*>(a.k), static_cast<const T*>(a.dout), a.log_alpha,
+                       a.beta, ws, a.L);
     return hipGetLastError();
   });
 }
@@ -1315,19 +1296,6 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
                        dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.beta, a.S0, ws, BH, a.L);
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_bwd_dprep(const BwdArgs& a, hipStream_t st) {
-  BwdWs ws;
-  carve(a, &ws);
-  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
-  return dispatch(a, [&](auto t, auto d, auto m) {
-    using T = typename decltype(t)::type;
-    hipLaunchKernelGGL((bwd_dprep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
-                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.dout), ws, a.L);
     return hipGetLastError();
   });
 }

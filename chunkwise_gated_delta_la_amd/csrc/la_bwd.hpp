@@ -32,14 +32,12 @@ struct BwdArgs {
 };
 
 size_t bwd_workspace_bytes(const BwdArgs& a);
-// The five launches in order: per-chunk prep (decays, T, transposed
-// scores), the forward walk (chunk entry states, U), the per-chunk
-// dS-independent products (P^T dO, Q^T diag(gam) dO), the reverse walk
-// (state gradients, dR, dv), the per-chunk gradients (dq, dk, dbeta,
-// dlog alpha).
+// The four launches in order: per-chunk prep (decays, T, and the
+// dS-independent products P^T dO and Q^T diag(gam) dO), the forward walk
+// (chunk entry states, U), the reverse walk (state gradients, dR, dv), the
+// per-chunk gradients (dq, dk, dbeta, dlog alpha).
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_dprep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st);
 

@@ -396,10 +396,9 @@ int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv,
  * in the hybrid-attention notes; train with the parallel form: "朴素线性注意力"
  * in the lecture notes).  The call differentiates the forward's chunk step
  * (WY/UT form, "HouseHolder变换和WY表示"; scalar decay, "Gated DeltaNet"):
- * a per-chunk prep kernel (decays, T, transposed scores), a forward walk
- * storing each chunk's entry state and U = T R, a per-chunk kernel for the
- * two products that do not depend on the state gradient (P^T dO and Q^T
- * diag(gam) dO), a reverse walk over chunks
+ * a per-chunk prep kernel (decays, T, and the two products that do not
+ * depend on the state gradient, P^T dO and Q^T diag(gam) dO), a forward walk
+ * storing each chunk's entry state and U = T R, a reverse walk over chunks
  * carrying the state gradient (dU = P^T dO + diag(f) K dS', dR = T^T dU,
  * dS = gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR), and a
  * parallel per-chunk kernel for dq, dk, dbeta and dlog_alpha.
@@ -420,9 +419,9 @@ int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv,
  *                        last chunk may be partial)
  *   workspace       at least la_chunk_bwd_workspace_bytes() bytes, 16-byte
  *                   aligned: per chunk the entry state, the gradient of the
- *                   leaving state and Q^T diag(gam) dO (3 d^2 floats), T and
- *                   P^T (2 C^2 floats); per token U, dR and P^T dO (3 d
- *                   floats) and g
+ *                   leaving state and Q^T diag(gam) dO (3 d^2 floats) and T
+ *                   (C^2 floats); per token U, dR and P^T dO (3 d floats)
+ *                   and g
  * Errors as la_chunk_fwd: missing required pointers LA_ERR_NULL; shapes
  * LA_ERR_SHAPE / LA_ERR_UNSUPPORTED (also LA_DTYPE_BF16_F32OUT); any overlap
  * between an output and an input, another output or the workspace
