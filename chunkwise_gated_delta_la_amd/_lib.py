@@ -75,6 +75,12 @@ def _declare(lib):
     lib.la_chunk_bwd.restype = i
     lib.la_chunk_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_bwd_workspace_bytes.restype = i
+    lib.la_chunk_bwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, fp, fp, fp, fp, fp,
+                                        fp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_chunk_bwd_varlen.restype = i
+    lib.la_chunk_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i,
+                                                        ctypes.POINTER(sz)]
+    lib.la_chunk_bwd_varlen_workspace_bytes.restype = i
     lib.la_last_error.argtypes = []
     lib.la_last_error.restype = ctypes.c_char_p
     lib.la_version.argtypes = []

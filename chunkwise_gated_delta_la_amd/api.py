@@ -419,3 +419,65 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, dout, dS_final=None, *, mode="gated_
                               workspace.numel(), _stream(dev))
     _lib.check(rc)
     return res
+
+
+def chunk_bwd_varlen_workspace_bytes(N, H, T, dk, dv, *, mode="gated_delta", C=64,
+                                     dtype=torch.bfloat16):
+    """Workspace bytes ``la_chunk_bwd_varlen`` needs for these sizes
+    (``la_chunk_bwd_varlen_workspace_bytes``)."""
+    code = _dtype_code(dtype, dtype)
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.get().la_chunk_bwd_varlen_workspace_bytes(N, H, T, dk, dv, C, _mode(mode),
+                                                              code, ctypes.byref(n)))
+    return n.value
+
+
+def chunk_bwd_varlen(q, k, v, log_alpha, beta, S0, dout, cu_seqlens, dS_final=None, *,
+                     mode="gated_delta", C=64, workspace=None, want_dS0=True):
+    """Gradients of ``chunk_fwd_varlen`` (``la_chunk_bwd_varlen``): q, k
+    ``[H, T, dk]``, v and ``dout`` ``[H, T, dv]`` (the inputs' dtype), gates
+    ``[H, T]``, cu_seqlens ``[N + 1]`` int32 on the GPU, S0 and dS_final
+    ``[N, H, dk, dv]`` float32 or None.  Returns a dict of float32 tensors as
+    ``chunk_bwd`` does, in the packed layout."""
+    m = _mode(mode)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, T, d]")
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
+    N = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _need(k, "k", (H, T, dk), dt, dev)
+    _need(v, "v", (H, T, dv), dt, dev)
+    _need(dout, "dout", (H, T, dv), dt, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (H, T), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (H, T), torch.float32, dev)
+    _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    _need(dS_final, "dS_final", (N, H, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty((H, T, dk), **f32), "dk": torch.empty((H, T, dk), **f32),
+           "dv": torch.empty((H, T, dv), **f32),
+           "dlog_alpha": torch.empty((H, T), **f32) if m in _DECAY else None,
+           "dbeta": torch.empty((H, T), **f32) if m in _ERASE else None,
+           "dS0": torch.empty((N, H, dk, dv), **f32) if want_dS0 else None}
+    need = chunk_bwd_varlen_workspace_bytes(N, H, T, dk, dv, mode=mode, C=C, dtype=dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        rc = lib.la_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(log_alpha if m in _DECAY else None),
+                                     _ptr(beta if m in _ERASE else None), _ptr(S0), _ptr(dout),
+                                     _ptr(dS_final), _ptr(cu_seqlens), _ptr(res["dq"]),
+                                     _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dlog_alpha"]),
+                                     _ptr(res["dbeta"]), _ptr(res["dS0"]), N, H, T, dk, dv, C,
+                                     m, _DTYPES[dt], _ptr(workspace), workspace.numel(),
+                                     _stream(dev))
+    _lib.check(rc)
+    return res

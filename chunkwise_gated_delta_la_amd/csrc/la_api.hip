@@ -356,6 +356,76 @@ la::BwdArgs bwd_args(int B, int H, int L, int d, int mode, int dtype, void* work
   return a;
 }
 
+// Pointer and mode checks shared by la_chunk_bwd and la_chunk_bwd_varlen.
+int check_bwd_args(const void* q, const void* k, const void* v, const float* log_alpha,
+                   const float* beta, const void* grad_out, const float* grad_q,
+                   const float* grad_k, const float* grad_v, const float* grad_log_alpha,
+                   const float* grad_beta, int mode, int dtype) {
+  if (!q || !k || !v || !grad_out || !grad_q || !grad_k || !grad_v)
+    return fail(LA_ERR_NULL, "q, k, v, grad_out, grad_q, grad_k and grad_v are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (la::mode_decay(mode) && !grad_log_alpha)
+    return fail(LA_ERR_NULL, "grad_log_alpha is required for the gated modes");
+  if (la::mode_erase(mode) && !grad_beta)
+    return fail(LA_ERR_NULL, "grad_beta is required for the delta modes");
+  return LA_OK;
+}
+
+// Workspace and alias checks, then the four launches.  n_x, n_g, n_s are
+// the element counts of a token tensor, a gate tensor and the states; cu
+// (packed batches) is an input of cu_bytes bytes.
+int run_bwd(const la::BwdArgs& a, size_t n_x, size_t n_g, size_t n_s, int dtype,
+            size_t workspace_bytes, size_t cu_bytes, void* stream) {
+  const size_t need = la::bwd_workspace_bytes(a);
+  if (!a.workspace)
+    return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
+                                      " bytes (la_chunk_bwd_workspace_bytes)");
+  if (workspace_bytes < need)
+    return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, this call needs " + std::to_string(need));
+  if (reinterpret_cast<uintptr_t>(a.workspace) % 16 != 0)
+    return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const bool gated = la::mode_decay(a.mode), erase = la::mode_erase(a.mode);
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const Range rq(a.q, n_x * esz), rk(a.k, n_x * esz), rv(a.v, n_x * esz);
+  const Range rdo(a.dout, n_x * esz);
+  const Range rla(gated ? a.log_alpha : nullptr, n_g * 4), rb(erase ? a.beta : nullptr, n_g * 4);
+  const Range rs0(a.S0, n_s * 4), rdsf(a.dS_final, n_s * 4), rcu(a.cu, cu_bytes);
+  const Range oq(a.dq, n_x * 4), ok(a.dk, n_x * 4), ov(a.dv, n_x * 4);
+  const Range ola(gated ? a.dlog_alpha : nullptr, n_g * 4);
+  const Range ob(erase ? a.dbeta : nullptr, n_g * 4), os0(a.dS0, n_s * 4);
+  const Range rws(a.workspace, need);
+  const Range* ins[] = {&rq, &rk, &rv, &rdo, &rla, &rb, &rs0, &rdsf, &rcu};
+  const Range* outs[] = {&oq, &ok, &ov, &ola, &ob, &os0, &rws};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range* in : ins)
+      if (outs[i]->overlaps(*in))
+        return fail(LA_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
+    for (size_t j = 0; j < i; ++j)
+      if (outs[i]->overlaps(*outs[j]))
+        return fail(LA_ERR_ALIAS, "two gradient outputs (or one and the workspace) overlap");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  struct Step {
+    const char* name;
+    hipError_t (*launch)(const la::BwdArgs&, hipStream_t);
+  };
+  const Step steps[] = {{"la_bwd_prep", la::launch_bwd_prep},
+                        {"la_bwd_states", la::launch_bwd_states},
+                        {"la_bwd_rev", la::launch_bwd_rev},
+                        {"la_bwd_grads", la::launch_bwd_grads}};
+  hipEvent_t e0 = prof_mark(st);
+  for (const Step& s : steps) {
+    const hipError_t e = s.launch(a, st);
+    hipEvent_t e1 = prof_mark(st);
+    prof_add(s.name, e0, e1);
+    if (e != hipSuccess) return fail_hip(s.name, e);
+    e0 = e1;
+  }
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,79 +479,59 @@ int la_chunk_bwd(const void* q, const void* k, const void* v, const float* log_a
                  int dk, int dv, int C, int mode, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (!q || !k || !v || !grad_out || !grad_q || !grad_k || !grad_v)
-    return fail(LA_ERR_NULL, "q, k, v, grad_out, grad_q, grad_k and grad_v are required");
-  if (int e = check_mode_dtype(mode, dtype)) return e;
-  if (int e = check_gates(mode, log_alpha, beta)) return e;
-  if (la::mode_decay(mode) && !grad_log_alpha)
-    return fail(LA_ERR_NULL, "grad_log_alpha is required for the gated modes");
-  if (la::mode_erase(mode) && !grad_beta)
-    return fail(LA_ERR_NULL, "grad_beta is required for the delta modes");
+  if (int e = check_bwd_args(q, k, v, log_alpha, beta, grad_out, grad_q, grad_k, grad_v,
+                             grad_log_alpha, grad_beta, mode, dtype))
+    return e;
   if (int e = check_bwd_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
   size_t n_x, n_g, n_s;
   if (!count({B, H, L, dk}, &n_x) || !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
     return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
   la::BwdArgs a = bwd_args(B, H, L, dk, mode, dtype, workspace);
-  const size_t need = la::bwd_workspace_bytes(a);
-  if (!workspace)
-    return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
-                                      " bytes (la_chunk_bwd_workspace_bytes)");
-  if (workspace_bytes < need)
-    return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                      " bytes, this call needs " + std::to_string(need));
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-    return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  const bool gated = la::mode_decay(mode), erase = la::mode_erase(mode);
-  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
-  const Range rq(q, n_x * esz), rk(k, n_x * esz), rv(v, n_x * esz), rdo(grad_out, n_x * esz);
-  const Range rla(gated ? log_alpha : nullptr, n_g * 4), rb(erase ? beta : nullptr, n_g * 4);
-  const Range rs0(S0, n_s * 4), rdsf(grad_S_final, n_s * 4);
-  const Range oq(grad_q, n_x * 4), ok(grad_k, n_x * 4), ov(grad_v, n_x * 4);
-  const Range ola(gated ? grad_log_alpha : nullptr, n_g * 4);
-  const Range ob(erase ? grad_beta : nullptr, n_g * 4), os0(grad_S0, n_s * 4);
-  const Range rws(workspace, need);
-  const Range* ins[] = {&rq, &rk, &rv, &rdo, &rla, &rb, &rs0, &rdsf};
-  const Range* outs[] = {&oq, &ok, &ov, &ola, &ob, &os0, &rws};
-  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
-    for (const Range* in : ins)
-      if (outs[i]->overlaps(*in))
-        return fail(LA_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
-    for (size_t j = 0; j < i; ++j)
-      if (outs[i]->overlaps(*outs[j]))
-        return fail(LA_ERR_ALIAS, "two gradient outputs (or one and the workspace) overlap");
-  }
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.log_alpha = log_alpha;
-  a.beta = beta;
-  a.S0 = S0;
-  a.dout = grad_out;
-  a.dS_final = grad_S_final;
-  a.dq = grad_q;
-  a.dk = grad_k;
-  a.dv = grad_v;
-  a.dlog_alpha = grad_log_alpha;
-  a.dbeta = grad_beta;
-  a.dS0 = grad_S0;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  struct Step {
-    const char* name;
-    hipError_t (*launch)(const la::BwdArgs&, hipStream_t);
-  };
-  const Step steps[] = {{"la_bwd_prep", la::launch_bwd_prep},
-                        {"la_bwd_states", la::launch_bwd_states},
-                        {"la_bwd_rev", la::launch_bwd_rev},
-                        {"la_bwd_grads", la::launch_bwd_grads}};
-  hipEvent_t e0 = prof_mark(st);
-  for (const Step& s : steps) {
-    const hipError_t e = s.launch(a, st);
-    hipEvent_t e1 = prof_mark(st);
-    prof_add(s.name, e0, e1);
-    if (e != hipSuccess) return fail_hip(s.name, e);
-    e0 = e1;
-  }
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
+  a.dout = grad_out; a.dS_final = grad_S_final;
+  a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_log_alpha;
+  a.dbeta = grad_beta; a.dS0 = grad_S0;
+  return run_bwd(a, n_x, n_g, n_s, dtype, workspace_bytes, 0, stream);
+}
+
+int la_chunk_bwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int C, int mode,
+                                        int dtype, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (dtype == LA_DTYPE_BF16_F32OUT)
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_bwd_varlen takes LA_DTYPE_F32 or LA_DTYPE_BF16");
+  if (int e = check_varlen_shape(N, H, T, dk, dv, C, mode, dtype)) return e;
+  la::BwdArgs a = bwd_args(N, H, T, dk, mode, dtype, nullptr);
+  a.packed = true;
+  *bytes = la::bwd_workspace_bytes(a);
   return LA_OK;
+}
+
+int la_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* beta, const float* S0, const void* grad_out,
+                        const float* grad_S_final, const int* cu_seqlens, float* grad_q,
+                        float* grad_k, float* grad_v, float* grad_log_alpha, float* grad_beta,
+                        float* grad_S0, int N, int H, int T, int dk, int dv, int C, int mode,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!cu_seqlens) return fail(LA_ERR_NULL, "cu_seqlens is required");
+  if (int e = check_bwd_args(q, k, v, log_alpha, beta, grad_out, grad_q, grad_k, grad_v,
+                             grad_log_alpha, grad_beta, mode, dtype))
+    return e;
+  if (dtype == LA_DTYPE_BF16_F32OUT)
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_bwd_varlen takes LA_DTYPE_F32 or LA_DTYPE_BF16");
+  if (int e = check_varlen_shape(N, H, T, dk, dv, C, mode, dtype)) return e;
+  size_t n_x, n_g, n_s;
+  if (!count({H, T, dk}, &n_x) || !count({H, T}, &n_g) || !count({N, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  la::BwdArgs a = bwd_args(N, H, T, dk, mode, dtype, workspace);
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
+  a.dout = grad_out; a.dS_final = grad_S_final;
+  a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_log_alpha;
+  a.dbeta = grad_beta; a.dS0 = grad_S0;
+  a.cu = cu_seqlens;
+  return run_bwd(a, n_x, n_g, n_s, dtype, workspace_bytes, (size_t)(N + 1) * sizeof(int),
+                 stream);
 }
 
 int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv, int dtype,

@@ -71,6 +71,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int LDC = C + 4;     // row pitch of float C x C tiles in LDS
 constexpr int LDX = 20;        // row pitch of float 16-column tiles in LDS
 
+// Per-chunk arrays are indexed by the chunk's slot: bh * NC + c for the
+// fixed-length layout, the forward's packed-batch slots (SeqMap) otherwise
+// (shapes below are the fixed-length ones).
 struct BwdWs {
   float* g;     // [BH, NC * C]     in-chunk cumsum of log alpha (padded rows: the total)
   float* T;     // [BH, NC, C, C]   (I + A)^-1, row-major (erase modes)
@@ -80,20 +83,28 @@ struct BwdWs {
   float* dR;    // [BH, NC * C, D]  T^T dU (erase modes)
   float* X1;    // [BH, NC * C, D]  P^T dO
   float* X2;    // [BH, NC, D, D]   Q^T diag(gam) dO
-  int NC;
   size_t nS;    // elements of Sent and dSx
   size_t nU;    // elements of U and dR
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+
+SeqMap seq_map(const BwdArgs& a) { return SeqMap{a.cu, a.B, a.H, a.L, C}; }
+
+// Chunk slots of a call: one per chunk-head (fixed length), H (ceil(T / C)
+// + N) for a packed batch.
+size_t slots(const BwdArgs& a) {
+  const size_t nc = ((size_t)a.L + C - 1) / C;
+  return (a.cu || a.packed) ? (size_t)a.H * (nc + (size_t)a.B) : (size_t)a.B * a.H * nc;
+}
+
 // Bytes of the workspace; with ws != NULL also its arrays in a.workspace.
 size_t carve(const BwdArgs& a, BwdWs* ws) {
-  const size_t BH = (size_t)a.B * a.H, NC = ((size_t)a.L + C - 1) / C, D = a.d;
+  const size_t ns = slots(a), D = a.d;
   const bool erase = mode_erase(a.mode);
-  const size_t n[8] = {BH * NC * C,     erase ? BH * NC * C * C : 0, BH * NC * D * D,
-                       erase ? BH * NC * C * D : 0, BH * NC * D * D,
-                       erase ? BH * NC * C * D : 0, BH * NC * C * D, BH * NC * D * D};
+  const size_t n[8] = {ns * C,     erase ? ns * C * C : 0, ns * D * D, erase ? ns * C * D : 0,
+                       ns * D * D, erase ? ns * C * D : 0, ns * C * D, ns * D * D};
   float* p[8];
   size_t off = 0;
   char* base = static_cast<char*>(a.workspace);
@@ -101,8 +112,39 @@ size_t carve(const BwdArgs& a, BwdWs* ws) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], (int)NC, n[2], n[3]};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], n[2], n[3]};
   return off;
+}
+
+// The chunk a parallel kernel's workgroup `item` (a slot) covers: its first
+// token row and row count; false for a packed-batch slot no chunk maps to.
+__device__ __forceinline__ bool chunk_of_slot(const SeqMap& sm, size_t item, size_t& row0,
+                                              int& nrows) {
+  if (!sm.cu) {
+    const int NC = (sm.L + C - 1) / C;
+    const size_t bh = item / NC;
+    const int c = (int)(item % NC);
+    row0 = bh * sm.L + (size_t)c * C;
+    nrows = min(C, sm.L - c * C);
+    return true;
+  }
+  const size_t sph = sm.slots_per_head();
+  const int h = (int)(item / sph), j = (int)(item % sph);
+  auto start = [&](int s) { return min(max(sm.cu[s], 0), sm.L); };
+  auto first_slot = [&](int s) { return start(s) / C + s; };
+  if (first_slot(0) > j) return false;
+  int lo = 0, hi = sm.N - 1;      // the last sequence whose first slot is <= j
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (first_slot(mid) <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int a = start(lo), len = min(max(sm.cu[lo + 1], a), sm.L) - a;
+  const int c = j - first_slot(lo);
+  if (c * C >= len) return false;
+  row0 = (size_t)h * sm.L + a + (size_t)c * C;
+  nrows = min(C, len - c * C);
+  return true;
 }
 
 template <typename T>
@@ -437,7 +479,7 @@ struct ChunkStage {
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ dout,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta, BwdWs ws, int L) {
+    const float* __restrict__ log_alpha, const float* __restrict__ beta, BwdWs ws, SeqMap sm) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int NKB = D / 32;
@@ -445,14 +487,13 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   constexpr int LDT = C + PE;         // row pitch of the transposed tiles
   constexpr int VPR = D / PE;
   constexpr int NT16 = D / 16;
-  const int NC = ws.NC;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave, g = lane / 16, n = lane % 16;
-  const int nrows = min(C, L - c * C);
-  const size_t row0 = (size_t)bh * L + (size_t)c * C;
-  const size_t cid = (size_t)bh * NC + c;
+  size_t row0;
+  int nrows;
+  if (!chunk_of_slot(sm, blockIdx.x, row0, nrows)) return;
+  const size_t cid = blockIdx.x;
   const T* qc = q + row0 * D;
   const T* kc = k + row0 * D;
 
@@ -585,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
-    const float* __restrict__ S0, BwdWs ws, int BH, int L) {
+    const float* __restrict__ S0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int PE = 16 / sizeof(T);
@@ -607,8 +648,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   int bh, ct;
   tile_of_block(blockIdx.x, BH, NCT, bh, ct);
   const int col0 = 16 * ct;
-  const int NC = ws.NC;
-  const size_t NCC = (size_t)NC * C;
+  const SeqInfo si = seq_info(sm, bh);
+  const int L = si.len;                        // tokens of this sequence
+  const int NC = (L + C - 1) / C;
+  if (NC == 0) return;                         // nothing to store
 
   // Waves 1-3 stage the chain's operands: chunk c's loads go out during the
   // step two before its use and land in LDS during the step before it (the
@@ -616,8 +659,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   ChunkStage<T, D, kErase, true> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
-    const size_t row0 = (size_t)bh * L + (size_t)c * C;
-    const size_t cid = (size_t)bh * NC + c;
+    const size_t row0 = si.row0 + (size_t)c * C;
+    const size_t cid = si.slot0 + c;
     st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
             tid - kWave);
   };
@@ -650,10 +693,10 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
     const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
     auto flush = [&](int c) {
       const int b = c & 1;
-      tile_flush<T, D, D>(SxT[b], Se, ((size_t)bh * NC + c) * D * D + col0, tid - kWave,
+      tile_flush<T, D, D>(SxT[b], Se, (si.slot0 + c) * D * D + col0, tid - kWave,
                           kThreads - kWave);
       if constexpr (kErase)
-        tile_flush<T, D, C>(UxT[b], Um, ((size_t)bh * NCC + (size_t)c * C) * D + col0,
+        tile_flush<T, D, C>(UxT[b], Um, (si.slot0 + c) * C * D + col0,
                             tid - kWave, kThreads - kWave);
     };
     for (int c = 0; c < NC; ++c) {
@@ -747,7 +790,7 @@ template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ beta,
     const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dv_out,
-    float* __restrict__ dS0, BwdWs ws, int BH, int L) {
+    float* __restrict__ dS0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int PE = 16 / sizeof(T);
@@ -770,8 +813,23 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   int bh, ct;
   tile_of_block(blockIdx.x, BH, NCT, bh, ct);
   const int col0 = 16 * ct;
-  const int NC = ws.NC;
-  const size_t NCC = (size_t)NC * C;
+  const SeqInfo si = seq_info(sm, bh);
+  const int L = si.len;                        // tokens of this sequence
+  const int NC = (L + C - 1) / C;
+  if (NC == 0) {
+    // an empty sequence passes the state gradient through
+    if (wave == 0 && dS0) {
+      const size_t sb = (size_t)bh * D * D;
+#pragma unroll
+      for (int tj = 0; tj < NKT; ++tj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const size_t o = sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n;
+          dS0[o] = dS_final ? dS_final[o] : 0.f;
+        }
+    }
+    return;
+  }
 
   // Waves 1-3 stage the chain's operands of each chunk -- K, T, the gates and
   // the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO (formed
@@ -779,8 +837,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   ChunkStage<T, D, kErase, false, true> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
-    const size_t row0 = (size_t)bh * L + (size_t)c * C;
-    const size_t cid = (size_t)bh * NC + c;
+    const size_t row0 = si.row0 + (size_t)c * C;
+    const size_t cid = si.slot0 + c;
     st.load(k, nullptr, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0,
             nrows, col0, tid - kWave, ws.X1 + cid * C * D, ws.X2 + cid * D * D);
   };
@@ -811,10 +869,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
     const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
     auto flush = [&](int s) {
       const int c = NC - 1 - s, b = s & 1;
-      tile_flush<T, D, D>(dSxT[b], dSe, ((size_t)bh * NC + c) * D * D + col0, tid - kWave,
+      tile_flush<T, D, D>(dSxT[b], dSe, (si.slot0 + c) * D * D + col0, tid - kWave,
                           kThreads - kWave);
       if constexpr (kErase)
-        tile_flush<T, D, C>(dRxT[b], dRm, ((size_t)bh * NCC + (size_t)c * C) * D + col0,
+        tile_flush<T, D, C>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0,
                             tid - kWave, kThreads - kWave);
     };
     for (int s = 0; s < NC; ++s) {
@@ -835,7 +893,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       const float* fc = fsb[b];      // exp(g_C - g)
       const float gamC = kGated ? gmc[C - 1] : 1.f;
       const int nrows = min(C, L - c * C);
-      const size_t row0 = (size_t)bh * L + (size_t)c * C;
+      const size_t row0 = si.row0 + (size_t)c * C;
       Frag2<T> bS[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) bS[kb] = frag2_from_acc<T>(dS[2 * kb], dS[2 * kb + 1]);
@@ -999,21 +1057,20 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const T* __restrict__ dout, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dla, float* __restrict__ dbeta, BwdWs ws,
-    int L) {
+    SeqMap sm) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr bool kSplit = IsBf16<T>::value;
   constexpr int NKB = D / 32, NCT = D / 16;
   using CS = ColStage<T, D>;
-  const int NC = ws.NC;
-  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave, g = lane / 16, n = lane % 16;
-  const int nrows = min(C, L - c * C);
-  const size_t row0 = (size_t)bh * L + (size_t)c * C;
-  const size_t cid = (size_t)bh * NC + c;
-  const size_t urow0 = (size_t)bh * NC * C + (size_t)c * C;   // row of U, dR
+  size_t row0;
+  int nrows;
+  if (!chunk_of_slot(sm, blockIdx.x, row0, nrows)) return;
+  const size_t cid = blockIdx.x;
+  const size_t urow0 = cid * C;   // row of U, dR
   const T* qc = q + row0 * D;
   const T* kc = k + row0 * D;
   const T* vc = v + row0 * D;
@@ -1033,7 +1090,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ __attribute__((aligned(16))) T Sb[CS::NP * 16 * CS::LDB];
   __shared__ __attribute__((aligned(16))) T Kcs[C * CS::LDQ];
   __shared__ __attribute__((aligned(16))) T Qcs[C * CS::LDQ];
-  __shared__ float dgam[C], dfv[C], dbe[C], rsum[C], csum[C], vdr[C];
+  __shared__ float dgam[C], dfv[C], vdr[C];
+  // per-tile partial sums, added in a fixed order (deterministic results):
+  // row sums of GG and of dA * (K K^T * Gamma) by column tile, column sums
+  // of GG by row tile
+  __shared__ float rsP[3][4][C];   // [0]: GG rows, [1]: dbeta rows, [2]: GG columns
   __shared__ float red[kWaves];
 
   // the first column tile's loads go out first
@@ -1049,9 +1110,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     gs[tid] = gg;
     gam[tid] = kGated ? __expf(gg) : 1.f;
     bs[tid] = (kErase && tid < nrows) ? beta[row0 + tid] : 0.f;
-    dbe[tid] = 0.f;
-    rsum[tid] = 0.f;
-    csum[tid] = 0.f;
+  }
+  {
+    float* part = &rsP[0][0][0];
+    for (int p = tid; p < 3 * 4 * C; p += kThreads) part[p] = 0.f;   // rsP, dbP, csP
   }
   if constexpr (kErase) {
     // V_r . dR_r: four threads per row
@@ -1073,8 +1135,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   if (tid < C) fs[tid] = kGated ? __expf(gs[C - 1] - gs[tid]) : 1.f;
 
   // C x C products on the lower tiles: scores, dO U^T, and (erase) K K^T,
-  // dR U^T; GG = (dO U^T) * P + dA * A goes straight into its row and
-  // column sums
+  // dR U^T; GG = (dO U^T) * P + dA * A goes straight into its per-tile row
+  // and column sums
 #pragma unroll 1
   for (int t = wave; t < 10; t += kWaves) {
     int ti, tj;
@@ -1108,15 +1170,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
         Hm[r * LDC + i] = dA * bs[r] * Gm;
         gg += dA * bs[r] * Kg;
         const float part = sum16(dA * Kg);
-        if (n == 0) atomicAdd(&dbe[r], part);
+        if (n == 0) rsP[1][tj][r] = part;
       }
       const float rs = sum16(gg);
-      if (n == 0) atomicAdd(&rsum[r], rs);
+      if (n == 0) rsP[0][tj][r] = rs;
       csp += gg;
     }
     csp += __shfl_xor(csp, 16);
     csp += __shfl_xor(csp, 32);
-    if (g == 0) atomicAdd(&csum[16 * tj + n], csp);
+    if (g == 0) rsP[2][ti][16 * tj + n] = csp;
   }
   __syncthreads();
 
@@ -1224,21 +1286,24 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     if (n == 0) {
       dgam[r] = a;
       dfv[r] = b;
-      dbe[r] += cc + (kErase ? vdr[r] : 0.f);
+      if constexpr (kErase)
+        vdr[r] += cc + rsP[1][0][r] + rsP[1][1][r] + rsP[1][2][r] + rsP[1][3][r];
     }
   }
   __syncthreads();
   if (wave == 0) {
     const int r = lane;
     const float dgC = red[0] + red[1] + red[2] + red[3];
-    float dg = rsum[r] - csum[r] + dgam[r] * gam[r] - dfv[r] * fs[r];
+    const float rsum = rsP[0][0][r] + rsP[0][1][r] + rsP[0][2][r] + rsP[0][3][r];
+    const float csum = rsP[2][0][r] + rsP[2][1][r] + rsP[2][2][r] + rsP[2][3][r];
+    float dg = rsum - csum + dgam[r] * gam[r] - dfv[r] * fs[r];
     const float dff = sum64(dfv[r] * fs[r]);
     if (r == C - 1) dg += dgC * gam[C - 1] + dff;
     const float inc = wave_inclusive_scan(dg);
     const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inc), C - 1));
     if (r < nrows) {
       if constexpr (kGated) dla[row0 + r] = tot - inc + dg;
-      if constexpr (kErase) dbeta[row0 + r] = dbe[r];
+      if constexpr (kErase) dbeta[row0 + r] = vdr[r];
     }
   }
 }
@@ -1275,13 +1340,14 @@ size_t bwd_workspace_bytes(const BwdArgs& a) { return carve(a, nullptr); }
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   BwdWs ws;
   carve(a, &ws);
-  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
+  const unsigned grid = (unsigned)slots(a);
+  const SeqMap sm = seq_map(a);
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_prep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
                        dim3(kThreads), 0, st, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.dout), a.log_alpha,
-                       a.beta, ws, a.L);
+                       a.beta, ws, sm);
     return hipGetLastError();
   });
 }
@@ -1295,7 +1361,7 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
                        dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.beta, a.S0, ws, BH, a.L);
+                       static_cast<const T*>(a.v), a.beta, a.S0, ws, seq_map(a), BH);
     return hipGetLastError();
   });
 }
@@ -1310,7 +1376,7 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
                        dim3(kThreads), 0, st, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), a.beta, static_cast<const T*>(a.dout),
-                       a.dS_final, a.dv, a.dS0, ws, BH, a.L);
+                       a.dS_final, a.dv, a.dS0, ws, seq_map(a), BH);
     return hipGetLastError();
   });
 }
@@ -1318,14 +1384,14 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st) {
   BwdWs ws;
   carve(a, &ws);
-  const unsigned grid = (unsigned)((size_t)a.B * a.H * ws.NC);
+  const unsigned grid = (unsigned)slots(a);
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_grads_kernel<T, decltype(d)::value, decltype(m)::value>),
                        dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.beta,
                        static_cast<const T*>(a.dout), a.dq, a.dk, a.dlog_alpha, a.dbeta, ws,
-                       a.L);
+                       seq_map(a));
     return hipGetLastError();
   });
 }

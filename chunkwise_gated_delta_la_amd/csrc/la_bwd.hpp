@@ -26,9 +26,14 @@ struct BwdArgs {
   float* dlog_alpha;      // gated modes
   float* dbeta;           // erase modes
   float* dS0;             // NULL: not written
-  int B, H, L, d, mode;
+  int B, H, L, d, mode;   // packed batch: B sequences, L tokens in all
   bool in_bf16;
   void* workspace;        // bwd_workspace_bytes(*this) bytes, 16-byte aligned
+  // Packed variable-length batch: cu_seqlens [B + 1] on the device, tokens
+  // [H, L, d], gates [H, L], states [B, H, d, d]; NULL: fixed length
+  // [B, H, L, d].
+  const int* cu = nullptr;
+  bool packed = false;    // size the workspace for a packed batch (cu may be NULL then)
 };
 
 size_t bwd_workspace_bytes(const BwdArgs& a);

@@ -442,6 +442,33 @@ int la_chunk_bwd_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
                                  int mode, int dtype, size_t* bytes);
 
 /*
+ * la_chunk_bwd_varlen -- la_chunk_bwd for a packed batch of N variable-length
+ * sequences, the gradients of la_chunk_fwd_varlen: tokens laid out as there
+ * (q, k, v, grad_out and the token gradients [H, T, d]; gates and their
+ * gradients [H, T]; S0, grad_S_final, grad_S0 [N, H, d, d]), with
+ * cu_seqlens [N + 1] int32 on the device (sequence s is tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1] - 1; the kernels clamp the offsets as
+ * la_chunk_fwd_varlen does).  Each sequence's gradients equal those of
+ * la_chunk_bwd on that sequence alone; an empty sequence passes grad_S_final
+ * to grad_S0.  Workspace: la_chunk_bwd_varlen_workspace_bytes(), the
+ * per-chunk arrays sized for H (ceil(T / C) + N) chunk slots.  Errors as
+ * la_chunk_bwd, plus LA_ERR_NULL for a NULL cu_seqlens.
+ */
+int la_chunk_bwd_varlen(const void* q, const void* k, const void* v,
+                        const float* log_alpha, const float* beta, const float* S0,
+                        const void* grad_out, const float* grad_S_final,
+                        const int* cu_seqlens, float* grad_q, float* grad_k,
+                        float* grad_v, float* grad_log_alpha, float* grad_beta,
+                        float* grad_S0, int N, int H, int T, int dk, int dv, int C,
+                        int mode, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* la_chunk_bwd_varlen_workspace_bytes -- workspace size for la_chunk_bwd_varlen
+ * with these sizes, mode and dtype (whatever the offsets), written to *bytes. */
+int la_chunk_bwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int C,
+                                        int mode, int dtype, size_t* bytes);
+
+/*
  * la_decode_step -- one token of the recurrence for B*H independent states
  * (decode / inference form), updating the state in place.
  *

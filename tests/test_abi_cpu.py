@@ -495,3 +495,44 @@ def test_chunk_bwd_unused_gradients_and_gates():
     assert bwd(lib, mode=0, la=None, be=None, gla=None, gbe=None,
                gq=ctypes.c_void_p(P + 64)) == ALIAS
     assert bwd(lib, mode=3, be=None, gbe=None, gq=ctypes.c_void_p(P + 64)) == ALIAS
+
+
+def bwd_varlen(lib, cu=fake(15), N=2, H=1, T=128, **kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), la=fake(3), be=fake(4), s0=fake(5), do=fake(6),
+             dsf=fake(7), gq=fake(8), gk=fake(9), gv=fake(10), gla=fake(11), gbe=fake(12),
+             gs0=fake(13), dk=64, dv=64, C=64, mode=2, dtype=1, ws=fake(14), wsb=P)
+    a.update(kw)
+    return lib.la_chunk_bwd_varlen(a["q"], a["k"], a["v"], a["la"], a["be"], a["s0"], a["do"],
+                                   a["dsf"], cu, a["gq"], a["gk"], a["gv"], a["gla"], a["gbe"],
+                                   a["gs0"], N, H, T, a["dk"], a["dv"], a["C"], a["mode"],
+                                   a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_varlen_workspace_size():
+    """Per-chunk arrays for H (ceil(T / C) + N) slots, whatever the offsets."""
+    lib = _lib.get()
+    for mode in range(4):
+        for (N, H, T, d) in ((1, 1, 64, 64), (5, 3, 200, 128), (64, 32, 65536, 128), (3, 2, 0, 64)):
+            n = ctypes.c_size_t(0)
+            assert lib.la_chunk_bwd_varlen_workspace_bytes(N, H, T, d, d, 64, mode, 1,
+                                                           ctypes.byref(n)) == OK
+            slots = H * (-(-T // 64) + N)
+            # the fixed-length formula with slots chunk-heads
+            assert n.value == expected_bwd_ws(1, slots, 64, d, mode in (1, 2))
+    n = ctypes.c_size_t(0)
+    assert lib.la_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 2,
+                                                   ctypes.byref(n)) == UNSUP
+    assert lib.la_chunk_bwd_varlen_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), NULL), (dict(q=None), NULL), (dict(gbe=None), NULL),
+    (dict(gla=None, mode=3), NULL), (dict(N=0), SHAPE), (dict(T=-1), SHAPE),
+    (dict(dk=96, dv=96), UNSUP), (dict(dtype=2), UNSUP), (dict(ws=None), WS),
+    (dict(cu=ctypes.c_void_p(9 * P)), ALIAS),          # cu_seqlens inside grad_k
+    (dict(gq=ctypes.c_void_p(15 * P)), ALIAS),         # grad_q is cu_seqlens
+])
+def test_chunk_bwd_varlen_rejects(kw, code):
+    lib = _lib.get()
+    assert bwd_varlen(lib, **kw) == code
+    assert lib.la_last_error().decode() != ""

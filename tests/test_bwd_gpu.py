@@ -149,3 +149,69 @@ def test_chunk_bwd_full_size_sampled():
     ref = reference(sub(x), sub(gr), w.mode, chunked=True)
     got = {k: (t[:, hs] if t is not None else None) for k, t in res.items()}
     compare(got, ref, w.mode, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_varlen_packed(mode, dtype, d):
+    """A packed batch of 9 sequences (empty first, middle and last; a single
+    token; partial, exact and several chunks): every gradient against the
+    token backward run per sequence; each sequence's packed gradients are
+    bit-equal to the fixed-length backward on it; empty sequences pass
+    dS_final to dS0.  Outputs start as NaN: every element must be written."""
+    from test_parity_gpu import _packed
+    lens = [0, 1, 63, 64, 0, 65, 200, 130, 0]
+    H = 3
+    w, x, S0, cu = _packed(lens, H, d, dtype, mode, seed=83)
+    log(f"case chunk_bwd_varlen {mode} {dtype} d{d} H{H} lens {lens}")
+    T = int(cu[-1])
+    N = len(lens)
+    gen = torch.Generator("cpu").manual_seed(84)
+    dout = torch.randn((H, T, d), generator=gen).to(w.torch_dtype)
+    dSf = torch.randn((N, H, d, d), generator=gen) * 0.1
+    dev = {n: t.cuda() for n, t in x.items()}
+    res = la.chunk_bwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                              S0.cuda(), dout.cuda(), cu.cuda(), dSf.cuda(), mode=mode)
+    torch.cuda.synchronize()
+    y = {n: t.to(torch.float64).numpy() for n, t in x.items()}
+    s0, go, gsf = (t.to(torch.float64).numpy() for t in (S0, dout, dSf))
+    for s in range(N):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            assert torch.equal(res["dS0"][s].cpu(), dSf[s]), f"sequence {s} (empty)"
+            continue
+        sl = lambda t: t[None, :, a:b]   # noqa: E731  -> [1, H, len, ...]
+        ref = oracle.recurrent_bwd(sl(y["q"]), sl(y["k"]), sl(y["v"]), sl(y["log_alpha"]),
+                                   sl(y["beta"]), s0[s][None], mode, sl(go), gsf[s][None])
+        got = {n: (None if t is None else (t[s][None] if n == "dS0" else t[None, :, a:b]))
+               for n, t in res.items()}
+        log(f"  sequence {s} ({b - a} tokens)")
+        compare(got, ref, mode, dtype)
+    # packed == fixed length, bit for bit
+    for s in (3, 6):
+        a, b = int(cu[s]), int(cu[s + 1])
+        one = la.chunk_bwd(*(dev[n][None, :, a:b].contiguous() for n in ("q", "k", "v")),
+                           dev["log_alpha"][None, :, a:b].contiguous(),
+                           dev["beta"][None, :, a:b].contiguous(), S0[s][None].cuda(),
+                           dout[None, :, a:b].contiguous().cuda(), dSf[s][None].cuda(),
+                           mode=mode)
+        torch.cuda.synchronize()
+        for n in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+            if one[n] is not None:
+                assert torch.equal(one[n][0], res[n][:, a:b]), f"sequence {s}: {n} differs"
+        assert torch.equal(one["dS0"][0], res["dS0"][s]), f"sequence {s}: dS0 differs"
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_deterministic(mode):
+    """Two calls on the same inputs give bit-identical gradients (every sum
+    in the kernels has a fixed order: no atomics)."""
+    w = recipe(mode, "bf16", B=1, H=4, L=2048 + 37, d=128, s0_std=0.02, seed=101)
+    log(f"case chunk_bwd_deterministic {w.name} seed={w.seed}")
+    x = workloads.make_inputs(w)
+    gr = workloads.make_upstream_grads(w, ds_std=0.05)
+    a = run_bwd(w, x, gr, mode)
+    b = run_bwd(w, x, gr, mode)
+    for n in a:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), f"{n} differs between two calls"
