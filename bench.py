@@ -644,6 +644,37 @@ def bench_varlen(base, n_seq, total, steps, warmup):
     return res
 
 
+def bench_bwd_varlen(base, n_seq, total, steps, warmup):
+    """la_chunk_bwd_varlen over the packed batch of bench_varlen (same length
+    mix, upstream gradients N(0, 1)): tokens/s and per-kernel times."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    lens = varlen_lengths(n_seq, total, seed=base.seed + 7)
+    w = base.scaled(name=f"varlen_{base.mode}_{base.dtype}_n{n_seq}h{base.H}t{total}d{base.dk}",
+                    B=1, L=total, s0_std=0.0)
+    log(f"[bench] packed backward {w.name}: generating inputs")
+    x = workloads.make_inputs(w)
+    d = {k: t[0].contiguous().cuda() for k, t in x.items() if k != "S0"}
+    gr = workloads.make_upstream_grads(w, ds_std=0.0)
+    dout = gr["dout"][0].contiguous().cuda()
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32,
+                      device="cuda")
+    nws = la.chunk_bwd_varlen_workspace_bytes(n_seq, w.H, total, w.dk, w.dv, mode=w.mode,
+                                              dtype=w.torch_dtype)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ms, kernels = _timed(lambda: la.chunk_bwd_varlen(d["q"], d["k"], d["v"], d["log_alpha"],
+                                                     d["beta"], None, dout, cu, mode=w.mode,
+                                                     workspace=ws), steps, warmup)
+    del d, dout, ws
+    torch.cuda.empty_cache()
+    return {"workload": "backward_" + w.name, "mode": w.mode, "sequences": n_seq,
+            "tokens": total, "length_min": min(lens), "length_max": max(lens),
+            "tokens_per_s": round(total / ms * 1e3, 1), "ms_per_step": round(ms, 4),
+            "kernels": kernels}
+
 def bench_decode(w, warmup=1):
     import torch
 
@@ -777,6 +808,7 @@ def main():
             "fused": bench_fused(w, args.steps, 1),
             "noncausal": bench_noncausal(workloads.WORKLOADS[2], args.steps, 1),
             "backward": bench_backward(w, args.steps, 1, args.bwd_cpu_tokens),
+            "backward_varlen": bench_bwd_varlen(w, 64, w.L, args.steps, 1),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
