@@ -788,9 +788,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
 // ------------------------------------------------------- reverse walk
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ beta,
-    const T* __restrict__ dout, const float* __restrict__ dS_final, float* __restrict__ dv_out,
-    float* __restrict__ dS0, BwdWs ws, SeqMap sm, int BH) {
+    const T* __restrict__ k, const float* __restrict__ beta, const float* __restrict__ dS_final,
+    float* __restrict__ dv_out, float* __restrict__ dS0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int PE = 16 / sizeof(T);
@@ -1374,9 +1373,8 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
-                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), a.beta, static_cast<const T*>(a.dout),
-                       a.dS_final, a.dv, a.dS0, ws, seq_map(a), BH);
+                       dim3(kThreads), 0, st, static_cast<const T*>(a.k), a.beta, a.dS_final,
+                       a.dv, a.dS0, ws, seq_map(a), BH);
     return hipGetLastError();
   });
 }

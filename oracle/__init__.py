@@ -45,7 +45,7 @@ from .recurrence import (  # noqa: F401
     recurrent_fwd,
     recurrent_step,
 )
-from .prologue import l2_normalise, prepare, sigmoid, softplus  # noqa: F401
+from .prologue import l2_normalise, prepare, prologue_bwd, sigmoid, softplus  # noqa: F401
 from .epilogue import add_dskip, out_norm  # noqa: F401
 from .noncausal import noncausal_fwd  # noqa: F401
 from .backward import recurrent_bwd  # noqa: F401

@@ -21,11 +21,20 @@ Test infrastructure (see the package docstring).  float64 NumPy only.
 The library routines ``scipy.special.expit`` (the logistic function) and
 ``numpy.logaddexp`` (log(e^x + e^y), here log(1 + e^a)) serve as steps.
 
+``prologue_bwd`` carries the gradients of the op's prepared inputs back to
+the raw ones by the chain rule, one step per activation: for x_hat = x r,
+r = (|x|^2 + eps)^(-1/2), dx = r (dx_hat - x_hat (x_hat . dx_hat)); for
+beta = sigmoid(b), db = dbeta sigmoid(b) (1 - sigmoid(b)); for log alpha =
+-gate_scale softplus(a), da = -gate_scale sigmoid(a) dlog_alpha (the
+derivative of softplus is the logistic function).
+
 Parity status: pinned in tests/test_oracle_pins.py by closed forms
 (sigmoid(0) = 1/2, sigmoid(log 3) = 3/4, softplus(0) = log 2,
 softplus(log(e - 1)) = 1, softplus(a) - softplus(-a) = a), by the norm of a
 normalised vector in closed form, and by the scale invariance of the whole
-op under normalisation.
+op under normalisation; ``prologue_bwd`` composed with the recurrence's
+backward by central finite differences of the loss in the raw inputs, for
+every mode and flag set.
 """
 import numpy as np
 import scipy.special
@@ -64,3 +73,30 @@ def prepare(q, k, a, b, mode, flags, gate_scale):
         if mode in ERASE_MODES:
             beta = sigmoid(b)
     return q, k, log_alpha, beta
+
+
+def prologue_bwd(q, k, a, b, mode, flags, gate_scale, dq, dk, dlog_alpha, dbeta):
+    """Gradients of the raw inputs of ``prepare`` from those of its outputs.
+
+    ``q, k, a, b`` are the raw inputs (as for ``prepare``); ``dq, dk,
+    dlog_alpha, dbeta`` the gradients of the prepared q, k, log alpha and
+    beta (None where the mode has none).  Returns (dq_raw, dk_raw, da, db).
+    """
+    dq = np.asarray(dq, dtype=np.float64)
+    dk = np.asarray(dk, dtype=np.float64)
+    if flags & QK_L2NORM:
+        out = []
+        for x, dx in ((q, dq), (k, dk)):
+            x = np.asarray(x, dtype=np.float64)
+            r = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + QK_NORM_EPS)
+            xh = x * r
+            out.append(r * (dx - xh * np.sum(xh * dx, axis=-1, keepdims=True)))
+        dq, dk = out
+    da, db = dlog_alpha, dbeta
+    if flags & GATES:
+        if mode in GATED_MODES and dlog_alpha is not None:
+            da = -gate_scale * sigmoid(a) * np.asarray(dlog_alpha, dtype=np.float64)
+        if mode in ERASE_MODES and dbeta is not None:
+            sb = sigmoid(b)
+            db = sb * (1.0 - sb) * np.asarray(dbeta, dtype=np.float64)
+    return dq, dk, da, db

@@ -673,3 +673,49 @@ def test_chunkwise_backward_equals_token_backward(mode, C):
             assert got[name] is None
             continue
         assert _rel(got[name], ref[name]) < 1e-11, (name, _rel(got[name], ref[name]))
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_prologue_backward_matches_finite_differences(mode, flags):
+    """The gradients of the raw inputs through the fused prologue (q, k
+    normalisation, gate activations) composed with the recurrence's
+    backward, against central finite differences of the loss taken through
+    prepare and the recurrence, element by element, on a tiny case."""
+    from oracle.backward import recurrent_bwd
+    rng = np.random.default_rng(71 + flags)
+    B, H, L, dk, dv = 1, 2, 5, 3, 2
+    q = rng.standard_normal((B, H, L, dk))
+    k = rng.standard_normal((B, H, L, dk))
+    v = rng.standard_normal((B, H, L, dv))
+    a = rng.standard_normal((B, H, L)) if flags & 1 else -0.05 + 0.01 * rng.standard_normal((B, H, L))
+    b = rng.standard_normal((B, H, L)) if flags & 1 else 0.3 + 0.4 * rng.random((B, H, L))
+    S0 = 0.1 * rng.standard_normal((B, H, dk, dv))
+    dO = rng.standard_normal((B, H, L, dv))
+    dSf = rng.standard_normal((B, H, dk, dv))
+    scale = 0.4
+
+    def loss(q, k, a, b):
+        qp, kp, la, be = oracle.prepare(q, k, a, b, mode, flags, scale)
+        return _loss(qp, kp, v, la, be, S0, mode, dO, dSf)
+
+    qp, kp, la, be = oracle.prepare(q, k, a, b, mode, flags, scale)
+    g = recurrent_bwd(qp, kp, v, la, be, S0, mode, dO, dSf)
+    dq, dk_, da, db = oracle.prologue_bwd(q, k, a, b, mode, flags, scale, g["dq"], g["dk"],
+                                          g["dlog_alpha"], g["dbeta"])
+    args = dict(q=q, k=k, a=a, b=b)
+    want = dict(q=dq, k=dk_)
+    if mode in oracle.GATED_MODES:
+        want["a"] = da
+    if mode in oracle.ERASE_MODES:
+        want["b"] = db
+    h = 1e-6
+    for name, grad in want.items():
+        x = args[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num[idx] = (loss(**{**args, name: xp}) - loss(**{**args, name: xm})) / (2 * h)
+        assert _rel(grad, num) < 1e-7, (name, _rel(grad, num))
