@@ -78,6 +78,12 @@ def _declare(lib):
     lib.la_chunk_bwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, fp, fp, fp, fp, fp,
                                         fp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_chunk_bwd_varlen.restype = i
+    lib.la_chunk_bwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                       i, i, i, i, i, i, i, i, op, vp, sz, vp]
+    lib.la_chunk_bwd_fused.restype = i
+    lib.la_chunk_bwd_fused_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, op,
+                                                       ctypes.POINTER(sz)]
+    lib.la_chunk_bwd_fused_workspace_bytes.restype = i
     lib.la_chunk_bwd_varlen_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i,
                                                         ctypes.POINTER(sz)]
     lib.la_chunk_bwd_varlen_workspace_bytes.restype = i

@@ -360,25 +360,36 @@ class kernel_timer:
 
 
 def chunk_bwd_workspace_bytes(B, H, L, dk, dv, *, mode="gated_delta", C=64,
-                              dtype=torch.bfloat16):
+                              dtype=torch.bfloat16, qk_l2norm=False, gate_act=False,
+                              fused=None):
     """Workspace bytes ``la_chunk_bwd`` needs for these sizes
-    (``la_chunk_bwd_workspace_bytes``)."""
+    (``la_chunk_bwd_workspace_bytes``), or ``la_chunk_bwd_fused`` with its
+    prologue (``la_chunk_bwd_fused_workspace_bytes``)."""
     code = _dtype_code(dtype, dtype)
     n = ctypes.c_size_t(0)
-    _lib.check(_lib.get().la_chunk_bwd_workspace_bytes(B, H, L, dk, dv, C, _mode(mode), code,
-                                                       ctypes.byref(n)))
+    opts = fused if fused is not None else _fused_opts(qk_l2norm, gate_act)
+    if opts is not None:
+        _lib.check(_lib.get().la_chunk_bwd_fused_workspace_bytes(
+            B, H, L, dk, dv, C, _mode(mode), code, ctypes.byref(opts), ctypes.byref(n)))
+    else:
+        _lib.check(_lib.get().la_chunk_bwd_workspace_bytes(B, H, L, dk, dv, C, _mode(mode),
+                                                           code, ctypes.byref(n)))
     return n.value
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, S0, dout, dS_final=None, *, mode="gated_delta",
-              C=64, workspace=None, want_dS0=True):
+              C=64, workspace=None, want_dS0=True, qk_l2norm=False, gate_act=False,
+              gate_scale=1.0 / 16.0):
     """Gradients of ``chunk_fwd`` (``la_chunk_bwd``) for upstream gradients
     ``dout [B, H, L, dv]`` (the inputs' dtype) and ``dS_final [B, H, dk, dv]``
-    float32 (or None: zero).
+    float32 (or None: zero).  With ``qk_l2norm`` / ``gate_act`` the
+    gradients of the fused forward's raw inputs (``la_chunk_bwd_fused``):
+    q, k unnormalised, log_alpha and beta the raw scores a and b.
 
     Returns a dict of float32 tensors ``dq, dk, dv [B, H, L, d]``,
-    ``dlog_alpha, dbeta [B, H, L]`` (None where the mode does not read the
-    gate) and ``dS0 [B, H, dk, dv]`` (None unless ``want_dS0``).
+    ``dlog_alpha, dbeta [B, H, L]`` (the gradients of the gate arguments
+    passed -- the raw scores with ``gate_act``; None where the mode does not
+    read the gate) and ``dS0 [B, H, dk, dv]`` (None unless ``want_dS0``).
     ``workspace`` is an optional uint8 device tensor of at least
     ``chunk_bwd_workspace_bytes(...)`` bytes.
     """
@@ -403,12 +414,23 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, dout, dS_final=None, *, mode="gated_
            "dlog_alpha": torch.empty((B, H, L), **f32) if m in _DECAY else None,
            "dbeta": torch.empty((B, H, L), **f32) if m in _ERASE else None,
            "dS0": torch.empty((B, H, dk, dv), **f32) if want_dS0 else None}
-    need = chunk_bwd_workspace_bytes(B, H, L, dk, dv, mode=mode, C=C, dtype=dt)
+    opts = _fused_opts(qk_l2norm, gate_act, gate_scale)
+    need = chunk_bwd_workspace_bytes(B, H, L, dk, dv, mode=mode, C=C, dtype=dt, fused=opts)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
     lib = _lib.get()
+    if opts is not None:
+        with torch.cuda.device(dev):
+            rc = lib.la_chunk_bwd_fused(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha if m in _DECAY else None),
+                _ptr(beta if m in _ERASE else None), _ptr(S0), _ptr(dout), _ptr(dS_final),
+                _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dlog_alpha"]),
+                _ptr(res["dbeta"]), _ptr(res["dS0"]), B, H, L, dk, dv, C, m, _DTYPES[dt],
+                ctypes.byref(opts), _ptr(workspace), workspace.numel(), _stream(dev))
+        _lib.check(rc)
+        return res
     with torch.cuda.device(dev):
         rc = lib.la_chunk_bwd(_ptr(q), _ptr(k), _ptr(v),
                               _ptr(log_alpha if m in _DECAY else None),

@@ -426,6 +426,43 @@ int run_bwd(const la::BwdArgs& a, size_t n_x, size_t n_g, size_t n_s, int dtype,
   return LA_OK;
 }
 
+// Workspace of la_chunk_bwd_fused: the prologue's arrays (normalised q and
+// k in the input type, their inverse norms, the activated gates), each
+// 256-byte aligned, then the backward's own workspace.
+struct ProWs {
+  size_t qn, kn, rq, rk, la, be, core;   // byte offsets
+  size_t bytes;                          // in all
+};
+
+ProWs pro_ws(const la::BwdArgs& a, int flags) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)a.B * a.H * a.L;
+  const size_t esz = a.in_bf16 ? 2 : 4;
+  const bool norm = flags & LA_PRO_QK_L2NORM, gates = flags & LA_PRO_GATES;
+  ProWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) { const size_t o = off; off += al(n); return o; };
+  w.qn = take(norm ? rows * a.d * esz : 0);
+  w.kn = take(norm ? rows * a.d * esz : 0);
+  w.rq = take(norm ? rows * 4 : 0);
+  w.rk = take(norm ? rows * 4 : 0);
+  w.la = take(gates && la::mode_decay(a.mode) ? rows * 4 : 0);
+  w.be = take(gates && la::mode_erase(a.mode) ? rows * 4 : 0);
+  w.core = off;
+  w.bytes = off + la::bwd_workspace_bytes(a);
+  return w;
+}
+
+// Fused flags the backward takes: the prologue's (the epilogue's backward is
+// not built).
+int check_bwd_fused(const la_fused_opts_t* opts, int mode, Fused* f) {
+  if (int e = check_fused(opts, mode, f)) return e;
+  if (f->flags & (LA_EPI_DSKIP | LA_EPI_OUT_NORM))
+    return fail(LA_ERR_UNSUPPORTED, "la_chunk_bwd_fused takes LA_PRO_GATES and "
+                                    "LA_PRO_QK_L2NORM only (no backward of the epilogue)");
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -532,6 +569,91 @@ int la_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float
   a.cu = cu_seqlens;
   return run_bwd(a, n_x, n_g, n_s, dtype, workspace_bytes, (size_t)(N + 1) * sizeof(int),
                  stream);
+}
+
+int la_chunk_bwd_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C, int mode,
+                                       int dtype, const la_fused_opts_t* opts, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(LA_ERR_NULL, "bytes is required");
+  if (int e = check_bwd_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  Fused f;
+  if (int e = check_bwd_fused(opts, mode, &f)) return e;
+  *bytes = pro_ws(bwd_args(B, H, L, dk, mode, dtype, nullptr), f.flags).bytes;
+  return LA_OK;
+}
+
+int la_chunk_bwd_fused(const void* q, const void* k, const void* v, const float* a_raw,
+                       const float* b_raw, const float* S0, const void* grad_out,
+                       const float* grad_S_final, float* grad_q, float* grad_k, float* grad_v,
+                       float* grad_a, float* grad_b, float* grad_S0, int B, int H, int L,
+                       int dk, int dv, int C, int mode, int dtype, const la_fused_opts_t* opts,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (int e = check_bwd_args(q, k, v, a_raw, b_raw, grad_out, grad_q, grad_k, grad_v, grad_a,
+                             grad_b, mode, dtype))
+    return e;
+  if (int e = check_bwd_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  Fused f;
+  if (int e = check_bwd_fused(opts, mode, &f)) return e;
+  size_t n_x, n_g, n_s;
+  if (!count({B, H, L, dk}, &n_x) || !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  la::BwdArgs a = bwd_args(B, H, L, dk, mode, dtype, nullptr);
+  const ProWs w = pro_ws(a, f.flags);
+  if (!workspace)
+    return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(w.bytes) +
+                                      " bytes (la_chunk_bwd_fused_workspace_bytes)");
+  if (workspace_bytes < w.bytes)
+    return fail(LA_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                      " bytes, this call needs " + std::to_string(w.bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  // the raw inputs against the outputs and the whole workspace (the backward
+  // proper checks what it reads from the workspace itself)
+  const bool gated = la::mode_decay(mode), erase = la::mode_erase(mode);
+  const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
+  const Range rq(q, n_x * esz), rk(k, n_x * esz), ra(gated ? a_raw : nullptr, n_g * 4);
+  const Range rb(erase ? b_raw : nullptr, n_g * 4), rws(workspace, w.bytes);
+  const Range oq(grad_q, n_x * 4), ok(grad_k, n_x * 4), ov(grad_v, n_x * 4);
+  const Range oa(gated ? grad_a : nullptr, n_g * 4), ob(erase ? grad_b : nullptr, n_g * 4);
+  const Range os0(grad_S0, n_s * 4);
+  for (const Range* in : {&rq, &rk, &ra, &rb})
+    for (const Range* out : {&oq, &ok, &ov, &oa, &ob, &os0, &rws})
+      if (in->overlaps(*out))
+        return fail(LA_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
+  char* base = static_cast<char*>(workspace);
+  const bool norm = f.flags & LA_PRO_QK_L2NORM;
+  const bool ga = (f.flags & LA_PRO_GATES) && gated, gb = (f.flags & LA_PRO_GATES) && erase;
+  la::BwdProArgs p{};
+  p.q = q; p.k = k; p.a_raw = a_raw; p.b_raw = b_raw;
+  p.qn = base + w.qn; p.kn = base + w.kn;
+  p.rq = reinterpret_cast<float*>(base + w.rq); p.rk = reinterpret_cast<float*>(base + w.rk);
+  p.la = reinterpret_cast<float*>(base + w.la); p.be = reinterpret_cast<float*>(base + w.be);
+  p.dq = grad_q; p.dk = grad_k; p.da = grad_a; p.db = grad_b;
+  p.rows = n_g; p.d = dk; p.in_bf16 = dtype != LA_DTYPE_F32;
+  p.norm = norm; p.gates_a = ga; p.gates_b = gb; p.scale = f.gate_scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool any = norm || ga || gb;
+  if (any) {
+    hipEvent_t e0 = prof_mark(st);
+    const hipError_t e = la::launch_bwd_pro(p, false, st);
+    prof_add("la_bwd_pro", e0, prof_mark(st));
+    if (e != hipSuccess) return fail_hip("launching the backward prologue", e);
+  }
+  a.workspace = base + w.core;
+  a.q = norm ? p.qn : q; a.k = norm ? p.kn : k; a.v = v;
+  a.log_alpha = ga ? p.la : a_raw; a.beta = gb ? p.be : b_raw; a.S0 = S0;
+  a.dout = grad_out; a.dS_final = grad_S_final;
+  a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_a; a.dbeta = grad_b;
+  a.dS0 = grad_S0;
+  if (int e = run_bwd(a, n_x, n_g, n_s, dtype, w.bytes - w.core, 0, stream)) return e;
+  if (any) {
+    hipEvent_t e0 = prof_mark(st);
+    const hipError_t e = la::launch_bwd_pro(p, true, st);
+    prof_add("la_bwd_pro_grad", e0, prof_mark(st));
+    if (e != hipSuccess) return fail_hip("launching the backward prologue's gradients", e);
+  }
+  return LA_OK;
 }
 
 int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv, int dtype,

@@ -1307,6 +1307,93 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   }
 }
 
+// ------------------------------------------------------ fused prologue
+// The fused forward's prologue, for its backward: per token row, the op's
+// inputs from the raw ones -- q and k normalised, x r with r = (|x|^2 +
+// 1e-6)^(-1/2); beta = sigmoid(b); log alpha = -scale softplus(a) -- and,
+// after the backward proper, the chain rule back to the raw inputs:
+// dx = r (dx_hat - x_hat (x_hat . dx_hat)), db = dbeta sigmoid(b)(1 -
+// sigmoid(b)), da = -scale sigmoid(a) dlog_alpha.  One wave per row.
+constexpr int kProRows = kThreads / kWave;
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplusf(float x) {
+  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a_raw,
+    const float* __restrict__ b_raw, T* __restrict__ qn, T* __restrict__ kn,
+    float* __restrict__ rq, float* __restrict__ rk, float* __restrict__ la,
+    float* __restrict__ be, size_t rows, int norm, int gates_a, int gates_b, float scale) {
+  constexpr int E = D / kWave;
+  const int lane = threadIdx.x % kWave;
+  const size_t row = (size_t)blockIdx.x * kProRows + threadIdx.x / kWave;
+  if (row >= rows) return;
+  if (norm) {
+    const T* src[2] = {q, k};
+    T* dst[2] = {qn, kn};
+    float* rr[2] = {rq, rk};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float x[E], ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        x[e] = to_f32(src[m][row * D + lane + kWave * e]);
+        ss += x[e] * x[e];
+      }
+      const float r = 1.f / sqrtf(sum64(ss) + kQKNormEps);
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[m][row * D + lane + kWave * e] = from_f32<T>(x[e] * r);
+      if (lane == 0) rr[m][row] = r;
+    }
+  }
+  if (lane == 0) {
+    if (gates_a) la[row] = -scale * softplusf(a_raw[row]);
+    if (gates_b) be[row] = sigmoidf(b_raw[row]);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_pro_grad_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a_raw,
+    const float* __restrict__ b_raw, const float* __restrict__ rq, const float* __restrict__ rk,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ da,
+    float* __restrict__ db, size_t rows, int norm, int gates_a, int gates_b, float scale) {
+  constexpr int E = D / kWave;
+  const int lane = threadIdx.x % kWave;
+  const size_t row = (size_t)blockIdx.x * kProRows + threadIdx.x / kWave;
+  if (row >= rows) return;
+  if (norm) {
+    const T* src[2] = {q, k};
+    const float* rr[2] = {rq, rk};
+    float* g[2] = {dq, dk};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float r = rr[m][row];
+      float xh[E], dx[E], dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const size_t i = row * D + lane + kWave * e;
+        xh[e] = to_f32(src[m][i]) * r;
+        dx[e] = g[m][i];
+        dot += xh[e] * dx[e];
+      }
+      dot = sum64(dot);
+#pragma unroll
+      for (int e = 0; e < E; ++e) g[m][row * D + lane + kWave * e] = r * (dx[e] - xh[e] * dot);
+    }
+  }
+  if (lane == 0) {
+    if (gates_a) da[row] = -scale * sigmoidf(a_raw[row]) * da[row];
+    if (gates_b) {
+      const float s = sigmoidf(b_raw[row]);
+      db[row] = s * (1.f - s) * db[row];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launch
 template <typename X>
 struct Type {
@@ -1392,6 +1479,31 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st) {
                        seq_map(a));
     return hipGetLastError();
   });
+}
+
+hipError_t launch_bwd_pro(const BwdProArgs& p, bool grad, hipStream_t st) {
+  if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((p.rows + kProRows - 1) / kProRows);
+  auto go = [&](auto t, auto d) -> hipError_t {
+    using T = typename decltype(t)::type;
+    constexpr int D = decltype(d)::value;
+    if (!grad)
+      hipLaunchKernelGGL((bwd_pro_kernel<T, D>), dim3(grid), dim3(kThreads), 0, st,
+                         static_cast<const T*>(p.q), static_cast<const T*>(p.k), p.a_raw,
+                         p.b_raw, static_cast<T*>(p.qn), static_cast<T*>(p.kn), p.rq, p.rk,
+                         p.la, p.be, p.rows, p.norm, p.gates_a, p.gates_b, p.scale);
+    else
+      hipLaunchKernelGGL((bwd_pro_grad_kernel<T, D>), dim3(grid), dim3(kThreads), 0, st,
+                         static_cast<const T*>(p.q), static_cast<const T*>(p.k), p.a_raw,
+                         p.b_raw, p.rq, p.rk, p.dq, p.dk, p.da, p.db, p.rows, p.norm,
+                         p.gates_a, p.gates_b, p.scale);
+    return hipGetLastError();
+  };
+  if (p.in_bf16)
+    return p.d == 64 ? go(Type<__bf16>{}, std::integral_constant<int, 64>{})
+                     : go(Type<__bf16>{}, std::integral_constant<int, 128>{});
+  return p.d == 64 ? go(Type<float>{}, std::integral_constant<int, 64>{})
+                   : go(Type<float>{}, std::integral_constant<int, 128>{});
 }
 
 }  // namespace la

@@ -47,4 +47,31 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st);
 
 
+// The fused prologue around the backward (la_chunk_bwd_fused): per token
+// row, normalised q and k with their inverse norms, and the activated
+// gates (grad = false); after the backward, the chain rule back to the raw
+// inputs, in place on the gradients (grad = true).
+struct BwdProArgs {
+  const void* q;          // raw q, k [rows, d], the input type
+  const void* k;
+  const float* a_raw;     // raw gate scores [rows]
+  const float* b_raw;
+  void* qn;               // normalised q, k [rows, d] (written)
+  void* kn;
+  float* rq;              // inverse norms [rows]
+  float* rk;
+  float* la;              // -scale softplus(a), sigmoid(b) [rows] (written)
+  float* be;
+  float* dq;              // gradients, transformed in place
+  float* dk;
+  float* da;
+  float* db;
+  size_t rows;
+  int d;
+  bool in_bf16;
+  int norm, gates_a, gates_b;
+  float scale;
+};
+hipError_t launch_bwd_pro(const BwdProArgs& p, bool grad, hipStream_t st);
+
 }  // namespace la

@@ -469,6 +469,38 @@ int la_chunk_bwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int
                                         int mode, int dtype, size_t* bytes);
 
 /*
+ * la_chunk_bwd_fused -- the gradients of la_chunk_fwd_fused with respect to
+ * its raw inputs, for the prologue's flags: with LA_PRO_QK_L2NORM q and k are
+ * the unnormalised vectors and grad_q, grad_k their gradients; with
+ * LA_PRO_GATES a_raw and b_raw are the raw gate scores and grad_a, grad_b
+ * their gradients (da = -gate_scale sigmoid(a) dlog_alpha, db = sigmoid(b)
+ * (1 - sigmoid(b)) dbeta; for x_hat = x / sqrt(|x|^2 + 1e-6), dx = (dx_hat -
+ * x_hat (x_hat . dx_hat)) / sqrt(|x|^2 + 1e-6)).  A prologue kernel writes the
+ * prepared inputs into the workspace, la_chunk_bwd runs on them, and a last
+ * kernel applies the chain rule in place.  Arguments, layouts and errors as
+ * la_chunk_bwd (a_raw, b_raw in place of log_alpha, beta; grad_a, grad_b in
+ * place of their gradients); opts as la_chunk_fwd_fused, where the epilogue
+ * flags (LA_EPI_DSKIP, LA_EPI_OUT_NORM) return LA_ERR_UNSUPPORTED: their
+ * backward is not built.  NULL opts or flags = 0 is la_chunk_bwd.
+ *   workspace  at least la_chunk_bwd_fused_workspace_bytes() bytes, 16-byte
+ *              aligned: the prepared q, k (input type) and inverse norms,
+ *              the activated gates, then la_chunk_bwd's workspace
+ */
+int la_chunk_bwd_fused(const void* q, const void* k, const void* v,
+                       const float* a_raw, const float* b_raw, const float* S0,
+                       const void* grad_out, const float* grad_S_final, float* grad_q,
+                       float* grad_k, float* grad_v, float* grad_a, float* grad_b,
+                       float* grad_S0, int B, int H, int L, int dk, int dv, int C,
+                       int mode, int dtype, const la_fused_opts_t* opts, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* la_chunk_bwd_fused_workspace_bytes -- workspace size for la_chunk_bwd_fused
+ * with these sizes, mode, dtype and options, written to *bytes. */
+int la_chunk_bwd_fused_workspace_bytes(int B, int H, int L, int dk, int dv, int C,
+                                       int mode, int dtype, const la_fused_opts_t* opts,
+                                       size_t* bytes);
+
+/*
  * la_decode_step -- one token of the recurrence for B*H independent states
  * (decode / inference form), updating the state in place.
  *

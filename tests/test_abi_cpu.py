@@ -536,3 +536,45 @@ def test_chunk_bwd_varlen_rejects(kw, code):
     lib = _lib.get()
     assert bwd_varlen(lib, **kw) == code
     assert lib.la_last_error().decode() != ""
+
+
+_Opts = _lib.FusedOpts
+
+
+def test_bwd_fused_workspace_size():
+    """The prologue's arrays (normalised q, k in the input type, inverse
+    norms, activated gates), each 256-byte aligned, then the backward's
+    own workspace."""
+    lib = _lib.get()
+    pad = lambda n: -(-n // 256) * 256     # noqa: E731
+    for mode in range(4):
+        for flags in (0, 1, 2, 3):
+            for (B, H, L, d, dtype) in ((1, 1, 64, 64, 1), (2, 3, 200, 128, 0)):
+                n = ctypes.c_size_t(0)
+                o = _Opts(flags, 0.0625, None, None, 0.0)
+                assert lib.la_chunk_bwd_fused_workspace_bytes(
+                    B, H, L, d, d, 64, mode, dtype, ctypes.byref(o), ctypes.byref(n)) == OK
+                rows, esz = B * H * L, 2 if dtype == 1 else 4
+                extra = 0
+                if flags & 2:
+                    extra += 2 * pad(rows * d * esz) + 2 * pad(rows * 4)
+                if flags & 1:
+                    extra += pad(rows * 4) * ((mode in (2, 3)) + (mode in (1, 2)))
+                assert n.value == extra + expected_bwd_ws(B, H, L, d, mode in (1, 2))
+
+
+@pytest.mark.parametrize("flags,scale,eps,code", [
+    (4, 0.0625, 0.0, NULL),            # LA_EPI_DSKIP without dskip (options checked first)
+    (8, 0.0625, 1e-6, UNSUP),          # LA_EPI_OUT_NORM: no backward
+    (1, 0.0, 0.0, UNSUP),              # gate_scale must be positive
+    (16, 0.0625, 0.0, UNSUP),          # unknown flag
+])
+def test_chunk_bwd_fused_rejects(flags, scale, eps, code):
+    lib = _lib.get()
+    o = _Opts(flags, scale, None, None, eps)
+    rc = lib.la_chunk_bwd_fused(fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
+                                fake(7), fake(8), fake(9), fake(10), fake(11), fake(12),
+                                fake(13), 1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o), fake(14),
+                                P, None)
+    assert rc == code
+    assert lib.la_last_error().decode() != ""

@@ -215,3 +215,42 @@ def test_chunk_bwd_deterministic(mode):
     for n in a:
         if a[n] is not None:
             assert torch.equal(a[n], b[n]), f"{n} differs between two calls"
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_fused_prologue(mode, dtype, d, flags):
+    """The gradients of the fused forward's raw inputs (unnormalised q, k
+    with flag 2; raw gate scores with flag 1) against the oracle's backward
+    through prepare and the recurrence, every element."""
+    w = recipe(mode, dtype, B=2, H=1, L=131, d=d, s0_std=0.05, seed=111 + flags)
+    log(f"case chunk_bwd_fused {mode} {dtype} d{d} flags={flags} seed={w.seed}")
+    r = workloads.make_raw_inputs(w)
+    scale = 1.0 / 16.0
+    q, k, a, b = r["q"], r["k"], r["a_raw"], r["b_raw"]
+    if not flags & 2:      # the op takes q, k as given: hand it normalised ones
+        q = (q.float() / torch.linalg.vector_norm(q.float(), dim=-1, keepdim=True)).to(q.dtype)
+        k = (k.float() / torch.linalg.vector_norm(k.float(), dim=-1, keepdim=True)).to(k.dtype)
+    if not flags & 1:      # the op takes the gates as given
+        a = -scale * torch.nn.functional.softplus(a)
+        b = torch.sigmoid(b)
+    gr = workloads.make_upstream_grads(w, ds_std=0.1)
+    x = dict(q=q, k=k, v=r["v"], log_alpha=a, beta=b, S0=r["S0"])
+    dev = to_cuda(x)
+    g = to_cuda(gr)
+    res = la.chunk_bwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], dev["S0"],
+                       g["dout"], g["dS_final"], mode=mode, qk_l2norm=bool(flags & 2),
+                       gate_act=bool(flags & 1), gate_scale=scale)
+    torch.cuda.synchronize()
+    y = workloads.to_f64(x)
+    gy = workloads.to_f64(gr)
+    qp, kp, lp, bp = oracle.prepare(y["q"], y["k"], y["log_alpha"], y["beta"], mode, flags,
+                                    scale)
+    ref = oracle.recurrent_bwd(qp, kp, y["v"], lp, bp, y["S0"], mode, gy["dout"],
+                               gy["dS_final"])
+    dq, dk_, da, db = oracle.prologue_bwd(y["q"], y["k"], y["log_alpha"], y["beta"], mode, flags,
+                                          scale, ref["dq"], ref["dk"], ref["dlog_alpha"],
+                                          ref["dbeta"])
+    ref = dict(ref, dq=dq, dk=dk_, dlog_alpha=da, dbeta=db)
+    compare(res, ref, mode, dtype)
