@@ -644,6 +644,31 @@ def bench_varlen(base, n_seq, total, steps, warmup):
     return res
 
 
+def bench_bwd_fused(w, steps, warmup):
+    """la_chunk_bwd_fused (q, k normalisation and the gate activations inside)
+    at a forward workload's sizes, from the raw inputs: tokens/s and the
+    per-kernel times (the prologue and its gradients are two extra kernels)."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    log(f"[bench] fused backward {w.name}: generating inputs")
+    r = {k: t.cuda() for k, t in workloads.make_raw_inputs(w).items()}
+    gr = {k: t.cuda() for k, t in workloads.make_upstream_grads(w, ds_std=0.02).items()}
+    nws = la.chunk_bwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode,
+                                       dtype=w.torch_dtype, qk_l2norm=True, gate_act=True)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ms, kernels = _timed(lambda: la.chunk_bwd(r["q"], r["k"], r["v"], r["a_raw"], r["b_raw"],
+                                              r["S0"], gr["dout"], gr["dS_final"], mode=w.mode,
+                                              workspace=ws, qk_l2norm=True, gate_act=True),
+                         steps, warmup)
+    del r, gr, ws
+    torch.cuda.empty_cache()
+    return {"workload": "backward_fused_" + w.name, "mode": w.mode,
+            "steps_fused": "qk_l2norm, gate_act", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.B * w.L / ms * 1e3, 1), "kernels": kernels}
+
 def bench_bwd_varlen(base, n_seq, total, steps, warmup):
     """la_chunk_bwd_varlen over the packed batch of bench_varlen (same length
     mix, upstream gradients N(0, 1)): tokens/s and per-kernel times."""
@@ -809,6 +834,7 @@ def main():
             "noncausal": bench_noncausal(workloads.WORKLOADS[2], args.steps, 1),
             "backward": bench_backward(w, args.steps, 1, args.bwd_cpu_tokens),
             "backward_varlen": bench_bwd_varlen(w, 64, w.L, args.steps, 1),
+            "backward_fused": bench_bwd_fused(w, args.steps, 1),
         }
     cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
