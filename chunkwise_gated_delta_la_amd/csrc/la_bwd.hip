@@ -1313,12 +1313,55 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 // 1e-6)^(-1/2); beta = sigmoid(b); log alpha = -scale softplus(a) -- and,
 // after the backward proper, the chain rule back to the raw inputs:
 // dx = r (dx_hat - x_hat (x_hat . dx_hat)), db = dbeta sigmoid(b)(1 -
-// sigmoid(b)), da = -scale sigmoid(a) dlog_alpha.  One wave per row.
-constexpr int kProRows = kThreads / kWave;
+// sigmoid(b)), da = -scale sigmoid(a) dlog_alpha.  d / 8 lanes per row.
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + __expf(-x)); }
 __device__ __forceinline__ float softplusf(float x) {
   return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+
+// Lanes per token row: each lane holds 8 consecutive elements (16 bytes of
+// bf16, two 16-byte vectors of float).
+template <int D>
+constexpr int pro_lanes() { return D / 8; }
+
+// Sum over the `W` lanes of a row group (W = 8 or 16, aligned groups).
+template <int W>
+__device__ __forceinline__ float sum_lanes(float x) {
+  if constexpr (W >= 16) x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 1);
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&x)[8]) {
+  if constexpr (IsBf16<T>::value) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
+  if constexpr (IsBf16<T>::value) {
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (__bf16)x[j];
+    *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
 }
 
 template <typename T, int D>
@@ -1327,9 +1370,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
     const float* __restrict__ b_raw, T* __restrict__ qn, T* __restrict__ kn,
     float* __restrict__ rq, float* __restrict__ rk, float* __restrict__ la,
     float* __restrict__ be, size_t rows, int norm, int gates_a, int gates_b, float scale) {
-  constexpr int E = D / kWave;
-  const int lane = threadIdx.x % kWave;
-  const size_t row = (size_t)blockIdx.x * kProRows + threadIdx.x / kWave;
+  constexpr int W = pro_lanes<D>();
+  const int sub = threadIdx.x % W;
+  const size_t row = (size_t)blockIdx.x * (kThreads / W) + threadIdx.x / W;
   if (row >= rows) return;
   if (norm) {
     const T* src[2] = {q, k};
@@ -1337,19 +1380,19 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
     float* rr[2] = {rq, rk};
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      float x[E], ss = 0.f;
+      float x[8];
+      load8(src[m] + row * D + 8 * sub, x);
+      float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        x[e] = to_f32(src[m][row * D + lane + kWave * e]);
-        ss += x[e] * x[e];
-      }
-      const float r = 1.f / sqrtf(sum64(ss) + kQKNormEps);
+      for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
+      const float r = 1.f / sqrtf(sum_lanes<W>(ss) + kQKNormEps);
 #pragma unroll
-      for (int e = 0; e < E; ++e) dst[m][row * D + lane + kWave * e] = from_f32<T>(x[e] * r);
-      if (lane == 0) rr[m][row] = r;
+      for (int j = 0; j < 8; ++j) x[j] *= r;
+      store8(dst[m] + row * D + 8 * sub, x);
+      if (sub == 0) rr[m][row] = r;
     }
   }
-  if (lane == 0) {
+  if (sub == 0) {
     if (gates_a) la[row] = -scale * softplusf(a_raw[row]);
     if (gates_b) be[row] = sigmoidf(b_raw[row]);
   }
@@ -1361,9 +1404,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_grad_kernel(
     const float* __restrict__ b_raw, const float* __restrict__ rq, const float* __restrict__ rk,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ da,
     float* __restrict__ db, size_t rows, int norm, int gates_a, int gates_b, float scale) {
-  constexpr int E = D / kWave;
-  const int lane = threadIdx.x % kWave;
-  const size_t row = (size_t)blockIdx.x * kProRows + threadIdx.x / kWave;
+  constexpr int W = pro_lanes<D>();
+  const int sub = threadIdx.x % W;
+  const size_t row = (size_t)blockIdx.x * (kThreads / W) + threadIdx.x / W;
   if (row >= rows) return;
   if (norm) {
     const T* src[2] = {q, k};
@@ -1372,20 +1415,22 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_grad_kernel(
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float r = rr[m][row];
-      float xh[E], dx[E], dot = 0.f;
+      float xh[8], dx[8];
+      load8(src[m] + row * D + 8 * sub, xh);
+      load8(g[m] + row * D + 8 * sub, dx);
+      float dot = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const size_t i = row * D + lane + kWave * e;
-        xh[e] = to_f32(src[m][i]) * r;
-        dx[e] = g[m][i];
-        dot += xh[e] * dx[e];
+      for (int j = 0; j < 8; ++j) {
+        xh[j] *= r;
+        dot += xh[j] * dx[j];
       }
-      dot = sum64(dot);
+      dot = sum_lanes<W>(dot);
 #pragma unroll
-      for (int e = 0; e < E; ++e) g[m][row * D + lane + kWave * e] = r * (dx[e] - xh[e] * dot);
+      for (int j = 0; j < 8; ++j) dx[j] = r * (dx[j] - xh[j] * dot);
+      store8(g[m] + row * D + 8 * sub, dx);
     }
   }
-  if (lane == 0) {
+  if (sub == 0) {
     if (gates_a) da[row] = -scale * sigmoidf(a_raw[row]) * da[row];
     if (gates_b) {
       const float s = sigmoidf(b_raw[row]);
@@ -1483,10 +1528,11 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_pro(const BwdProArgs& p, bool grad, hipStream_t st) {
   if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((p.rows + kProRows - 1) / kProRows);
   auto go = [&](auto t, auto d) -> hipError_t {
     using T = typename decltype(t)::type;
     constexpr int D = decltype(d)::value;
+    constexpr size_t per_block = kThreads / pro_lanes<D>();
+    const unsigned grid = (unsigned)((p.rows + per_block - 1) / per_block);
     if (!grad)
       hipLaunchKernelGGL((bwd_pro_kernel<T, D>), dim3(grid), dim3(kThreads), 0, st,
                          static_cast<const T*>(p.q), static_cast<const T*>(p.k), p.a_raw,
