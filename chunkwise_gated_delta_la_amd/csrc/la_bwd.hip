@@ -345,14 +345,21 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 // three staging waves in one batch (every load issued, at clamped indices,
 // before the first LDS write), then written to one half of the walk's
 // double buffer.  Rows past the end of the sequence read as zero.
-template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false>
+//
+// With KT (bf16) the staging also writes K^T ([D][C + 4]) for the chain's
+// K^T operands: each thread loads the same 16 bytes of two consecutive rows
+// and writes the transposed pairs as 32-bit words.
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false, bool KT = false>
 struct ChunkStage {
   static constexpr int NT = kThreads - kWave;
   static constexpr int PE = 16 / sizeof(T);
   static constexpr int LDK = D + PE;
+  static constexpr int LDKT = C + 4;              // row pitch of K^T (KT)
   static constexpr int VPR = D / PE;
   static constexpr int NK = C * VPR;
-  static constexpr int IK = (NK + NT - 1) / NT;
+  static constexpr int NPK = NK / 2;              // row-pair items (KT)
+  static constexpr int IP = (NPK + NT - 1) / NT;
+  static constexpr int IK = KT ? 2 * IP : (NK + NT - 1) / NT;
   static constexpr int NTV = C * C / 4;
   static constexpr int IT = ERASE ? (NTV + NT - 1) / NT : 1;
   static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
@@ -386,11 +393,25 @@ struct ChunkStage {
         x2[i] = *reinterpret_cast<const f32x4*>(X2g + (size_t)(p / 4) * D + col0 + 4 * (p % 4));
       }
     }
+    if constexpr (KT) {
 #pragma unroll
-    for (int i = 0; i < IK; ++i) {
-      const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
-      kx[i] = r < nrows ? x : z;
+      for (int i = 0; i < IP; ++i) {
+        const int p = min(t + i * NT, NPK - 1), r = 2 * (p / VPR), cv = p % VPR;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(
+              k + (row0 + min(r + h, nrows - 1)) * D + cv * PE);
+          kx[2 * i + h] = r + h < nrows ? x : z;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IK; ++i) {
+        const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
+        const u32x4 x =
+            *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
+        kx[i] = r < nrows ? x : z;
+      }
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -418,7 +439,7 @@ struct ChunkStage {
 
   __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* fsb,
                                         float* bsb, int t, float* X1b = nullptr,
-                                        float* X2b = nullptr) const {
+                                        float* X2b = nullptr, T* KTb = nullptr) const {
     if constexpr (WITH_X) {
 #pragma unroll
       for (int i = 0; i < IX1; ++i) {
@@ -431,10 +452,31 @@ struct ChunkStage {
         if (p < NX2) *reinterpret_cast<f32x4*>(X2b + (p / 4) * LDX + 4 * (p % 4)) = x2[i];
       }
     }
+    if constexpr (KT) {
 #pragma unroll
-    for (int i = 0; i < IK; ++i) {
-      const int p = t + i * NT;
-      if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
+      for (int i = 0; i < IP; ++i) {
+        const int p = t + i * NT;
+        if (p < NPK) {
+          const int r = 2 * (p / VPR), c0 = (p % VPR) * PE;
+          *reinterpret_cast<u32x4*>(Kb + r * LDK + c0) = kx[2 * i];
+          *reinterpret_cast<u32x4*>(Kb + (r + 1) * LDK + c0) = kx[2 * i + 1];
+          const u32x4 a = kx[2 * i], b = kx[2 * i + 1];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // elements 2w, 2w + 1 of both rows: (a lo, b lo), (a hi, b hi)
+            const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
+            const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(KTb + (c0 + 2 * w) * LDKT + r) = lo;
+            *reinterpret_cast<uint32_t*>(KTb + (c0 + 2 * w + 1) * LDKT + r) = hi;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IK; ++i) {
+        const int p = t + i * NT;
+        if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
+      }
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -633,7 +675,11 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
 
+  // bf16: K^T staged transposed for the chain's K^T operands
+  constexpr bool kKt = IsBf16<T>::value;
+  constexpr int LDKT = C + 4;
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
+  __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
   __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
   __shared__ __attribute__((aligned(16))) float SxT[2][16 * (D + 4)];            // S entering
@@ -656,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   // Waves 1-3 stage the chain's operands: chunk c's loads go out during the
   // step two before its use and land in LDS during the step before it (the
   // barriers wait for LDS traffic only, so the loads stay in flight).
-  ChunkStage<T, D, kErase, true> st;
+  ChunkStage<T, D, kErase, true, false, kKt> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -665,7 +711,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
             tid - kWave);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tid - kWave);
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tid - kWave, nullptr,
+             nullptr, KTb[b]);
   };
 
   f32x4 S[NKT];
@@ -778,7 +825,9 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
         for (int e = 0; e < 4; ++e) S[tj][e] *= gamC;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bX[kb], S[tj]);
+          mma_ab2(kKt ? frag_row(&KTb[b][(16 * tj + n) * LDKT + 32 * kb], g)
+                      : frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g),
+                  bX[kb], S[tj]);
       }
     }
     __syncthreads();
@@ -796,7 +845,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
 
+  constexpr bool kKt = IsBf16<T>::value;
+  constexpr int LDKT = C + 4;
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
+  __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
   __shared__ __attribute__((aligned(16))) float X1[2][C * LDX];   // P^T dO (16 columns)
   __shared__ __attribute__((aligned(16))) float X2[2][D * LDX];   // Q^T diag(gam) dO
@@ -833,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   // Waves 1-3 stage the chain's operands of each chunk -- K, T, the gates and
   // the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO (formed
   // in parallel beforehand) -- two chunks ahead, as in the forward walk.
-  ChunkStage<T, D, kErase, false, true> st;
+  ChunkStage<T, D, kErase, false, true, kKt> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -843,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   };
   auto store = [&](int b) {
     st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tid - kWave, X1[b],
-             X2[b]);
+             X2[b], KTb[b]);
   };
 
   f32x4 dS[NKT];
@@ -949,7 +1001,9 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma_ab2(frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g), bR[kb], dS[tj]);
+            mma_ab2(kKt ? frag_row(&KTb[b][(16 * tj + n) * LDKT + 32 * kb], g)
+                        : frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g),
+                    bR[kb], dS[tj]);
         }
       } else {
 #pragma unroll
