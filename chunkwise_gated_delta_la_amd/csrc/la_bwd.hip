@@ -81,10 +81,12 @@ struct BwdWs {
   float* U;     // [BH, NC * C, D]  T R (erase modes)
   float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
   float* dR;    // [BH, NC * C, D]  T^T dU (erase modes)
-  float* X1;    // [BH, NC * C, D]  P^T dO
-  float* X2;    // [BH, NC, D, D]   Q^T diag(gam) dO
+  float* X1;    // [BH, NC, D, C]   (P^T dO)^T: per chunk, column-major
+  float* X2;    // [BH, NC, D, D]   (Q^T diag(gam) dO)^T: per chunk, column-major
+  float* TT;    // [BH, NC, C, C]   T^T, in SplitMat form (erase modes)
   size_t nS;    // elements of Sent and dSx
   size_t nU;    // elements of U and dR
+  size_t nT;    // elements of TT
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -103,16 +105,17 @@ size_t slots(const BwdArgs& a) {
 size_t carve(const BwdArgs& a, BwdWs* ws) {
   const size_t ns = slots(a), D = a.d;
   const bool erase = mode_erase(a.mode);
-  const size_t n[8] = {ns * C,     erase ? ns * C * C : 0, ns * D * D, erase ? ns * C * D : 0,
-                       ns * D * D, erase ? ns * C * D : 0, ns * C * D, ns * D * D};
-  float* p[8];
+  const size_t n[9] = {ns * C,     erase ? ns * C * C : 0, ns * D * D, erase ? ns * C * D : 0,
+                       ns * D * D, erase ? ns * C * D : 0, ns * C * D, ns * D * D,
+                       erase ? ns * C * C : 0};
+  float* p[9];
   size_t off = 0;
   char* base = static_cast<char*>(a.workspace);
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 9; ++i) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], n[2], n[3]};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], n[2], n[3], n[8]};
   return off;
 }
 
@@ -349,7 +352,12 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 // With KT (bf16) the staging also writes K^T ([D][C + 4]) for the chain's
 // K^T operands: each thread loads the same 16 bytes of two consecutive rows
 // and writes the transposed pairs as 32-bit words.
-template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false, bool KT = false>
+//
+// With TS (the reverse walk) T comes as T^T in SplitMat form: for bf16 its
+// hi and lo planes are staged as two bf16 [C][C + 8] tiles, the chain's
+// split operands as they are; for float as the float tile.
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false, bool KT = false,
+          bool TS = false>
 struct ChunkStage {
   static constexpr int NT = kThreads - kWave;
   static constexpr int PE = 16 / sizeof(T);
@@ -360,12 +368,15 @@ struct ChunkStage {
   static constexpr int NPK = NK / 2;              // row-pair items (KT)
   static constexpr int IP = (NPK + NT - 1) / NT;
   static constexpr int IK = KT ? 2 * IP : (NK + NT - 1) / NT;
-  static constexpr int NTV = C * C / 4;
+  static constexpr int NTV = C * C / 4;          // 16-byte vectors of T (either form)
+  static constexpr bool kTPlanes = TS && IsBf16<T>::value;
+  static constexpr int LDTT = C + 8;              // row pitch of the bf16 T^T planes
   static constexpr int IT = ERASE ? (NTV + NT - 1) / NT : 1;
   static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
   static constexpr int NV = C * VV;
   static constexpr int IV = WITH_V ? (NV + NT - 1) / NT : 1;
-  static constexpr int NX1 = C * 4, NX2 = D * 4;  // 16-float rows of X1, X2: 4 vectors
+  // 16 columns of X1^T [D][C] and X2^T [D][D]: 16 rows of C / 4 and D / 4 vectors
+  static constexpr int NX1 = 16 * C / 4, NX2 = 16 * D / 4;
   static constexpr int IX1 = WITH_X ? (NX1 + NT - 1) / NT : 1;
   static constexpr int IX2 = WITH_X ? (NX2 + NT - 1) / NT : 1;
   u32x4 kx[IK];
@@ -378,19 +389,22 @@ struct ChunkStage {
                                        const float* __restrict__ beta, const float* Tg,
                                        const float* gg, size_t row0, int nrows, int col0,
                                        int t, const float* X1g = nullptr,
-                                       const float* X2g = nullptr) {
+                                       const float* X2g = nullptr, const T* Th = nullptr,
+                                       const T* Tl = nullptr) {
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     if constexpr (WITH_X) {
       // 16 columns (col0 ..) of the chunk's X1 [C, D] and X2 [D, D]
 #pragma unroll
       for (int i = 0; i < IX1; ++i) {
         const int p = min(t + i * NT, NX1 - 1);
-        x1[i] = *reinterpret_cast<const f32x4*>(X1g + (size_t)(p / 4) * D + col0 + 4 * (p % 4));
+        x1[i] = *reinterpret_cast<const f32x4*>(X1g + (size_t)(col0 + p / (C / 4)) * C +
+                                                4 * (p % (C / 4)));
       }
 #pragma unroll
       for (int i = 0; i < IX2; ++i) {
         const int p = min(t + i * NT, NX2 - 1);
-        x2[i] = *reinterpret_cast<const f32x4*>(X2g + (size_t)(p / 4) * D + col0 + 4 * (p % 4));
+        x2[i] = *reinterpret_cast<const f32x4*>(X2g + (size_t)(col0 + p / (D / 4)) * D +
+                                                4 * (p % (D / 4)));
       }
     }
     if constexpr (KT) {
@@ -416,8 +430,16 @@ struct ChunkStage {
     if constexpr (ERASE) {
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
-        const int p = min(t + i * NT, NTV - 1), r = p / (C / 4), cv = p % (C / 4);
-        tx[i] = *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
+        const int p = min(t + i * NT, NTV - 1);
+        if constexpr (kTPlanes) {
+          // plane p / 512, row (p % 512) / 8, 8 elements from (p % 8) * 8
+          const int pl = p / (NTV / 2), rem = p % (NTV / 2);
+          const T* src = (pl ? Tl : Th) + (rem / 8) * C + 8 * (rem % 8);
+          tx[i] = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4*>(src));
+        } else {
+          const int r = p / (C / 4), cv = p % (C / 4);
+          tx[i] = *reinterpret_cast<const f32x4*>(Tg + r * C + 4 * cv);
+        }
       }
     }
     if constexpr (WITH_V) {
@@ -444,12 +466,14 @@ struct ChunkStage {
 #pragma unroll
       for (int i = 0; i < IX1; ++i) {
         const int p = t + i * NT;
-        if (p < NX1) *reinterpret_cast<f32x4*>(X1b + (p / 4) * LDX + 4 * (p % 4)) = x1[i];
+        if (p < NX1)
+          *reinterpret_cast<f32x4*>(X1b + (p / (C / 4)) * (C + 4) + 4 * (p % (C / 4))) = x1[i];
       }
 #pragma unroll
       for (int i = 0; i < IX2; ++i) {
         const int p = t + i * NT;
-        if (p < NX2) *reinterpret_cast<f32x4*>(X2b + (p / 4) * LDX + 4 * (p % 4)) = x2[i];
+        if (p < NX2)
+          *reinterpret_cast<f32x4*>(X2b + (p / (D / 4)) * (D + 4) + 4 * (p % (D / 4))) = x2[i];
       }
     }
     if constexpr (KT) {
@@ -482,7 +506,15 @@ struct ChunkStage {
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
         const int p = t + i * NT;
-        if (p < NTV) *reinterpret_cast<f32x4*>(Tb + (p / (C / 4)) * LDC + 4 * (p % (C / 4))) = tx[i];
+        if (p < NTV) {
+          if constexpr (kTPlanes) {
+            const int pl = p / (NTV / 2), rem = p % (NTV / 2);
+            T* dst = reinterpret_cast<T*>(Tb) + pl * C * LDTT + (rem / 8) * LDTT + 8 * (rem % 8);
+            *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, tx[i]);
+          } else {
+            *reinterpret_cast<f32x4*>(Tb + (p / (C / 4)) * LDC + 4 * (p % (C / 4))) = tx[i];
+          }
+        }
       }
     }
     if constexpr (WITH_V) {
@@ -630,11 +662,20 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     }
 #pragma unroll
     for (int r = 0; r < C; ++r) ws.T[(cid * C + r) * C + lane] = x[r];
+    // row `lane` of T^T, in the operand form of the reverse walk
+    const SplitMat<T> Tt = SplitMat<T>::make(ws.TT, ws.nT);
+#pragma unroll
+    for (int q8 = 0; q8 < C / 8; ++q8) {
+      const float y[8] = {x[8 * q8], x[8 * q8 + 1], x[8 * q8 + 2], x[8 * q8 + 3],
+                          x[8 * q8 + 4], x[8 * q8 + 5], x[8 * q8 + 6], x[8 * q8 + 7]};
+      Tt.put8((cid * C + lane) * C + 8 * q8, y);
+    }
     return;
   }
 
   // X1 tiles (rows i of P^T, columns j of dO): 4 x NT16; X2 tiles: NT16 x NT16,
-  // over the waves not solving T
+  // over the waves not solving T; both stored transposed (per column), the
+  // layout the reverse walk stages 16 columns of
   constexpr int N1 = 4 * NT16, N2 = NT16 * NT16;
   const int w0 = kErase ? 1 : 0, nw = kWaves - w0;
   for (int t = wave - w0; t < N1 + N2; t += nw) {
@@ -646,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       for (int kb = 0; kb < 2; ++kb)
         mma_a2b(frag2_rowx<T>(Pt + (r0 + n) * LDC + 32 * kb, g),
                 frag_row(OT + (c0 + n) * LDT + 32 * kb, g), acc);
-      out = ws.X1 + (cid * C + r0) * D + c0;
+      out = ws.X1 + (cid * D + c0 + n) * C + r0;
     } else {
       const int r0 = 16 * ((t - N1) / NT16), c0 = 16 * ((t - N1) % NT16);
 #pragma unroll
@@ -657,10 +698,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
         for (int j = 0; j < 8; ++j) x[j] = to_f32(o.v[j]) * gam[32 * kb + kidx(g, j)];
         mma_ab2(frag_row(QT + (r0 + n) * LDT + 32 * kb, g), frag2_of<T>(x), acc);
       }
-      out = ws.X2 + (cid * D + r0) * D + c0;
+      out = ws.X2 + (cid * D + c0 + n) * D + r0;
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[(size_t)(4 * g + e) * D + n] = acc[e];
+    // transposed: this lane's four rows are contiguous
+    *reinterpret_cast<f32x4*>(out + 4 * g) = acc;
   }
 }
 
@@ -845,13 +886,18 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
 
-  constexpr bool kKt = IsBf16<T>::value;
+  constexpr bool kKt = false;     // (no room for a transposed K next to the T^T planes)
   constexpr int LDKT = C + 4;
+  constexpr bool kTPlanes = IsBf16<T>::value;
+  constexpr int LDTT = C + 8;
+  // T^T: bf16 hi and lo planes [C][C + 8] (bf16 inputs) or float [C][C + 4]
+  constexpr int kTWords = kTPlanes ? C * LDTT : C * LDC;   // floats per buffer
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
   __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
-  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
-  __shared__ __attribute__((aligned(16))) float X1[2][C * LDX];   // P^T dO (16 columns)
-  __shared__ __attribute__((aligned(16))) float X2[2][D * LDX];   // Q^T diag(gam) dO
+  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? kTWords : 4];
+  // 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO, transposed
+  __shared__ __attribute__((aligned(16))) float X1[2][16 * (C + 4)];
+  __shared__ __attribute__((aligned(16))) float X2[2][16 * (D + 4)];
   __shared__ __attribute__((aligned(16))) float dSxT[2][16 * (D + 4)];             // dS'
   __shared__ __attribute__((aligned(16))) float dRxT[2][kErase ? 16 * (C + 4) : 4];  // dR
   __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
@@ -885,13 +931,21 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   // Waves 1-3 stage the chain's operands of each chunk -- K, T, the gates and
   // the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO (formed
   // in parallel beforehand) -- two chunks ahead, as in the forward walk.
-  ChunkStage<T, D, kErase, false, true, kKt> st;
+  ChunkStage<T, D, kErase, false, true, kKt, true> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
     const size_t cid = si.slot0 + c;
-    st.load(k, nullptr, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0,
-            nrows, col0, tid - kWave, ws.X1 + cid * C * D, ws.X2 + cid * D * D);
+    const SplitMat<T> Tt = SplitMat<T>::make(ws.TT, ws.nT);
+    const T* th = nullptr;
+    const T* tl = nullptr;
+    if constexpr (kTPlanes && kErase) {
+      th = Tt.p + cid * C * C;
+      tl = Tt.p + Tt.plane + cid * C * C;
+    }
+    st.load(k, nullptr, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr,
+            ws.g + cid * C, row0, nrows, col0, tid - kWave, ws.X1 + cid * C * D,
+            ws.X2 + cid * D * D, th, tl);
   };
   auto store = [&](int b) {
     st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tid - kWave, X1[b],
@@ -956,12 +1010,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           mma_ab2(frag_row(&Kb[b][(16 * ti + n) * LDK + 32 * kb], g), bS[kb], y);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&X1[b][n * (C + 4) + 16 * ti + 4 * g]);
+        const f32x4 fr = *reinterpret_cast<const f32x4*>(fc + 16 * ti + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ti + 4 * g + e;
-          const float f = kGated ? fc[r] : 1.f;
-          dU[ti][e] = X1[b][r * LDX + n] + f * y[e];
-        }
+        for (int e = 0; e < 4; ++e) dU[ti][e] = x1[e] + (kGated ? fr[e] : 1.f) * y[e];
       }
       float* dvo = dv_out + row0 * D + col0 + n;
       if constexpr (kErase) {
@@ -973,7 +1025,17 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
           dR[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma_a2b2(frag2_col<T>(&Tb[b][32 * kb * LDC + 16 * ti + n], LDC, g), bU[kb], dR[ti]);
+          {
+            Frag2<T> at;
+            if constexpr (kTPlanes) {
+              const T* tp = reinterpret_cast<const T*>(Tb[b]) + (16 * ti + n) * LDTT + 32 * kb;
+              at.hi = frag_row(tp, g);
+              at.lo = frag_row(tp + C * LDTT, g);
+            } else {
+              at = frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g);
+            }
+            mma_a2b2(at, bU[kb], dR[ti]);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti + 4 * g + e;
@@ -996,9 +1058,11 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
         }
 #pragma unroll
         for (int tj = 0; tj < NKT; ++tj) {
+          {
+            const f32x4 x2 = *reinterpret_cast<const f32x4*>(&X2[b][n * (D + 4) + 16 * tj + 4 * g]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
+            for (int e = 0; e < 4; ++e) dS[tj][e] = gamC * dS[tj][e] + x2[e];
+          }
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
             mma_ab2(kKt ? frag_row(&KTb[b][(16 * tj + n) * LDKT + 32 * kb], g)
@@ -1014,10 +1078,11 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             if (r < nrows) dvo[(size_t)r * D] = dU[ti][e];
           }
 #pragma unroll
-        for (int tj = 0; tj < NKT; ++tj)
+        for (int tj = 0; tj < NKT; ++tj) {
+          const f32x4 x2 = *reinterpret_cast<const f32x4*>(&X2[b][n * (D + 4) + 16 * tj + 4 * g]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dS[tj][e] = gamC * dS[tj][e] + X2[b][(16 * tj + 4 * g + e) * LDX + n];
+          for (int e = 0; e < 4; ++e) dS[tj][e] = gamC * dS[tj][e] + x2[e];
+        }
       }
     }
     __syncthreads();

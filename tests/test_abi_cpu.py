@@ -452,6 +452,8 @@ def expected_bwd_ws(B, H, L, d, erase):
     bh = B * H
     arrays = [bh * nc * 64, bh * nc * d * d, bh * nc * d * d, bh * nc * 64 * d, bh * nc * d * d]
     if erase:
+        arrays += [bh * nc * 64 * 64]             # T^T for the reverse walk
+    if erase:
         arrays += [bh * nc * 64 * 64, bh * nc * 64 * d, bh * nc * 64 * d]
     return sum(pad(n) for n in arrays)
 
