@@ -356,8 +356,11 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 // With TS (the reverse walk) T comes as T^T in SplitMat form: for bf16 its
 // hi and lo planes are staged as two bf16 [C][C + 8] tiles, the chain's
 // split operands as they are; for float as the float tile.
+//
+// With SPL (the forward walk, bf16) T comes as float rows and is split into
+// the same bf16 hi and lo planes on its way into LDS.
 template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false, bool KT = false,
-          bool TS = false>
+          bool TS = false, bool SPL = false>
 struct ChunkStage {
   static constexpr int NT = kThreads - kWave;
   static constexpr int PE = 16 / sizeof(T);
@@ -370,6 +373,7 @@ struct ChunkStage {
   static constexpr int IK = KT ? 2 * IP : (NK + NT - 1) / NT;
   static constexpr int NTV = C * C / 4;          // 16-byte vectors of T (either form)
   static constexpr bool kTPlanes = TS && IsBf16<T>::value;
+  static constexpr bool kTSplit = SPL && IsBf16<T>::value;
   static constexpr int LDTT = C + 8;              // row pitch of the bf16 T^T planes
   static constexpr int IT = ERASE ? (NTV + NT - 1) / NT : 1;
   static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
@@ -511,6 +515,15 @@ struct ChunkStage {
             const int pl = p / (NTV / 2), rem = p % (NTV / 2);
             T* dst = reinterpret_cast<T*>(Tb) + pl * C * LDTT + (rem / 8) * LDTT + 8 * (rem % 8);
             *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, tx[i]);
+          } else if constexpr (kTSplit) {
+            // row p / 16, four columns from 4 (p % 16): hi and lo parts
+            uint32_t h0, l0, h1, l1;
+            split_pair(tx[i][0], tx[i][1], h0, l0);
+            split_pair(tx[i][2], tx[i][3], h1, l1);
+            T* dst = reinterpret_cast<T*>(Tb) + (p / (C / 4)) * LDTT + 4 * (p % (C / 4));
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{h0, h1};
+            *reinterpret_cast<u32x2*>(dst + C * LDTT) = u32x2{l0, l1};
           } else {
             *reinterpret_cast<f32x4*>(Tb + (p / (C / 4)) * LDC + 4 * (p % (C / 4))) = tx[i];
           }
@@ -716,12 +729,16 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
 
-  // bf16: K^T staged transposed for the chain's K^T operands
+  // bf16: K^T staged transposed for the chain's K^T operands, and T as its
+  // bf16 hi and lo planes [C][C + 8]
   constexpr bool kKt = IsBf16<T>::value;
   constexpr int LDKT = C + 4;
+  constexpr bool kTPlanes = IsBf16<T>::value;
+  constexpr int LDTT = C + 8;
+  constexpr int kTWords = kTPlanes ? C * LDTT : C * LDC;   // floats per buffer
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
   __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
-  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? C * LDC : 4];
+  __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? kTWords : 4];
   __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
   __shared__ __attribute__((aligned(16))) float SxT[2][16 * (D + 4)];            // S entering
   __shared__ __attribute__((aligned(16))) float UxT[2][kErase ? 16 * (C + 4) : 4];  // U
@@ -743,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   // Waves 1-3 stage the chain's operands: chunk c's loads go out during the
   // step two before its use and land in LDS during the step before it (the
   // barriers wait for LDS traffic only, so the loads stay in flight).
-  ChunkStage<T, D, kErase, true, false, kKt> st;
+  ChunkStage<T, D, kErase, true, false, kKt, false, true> st;
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -841,7 +858,17 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
           U[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma_a2b2(frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g), bR[kb], U[ti]);
+          {
+            Frag2<T> at;
+            if constexpr (kTPlanes) {
+              const T* tp = reinterpret_cast<const T*>(Tb[b]) + (16 * ti + n) * LDTT + 32 * kb;
+              at.hi = frag_row(tp, g);
+              at.lo = frag_row(tp + C * LDTT, g);
+            } else {
+              at = frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g);
+            }
+            mma_a2b2(at, bR[kb], U[ti]);
+          }
         }
         tile_put<C>(UxT[b], U, g, n);
 #pragma unroll
