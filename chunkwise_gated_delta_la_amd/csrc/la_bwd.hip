@@ -927,6 +927,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   __shared__ __attribute__((aligned(16))) float X2[2][16 * (D + 4)];
   __shared__ __attribute__((aligned(16))) float dSxT[2][16 * (D + 4)];             // dS'
   __shared__ __attribute__((aligned(16))) float dRxT[2][kErase ? 16 * (C + 4) : 4];  // dR
+  // dv (beta dR, or dU) handed over like dR where LDS allows (not float at
+  // d = 128: the chain stores it itself there)
+  constexpr bool kDvTile = IsBf16<T>::value || D == 64;
+  __shared__ __attribute__((aligned(16))) float dvxT[2][kDvTile ? 16 * (C + 4) : 4];
   __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
@@ -1006,6 +1010,22 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       if constexpr (kErase)
         tile_flush<T, D, C>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0,
                             tid - kWave, kThreads - kWave);
+      if constexpr (kDvTile) {
+        // dv rows of the chunk (those inside the sequence), 8 columns a thread
+        const int nrows = min(C, L - c * C);
+        float* dvc = dv_out + (si.row0 + (size_t)c * C) * D + col0;
+        for (int p = tid - kWave; p < 2 * C; p += kThreads - kWave) {
+          const int r = p / 2, c0 = 8 * (p % 2);
+          if (r < nrows) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = dvxT[b][(c0 + j) * (C + 4) + r];
+            *reinterpret_cast<f32x4*>(dvc + (size_t)r * D + c0) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4*>(dvc + (size_t)r * D + c0 + 4) =
+                f32x4{x[4], x[5], x[6], x[7]};
+          }
+        }
+      }
     };
     for (int s = 0; s < NC; ++s) {
       if (s >= 1) flush(s - 1);
@@ -1063,13 +1083,26 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             }
             mma_a2b2(at, bU[kb], dR[ti]);
           }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti + 4 * g + e;
-            if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
-          }
         }
         tile_put<C>(dRxT[b], dR, g, n);
+        if constexpr (kDvTile) {
+          f32x4 dvv[4];
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&bsb[b][16 * ti + 4 * g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dvv[ti][e] = br[e] * dR[ti][e];
+          }
+          tile_put<C>(dvxT[b], dvv, g, n);
+        } else {
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * ti + 4 * g + e;
+              if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
+            }
+        }
         // dS <- gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR
         Frag2<T> bR[2];
 #pragma unroll
@@ -1097,13 +1130,17 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
                     bR[kb], dS[tj]);
         }
       } else {
+        if constexpr (kDvTile) {
+          tile_put<C>(dvxT[b], dU, g, n);
+        } else {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+          for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti + 4 * g + e;
-            if (r < nrows) dvo[(size_t)r * D] = dU[ti][e];
-          }
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * ti + 4 * g + e;
+              if (r < nrows) dvo[(size_t)r * D] = dU[ti][e];
+            }
+        }
 #pragma unroll
         for (int tj = 0; tj < NKT; ++tj) {
           const f32x4 x2 = *reinterpret_cast<const f32x4*>(&X2[b][n * (D + 4) + 16 * tj + 4 * g]);
