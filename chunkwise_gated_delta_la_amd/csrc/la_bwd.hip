@@ -592,9 +592,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) T QT[D * LDT];
   __shared__ __attribute__((aligned(16))) T OT[D * LDT];
 
-  // Q and dO rows, transposed into LDS (rows past the end as zero)
+  // Q and dO rows, transposed into LDS (rows past the end as zero); the
+  // row index runs fastest across lanes, so a transposed write of one
+  // column touches consecutive LDS words
   for (int p = tid; p < 2 * C * VPR; p += kThreads) {
-    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem / VPR, c0 = (rem % VPR) * PE;
+    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem % C, c0 = (rem / C) * PE;
     const T* src = (m == 0 ? q : dout) + (row0 + min(r, nrows - 1)) * D + c0;
     T* dst = m == 0 ? QT : OT;
 #pragma unroll
