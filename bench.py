@@ -553,7 +553,7 @@ def bwd_kernel_bytes(name, w):
     st = bh * nc * d * d * 4       # one state per chunk-head
     S = bh * d * d * 4             # one state per head
     return {
-        "la_bwd_prep": tok * (3 * d * esz + 8) + ptok * 4 + (cc if erase else 0)
+        "la_bwd_prep": tok * (3 * d * esz + 8) + ptok * 4 + (2 * cc if erase else 0)
                        + ptok * d * 4 + st,
         "la_bwd_states": tok * (2 * d * esz + 8) + ptok * 4 + (cc if erase else 0) + S + st
                          + (ptok * d * 4 if erase else 0),
