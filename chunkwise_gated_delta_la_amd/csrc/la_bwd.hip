@@ -1170,11 +1170,12 @@ __device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
 }
 
 // One column tile of the C x D phase, staged in LDS by all waves: the 16
-// rows of S and dS' (B^T operands: hi and lo planes for bf16 inputs) and
-// the 16 columns of K and Q (B operands of the products over the chunk, and
-// the row dots).  Loaded into registers one tile ahead, stored after the
-// barrier that ends the previous tile.
-template <typename T, int D>
+// rows of S and dS' (B^T operands: hi and lo planes for bf16 inputs) and,
+// with kQK, the 16 columns of K and Q (B operands of the products over the
+// chunk, and the row dots; without it the kernel holds whole K and Q rows).
+// Loaded into registers one tile ahead, stored after the barrier that ends
+// the previous tile.
+template <typename T, int D, bool kQK>
 struct ColStage {
   static constexpr bool kSplit = IsBf16<T>::value;
   static constexpr int PE = 16 / sizeof(T);
@@ -1185,9 +1186,9 @@ struct ColStage {
   static constexpr int NS = NP * 16 * VPRD;       // state vectors (1024)
   static constexpr int IS = NS / kThreads;
   static constexpr int VV = 16 / PE;              // vectors per 16-column token row
-  static constexpr int NQ = 2 * C * VV;
+  static constexpr int NQ = kQK ? 2 * C * VV : 0;
   static constexpr int IQ = (NQ + kThreads - 1) / kThreads;
-  u32x4 sx[IS], qx[IQ];
+  u32x4 sx[IS], qx[IQ > 0 ? IQ : 1];
 
   __device__ __forceinline__ void load(const SplitMat<T>& Sm, const SplitMat<T>& dSm, size_t s0,
                                        const T* kc, const T* qc, int nrows, int cb0, int t) {
@@ -1246,7 +1247,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   constexpr bool kGated = mode_decay(MODE);
   constexpr bool kSplit = IsBf16<T>::value;
   constexpr int NKB = D / 32, NCT = D / 16;
-  using CS = ColStage<T, D>;
+  // K and Q rows of the chunk staged in LDS once (rows of 256 bytes at
+  // most), read by both product phases; wider rows (float, d = 128) go by
+  // 16-column slices with each column tile
+  constexpr bool kFull = D * (int)sizeof(T) <= 256;
+  using CS = ColStage<T, D, !kFull>;
+  constexpr int LDK = D + CS::PE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave, g = lane / 16, n = lane % 16;
@@ -1269,11 +1275,20 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ __attribute__((aligned(16))) float gam[C];
   __shared__ __attribute__((aligned(16))) float fs[C];
   __shared__ __attribute__((aligned(16))) float bs[C];
-  __shared__ __attribute__((aligned(16))) float Em[C * LDC];
-  __shared__ __attribute__((aligned(16))) float Hm[kErase ? C * LDC : 4];
-  __shared__ __attribute__((aligned(16))) T Sb[CS::NP * 16 * CS::LDB];
-  __shared__ __attribute__((aligned(16))) T Kcs[C * CS::LDQ];
-  __shared__ __attribute__((aligned(16))) T Qcs[C * CS::LDQ];
+  // the C x C tiles E and H live until each wave holds its fragments of
+  // them; the column-tile staging reuses their bytes after that
+  constexpr int kEH = (kErase ? 2 : 1) * C * LDC * (int)sizeof(float);
+  constexpr int kStage =
+      (CS::NP * 16 * CS::LDB + (kFull ? 0 : 2 * C * CS::LDQ)) * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) float pool[(kEH > kStage ? kEH : kStage) / 4];
+  __shared__ __attribute__((aligned(16))) T KQ[kFull ? 2 * C * LDK : 8];
+  float* const Em = pool;
+  float* const Hm = pool + C * LDC;
+  T* const Sb = reinterpret_cast<T*>(pool);
+  T* const Kcs = Sb + CS::NP * 16 * CS::LDB;
+  T* const Qcs = Kcs + C * CS::LDQ;
+  T* const Kl = KQ;
+  T* const Ql = KQ + C * LDK;
   __shared__ float dgam[C], dfv[C], vdr[C];
   // per-tile partial sums, added in a fixed order (deterministic results):
   // row sums of GG and of dA * (K K^T * Gamma) by column tile, column sums
@@ -1281,7 +1296,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ float rsP[3][4][C];   // [0]: GG rows, [1]: dbeta rows, [2]: GG columns
   __shared__ float red[kWaves];
 
-  // the first column tile's loads go out first
+  // K and Q rows (zero past nrows), then the first column tile's loads
+  constexpr int VR = D * (int)sizeof(T) / 16;      // 16-byte vectors per row
+  constexpr int IK = kFull ? 2 * C * VR / kThreads : 0;
+  u32x4 kq[IK > 0 ? IK : 1];
+#pragma unroll
+  for (int i = 0; i < IK; ++i) {
+    const int p = tid + i * kThreads, m = p / (C * VR), r = (p / VR) % C, c = p % VR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>((m == 0 ? kc : qc) +
+                                                   (size_t)min(r, nrows - 1) * D + c * CS::PE);
+    kq[i] = r < nrows ? x : u32x4{0u, 0u, 0u, 0u};
+  }
   CS st;
   st.load(Sm, dSm, s0, kc, qc, nrows, 0, tid);
 
@@ -1294,6 +1319,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     gs[tid] = gg;
     gam[tid] = kGated ? __expf(gg) : 1.f;
     bs[tid] = (kErase && tid < nrows) ? beta[row0 + tid] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < IK; ++i) {
+    const int p = tid + i * kThreads, m = p / (C * VR), r = (p / VR) % C, c = p % VR;
+    *reinterpret_cast<u32x4*>((m == 0 ? Kl : Ql) + r * LDK + c * CS::PE) = kq[i];
   }
   {
     float* part = &rsP[0][0][0];
@@ -1320,25 +1350,42 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 
   // C x C products on the lower tiles: scores, dO U^T, and (erase) K K^T,
   // dR U^T; GG = (dO U^T) * P + dA * A goes straight into its per-tile row
-  // and column sums
+  // and column sums.  Wave w owns the row block w (tiles (w, 0) .. (w, w)):
+  // its dO and dR (or V) rows load once and stay as operands of the C x D
+  // products below.
+  const int ti = wave, ra = 16 * ti + n;
+  Frag<T> aDO[NKB], aV[NKB];
+  Frag2<T> aDR[NKB], aU[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
+    if constexpr (kErase) {
+      aDR[kb] = dRm.row(u0 + (size_t)ra * D + 32 * kb, g);
+      aU[kb] = Um.row(u0 + (size_t)ra * D + 32 * kb, g);
+    } else {
+      aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
+    }
+  }
+  // a K or Q row of the chunk: from LDS when staged there, else global
+  auto kqrow = [&](const T* lds, const T* glob, int r, int c0) {
+    if constexpr (kFull) return frag_row(lds + r * LDK + c0, g);
+    else return chunk_row<T, D>(glob, r, nrows, c0, g);
+  };
 #pragma unroll 1
-  for (int t = wave; t < 10; t += kWaves) {
-    int ti, tj;
-    lower_tile(t, ti, tj);
-    const int ra = 16 * ti + n, rb = 16 * tj + n;
+  for (int tj = 0; tj <= ti; ++tj) {
+    const int rb = 16 * tj + n;
     f32x4 qk = zero4(), dp = zero4(), kk = zero4(), dru = zero4();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const Frag<T> bk = chunk_row<T, D>(kc, rb, nrows, 32 * kb, g);
-      const Frag<T> ado = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
-      mma(chunk_row<T, D>(qc, ra, nrows, 32 * kb, g), bk, qk);
+      const Frag<T> bk = kqrow(Kl, kc, rb, 32 * kb);
+      mma(kqrow(Ql, qc, ra, 32 * kb), bk, qk);
       if constexpr (kErase) {
-        mma(chunk_row<T, D>(kc, ra, nrows, 32 * kb, g), bk, kk);
+        mma(kqrow(Kl, kc, ra, 32 * kb), bk, kk);
         const Frag2<T> bu = Um.row(u0 + (size_t)rb * D + 32 * kb, g);
-        mma_ab2(ado, bu, dp);
-        mma_a2b2(dRm.row(u0 + (size_t)ra * D + 32 * kb, g), bu, dru);
+        mma_ab2(aDO[kb], bu, dp);
+        mma_a2b2(aDR[kb], bu, dru);
       } else {
-        mma(ado, chunk_row<T, D>(vc, rb, nrows, 32 * kb, g), dp);
+        mma(aDO[kb], chunk_row<T, D>(vc, rb, nrows, 32 * kb, g), dp);
       }
     }
     float csp = 0.f;
@@ -1368,7 +1415,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 
   // C x D products: wave w owns the rows 16 w .. 16 w + 15; the column
   // tiles go by in order, staged in LDS for all four waves
-  const int ti = wave, ra = 16 * ti + n;
   Frag2<T> aE[2], aEt[2], aG[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -1384,18 +1430,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
       aG[kb] = frag2_of<T>(x);
     }
   }
-  Frag<T> aDO[NKB], aV[NKB];
-  Frag2<T> aDR[NKB], aU[NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    aDO[kb] = chunk_row<T, D>(dOc, ra, nrows, 32 * kb, g);
-    if constexpr (kErase) {
-      aDR[kb] = dRm.row(u0 + (size_t)ra * D + 32 * kb, g);
-      aU[kb] = Um.row(u0 + (size_t)ra * D + 32 * kb, g);
-    } else {
-      aV[kb] = chunk_row<T, D>(vc, ra, nrows, 32 * kb, g);
-    }
-  }
   float dgc_part = 0.f;
   float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
         rdb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1405,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 #pragma unroll 1
   for (int cj = 0; cj < NCT; ++cj) {
     const int cb = 16 * cj + n;
-    if (cj > 0) __syncthreads();          // the previous tile's LDS reads are done
+    __syncthreads();   // E and H fragments taken (first tile), the previous tile's reads done
     st.store(Sb, Kcs, Qcs, tid);
     __syncthreads();
     if (cj + 1 < NCT) st.load(Sm, dSm, s0, kc, qc, nrows, 16 * (cj + 1), tid);
@@ -1431,19 +1465,23 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
         mma_ab2(aV[kb], bdS, m3);
       }
     }
+    // this column tile's K and Q columns
+    constexpr int LQ = kFull ? LDK : CS::LDQ;
+    const T* const Kt = kFull ? Kl + 16 * cj : Kcs;
+    const T* const Qt = kFull ? Ql + 16 * cj : Qcs;
     f32x4 ek = zero4(), etq = zero4(), gk = zero4();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const Frag<T> bK = frag_col(Kcs + 32 * kb * CS::LDQ + n, CS::LDQ, g);
+      const Frag<T> bK = frag_col(Kt + 32 * kb * LQ + n, LQ, g);
       mma_a2b(aE[kb], bK, ek);
-      mma_a2b(aEt[kb], frag_col(Qcs + 32 * kb * CS::LDQ + n, CS::LDQ, g), etq);
+      mma_a2b(aEt[kb], frag_col(Qt + 32 * kb * LQ + n, LQ, g), etq);
       if constexpr (kErase) mma_a2b(aG[kb], bK, gk);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ti + 4 * g + e;
-      const float qv = to_f32(Qcs[r * CS::LDQ + n]);
-      const float kv = to_f32(Kcs[r * CS::LDQ + n]);
+      const float qv = to_f32(Qt[r * LQ + n]);
+      const float kv = to_f32(Kt[r * LQ + n]);
       float dQ = gam[r] * m1[e] + ek[e];
       float dK = fs[r] * m3[e] + etq[e];
       rdg[e] += qv * m1[e];
