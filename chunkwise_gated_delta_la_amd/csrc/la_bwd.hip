@@ -592,15 +592,33 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) T QT[D * LDT];
   __shared__ __attribute__((aligned(16))) T OT[D * LDT];
 
-  // Q and dO rows, transposed into LDS (rows past the end as zero); the
-  // row index runs fastest across lanes, so a transposed write of one
-  // column touches consecutive LDS words
-  for (int p = tid; p < 2 * C * VPR; p += kThreads) {
-    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem % C, c0 = (rem / C) * PE;
-    const T* src = (m == 0 ? q : dout) + (row0 + min(r, nrows - 1)) * D + c0;
-    T* dst = m == 0 ? QT : OT;
+  // Q and dO rows, transposed into LDS (rows past the end as zero): all
+  // loads go out before the first write.  The row index runs fastest across
+  // lanes, so a transposed write of one column touches consecutive LDS words.
+  constexpr int NQV = 2 * C * VPR / kThreads;
+  u32x4 qv[NQV];
 #pragma unroll
-    for (int j = 0; j < PE; ++j) dst[(c0 + j) * LDT + r] = r < nrows ? src[j] : T(0.f);
+  for (int i = 0; i < NQV; ++i) {
+    const int p = tid + i * kThreads;
+    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem % C, c0 = (rem / C) * PE;
+    const u32x4 x = *reinterpret_cast<const u32x4*>((m == 0 ? q : dout) +
+                                                   (row0 + min(r, nrows - 1)) * D + c0);
+    qv[i] = r < nrows ? x : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < NQV; ++i) {
+    const int p = tid + i * kThreads;
+    const int m = p / (C * VPR), rem = p % (C * VPR), r = rem % C, c0 = (rem / C) * PE;
+    T* dst = (m == 0 ? QT : OT) + c0 * LDT + r;
+    if constexpr (IsBf16<T>::value) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, qv[i]);
+#pragma unroll
+      for (int j = 0; j < PE; ++j) dst[j * LDT] = x[j];
+    } else {
+      const f32x4 x = __builtin_bit_cast(f32x4, qv[i]);
+#pragma unroll
+      for (int j = 0; j < PE; ++j) dst[j * LDT] = x[j];
+    }
   }
   if (wave == 0) {
     float la = 0.f, b = 0.f;
@@ -616,16 +634,29 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   }
   __syncthreads();
 
-  for (int t = wave; t < 16; t += kWaves) {
-    const int ti = t / 4, tj = t % 4;
+  // wave w computes the tiles (ti, w): its Q (and K) rows of block w and
+  // the K rows of every block load once, up front
+  const int tj = wave;
+  Frag<T> kr[4][NKB], qb[NKB], kb2[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    qb[kb] = chunk_row<T, D>(qc, 16 * tj + n, nrows, 32 * kb, g);
+    if constexpr (kErase) kb2[kb] = chunk_row<T, D>(kc, 16 * tj + n, nrows, 32 * kb, g);
+  }
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+    if (kErase || ti <= tj)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        kr[ti][kb] = chunk_row<T, D>(kc, 16 * ti + n, nrows, 32 * kb, g);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
     // P^T tile: rows i = 16 ti + 4 g + e (keys), columns r = 16 tj + n
     // (queries), nonzero for r >= i
     f32x4 acc = zero4();
     if (tj >= ti) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mma(chunk_row<T, D>(kc, 16 * ti + n, nrows, 32 * kb, g),
-            chunk_row<T, D>(qc, 16 * tj + n, nrows, 32 * kb, g), acc);
+      for (int kb = 0; kb < NKB; ++kb) mma(kr[ti][kb], qb[kb], acc);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -639,9 +670,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       f32x4 a2 = zero4();
       if (ti >= tj) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          mma(chunk_row<T, D>(kc, 16 * ti + n, nrows, 32 * kb, g),
-              chunk_row<T, D>(kc, 16 * tj + n, nrows, 32 * kb, g), a2);
+        for (int kb = 0; kb < NKB; ++kb) mma(kr[ti][kb], kb2[kb], a2);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
