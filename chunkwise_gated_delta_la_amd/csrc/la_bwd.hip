@@ -718,34 +718,40 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   }
 
   // X1 tiles (rows i of P^T, columns j of dO): 4 x NT16; X2 tiles: NT16 x NT16,
-  // over the waves not solving T; both stored transposed (per column), the
-  // layout the reverse walk stages 16 columns of
-  constexpr int N1 = 4 * NT16, N2 = NT16 * NT16;
+  // over the waves not solving T, a column tile of dO per wave at a time (its
+  // operand and the gam-scaled split of it serve 4 + NT16 tiles); both
+  // stored transposed (per column), the layout the reverse walk stages 16
+  // columns of
   const int w0 = kErase ? 1 : 0, nw = kWaves - w0;
-  for (int t = wave - w0; t < N1 + N2; t += nw) {
-    f32x4 acc = zero4();
-    float* out;
-    if (t < N1) {
-      const int r0 = 16 * (t / NT16), c0 = 16 * (t % NT16);
+  for (int ct = wave - w0; ct < NT16; ct += nw) {
+    const int c0 = 16 * ct;
+    Frag<T> bo[2];
+    Frag2<T> bog[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bo[kb] = frag_row(OT + (c0 + n) * LDT + 32 * kb, g);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = to_f32(bo[kb].v[j]) * gam[32 * kb + kidx(g, j)];
+      bog[kb] = frag2_of<T>(x);
+    }
+    // transposed stores: this lane's four rows are contiguous
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        mma_a2b(frag2_rowx<T>(Pt + (r0 + n) * LDC + 32 * kb, g),
-                frag_row(OT + (c0 + n) * LDT + 32 * kb, g), acc);
-      out = ws.X1 + (cid * D + c0 + n) * C + r0;
-    } else {
-      const int r0 = 16 * ((t - N1) / NT16), c0 = 16 * ((t - N1) % NT16);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const Frag<T> o = frag_row(OT + (c0 + n) * LDT + 32 * kb, g);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = to_f32(o.v[j]) * gam[32 * kb + kidx(g, j)];
-        mma_ab2(frag_row(QT + (r0 + n) * LDT + 32 * kb, g), frag2_of<T>(x), acc);
-      }
-      out = ws.X2 + (cid * D + c0 + n) * D + r0;
+        mma_a2b(frag2_rowx<T>(Pt + (16 * it + n) * LDC + 32 * kb, g), bo[kb], acc);
+      *reinterpret_cast<f32x4*>(ws.X1 + (cid * D + c0 + n) * C + 16 * it + 4 * g) = acc;
     }
-    // transposed: this lane's four rows are contiguous
-    *reinterpret_cast<f32x4*>(out + 4 * g) = acc;
+#pragma unroll
+    for (int it = 0; it < NT16; ++it) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma_ab2(frag_row(QT + (16 * it + n) * LDT + 32 * kb, g), bog[kb], acc);
+      *reinterpret_cast<f32x4*>(ws.X2 + (cid * D + c0 + n) * D + 16 * it + 4 * g) = acc;
+    }
   }
 }
 
