@@ -1406,8 +1406,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     if constexpr (kFull) return frag_row(lds + r * LDK + c0, g);
     else return chunk_row<T, D>(glob, r, nrows, c0, g);
   };
-#pragma unroll 1
-  for (int tj = 0; tj <= ti; ++tj) {
+  // the B operand rows of U (erase) or V; the diagonal tile takes the
+  // wave's own rows, already in registers
+  using BOp = std::conditional_t<kErase, Frag2<T>, Frag<T>>;
+  auto brow = [&](int rb, int kb) -> BOp {
+    if constexpr (kErase) return Um.row(u0 + (size_t)rb * D + 32 * kb, g);
+    else return chunk_row<T, D>(vc, rb, nrows, 32 * kb, g);
+  };
+  auto tile = [&](int tj, const BOp(&bo)[NKB]) {
     const int rb = 16 * tj + n;
     f32x4 qk = zero4(), dp = zero4(), kk = zero4(), dru = zero4();
 #pragma unroll
@@ -1416,11 +1422,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
       mma(kqrow(Ql, qc, ra, 32 * kb), bk, qk);
       if constexpr (kErase) {
         mma(kqrow(Kl, kc, ra, 32 * kb), bk, kk);
-        const Frag2<T> bu = Um.row(u0 + (size_t)rb * D + 32 * kb, g);
-        mma_ab2(aDO[kb], bu, dp);
-        mma_a2b2(aDR[kb], bu, dru);
+        mma_ab2(aDO[kb], bo[kb], dp);
+        mma_a2b2(aDR[kb], bo[kb], dru);
       } else {
-        mma(aDO[kb], chunk_row<T, D>(vc, rb, nrows, 32 * kb, g), dp);
+        mma(aDO[kb], bo[kb], dp);
       }
     }
     float csp = 0.f;
@@ -1445,7 +1450,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     csp += __shfl_xor(csp, 16);
     csp += __shfl_xor(csp, 32);
     if (g == 0) rsP[2][ti][16 * tj + n] = csp;
+  };
+#pragma unroll 1
+  for (int tj = 0; tj < ti; ++tj) {
+    BOp bu[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) bu[kb] = brow(16 * tj + n, kb);
+    tile(tj, bu);
   }
+  if constexpr (kErase) tile(ti, aU);
+  else tile(ti, aV);
   __syncthreads();
 
   // C x D products: wave w owns the rows 16 w .. 16 w + 15; the column
