@@ -608,16 +608,19 @@ int la_chunk_bwd_fused(const void* q, const void* k, const void* v, const float*
                                       " bytes, this call needs " + std::to_string(w.bytes));
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(LA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  // the raw inputs against the outputs and the whole workspace (the backward
-  // proper checks what it reads from the workspace itself)
+  // every input against the outputs and the whole workspace: the prologue
+  // writes its arrays before the backward proper reads v, grad_out, S0 and
+  // grad_S_final, so an input inside the prologue's region would be
+  // overwritten first (the backward proper checks its own part again)
   const bool gated = la::mode_decay(mode), erase = la::mode_erase(mode);
   const size_t esz = dtype == LA_DTYPE_F32 ? 4 : 2;
-  const Range rq(q, n_x * esz), rk(k, n_x * esz), ra(gated ? a_raw : nullptr, n_g * 4);
-  const Range rb(erase ? b_raw : nullptr, n_g * 4), rws(workspace, w.bytes);
+  const Range rq(q, n_x * esz), rk(k, n_x * esz), rv(v, n_x * esz), rdo(grad_out, n_x * esz);
+  const Range ra(gated ? a_raw : nullptr, n_g * 4), rb(erase ? b_raw : nullptr, n_g * 4);
+  const Range rs0(S0, n_s * 4), rdsf(grad_S_final, n_s * 4), rws(workspace, w.bytes);
   const Range oq(grad_q, n_x * 4), ok(grad_k, n_x * 4), ov(grad_v, n_x * 4);
   const Range oa(gated ? grad_a : nullptr, n_g * 4), ob(erase ? grad_b : nullptr, n_g * 4);
   const Range os0(grad_S0, n_s * 4);
-  for (const Range* in : {&rq, &rk, &ra, &rb})
+  for (const Range* in : {&rq, &rk, &rv, &rdo, &ra, &rb, &rs0, &rdsf})
     for (const Range* out : {&oq, &ok, &ov, &oa, &ob, &os0, &rws})
       if (in->overlaps(*out))
         return fail(LA_ERR_ALIAS, "a gradient output or the workspace overlaps an input");

@@ -22,7 +22,8 @@ S_t = a (S - b k k^T S) + b k v^T (a = 1 for ``delta``; ``linear`` and
 * dk_t  = b dS_t v - a b (dS_t S^T k + S dS_t^T k)      (erase modes)
           dS_t v                                         (otherwise)
 * dbeta_t      = k^T dS_t v - a k^T dS_t S^T k
-* dlog_alpha_t = a <dS_t, S - b k k^T S>   (<A, B> = sum of the products)
+* dlog_alpha_t = a <dS_t, S - b k k^T S>   (<A, B> = sum of the products;
+  evaluated as a (<dS_t, S> - b k^T dS_t S^T k))
 * dS_{t-1} = a (dS_t - b k (k^T dS_t))     (the update's matrix is
   symmetric), and dS0 = dS_0 at the end.
 
@@ -39,13 +40,20 @@ import numpy as np
 from .recurrence import ERASE_MODES, GATED_MODES, _check_mode, recurrent_step
 
 
-def recurrent_bwd(q, k, v, log_alpha, beta, S0, mode, dO, dS_final=None):
+def recurrent_bwd(q, k, v, log_alpha, beta, S0, mode, dO, dS_final=None, checkpoint=None):
     """Gradients of sum(dO * O) + sum(dS_final * S_final).
 
     Shapes as in ``recurrent_fwd``; ``dO [B, H, L, dv]``, ``dS_final
     [B, H, dk, dv]`` or None.  Returns a dict with ``dq, dk, dv [B, H, L, d]``,
     ``dlog_alpha, dbeta [B, H, L]`` (None where the mode does not read the
     gate) and ``dS0 [B, H, dk, dv]``.
+
+    ``checkpoint``: None keeps every state S_0 .. S_L of the forward (small
+    cases); an integer n keeps only S_0, S_n, S_2n, ... and recomputes the
+    states inside each run of n tokens from its first one just before the
+    reverse walk crosses it, so memory is O(L / n + n) states instead of
+    O(L).  The recomputation repeats the forward's own steps in the same
+    order, so the gradients are bit-identical for every n.
     """
     _check_mode(mode)
     q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
@@ -54,38 +62,57 @@ def recurrent_bwd(q, k, v, log_alpha, beta, S0, mode, dO, dS_final=None):
     erase, gated = mode in ERASE_MODES, mode in GATED_MODES
     la = np.asarray(log_alpha, dtype=np.float64) if gated else np.zeros((B, H, L))
     be = np.asarray(beta, dtype=np.float64) if erase else np.ones((B, H, L))
-    # the states S_0 .. S_L of the forward (small cases only)
-    states = np.empty((L + 1, B, H, dk, dv))
-    states[0] = 0.0 if S0 is None else np.asarray(S0, dtype=np.float64)
-    for t in range(L):
-        states[t + 1], _ = recurrent_step(states[t], q[:, :, t], k[:, :, t], v[:, :, t],
-                                          la[:, :, t], be[:, :, t], mode)
+    span = L if checkpoint is None else int(checkpoint)
+    if span < 1:
+        raise ValueError("checkpoint must be a positive number of tokens")
+
+    def run(S, t0, t1):
+        """The forward's states S_t0 .. S_t1, starting from S = S_t0."""
+        out = np.empty((t1 - t0 + 1, B, H, dk, dv))
+        out[0] = S
+        for t in range(t0, t1):
+            out[t - t0 + 1], _ = recurrent_step(out[t - t0], q[:, :, t], k[:, :, t], v[:, :, t],
+                                                la[:, :, t], be[:, :, t], mode)
+        return out
+
+    # forward: the state at the start of every run of `span` tokens
+    starts = list(range(0, L, span))
+    ckpt = {0: np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)}
+    for i, t0 in enumerate(starts[:-1]):
+        ckpt[starts[i + 1]] = run(ckpt[t0], t0, starts[i + 1])[-1]
     dS = np.zeros((B, H, dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
     g = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v))}
     dla, dbe = np.zeros((B, H, L)), np.zeros((B, H, L))
+    states, t0 = None, L
     for t in range(L - 1, -1, -1):
-        S, St = states[t], states[t + 1]
+        if t < t0:
+            # entering the run that holds token t: recompute its states
+            t0 = (t // span) * span
+            states = run(ckpt[t0], t0, min(t0 + span, L))
+        S, St = states[t - t0], states[t - t0 + 1]
         qt, kt, vt, dot = q[:, :, t], k[:, :, t], v[:, :, t], dO[:, :, t]
         a = np.exp(la[:, :, t])[..., None]           # [B, H, 1]
         b = be[:, :, t][..., None]
         dS = dS + qt[..., :, None] * dot[..., None, :]
-        g["dq"][:, :, t] = np.einsum("bhij,bhj->bhi", St, dot)
-        kdS = np.einsum("bhi,bhij->bhj", kt, dS)      # k^T dS        [dv]
-        dSv = np.einsum("bhij,bhj->bhi", dS, vt)      # dS v          [dk]
+        g["dq"][:, :, t] = (St @ dot[..., :, None])[..., 0]
+        kdS = (kt[..., None, :] @ dS)[..., 0, :]      # k^T dS        [dv]
+        dSv = (dS @ vt[..., :, None])[..., 0]         # dS v          [dk]
         g["dv"][:, :, t] = b * kdS
         if erase:
-            Sk = np.einsum("bhij,bhi->bhj", S, kt)    # S^T k         [dv]
-            dSSk = np.einsum("bhij,bhj->bhi", dS, Sk)   # dS S^T k    [dk]
-            SdSk = np.einsum("bhij,bhj->bhi", S, kdS)   # S dS^T k    [dk]
+            Sk = (kt[..., None, :] @ S)[..., 0, :]    # S^T k         [dv]
+            dSSk = (dS @ Sk[..., :, None])[..., 0]    # dS S^T k      [dk]
+            SdSk = (S @ kdS[..., :, None])[..., 0]    # S dS^T k      [dk]
             g["dk"][:, :, t] = b * dSv - a * b * (dSSk + SdSk)
-            dbe[:, :, t] = np.einsum("bhi,bhi->bh", kt, dSv) - a[..., 0] * np.einsum(
-                "bhj,bhj->bh", kdS, Sk)
-            inner = S - b[..., None] * kt[..., :, None] * Sk[..., None, :]
+            kdSv = np.sum(kt * dSv, axis=-1)          # k^T dS v
+            kdSSk = np.sum(kdS * Sk, axis=-1)         # k^T dS S^T k
+            dbe[:, :, t] = kdSv - a[..., 0] * kdSSk
+            # <dS, S - b k k^T S> = <dS, S> - b k^T dS S^T k
+            inner = np.sum(dS * S, axis=(-2, -1)) - b[..., 0] * kdSSk
         else:
             g["dk"][:, :, t] = dSv
-            inner = S
+            inner = np.sum(dS * S, axis=(-2, -1))
         if gated:
-            dla[:, :, t] = a[..., 0] * np.einsum("bhij,bhij->bh", dS, inner)
+            dla[:, :, t] = a[..., 0] * inner
         # dS_{t-1} = a (dS - b k (k^T dS))
         if erase:
             dS = a[..., None] * (dS - b[..., None] * kt[..., :, None] * kdS[..., None, :])

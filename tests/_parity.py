@@ -102,3 +102,17 @@ def oracle_decode(x, mode, heads=None):
                                y["log_alpha"][:, bs, hs][:, None],
                                y["beta"][:, bs, hs][:, None], mode)
     return o[:, 0], S[0]
+
+
+def assert_out_pair(name, out_bf16, out_f32, ref, dtype="bf16", rounded=True):
+    """The same call with a bfloat16 and a float32 output: the float output
+    is held to the plain bound of `dtype` and, when `rounded`, the bf16
+    output must be exactly the float one rounded to nearest even -- the
+    pairing that justifies the bf16 output's looser per-element bound (the
+    bf16 output is also checked under that bound)."""
+    import torch
+    assert_close(f"{name} (f32 out)", f64(out_f32), ref, dtype)
+    assert_close(name, f64(out_bf16), ref, dtype, bf16_out=True)
+    if rounded:
+        assert torch.equal(out_f32.to(torch.bfloat16), out_bf16), (
+            f"{name}: bf16 out != rne(f32 out)")

@@ -580,3 +580,23 @@ def test_chunk_bwd_fused_rejects(flags, scale, eps, code):
                                 P, None)
     assert rc == code
     assert lib.la_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("arg", [2, 5, 6, 7])      # v, S0, grad_out, grad_S_final
+def test_chunk_bwd_fused_rejects_an_input_in_the_prologue_region(arg):
+    """The fused backward's prologue writes normalised q, k and the gates at
+    the start of the workspace before the backward proper reads v, grad_out,
+    S0 and grad_S_final: any of them inside that region must be rejected
+    (it would be overwritten first), not only inside the backward's own
+    part of the workspace."""
+    lib = _lib.get()
+    o = _Opts(3, 0.0625, None, None, 0.0)
+    n = ctypes.c_size_t(0)
+    assert lib.la_chunk_bwd_fused_workspace_bytes(1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o),
+                                                  ctypes.byref(n)) == OK
+    ws = 20 * P
+    args = [fake(i) for i in range(14)]
+    args[arg] = ctypes.c_void_p(ws + 256)               # inside the normalised-q array
+    rc = lib.la_chunk_bwd_fused(*args, 1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o),
+                                ctypes.c_void_p(ws), n.value, None)
+    assert rc == ALIAS, lib.la_last_error().decode()

@@ -1,10 +1,12 @@
 """GPU parity of the backward (la_chunk_bwd) against the float64 oracle.
 
 The reference is ``oracle.recurrent_bwd`` -- the reverse of the token
-recurrence, pinned on the CPU by finite differences -- on small cases, and
-``oracle.chunkwise_bwd`` (pinned on the CPU to the token backward) on the
-longer ones.  Both consume float64 copies of exactly the tensors handed to
-the GPU.  Tolerances per gradient as for the forward: float32 inputs
+recurrence, the plain derivative of the definition, pinned on the CPU by
+finite differences -- in every test.  Long sequences run it with
+checkpointed states (every 64th state kept, each run of 64 tokens recomputed
+before the reverse walk crosses it; bit-identical to keeping every state),
+so no reference shares the chunk algebra the kernels use.  It consumes
+float64 copies of exactly the tensors handed to the GPU.  Tolerances per gradient as for the forward: float32 inputs
 max|err| <= 1e-4 max|ref|; bf16 inputs max|err| <= 2e-2 RMS(ref) (the
 gradients are float32, so no output rounding is added).
 """
@@ -35,15 +37,13 @@ def run_bwd(w, x, gr, mode, with_s0=True, with_dsf=True):
     return res
 
 
-def reference(x, gr, mode, with_s0=True, with_dsf=True, chunked=False):
+def reference(x, gr, mode, with_s0=True, with_dsf=True, checkpoint=None):
     y = workloads.to_f64(x)
     gy = workloads.to_f64(gr)
     args = (y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
             y["S0"] if with_s0 else None, mode)
     dsf = gy["dS_final"] if with_dsf else None
-    if chunked:
-        return oracle.chunkwise_bwd(*args, 64, gy["dout"], dsf)
-    return oracle.recurrent_bwd(*args, gy["dout"], dsf)
+    return oracle.recurrent_bwd(*args, gy["dout"], dsf, checkpoint=checkpoint)
 
 
 def compare(res, ref, mode, dtype):
@@ -75,6 +75,22 @@ def test_chunk_bwd_small(mode, dtype, d, L):
     compare(res, ref, mode, dtype)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", ERASE)
+def test_chunk_bwd_nonunit_keys(mode, dtype, d):
+    """The delta modes with keys rescaled per token by a factor in
+    [0.5, 1.5] (the erase terms scale with |k|^2): every gradient against
+    the token backward."""
+    from test_parity_gpu import _nonunit_keys
+    w = recipe(mode, dtype, B=2, H=1, L=131, d=d, s0_std=0.05, seed=119)
+    log(f"case chunk_bwd_nonunit {w.name} seed={w.seed}")
+    x = _nonunit_keys(w, workloads.make_inputs(w), 120)
+    gr = workloads.make_upstream_grads(w, ds_std=0.1)
+    res = run_bwd(w, x, gr, mode)
+    ref = reference(x, gr, mode)
+    compare(res, ref, mode, dtype)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_chunk_bwd_zero_state_and_no_state_gradient(mode):
     """S0 = NULL and dS_final = NULL read as zeros."""
@@ -89,14 +105,15 @@ def test_chunk_bwd_zero_state_and_no_state_gradient(mode):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_chunk_bwd_long(mode):
-    """A long bf16 sequence at d = 128 (64 chunks) against the chunkwise
-    float64 backward; the walks carry the state gradient over every chunk."""
+    """A long bf16 sequence at d = 128 (64 chunks, a ragged last one)
+    against the token backward; the walks carry the state gradient over
+    every chunk."""
     w = recipe(mode, "bf16", B=1, H=2, L=4096 - 17, d=128, s0_std=0.02, seed=77)
     log(f"case chunk_bwd_long {w.name} seed={w.seed}")
     x = workloads.make_inputs(w)
     gr = workloads.make_upstream_grads(w, ds_std=0.05)
     res = run_bwd(w, x, gr, mode)
-    ref = reference(x, gr, mode, chunked=True)
+    ref = reference(x, gr, mode, checkpoint=64)
     compare(res, ref, mode, "bf16")
 
 
@@ -136,9 +153,9 @@ def test_chunk_bwd_state_gradient_chains_over_a_split():
 
 def test_chunk_bwd_full_size_sampled():
     """The long-context workload at full size (B=1, H=32, L=65536, d=128,
-    bf16), launched as the bench launches it; the float64 chunkwise backward
-    recomputes two sampled heads over the whole sequence (heads do not
-    interact)."""
+    bf16), launched as the bench launches it; the float64 token backward
+    (checkpointed) recomputes two sampled heads over the whole sequence
+    (heads do not interact)."""
     w = workloads.WORKLOADS[4]
     log(f"case chunk_bwd_full {w.name} seed={w.seed}")
     x = workloads.make_inputs(w)
@@ -146,7 +163,7 @@ def test_chunk_bwd_full_size_sampled():
     res = run_bwd(w, x, gr, w.mode)
     hs = [0, w.H - 1]
     sub = lambda d: {k: t[:, hs].contiguous() for k, t in d.items()}   # noqa: E731
-    ref = reference(sub(x), sub(gr), w.mode, chunked=True)
+    ref = reference(sub(x), sub(gr), w.mode, checkpoint=64)
     got = {k: (t[:, hs] if t is not None else None) for k, t in res.items()}
     compare(got, ref, w.mode, "bf16")
 

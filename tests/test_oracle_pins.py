@@ -719,3 +719,47 @@ def test_prologue_backward_matches_finite_differences(mode, flags):
             xm[idx] -= h
             num[idx] = (loss(**{**args, name: xp}) - loss(**{**args, name: xm})) / (2 * h)
         assert _rel(grad, num) < 1e-7, (name, _rel(grad, num))
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+def test_checkpointed_token_backward_is_bit_identical(mode):
+    """Keeping only every n-th state and recomputing each run of n tokens
+    repeats the forward's own steps, so the gradients equal those of the
+    backward that keeps every state, bit for bit, whatever n (1, a divisor
+    of L, a ragged last run, n > L)."""
+    from oracle.backward import recurrent_bwd
+    q, k, v, la, be, S0 = _rand(81, B=2, H=1, L=23, dk=4, dv=3, unit_keys=False)
+    rng = np.random.default_rng(82)
+    dO = rng.standard_normal((2, 1, 23, 3))
+    dSf = rng.standard_normal((2, 1, 4, 3))
+    ref = recurrent_bwd(q, k, v, la, be, S0, mode, dO, dSf)
+    for n in (1, 5, 23, 64):
+        got = recurrent_bwd(q, k, v, la, be, S0, mode, dO, dSf, checkpoint=n)
+        for name, r in ref.items():
+            if r is None:
+                assert got[name] is None
+            else:
+                assert np.array_equal(got[name], r), (n, name)
+
+
+@pytest.mark.parametrize("mode", oracle.MODES)
+@pytest.mark.parametrize("d", [32, 128])
+def test_chunkwise_backward_equals_token_backward_at_kernel_chunk(mode, d):
+    """The chunkwise backward at the kernels' chunk size C = 64, with a
+    state wider than a chunk (d = 128 > C) and narrower (d = 32 < C), over
+    three full chunks and a ragged fourth (L = 200), keys not normalised
+    (the erase terms then scale with |k|^2), against the token backward."""
+    from oracle.backward import recurrent_bwd
+    q, k, v, la, be, S0 = _rand(91 + d, B=1, H=1, L=200, dk=d, dv=d, unit_keys=False)
+    k *= 1.0 / np.sqrt(d)                     # |k| around 1, not equal to 1
+    q *= 1.0 / np.sqrt(d)
+    rng = np.random.default_rng(92 + d)
+    dO = rng.standard_normal((1, 1, 200, d))
+    dSf = 0.1 * rng.standard_normal((1, 1, d, d))
+    ref = recurrent_bwd(q, k, v, la, be, S0, mode, dO, dSf)
+    got = oracle.chunkwise_bwd(q, k, v, la, be, S0, mode, 64, dO, dSf)
+    for name in ("dq", "dk", "dv", "dS0", "dlog_alpha", "dbeta"):
+        if ref[name] is None:
+            assert got[name] is None
+            continue
+        assert _rel(got[name], ref[name]) < 1e-10, (name, _rel(got[name], ref[name]))

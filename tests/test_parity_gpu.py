@@ -14,7 +14,8 @@ import torch
 import chunkwise_gated_delta_la_amd as la
 import oracle
 import workloads
-from _parity import assert_close, f64, log, oracle_decode, oracle_fwd, to_cuda
+from _parity import (assert_close, assert_out_pair, f64, log, oracle_decode, oracle_fwd,
+                     to_cuda)
 from workloads import WORKLOADS, Workload
 
 pytestmark = pytest.mark.gpu
@@ -100,11 +101,19 @@ def test_decode_full_size_sampled():
     rng = np.random.default_rng(5)
     heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(b), int(h)) for b, h in
                                             zip(rng.integers(0, w.B, 10), rng.integers(0, w.H, 10))]
+    # the same 128 steps with a float32 output
+    S32 = d["S0"].clone()
+    outs32 = torch.empty((w.steps, w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+    for n in range(w.steps):
+        la.decode_step(d["q"][n], d["k"][n], d["v"][n], d["log_alpha"][n], d["beta"][n], S32,
+                       mode=w.mode, out=outs32[n])
+    torch.cuda.synchronize()
     o_ref, S_ref = oracle_decode(x, w.mode, heads)
     bs = [b for b, _ in heads]
     hs = [h for _, h in heads]
-    assert_close("o[sampled]", f64(outs[:, bs, hs]), o_ref, w.dtype, bf16_out=True)
+    assert_out_pair("o[sampled]", outs[:, bs, hs], outs32[:, bs, hs], o_ref, w.dtype)
     assert_close("S[sampled]", f64(S[bs, hs]), S_ref, w.dtype)
+    assert torch.equal(S32, S), "the output dtype must not change the state"
 
 
 # ------------------------------------------------------------------ chunk forward
@@ -222,7 +231,15 @@ def test_chunk_varlen_packed(mode, dtype, d):
     la.chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
                         S0.cuda(), cu.cuda(), mode=mode, out=out, S_final=S)
     torch.cuda.synchronize()
-    assert_close("o", f64(out), o_ref, dtype, bf16_out=dtype == "bf16")
+    if dtype == "bf16":
+        out32 = torch.full((H, T, d), float("nan"), dtype=torch.float32, device="cuda")
+        _, S32 = la.chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["log_alpha"],
+                                     dev["beta"], S0.cuda(), cu.cuda(), mode=mode, out=out32)
+        torch.cuda.synchronize()
+        assert_out_pair("o", out, out32, o_ref, dtype)
+        assert torch.equal(S32, S), "the output dtype must not change the state"
+    else:
+        assert_close("o", f64(out), o_ref, dtype)
     assert_close("S_final", f64(S), S_ref, dtype)
     # empty sequences pass their state through unchanged
     for s, n in enumerate(lens):
@@ -238,6 +255,50 @@ def test_chunk_varlen_packed(mode, dtype, d):
         torch.cuda.synchronize()
         assert torch.equal(o1[0], out[:, a:b]) and torch.equal(S1[0], S[s]), (
             f"sequence {s}: packed and fixed-length calls differ")
+
+
+def _nonunit_keys(w, x, seed):
+    """Keys rescaled per token by a factor drawn uniform in [0.5, 1.5]: the
+    recurrence is defined for any |k|, and larger keys grow the entries of
+    A = strict_lower(diag(beta) K K^T * Gamma) that the T solve inverts
+    (beta |k|^2 up to 2.25: the erase can overshoot)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lead = x["k"].shape[:-1]
+    scale = 0.5 + torch.rand(lead + (1,), generator=gen)
+    return dict(x, k=(x["k"].float() * scale).to(x["k"].dtype))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("f32", 128)])
+@pytest.mark.parametrize("mode", ("delta", "gated_delta"))
+def test_chunk_nonunit_keys(mode, dtype, d):
+    """The delta modes with |k| in [0.5, 1.5] over 5 full chunks and a
+    partial one, with S0: every element of the forward against the oracle
+    (bf16: float and bf16 outputs); the sequence-parallel forward (P = 3);
+    and 12 decode steps."""
+    w = recipe(mode, dtype, B=2, H=2, L=64 * 5 + 13, d=d, s0_std=0.3, seed=113)
+    log(f"chunk non-unit keys {w}")
+    x = _nonunit_keys(w, workloads.make_inputs(w), 114)
+    o_ref, S_ref = oracle_fwd(x, mode)
+    check_fwd(w, x, o_ref, S_ref)
+    dev = to_cuda(x)
+    if dtype == "bf16":
+        out, S = _seg_call(dev, mode, 3, dev["S0"])
+        out32, _ = _seg_call(dev, mode, 3, dev["S0"], out_dtype=torch.float32)
+        assert_out_pair("o P=3", out, out32, o_ref)
+        assert_close("S_final P=3", f64(S), S_ref, "bf16")
+    steps = 12
+    col = lambda t, n: t[:, :, n].contiguous()       # noqa: E731
+    Sd = dev["S0"].clone()
+    outs = [la.decode_step(col(dev["q"], n), col(dev["k"], n), col(dev["v"], n),
+                           col(dev["log_alpha"], n), col(dev["beta"], n), Sd, mode=mode,
+                           out_dtype=torch.float32) for n in range(steps)]
+    torch.cuda.synchronize()
+    y = workloads.to_f64(x)
+    mv = lambda t: np.moveaxis(t, 2, 0)[:steps]      # noqa: E731
+    o_d, S_d = oracle.decode_steps(y["S0"], mv(y["q"]), mv(y["k"]), mv(y["v"]),
+                                   mv(y["log_alpha"]), mv(y["beta"]), mode)
+    assert_close("decode o", np.stack([f64(o) for o in outs]), o_d, dtype)
+    assert_close("decode S", f64(Sd), S_d, dtype)
 
 
 # ------------------------------------------------------------------ sequence-parallel
@@ -264,11 +325,10 @@ def test_chunk_segmented(mode, d):
     for P in (2, 3, 7, 10):
         log(f"chunk segmented P={P} {w}")
         out, S = _seg_call(dev, mode, P, dev["S0"])
-        assert_close(f"o P={P}", f64(out), o_ref, "bf16", bf16_out=True)
+        out32, S32 = _seg_call(dev, mode, P, dev["S0"], out_dtype=torch.float32)
+        assert_out_pair(f"o P={P}", out, out32, o_ref)
         assert_close(f"S_final P={P}", f64(S), S_ref, "bf16")
-    out32, S32 = _seg_call(dev, mode, 3, dev["S0"], out_dtype=torch.float32)
-    out, S = _seg_call(dev, mode, 3, dev["S0"])
-    assert torch.equal(out32.to(torch.bfloat16), out) and torch.equal(S32, S)
+        assert torch.equal(S32, S), "the output dtype must not change the state"
     S_io = dev["S0"].clone()
     _seg_call(dev, mode, 7, S_io, S_final=S_io)
     assert_close("S in place P=7", f64(S_io), S_ref, "bf16")
@@ -284,7 +344,8 @@ def test_chunk_segmented_zero_state_and_single(mode):
     o_ref, S_ref = oracle_fwd(x, mode)
     dev = to_cuda(x)
     out, S = _seg_call(dev, mode, 4)
-    assert_close("o P=4", f64(out), o_ref, "bf16", bf16_out=True)
+    out32, _ = _seg_call(dev, mode, 4, out_dtype=torch.float32)
+    assert_out_pair("o P=4", out, out32, o_ref)
     assert_close("S_final P=4", f64(S), S_ref, "bf16")
     a_o, a_S = _seg_call(dev, mode, 1)
     b_o, b_S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], None,
@@ -383,10 +444,10 @@ def test_chunk_fused_prologue(mode, d, flags):
     o_ref, S_ref = _fused_oracle(r, mode, f)
     dev = to_cuda(r)
     out, S = _fused_call(dev, mode, f)
-    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
-    assert_close("S_final", f64(S), S_ref, "bf16")
     out32, S32 = _fused_call(dev, mode, f, out_dtype=torch.float32)
-    assert torch.equal(out32.to(torch.bfloat16), out) and torch.equal(S32, S)
+    assert_out_pair("o", out, out32, o_ref)
+    assert_close("S_final", f64(S), S_ref, "bf16")
+    assert torch.equal(S32, S)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -400,8 +461,10 @@ def test_chunk_fused_prologue_segmented(mode):
     assert P > 1
     r = _raw(w, 3)
     o_ref, S_ref = _fused_oracle(r, mode, 3)
-    out, S = _fused_call(to_cuda(r), mode, 3)
-    assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
+    dev = to_cuda(r)
+    out, S = _fused_call(dev, mode, 3)
+    out32, _ = _fused_call(dev, mode, 3, out_dtype=torch.float32)
+    assert_out_pair("o", out, out32, o_ref)
     assert_close("S_final", f64(S), S_ref, "bf16")
 
 
@@ -425,9 +488,11 @@ def test_chunk_fused_shard_sampled():
     r = _raw(w, 3)
     heads = [(0, 0), (0, w.H - 1)]
     o_ref, S_ref = _fused_oracle(r, w.mode, 3, heads)
-    out, S = _fused_call(to_cuda(r), w.mode, 3)
+    dev = to_cuda(r)
+    out, S = _fused_call(dev, w.mode, 3)
     sel = lambda t: t[[0, 0], [0, w.H - 1]]   # noqa: E731
-    assert_close("o", f64(sel(out)), o_ref, "bf16", bf16_out=True)
+    out32 = _fused_call(dev, w.mode, 3, out_dtype=torch.float32)[0]
+    assert_out_pair("o", sel(out), sel(out32), o_ref)
     assert_close("S_final", f64(sel(S)), S_ref, "bf16")
 
 
@@ -458,6 +523,14 @@ def test_fused_extreme_inputs(mode):
     assert torch.isfinite(out.float()).all() and torch.isfinite(S).all()
     assert_close("o", f64(out), o_ref, "bf16", bf16_out=True)
     assert_close("S_final", f64(S), S_ref, "bf16")
+    # float output at the plain bound (the output norm of a bf16 output reads
+    # its rounded values, so the two outputs differ by more than one rounding)
+    out32, _ = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["a_raw"], dev["b_raw"], dev["S0"],
+                            mode=mode, qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE,
+                            dskip=D.cuda(), out_norm=True, norm_weight=nw.cuda(),
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("o (f32 out)", f64(out32), o_ref, "bf16")
     # the same tokens one by one through the fused decode step
     y = {key: t.to(torch.float64).numpy() for key, t in r.items()}
     q, k, lg, be = oracle.prepare(y["q"], y["k"], y["a_raw"], y["b_raw"], mode, 3, GATE_SCALE)
@@ -477,6 +550,15 @@ def test_fused_extreme_inputs(mode):
     assert np.all(np.isfinite(od)) and torch.isfinite(Sg).all()
     assert_close("decode o", od, o_d, "bf16", bf16_out=True)
     assert_close("decode S", f64(Sg), S_d, "bf16")
+    Sg32 = dev["S0"].clone()
+    outs32 = [la.decode_step(col(dev["q"], n), col(dev["k"], n), col(dev["v"], n),
+                             col(dev["a_raw"], n), col(dev["b_raw"], n), Sg32, mode=mode,
+                             qk_l2norm=True, gate_act=True, gate_scale=GATE_SCALE,
+                             dskip=D.cuda(), out_norm=True, norm_weight=nw.cuda(),
+                             out_dtype=torch.float32) for n in range(steps)]
+    torch.cuda.synchronize()
+    assert_out_pair("decode o", torch.stack(outs), torch.stack(outs32), o_d)
+    assert torch.equal(Sg32, Sg)
 
 
 @pytest.mark.parametrize("flags", ["gates", "norm", "both"])
@@ -703,9 +785,17 @@ def test_state_carry_and_in_place(mode):
     o2, _ = la.chunk_fwd(part(d["q"], L1, w.L), part(d["k"], L1, w.L), part(d["v"], L1, w.L),
                          part(d["log_alpha"], L1, w.L), part(d["beta"], L1, w.L), S,
                          mode=mode, S_final=S)
+    S32 = d["S0"].clone()
+    o1f, _ = la.chunk_fwd(part(d["q"], 0, L1), part(d["k"], 0, L1), part(d["v"], 0, L1),
+                          part(d["log_alpha"], 0, L1), part(d["beta"], 0, L1), S32, mode=mode,
+                          S_final=S32, out_dtype=torch.float32)
+    o2f, _ = la.chunk_fwd(part(d["q"], L1, w.L), part(d["k"], L1, w.L), part(d["v"], L1, w.L),
+                          part(d["log_alpha"], L1, w.L), part(d["beta"], L1, w.L), S32,
+                          mode=mode, S_final=S32, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_close("o", np.concatenate([f64(o1), f64(o2)], axis=2), o_ref, "bf16", bf16_out=True)
+    assert_out_pair("o", torch.cat([o1, o2], dim=2), torch.cat([o1f, o2f], dim=2), o_ref)
     assert_close("S_final", f64(S), S_ref, "bf16")
+    assert torch.equal(S32, S)
 
 
 @pytest.mark.parametrize("mode", MODES)
