@@ -13,7 +13,7 @@ memory) and passes torch's current HIP stream.
     out, S = noncausal_fwd(q, k, v, S0)                                   # O = Q (S0 + K^T V)
 """
 from ._lib import LAError, LIB_PATH  # noqa: F401
-from .api import (MODES, chunk_fwd, chunk_fwd_varlen, chunk_segments,  # noqa: F401
+from .api import (MODES, chunk_fwd, chunk_fwd_noalloc, chunk_fwd_varlen, chunk_segments,  # noqa: F401
                   chunk_varlen_workspace_bytes, chunk_workspace_bytes, decode_step,
                   kernel_timer, noncausal_fwd, version, chunk_bwd,
                   chunk_bwd_workspace_bytes, chunk_bwd_varlen,

@@ -38,6 +38,9 @@ def _declare(lib):
     lib.la_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
                                  i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_chunk_fwd.restype = i
+    lib.la_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp,
+                                         i, i, i, i, i, i, i, i, vp]
+    lib.la_chunk_fwd_noalloc.restype = i
     lib.la_chunk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_workspace_bytes.restype = i
     lib.la_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp,

@@ -187,6 +187,44 @@ def chunk_fwd(q, k, v, log_alpha=None, beta=None, S0=None, *, mode="gated_delta"
     return out, S_final
 
 
+NOALLOC_SCRATCH_BYTES = 128 << 20      # LA_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0, out, S_final=None, *,
+                      mode="gated_delta", C=64):
+    """``la_chunk_fwd_noalloc``: the chunkwise forward with the library's
+    static per-GPU scratch in place of a workspace, for callers that must not
+    allocate.  The caller passes every tensor, ``out`` and ``S_final`` (or
+    None) included; nothing is allocated here or in the library.  Calls that
+    overlap in time on one GPU race on the shared scratch.  Shapes and dtypes
+    as ``chunk_fwd``; the output dtype is ``out``'s."""
+    m = _mode(mode)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"q must be float32 or bfloat16, got {dt}")
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    _need(k, "k", (B, H, L, dk), dt, dev)
+    _need(v, "v", (B, H, L, dv), dt, dev)
+    _need(log_alpha if m in _DECAY else None, "log_alpha", (B, H, L), torch.float32, dev)
+    _need(beta if m in _ERASE else None, "beta", (B, H, L), torch.float32, dev)
+    _need(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    code = _dtype_code(dt, out.dtype)
+    _need(out, "out", (B, H, L, dv), out.dtype, dev)
+    _need(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    lib = _lib.get()
+    with torch.cuda.device(dev):
+        la, be = _ptr(log_alpha if m in _DECAY else None), _ptr(beta if m in _ERASE else None)
+        rc = lib.la_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), la, be, _ptr(S0), _ptr(out),
+                                      _ptr(S_final), B, H, L, dk, dv, C, m, code, _stream(dev))
+    _lib.check(rc)
+    return out, S_final
+
+
 def noncausal_fwd(q, k, v, S0=None, *, out=None, S_final=None, return_state=True,
                   out_dtype=None, workspace=None):
     """Bidirectional linear attention (``la_noncausal_fwd``): S = S0 + K^T V

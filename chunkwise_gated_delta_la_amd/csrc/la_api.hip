@@ -17,6 +17,12 @@
 #include "la_kernels.hpp"
 #include "la_bwd.hpp"
 
+// Scratch of la_chunk_fwd_noalloc: one array per GPU, in the library's code
+// object.  Host code never uses this name as an address (on the host it is
+// only a handle for the symbol lookup): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -225,9 +231,10 @@ int check_varlen_shape(int N, int H, int T, int dk, int dv, int C, int mode, int
 // entry points.  n_* are element counts of the tensors; cu (packed batches)
 // is an input of cu_bytes bytes.
 int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_t n_s,
-              int dtype, size_t workspace_bytes, size_t cu_bytes, void* stream) {
+              int dtype, size_t workspace_bytes, size_t cu_bytes, void* stream,
+              bool check_only = false) {
   const size_t need = la::chunk_workspace_bytes(a);
-  if (need > 0) {
+  if (need > 0 && !check_only) {
     if (!a.workspace)
       return fail(LA_ERR_WORKSPACE, "this call needs a workspace of " + std::to_string(need) +
                                         " bytes (la_chunk_workspace_bytes)");
@@ -255,6 +262,7 @@ int run_chunk(const la::ChunkArgs& a, size_t n_qk, size_t n_v, size_t n_g, size_
     return fail(LA_ERR_ALIAS, "S_final partially overlaps S0 (only S_final == S0 is allowed)");
   for (const Range* in : {&rq, &rk, &rv, &rla, &rb, &rs0, &ro, &rsf, &rcu, &rds, &rnw})
     if (rws.overlaps(*in)) return fail(LA_ERR_ALIAS, "workspace overlaps an input or output");
+  if (check_only) return LA_OK;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = prof_mark(st);
@@ -460,6 +468,30 @@ int check_bwd_fused(const la_fused_opts_t* opts, int mode, Fused* f) {
   if (f->flags & (LA_EPI_DSKIP | LA_EPI_OUT_NORM))
     return fail(LA_ERR_UNSUPPORTED, "la_chunk_bwd_fused takes LA_PRO_GATES and "
                                     "LA_PRO_QK_L2NORM only (no backward of the epilogue)");
+  return LA_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LA_ERR_HIP, "device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip("hipGetSymbolAddress(scratch)", e);
+    if (!p) return fail(LA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return LA_OK;
 }
 
@@ -752,6 +784,36 @@ int la_chunk_fwd(const void* q, const void* k, const void* v, const float* log_a
                                dtype, workspace);
   a.P = la::plan_segments(a);
   return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, workspace_bytes, 0, stream);
+}
+
+int la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, void* out, float* S_final, int B,
+                         int H, int L, int dk, int dv, int C, int mode, int dtype,
+                         void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !out) return fail(LA_ERR_NULL, "q, k, v and out are required");
+  if (int e = check_mode_dtype(mode, dtype)) return e;
+  if (int e = check_gates(mode, log_alpha, beta)) return e;
+  if (int e = check_chunk_shape(B, H, L, dk, dv, C, mode, dtype)) return e;
+  size_t n_qk, n_v, n_g, n_s;
+  if (!count({B, H, L, dk}, &n_qk) || !count({B, H, L, dv}, &n_v) ||
+      !count({B, H, L}, &n_g) || !count({B, H, dk, dv}, &n_s))
+    return fail(LA_ERR_SHAPE, "tensor sizes overflow size_t");
+  la::ChunkArgs a = chunk_args(q, k, v, log_alpha, beta, S0, out, S_final, B, H, L, dk, C, mode,
+                               dtype, nullptr);
+  a.P = la::plan_segments(a);
+  const size_t need = la::chunk_workspace_bytes(a);
+  if (need > LA_NOALLOC_SCRATCH_BYTES)
+    return fail(LA_ERR_WORKSPACE, "this call needs " + std::to_string(need) +
+                                      " bytes of scratch; la_chunk_fwd_noalloc holds " +
+                                      std::to_string(LA_NOALLOC_SCRATCH_BYTES) +
+                                      " (use la_chunk_fwd with a workspace)");
+  // tensor checks first: no HIP call before every argument error is reported
+  if (int e = run_chunk(a, n_qk, n_v, n_g, n_s, dtype, 0, 0, stream, true)) return e;
+  if (need > 0) {
+    if (int e = scratch_address(&a.workspace)) return e;
+  }
+  return run_chunk(a, n_qk, n_v, n_g, n_s, dtype, need, 0, stream);
 }
 
 int la_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* a_raw,

@@ -193,6 +193,35 @@ int la_chunk_fwd(const void* q, const void* k, const void* v,
                  size_t workspace_bytes, void* stream);
 
 /*
+ * la_chunk_fwd_noalloc -- la_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results.  The scratch la_chunk_fwd keeps
+ * in its workspace lives instead in a static device array of the library,
+ * LA_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the library's first
+ * use on that GPU until the process ends; its address is looked up once per
+ * device (hipGetSymbolAddress) on the first call there.  Nothing is
+ * allocated: no hipMalloc / hipFree / torch allocation in the call.
+ *
+ * Limit: a call whose la_chunk_workspace_bytes() exceeds
+ * LA_NOALLOC_SCRATCH_BYTES returns LA_ERR_WORKSPACE before anything is
+ * enqueued (e.g. B*H*ceil(L/C) above 21,845 chunk-heads in the bf16 delta
+ * modes); use la_chunk_fwd with a workspace for those.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents: each call writes every scratch byte it reads before
+ * reading it, so nothing needs clearing, but calls that overlap in time on
+ * one GPU (two streams, two host threads) race on it -- serialise them.
+ * Errors as la_chunk_fwd, plus LA_ERR_HIP if the array's address cannot be
+ * obtained.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int la_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, const float* S0,
+                         void* out, float* S_final, int B, int H, int L, int dk,
+                         int dv, int C, int mode, int dtype, void* stream);
+
+/*
  * la_chunk_workspace_bytes -- size of the workspace la_chunk_fwd needs for
  * these sizes, mode and dtype, written to *bytes (0 if it needs none).
  * Validates the same shape, mode and dtype rules as la_chunk_fwd and

@@ -600,3 +600,29 @@ def test_chunk_bwd_fused_rejects_an_input_in_the_prologue_region(arg):
     rc = lib.la_chunk_bwd_fused(*args, 1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o),
                                 ctypes.c_void_p(ws), n.value, None)
     assert rc == ALIAS, lib.la_last_error().decode()
+
+
+def test_chunk_fwd_noalloc_rejects_before_any_launch():
+    """la_chunk_fwd_noalloc validates like la_chunk_fwd and rejects a call
+    whose scratch would exceed the static array (the long-context workload
+    needs 192 MiB of T factors, the array holds 128 MiB) before any HIP
+    call; float inputs need no scratch at all."""
+    lib = _lib.get()
+    f = lib.la_chunk_fwd_noalloc
+    args = [fake(i) for i in range(8)]
+    assert f(*args, 1, 32, 65536, 128, 128, 64, 2, 1, None) == WS
+    assert "scratch" in lib.la_last_error().decode()
+    assert f(None, *args[1:], 1, 1, 64, 64, 64, 64, 2, 1, None) == NULL
+    assert f(*args, 1, 1, 64, 96, 96, 64, 2, 1, None) == UNSUP
+    a = list(args)
+    a[6] = ctypes.c_void_p(P + 128)                     # out overlaps q
+    assert f(*a, 1, 1, 64, 64, 64, 64, 2, 1, None) == ALIAS
+    # the limit is the workspace la_chunk_fwd would need for the same call
+    over = 0
+    for (B, H, L) in ((8, 16, 4096), (1, 1, 64 * 21846), (4, 32, 8192), (1, 32, 65536)):
+        n = ctypes.c_size_t(0)
+        assert lib.la_chunk_workspace_bytes(B, H, L, 128, 128, 64, 2, 1, ctypes.byref(n)) == OK
+        if n.value > 128 << 20:
+            assert f(*args, B, H, L, 128, 128, 64, 2, 1, None) == WS
+            over += 1
+    assert over >= 2
