@@ -31,6 +31,7 @@ METRIC = ("chunkwise gated-delta fwd tokens/s (% MFMA peak); "
           "decode state GB/s (% HBM)")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK = 2.5e15        # MI355X dense bf16 MFMA, flop/s
+FP32_MFMA_PEAK = 157.3e12      # MI355X dense fp32 matrix, flop/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "chunkwise_gated_delta_la_amd", "csrc")
 # Source files each kernel is built from: a traffic measurement is used
@@ -73,11 +74,24 @@ ERASE_MODES = ("delta", "gated_delta")           # beta and the T factor
 GATE_BYTES = {"linear": 0, "delta": 4, "gated_delta": 8, "gated_linear": 4}
 
 
-def fwd_flops_per_token_head(w):
+def fwd_flops_per_token_head(w, exact=False):
+    """Dense-block chunkwise flops per (token, head): the C x C products
+    (Q K^T, its product with the values, and in the delta modes K K^T, W and
+    U) counted in full; `exact` counts their causal triangle only (half)."""
     d, C = w.dk, w.C
+    f = 1 if exact else 2
     if w.mode not in ERASE_MODES:
-        return 4 * C * d + 4 * d * d
-    return 10 * C * d + 6 * d * d
+        return f * C * d + 4 * d * d
+    return 5 * f * C * d + 6 * d * d
+
+
+def op_bytes(w):
+    """Algorithmic HBM bytes of one forward call: q, k, v read and o written
+    once, the gates the mode reads, S0 (when given) read and S_final
+    written once per (b, h).  No intermediate of the design (the T records)
+    is counted."""
+    return (fwd_min_bytes_per_token_head(w) * w.B * w.H * w.L
+            + kernel_bytes_per_head("la_chunk", w) * w.B * w.H)
 
 
 def t_bytes_per_token_head(w):
@@ -240,14 +254,15 @@ def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, com
 
 # ------------------------------------------------------------------ legs
 
-def bench_forward(w, steps, warmup):
+def bench_forward(w, steps, warmup, x=None):
     import torch
 
     import chunkwise_gated_delta_la_amd as la
     import workloads
 
-    log(f"[bench] forward workload {w.name}: generating inputs")
-    x = workloads.make_inputs(w)
+    if x is None:
+        log(f"[bench] forward workload {w.name}: generating inputs")
+        x = workloads.make_inputs(w)
     copies = []
     for _ in range(2):
         copies.append({k: t.cuda() for k, t in x.items()})
@@ -280,20 +295,35 @@ def bench_forward(w, steps, warmup):
     P = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C, dtype=w.torch_dtype)
     kernels = _kernel_table(kt.stats, w, token_heads, w.B * w.H, P)
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
-    dk = kernels[dom]
-    traffic = measured_traffic(dom, w.name)
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["achieved_GBs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": dk["algorithmic_bytes"]}
     flops = fwd_flops_per_token_head(w) * token_heads
-    min_bytes = (fwd_min_bytes_per_token_head(w) * token_heads
-                 + kernel_bytes_per_head("la_chunk", w) * w.B * w.H)
+    flops_exact = fwd_flops_per_token_head(w, exact=True) * token_heads
+    min_bytes = op_bytes(w)
+    dom_s = kernels[dom]["avg_ms"] * 1e-3
+    if w.dtype == "f32":
+        # float32 matrix work, arithmetic intensity above the fp32 ridge
+        ach = flops / dom_s / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 3),
+                    "peak": FP32_MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+                    "frac": round(ach * 1e12 / FP32_MFMA_PEAK, 5), "traffic": None,
+                    "algorithmic_flops": flops}
+    else:
+        # the op's own bytes over the chain kernel's time; the T records the
+        # design keeps between its two kernels are reported beside them
+        ach = min_bytes / dom_s / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dom, w.name), "algorithmic_bytes": min_bytes,
+                    "bytes_basis": "q, k, v, o, gates, S0, S_final once each",
+                    "t_record_bytes": t_bytes_per_token_head(w) * token_heads}
+    peak = FP32_MFMA_PEAK if w.dtype == "f32" else BF16_MFMA_PEAK
     res = {
         "value": w.B * w.L / sec,
         "ms_per_step": sec * 1e3,
         "segments": P,
         "mfma_frac_of_bf16_peak": flops / sec / BF16_MFMA_PEAK,
+        "mfma_frac": flops / sec / peak,
+        "mfma_frac_exact": flops_exact / sec / peak,
+        "mfma_peak": peak,
         "hbm_frac_of_min_bytes": min_bytes / sec / (HBM_PEAK_GBS * 1e9),
         "kernels": kernels,
         "roofline": roofline,
@@ -314,6 +344,22 @@ def _kernel_table(stats, w, token_heads, heads, P=1):
                          "achieved_GBs": round(by / (avg_ms * 1e-3) / 1e9, 1),
                          "hbm_frac": round(by / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)}
     return kernels
+
+
+def bench_config(w, steps, warmup, cpu=None):
+    """One of the forward configurations at its own sizes: tokens/s, the
+    fraction of the MFMA peak of its dtype (dense-block and triangle-exact
+    flop counts), the fraction of HBM peak of its algorithmic bytes, the
+    dominant kernel's roofline, and the CPU oracle measured beside it."""
+    _, res = bench_forward(w, steps, warmup)
+    return {"workload": w.name, "mode": w.mode, "dtype": w.dtype,
+            "tokens_per_s": round(res["value"], 1),
+            "ms_per_step": round(res["ms_per_step"], 5),
+            "mfma_peak_flops": res["mfma_peak"],
+            "mfma_frac": round(res["mfma_frac"], 5),
+            "mfma_frac_exact": round(res["mfma_frac_exact"], 5),
+            "hbm_frac_of_min_bytes": round(res["hbm_frac_of_min_bytes"], 4),
+            "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": cpu}
 
 
 def bench_mode(w, steps, warmup):
@@ -746,24 +792,84 @@ def bench_decode(w, warmup=1):
     }
 
 
-def cpu_baseline(w, x, tokens):
-    """The float64 oracle, as it stands, on the first `tokens` tokens of
-    every head of the forward workload, BLAS limited to one thread."""
-    import workloads
-    import oracle
+_POOL_INPUTS = {}
+
+
+def cpu_workers():
+    """Worker processes for the oracle baseline: the CPUs this process may
+    run on, bounded by a cgroup CPU quota when one is set, and by
+    LA_BENCH_CPU_WORKERS (default 16, one GPU's share of a shared host)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, -(-int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, min(n, int(os.environ.get("LA_BENCH_CPU_WORKERS", "16"))))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_task(task):
+    """One worker's share: the oracle on a slice of (batch, head) pairs."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
-    sub = {k: (t[:, :, :tokens] if k != "S0" else t) for k, t in x.items()}
-    y = workloads.to_f64(sub)
-    log(f"[bench] cpu baseline: oracle on {tokens} tokens x {w.B * w.H} heads")
+    import oracle
+    key, heads, tokens = task
+    w, x = _POOL_INPUTS[key]
+    bs = [b for b, _ in heads]
+    hs = [h for _, h in heads]
     with threadpool_limits(1):
+        if w.is_decode:            # decode: [steps, B, H, ...]
+            sel = lambda t: t[:tokens, bs, hs][:, None].to("cpu").double().numpy()   # noqa: E731
+            oracle.decode_steps(x["S0"][bs, hs][None].double().numpy(), sel(x["q"]),
+                                sel(x["k"]), sel(x["v"]), sel(x["log_alpha"]), sel(x["beta"]),
+                                w.mode)
+        else:
+            sel = lambda t: t[bs, hs][None, :, :tokens].double().numpy()   # noqa: E731
+            s0 = x["S0"][bs, hs][None].double().numpy() if w.s0_std > 0 else None
+            oracle.recurrent_fwd(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["log_alpha"]),
+                                 sel(x["beta"]), s0, w.mode)
+    return len(heads) * tokens
+
+
+def cpu_baseline(w, x, tokens):
+    """The float64 oracle, as it stands, on the first `tokens` tokens (decode:
+    steps) of every (batch, head) sequence of workload `w`, split over a
+    pool of worker processes (one BLAS thread each).  Must run before this
+    process touches the GPU (the pool forks)."""
+    import multiprocessing as mp
+
+    n = cpu_workers()
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per = -(-len(pairs) // n)
+    tasks = [(w.name, pairs[i:i + per], tokens) for i in range(0, len(pairs), per)]
+    _POOL_INPUTS[w.name] = (w, x)
+    log(f"[bench] cpu baseline {w.name}: oracle on {tokens} tokens x {len(pairs)} heads, "
+        f"{len(tasks)} tasks on {n} workers")
+    with mp.get_context("fork").Pool(min(n, len(tasks))) as pool:
         t0 = time.perf_counter()
-        oracle.recurrent_fwd(y["q"], y["k"], y["v"], y["log_alpha"], y["beta"],
-                             y["S0"] if w.s0_std > 0 else None, w.mode)
+        done = sum(pool.map(_oracle_task, tasks, chunksize=1))
         sec = time.perf_counter() - t0
-    return {"value": w.B * tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {tokens} of {w.L} tokens of all {w.B}x{w.H} (batch, head) "
-                      f"sequences of {w.name}, float64 token recurrence, {sec:.1f} s"}
+    del _POOL_INPUTS[w.name]
+    unit_tokens = done / w.H          # (b, token) pairs: tokens/s counts B * L
+    what = "steps" if w.is_decode else "tokens"
+    full = w.steps if w.is_decode else w.L
+    return {"value": round(unit_tokens / sec, 1), "unit": "tokens/s", "cores": min(n, len(tasks)),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "sample": f"first {tokens} of {full} {what} of all {w.B}x{w.H} (batch, head) "
+                      f"sequences of {w.name}, float64 token recurrence, "
+                      f"{min(n, len(tasks))} worker processes, {sec:.1f} s wall"}
 
 
 def main():
@@ -778,7 +884,10 @@ def main():
                          "split over N GPUs (H / N heads on this GPU)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra measurements (other mode, packed batch)")
+                    help="skip the extra measurements (other configurations, modes, packed "
+                         "batch, fused steps, backward)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the legs of the other forward configurations (1-3)")
     ap.add_argument("--only-backward", action="store_true",
                     help="only time la_chunk_bwd at the forward workload's sizes and print "
                          "that measurement (for profiling runs)")
@@ -807,8 +916,27 @@ def main():
               "see the design notes, but no multi-GPU path is built).", file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import workloads
+
+    w = workloads.head_shard(workloads.WORKLOADS[args.workload], args.shard)
+    configs = () if (args.no_extra or args.no_configs or args.only_backward or
+                     args.calibrate_copy) else (1, 2, 3)
+    # The CPU oracle baselines run first: their worker pool forks, which
+    # must happen before this process touches the GPU.
+    x = cpu = None
+    cpu_cfg = {}
+    if not (args.only_backward or args.calibrate_copy):
+        x = workloads.make_inputs(w)
+        if args.cpu_tokens > 0:
+            cpu = cpu_baseline(w, x, min(args.cpu_tokens, w.L))
+            for i in configs:
+                wi = workloads.WORKLOADS[i]
+                cpu_cfg[i] = cpu_baseline(wi, workloads.make_inputs(wi), wi.L)
+            if not args.no_decode:
+                wd = workloads.WORKLOADS[5]
+                cpu_cfg[5] = cpu_baseline(wd, workloads.make_inputs(wd), 16)
+
+    import torch
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -816,13 +944,17 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
-    w = workloads.head_shard(workloads.WORKLOADS[args.workload], args.shard)
     if args.only_backward:
         print(json.dumps({"backward": bench_backward(w, args.steps, args.warmup,
                                                      args.bwd_cpu_tokens)}), flush=True)
         return
-    x, fwd = bench_forward(w, args.steps, args.warmup)
-    dec = None if args.no_decode else bench_decode(workloads.WORKLOADS[5])
+    _, fwd = bench_forward(w, args.steps, args.warmup, x)
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(workloads.WORKLOADS[5])
+        dec["cpu_baseline"] = cpu_cfg.get(5)
+    cfg = {f"config{i}": bench_config(workloads.WORKLOADS[i], args.steps, 1, cpu_cfg.get(i))
+           for i in configs}
     extra = None
     if not args.no_extra:
         extra = {
@@ -836,7 +968,6 @@ def main():
             "backward_varlen": bench_bwd_varlen(w, 64, w.L, args.steps, 1),
             "backward_fused": bench_bwd_fused(w, args.steps, 1),
         }
-    cpu = cpu_baseline(w, x, args.cpu_tokens) if args.cpu_tokens > 0 else None
     line = {
         "metric": METRIC,
         "value": fwd["value"],
@@ -855,10 +986,12 @@ def main():
                    "float32 gates and state", "segments": fwd["segments"],
                    "head_shard_of": args.shard},
         "mfma_frac_of_bf16_peak": round(fwd["mfma_frac_of_bf16_peak"], 4),
+        "mfma_frac_exact": round(fwd["mfma_frac_exact"], 4),
         "hbm_frac_of_min_bytes": round(fwd["hbm_frac_of_min_bytes"], 4),
         "roofline": fwd["roofline"],
         "kernels": fwd["kernels"],
         "decode": dec,
+        "configs": cfg,
         "extra": extra,
         "cpu_baseline": cpu,
     }
