@@ -6,7 +6,8 @@
 //    A = strict_lower(diag(beta) K K^T * Gamma) and T = (I + A)^-1.  T does
 //    not depend on the state, so all chunks are solved at once, at full
 //    occupancy, and written to a workspace as the exact MFMA operand
-//    fragments the second kernel feeds to U_new = T R (6 KiB per chunk).
+//    fragments the second kernel feeds to U_new = T R, split into bf16 hi
+//    and lo parts (12 KiB per chunk).
 //
 // 2. chunk_pipe_kernel, one 256-thread workgroup per 16-column tile of one
 //    (batch, head) state, walking the chunks in order.  Per chunk c, with a
@@ -55,6 +56,8 @@
 // Precision as in the float kernel's bf16 path: q, k, v exact, float
 // operands split into bf16 hi + lo, T a single bf16, float accumulation and
 // state.
+#include <type_traits>
+
 #include "la_device.hpp"
 #include "la_kernels.hpp"
 
@@ -250,12 +253,15 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows,
 // ---------------------------------------------------------------- T solve
 
 // Fragment index of the T operand (row tile ti, 32-deep block kb), kb <= ti / 2.
+// A record holds the kTFrags fragments of bf16(T) (hi) and then those of
+// bf16(T - hi) (lo): T enters U_new = T R as a split operand.
 __device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
 constexpr int kTFrags = 6;
+constexpr int kTRecFrags = 2 * kTFrags;   // 16-byte lane slots per record, per lane
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
-__device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int g, int n) {
+__device__ __forceinline__ void t_diag(const float* Ab, float* Df, float* Tf, int g, int n) {
   const float* A = Ab + bid(g, g) * 16 * LDB;
   f32x4 arow[16][4];
 #pragma unroll
@@ -278,7 +284,7 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int 
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     Df[g * 16 * LDB + r * LDB + n] = x[r];
-    Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)x[r];
+    Tf[(16 * g + r) * LDT + 16 * g + n] = x[r];
   }
 }
 
@@ -287,7 +293,7 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int 
 //   [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
 // (block inverse of a 2 x 2 block lower-triangular matrix, applied twice),
 // four dependent product steps.  Products split both operands.
-__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, T16* Tb,
+__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, float* Tf,
                                       int g, int n) {
   auto blkA = [&](int i, int j) { return Ab + bid(i, j) * 16 * LDB; };
   auto blkD = [&](int i) { return Df + i * 16 * LDB; };
@@ -333,12 +339,12 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 4 * g + e;
-    Tb[(16 + r) * LDT + n] = (T16)t10[e];
-    Tb[(48 + r) * LDT + 32 + n] = (T16)t32[e];
-    Tb[(32 + r) * LDT + n] = (T16)(-y00[e]);
-    Tb[(32 + r) * LDT + 16 + n] = (T16)(-y01[e]);
-    Tb[(48 + r) * LDT + n] = (T16)(-y10[e]);
-    Tb[(48 + r) * LDT + 16 + n] = (T16)(-y11[e]);
+    Tf[(16 + r) * LDT + n] = t10[e];
+    Tf[(48 + r) * LDT + 32 + n] = t32[e];
+    Tf[(32 + r) * LDT + n] = -y00[e];
+    Tf[(32 + r) * LDT + 16 + n] = -y01[e];
+    Tf[(48 + r) * LDT + n] = -y10[e];
+    Tf[(48 + r) * LDT + 16 + n] = -y11[e];
   }
 }
 
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
   __shared__ __attribute__((aligned(16))) float Ab[TS ? 10 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float Df[TS ? 4 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float T32f[TS ? 16 * LDB : 1];
-  __shared__ __attribute__((aligned(16))) T16 Tb[TS ? C * LDT : 1];
+  __shared__ __attribute__((aligned(16))) float Tf[TS ? C * LDT : 1];
   __shared__ __attribute__((aligned(16))) float gsh[C];               // row exponents
   __shared__ __attribute__((aligned(16))) float gcsh[PRO ? C : 1];    // column exponents
   __shared__ __attribute__((aligned(16))) float bsh[C];
@@ -499,8 +505,8 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
     // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
-      Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
+      Tf[(4 * g + e) * LDT + 16 + n] = 0.f;
+      Tf[(32 + 4 * g + e) * LDT + 48 + n] = 0.f;
     }
     __syncthreads();
 
@@ -527,49 +533,60 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
       }
     }
     __syncthreads();
-    t_diag(Ab, Df, Tb, g, n);
+    t_diag(Ab, Df, Tf, g, n);
     __syncthreads();
-    t_col(Ab, Df, T32f, Tb, g, n);
+    t_col(Ab, Df, T32f, Tf, g, n);
     __syncthreads();
-    u32x4* dst = tws + item * (kTFrags * kWave);
+    u32x4* dst = tws + item * (kTRecFrags * kWave);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int kb = 0; kb <= ti / 2; ++kb) {
-        const Frag<T16> f = frag_row(Tb + (16 * ti + n) * LDT + 32 * kb, g);
-        dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.v);
+        const Frag2<T16> f = frag2_row<T16>(Tf + (16 * ti + n) * LDT + 32 * kb, g);
+        dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.hi.v);
+        dst[(kTFrags + tfi(ti, kb)) * kWave + lane] = __builtin_bit_cast(u32x4, f.lo.v);
       }
   }
 }
 
 
-// ---------------------------------------------------------------- side roles
+// ---------------------------------------------------------------- output roles
 
-// Scores and Q S of chunk c for row tiles TI0 (and TI1 if NTI == 2), kept in
-// registers.  sc[u][tj] is the K Q^T tile (tj, ti): lane (g, n) holds
-// Aqk[16 ti + n][16 tj + 4 g + e] (decayed, masked); qs[u] holds
-// gam[16 ti + 4 g + e] (Q S)[16 ti + 4 g + e][n].  roff[kb] is the lane's
-// byte offset of operand row n over dk block kb in a Q or K tile.  The decay
-// of score (r, i) is exp(gsc[r] - gkc[i]) and Q S row r is scaled by
-// esc[r]: the exponents g and the factors exp(g), or with normalised q and
-// k the same with the logs of the inverse norms folded in.
-template <int D, bool GATED, int NTI, int TI0, int TI1>
-__device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const float* gsc,
-                                          const float* gkc, const float* esc,
-                                          const Frag<T16>* Sx,
-                                          const uint32_t (&roff)[D / 32], f32x4 (&sc)[2][4],
-                                          f32x4 (&qs)[2], int g, int n, int lane) {
+// Q rows of row tile TI of a chunk straight from HBM as operand fragments:
+// lane (g, n) holds row 16 TI + n, columns 32 kb + 8 g .. + 7 of each dk
+// block (one 16-byte load per block) -- the same contraction order as the
+// K rows in LDS and the permuted state rows.  Rows at or past nrows (the
+// end of the sequence in a partial last chunk) read the last valid row.
+template <int D, int TI>
+__device__ __forceinline__ void load_q(Frag<T16> (&qf)[D / 32], const T16* q, size_t r0,
+                                       int nrows, int g, int n) {
+  const T16* row = q + (r0 + (size_t)min(16 * TI + n, nrows - 1)) * D + 8 * g;
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) qf[kb].v = *reinterpret_cast<const bf16x8*>(row + 32 * kb);
+}
+
+// Scores and Q S of one chunk for row tile TI, kept in registers.  sc[t] is
+// the K Q^T tile (t, TI): lane (g, n) holds Aqk[16 TI + n][16 t + 4 g + e]
+// (decayed, masked).  The output is formed transposed, O^T = S^T Q^T +
+// U_new^T Aqk^T: the same operand fragments with A and B swapped (an A and a
+// B fragment have the same lane layout), so that lane (g, n) holds token
+// 16 TI + n at the four adjacent columns 4 g + e and writes them with one
+// store.  qs holds gam[16 TI + n] (Q S)[16 TI + n][4 g + e].  roff[kb] is
+// the lane's byte offset of operand row n over dk block kb in a K tile.  The
+// decay of score (r, i) is exp(gsc[r] - gkc[i]) and Q S row r is scaled by
+// esc[r]: the exponents g and the factors exp(g), or with normalised q and k
+// the same with the logs of the inverse norms folded in.
+template <int D, bool GATED, int TI>
+__device__ __forceinline__ void scores_qs(const Frag<T16> (&qf)[D / 32], const T16* Kt,
+                                          const float* gsc, const float* gkc, const float* esc,
+                                          const Frag<T16>* Sx, const uint32_t (&roff)[D / 32],
+                                          f32x4 (&sc)[4], f32x4& qs, int g, int n, int lane) {
   constexpr int NKB = D / 32;
-  constexpr int NT = (NTI == 2 ? (TI0 > TI1 ? TI0 : TI1) : TI0) + 1;
   constexpr uint32_t kRows16 = 32 * D;          // bytes of 16 tile rows
-  Frag<T16> qf[NTI][NKB], kf[NT][NKB];
+  Frag<T16> kf[TI + 1][NKB];
   Frag2<T16> sx[NKB];
 #pragma unroll
-  for (int u = 0; u < NTI; ++u)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) qf[u][kb] = frag_row_at<D>(Qt, roff[kb] + kRows16 * (u ? TI1 : TI0));
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t <= TI; ++t)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) kf[t][kb] = frag_row_at<D>(Kt, roff[kb] + kRows16 * t);
 #pragma unroll
@@ -577,101 +594,83 @@ __device__ __forceinline__ void scores_qs(const T16* Qt, const T16* Kt, const fl
     sx[kb].hi = Sx[(2 * kb) * kWave + lane];
     sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
   }
-  float gq[NTI];
-  f32x4 gk[NT], eq[NTI];
+  float gq = 0.f, eq = 1.f;
+  f32x4 gk[TI + 1];
   if constexpr (GATED) {
+    gq = gsc[16 * TI + n];
+    eq = esc[16 * TI + n];
 #pragma unroll
-    for (int u = 0; u < NTI; ++u) {
-      gq[u] = gsc[16 * (u ? TI1 : TI0) + n];
-      eq[u] = *reinterpret_cast<const f32x4*>(esc + 16 * (u ? TI1 : TI0) + 4 * g);
-    }
+    for (int t = 0; t <= TI; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gkc + 16 * t + 4 * g);
+  }
+  qs = zero4();
 #pragma unroll
-    for (int t = 0; t < NT; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gkc + 16 * t + 4 * g);
+  for (int kb = 0; kb < NKB; ++kb) {
+    mma(sx[kb].lo, qf[kb], qs);
+    mma(sx[kb].hi, qf[kb], qs);
   }
 #pragma unroll
-  for (int u = 0; u < NTI; ++u) {
-    const int ti = u ? TI1 : TI0;
-    qs[u] = zero4();
+  for (int t = 0; t < 4; ++t) {
+    sc[t] = zero4();
+    if (t > TI) continue;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) mma_ab2(qf[u][kb], sx[kb], qs[u]);
+    for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[kb], sc[t]);
+    // element (K row 16 t + 4 g + e, Q row 16 TI + n) = Aqk[r][i]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sc[u][t] = zero4();
-      if (t > ti) continue;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[u][kb], sc[u][t]);
-      // element (K row 16 t + 4 g + e, Q row 16 ti + n) = Aqk[r][cc]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = t < ti || 4 * g + e <= n;
-        float decay = 1.f;
-        if constexpr (GATED) decay = __expf(keep ? gq[u] - gk[t][e] : 0.f);
-        sc[u][t][e] = keep ? sc[u][t][e] * decay : 0.f;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const bool keep = t < TI || 4 * g + e <= n;
+      float decay = 1.f;
+      if constexpr (GATED) decay = __expf(keep ? gq - gk[t][e] : 0.f);
+      sc[t][e] = keep ? sc[t][e] * decay : 0.f;
     }
-    if constexpr (GATED) qs[u] *= eq[u];
   }
+  if constexpr (GATED) qs *= eq;
 }
 
-// Output of one chunk for the row tiles of scores_qs: O = qs + Aqk U_new
-// (U_new = V in the modes without erase), into o[u] (row tile u ? TI1 : TI0, accumulator
-// layout).  U_new arrives in float (Uf, accumulator layout, tile ti at
-// ti * 64 + lane) and is split here.  DSKIP: plus the residual dcol * V of
-// the lane's column (the value tile read in the same accumulator layout).
-template <int D, int MODE, bool DSKIP, int NTI, int TI0, int TI1>
-__device__ __forceinline__ void out_rows(const f32x4 (&sc)[2][4], const f32x4 (&qs)[2],
-                                         const f32x4* Uf, const T16* Vt, f32x4 (&o)[2],
-                                         int g, int n, int lane, float dcol) {
+// Output of row tile TI, transposed: O^T = qs + U_new^T Aqk^T (U_new = V in
+// the modes without erase).  U_new arrives split (Uf: hi and lo fragments of
+// 32-deep block kb at (2 kb) * 64 + lane and (2 kb + 1) * 64 + lane).
+// DSKIP: plus the residual D * V at the lane's token and four columns
+// (dcol4, and four adjacent values of the value tile's row).
+template <int D, int MODE, bool DSKIP, int TI>
+__device__ __forceinline__ void out_rows(const f32x4 (&sc)[4], const f32x4& qs,
+                                         const Frag<T16>* Uf, const T16* Vt, f32x4& o, int g,
+                                         int n, int lane, const f32x4& dcol4) {
   constexpr bool kDelta = mode_erase(MODE);
-  Frag2<T16> uf[2];
+  o = qs;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb <= TI / 2; ++kb) {
+    const Frag2<T16> a = frag2_from_acc<T16>(sc[2 * kb], sc[2 * kb + 1]);
     if constexpr (kDelta) {
-      uf[kb] = frag2_from_acc<T16>(Uf[(2 * kb) * kWave + lane], Uf[(2 * kb + 1) * kWave + lane]);
+      Frag2<T16> u;
+      u.hi = Uf[(2 * kb) * kWave + lane];
+      u.lo = Uf[(2 * kb + 1) * kWave + lane];
+      mma_a2b2(u, a, o);
     } else {
-      uf[kb].hi = frag_col_tr_v(Vt, 32 * kb, g, n);
+      const Frag<T16> u = frag_col_tr_v(Vt, 32 * kb, g, n);
+      mma(u, a.lo, o);
+      mma(u, a.hi, o);
     }
   }
+  if constexpr (DSKIP) {
+    const bf16x4 vr = lds_ld<bf16x4>(Vt, (uint32_t)(((16 * TI + n) * 16 + 4 * g) * 2));
 #pragma unroll
-  for (int u = 0; u < NTI; ++u) {
-    const int ti = u ? TI1 : TI0;
-    o[u] = qs[u];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (2 * kb > ti) continue;
-      const Frag2<T16> a = frag2_from_acc<T16>(sc[u][2 * kb], sc[u][2 * kb + 1]);
-      if constexpr (kDelta) {
-        mma_a2b2(a, uf[kb], o[u]);
-      } else {
-        mma(a.lo, uf[kb].hi, o[u]);
-        mma(a.hi, uf[kb].hi, o[u]);
-      }
-    }
-    if constexpr (DSKIP) o[u] += dcol * v_acc_at(Vt, vacc_off(g, n) + 512 * ti);
+    for (int e = 0; e < 4; ++e) o[e] += dcol4[e] * (float)vr[e];
   }
 }
 
-// Store of the rows out_rows produced; rows at or past nrows (past the end
-// of the sequence in a partial last chunk) are not written.
-template <int D, int NTI, int TI0, int TI1>
-__device__ __forceinline__ void store_rows(const f32x4 (&o)[2], void* out_, size_t ob0,
-                                           int out_bf16, int g, int nrows) {
-#pragma unroll
-  for (int u = 0; u < NTI; ++u) {
-    const int ti = u ? TI1 : TI0;
-    const int r0 = 16 * ti + 4 * g;
-    const size_t ob = ob0 + (size_t)r0 * D;
-    if (out_bf16) {
-      T16* out = static_cast<T16*>(out_);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (r0 + e < nrows) out[ob + (size_t)e * D] = (T16)o[u][e];
-    } else {
-      float* out = static_cast<float*>(out_);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (r0 + e < nrows) out[ob + (size_t)e * D] = o[u][e];
-    }
+// Store of row tile TI: token 16 TI + n, columns 4 g .. 4 g + 3 of the tile
+// (one 8-byte bf16 or 16-byte float store per lane); tokens at or past nrows
+// (past the end of the sequence in a partial last chunk) are not written.
+template <int D, int TI>
+__device__ __forceinline__ void store_rows(const f32x4& o, void* out_, size_t ob0, int out_bf16,
+                                           int g, int n, int nrows) {
+  if (16 * TI + n >= nrows) return;
+  const size_t ob = ob0 + (size_t)(16 * TI + n) * D + 4 * g;
+  if (out_bf16) {
+    const bf16x4 h = __builtin_convertvector(o, bf16x4);
+    *reinterpret_cast<bf16x4*>(static_cast<T16*>(out_) + ob) = h;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + ob) = o;
   }
 }
 
@@ -680,8 +679,42 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
   return wave_inclusive_scan(p[lane]);
 }
 
+// Bound on the chain halves' wait for each other, in s_sleep periods of 64
+// clocks (about 0.5 ms): the partner arrives within one chunk step (a few
+// thousand clocks), so the bound only keeps a logic error from hanging the
+// GPU.
+constexpr int kSpinLimit = 1 << 14;
+
 // ---------------------------------------------------------------- chain kernel
 
+// One workgroup per (stream, 16-column tile of the state); the dv columns of
+// S evolve independently, so a stream's state is split into D / 16 tiles
+// that walk the chunks in parallel.  Waves and their roles:
+//
+//   waves 0, 1   the serial chain, each on half of the state's rows (dk):
+//                partial K S over its half, the two halves exchanged through
+//                LDS (a flag per half, no barrier), then each computes the
+//                whole R = diag(beta)(V - diag(gam) K S) and U_new = T R
+//                (T split) and updates its half, S <- gam_C S + K^T
+//                diag(gam_C / gam) U_new, publishing its split for the
+//                output waves.  Without erase: S <- gam_C S + K^T diag(f) V.
+//   DMA K        K of chunk c+2 and the gates of chunk c+4 into LDS rings
+//   DMA V        V of chunk c+3 and the T record of chunk c+2; the decay
+//                tables of chunk c+2; beta V (or f V) of chunk c+1 in the
+//                chain's accumulator layout; the zero rows of a partial V
+//   output (4)   one row tile each: the output of chunk c-1 from the U_new
+//                published at the last barrier (formed transposed: one
+//                store per lane of four adjacent columns), then the masked
+//                decayed scores and diag(gam) Q S of chunk c (Q straight
+//                from HBM, prefetched one chunk ahead) kept in registers
+//
+// OUT: 8 waves (chain 0, 1; output tiles 3, 2 on waves 2, 3 and 0, 1 on
+// waves 6, 7; DMA K wave 4, DMA V wave 5).  The state pass (OUT = false)
+// has no output waves: 4 waves (chain 0, 1; DMA K 2; DMA V 3).  Waves go to
+// the four SIMDs round robin, so the two chain halves run on their own
+// SIMDs, each beside a DMA wave, and the output waves pair the row tiles of
+// most and least work on the other two.  One barrier per chunk.
+//
 // OUT = false is the state pass of the sequence-parallel forward: the chain
 // alone, with no Q and no outputs.  FUSED: q and k are normalised inside the
 // op -- with r_t = 1 / |x_t| per token, every product of the method sees
@@ -693,7 +726,7 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 // (MODE is then one of the decayed modes; log alpha = 0 stands for none).
 // DSKIP: the output gains the residual D * v (Mamba's term in v), D [H, dv].
 template <int D, int MODE, bool OUT, bool FUSED, bool DSKIP>
-__global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
+__global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const u32x4* __restrict__ tws, void* __restrict__ out_, StreamMap smap, int NS,
@@ -704,34 +737,39 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   static_assert(!DSKIP || OUT, "the residual is part of the output");
   constexpr int NKT = D / 16;                    // 16-row tiles of the state
   constexpr int NKB = D / 32;                    // 32-deep blocks over dk
+  constexpr int HT = NKT / 2, HB = NKB / 2;      // of one chain half
   constexpr int NCT = D / 16;                    // column tiles per head
-  constexpr int TILE = C * D;                    // elements of a Q / K tile
-  constexpr uint32_t kTileB = 2 * TILE;          // bytes of a Q / K tile
+  constexpr int TILE = C * D;                    // elements of a K tile
+  constexpr uint32_t kTileB = 2 * TILE;          // bytes of a K tile
   constexpr uint32_t kRows16 = 32 * D;           // bytes of 16 tile rows
   constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
-  constexpr int NG = 5;                          // gate ring depth (DMA 4 ahead)
-  // DMA instructions per chunk of wave 3: V (2), T, beta, log alpha, lk, lq
-  constexpr int NDMA3 =
-      2 + (kDelta ? kTFrags + 1 : 0) + (kGated ? 1 : 0) + (FUSED ? 1 : 0) + (FUSED && OUT ? 1 : 0);
+  constexpr int NG = 5;                          // gate rings (DMA 4 ahead)
+  constexpr int NV = 5;                          // value ring (DMA 3 ahead)
+  constexpr int kDmaK = OUT ? 4 : 2, kDmaV = OUT ? 5 : 3;
+  constexpr bool kQSide = FUSED && OUT;          // (the state pass has no Q side: only lk)
+  constexpr int NDMAK = NTILE + (kDelta ? 1 : 0) + (kGated ? 1 : 0) + (FUSED ? 1 : 0) +
+                        (kQSide ? 1 : 0);        // per chunk of the DMA K wave
+  constexpr int NDMAV = 2 + (kDelta ? kTRecFrags : 0);   // per chunk of the DMA V wave
+  constexpr bool kBV = kDelta || MODE == kModeGatedLinear;  // beta V or f V for the chain
 
-  __shared__ __attribute__((aligned(16))) T16 Qs[3][TILE];
   __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
-  __shared__ __attribute__((aligned(16))) T16 Vs[4][C * 16];
-  __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTFrags * kWave : 1];
+  __shared__ __attribute__((aligned(16))) T16 Vs[NV][C * 16];
+  __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTRecFrags * kWave : 1];
   __shared__ __attribute__((aligned(16))) float Ls[kGated ? NG : 1][C];  // log alpha
   __shared__ __attribute__((aligned(16))) float Bs[kDelta ? NG : 1][C];  // beta
   __shared__ __attribute__((aligned(16))) float Gs[kGated ? 3 : 1][C];   // g (in-chunk cumsum)
   __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
-  // (the state pass has no Q side: only lk)
-  constexpr bool kQSide = FUSED && OUT;
   __shared__ __attribute__((aligned(16))) float LQs[kQSide ? NG : 1][C];  // log(1 / |q|)
   __shared__ __attribute__((aligned(16))) float LKs[FUSED ? NG : 1][C];   // log(1 / |k|)
   __shared__ __attribute__((aligned(16))) float Gk[kQSide ? 3 : 1][C];    // g - lk (score columns)
   __shared__ __attribute__((aligned(16))) float Eq[kQSide ? 3 : 1][C];    // exp(g + lq) (Q S rows)
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
-  __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
+  __shared__ __attribute__((aligned(16))) f32x4 BVs[kBV ? 2 : 1][kBV ? 4 * kWave : 1];
+  __shared__ __attribute__((aligned(16))) f32x4 XP[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
+  __shared__ int XF[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -740,7 +778,7 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int n = lane % 16;
 
   // stream (sequence or segment) and column tile; the column tiles of one
-  // stream share an XCD (blocks go to XCDs round robin), so its Q, K and T
+  // stream share an XCD (blocks go to XCDs round robin), so its K, Q and T
   // reads are shared in that XCD's L2
   int sidx, ct;
   {
@@ -757,7 +795,6 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   const int col0 = ct * 16;
   const int col = col0 + n;
   const StreamInfo si = stream_info(smap, sidx);
-  const float dcol = DSKIP ? dskip[(size_t)si.head * D + col] : 0.f;
   const size_t hbase = si.row0;                 // first token row
   const int L = si.len;                         // tokens of this stream
   if (L == 0) {
@@ -780,75 +817,60 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
   // causal.
   const int NC = (L + C - 1) / C;
   const int nlast = L - (NC - 1) * C;
-  const u32x4* tw = tws + si.slot0 * (kTFrags * kWave);
+  const u32x4* tw = tws + si.slot0 * (kTRecFrags * kWave);
+  const bool vzero = si.eye;          // a transition stream reads no V: its ring holds zeros
 
-  // lane offsets of operand row n over each dk block in a Q or K tile
+  // lane offsets of operand row n over each dk block in a K tile
   uint32_t roff[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) roff[kb] = unit_off<D>(n, 4 * kb + g);
 
-  // Lane offsets of the DMA sources (loop-invariant): a Q or K tile for
-  // waves 1 and 2; for wave 3 the two V instructions (rows 32 m + l / 2,
-  // columns col0 + 8 (l % 2) ..) and the T fragments.
-  uint32_t doff[NTILE];
-  dma_tile_offsets<D>(doff, lane, C);
-  auto v_off = [&](int m, int nrows) {
-    return (uint32_t)((min(32 * m + lane / 2, nrows - 1) * D + 8 * (lane % 2)) * 2);
+  // Ring slot offsets go through readfirstlane: opaque to the loop
+  // optimiser, which would otherwise turn each lane address into an
+  // induction variable of its own plus a wrap correction (two adds per
+  // address and a register each) instead of one add to a scalar.
+  auto slot = [](int c, int depth, uint32_t bytes) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(c % depth) * bytes));
   };
-  uint32_t voff[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) voff[m] = v_off(m, C);
 
-  // DMA of chunk cc: wave 1 K, wave 2 Q, wave 3 this tile's V columns and T
-  // (a transition stream reads no V: its ring holds zeros)
-  const bool vzero = si.eye;
-  auto issue_chunk = [&](int cc) {
+  // DMA of K of chunk cc (the DMA K wave); rows past the sequence read the
+  // last valid row
+  auto issue_k = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
-    const bool part = cc == NC - 1 && nlast < C;     // partial last chunk
-    // (one branch per wave, so that each LDS destination is a compile-time
-    // array and its address stays scalar)
-    auto tile = [&](T16* dst, const T16* src) {
-      if (part) {
-        uint32_t po[NTILE];
-        dma_tile_offsets<D>(po, lane, nlast);
-        dma_tile<D>(dst, src, po);
-      } else {
-        dma_tile<D>(dst, src, doff);
-      }
-    };
-    if (wave == 1) {
-      tile(Ks[cc % 3], k + r0 * D);
-    } else if (wave == 2) {
-      if constexpr (OUT) tile(Qs[cc % 3], q + r0 * D);
-    } else {
-      const uint32_t vb = lds_addr(Vs[cc % 4]);
-      if (!vzero) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          dma16s(v + r0 * D + col0, part ? v_off(m, nlast) : voff[m],
-                 __builtin_amdgcn_readfirstlane(vb + 1024 * m));
-      }
-      if constexpr (kDelta) {
-        const uint32_t tb = lds_addr(Ts[cc % 3]);
-        const u32x4* src = tw + (size_t)cc * (kTFrags * kWave);
-#pragma unroll
-        for (int f = 0; f < kTFrags; ++f)
-          dma16s(src, (uint32_t)((f * kWave + lane) * 16), __builtin_amdgcn_readfirstlane(tb + 1024 * f));
-      }
-    }
+    uint32_t po[NTILE];
+    dma_tile_offsets<D>(po, lane, cc == NC - 1 ? nlast : C);
+    dma_tile<D>(Ks[cc % 3], k + r0 * D, po);
   };
-  // DMA of the gates of chunk cc (wave 3); lanes past the sequence read the
-  // last valid token's gates (tables() zeroes them)
+  // DMA of this tile's V columns (rows 32 m + l / 2, columns col0 + 8 (l % 2)
+  // ..) and of the T record of chunk cc (the DMA V wave)
+  auto issue_v = [&](int cc) {
+    const size_t r0 = hbase + (size_t)cc * C;
+    const int nr = cc == NC - 1 ? nlast : C;
+    const uint32_t vb = lds_addr(Vs[cc % NV]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      dma16s(v + r0 * D + col0, (uint32_t)((min(32 * m + lane / 2, nr - 1) * D + 8 * (lane % 2)) * 2),
+             __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+  };
+  auto issue_t = [&](int cc) {
+    const uint32_t tb = lds_addr(Ts[cc % 3]);
+    const u32x4* src = tw + (size_t)cc * (kTRecFrags * kWave);
+#pragma unroll
+    for (int f = 0; f < kTRecFrags; ++f)
+      dma16s(src, (uint32_t)((f * kWave + lane) * 16), __builtin_amdgcn_readfirstlane(tb + 1024 * f));
+  };
+  // DMA of the gates of chunk cc (the DMA K wave); lanes past the sequence
+  // read the last valid token's gates (tables() zeroes them)
   auto issue_gates = [&](int cc) {
     const size_t r0 = hbase + (size_t)cc * C;
     const uint32_t go = (uint32_t)(cc == NC - 1 ? min(lane, nlast - 1) : lane) * 4;
     if constexpr (kDelta) dma4s(beta + r0, go, lds_addr(Bs[cc % NG]));
     if constexpr (kGated) dma4s(log_alpha + r0, go, lds_addr(Ls[cc % NG]));
     if constexpr (FUSED) dma4s(pro.lk + r0, go, lds_addr(LKs[cc % NG]));
-    if constexpr (FUSED && OUT) dma4s(pro.lq + r0, go, lds_addr(LQs[cc % NG]));
+    if constexpr (kQSide) dma4s(pro.lq + r0, go, lds_addr(LQs[cc % NG]));
   };
   // Gates of rows past the sequence set to zero, then the decay tables of
-  // chunk cc from its gates (wave 2, after the gates have landed)
+  // chunk cc from its gates (the DMA V wave, after the gates have landed)
   auto tables = [&](int cc) {
     if (cc == NC - 1 && lane >= nlast) {
       if constexpr (kDelta) Bs[cc % NG][lane] = 0.f;
@@ -877,35 +899,62 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
       if constexpr (kDelta) BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
     }
   };
+  // beta V (erase) or f V (gated linear) of chunk cc in the chain's
+  // accumulator layout (rows 16 ti + 4 g + e, column n), float
+  auto make_bv = [&](int cc) {
+    if constexpr (kBV) {
+      const T16* Vt = Vs[cc % NV];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const f32x4 vv = v_acc_at(Vt, vacc_off(g, n) + 512 * ti);
+        f32x4 s;
+        if constexpr (kDelta) s = *reinterpret_cast<const f32x4*>(&Bs[cc % NG][16 * ti + 4 * g]);
+        else s = *reinterpret_cast<const f32x4*>(&Fs[cc % 3][16 * ti + 4 * g]);
+        BVs[cc % 2][ti * kWave + lane] = vv * s;
+      }
+    }
+  };
+  // V rows past the sequence set to zero once the last chunk's V has landed
+  auto zero_v_tail = [&]() {
+    if (nlast < C && lane >= nlast) {
+      u32x4* row = reinterpret_cast<u32x4*>(Vs[(NC - 1) % NV] + lane * 16);
+      row[0] = u32x4{0u, 0u, 0u, 0u};
+      row[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   // Each role runs its own loop with the same barriers (two in the
   // prologue, one per chunk), so the registers one role carries from chunk
   // to chunk are not live in the other's code.
-  if (wave == 0) {
-    // ================= chain
-    f32x4 S[NKT];
-    Frag2<T16> sf[NKB];            // bf16 split of S, as published in Sx
+  if (wave < 2) {
+    // ================= chain: half h of the state's rows
+    const int h = wave;
+    f32x4 S[HT];
+    Frag2<T16> sf[HB];            // bf16 split of this half of S, as published in Sx
     if (si.eye) {
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[tj][i] = dk_of_row(16 * tj + 4 * g + i) == col ? 1.f : 0.f;
-    } else if (si.s0) {
-#pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
+      for (int j = 0; j < HT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          S[tj][i] = si.s0[(size_t)dk_of_row(16 * tj + 4 * g + i) * D + col];
+          S[j][i] = dk_of_row(16 * (h * HT + j) + 4 * g + i) == col ? 1.f : 0.f;
+    } else if (si.s0) {
+#pragma unroll
+      for (int j = 0; j < HT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[j][i] = si.s0[(size_t)dk_of_row(16 * (h * HT + j) + 4 * g + i) * D + col];
     } else {
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj) S[tj] = zero4();
+      for (int j = 0; j < HT; ++j) S[j] = zero4();
     }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-      Sx[0][(2 * kb) * kWave + lane] = sf[kb].hi;
-      Sx[0][(2 * kb + 1) * kWave + lane] = sf[kb].lo;
+    for (int j = 0; j < HB; ++j) {
+      const int kb = h * HB + j;
+      sf[j] = frag2_from_acc<T16>(S[2 * j], S[2 * j + 1]);
+      Sx[0][(2 * kb) * kWave + lane] = sf[j].hi;
+      Sx[0][(2 * kb + 1) * kWave + lane] = sf[j].lo;
     }
+    if (lane == 0) XF[h] = 0;
     __syncthreads();
     __syncthreads();
     // S is carried decayed by the coming chunk's gam_C: the accumulator of
@@ -913,25 +962,17 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
     if constexpr (kGated) {
       const float g0 = Es[0][C - 1];
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj) S[tj] *= g0;
+      for (int j = 0; j < HT; ++j) S[j] *= g0;
     }
 
     // loop-invariant lane offsets
-    uint32_t ktr[NKT / 2];
+    uint32_t ktr[HT / 2];
 #pragma unroll
-    for (int kbs = 0; kbs < NKT / 2; ++kbs) ktr[kbs] = tr_off<D>(g, n, kbs);
-    const uint32_t voff = vacc_off(g, n);
-    const uint32_t toff = (uint32_t)lane * 16;
+    for (int j = 0; j < HT / 2; ++j) ktr[j] = tr_off<D>(g, n, h * (HT / 2) + j);
     const uint32_t goff = (uint32_t)(4 * g) * 4;        // tables: row 16 ti + 4 g
-    const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf slots
+    const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf / BVs / XP slots
+    const uint32_t xown = (uint32_t)h * 4 * kWave * 16, xother = (uint32_t)(1 - h) * 4 * kWave * 16;
 
-    // Ring slot offsets go through readfirstlane: opaque to the loop
-    // optimiser, which would otherwise turn each lane address into an
-    // induction variable of its own plus a wrap correction (two adds per
-    // address and a register each) instead of one add to a scalar.
-    auto slot = [](int c, int depth, uint32_t bytes) {
-      return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(c % depth) * bytes));
-    };
     for (int c = 0; c < NC; ++c) {
       const uint32_t kslot = slot(c, 3, kTileB);
       // gam_C of chunk c+1 (its tables are two chunks ahead), read first:
@@ -943,274 +984,277 @@ __global__ __launch_bounds__(kThreads) void chunk_pipe_kernel(
         const float e = lds_ld<float>(Es, slot(c + 1 < NC ? c + 1 : c, 3, C * 4) + (C - 1) * 4);
         gn = c + 1 < NC ? e : 1.f;
       }
+      Frag<T16> ktf[HT][2];
       if constexpr (kDelta) {
-        const uint32_t vslot = slot(c, 4, C * 16 * 2);
-        const uint32_t gslot = slot(c, NG, C * 4);
         const uint32_t tslot = slot(c, 3, C * 4);
-        Frag<T16> kf[4][NKB], tf[kTFrags];
-        f32x4 vv[4], bb[4], bg[4];
+        const uint32_t bvslot = slot(c, 2, 4 * kWave * 16);
+        Frag<T16> kf[4][HB], th[kTFrags], tl[kTFrags];
+        f32x4 bv[4], bb[4], fr[4];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint32_t a = kslot + roff[kb];
+        for (int j = 0; j < HB; ++j) {
+          const uint32_t a = kslot + roff[h * HB + j];
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = frag_row_at<D>(Ks, a + kRows16 * ti);
+          for (int ti = 0; ti < 4; ++ti) kf[ti][j] = frag_row_at<D>(Ks, a + kRows16 * ti);
         }
-        {
-          const uint32_t a = vslot + voff;
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) vv[ti] = v_acc_at(Vs, a + 512 * ti);
-        }
-        {
-          const uint32_t a = gslot + goff;
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti) bb[ti] = lds_ld<f32x4>(Bs, a + 64 * ti);
-        }
+        for (int ti = 0; ti < 4; ++ti) bv[ti] = lds_ld<f32x4>(BVs, bvslot + xoff + ti * kWave * 16);
         if constexpr (kGated) {
-          const uint32_t a = tslot + goff;
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) bg[ti] = lds_ld<f32x4>(BGs, a + 64 * ti);
+          for (int ti = 0; ti < 4; ++ti) {
+            bb[ti] = lds_ld<f32x4>(BGs, tslot + goff + 64 * ti);
+            fr[ti] = lds_ld<f32x4>(Fs, tslot + goff + 64 * ti);
+          }
+        } else {
+          const uint32_t gslot = slot(c, NG, C * 4);
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) bb[ti] = lds_ld<f32x4>(Bs, gslot + goff + 64 * ti);
         }
         {
-          const uint32_t a = slot(c, 3, kTFrags * kWave * 16) + toff;
+          const uint32_t a = slot(c, 3, kTRecFrags * kWave * 16) + xoff;
 #pragma unroll
-          for (int f = 0; f < kTFrags; ++f) tf[f].v = lds_ld<bf16x8>(Ts, a + f * kWave * 16);
+          for (int f = 0; f < kTFrags; ++f) {
+            th[f].v = lds_ld<bf16x8>(Ts, a + f * kWave * 16);
+            tl[f].v = lds_ld<bf16x8>(Ts, a + (kTFrags + f) * kWave * 16);
+          }
         }
-        // Everything above is read before any product starts; the operands
-        // of the state update (K^T, and the gate ratios) are read while the
-        // K S products run, one read per MFMA, so that no LDS latency is
-        // exposed after the first.
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 ks[4], rr[4], un[4];
+        // this half's share of K S (the state enters as bf16: its rounding
+        // stays well inside the tolerance, the split being kept everywhere
+        // else)
+        f32x4 ks[4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) ks[ti] = zero4();
-        // row tile outer: each ks[ti] is final early, so R and its split for
-        // that tile can proceed under the remaining products
+        for (int ti = 0; ti < 4; ++ti) {
+          ks[ti] = zero4();
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+          for (int j = 0; j < HB; ++j) mma(kf[ti][j], sf[j].hi, ks[ti]);
+        }
+        // publish it, then flag it (the stores complete before the flag)
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) mma_ab2(kf[ti][kb], sf[kb], ks[ti]);
-        Frag<T16> ktf[NKT][2];
+        for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(XP, xown + xoff + ti * kWave * 16, ks[ti]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) *(volatile LA_LDS int*)&XF[h] = c + 1;
+        // the operands of the state update while the partner finishes
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int tj = 0; tj < NKT; ++tj)
-            ktf[tj][kb] = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
-        f32x4 fr[4];
-        if constexpr (kGated) {
-          const uint32_t a = tslot + goff;
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti) fr[ti] = lds_ld<f32x4>(Fs, a + 64 * ti);
+          for (int j = 0; j < HT; ++j)
+            ktf[j][kb] = frag_tr_at(Ks, kslot + ktr[j / 2] + 8 * (j % 2) + 64 * D * kb, kRows16);
+        // wait for the other half's share (bounded: see kSpinLimit)
+        for (int it = 0; it < kSpinLimit; ++it) {
+          if (__builtin_amdgcn_readfirstlane(*(volatile LA_LDS int*)&XF[1 - h]) > c) break;
+          __builtin_amdgcn_s_sleep(1);
         }
+        asm volatile("" ::: "memory");
+        // R = diag(beta) V - diag(beta gam) K S, the sum of the halves taken
+        // in the same order on both waves
+        f32x4 rr[4], un[4];
 #pragma unroll
-        for (int i = 0; i < 2 * NKB * 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        for (int ti = 0; ti < 4; ++ti) {
+          const f32x4 other = lds_ld<f32x4>(XP, xother + xoff + ti * kWave * 16);
+          const f32x4 sum = h == 0 ? ks[ti] + other : other + ks[ti];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rr[ti][i] = fmaf(-bb[ti][i], sum[i], bv[ti][i]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // R = diag(beta) V - diag(beta gam) K S
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (kGated) rr[ti][i] = fmaf(-bg[ti][i], ks[ti][i], bb[ti][i] * vv[ti][i]);
-            else rr[ti][i] = bb[ti][i] * (vv[ti][i] - ks[ti][i]);
-          }
         Frag2<T16> rf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) rf[kb] = frag2_from_acc<T16>(rr[2 * kb], rr[2 * kb + 1]);
+        // U_new = T R, both split
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           un[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            if (kb <= ti / 2) mma_ab2(tf[tfi(ti, kb)], rf[kb], un[ti]);
+            if (kb <= ti / 2) {
+              mma(tl[tfi(ti, kb)], rf[kb].hi, un[ti]);
+              mma(th[tfi(ti, kb)], rf[kb].lo, un[ti]);
+              mma(th[tfi(ti, kb)], rf[kb].hi, un[ti]);
+            }
         }
-        // U_new in float for the output waves
-        {
-          const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
+        // U_new split for the output waves (by the second half, which has
+        // no other publication of its own here)
+        if constexpr (OUT) {
+          if (h == 1) {
+            const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(Uf, a + ti * kWave * 16, un[ti]);
+            for (int kb = 0; kb < 2; ++kb) {
+              const Frag2<T16> u = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
+              lds_st<bf16x8>(Uf, a + (2 * kb) * kWave * 16, u.hi.v);
+              lds_st<bf16x8>(Uf, a + (2 * kb + 1) * kWave * 16, u.lo.v);
+            }
+          }
         }
         // operand of the state update: diag(gam_C / gam) U_new (gated), U_new
         Frag2<T16> ut[2];
-        if constexpr (kGated) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (kGated) {
             const f32x4 flo = fr[2 * kb], fhi = fr[2 * kb + 1];
             const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
             const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
             ut[kb] = frag2_from_acc_scaled<T16>(un[2 * kb], un[2 * kb + 1], slo, shi);
+          } else {
+            ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
           }
+        }
+        // S += K^T ut on this half (S is already decayed by gam_C)
+#pragma unroll
+        for (int j = 0; j < HT; ++j)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[j][kb], ut[kb], S[j]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < HT; ++j)
+            ktf[j][kb] = frag_tr_at(Ks, kslot + ktr[j / 2] + 8 * (j % 2) + 64 * D * kb, kRows16);
+        if constexpr (kGated) {
+          // S += K^T diag(gam_C / gam) V (S is already decayed by gam_C):
+          // f V in float from the DMA V wave, split here
+          const uint32_t bvslot = slot(c, 2, 4 * kWave * 16);
+          Frag2<T16> ut[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            ut[kb] = frag2_from_acc<T16>(lds_ld<f32x4>(BVs, bvslot + xoff + (2 * kb) * kWave * 16),
+                                         lds_ld<f32x4>(BVs, bvslot + xoff + (2 * kb + 1) * kWave * 16));
+#pragma unroll
+          for (int j = 0; j < HT; ++j)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[j][kb], ut[kb], S[j]);
         } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) ut[kb] = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
-        }
-        // S += K^T ut (S is already decayed by gam_C); state tile outer, so
-        // the split of each finished pair of tiles overlaps the products of
-        // the next
-#pragma unroll
-        for (int tj = 0; tj < NKT; ++tj)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[tj][kb], ut[kb], S[tj]);
-      } else if constexpr (kGated) {
-        // S += K^T diag(gam_C / gam) V (S is already decayed by gam_C): V in
-        // accumulator layout, scaled and split like U_new above
-        const uint32_t vslot = slot(c, 4, C * 16 * 2);
-        const uint32_t tslot = slot(c, 3, C * 4);
-        f32x4 vv[4], fr[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          vv[ti] = v_acc_at(Vs, vslot + voff + 512 * ti);
-          fr[ti] = lds_ld<f32x4>(Fs, tslot + goff + 64 * ti);
-        }
-        Frag2<T16> ut[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const f32x4 flo = fr[2 * kb], fhi = fr[2 * kb + 1];
-          const float slo[4] = {flo[0], flo[1], flo[2], flo[3]};
-          const float shi[4] = {fhi[0], fhi[1], fhi[2], fhi[3]};
-          ut[kb] = frag2_from_acc_scaled<T16>(vv[2 * kb], vv[2 * kb + 1], slo, shi);
-        }
-#pragma unroll
-        for (int tj = 0; tj < NKT; ++tj)
+          // S <- S + K^T V (V exact)
+          const uint32_t vslot = slot(c, NV, C * 16 * 2);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            const Frag<T16> kt = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
-            mma_ab2(kt, ut[kb], S[tj]);
-          }
-      } else {
-        // S <- S + K^T V
-        const uint32_t vslot = slot(c, 4, C * 16 * 2);
+            const Frag<T16> vf = frag_col_tr_v((const char*)Vs + vslot, 32 * kb, g, n);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const Frag<T16> vf = frag_col_tr_v((const char*)Vs + vslot, 32 * kb, g, n);
-#pragma unroll
-          for (int tj = 0; tj < NKT; ++tj) {
-            const Frag<T16> kt = frag_tr_at(Ks, kslot + ktr[tj / 2] + 8 * (tj % 2) + 64 * D * kb, kRows16);
-            mma(kt, vf, S[tj]);
+            for (int j = 0; j < HT; ++j) mma(ktf[j][kb], vf, S[j]);
           }
         }
       }
-      // publish the split of S_{c+1}; in gated mode the split consumes S and
-      // the state carried on is S_{c+1} decayed by gam_C of chunk c+1
+      // publish the split of this half of S_{c+1}; in gated mode the split
+      // consumes S and the state carried on is S_{c+1} decayed by gam_C of
+      // chunk c+1
       {
         const uint32_t a = slot(c + 1, 2, 2 * NKB * kWave * 16) + xoff;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int j = 0; j < HB; ++j) {
+          const int kb = h * HB + j;
           if constexpr (kGated) {
-            const f32x4 d0 = S[2 * kb] * gn, d1 = S[2 * kb + 1] * gn;
-            sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
-            S[2 * kb] = d0;
-            S[2 * kb + 1] = d1;
+            const f32x4 d0 = S[2 * j] * gn, d1 = S[2 * j + 1] * gn;
+            sf[j] = frag2_from_acc<T16>(S[2 * j], S[2 * j + 1]);
+            S[2 * j] = d0;
+            S[2 * j + 1] = d1;
           } else {
-            sf[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+            sf[j] = frag2_from_acc<T16>(S[2 * j], S[2 * j + 1]);
           }
-          lds_st<bf16x8>(Sx, a + (2 * kb) * kWave * 16, sf[kb].hi.v);
-          lds_st<bf16x8>(Sx, a + (2 * kb + 1) * kWave * 16, sf[kb].lo.v);
+          lds_st<bf16x8>(Sx, a + (2 * kb) * kWave * 16, sf[j].hi.v);
+          lds_st<bf16x8>(Sx, a + (2 * kb + 1) * kWave * 16, sf[j].lo.v);
         }
       }
       __syncthreads();
     }
     if (si.sf) {
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj)
+      for (int j = 0; j < HT; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          si.sf[(size_t)dk_of_row(16 * tj + 4 * g + i) * D + col] = S[tj][i];
+          si.sf[(size_t)dk_of_row(16 * (h * HT + j) + 4 * g + i) * D + col] = S[j][i];
     }
-  } else {
-    // ================= side waves
-    if (vzero && wave == 3) {
+  } else if (wave == kDmaK) {
+    // ================= DMA of K and the gates
+    issue_k(0);
+    if (NC > 1) issue_k(1);
+    for (int cc = 0; cc < NG - 1 && cc < NC; ++cc) issue_gates(cc);
+    vm_wait<0>();
+    __syncthreads();
+    __syncthreads();
+    for (int c = 0; c < NC; ++c) {
+      // the slots these fill held chunk c-1, last read before the barrier
+      // that opened this chunk
+      if (c + 2 < NC) issue_k(c + 2);
+      if (c + NG - 1 < NC) issue_gates(c + NG - 1);
+      // Everything issued before this chunk has landed.  Loads complete in
+      // issue order, so while any earlier transfer is outstanding all N of
+      // this chunk's are too.
+      if (c + NG - 1 < NC) vm_wait<NDMAK>();
+      else vm_wait<0>();
+      __syncthreads();
+    }
+  } else if (wave == kDmaV) {
+    // ================= DMA of V and T; tables; beta V
+    if (vzero) {
       // the V ring of a transition stream: zero once, never loaded
       u32x4* vr = reinterpret_cast<u32x4*>(&Vs[0][0]);
 #pragma unroll
-      for (int i = 0; i < 4 * C * 16 * 2 / 16 / kWave; ++i) vr[i * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < NV * C * 16 * 2 / 16 / kWave; ++i) vr[i * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
     }
-    issue_chunk(0);
-    if (NC > 1) issue_chunk(1);
-    if (wave == 3)
-      for (int cc = 0; cc < NG - 1 && cc < NC; ++cc) issue_gates(cc);
+    for (int cc = 0; cc < 3 && cc < NC; ++cc)
+      if (!vzero) issue_v(cc);
+    if constexpr (kDelta) {
+      issue_t(0);
+      if (NC > 1) issue_t(1);
+    }
     vm_wait<0>();
-    // V rows past the sequence set to zero once the last chunk's V has
-    // landed: here for a single chunk, else at the end of chunk NC - 2
-    auto zero_v_tail = [&]() {
-      if (nlast < C && lane >= nlast) {
-        u32x4* row = reinterpret_cast<u32x4*>(Vs[(NC - 1) % 4] + lane * 16);
-        row[0] = u32x4{0u, 0u, 0u, 0u};
-        row[1] = u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    if (wave == 3 && NC == 1) zero_v_tail();
+    if (NC <= 3) zero_v_tail();
+    __syncthreads();        // (the DMA K wave's gates have landed)
+    tables(0);
+    if (NC > 1) tables(1);
+    make_bv(0);
     __syncthreads();
-    if (wave == 2) {
-      tables(0);
-      if (NC > 1) tables(1);
-    }
-    __syncthreads();
-
-    f32x4 sc[2][4], qs[2];       // scores and Q S of the current chunk
-    f32x4 ot[2];                 // output rows of the previous chunk
     for (int c = 0; c < NC; ++c) {
-      const bool steady = c + NG - 1 < NC;      // every DMA of this step issued
-      // Loads for later chunks first: the slots they fill held chunk c-1
-      // (Q, K, T, gates) or c-2 (V), all last read before the barrier that
-      // opened this chunk, so the transfers get two chunks' time to land.
-      if (c + 2 < NC) issue_chunk(c + 2);
-      if (wave == 3 && c + NG - 1 < NC) issue_gates(c + NG - 1);
-      if (OUT && c > 0) {
-        const f32x4* U = Uf[kDelta ? (c - 1) % 2 : 0];
-        const T16* Vp = Vs[(c - 1) % 4];
-        const size_t ob0 = (hbase + (size_t)(c - 1) * C) * D + col;
-        if (wave == 1) {
-          out_rows<D, MODE, DSKIP, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-          store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, C);
-        } else if (wave == 2) {
-          out_rows<D, MODE, DSKIP, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-          store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, C);
-        } else {
-          out_rows<D, MODE, DSKIP, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-          store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, C);
-        }
-      }
-      if (wave == 2 && c + 2 < NC) tables(c + 2);
-      if constexpr (OUT) {
-        const T16* Kc = Ks[c % 3];
-        const float* gc = Gs[kGated ? c % 3 : 0];
-        const float* gk = kQSide ? Gk[c % 3] : gc;
-        const float* ec = kQSide ? Eq[c % 3] : Es[kGated ? c % 3 : 0];
-        const Frag<T16>* Sc = Sx[c % 2];
-        if (wave == 1) scores_qs<D, kGated, 2, 0, 1>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
-        else if (wave == 2) scores_qs<D, kGated, 1, 2, 2>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
-        else scores_qs<D, kGated, 1, 3, 3>(Qs[c % 3], Kc, gc, gk, ec, Sc, roff, sc, qs, g, n, lane);
-      }
-      // Everything issued before this chunk has landed.  Loads complete in
-      // issue order, so while any earlier transfer is outstanding all N of
-      // this chunk's are too: at most N outstanding (this chunk's output
-      // stores, issued later, included) means the earlier ones are done.
-      if (steady) {
-        if (wave == 3) vm_wait<NDMA3>();
-        else vm_wait<NTILE>();
-      } else {
-        vm_wait<0>();
-      }
-      if (wave == 3 && c == NC - 2) zero_v_tail();
+      if (c + 3 < NC && !vzero) issue_v(c + 3);
+      if constexpr (kDelta)
+        if (c + 2 < NC) issue_t(c + 2);
+      if (c + 2 < NC) tables(c + 2);
+      if (c + 1 < NC) make_bv(c + 1);
+      if (c + 3 < NC) vm_wait<NDMAV>();
+      else vm_wait<0>();
+      // the last chunk's V landed at the latest in the wait above at c = NC - 3
+      if (c == NC - 3) zero_v_tail();
       __syncthreads();
     }
+  } else {
+    // ================= output waves, one row tile each
     if constexpr (OUT) {
-      const int c = NC - 1;
-      const size_t ob0 = (hbase + (size_t)c * C) * D + col;
-      const f32x4* U = Uf[kDelta ? c % 2 : 0];
-      const T16* Vp = Vs[c % 4];
-      if (wave == 1) {
-        out_rows<D, MODE, DSKIP, 2, 0, 1>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-        store_rows<D, 2, 0, 1>(ot, out_, ob0, out_bf16, g, nlast);
-      } else if (wave == 2) {
-        out_rows<D, MODE, DSKIP, 1, 2, 2>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-        store_rows<D, 1, 2, 2>(ot, out_, ob0, out_bf16, g, nlast);
-      } else {
-        out_rows<D, MODE, DSKIP, 1, 3, 3>(sc, qs, U, Vp, ot, g, n, lane, dcol);
-        store_rows<D, 1, 3, 3>(ot, out_, ob0, out_bf16, g, nlast);
-      }
+      const f32x4 dcol4 = DSKIP ? *reinterpret_cast<const f32x4*>(dskip + (size_t)si.head * D + col0 + 4 * g)
+                                : zero4();
+      auto run = [&](auto ti_c) {
+        constexpr int TI = decltype(ti_c)::value;
+        Frag<T16> qc[NKB], qn[NKB];
+        load_q<D, TI>(qc, q, hbase, NC == 1 ? nlast : C, g, n);
+        __syncthreads();
+        __syncthreads();
+        f32x4 sc[4], qs, ot;
+        for (int c = 0; c < NC; ++c) {
+          {
+            // Q of the next chunk (the last chunk's again at the end: the
+            // load is unconditional)
+            const int cn = c + 1 < NC ? c + 1 : c;
+            load_q<D, TI>(qn, q, hbase + (size_t)cn * C, cn == NC - 1 ? nlast : C, g, n);
+          }
+          if (c > 0) {
+            out_rows<D, MODE, DSKIP, TI>(sc, qs, Uf[kDelta ? (c - 1) % 2 : 0], Vs[(c - 1) % NV], ot,
+                                         g, n, lane, dcol4);
+            store_rows<D, TI>(ot, out_, (hbase + (size_t)(c - 1) * C) * D + col0, out_bf16, g, n, C);
+          }
+          const T16* Kc = Ks[c % 3];
+          const float* gc = Gs[kGated ? c % 3 : 0];
+          const float* gk = kQSide ? Gk[c % 3] : gc;
+          const float* ec = kQSide ? Eq[c % 3] : Es[kGated ? c % 3 : 0];
+          scores_qs<D, kGated, TI>(qc, Kc, gc, gk, ec, Sx[c % 2], roff, sc, qs, g, n, lane);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) qc[kb] = qn[kb];
+          __syncthreads();
+        }
+        const int c = NC - 1;
+        out_rows<D, MODE, DSKIP, TI>(sc, qs, Uf[kDelta ? c % 2 : 0], Vs[c % NV], ot, g, n, lane,
+                                     dcol4);
+        store_rows<D, TI>(ot, out_, (hbase + (size_t)c * C) * D + col0, out_bf16, g, n, nlast);
+      };
+      if (wave == 2) run(std::integral_constant<int, 3>{});
+      else if (wave == 3) run(std::integral_constant<int, 2>{});
+      else if (wave == 6) run(std::integral_constant<int, 0>{});
+      else run(std::integral_constant<int, 1>{});
     }
   }
 }
@@ -1639,7 +1683,7 @@ constexpr int kMaxSegments = 64;
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t tsolve_bytes(const ChunkArgs& a) {
-  return mode_erase(a.mode) ? chunk_slots(a) * kTFrags * kWave * sizeof(u32x4) : 0;
+  return mode_erase(a.mode) ? chunk_slots(a) * kTRecFrags * kWave * sizeof(u32x4) : 0;
 }
 
 size_t seg_states_offset(const ChunkArgs& a) { return align256(tsolve_bytes(a)); }
@@ -1684,7 +1728,7 @@ template <int D, int MODE, bool OUT, bool FUSED, bool DSKIP>
 hipError_t launch_one(const ChunkArgs& a, int pass, hipStream_t st) {
   const StreamMap m = stream_map(a, pass);
   const size_t ns = (size_t)a.B * a.H * m.per_seq();
-  const dim3 grid((unsigned)(ns * (D / 16))), block(kThreads);
+  const dim3 grid((unsigned)(ns * (D / 16))), block(OUT ? 512 : 256);
   const ProArrays pro = FUSED ? pro_arrays(a) : ProArrays{};
   chunk_pipe_kernel<D, MODE, OUT, FUSED, DSKIP><<<grid, block, 0, st>>>(
       static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
