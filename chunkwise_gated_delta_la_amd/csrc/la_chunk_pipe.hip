@@ -627,13 +627,13 @@ __device__ __forceinline__ void scores_qs(const Frag<T16> (&qf)[D / 32], const T
 }
 
 // Output of row tile TI, transposed: O^T = qs + U_new^T Aqk^T (U_new = V in
-// the modes without erase).  U_new arrives split (Uf: hi and lo fragments of
-// 32-deep block kb at (2 kb) * 64 + lane and (2 kb + 1) * 64 + lane).
+// the modes without erase).  U_new arrives in float (Uf, accumulator tile ti
+// at ti * 64 + lane) and is split here.
 // DSKIP: plus the residual D * V at the lane's token and four columns
 // (dcol4, and four adjacent values of the value tile's row).
 template <int D, int MODE, bool DSKIP, int TI>
 __device__ __forceinline__ void out_rows(const f32x4 (&sc)[4], const f32x4& qs,
-                                         const Frag<T16>* Uf, const T16* Vt, f32x4& o, int g,
+                                         const f32x4* Uf, const T16* Vt, f32x4& o, int g,
                                          int n, int lane, const f32x4& dcol4) {
   constexpr bool kDelta = mode_erase(MODE);
   o = qs;
@@ -641,9 +641,8 @@ __device__ __forceinline__ void out_rows(const f32x4 (&sc)[4], const f32x4& qs,
   for (int kb = 0; kb <= TI / 2; ++kb) {
     const Frag2<T16> a = frag2_from_acc<T16>(sc[2 * kb], sc[2 * kb + 1]);
     if constexpr (kDelta) {
-      Frag2<T16> u;
-      u.hi = Uf[(2 * kb) * kWave + lane];
-      u.lo = Uf[(2 * kb + 1) * kWave + lane];
+      const Frag2<T16> u =
+          frag2_from_acc<T16>(Uf[(2 * kb) * kWave + lane], Uf[(2 * kb + 1) * kWave + lane]);
       mma_a2b2(u, a, o);
     } else {
       const Frag<T16> u = frag_col_tr_v(Vt, 32 * kb, g, n);
@@ -698,10 +697,11 @@ constexpr int kSpinLimit = 1 << 14;
 //                (T split) and updates its half, S <- gam_C S + K^T
 //                diag(gam_C / gam) U_new, publishing its split for the
 //                output waves.  Without erase: S <- gam_C S + K^T diag(f) V.
-//   DMA K        K of chunk c+2 and the gates of chunk c+4 into LDS rings
+//   DMA K        K of chunk c+2 and the gates of chunk c+4 into LDS rings;
+//                beta V (or f V) of chunk c+1 in the chain's accumulator
+//                layout
 //   DMA V        V of chunk c+3 and the T record of chunk c+2; the decay
-//                tables of chunk c+2; beta V (or f V) of chunk c+1 in the
-//                chain's accumulator layout; the zero rows of a partial V
+//                tables of chunk c+2; the zero rows of a partial V
 //   output (4)   one row tile each: the output of chunk c-1 from the U_new
 //                published at the last barrier (formed transposed: one
 //                store per lane of four adjacent columns), then the masked
@@ -766,7 +766,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   __shared__ __attribute__((aligned(16))) float Gk[kQSide ? 3 : 1][C];    // g - lk (score columns)
   __shared__ __attribute__((aligned(16))) float Eq[kQSide ? 3 : 1][C];    // exp(g + lq) (Q S rows)
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
-  __shared__ __attribute__((aligned(16))) Frag<T16> Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
+  __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
   __shared__ __attribute__((aligned(16))) f32x4 BVs[kBV ? 2 : 1][kBV ? 4 * kWave : 1];
   __shared__ __attribute__((aligned(16))) f32x4 XP[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
   __shared__ int XF[2];
@@ -990,12 +990,32 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         const uint32_t bvslot = slot(c, 2, 4 * kWave * 16);
         Frag<T16> kf[4][HB], th[kTFrags], tl[kTFrags];
         f32x4 bv[4], bb[4], fr[4];
+        // first only what the exchange waits for: the LDS counter retires in
+        // order, so any read issued before the partial's stores would delay
+        // the flag
 #pragma unroll
         for (int j = 0; j < HB; ++j) {
           const uint32_t a = kslot + roff[h * HB + j];
 #pragma unroll
           for (int ti = 0; ti < 4; ++ti) kf[ti][j] = frag_row_at<D>(Ks, a + kRows16 * ti);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // this half's share of K S (the state enters as bf16: its rounding
+        // stays well inside the tolerance, the split being kept everywhere
+        // else)
+        f32x4 ks[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          ks[ti] = zero4();
+#pragma unroll
+          for (int j = 0; j < HB; ++j) mma(kf[ti][j], sf[j].hi, ks[ti]);
+        }
+        // publish it, then flag it (the stores complete before the flag)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(XP, xown + xoff + ti * kWave * 16, ks[ti]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) *(volatile LA_LDS int*)&XF[h] = c + 1;
+        // the other operands while the partner finishes
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) bv[ti] = lds_ld<f32x4>(BVs, bvslot + xoff + ti * kWave * 16);
         if constexpr (kGated) {
@@ -1017,23 +1037,6 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
             tl[f].v = lds_ld<bf16x8>(Ts, a + (kTFrags + f) * kWave * 16);
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // this half's share of K S (the state enters as bf16: its rounding
-        // stays well inside the tolerance, the split being kept everywhere
-        // else)
-        f32x4 ks[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          ks[ti] = zero4();
-#pragma unroll
-          for (int j = 0; j < HB; ++j) mma(kf[ti][j], sf[j].hi, ks[ti]);
-        }
-        // publish it, then flag it (the stores complete before the flag)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(XP, xown + xoff + ti * kWave * 16, ks[ti]);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (lane == 0) *(volatile LA_LDS int*)&XF[h] = c + 1;
-        // the operands of the state update while the partner finishes
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1070,17 +1073,12 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
               mma(th[tfi(ti, kb)], rf[kb].hi, un[ti]);
             }
         }
-        // U_new split for the output waves (by the second half, which has
-        // no other publication of its own here)
+        // U_new in float for the output waves (which split it)
         if constexpr (OUT) {
-          if (h == 1) {
+          if (h == 0) {
             const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const Frag2<T16> u = frag2_from_acc<T16>(un[2 * kb], un[2 * kb + 1]);
-              lds_st<bf16x8>(Uf, a + (2 * kb) * kWave * 16, u.hi.v);
-              lds_st<bf16x8>(Uf, a + (2 * kb + 1) * kWave * 16, u.lo.v);
-            }
+            for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(Uf, a + ti * kWave * 16, un[ti]);
           }
         }
         // operand of the state update: diag(gam_C / gam) U_new (gated), U_new
@@ -1173,6 +1171,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       // that opened this chunk
       if (c + 2 < NC) issue_k(c + 2);
       if (c + NG - 1 < NC) issue_gates(c + NG - 1);
+      if (c + 1 < NC) make_bv(c + 1);
       // Everything issued before this chunk has landed.  Loads complete in
       // issue order, so while any earlier transfer is outstanding all N of
       // this chunk's are too.
@@ -1206,7 +1205,6 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       if constexpr (kDelta)
         if (c + 2 < NC) issue_t(c + 2);
       if (c + 2 < NC) tables(c + 2);
-      if (c + 1 < NC) make_bv(c + 1);
       if (c + 3 < NC) vm_wait<NDMAV>();
       else vm_wait<0>();
       // the last chunk's V landed at the latest in the wait above at c = NC - 3
