@@ -575,10 +575,15 @@ __device__ __forceinline__ void load_q(Frag<T16> (&qf)[D / 32], const T16* q, si
 // the lane's byte offset of operand row n over dk block kb in a K tile.  The
 // decay of score (r, i) is exp(gsc[r] - gkc[i]) and Q S row r is scaled by
 // esc[r]: the exponents g and the factors exp(g), or with normalised q and k
-// the same with the logs of the inverse norms folded in.
+// the same with the logs of the inverse norms folded in.  Below the diagonal
+// tile (column tile t < TI) the decay is the product of a row factor ra[r] =
+// exp(gsc[r] - g[16 TI]) and a column factor cb[i] = exp(g[16 TI] - gkc[i])
+// (g does not increase along the chunk, so neither factor exceeds the
+// inverse norm it carries): two products instead of an exponential.
 template <int D, bool GATED, int TI>
 __device__ __forceinline__ void scores_qs(const Frag<T16> (&qf)[D / 32], const T16* Kt,
                                           const float* gsc, const float* gkc, const float* esc,
+                                          const float* ra, const float* cb,
                                           const Frag<T16>* Sx, const uint32_t (&roff)[D / 32],
                                           f32x4 (&sc)[4], f32x4& qs, int g, int n, int lane) {
   constexpr int NKB = D / 32;
@@ -594,13 +599,18 @@ __device__ __forceinline__ void scores_qs(const Frag<T16> (&qf)[D / 32], const T
     sx[kb].hi = Sx[(2 * kb) * kWave + lane];
     sx[kb].lo = Sx[(2 * kb + 1) * kWave + lane];
   }
-  float gq = 0.f, eq = 1.f;
-  f32x4 gk[TI + 1];
+  float gq = 0.f, eq = 1.f, rq = 1.f;
+  f32x4 gk = zero4(), cf[TI + 1];
   if constexpr (GATED) {
     gq = gsc[16 * TI + n];
     eq = esc[16 * TI + n];
+    gk = *reinterpret_cast<const f32x4*>(gkc + 16 * TI + 4 * g);
+    if constexpr (TI > 0) {
+      rq = ra[16 * TI + n];
 #pragma unroll
-    for (int t = 0; t <= TI; ++t) gk[t] = *reinterpret_cast<const f32x4*>(gkc + 16 * t + 4 * g);
+      for (int t = 0; t < TI; ++t)
+        cf[t] = *reinterpret_cast<const f32x4*>(cb + (TI - 1) * C + 16 * t + 4 * g);
+    }
   }
   qs = zero4();
 #pragma unroll
@@ -615,12 +625,16 @@ __device__ __forceinline__ void scores_qs(const Frag<T16> (&qf)[D / 32], const T
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) mma(kf[t][kb], qf[kb], sc[t]);
     // element (K row 16 t + 4 g + e, Q row 16 TI + n) = Aqk[r][i]
+    if (t < TI) {
+      if constexpr (GATED) sc[t] = (sc[t] * rq) * cf[t];
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool keep = t < TI || 4 * g + e <= n;
-      float decay = 1.f;
-      if constexpr (GATED) decay = __expf(keep ? gq - gk[t][e] : 0.f);
-      sc[t][e] = keep ? sc[t][e] * decay : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = 4 * g + e <= n;
+        float decay = 1.f;
+        if constexpr (GATED) decay = __expf(keep ? gq - gk[e] : 0.f);
+        sc[t][e] = keep ? sc[t][e] * decay : 0.f;
+      }
     }
   }
   if constexpr (GATED) qs *= eq;
@@ -765,6 +779,9 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   __shared__ __attribute__((aligned(16))) float LKs[FUSED ? NG : 1][C];   // log(1 / |k|)
   __shared__ __attribute__((aligned(16))) float Gk[kQSide ? 3 : 1][C];    // g - lk (score columns)
   __shared__ __attribute__((aligned(16))) float Eq[kQSide ? 3 : 1][C];    // exp(g + lq) (Q S rows)
+  constexpr bool kFac = kGated && OUT;           // factored score decays below the diagonal
+  __shared__ __attribute__((aligned(16))) float Ra[kFac ? 3 : 1][C];      // exp(gsc[r] - g[16 (r / 16)])
+  __shared__ __attribute__((aligned(16))) float Cb[kFac ? 3 : 1][kFac ? 3 * C : 1];  // exp(g[16 t] - gkc[i]), t = 1..3
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
   __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
   __shared__ __attribute__((aligned(16))) f32x4 BVs[kBV ? 2 : 1][kBV ? 4 * kWave : 1];
@@ -876,6 +893,23 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       if constexpr (kDelta) Bs[cc % NG][lane] = 0.f;
       if constexpr (kGated) Ls[cc % NG][lane] = 0.f;
     }
+    // the score decay's factors below the diagonal tile: row factor against
+    // g at the start of the row's tile, column factors against g at the start
+    // of each later tile (the unused ones, i >= 16 t, clamped: never read)
+    auto factors = [&](float gv, float gsc, float gkc) {
+      if constexpr (kFac) {
+        const float g16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 16));
+        const float g32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 32));
+        const float g48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 48));
+        const float g00 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 0));
+        const int tr = lane / 16;
+        const float gt = tr == 0 ? g00 : tr == 1 ? g16 : tr == 2 ? g32 : g48;
+        Ra[cc % 3][lane] = __expf(gsc - gt);
+        Cb[cc % 3][0 * C + lane] = __expf(fminf(g16 - gkc, 80.f));
+        Cb[cc % 3][1 * C + lane] = __expf(fminf(g32 - gkc, 80.f));
+        Cb[cc % 3][2 * C + lane] = __expf(fminf(g48 - gkc, 80.f));
+      }
+    };
     if constexpr (FUSED) {
       const float gv = cumsum64(Ls[cc % NG], lane);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
@@ -885,6 +919,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         Gs[cc % 3][lane] = gv + lq;
         Gk[cc % 3][lane] = gv - lk;
         Eq[cc % 3][lane] = __expf(gv + lq);
+        factors(gv, gv + lq, gv - lk);
       }
       Es[cc % 3][lane] = __expf(gv);
       Fs[cc % 3][lane] = __expf(gC - gv + lk);
@@ -897,6 +932,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       Es[cc % 3][lane] = e;
       Fs[cc % 3][lane] = __expf(gC - gv);
       if constexpr (kDelta) BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
+      factors(gv, gv, gv);
     }
   };
   // beta V (erase) or f V (gated linear) of chunk cc in the chain's
@@ -1239,7 +1275,8 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
           const float* gc = Gs[kGated ? c % 3 : 0];
           const float* gk = kQSide ? Gk[c % 3] : gc;
           const float* ec = kQSide ? Eq[c % 3] : Es[kGated ? c % 3 : 0];
-          scores_qs<D, kGated, TI>(qc, Kc, gc, gk, ec, Sx[c % 2], roff, sc, qs, g, n, lane);
+          scores_qs<D, kGated, TI>(qc, Kc, gc, gk, ec, Ra[kFac ? c % 3 : 0], Cb[kFac ? c % 3 : 0],
+                                   Sx[c % 2], roff, sc, qs, g, n, lane);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) qc[kb] = qn[kb];
           __syncthreads();
