@@ -692,11 +692,6 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
   return wave_inclusive_scan(p[lane]);
 }
 
-// Bound on the chain halves' wait for each other, in s_sleep periods of 64
-// clocks (about 0.5 ms): the partner arrives within one chunk step (a few
-// thousand clocks), so the bound only keeps a logic error from hanging the
-// GPU.
-constexpr int kSpinLimit = 1 << 14;
 
 // ---------------------------------------------------------------- chain kernel
 
@@ -705,12 +700,13 @@ constexpr int kSpinLimit = 1 << 14;
 // that walk the chunks in parallel.  Waves and their roles:
 //
 //   waves 0, 1   the serial chain, each on half of the state's rows (dk):
-//                partial K S over its half, the two halves exchanged through
-//                LDS (a flag per half, no barrier), then each computes the
-//                whole R = diag(beta)(V - diag(gam) K S) and U_new = T R
-//                (T split) and updates its half, S <- gam_C S + K^T
-//                diag(gam_C / gam) U_new, publishing its split for the
-//                output waves.  Without erase: S <- gam_C S + K^T diag(f) V.
+//                the whole K S (the other half's bf16 state read from the
+//                split both publish for the output waves), R = diag(beta)(V -
+//                diag(gam) K S) and U_new = T R (T split), then the update of
+//                its half, S <- gam_C S + K^T diag(gam_C / gam) U_new, and
+//                its half's split published.  The two never wait for each
+//                other inside a chunk.  Without erase: S <- gam_C S + K^T
+//                diag(f) V.
 //   DMA K        K of chunk c+2 and the gates of chunk c+4 into LDS rings;
 //                beta V (or f V) of chunk c+1 in the chain's accumulator
 //                layout
@@ -785,8 +781,6 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
   __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
   __shared__ __attribute__((aligned(16))) f32x4 BVs[kBV ? 2 : 1][kBV ? 4 * kWave : 1];
-  __shared__ __attribute__((aligned(16))) f32x4 XP[kDelta ? 2 : 1][kDelta ? 4 * kWave : 1];
-  __shared__ int XF[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -990,7 +984,6 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       Sx[0][(2 * kb) * kWave + lane] = sf[j].hi;
       Sx[0][(2 * kb + 1) * kWave + lane] = sf[j].lo;
     }
-    if (lane == 0) XF[h] = 0;
     __syncthreads();
     __syncthreads();
     // S is carried decayed by the coming chunk's gam_C: the accumulator of
@@ -1006,8 +999,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
 #pragma unroll
     for (int j = 0; j < HT / 2; ++j) ktr[j] = tr_off<D>(g, n, h * (HT / 2) + j);
     const uint32_t goff = (uint32_t)(4 * g) * 4;        // tables: row 16 ti + 4 g
-    const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf / BVs / XP slots
-    const uint32_t xown = (uint32_t)h * 4 * kWave * 16, xother = (uint32_t)(1 - h) * 4 * kWave * 16;
+    const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf / BVs slots
 
     for (int c = 0; c < NC; ++c) {
       const uint32_t kslot = slot(c, 3, kTileB);
@@ -1024,34 +1016,38 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       if constexpr (kDelta) {
         const uint32_t tslot = slot(c, 3, C * 4);
         const uint32_t bvslot = slot(c, 2, 4 * kWave * 16);
-        Frag<T16> kf[4][HB], th[kTFrags], tl[kTFrags];
+        Frag<T16> kf[4][NKB], th[kTFrags], tl[kTFrags], sh[NKB];
         f32x4 bv[4], bb[4], fr[4];
-        // first only what the exchange waits for: the LDS counter retires in
-        // order, so any read issued before the partial's stores would delay
-        // the flag
+        // K S over the whole state: this half's bf16 S from registers, the
+        // other half's from the split both halves published at the end of
+        // the last chunk (the state enters K S as one bf16: its rounding
+        // stays well inside the tolerance, the split being kept everywhere
+        // else).  Both halves form the same products in the same order, so
+        // they hold the same K S and need no exchange.
+        {
+          const uint32_t a = slot(c, 2, 2 * NKB * kWave * 16) + xoff;
 #pragma unroll
-        for (int j = 0; j < HB; ++j) {
-          const uint32_t a = kslot + roff[h * HB + j];
+          for (int kb = 0; kb < NKB; ++kb) {
+            // (register arrays only ever indexed by compile-time values)
+            if (kb / HB == h) sh[kb] = sf[kb % HB].hi;
+            else sh[kb].v = lds_ld<bf16x8>(Sx, a + (2 * kb) * kWave * 16);
+          }
+        }
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) kf[ti][j] = frag_row_at<D>(Ks, a + kRows16 * ti);
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t a = kslot + roff[kb];
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = frag_row_at<D>(Ks, a + kRows16 * ti);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // this half's share of K S (the state enters as bf16: its rounding
-        // stays well inside the tolerance, the split being kept everywhere
-        // else)
         f32x4 ks[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           ks[ti] = zero4();
 #pragma unroll
-          for (int j = 0; j < HB; ++j) mma(kf[ti][j], sf[j].hi, ks[ti]);
+          for (int kb = 0; kb < NKB; ++kb) mma(kf[ti][kb], sh[kb], ks[ti]);
         }
-        // publish it, then flag it (the stores complete before the flag)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(XP, xown + xoff + ti * kWave * 16, ks[ti]);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (lane == 0) *(volatile LA_LDS int*)&XF[h] = c + 1;
-        // the other operands while the partner finishes
+        // the other operands under the products
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) bv[ti] = lds_ld<f32x4>(BVs, bvslot + xoff + ti * kWave * 16);
         if constexpr (kGated) {
@@ -1078,22 +1074,12 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
 #pragma unroll
           for (int j = 0; j < HT; ++j)
             ktf[j][kb] = frag_tr_at(Ks, kslot + ktr[j / 2] + 8 * (j % 2) + 64 * D * kb, kRows16);
-        // wait for the other half's share (bounded: see kSpinLimit)
-        for (int it = 0; it < kSpinLimit; ++it) {
-          if (__builtin_amdgcn_readfirstlane(*(volatile LA_LDS int*)&XF[1 - h]) > c) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        asm volatile("" ::: "memory");
-        // R = diag(beta) V - diag(beta gam) K S, the sum of the halves taken
-        // in the same order on both waves
+        // R = diag(beta) V - diag(beta gam) K S
         f32x4 rr[4], un[4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const f32x4 other = lds_ld<f32x4>(XP, xother + xoff + ti * kWave * 16);
-          const f32x4 sum = h == 0 ? ks[ti] + other : other + ks[ti];
+        for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rr[ti][i] = fmaf(-bb[ti][i], sum[i], bv[ti][i]);
-        }
+          for (int i = 0; i < 4; ++i) rr[ti][i] = fmaf(-bb[ti][i], ks[ti][i], bv[ti][i]);
         Frag2<T16> rf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) rf[kb] = frag2_from_acc<T16>(rr[2 * kb], rr[2 * kb + 1]);
