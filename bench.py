@@ -50,7 +50,7 @@ KERNEL_SYMBOLS = {"chunk_kernel": "la_chunk", "chunk_pipe_kernel": "la_chunk",
                   "bwd_prep_kernel": "la_bwd_prep", "bwd_states_kernel": "la_bwd_states",
                   "bwd_rev_kernel": "la_bwd_rev",
                   "bwd_grads_kernel": "la_bwd_grads"}
-T_BYTES_PER_CHUNK = 12 * 1024  # T operand fragments (hi and lo) of one (b, h, chunk)
+T_BYTES_PER_CHUNK = 6 * 1024   # T operand fragments of one (b, h, chunk)
 
 
 def log(msg):
@@ -64,7 +64,7 @@ def log(msg):
 #   la_chunk (the chain kernel) moves q, k, v in and o out (4 d e), plus
 #            beta (delta modes) and log_alpha (gated) at 4 B each, plus,
 #            for bf16 inputs in the delta modes, the chunk's T factor
-#            (12 KiB per chunk: 192 B per token); per (b, h): S0 in (when
+#            (6 KiB per chunk: 96 B per token); per (b, h): S0 in (when
 #            given) and S_final out at dk dv 4 B
 #   la_tsolve (bf16 delta modes) reads k and the gates and writes T
 # Per (b, h) state of one decode step: S in and out (2 dk dv 4 B), q, k, v,

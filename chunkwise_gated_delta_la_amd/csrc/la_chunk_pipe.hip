@@ -6,8 +6,7 @@
 //    A = strict_lower(diag(beta) K K^T * Gamma) and T = (I + A)^-1.  T does
 //    not depend on the state, so all chunks are solved at once, at full
 //    occupancy, and written to a workspace as the exact MFMA operand
-//    fragments the second kernel feeds to U_new = T R, split into bf16 hi
-//    and lo parts (12 KiB per chunk).
+//    fragments the second kernel feeds to U_new = T R (6 KiB per chunk).
 //
 // 2. chunk_pipe_kernel, one 256-thread workgroup per 16-column tile of one
 //    (batch, head) state, walking the chunks in order.  Per chunk c, with a
@@ -253,15 +252,15 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows,
 // ---------------------------------------------------------------- T solve
 
 // Fragment index of the T operand (row tile ti, 32-deep block kb), kb <= ti / 2.
-// A record holds the kTFrags fragments of bf16(T) (hi) and then those of
-// bf16(T - hi) (lo): T enters U_new = T R as a split operand.
+// A record holds the kTFrags fragments of bf16(T): T enters U_new = T R as a
+// single bf16 (its rounding costs well under the tolerance; R is split).
 __device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
 constexpr int kTFrags = 6;
-constexpr int kTRecFrags = 2 * kTFrags;   // 16-byte lane slots per record, per lane
+constexpr int kTRecFrags = kTFrags;       // 16-byte lane slots per record, per lane
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
-__device__ __forceinline__ void t_diag(const float* Ab, float* Df, float* Tf, int g, int n) {
+__device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int g, int n) {
   const float* A = Ab + bid(g, g) * 16 * LDB;
   f32x4 arow[16][4];
 #pragma unroll
@@ -284,7 +283,7 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, float* Tf, in
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     Df[g * 16 * LDB + r * LDB + n] = x[r];
-    Tf[(16 * g + r) * LDT + 16 * g + n] = x[r];
+    Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)x[r];
   }
 }
 
@@ -293,7 +292,7 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, float* Tf, in
 //   [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
 // (block inverse of a 2 x 2 block lower-triangular matrix, applied twice),
 // four dependent product steps.  Products split both operands.
-__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, float* Tf,
+__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, T16* Tb,
                                       int g, int n) {
   auto blkA = [&](int i, int j) { return Ab + bid(i, j) * 16 * LDB; };
   auto blkD = [&](int i) { return Df + i * 16 * LDB; };
@@ -339,12 +338,12 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 4 * g + e;
-    Tf[(16 + r) * LDT + n] = t10[e];
-    Tf[(48 + r) * LDT + 32 + n] = t32[e];
-    Tf[(32 + r) * LDT + n] = -y00[e];
-    Tf[(32 + r) * LDT + 16 + n] = -y01[e];
-    Tf[(48 + r) * LDT + n] = -y10[e];
-    Tf[(48 + r) * LDT + 16 + n] = -y11[e];
+    Tb[(16 + r) * LDT + n] = (T16)t10[e];
+    Tb[(48 + r) * LDT + 32 + n] = (T16)t32[e];
+    Tb[(32 + r) * LDT + n] = (T16)(-y00[e]);
+    Tb[(32 + r) * LDT + 16 + n] = (T16)(-y01[e]);
+    Tb[(48 + r) * LDT + n] = (T16)(-y10[e]);
+    Tb[(48 + r) * LDT + 16 + n] = (T16)(-y11[e]);
   }
 }
 
@@ -414,7 +413,7 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
   __shared__ __attribute__((aligned(16))) float Ab[TS ? 10 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float Df[TS ? 4 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float T32f[TS ? 16 * LDB : 1];
-  __shared__ __attribute__((aligned(16))) float Tf[TS ? C * LDT : 1];
+  __shared__ __attribute__((aligned(16))) T16 Tb[TS ? C * LDT : 1];
   __shared__ __attribute__((aligned(16))) float gsh[C];               // row exponents
   __shared__ __attribute__((aligned(16))) float gcsh[PRO ? C : 1];    // column exponents
   __shared__ __attribute__((aligned(16))) float bsh[C];
@@ -505,8 +504,8 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
     // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      Tf[(4 * g + e) * LDT + 16 + n] = 0.f;
-      Tf[(32 + 4 * g + e) * LDT + 48 + n] = 0.f;
+      Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
+      Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
     }
     __syncthreads();
 
@@ -533,18 +532,17 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
       }
     }
     __syncthreads();
-    t_diag(Ab, Df, Tf, g, n);
+    t_diag(Ab, Df, Tb, g, n);
     __syncthreads();
-    t_col(Ab, Df, T32f, Tf, g, n);
+    t_col(Ab, Df, T32f, Tb, g, n);
     __syncthreads();
     u32x4* dst = tws + item * (kTRecFrags * kWave);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int kb = 0; kb <= ti / 2; ++kb) {
-        const Frag2<T16> f = frag2_row<T16>(Tf + (16 * ti + n) * LDT + 32 * kb, g);
-        dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.hi.v);
-        dst[(kTFrags + tfi(ti, kb)) * kWave + lane] = __builtin_bit_cast(u32x4, f.lo.v);
+        const Frag<T16> f = frag_row(Tb + (16 * ti + n) * LDT + 32 * kb, g);
+        dst[tfi(ti, kb) * kWave + lane] = __builtin_bit_cast(u32x4, f.v);
       }
   }
 }
@@ -702,7 +700,7 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 //   waves 0, 1   the serial chain, each on half of the state's rows (dk):
 //                the whole K S (the other half's bf16 state read from the
 //                split both publish for the output waves), R = diag(beta)(V -
-//                diag(gam) K S) and U_new = T R (T split), then the update of
+//                diag(gam) K S) and U_new = T R, then the update of
 //                its half, S <- gam_C S + K^T diag(gam_C / gam) U_new, and
 //                its half's split published.  The two never wait for each
 //                other inside a chunk.  Without erase: S <- gam_C S + K^T
@@ -754,20 +752,26 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   constexpr uint32_t kRows16 = 32 * D;           // bytes of 16 tile rows
   constexpr int NTILE = TILE * 2 / 1024;         // DMA instructions per tile
   constexpr int NG = 5;                          // gate rings (DMA 4 ahead)
-  constexpr int NV = 5;                          // value ring (DMA 3 ahead)
+  // The state pass keeps its LDS within 80 KiB, so that two of its
+  // workgroups share a compute unit: K one chunk ahead (two slots), V three
+  // ahead (four slots), and only the high part of the published state split
+  // (no output waves read the low part).
+  constexpr int KR = OUT ? 3 : 2;                // K ring (DMA KR - 1 ahead)
+  constexpr int NV = OUT ? 5 : 4;                // value ring (DMA 3 ahead)
+  constexpr int SXP = OUT ? 2 : 1;               // parts of the state split in Sx
   constexpr int kDmaK = OUT ? 4 : 2, kDmaV = OUT ? 5 : 3;
   constexpr bool kQSide = FUSED && OUT;          // (the state pass has no Q side: only lk)
-  constexpr int NDMAK = NTILE + (kDelta ? 1 : 0) + (kGated ? 1 : 0) + (FUSED ? 1 : 0) +
-                        (kQSide ? 1 : 0);        // per chunk of the DMA K wave
+  constexpr int NGATE = (kDelta ? 1 : 0) + (kGated ? 1 : 0) + (FUSED ? 1 : 0) + (kQSide ? 1 : 0);
+  constexpr int NDMAK = NTILE + NGATE;           // per chunk of the DMA K wave
   constexpr int NDMAV = 2 + (kDelta ? kTRecFrags : 0);   // per chunk of the DMA V wave
   constexpr bool kBV = kDelta || MODE == kModeGatedLinear;  // beta V or f V for the chain
 
-  __shared__ __attribute__((aligned(16))) T16 Ks[3][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Ks[KR][TILE];
   __shared__ __attribute__((aligned(16))) T16 Vs[NV][C * 16];
   __shared__ __attribute__((aligned(16))) u32x4 Ts[kDelta ? 3 : 1][kDelta ? kTRecFrags * kWave : 1];
   __shared__ __attribute__((aligned(16))) float Ls[kGated ? NG : 1][C];  // log alpha
   __shared__ __attribute__((aligned(16))) float Bs[kDelta ? NG : 1][C];  // beta
-  __shared__ __attribute__((aligned(16))) float Gs[kGated ? 3 : 1][C];   // g (in-chunk cumsum)
+  __shared__ __attribute__((aligned(16))) float Gs[kGated && OUT ? 3 : 1][C];   // g (in-chunk cumsum)
   __shared__ __attribute__((aligned(16))) float Es[kGated ? 3 : 1][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float Fs[kGated ? 3 : 1][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float BGs[kGated ? 3 : 1][C];  // beta exp(g)
@@ -778,9 +782,21 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   constexpr bool kFac = kGated && OUT;           // factored score decays below the diagonal
   __shared__ __attribute__((aligned(16))) float Ra[kFac ? 3 : 1][C];      // exp(gsc[r] - g[16 (r / 16)])
   __shared__ __attribute__((aligned(16))) float Cb[kFac ? 3 : 1][kFac ? 3 * C : 1];  // exp(g[16 t] - gkc[i]), t = 1..3
-  __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][2 * NKB * kWave];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Sx[2][SXP * NKB * kWave];
   __shared__ __attribute__((aligned(16))) f32x4 Uf[kDelta && OUT ? 2 : 1][kDelta && OUT ? 4 * kWave : 1];
   __shared__ __attribute__((aligned(16))) f32x4 BVs[kBV ? 2 : 1][kBV ? 4 * kWave : 1];
+  // Q: where the rest already holds more than half of the compute unit's
+  // LDS (one workgroup per unit either way) or Q still fits under that
+  // half, the DMA V wave stages Q in a ring of two tiles, one chunk ahead,
+  // and the output waves read their rows from it; otherwise each output wave
+  // loads its rows from HBM straight into registers, one chunk ahead.
+  constexpr size_t kLdsRest =
+      sizeof(Ks) + sizeof(Vs) + sizeof(Ts) + sizeof(Ls) + sizeof(Bs) + sizeof(Gs) + sizeof(Es) +
+      sizeof(Fs) + sizeof(BGs) + sizeof(LQs) + sizeof(LKs) + sizeof(Gk) + sizeof(Eq) + sizeof(Ra) +
+      sizeof(Cb) + sizeof(Sx) + sizeof(Uf) + sizeof(BVs);
+  constexpr size_t kHalfLds = 80 * 1024;
+  constexpr bool kQLds = OUT && (kLdsRest > kHalfLds || kLdsRest + 4 * TILE <= kHalfLds);
+  __shared__ __attribute__((aligned(16))) T16 Qs[kQLds ? 2 : 1][kQLds ? TILE : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -850,7 +866,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     const size_t r0 = hbase + (size_t)cc * C;
     uint32_t po[NTILE];
     dma_tile_offsets<D>(po, lane, cc == NC - 1 ? nlast : C);
-    dma_tile<D>(Ks[cc % 3], k + r0 * D, po);
+    dma_tile<D>(Ks[cc % KR], k + r0 * D, po);
   };
   // DMA of this tile's V columns (rows 32 m + l / 2, columns col0 + 8 (l % 2)
   // ..) and of the T record of chunk cc (the DMA V wave)
@@ -862,6 +878,15 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     for (int m = 0; m < 2; ++m)
       dma16s(v + r0 * D + col0, (uint32_t)((min(32 * m + lane / 2, nr - 1) * D + 8 * (lane % 2)) * 2),
              __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+  };
+  // DMA of Q of chunk cc (the DMA V wave), rows as for K
+  auto issue_q = [&](int cc) {
+    if constexpr (kQLds) {
+      const size_t r0 = hbase + (size_t)cc * C;
+      uint32_t po[NTILE];
+      dma_tile_offsets<D>(po, lane, cc == NC - 1 ? nlast : C);
+      dma_tile<D>(Qs[cc % 2], q + r0 * D, po);
+    }
   };
   auto issue_t = [&](int cc) {
     const uint32_t tb = lds_addr(Ts[cc % 3]);
@@ -922,7 +947,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       const float gv = cumsum64(Ls[cc % NG], lane);
       const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
       const float e = __expf(gv);
-      Gs[cc % 3][lane] = gv;
+      if constexpr (OUT) Gs[cc % 3][lane] = gv;
       Es[cc % 3][lane] = e;
       Fs[cc % 3][lane] = __expf(gC - gv);
       if constexpr (kDelta) BGs[cc % 3][lane] = Bs[cc % NG][lane] * e;
@@ -981,8 +1006,8 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     for (int j = 0; j < HB; ++j) {
       const int kb = h * HB + j;
       sf[j] = frag2_from_acc<T16>(S[2 * j], S[2 * j + 1]);
-      Sx[0][(2 * kb) * kWave + lane] = sf[j].hi;
-      Sx[0][(2 * kb + 1) * kWave + lane] = sf[j].lo;
+      Sx[0][(SXP * kb) * kWave + lane] = sf[j].hi;
+      if constexpr (OUT) Sx[0][(2 * kb + 1) * kWave + lane] = sf[j].lo;
     }
     __syncthreads();
     __syncthreads();
@@ -1002,7 +1027,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf / BVs slots
 
     for (int c = 0; c < NC; ++c) {
-      const uint32_t kslot = slot(c, 3, kTileB);
+      const uint32_t kslot = slot(c, KR, kTileB);
       // gam_C of chunk c+1 (its tables are two chunks ahead), read first:
       // the split at the end of the chunk waits for it.  The load is
       // unconditional, from a clamped slot, so that no branch splits the
@@ -1016,7 +1041,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       if constexpr (kDelta) {
         const uint32_t tslot = slot(c, 3, C * 4);
         const uint32_t bvslot = slot(c, 2, 4 * kWave * 16);
-        Frag<T16> kf[4][NKB], th[kTFrags], tl[kTFrags], sh[NKB];
+        Frag<T16> kf[4][NKB], th[kTFrags], sh[NKB];
         f32x4 bv[4], bb[4], fr[4];
         // K S over the whole state: this half's bf16 S from registers, the
         // other half's from the split both halves published at the end of
@@ -1025,12 +1050,12 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         // else).  Both halves form the same products in the same order, so
         // they hold the same K S and need no exchange.
         {
-          const uint32_t a = slot(c, 2, 2 * NKB * kWave * 16) + xoff;
+          const uint32_t a = slot(c, 2, SXP * NKB * kWave * 16) + xoff;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
             // (register arrays only ever indexed by compile-time values)
             if (kb / HB == h) sh[kb] = sf[kb % HB].hi;
-            else sh[kb].v = lds_ld<bf16x8>(Sx, a + (2 * kb) * kWave * 16);
+            else sh[kb].v = lds_ld<bf16x8>(Sx, a + (SXP * kb) * kWave * 16);
           }
         }
 #pragma unroll
@@ -1064,10 +1089,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         {
           const uint32_t a = slot(c, 3, kTRecFrags * kWave * 16) + xoff;
 #pragma unroll
-          for (int f = 0; f < kTFrags; ++f) {
-            th[f].v = lds_ld<bf16x8>(Ts, a + f * kWave * 16);
-            tl[f].v = lds_ld<bf16x8>(Ts, a + (kTFrags + f) * kWave * 16);
-          }
+          for (int f = 0; f < kTFrags; ++f) th[f].v = lds_ld<bf16x8>(Ts, a + f * kWave * 16);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -1083,17 +1105,13 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         Frag2<T16> rf[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) rf[kb] = frag2_from_acc<T16>(rr[2 * kb], rr[2 * kb + 1]);
-        // U_new = T R, both split
+        // U_new = T R, R split
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           un[ti] = zero4();
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            if (kb <= ti / 2) {
-              mma(tl[tfi(ti, kb)], rf[kb].hi, un[ti]);
-              mma(th[tfi(ti, kb)], rf[kb].lo, un[ti]);
-              mma(th[tfi(ti, kb)], rf[kb].hi, un[ti]);
-            }
+            if (kb <= ti / 2) mma_ab2(th[tfi(ti, kb)], rf[kb], un[ti]);
         }
         // U_new in float for the output waves (which split it)
         if constexpr (OUT) {
@@ -1155,7 +1173,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       // consumes S and the state carried on is S_{c+1} decayed by gam_C of
       // chunk c+1
       {
-        const uint32_t a = slot(c + 1, 2, 2 * NKB * kWave * 16) + xoff;
+        const uint32_t a = slot(c + 1, 2, SXP * NKB * kWave * 16) + xoff;
 #pragma unroll
         for (int j = 0; j < HB; ++j) {
           const int kb = h * HB + j;
@@ -1167,8 +1185,8 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
           } else {
             sf[j] = frag2_from_acc<T16>(S[2 * j], S[2 * j + 1]);
           }
-          lds_st<bf16x8>(Sx, a + (2 * kb) * kWave * 16, sf[j].hi.v);
-          lds_st<bf16x8>(Sx, a + (2 * kb + 1) * kWave * 16, sf[j].lo.v);
+          lds_st<bf16x8>(Sx, a + (SXP * kb) * kWave * 16, sf[j].hi.v);
+          if constexpr (OUT) lds_st<bf16x8>(Sx, a + (2 * kb + 1) * kWave * 16, sf[j].lo.v);
         }
       }
       __syncthreads();
@@ -1182,8 +1200,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     }
   } else if (wave == kDmaK) {
     // ================= DMA of K and the gates
-    issue_k(0);
-    if (NC > 1) issue_k(1);
+    for (int cc = 0; cc < KR - 1 && cc < NC; ++cc) issue_k(cc);
     for (int cc = 0; cc < NG - 1 && cc < NC; ++cc) issue_gates(cc);
     vm_wait<0>();
     __syncthreads();
@@ -1191,14 +1208,20 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     for (int c = 0; c < NC; ++c) {
       // the slots these fill held chunk c-1, last read before the barrier
       // that opened this chunk
-      if (c + 2 < NC) issue_k(c + 2);
+      if (c + KR - 1 < NC) issue_k(c + KR - 1);
       if (c + NG - 1 < NC) issue_gates(c + NG - 1);
       if (c + 1 < NC) make_bv(c + 1);
-      // Everything issued before this chunk has landed.  Loads complete in
-      // issue order, so while any earlier transfer is outstanding all N of
-      // this chunk's are too.
-      if (c + NG - 1 < NC) vm_wait<NDMAK>();
-      else vm_wait<0>();
+      // Everything issued before this chunk has landed (with K one chunk
+      // ahead, this chunk's K too: it is issued before the gates).  Loads
+      // complete in issue order, so while any earlier transfer is
+      // outstanding all N of this chunk's are too.
+      if constexpr (KR == 3) {
+        if (c + NG - 1 < NC) vm_wait<NDMAK>();
+        else vm_wait<0>();
+      } else {
+        if (c + NG - 1 < NC) vm_wait<NGATE>();
+        else vm_wait<0>();
+      }
       __syncthreads();
     }
   } else if (wave == kDmaV) {
@@ -1209,6 +1232,7 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
 #pragma unroll
       for (int i = 0; i < NV * C * 16 * 2 / 16 / kWave; ++i) vr[i * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
     }
+    issue_q(0);
     for (int cc = 0; cc < 3 && cc < NC; ++cc)
       if (!vzero) issue_v(cc);
     if constexpr (kDelta) {
@@ -1223,6 +1247,10 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     make_bv(0);
     __syncthreads();
     for (int c = 0; c < NC; ++c) {
+      // Q of the next chunk first (its slot held chunk c-1, last read before
+      // the barrier that opened this chunk): the wait below leaves only this
+      // chunk's V and T transfers outstanding
+      if (c + 1 < NC) issue_q(c + 1);
       if (c + 3 < NC && !vzero) issue_v(c + 3);
       if constexpr (kDelta)
         if (c + 2 < NC) issue_t(c + 2);
@@ -1241,12 +1269,16 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       auto run = [&](auto ti_c) {
         constexpr int TI = decltype(ti_c)::value;
         Frag<T16> qc[NKB], qn[NKB];
-        load_q<D, TI>(qc, q, hbase, NC == 1 ? nlast : C, g, n);
+        if constexpr (!kQLds) load_q<D, TI>(qc, q, hbase, NC == 1 ? nlast : C, g, n);
         __syncthreads();
         __syncthreads();
         f32x4 sc[4], qs, ot;
         for (int c = 0; c < NC; ++c) {
-          {
+          if constexpr (kQLds) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              qc[kb] = frag_row_at<D>(Qs, slot(c, 2, kTileB) + roff[kb] + kRows16 * TI);
+          } else {
             // Q of the next chunk (the last chunk's again at the end: the
             // load is unconditional)
             const int cn = c + 1 < NC ? c + 1 : c;
@@ -1257,14 +1289,16 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
                                          g, n, lane, dcol4);
             store_rows<D, TI>(ot, out_, (hbase + (size_t)(c - 1) * C) * D + col0, out_bf16, g, n, C);
           }
-          const T16* Kc = Ks[c % 3];
+          const T16* Kc = Ks[c % KR];
           const float* gc = Gs[kGated ? c % 3 : 0];
           const float* gk = kQSide ? Gk[c % 3] : gc;
           const float* ec = kQSide ? Eq[c % 3] : Es[kGated ? c % 3 : 0];
           scores_qs<D, kGated, TI>(qc, Kc, gc, gk, ec, Ra[kFac ? c % 3 : 0], Cb[kFac ? c % 3 : 0],
                                    Sx[c % 2], roff, sc, qs, g, n, lane);
+          if constexpr (!kQLds) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) qc[kb] = qn[kb];
+            for (int kb = 0; kb < NKB; ++kb) qc[kb] = qn[kb];
+          }
           __syncthreads();
         }
         const int c = NC - 1;
@@ -1844,36 +1878,39 @@ ProArrays pro_arrays(const ChunkArgs& a) {
                    reinterpret_cast<float*>(base + 2 * s), reinterpret_cast<float*>(base + 3 * s)};
 }
 
-// Rough cost, in chunk steps of the whole-sequence walk, of P segments: the
-// state pass and the output pass, each in rounds of as many workgroups as
-// fit on the compute units at once (two state-pass workgroups share one: it
-// has no Q ring, at most 80 KiB of LDS), times their measured step costs
-// relative to a step of the walk (0.85 and 1.05), plus the scan (per
-// segment about 1.6 steps with erase, a dk x dk by dk x 8 product per
-// workgroup, and 0.3 without).
+// Rough cost, in chunk steps of the whole-sequence walk, of P segments,
+// fitted to measured step times (gated delta rule, dk = dv = 128, L = 65536,
+// one to sixteen heads):
+// * state pass: two of its workgroups fit on a compute unit, but two sharing
+//   one run slower: 0.8 of a walk step while every workgroup has a unit of
+//   its own, 1.35 per round of two per unit beyond that;
+// * output pass: one workgroup per unit, 1.05 of a walk step per round;
+// * each pass fills and drains its pipeline (about 3 steps), and the scan
+//   adds about 2 steps per segment with erase (a dk x dk by dk x 8 product
+//   per workgroup), 0.3 without.
+// Segments are used when they save at least 5% on this estimate.
 int plan_segments(const ChunkArgs& a) {
   if (!a.in_bf16 || a.cu) return 1;
   const long chains = (long)a.B * a.H * (a.d / 16);
   const int nc = (a.L + C - 1) / C;
-  auto rounds = [](long n, int per_cu) {
-    const long slots = (long)kComputeUnits * per_cu;
-    return (double)((n + slots - 1) / slots);
-  };
-  const double whole = rounds(chains, 1) * nc;
+  const long cus = kComputeUnits;
+  const double whole = (double)((chains + cus - 1) / cus) * nc;
   double best = whole;
   int best_p = 1;
   for (int P = 2; P <= nc / kMinSegChunks && P <= kMaxSegments; ++P) {
     const long n1 = chains * ((P - 1) + (mode_erase(a.mode) ? P - 2 : 0));
     const long n3 = chains * P;
-    const int seg = (nc + P - 1) / P;
-    const double scan = mode_erase(a.mode) ? 1.6 : 0.3;
-    const double cost = (0.85 * rounds(n1, 2) + 1.05 * rounds(n3, 1)) * seg + scan * P;
+    const double steps = (double)((nc + P - 1) / P) + 3.0;
+    const double state = n1 <= cus ? 0.8 : 1.35 * (double)((n1 + 2 * cus - 1) / (2 * cus));
+    const double out = 1.05 * (double)((n3 + cus - 1) / cus);
+    const double scan = (mode_erase(a.mode) ? 2.0 : 0.3) * P;
+    const double cost = (state + out) * steps + scan;
     if (cost < best) {
       best = cost;
       best_p = P;
     }
   }
-  return best < 0.85 * whole ? best_p : 1;
+  return best < 0.95 * whole ? best_p : 1;
 }
 
 hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {

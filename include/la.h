@@ -168,7 +168,7 @@ typedef enum {
  *              arguments; may be NULL when that is 0.  Its contents on entry
  *              are ignored and on return are unspecified.  The bf16 delta
  *              modes keep each chunk's T factor there (B*H*ceil(L/C) *
- *              12 KiB: T as bf16 hi and lo parts); float inputs need none,
+ *              6 KiB: T as bf16 operand fragments); float inputs need none,
  *              nor do the modes without erase (LINEAR, GATED_LINEAR)
  *              unless the call runs sequence-parallel (below).
  *   stream     hipStream_t
@@ -205,7 +205,7 @@ int la_chunk_fwd(const void* q, const void* k, const void* v,
  *
  * Limit: a call whose la_chunk_workspace_bytes() exceeds
  * LA_NOALLOC_SCRATCH_BYTES returns LA_ERR_WORKSPACE before anything is
- * enqueued (e.g. B*H*ceil(L/C) above 10,922 chunk-heads in the bf16 delta
+ * enqueued (e.g. B*H*ceil(L/C) above 21,845 chunk-heads in the bf16 delta
  * modes); use la_chunk_fwd with a workspace for those.
  *
  * Every call on one GPU shares that GPU's array, and the array keeps the
@@ -361,7 +361,7 @@ int la_chunk_segments(int B, int H, int L, int dk, int dv, int C, int mode,
  *   N, H, T, dk, dv, C        N >= 1, T >= 0; sizes as in la_chunk_fwd
  *   mode, dtype, workspace, workspace_bytes, stream   as in la_chunk_fwd;
  *              the workspace size comes from la_chunk_varlen_workspace_bytes
- *              (bf16 delta modes: H * (ceil(T/C) + N) * 12 KiB, whatever the
+ *              (bf16 delta modes: H * (ceil(T/C) + N) * 6 KiB, whatever the
  *              offsets)
  *
  * The offsets are read on the device and cannot be validated before the

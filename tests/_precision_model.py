@@ -8,8 +8,8 @@ bf16, as chosen per operand.  With every operand exact (float64) it is the
 chunkwise form of the recurrence.  Used to size the kernels' precision
 budget against the bf16 tolerance max|err| <= 2e-2 RMS(ref).
 
-The kernels' choice: T = (I + A)^-1 split (as T diag(beta) in the T R
-product), the state S as a single bf16 in the chain's K S product and split
+The kernels' choice: T = (I + A)^-1 as a single bf16 in the T R product
+(R split), the state S as a single bf16 in the chain's K S product and split
 everywhere else (Q S), U_new split in the state update and in
 (Q K^T * Gamma) U_new, the scores split.
 """
@@ -17,7 +17,7 @@ import torch
 
 BF = torch.bfloat16
 
-KERNEL = dict(T="split", S_chain="hi", S_out="split", U_upd="split", scores="split",
+KERNEL = dict(T="hi", S_chain="hi", S_out="split", U_upd="split", scores="split",
               U_out="split")
 
 

@@ -18,7 +18,7 @@ from chunkwise_gated_delta_la_amd import _lib  # noqa: E402
 
 HEADER = os.path.join(ROOT, "include", "la.h")
 OK, NULL, SHAPE, UNSUP, ALIAS, WS = 0, 1, 2, 3, 4, 6
-TSOLVE_BYTES = 12 * 1024    # T operand fragments (hi, lo) per chunk (bf16 delta modes)
+TSOLVE_BYTES = 6 * 1024     # T operand fragments per chunk (bf16 delta modes)
 
 
 def _declared_functions():
