@@ -420,6 +420,40 @@ def bench_segments(w, steps, warmup):
     return res
 
 
+def segment_sweep(base, steps, warmup, heads=(1, 2, 4, 8, 16),
+                  counts=(1, 2, 3, 4, 6, 8, 12, 16, 24, 32)):
+    """ms per forward of the sequence-parallel path at explicit segment
+    counts against la_chunk_fwd's own plan, for a few head counts of one
+    long-sequence workload (the evidence the plan's cost model is fitted
+    to).  One JSON object: {H: {"plan": P, "ms": {P: ms}}}."""
+    import torch
+
+    import chunkwise_gated_delta_la_amd as la
+    import workloads
+
+    res = {}
+    for H in heads:
+        w = base.scaled(H=H, name=f"{base.name}_h{H}")
+        nc = -(-w.L // w.C)
+        plan = la.chunk_segments(w.B, w.H, w.L, w.dk, w.dv, mode=w.mode, C=w.C,
+                                 dtype=w.torch_dtype)
+        log(f"[bench] segment sweep H={H} (plan P={plan})")
+        x = {k: t.cuda() for k, t in workloads.make_inputs(w).items()}
+        out = torch.empty((w.B, w.H, w.L, w.dv), dtype=w.torch_dtype, device="cuda")
+        S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+        ms = {}
+        for P in sorted({c for c in counts if c <= nc} | {plan}):
+            def step():
+                la.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"],
+                             x["S0"] if w.s0_std > 0 else None, mode=w.mode, C=w.C, out=out,
+                             S_final=S_final, segments=P)
+            ms[P] = round(_timed(step, steps, warmup)[0], 4)
+        res[H] = {"plan": plan, "ms": ms}
+        del x, out, S_final
+        torch.cuda.empty_cache()
+    return res
+
+
 def _timed(step, steps, warmup):
     """ms per call of step() (host clock around synchronised runs) and the
     library's per-kernel HIP-event times over the same calls."""
@@ -895,6 +929,9 @@ def main():
                     help="tokens per head of the backward's CPU oracle sample (0 = skip)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens per head of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--segment-sweep", action="store_true",
+                    help="only time the forward at explicit segment counts against the "
+                         "plan, for 1-16 heads of the workload's sequence")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (traffic calibration)")
     ap.add_argument("--ingest-pmc", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH",
@@ -925,7 +962,7 @@ def main():
     # must happen before this process touches the GPU.
     x = cpu = None
     cpu_cfg = {}
-    if not (args.only_backward or args.calibrate_copy):
+    if not (args.only_backward or args.calibrate_copy or args.segment_sweep):
         x = workloads.make_inputs(w)
         if args.cpu_tokens > 0:
             cpu = cpu_baseline(w, x, min(args.cpu_tokens, w.L))
@@ -943,6 +980,11 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.segment_sweep:
+        print(json.dumps({"segment_sweep": {
+            "workload": workloads.WORKLOADS[args.workload].name,
+            "sweep": segment_sweep(workloads.WORKLOADS[args.workload], 5, 2)}}), flush=True)
         return
     if args.only_backward:
         print(json.dumps({"backward": bench_backward(w, args.steps, args.warmup,
