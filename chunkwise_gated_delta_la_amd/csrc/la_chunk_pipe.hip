@@ -8,29 +8,20 @@
 //    occupancy, and written to a workspace as the exact MFMA operand
 //    fragments the second kernel feeds to U_new = T R (6 KiB per chunk).
 //
-// 2. chunk_pipe_kernel, one 256-thread workgroup per 16-column tile of one
-//    (batch, head) state, walking the chunks in order.  Per chunk c, with a
-//    single barrier at the end:
-//
-//      wave 0 (chain)  K S, R = diag(beta)(V - diag(gam) K S), U_new = T R
-//                      (publish U_new), S <- gam_C S + K^T diag(gam_C/gam)
-//                      U_new (publish S, already decayed for chunk c+1 in
-//                      the copy the chain keeps)
-//      waves 1-3       first the DMA of chunk c+2 (Q, K, V, T) and of the
-//                      gates of chunk c+4; then the output of chunk c-1 from
-//                      the U_new published at the last barrier; the decay
-//                      tables of chunk c+2; masked decayed scores and
-//                      diag(gam) Q S of chunk c for their row tiles (wave 1:
-//                      tiles 0 and 1, wave 2: tile 2, wave 3: tile 3), kept
-//                      in registers until the next chunk
-//
-//    so the serial chain only ever waits for its own products, and does as
-//    little besides them as possible: every LDS address it uses is one add
-//    of a loop-invariant lane offset to the ring slot, and the float to
-//    bf16 splits it needs take two instructions per value.  Inputs go from
-//    HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16
-//    bytes land at base + 16 l) without passing through registers, issued
-//    two chunks ahead and waited for one chunk later.
+// 2. chunk_pipe_kernel, one 512-thread workgroup per 16-column tile of one
+//    (batch, head) state, walking the chunks in order with a single barrier
+//    per chunk: two waves carry the serial chain (K S, R, U_new = T R and
+//    the state update, each on half of the state's rows), four form the
+//    output of their row tiles from what the chain published, and two move
+//    the inputs and build the decay tables (the roles are listed at the
+//    kernel).  The chain waves only ever wait for their own products, and
+//    do as little besides them as possible: every LDS address they use is
+//    one add of a loop-invariant lane offset to the ring slot, and the
+//    float to bf16 splits take two instructions per value.  Inputs go from
+//    HBM straight into LDS rings (global_load_lds_dwordx4: lane l's 16 bytes
+//    land at base + 16 l) without passing through registers, issued ahead
+//    of the chunk that reads them and waited for before the barrier that
+//    opens it.
 //
 // State rows.  The rows of the state (the dk index) are kept in the
 // registers in a fixed permuted order: register row p = 32 kb + 16 h +
@@ -700,7 +691,8 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 //   waves 0, 1   the serial chain, each on half of the state's rows (dk):
 //                the whole K S (the other half's bf16 state read from the
 //                split both publish for the output waves), R = diag(beta)(V -
-//                diag(gam) K S) and U_new = T R, then the update of
+//                diag(gam) K S) and U_new = T R (each publishes two of its
+//                four row tiles for the output waves), then the update of
 //                its half, S <- gam_C S + K^T diag(gam_C / gam) U_new, and
 //                its half's split published.  The two never wait for each
 //                other inside a chunk.  Without erase: S <- gam_C S + K^T
@@ -708,13 +700,15 @@ __device__ __forceinline__ float cumsum64(const float* p, int lane) {
 //   DMA K        K of chunk c+2 and the gates of chunk c+4 into LDS rings;
 //                beta V (or f V) of chunk c+1 in the chain's accumulator
 //                layout
-//   DMA V        V of chunk c+3 and the T record of chunk c+2; the decay
-//                tables of chunk c+2; the zero rows of a partial V
+//   DMA V        Q of chunk c+1 (where Q is staged in LDS), V of chunk
+//                c+3 and the T record of chunk c+2; the decay tables of
+//                chunk c+2; the zero rows of a partial V
 //   output (4)   one row tile each: the output of chunk c-1 from the U_new
 //                published at the last barrier (formed transposed: one
 //                store per lane of four adjacent columns), then the masked
-//                decayed scores and diag(gam) Q S of chunk c (Q straight
-//                from HBM, prefetched one chunk ahead) kept in registers
+//                decayed scores and diag(gam) Q S of chunk c kept in
+//                registers (Q from the LDS ring, or straight from HBM one
+//                chunk ahead where staging it would halve the occupancy)
 //
 // OUT: 8 waves (chain 0, 1; output tiles 3, 2 on waves 2, 3 and 0, 1 on
 // waves 6, 7; DMA K wave 4, DMA V wave 5).  The state pass (OUT = false)
@@ -1113,12 +1107,16 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
           for (int kb = 0; kb < 2; ++kb)
             if (kb <= ti / 2) mma_ab2(th[tfi(ti, kb)], rf[kb], un[ti]);
         }
-        // U_new in float for the output waves (which split it)
+        // U_new in float for the output waves (which split it); both halves
+        // hold all of it, each publishes two of its row tiles
         if constexpr (OUT) {
+          const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
           if (h == 0) {
-            const uint32_t a = slot(c, 2, 4 * kWave * 16) + xoff;
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) lds_st<f32x4>(Uf, a + ti * kWave * 16, un[ti]);
+            lds_st<f32x4>(Uf, a + 0 * kWave * 16, un[0]);
+            lds_st<f32x4>(Uf, a + 1 * kWave * 16, un[1]);
+          } else {
+            lds_st<f32x4>(Uf, a + 2 * kWave * 16, un[2]);
+            lds_st<f32x4>(Uf, a + 3 * kWave * 16, un[3]);
           }
         }
         // operand of the state update: diag(gam_C / gam) U_new (gated), U_new
