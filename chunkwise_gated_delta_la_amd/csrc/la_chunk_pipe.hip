@@ -1312,6 +1312,328 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
   }
 }
 
+// ---------------------------------------------------------------- wide kernel (no erase)
+//
+// The modes without erase carry no per-chunk solve, and their chain is one
+// product per chunk (S <- gam_C S + K^T diag(f) V), so a chunk step is
+// mostly the output: scores, Q S and Aqk V.  The chain kernel above repeats
+// the scores and the staging of Q and K in each of a head's D / 16 column
+// tiles.  This kernel gives one workgroup 64 state columns of a stream, one
+// wave per 16-column tile, so the four tiles share one copy of the chunk's
+// Q, K and masked decayed scores:
+//
+//   every wave   issues a quarter of the DMA of chunk c+2 (Q, K: rings of
+//                three swizzled tiles) and its own tile's V columns; forms
+//                its share of the ten lower score tiles of chunk c+1
+//                (Aqk^T tiles K Q^T, packed as the split operand blocks
+//                (TI, kb) the output reads: wave 0 blocks (3,0), (0,0);
+//                wave 1 (3,1), (2,1); wave 2 (2,0); wave 3 (1,0)) into a
+//                double buffer; then, for chunk c, O^T = S^T Q^T diag(gam)
+//                + V^T Aqk^T for its 16 columns and all 64 rows (S split,
+//                V exact, the scores split), and S <- gam_C S + K^T diag(f) V
+//                (V exact, or f V split with decay).
+//
+// One barrier per chunk.  The state tile stays in the wave's accumulators
+// in the permuted row order of the chain kernel; the output is stored
+// transposed (one 8- or 16-byte store per lane and row tile).  The gates
+// arrive by DMA (wave 0) and each wave forms the chunk's cumulative decay
+// in registers, exchanging values across lanes with ds_bpermute.
+template <int D, bool GATED>
+__global__ __launch_bounds__(256) void lin_wide_kernel(
+    const T16* __restrict__ q, const T16* __restrict__ k, const T16* __restrict__ v,
+    const float* __restrict__ log_alpha, void* __restrict__ out_, StreamMap smap, int NS,
+    int out_bf16) {
+  constexpr int NKB = D / 32;
+  constexpr int NST = D / 16;              // state row tiles (dk)
+  constexpr int NCG = D / 64;              // 64-column groups per stream
+  constexpr int TILE = C * D;
+  constexpr uint32_t kTileB = 2 * TILE;
+  constexpr uint32_t kRows16 = 32 * D;
+  constexpr int NTILE = TILE * 2 / 1024;   // DMA instructions per Q or K tile
+  constexpr int NTW = NTILE / 4;           // of them per wave
+  constexpr int NR = 3;                    // Q, K, V rings: DMA two chunks ahead
+  constexpr int NAB = 6;                   // score blocks (TI, kb), kb <= TI / 2
+  constexpr int NDMA = 2 * NTW + 2;        // per wave and chunk (+1 gates on wave 0)
+  static_assert(NTILE % 4 == 0, "the tile DMA splits over four waves");
+
+  __shared__ __attribute__((aligned(16))) T16 Qs[NR][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Ks[NR][TILE];
+  __shared__ __attribute__((aligned(16))) T16 Vs[NR][4][C * 16];
+  __shared__ __attribute__((aligned(16))) Frag<T16> Ab[2 * NAB * kWave];
+  __shared__ __attribute__((aligned(16))) float Ls[GATED ? NR : 1][C];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int g = lane / 16;
+  const int n = lane % 16;
+
+  // stream and column group; the groups of one stream share an XCD
+  int sidx, cg;
+  {
+    const int b = blockIdx.x;
+    if (NCG > 1 && NS % 8 == 0) {
+      const int x = b % 8, s = b / 8;
+      cg = s % NCG;
+      sidx = (s / NCG) * 8 + x;
+    } else {
+      sidx = b / NCG;
+      cg = b % NCG;
+    }
+  }
+  const int col0 = 64 * cg + 16 * wave;       // this wave's state columns
+  const int col = col0 + n;
+  const StreamInfo si = stream_info(smap, sidx);
+  const size_t hbase = si.row0;
+  const int L = si.len;
+  if (L == 0) {
+    if (si.sf) {
+#pragma unroll
+      for (int r = 0; r < D / 4; ++r) {
+        const size_t e = (size_t)(4 * r + g) * D + col;
+        si.sf[e] = si.s0 ? si.s0[e] : 0.f;
+      }
+    }
+    return;
+  }
+  // chunks; rows past the sequence read the last valid row, have log alpha
+  // = 0 and V = 0, and are not stored (as in the chain kernel)
+  const int NC = (L + C - 1) / C;
+  const int nlast = L - (NC - 1) * C;
+
+  uint32_t roff[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) roff[kb] = unit_off<D>(n, 4 * kb + g);
+  auto slot = [](int c, int depth, uint32_t bytes) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(c % depth) * bytes));
+  };
+
+  // this wave's part of the DMA of chunk cc
+  auto issue = [&](int cc) {
+    const size_t r0 = hbase + (size_t)cc * C;
+    const int nr = cc == NC - 1 ? nlast : C;
+    // source offset of lane l's unit of DMA instruction m (the swizzled
+    // layout of dma_tile_offsets), computed per instruction: m depends on
+    // the wave, and a register array indexed by it would go to scratch
+    auto toff = [&](int m) {
+      constexpr int RB = 2 * D;
+      const int byte = 1024 * m + 16 * lane;
+      const int r = byte / RB, ul = (byte % RB) / 16;
+      return (uint32_t)(min(r, nr - 1) * RB + ((ul ^ swz_key<D>(r)) << 4));
+    };
+    const uint32_t qb = lds_addr(Qs[cc % NR]), kb_ = lds_addr(Ks[cc % NR]);
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int m = wave * NTW + i;
+      const uint32_t o = toff(m);
+      dma16s(q + r0 * D, o, __builtin_amdgcn_readfirstlane(qb + 1024 * m));
+      dma16s(k + r0 * D, o, __builtin_amdgcn_readfirstlane(kb_ + 1024 * m));
+    }
+    const uint32_t vb = lds_addr(Vs[cc % NR][wave]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      dma16s(v + r0 * D + col0,
+             (uint32_t)((min(32 * m + lane / 2, nr - 1) * D + 8 * (lane % 2)) * 2),
+             __builtin_amdgcn_readfirstlane(vb + 1024 * m));
+    if constexpr (GATED)
+      if (wave == 0)
+        dma4s(log_alpha + r0, (uint32_t)min(lane, nr - 1) * 4, lds_addr(Ls[cc % NR]));
+  };
+  // V rows past the sequence set to zero once the last chunk's V has landed
+  auto zero_v_tail = [&]() {
+    if (nlast < C && lane >= nlast) {
+      u32x4* row = reinterpret_cast<u32x4*>(Vs[(NC - 1) % NR][wave] + lane * 16);
+      row[0] = u32x4{0u, 0u, 0u, 0u};
+      row[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // the chunk's cumulative log decay g (lane = token), 0 past the sequence
+  auto gates = [&](int cc) {
+    const float la = lane < (cc == NC - 1 ? nlast : C) ? Ls[cc % NR][lane] : 0.f;
+    return wave_inclusive_scan(la);
+  };
+  auto lane_val = [](float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+  };
+
+  // score tile (TI, t) of chunk cc, t <= TI: K rows 16 t .. against Q rows
+  // 16 TI .., masked on the diagonal, decayed by exp(g_r - g_i)
+  auto score_tile = [&](int cc, int TI, int t, float gv) {
+    const uint32_t ks = slot(cc, NR, kTileB), qs = ks;
+    f32x4 s = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag<T16> kf = frag_row_at<D>(Ks, ks + roff[kb] + kRows16 * t);
+      const Frag<T16> qf = frag_row_at<D>(Qs, qs + roff[kb] + kRows16 * TI);
+      mma(kf, qf, s);
+    }
+    // element (K row i = 16 t + 4 g + e, Q row r = 16 TI + n)
+    float gr = 0.f;
+    if constexpr (GATED) gr = lane_val(gv, 16 * TI + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * t + 4 * g + e, r = 16 * TI + n;
+      float d = 1.f;
+      if constexpr (GATED) d = __expf(fminf(gr - lane_val(gv, i), 0.f));
+      s[e] = i <= r ? s[e] * d : 0.f;
+    }
+    return s;
+  };
+  auto put_block = [&](int bi, const f32x4& a, const f32x4& b) {
+    const Frag2<T16> f = frag2_from_acc<T16>(a, b);
+    const uint32_t o = (uint32_t)lane * 16;
+    lds_st<bf16x8>(Ab, o + (2 * bi) * kWave * 16, f.hi.v);
+    lds_st<bf16x8>(Ab, o + (2 * bi + 1) * kWave * 16, f.lo.v);
+  };
+  // this wave's blocks of chunk cc (block index tfi(TI, kb))
+  auto scores = [&](int cc) {
+    float gv = 0.f;
+    if constexpr (GATED) gv = gates(cc);
+    if (wave == 0) {
+      put_block(tfi(3, 0), score_tile(cc, 3, 0, gv), score_tile(cc, 3, 1, gv));
+      put_block(tfi(0, 0), score_tile(cc, 0, 0, gv), zero4());
+    } else if (wave == 1) {
+      put_block(tfi(3, 1), score_tile(cc, 3, 2, gv), score_tile(cc, 3, 3, gv));
+      put_block(tfi(2, 1), score_tile(cc, 2, 2, gv), zero4());
+    } else if (wave == 2) {
+      put_block(tfi(2, 0), score_tile(cc, 2, 0, gv), score_tile(cc, 2, 1, gv));
+    } else {
+      put_block(tfi(1, 0), score_tile(cc, 1, 0, gv), score_tile(cc, 1, 1, gv));
+    }
+  };
+
+  // the state tile: register row p of tile j holds dk index dk_of_row(p)
+  f32x4 S[NST];
+  if (si.s0) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[j][i] = si.s0[(size_t)dk_of_row(16 * j + 4 * g + i) * D + col];
+  } else {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) S[j] = zero4();
+  }
+  // K^T operand offsets of state tile j (token block 0)
+  uint32_t ktr[NST];
+#pragma unroll
+  for (int j = 0; j < NST; ++j) ktr[j] = tr_off<D>(g, n, j / 2) + 8 * (j % 2);
+
+  // Everything but the last issued chunk has landed: each wave waits for its
+  // own transfers (vector-memory operations retire in issue order; stores
+  // issued after the chunk's DMA only make the wait stricter).
+  auto wait_but_last = [&]() {
+    if constexpr (GATED) {
+      if (wave == 0) vm_wait<NDMA + 1>();
+      else vm_wait<NDMA>();
+    } else {
+      vm_wait<NDMA>();
+    }
+  };
+
+  issue(0);
+  if (NC > 1) {
+    issue(1);
+    wait_but_last();
+  } else {
+    vm_wait<0>();
+    zero_v_tail();
+  }
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    // chunk c landed before the barrier that opened this step; c+2 goes to
+    // the slot chunk c-1 held, read for the last time before that barrier
+    if (c + 2 < NC) issue(c + 2);
+    scores(c);
+    __syncthreads();
+    const uint32_t ts = slot(c, NR, kTileB);
+    const uint32_t as = (uint32_t)lane * 16;
+    const T16* Vt = Vs[c % NR][wave];
+    float gv = 0.f, gC = 0.f;
+    if constexpr (GATED) {
+      gv = gates(c);
+      gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), kWave - 1));
+    }
+    // V columns of this tile over the two token blocks (exact)
+    Frag<T16> vf[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) vf[kb] = frag_col_tr_v(Vt, 32 * kb, g, n);
+    // S split (the entering state) as the A operand of S^T Q^T
+    Frag2<T16> sx[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sx[kb] = frag2_from_acc<T16>(S[2 * kb], S[2 * kb + 1]);
+    const int nrows = c == NC - 1 ? nlast : C;
+    const size_t ob0 = (hbase + (size_t)c * C) * D + col0;
+    auto out_tile = [&](auto ti_c) {
+      constexpr int TI = decltype(ti_c)::value;
+      f32x4 o = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const Frag<T16> qf = frag_row_at<D>(Qs, ts + roff[kb] + kRows16 * TI);
+        mma(sx[kb].lo, qf, o);
+        mma(sx[kb].hi, qf, o);
+      }
+      if constexpr (GATED) o *= __expf(lane_val(gv, 16 * TI + n));
+#pragma unroll
+      for (int kb = 0; kb <= TI / 2; ++kb) {
+        Frag<T16> ah, al;
+        ah.v = lds_ld<bf16x8>(Ab, as + (2 * tfi(TI, kb)) * kWave * 16);
+        al.v = lds_ld<bf16x8>(Ab, as + (2 * tfi(TI, kb) + 1) * kWave * 16);
+        mma(vf[kb], al, o);
+        mma(vf[kb], ah, o);
+      }
+      store_rows<D, TI>(o, out_, ob0, out_bf16, g, n, nrows);
+    };
+    out_tile(std::integral_constant<int, 0>{});
+    out_tile(std::integral_constant<int, 1>{});
+    out_tile(std::integral_constant<int, 2>{});
+    out_tile(std::integral_constant<int, 3>{});
+    // S <- gam_C S + K^T diag(f) V
+    if constexpr (GATED) {
+      const float dC = __expf(gC);
+#pragma unroll
+      for (int j = 0; j < NST; ++j) S[j] *= dC;
+      // f V, split: slot j of block kb is token 32 kb + kidx(g, j)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag2<T16> fv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float f = __expf(gC - lane_val(gv, 32 * kb + kidx(g, j)));
+          fv.set(j, (float)vf[kb].v[j] * f);
+        }
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+          const Frag<T16> kt = frag_tr_at(Ks, ts + ktr[j] + 64 * D * kb, kRows16);
+          mma_ab2(kt, fv, S[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < NST; ++j) {
+          const Frag<T16> kt = frag_tr_at(Ks, ts + ktr[j] + 64 * D * kb, kRows16);
+          mma(kt, vf[kb], S[j]);
+        }
+    }
+    // chunk c+1 lands before the barrier (the one issued at this step's top
+    // may stay in flight: it is read two steps on)
+    if (c + 2 < NC) wait_but_last();
+    else vm_wait<0>();
+    // the last chunk's V, issued at c = NC - 3, has landed in the full wait
+    // of c = NC - 2 and is read at c = NC - 1
+    if (c == NC - 2) zero_v_tail();
+    __syncthreads();
+  }
+  if (si.sf) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) si.sf[(size_t)dk_of_row(16 * j + 4 * g + i) * D + col] = S[j][i];
+  }
+}
+
 // ---------------------------------------------------------------- segment scan
 
 constexpr int kScanThreads = 512;
@@ -1991,7 +2313,37 @@ hipError_t launch_seg_scan(const ChunkArgs& a, hipStream_t st) {
   return a.d == 64 ? launch_scan_d<64>(a, st) : launch_scan_d<128>(a, st);
 }
 
+// The wide kernel serves the whole-sequence walk of the modes without erase
+// (not the segment passes, nor the fused q, k norms or residual, which the
+// chain kernel's tables and output waves carry) where its workgroups (one
+// per stream and 64 columns) fill the compute units: per column tile and
+// chunk it is faster, but it has a quarter of the chain kernel's
+// workgroups, each with a chain as long.
+bool use_wide(const ChunkArgs& a) {
+  const long wgs = (long)a.B * a.H * (a.d / 64);
+  return !mode_erase(a.mode) && a.P <= 1 && !(a.pro & kProQKNorm) && !a.dskip &&
+         wgs >= kComputeUnits;
+}
+
+template <int D>
+hipError_t launch_wide_d(const ChunkArgs& call, hipStream_t st) {
+  const ChunkArgs a = kernel_args(call);
+  const StreamMap m = stream_map(a, kPassWhole);
+  const size_t ns = (size_t)a.B * a.H;
+  const dim3 grid((unsigned)(ns * (D / 64))), block(256);
+  if (mode_decay(a.mode))
+    lin_wide_kernel<D, true><<<grid, block, 0, st>>>(
+        static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
+        a.log_alpha, a.out, m, (int)ns, a.out_bf16 ? 1 : 0);
+  else
+    lin_wide_kernel<D, false><<<grid, block, 0, st>>>(
+        static_cast<const T16*>(a.q), static_cast<const T16*>(a.k), static_cast<const T16*>(a.v),
+        a.log_alpha, a.out, m, (int)ns, a.out_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_pipe(const ChunkArgs& a, hipStream_t st) {
+  if (use_wide(a)) return a.d == 64 ? launch_wide_d<64>(a, st) : launch_wide_d<128>(a, st);
   const int pass = a.P > 1 ? kPassOut : kPassWhole;
   return a.d == 64 ? launch_d<64, true>(a, pass, st) : launch_d<128, true>(a, pass, st);
 }

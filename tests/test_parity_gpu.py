@@ -131,6 +131,34 @@ def test_chunk_small(mode, dtype, d, s0):
     check_fwd(w, x, o_ref, S_ref)
 
 
+@pytest.mark.parametrize("mode", ["linear", "gated_linear"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_no_erase_repeat_bit_identical(mode, d):
+    """Ten calls on the same inputs agree bit for bit (a read of a tile still
+    being written by the DMA would not), and the first matches the oracle;
+    lengths with 1, 2, 3 and 5 chunks and a ragged tail.  (Batches this
+    small run the chain kernel; tests/test_wide_gpu.py repeats the check on
+    the wide kernel.)"""
+    for L in (40, 128, 170, 320):
+        w = recipe(mode, "bf16", B=2, H=3, L=L, d=d, s0_std=0.3 if L != 128 else 0.0, seed=L)
+        log(f"wide repeat {w}")
+        x = workloads.make_inputs(w)
+        dev = to_cuda(x)
+        s0 = dev["S0"] if w.s0_std > 0 else None
+        outs = []
+        for _ in range(10):
+            o, S = la.chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], s0,
+                                mode=mode, C=w.C, return_state=True, out_dtype=torch.float32)
+            outs.append((o.clone(), S.clone()))
+        torch.cuda.synchronize()
+        for o, S in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(S, outs[0][1]), \
+                f"{w}: repeated calls differ"
+        o_ref, S_ref = oracle_fwd(x, mode)
+        assert_close("o (f32 out)", f64(outs[0][0]), o_ref, "bf16")
+        assert_close("S_final", f64(outs[0][1]), S_ref, "bf16")
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_chunk_single_chunk_single_head(mode):
     w = recipe(mode, "bf16", B=1, H=1, L=64, d=128, s0_std=0.5, seed=3)
