@@ -1019,6 +1019,18 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
     for (int j = 0; j < HT / 2; ++j) ktr[j] = tr_off<D>(g, n, h * (HT / 2) + j);
     const uint32_t goff = (uint32_t)(4 * g) * 4;        // tables: row 16 ti + 4 g
     const uint32_t xoff = (uint32_t)lane * 16;          // Sx / Uf / BVs slots
+    // The K rows of K S for chunk c+1 are loaded at the end of chunk c (the
+    // DMA K wave lands each chunk's K within the step that issues it), so
+    // that K S starts as soon as the barrier opens the chunk.  (The state
+    // pass lands K one chunk ahead only: it loads them in the step.)
+    constexpr bool kKPre = OUT && kDelta;
+    Frag<T16> kfn[4][NKB];
+    if constexpr (kKPre) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) kfn[ti][kb] = frag_row_at<D>(Ks, roff[kb] + kRows16 * ti);
+    }
 
     for (int c = 0; c < NC; ++c) {
       const uint32_t kslot = slot(c, KR, kTileB);
@@ -1052,11 +1064,18 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
             else sh[kb].v = lds_ld<bf16x8>(Sx, a + (SXP * kb) * kWave * 16);
           }
         }
+        if constexpr (kKPre) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint32_t a = kslot + roff[kb];
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = frag_row_at<D>(Ks, a + kRows16 * ti);
+            for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = kfn[ti][kb];
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            const uint32_t a = kslot + roff[kb];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) kf[ti][kb] = frag_row_at<D>(Ks, a + kRows16 * ti);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 ks[4];
@@ -1137,6 +1156,14 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
         for (int j = 0; j < HT; ++j)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) mma_ab2(ktf[j][kb], ut[kb], S[j]);
+        if constexpr (kKPre) {
+          const uint32_t ns = slot(c + 1 < NC ? c + 1 : c, KR, kTileB);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+              kfn[ti][kb] = frag_row_at<D>(Ks, ns + roff[kb] + kRows16 * ti);
+        }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -1209,11 +1236,12 @@ __global__ __launch_bounds__(OUT ? 512 : 256) void chunk_pipe_kernel(
       if (c + KR - 1 < NC) issue_k(c + KR - 1);
       if (c + NG - 1 < NC) issue_gates(c + NG - 1);
       if (c + 1 < NC) make_bv(c + 1);
-      // Everything issued before this chunk has landed (with K one chunk
-      // ahead, this chunk's K too: it is issued before the gates).  Loads
-      // complete in issue order, so while any earlier transfer is
-      // outstanding all N of this chunk's are too.
-      if constexpr (KR == 3) {
+      // Everything issued before this chunk has landed, and this chunk's K
+      // too where it is issued one chunk ahead (the state pass) or the chain
+      // reads it early (the delta modes' output pass): it is issued before
+      // the gates.  Loads complete in issue order, so while any earlier
+      // transfer is outstanding all N of this chunk's are too.
+      if constexpr (KR == 3 && !(OUT && kDelta)) {
         if (c + NG - 1 < NC) vm_wait<NDMAK>();
         else vm_wait<0>();
       } else {
