@@ -251,7 +251,7 @@ constexpr int kTRecFrags = kTFrags;       // 16-byte lane slots per record, per 
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
-__device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int g, int n) {
+__device__ __forceinline__ void t_diag(const float* Ab, float* Df, int g, int n) {
   const float* A = Ab + bid(g, g) * 16 * LDB;
   f32x4 arow[16][4];
 #pragma unroll
@@ -272,19 +272,18 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, T16* Tb, int 
     x[r] = s0 + s1;
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    Df[g * 16 * LDB + r * LDB + n] = x[r];
-    Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)x[r];
-  }
+  for (int r = 0; r < 16; ++r) Df[g * 16 * LDB + r * LDB + n] = x[r];
 }
 
 // Blocks of T below the diagonal from the diagonal blocks D_i (Df) and A:
 //   T10 = -D1 A10 D0,  T32 = -D3 A32 D2,
 //   [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
 // (block inverse of a 2 x 2 block lower-triangular matrix, applied twice),
-// four dependent product steps.  Products split both operands.
-__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f, T16* Tb,
-                                      int g, int n) {
+// four dependent product steps.  Products split both operands.  The six
+// blocks come back in accumulator layout: tb[0..5] = T10, T32, T20, T21,
+// T30, T31 (element (4 g + e, n) of each).
+__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f,
+                                      f32x4 (&tb)[6], int g, int n) {
   auto blkA = [&](int i, int j) { return Ab + bid(i, j) * 16 * LDB; };
   auto blkD = [&](int i) { return Df + i * 16 * LDB; };
   auto dacc = [&](int i) {     // D_i in accumulator layout
@@ -326,16 +325,12 @@ __device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T
     mma_a2b2(td, frag2_from_acc<T16>(x00, x10b), y10);
     mma_a2b2(td, frag2_from_acc<T16>(x01, x11), y11);
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 4 * g + e;
-    Tb[(16 + r) * LDT + n] = (T16)t10[e];
-    Tb[(48 + r) * LDT + 32 + n] = (T16)t32[e];
-    Tb[(32 + r) * LDT + n] = (T16)(-y00[e]);
-    Tb[(32 + r) * LDT + 16 + n] = (T16)(-y01[e]);
-    Tb[(48 + r) * LDT + n] = (T16)(-y10[e]);
-    Tb[(48 + r) * LDT + 16 + n] = (T16)(-y11[e]);
-  }
+  tb[0] = t10;
+  tb[1] = t32;
+  tb[2] = -y00;
+  tb[3] = -y01;
+  tb[4] = -y10;
+  tb[5] = -y11;
 }
 
 // Gate activations of the fused prologue, from their definitions: the
@@ -404,7 +399,11 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
   __shared__ __attribute__((aligned(16))) float Ab[TS ? 10 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float Df[TS ? 4 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float T32f[TS ? 16 * LDB : 1];
-  __shared__ __attribute__((aligned(16))) T16 Tb[TS ? C * LDT : 1];
+  // The bf16 T tile that the record is gathered from takes the A blocks'
+  // place once they have been read for the last time: a third less LDS, so
+  // eight of these one-wave workgroups share a compute unit instead of five.
+  static_assert(!TS || C * LDT * sizeof(T16) <= sizeof(Ab), "T tile fits in the A blocks");
+  T16* const Tb = reinterpret_cast<T16*>(Ab);
   __shared__ __attribute__((aligned(16))) float gsh[C];               // row exponents
   __shared__ __attribute__((aligned(16))) float gcsh[PRO ? C : 1];    // column exponents
   __shared__ __attribute__((aligned(16))) float bsh[C];
@@ -492,14 +491,6 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
     gsh[lane] = gv + lkv;
     if constexpr (PRO) gcsh[lane] = gv - lkv;
     bsh[lane] = bv;
-    // the upper blocks (0, 1) and (2, 3) inside T's operand fragments are zero
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Tb[(4 * g + e) * LDT + 16 + n] = (T16)0.f;
-      Tb[(32 + 4 * g + e) * LDT + 48 + n] = (T16)0.f;
-    }
-    __syncthreads();
-
     // A blocks (R, t), t <= R: element (4 g + e, n) is row 16 R + 4 g + e,
     // column 16 t + n
 #pragma unroll
@@ -523,9 +514,30 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
       }
     }
     __syncthreads();
-    t_diag(Ab, Df, Tb, g, n);
+    t_diag(Ab, Df, g, n);
     __syncthreads();
-    t_col(Ab, Df, T32f, Tb, g, n);
+    f32x4 tb[6];
+    t_col(Ab, Df, T32f, tb, g, n);
+    __syncthreads();     // (the A blocks are read for the last time)
+    // T into its bf16 tile over the A blocks: the diagonal blocks from Df
+    // (lane (g, n): column n of block g), the six blocks below from t_col,
+    // and zeros for the upper blocks (0, 1) and (2, 3) that T's operand
+    // fragments span
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)Df[g * 16 * LDB + r * LDB + n];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      Tb[(16 + r) * LDT + n] = (T16)tb[0][e];
+      Tb[(48 + r) * LDT + 32 + n] = (T16)tb[1][e];
+      Tb[(32 + r) * LDT + n] = (T16)tb[2][e];
+      Tb[(32 + r) * LDT + 16 + n] = (T16)tb[3][e];
+      Tb[(48 + r) * LDT + n] = (T16)tb[4][e];
+      Tb[(48 + r) * LDT + 16 + n] = (T16)tb[5][e];
+      Tb[r * LDT + 16 + n] = (T16)0.f;
+      Tb[(32 + r) * LDT + 48 + n] = (T16)0.f;
+    }
     __syncthreads();
     u32x4* dst = tws + item * (kTRecFrags * kWave);
 #pragma unroll
