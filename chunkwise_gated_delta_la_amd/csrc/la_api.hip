@@ -118,6 +118,8 @@ int check_chunk_shape(int B, int H, int L, int dk, int dv, int C, int mode, int 
   if (int e = check_mode_dtype(mode, dtype)) return e;
   if (B <= 0 || H <= 0 || L <= 0 || dk <= 0 || dv <= 0 || C <= 0)
     return fail(LA_ERR_SHAPE, "B, H, L, dk, dv and C must be positive");
+  if (L > LA_MAX_TOKENS)
+    return fail(LA_ERR_SHAPE, "L must be at most LA_MAX_TOKENS, got " + std::to_string(L));
   if (dk != dv || (dk != 64 && dk != 128))
     return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd supports dk == dv in {64, 128}, got dk=" +
                                         std::to_string(dk) + " dv=" + std::to_string(dv));
@@ -212,6 +214,8 @@ int check_varlen_shape(int N, int H, int T, int dk, int dv, int C, int mode, int
   if (int e = check_mode_dtype(mode, dtype)) return e;
   if (N <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0 || C <= 0)
     return fail(LA_ERR_SHAPE, "N, H, dk, dv and C must be positive and T non-negative");
+  if (T > LA_MAX_TOKENS)
+    return fail(LA_ERR_SHAPE, "T must be at most LA_MAX_TOKENS, got " + std::to_string(T));
   if (dk != dv || (dk != 64 && dk != 128))
     return fail(LA_ERR_UNSUPPORTED, "la_chunk_fwd_varlen supports dk == dv in {64, 128}, got "
                                     "dk=" + std::to_string(dk) + " dv=" + std::to_string(dv));

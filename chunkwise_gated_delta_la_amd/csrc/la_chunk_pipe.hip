@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "la_device.hpp"
+#include "la_index.hpp"
 #include "la_kernels.hpp"
 
 namespace la {
@@ -81,27 +82,9 @@ __device__ __forceinline__ bf16x4 read_tr(const void* base, uint32_t off) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-// Unit key of row r of a C x D tile: logical 16-byte unit u of the row is
-// stored at position u ^ key(r).  Operand-row reads (16 lanes on 16
-// consecutive rows, one unit each) need key to be one-to-one on those rows;
-// transposed reads (16 lanes on 4 consecutive rows 4 g .. 4 g + 3, units
-// 4 kb + 0..3) need its bits above the unit's low two to follow r mod 4.
-template <int D>
-__device__ __forceinline__ constexpr int swz_key(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
-                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
-
-// Byte offset of logical unit u of row r.
-template <int D>
-__device__ __forceinline__ constexpr uint32_t unit_off(int r, int u) {
-  return (uint32_t)(2 * r * D + ((u ^ swz_key<D>(r)) << 4));
-}
-
-// dk index held by register row p of the state.
-__device__ __forceinline__ constexpr int dk_of_row(int p) {
-  return (p & ~31) | ((p & 12) << 1) | ((p & 16) >> 2) | (p & 3);
-}
+// The tile swizzle (swz_key, unit_off), the state-row order (dk_of_row)
+// and the transposed-read offsets are in la_index.hpp, shared with the host
+// checker of the index maps.
 
 // Operand row R over dk block kb: the unit 4 kb + g (the key depends only on
 // R's low four bits, so 16-row steps are a constant 32 D bytes).
@@ -113,17 +96,12 @@ __device__ __forceinline__ Frag<T16> frag_row_at(const void* tile, uint32_t off)
 }
 
 // Transposed K operand over token rows r0 + kidx(g, j) for state tile
-// tj = 2 kbs + h: lane (g, n) gets K[r0 + kidx(g, j)][dk_of_row(16 tj + n)].
-// Lane k of group g addresses row r0 + 4 g + k / 4 (+ 16) at the four
-// columns 32 kbs + 8 (k % 4) + 4 h .. + 3, so lane n receives element n % 4
-// of the runs of lanes n / 4 + 4 j: column 32 kbs + 8 (n / 4) + 4 h + n % 4.
-// tr_off gives the lane's offset for r0 = 0, h = 0; r0 adds 2 D r0 bytes,
-// h adds 8.
-template <int D>
-__device__ __forceinline__ uint32_t tr_off(int g, int n, int kbs) {
-  return unit_off<D>(4 * g + (n >> 2), 4 * kbs + (n & 3));
-}
-
+// tj = 2 kbs + h: lane (g, n) gets K[r0 + kidx(g, j)][dk_of_row(16 tj + n)],
+// kidx(g, j) = 4 g + j for j < 4 and 16 + 4 g + j - 4 above (the order in
+// which an accumulator pair gives its rows).  Lane k of group g addresses
+// row r0 + 4 g + k / 4 (+ 16) at the four columns 32 kbs + 8 (k % 4) + 4 h
+// .. + 3 (tr_off), so lane n receives element n % 4 of the runs of lanes
+// n / 4 + 4 j: column 32 kbs + 8 (n / 4) + 4 h + n % 4.
 __device__ __forceinline__ Frag<T16> frag_tr_at(const void* tile, uint32_t off, uint32_t half) {
   Frag<T16> f;
   const bf16x4 a = read_tr(tile, off);
@@ -135,15 +113,11 @@ __device__ __forceinline__ Frag<T16> frag_tr_at(const void* tile, uint32_t off, 
 // Column n of a plain C x 16 bf16 tile (this workgroup's V columns) as an
 // operand over rows r0 .. r0 + 31.
 __device__ __forceinline__ Frag<T16> frag_col_tr_v(const void* tile, int r0, int g, int n) {
-  const uint32_t off = (uint32_t)(((r0 + 4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
-  return frag_tr_at(tile, off, 16 * 16 * 2);
+  return frag_tr_at(tile, col_tr_off(r0, g, n), 16 * 16 * 2);
 }
 
 // V in accumulator layout for rows 16 ti + 4 g + i, column n: off is the
 // lane's byte offset for ti = 0 (vacc_off), ti adds 512 bytes.
-__device__ __forceinline__ uint32_t vacc_off(int g, int n) {
-  return (uint32_t)(((4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
-}
 __device__ __forceinline__ f32x4 v_acc_at(const void* tile, uint32_t off) {
   const bf16x4 a = read_tr(tile, off);
   return f32x4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
@@ -174,9 +148,6 @@ __device__ __forceinline__ Frag2<T16> frag2_blk32(const float* p0, const float* 
   }
   return f;
 }
-
-// Index of the lower 16 x 16 block (i, j), i >= j, in the compact A store.
-__device__ __forceinline__ constexpr int bid(int i, int j) { return i * (i + 1) / 2 + j; }
 
 
 // ---------------------------------------------------------------- DMA loads
@@ -222,13 +193,8 @@ __device__ __forceinline__ void vm_wait() {
 template <int D>
 __device__ __forceinline__ void dma_tile_offsets(uint32_t (&off)[C * 2 * D / 1024], int lane,
                                                  int nrows) {
-  constexpr int RB = 2 * D;
 #pragma unroll
-  for (int m = 0; m < C * RB / 1024; ++m) {
-    const int byte = 1024 * m + 16 * lane;
-    const int r = byte / RB, ul = (byte % RB) / 16;
-    off[m] = (uint32_t)(min(r, nrows - 1) * RB + ((ul ^ swz_key<D>(r)) << 4));
-  }
+  for (int m = 0; m < C * 2 * D / 1024; ++m) off[m] = dma_src_off<D>(m, lane, nrows);
 }
 
 template <int D>
@@ -242,12 +208,10 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows,
 
 // ---------------------------------------------------------------- T solve
 
-// Fragment index of the T operand (row tile ti, 32-deep block kb), kb <= ti / 2.
-// A record holds the kTFrags fragments of bf16(T): T enters U_new = T R as a
-// single bf16 (its rounding costs well under the tolerance; R is split).
-__device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
-constexpr int kTFrags = 6;
-constexpr int kTRecFrags = kTFrags;       // 16-byte lane slots per record, per lane
+// A T record holds the kTFrags fragments of bf16(T), fragment tfi(ti, kb)
+// for row tile ti and 32-deep block kb <= ti / 2 (la_index.hpp): T enters
+// U_new = T R as a single bf16 (its rounding costs well under the
+// tolerance; R is split).
 
 // Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
 // g by forward substitution; the block's rows are loaded first.
@@ -2252,7 +2216,7 @@ ProArrays pro_arrays(const ChunkArgs& a) {
 int plan_segments(const ChunkArgs& a) {
   if (!a.in_bf16 || a.cu) return 1;
   const long chains = (long)a.B * a.H * (a.d / 16);
-  const int nc = (a.L + C - 1) / C;
+  const long nc = ((long)a.L + C - 1) / C;
   const long cus = kComputeUnits;
   const double whole = (double)((chains + cus - 1) / cus) * nc;
   double best = whole;

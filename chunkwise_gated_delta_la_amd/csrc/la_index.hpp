@@ -1,0 +1,87 @@
+// Index maps of the chunk kernels' LDS tiles and register fragments: pure
+// integer functions, compiled for the device (the kernels) and for the host
+// (tests/native/index_check.cpp, which simulates the transfers and reads
+// that use them and checks every lane against the element it must get).
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 used throughout: lane
+// l = 16 g + n holds row (A) or column (B) n and the eight k indices
+// 8 g .. 8 g + 7 of a 32-deep block; an accumulator tile holds rows
+// 4 g + i, i = 0..3, of column n.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kTileC = 64;        // rows of a chunk tile (the chunk size)
+
+// Unit key of row r of a C x D bf16 tile: logical 16-byte unit u of the row
+// is stored at position u ^ key(r).  Operand-row reads (16 lanes on 16
+// consecutive rows, one unit each) need key to be one-to-one on those rows;
+// transposed reads (16 lanes on 4 consecutive rows 4 g .. 4 g + 3, units
+// 4 kb + 0..3) need its bits above the unit's low two to follow r mod 4.
+template <int D>
+__host__ __device__ __forceinline__ constexpr int swz_key(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset of logical unit u of row r in a swizzled tile.
+template <int D>
+__host__ __device__ __forceinline__ constexpr uint32_t unit_off(int r, int u) {
+  return (uint32_t)(2 * r * D + ((u ^ swz_key<D>(r)) << 4));
+}
+
+// dk index held by register row p of the state: register row
+// p = 32 kb + 16 h + 4 g + j holds dk index 32 kb + 8 g + 4 h + j.
+__host__ __device__ __forceinline__ constexpr int dk_of_row(int p) {
+  return (p & ~31) | ((p & 12) << 1) | ((p & 16) >> 2) | (p & 3);
+}
+
+// Lane offset of the transposed K operand over token rows 0..3 (+ 16) for
+// the state tiles 2 kbs + h: lane k of group g addresses row 4 g + k / 4 at
+// the four columns 32 kbs + 8 (k % 4) .. + 3; h adds 8 bytes, a token-row
+// offset r0 adds 2 D r0 bytes.
+template <int D>
+__host__ __device__ __forceinline__ constexpr uint32_t tr_off(int g, int n, int kbs) {
+  return unit_off<D>(4 * g + (n >> 2), 4 * kbs + (n & 3));
+}
+
+// Lane offset into a plain C x 16 bf16 tile (row pitch 32 bytes) of the
+// transposed read that gives column n over rows r0 + 4 g + 0..3: lane k of
+// group g addresses row r0 + 4 g + k / 4 at columns 4 (k % 4) .. + 3.
+__host__ __device__ __forceinline__ constexpr uint32_t col_tr_off(int r0, int g, int n) {
+  return (uint32_t)(((r0 + 4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
+}
+
+// The same for r0 = 0: V in accumulator layout (rows 16 ti + 4 g + i,
+// column n) from row tile ti at 512 ti bytes further.
+__host__ __device__ __forceinline__ constexpr uint32_t vacc_off(int g, int n) {
+  return (uint32_t)(((4 * g + (n >> 2)) * 16 + 4 * (n & 3)) * 2);
+}
+
+// Source byte offset, within the C rows of a tile in memory (row pitch 2 D
+// bytes), of what lane `lane` of DMA instruction m moves: each instruction
+// moves 1 KiB into LDS bytes 1024 m + 16 lane, i.e. row r, stored position
+// ul, which holds logical unit ul ^ key(r).  Rows at or past nrows read the
+// last valid row.
+template <int D>
+__host__ __device__ __forceinline__ constexpr uint32_t dma_src_off(int m, int lane, int nrows) {
+  const int byte = 1024 * m + 16 * lane;
+  const int r = byte / (2 * D), ul = (byte % (2 * D)) / 16;
+  const int rs = r < nrows - 1 ? r : nrows - 1;
+  return (uint32_t)(rs * (2 * D) + ((ul ^ swz_key<D>(r)) << 4));
+}
+
+// Index of the lower 16 x 16 block (i, j), i >= j, in a compact store of the
+// lower blocks of a 64 x 64 matrix.
+__host__ __device__ __forceinline__ constexpr int bid(int i, int j) { return i * (i + 1) / 2 + j; }
+
+// Fragment index of the T operand (row tile ti, 32-deep block kb),
+// kb <= ti / 2: a record holds the kTFrags fragments of bf16(T).
+__host__ __device__ __forceinline__ constexpr int tfi(int ti, int kb) { return ti < 2 ? ti : 2 * ti - 2 + kb; }
+constexpr int kTFrags = 6;
+constexpr int kTRecFrags = kTFrags;       // 16-byte lane slots per record, per lane
+
+}  // namespace la

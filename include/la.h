@@ -121,10 +121,16 @@ typedef struct {
   float norm_eps;            /* LA_EPI_OUT_NORM: > 0                       */
 } la_fused_opts_t;
 
+/* Longest sequence (L) or packed batch (T), in tokens, that any entry point
+ * takes: 2^31 - 1025, so that a length rounded up to the largest row block
+ * the kernels walk (1024 tokens) still fits a 32-bit signed index. */
+#define LA_MAX_TOKENS 2147482623
+
 typedef enum {
   LA_OK = 0,
   LA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  LA_ERR_SHAPE = 2,       /* non-positive size, or sizes past the grid limit */
+  LA_ERR_SHAPE = 2,       /* non-positive size, sizes past the grid limit,
+                             or a length above LA_MAX_TOKENS             */
   LA_ERR_UNSUPPORTED = 3, /* (dk, dv, C, dtype, mode) outside the built set  */
   LA_ERR_ALIAS = 4,       /* an output overlaps an input (see each call)     */
   LA_ERR_HIP = 5,         /* HIP launch failure                              */
