@@ -70,6 +70,13 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int LDC = C + 4;     // row pitch of float C x C tiles in LDS
 constexpr int LDX = 20;        // row pitch of float 16-column tiles in LDS
+// The walks: two chain waves (one per half of the state's rows) and the
+// staging waves
+constexpr int kWalkChain = 2 * kWave;
+constexpr int kStatesStage = 128;              // staging threads of the forward walk
+constexpr int kRevStage = 128;                 // and of the reverse walk
+constexpr int kStatesThreads = kWalkChain + kStatesStage;
+constexpr int kRevThreads = kWalkChain + kRevStage;
 
 // Per-chunk arrays are indexed by the chunk's slot: bh * NC + c for the
 // fixed-length layout, the forward's packed-batch slots (SeqMap) otherwise
@@ -342,16 +349,35 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
   }
 }
 
+// The K^T operand of a walk's state update (state tile tj, token block kb)
+// from the row-major K tile in LDS (row pitch LD elements): lane (g, n)
+// gets K[32 kb + kidx(g, j)][16 tj + n].  For bf16, two transposed reads
+// (ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element i % 4 of the 4-element runs addressed by lanes i / 4 + 4 j), lane
+// k of group g addressing row 32 kb + 4 g + k / 4 (then 16 rows further) at
+// the columns 16 tj + 4 (k % 4) .. + 3; for float, a strided column read.
+typedef short bwd_s16x4 __attribute__((ext_vector_type(4)));
+template <typename T, int LD>
+__device__ __forceinline__ Frag<T> frag_kt(const T* Kt, int kb, int tj, int g, int n) {
+  if constexpr (IsBf16<T>::value) {
+    typedef __attribute__((address_space(3))) bwd_s16x4 lds_s16x4;
+    const T* p = Kt + (32 * kb + 4 * g + (n >> 2)) * LD + 16 * tj + 4 * (n & 3);
+    const bwd_s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const bwd_s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * LD));
+    Frag<T> f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    return f;
+  } else {
+    return frag_col(Kt + 32 * kb * LD + 16 * tj + n, LD, g);
+  }
+}
+
 // The chain operands of one chunk -- K rows, T (erase modes), 16 columns of
 // V (forward walk), the decays (as exp(g) and exp(g_C - g)) and beta -- read
-// by the 192 threads of the
-// three staging waves in one batch (every load issued, at clamped indices,
-// before the first LDS write), then written to one half of the walk's
-// double buffer.  Rows past the end of the sequence read as zero.
-//
-// With KT (bf16) the staging also writes K^T ([D][C + 4]) for the chain's
-// K^T operands: each thread loads the same 16 bytes of two consecutive rows
-// and writes the transposed pairs as 32-bit words.
+// by the NT threads of the staging waves in one batch (every load issued,
+// at clamped indices, before the first LDS write), then written to one half
+// of the walk's double buffer.  Rows past the end of the sequence read as
+// zero.
 //
 // With TS (the reverse walk) T comes as T^T in SplitMat form: for bf16 its
 // hi and lo planes are staged as two bf16 [C][C + 8] tiles, the chain's
@@ -359,18 +385,14 @@ __device__ __forceinline__ void tile_of_block(int b, int BH, int NCT, int& bh, i
 //
 // With SPL (the forward walk, bf16) T comes as float rows and is split into
 // the same bf16 hi and lo planes on its way into LDS.
-template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X = false, bool KT = false,
-          bool TS = false, bool SPL = false>
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X, bool TS, bool SPL, int NT_>
 struct ChunkStage {
-  static constexpr int NT = kThreads - kWave;
+  static constexpr int NT = NT_;
   static constexpr int PE = 16 / sizeof(T);
   static constexpr int LDK = D + PE;
-  static constexpr int LDKT = C + 4;              // row pitch of K^T (KT)
   static constexpr int VPR = D / PE;
   static constexpr int NK = C * VPR;
-  static constexpr int NPK = NK / 2;              // row-pair items (KT)
-  static constexpr int IP = (NPK + NT - 1) / NT;
-  static constexpr int IK = KT ? 2 * IP : (NK + NT - 1) / NT;
+  static constexpr int IK = (NK + NT - 1) / NT;
   static constexpr int NTV = C * C / 4;          // 16-byte vectors of T (either form)
   static constexpr bool kTPlanes = TS && IsBf16<T>::value;
   static constexpr bool kTSplit = SPL && IsBf16<T>::value;
@@ -411,25 +433,12 @@ struct ChunkStage {
                                                 4 * (p % (D / 4)));
       }
     }
-    if constexpr (KT) {
 #pragma unroll
-      for (int i = 0; i < IP; ++i) {
-        const int p = min(t + i * NT, NPK - 1), r = 2 * (p / VPR), cv = p % VPR;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(
-              k + (row0 + min(r + h, nrows - 1)) * D + cv * PE);
-          kx[2 * i + h] = r + h < nrows ? x : z;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < IK; ++i) {
-        const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
-        const u32x4 x =
-            *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
-        kx[i] = r < nrows ? x : z;
-      }
+    for (int i = 0; i < IK; ++i) {
+      const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
+      const u32x4 x =
+          *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
+      kx[i] = r < nrows ? x : z;
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -465,7 +474,7 @@ struct ChunkStage {
 
   __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* fsb,
                                         float* bsb, int t, float* X1b = nullptr,
-                                        float* X2b = nullptr, T* KTb = nullptr) const {
+                                        float* X2b = nullptr) const {
     if constexpr (WITH_X) {
 #pragma unroll
       for (int i = 0; i < IX1; ++i) {
@@ -480,31 +489,10 @@ struct ChunkStage {
           *reinterpret_cast<f32x4*>(X2b + (p / (D / 4)) * (D + 4) + 4 * (p % (D / 4))) = x2[i];
       }
     }
-    if constexpr (KT) {
 #pragma unroll
-      for (int i = 0; i < IP; ++i) {
-        const int p = t + i * NT;
-        if (p < NPK) {
-          const int r = 2 * (p / VPR), c0 = (p % VPR) * PE;
-          *reinterpret_cast<u32x4*>(Kb + r * LDK + c0) = kx[2 * i];
-          *reinterpret_cast<u32x4*>(Kb + (r + 1) * LDK + c0) = kx[2 * i + 1];
-          const u32x4 a = kx[2 * i], b = kx[2 * i + 1];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // elements 2w, 2w + 1 of both rows: (a lo, b lo), (a hi, b hi)
-            const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
-            const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
-            *reinterpret_cast<uint32_t*>(KTb + (c0 + 2 * w) * LDKT + r) = lo;
-            *reinterpret_cast<uint32_t*>(KTb + (c0 + 2 * w + 1) * LDKT + r) = hi;
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < IK; ++i) {
-        const int p = t + i * NT;
-        if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
-      }
+    for (int i = 0; i < IK; ++i) {
+      const int p = t + i * NT;
+      if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -756,8 +744,14 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 }
 
 // ------------------------------------------------------- forward walk
+// Five waves, as in the reverse walk: waves 0 and 1 carry the state, each
+// on half of its rows (dk), and form the whole K S (the other half's rows
+// from the float tile of the state entering the chunk, which both hand to
+// the staging waves), R and U = T R (T lower triangular: row tiles 0 and 1
+// skip the block above the diagonal, exact zeros), then update only their
+// rows; waves 2-4 stage the operands and store S and U.
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_states_kernel(
+__global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ S0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
@@ -765,19 +759,19 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   constexpr int PE = 16 / sizeof(T);
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
+  constexpr int HT = NKT / 2, HB = NKB / 2;      // of one chain half
 
-  // bf16: K^T staged transposed for the chain's K^T operands, and T as its
-  // bf16 hi and lo planes [C][C + 8]
-  constexpr bool kKt = IsBf16<T>::value;
-  constexpr int LDKT = C + 4;
+  // bf16: T as its bf16 hi and lo planes [C][C + 8]
   constexpr bool kTPlanes = IsBf16<T>::value;
   constexpr int LDTT = C + 8;
   constexpr int kTWords = kTPlanes ? C * LDTT : C * LDC;   // floats per buffer
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
-  __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? kTWords : 4];
   __shared__ __attribute__((aligned(16))) float Vb[2][C * LDX];
-  __shared__ __attribute__((aligned(16))) float SxT[2][16 * (D + 4)];            // S entering
+  // the state entering chunk c in slot c % 3: written by the chain halves
+  // at the end of step c - 1, read by the other half in step c, stored in
+  // step c + 1
+  __shared__ __attribute__((aligned(16))) float SxT[3][16 * (D + 4)];
   __shared__ __attribute__((aligned(16))) float UxT[2][kErase ? 16 * (C + 4) : 4];  // U
   __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
@@ -794,32 +788,36 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   const int NC = (L + C - 1) / C;
   if (NC == 0) return;                         // nothing to store
 
-  // Waves 1-3 stage the chain's operands: chunk c's loads go out during the
-  // step two before its use and land in LDS during the step before it (the
-  // barriers wait for LDS traffic only, so the loads stay in flight).
-  ChunkStage<T, D, kErase, true, false, kKt, false, true> st;
+  // The staging waves stage the chain's operands: chunk c's loads go out
+  // during the step two before its use and land in LDS during the step
+  // before it (the barriers wait for LDS traffic only, so the loads stay in
+  // flight).
+  ChunkStage<T, D, kErase, true, false, false, true, kStatesStage> st;
+  const int ts = tid - kWalkChain;             // staging thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
     const size_t cid = si.slot0 + c;
     st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
-            tid - kWave);
+            ts);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tid - kWave, nullptr,
-             nullptr, KTb[b]);
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], ts);
   };
 
-  f32x4 S[NKT];
-  if (wave == 0) {
+  const int h = wave;                          // chain half (waves 0, 1)
+  f32x4 S[HT];                                 // rows 16 (h HT + j) + 4 g + e
+  if (wave < 2) {
     const size_t sb = (size_t)bh * D * D;
 #pragma unroll
-    for (int tj = 0; tj < NKT; ++tj)
+    for (int j = 0; j < HT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S[tj][e] = S0 ? S0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
-  }
-  if (wave != 0) {
+        S[j][e] = S0 ? S0[sb + (size_t)(16 * (h * HT + j) + 4 * g + e) * D + col0 + n] : 0.f;
+#pragma unroll
+    for (int j = 0; j < HT; ++j)
+      *reinterpret_cast<f32x4*>(&SxT[0][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) = S[j];
+  } else {
     load(0);
     store(0);
     load(min(1, NC - 1));
@@ -828,18 +826,15 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
 
   // each role runs its own loop (one barrier per chunk in both), so the
   // staging loads meet no other role's registers and are not waited for early
-  if (wave != 0) {
+  if (wave >= 2) {
     // the state and U tiles of chunk c, handed over by the chain, go to the
     // workspace during the next step
     const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
     const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
     auto flush = [&](int c) {
-      const int b = c & 1;
-      tile_flush<T, D, D>(SxT[b], Se, (si.slot0 + c) * D * D + col0, tid - kWave,
-                          kThreads - kWave);
+      tile_flush<T, D, D>(SxT[c % 3], Se, (si.slot0 + c) * D * D + col0, ts, kStatesStage);
       if constexpr (kErase)
-        tile_flush<T, D, C>(UxT[b], Um, (si.slot0 + c) * C * D + col0,
-                            tid - kWave, kThreads - kWave);
+        tile_flush<T, D, C>(UxT[c & 1], Um, (si.slot0 + c) * C * D + col0, ts, kStatesStage);
     };
     for (int c = 0; c < NC; ++c) {
       if (c >= 1) flush(c - 1);
@@ -853,7 +848,6 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
     {
-      tile_put<D>(SxT[b], S, g, n);
       const float* gmc = gsb[b];     // exp(g)
       const float* fc = fsb[b];      // exp(g_C - g)
       const float gamC = kGated ? gmc[C - 1] : 1.f;
@@ -871,9 +865,20 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
       }
       Frag2<T> bX[2];
       if constexpr (kErase) {
+        // S split over dk: this half's rows from registers, the other's from
+        // the tile it wrote at the end of the last step (register arrays
+        // only ever indexed by compile-time values)
         Frag2<T> bS[NKB];
+        const float* xo = SxT[c % 3] + n * (D + 4) + 4 * g;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) bS[kb] = frag2_from_acc<T>(S[2 * kb], S[2 * kb + 1]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (kb / HB == h) {
+            bS[kb] = frag2_from_acc<T>(S[2 * (kb % HB)], S[2 * (kb % HB) + 1]);
+          } else {
+            bS[kb] = frag2_from_acc<T>(*reinterpret_cast<const f32x4*>(xo + 32 * kb),
+                                       *reinterpret_cast<const f32x4*>(xo + 32 * kb + 16));
+          }
+        }
         f32x4 R[4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
@@ -894,8 +899,8 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
         for (int ti = 0; ti < 4; ++ti) {
           U[ti] = zero4();
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-          {
+          for (int kb = 0; kb < 2; ++kb) {
+            if (kb > ti / 2) continue;      // T is zero above the diagonal blocks
             Frag2<T> at;
             if constexpr (kTPlanes) {
               const T* tp = reinterpret_cast<const T*>(Tb[b]) + (16 * ti + n) * LDTT + 32 * kb;
@@ -907,7 +912,11 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
             mma_a2b2(at, bR[kb], U[ti]);
           }
         }
-        tile_put<C>(UxT[b], U, g, n);
+        // each half hands over two of the four row tiles of U
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<f32x4*>(&UxT[b][n * (C + 4) + 16 * (2 * h + t) + 4 * g]) =
+              h == 0 ? U[t] : U[2 + t];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           bX[kb] = frag2_from_acc_scaled<T>(U[2 * kb], U[2 * kb + 1], flo[kb], fhi[kb]);
@@ -923,25 +932,37 @@ __global__ __launch_bounds__(kThreads) void bwd_states_kernel(
           bX[kb] = frag2_from_acc_scaled<T>(vlo, vhi, flo[kb], fhi[kb]);
         }
       }
-      // S <- gam_C S + K^T diag(f) U
+      // S <- gam_C S + K^T diag(f) U, this half's rows
 #pragma unroll
-      for (int tj = 0; tj < NKT; ++tj) {
+      for (int j = 0; j < HT; ++j) {
+        const int tj = h * HT + j;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[tj][e] *= gamC;
+        for (int e = 0; e < 4; ++e) S[j][e] *= gamC;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mma_ab2(kKt ? frag_row(&KTb[b][(16 * tj + n) * LDKT + 32 * kb], g)
-                      : frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g),
-                  bX[kb], S[tj]);
+        for (int kb = 0; kb < 2; ++kb) mma_ab2(frag_kt<T, LDK>(Kb[b], kb, tj, g, n), bX[kb], S[j]);
       }
+      // this half's rows of the state entering the next chunk (after the last
+      // chunk into a slot no one reads: no branch in the loop body)
+#pragma unroll
+      for (int j = 0; j < HT; ++j)
+        *reinterpret_cast<f32x4*>(&SxT[(c + 1) % 3][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) =
+            S[j];
     }
     __syncthreads();
   }
 }
 
 // ------------------------------------------------------- reverse walk
+// Five waves: waves 0 and 1 carry the chain, each on half of the state
+// gradient's rows (dk); waves 2-4 stage the operands and store the results.
+// Each chain half forms the whole dU = X1 + diag(f) K dS' and dR = T^T dU
+// (dS' from its own rows in registers and the other half's from the float
+// tile both hand to the staging waves) and updates only its rows of dS; the
+// two never wait for each other inside a chunk.  T^T is upper triangular,
+// so its row tiles 2 and 3 skip the 32-deep block below the diagonal (exact
+// zeros: the sums are unchanged).
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
+__global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
     const T* __restrict__ k, const float* __restrict__ beta, const float* __restrict__ dS_final,
     float* __restrict__ dv_out, float* __restrict__ dS0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
@@ -949,20 +970,20 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   constexpr int PE = 16 / sizeof(T);
   constexpr int LDK = D + PE;
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
+  constexpr int HT = NKT / 2, HB = NKB / 2;      // of one chain half
 
-  constexpr bool kKt = false;     // (no room for a transposed K next to the T^T planes)
-  constexpr int LDKT = C + 4;
   constexpr bool kTPlanes = IsBf16<T>::value;
   constexpr int LDTT = C + 8;
   // T^T: bf16 hi and lo planes [C][C + 8] (bf16 inputs) or float [C][C + 4]
   constexpr int kTWords = kTPlanes ? C * LDTT : C * LDC;   // floats per buffer
   __shared__ __attribute__((aligned(16))) T Kb[2][C * LDK];
-  __shared__ __attribute__((aligned(16))) T KTb[2][kKt ? D * LDKT : PE];
   __shared__ __attribute__((aligned(16))) float Tb[2][kErase ? kTWords : 4];
   // 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO, transposed
   __shared__ __attribute__((aligned(16))) float X1[2][16 * (C + 4)];
   __shared__ __attribute__((aligned(16))) float X2[2][16 * (D + 4)];
-  __shared__ __attribute__((aligned(16))) float dSxT[2][16 * (D + 4)];             // dS'
+  // dS' entering step s in slot s % 3: written by the chain halves at the end
+  // of step s - 1, read by the other half in step s, stored in step s + 1
+  __shared__ __attribute__((aligned(16))) float dSxT[3][16 * (D + 4)];
   __shared__ __attribute__((aligned(16))) float dRxT[2][kErase ? 16 * (C + 4) : 4];  // dR
   // dv (beta dR, or dU) handed over like dR where LDS allows (not float at
   // d = 128: the chain stores it itself there)
@@ -996,10 +1017,12 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
     return;
   }
 
-  // Waves 1-3 stage the chain's operands of each chunk -- K, T, the gates and
-  // the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO (formed
-  // in parallel beforehand) -- two chunks ahead, as in the forward walk.
-  ChunkStage<T, D, kErase, false, true, kKt, true> st;
+  // The staging waves stage the chain's operands of each chunk -- K, T, the
+  // gates and the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO
+  // (formed in parallel beforehand) -- two chunks ahead, as in the forward
+  // walk.
+  ChunkStage<T, D, kErase, false, true, true, false, kRevStage> st;
+  const int ts = tid - kWalkChain;             // staging thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -1012,46 +1035,48 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
       tl = Tt.p + Tt.plane + cid * C * C;
     }
     st.load(k, nullptr, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr,
-            ws.g + cid * C, row0, nrows, col0, tid - kWave, ws.X1 + cid * C * D,
+            ws.g + cid * C, row0, nrows, col0, ts, ws.X1 + cid * C * D,
             ws.X2 + cid * D * D, th, tl);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tid - kWave, X1[b],
-             X2[b], KTb[b]);
+    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], ts, X1[b], X2[b]);
   };
 
-  f32x4 dS[NKT];
-  if (wave == 0) {
+  const int h = wave;                          // chain half (waves 0, 1)
+  f32x4 dS[HT];                                // rows 16 (h HT + j) + 4 g + e
+  if (wave < 2) {
     const size_t sb = (size_t)bh * D * D;
 #pragma unroll
-    for (int tj = 0; tj < NKT; ++tj)
+    for (int j = 0; j < HT; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        dS[tj][e] = dS_final ? dS_final[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] : 0.f;
-  }
-  if (wave != 0) {
+        dS[j][e] = dS_final
+                       ? dS_final[sb + (size_t)(16 * (h * HT + j) + 4 * g + e) * D + col0 + n]
+                       : 0.f;
+#pragma unroll
+    for (int j = 0; j < HT; ++j)
+      *reinterpret_cast<f32x4*>(&dSxT[0][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) = dS[j];
+  } else {
     load(NC - 1);
     store(0);
     load(max(NC - 2, 0));
   }
   __syncthreads();
-  if (wave != 0) {
+  if (wave >= 2) {
     // dS' and dR of the chunk of step s, handed over by the chain, go to the
     // workspace during step s + 1
     const SplitMat<T> dSe = SplitMat<T>::make(ws.dSx, ws.nS);
     const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
     auto flush = [&](int s) {
       const int c = NC - 1 - s, b = s & 1;
-      tile_flush<T, D, D>(dSxT[b], dSe, (si.slot0 + c) * D * D + col0, tid - kWave,
-                          kThreads - kWave);
+      tile_flush<T, D, D>(dSxT[s % 3], dSe, (si.slot0 + c) * D * D + col0, ts, kRevStage);
       if constexpr (kErase)
-        tile_flush<T, D, C>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0,
-                            tid - kWave, kThreads - kWave);
+        tile_flush<T, D, C>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0, ts, kRevStage);
       if constexpr (kDvTile) {
         // dv rows of the chunk (those inside the sequence), 8 columns a thread
         const int nrows = min(C, L - c * C);
         float* dvc = dv_out + (si.row0 + (size_t)c * C) * D + col0;
-        for (int p = tid - kWave; p < 2 * C; p += kThreads - kWave) {
+        for (int p = ts; p < 2 * C; p += kRevStage) {
           const int r = p / 2, c0 = 8 * (p % 2);
           if (r < nrows) {
             float x[8];
@@ -1077,15 +1102,25 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
   for (int s = 0; s < NC; ++s) {
     const int c = NC - 1 - s, b = s & 1;
     {
-      tile_put<D>(dSxT[b], dS, g, n);
       const float* gmc = gsb[b];     // exp(g)
       const float* fc = fsb[b];      // exp(g_C - g)
       const float gamC = kGated ? gmc[C - 1] : 1.f;
       const int nrows = min(C, L - c * C);
       const size_t row0 = si.row0 + (size_t)c * C;
+      // dS' split over dk: this half's rows from registers, the other's from
+      // the tile it wrote at the end of the last step (register arrays only
+      // ever indexed by compile-time values)
       Frag2<T> bS[NKB];
+      const float* xo = dSxT[s % 3] + n * (D + 4) + 4 * g;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) bS[kb] = frag2_from_acc<T>(dS[2 * kb], dS[2 * kb + 1]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        if (kb / HB == h) {
+          bS[kb] = frag2_from_acc<T>(dS[2 * (kb % HB)], dS[2 * (kb % HB) + 1]);
+        } else {
+          bS[kb] = frag2_from_acc<T>(*reinterpret_cast<const f32x4*>(xo + 32 * kb),
+                                     *reinterpret_cast<const f32x4*>(xo + 32 * kb + 16));
+        }
+      }
       // dU = P^T dO + diag(f) K dS'
       f32x4 dU[4];
 #pragma unroll
@@ -1100,16 +1135,31 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
         for (int e = 0; e < 4; ++e) dU[ti][e] = x1[e] + (kGated ? fr[e] : 1.f) * y[e];
       }
       float* dvo = dv_out + row0 * D + col0 + n;
+      // each half hands over (or stores) two of the four row tiles of dv and dR
+      auto hand = [&](float* X, const f32x4 (&v)[4]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<f32x4*>(X + n * (C + 4) + 16 * (2 * h + t) + 4 * g) =
+              h == 0 ? v[t] : v[2 + t];
+      };
+      auto store_dv = [&](const f32x4 (&v)[4]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * (2 * h + t) + 4 * g + e;
+            if (r < nrows) dvo[(size_t)r * D] = h == 0 ? v[t][e] : v[2 + t][e];
+          }
+      };
       if constexpr (kErase) {
         const Frag2<T> bU[2] = {frag2_from_acc<T>(dU[0], dU[1]), frag2_from_acc<T>(dU[2], dU[3])};
         f32x4 dR[4];
-
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           dR[ti] = zero4();
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-          {
+          for (int kb = 0; kb < 2; ++kb) {
+            if (kb < ti / 2) continue;      // T^T is zero below the diagonal blocks
             Frag2<T> at;
             if constexpr (kTPlanes) {
               const T* tp = reinterpret_cast<const T*>(Tb[b]) + (16 * ti + n) * LDTT + 32 * kb;
@@ -1121,26 +1171,18 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
             mma_a2b2(at, bU[kb], dR[ti]);
           }
         }
-        tile_put<C>(dRxT[b], dR, g, n);
-        if constexpr (kDvTile) {
-          f32x4 dvv[4];
+        hand(dRxT[b], dR);
+        f32x4 dvv[4];
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) {
-            const f32x4 br = *reinterpret_cast<const f32x4*>(&bsb[b][16 * ti + 4 * g]);
+        for (int ti = 0; ti < 4; ++ti) {
+          const f32x4 br = *reinterpret_cast<const f32x4*>(&bsb[b][16 * ti + 4 * g]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dvv[ti][e] = br[e] * dR[ti][e];
-          }
-          tile_put<C>(dvxT[b], dvv, g, n);
-        } else {
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * ti + 4 * g + e;
-              if (r < nrows) dvo[(size_t)r * D] = bsb[b][r] * dR[ti][e];
-            }
+          for (int e = 0; e < 4; ++e) dvv[ti][e] = br[e] * dR[ti][e];
         }
-        // dS <- gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR
+        if constexpr (kDvTile) hand(dvxT[b], dvv);
+        else store_dv(dvv);
+        // dS <- gam_C dS' + Q^T diag(gam) dO - K^T diag(beta gam) dR, this
+        // half's rows
         Frag2<T> bR[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -1154,46 +1196,43 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_kernel(
           bR[kb] = frag2_from_acc_scaled<T>(dR[2 * kb], dR[2 * kb + 1], slo, shi);
         }
 #pragma unroll
-        for (int tj = 0; tj < NKT; ++tj) {
+        for (int j = 0; j < HT; ++j) {
+          const int tj = h * HT + j;
           {
             const f32x4 x2 = *reinterpret_cast<const f32x4*>(&X2[b][n * (D + 4) + 16 * tj + 4 * g]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dS[tj][e] = gamC * dS[tj][e] + x2[e];
+            for (int e = 0; e < 4; ++e) dS[j][e] = gamC * dS[j][e] + x2[e];
           }
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            mma_ab2(kKt ? frag_row(&KTb[b][(16 * tj + n) * LDKT + 32 * kb], g)
-                        : frag_col(&Kb[b][32 * kb * LDK + 16 * tj + n], LDK, g),
-                    bR[kb], dS[tj]);
+            mma_ab2(frag_kt<T, LDK>(Kb[b], kb, tj, g, n), bR[kb], dS[j]);
         }
       } else {
-        if constexpr (kDvTile) {
-          tile_put<C>(dvxT[b], dU, g, n);
-        } else {
+        if constexpr (kDvTile) hand(dvxT[b], dU);
+        else store_dv(dU);
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * ti + 4 * g + e;
-              if (r < nrows) dvo[(size_t)r * D] = dU[ti][e];
-            }
-        }
-#pragma unroll
-        for (int tj = 0; tj < NKT; ++tj) {
+        for (int j = 0; j < HT; ++j) {
+          const int tj = h * HT + j;
           const f32x4 x2 = *reinterpret_cast<const f32x4*>(&X2[b][n * (D + 4) + 16 * tj + 4 * g]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dS[tj][e] = gamC * dS[tj][e] + x2[e];
+          for (int e = 0; e < 4; ++e) dS[j][e] = gamC * dS[j][e] + x2[e];
         }
       }
+      // this half's rows of dS' entering the next step
+#pragma unroll
+      for (int j = 0; j < HT; ++j)
+        *reinterpret_cast<f32x4*>(&dSxT[(s + 1) % 3][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) =
+            dS[j];
     }
     __syncthreads();
   }
   if (dS0) {
     const size_t sb = (size_t)bh * D * D;
 #pragma unroll
-    for (int tj = 0; tj < NKT; ++tj)
+    for (int j = 0; j < HT; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dS0[sb + (size_t)(16 * tj + 4 * g + e) * D + col0 + n] = dS[tj][e];
+      for (int e = 0; e < 4; ++e)
+        dS0[sb + (size_t)(16 * (h * HT + j) + 4 * g + e) * D + col0 + n] = dS[j][e];
   }
 }
 
@@ -1763,7 +1802,7 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
-                       dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.k),
+                       dim3(grid), dim3(kStatesThreads), 0, st, static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.beta, a.S0, ws, seq_map(a), BH);
     return hipGetLastError();
   });
@@ -1777,7 +1816,7 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
     hipLaunchKernelGGL((bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
-                       dim3(kThreads), 0, st, static_cast<const T*>(a.k), a.beta, a.dS_final,
+                       dim3(kRevThreads), 0, st, static_cast<const T*>(a.k), a.beta, a.dS_final,
                        a.dv, a.dS0, ws, seq_map(a), BH);
     return hipGetLastError();
   });
