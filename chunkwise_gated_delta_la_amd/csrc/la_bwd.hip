@@ -83,7 +83,6 @@ constexpr int kRevThreads = kWalkChain + kRevStage;
 // (shapes below are the fixed-length ones).
 struct BwdWs {
   float* g;     // [BH, NC * C]     in-chunk cumsum of log alpha (padded rows: the total)
-  float* T;     // [BH, NC, C, C]   (I + A)^-1, row-major (erase modes)
   float* Sent;  // [BH, NC, D, D]   state entering each chunk
   float* U;     // [BH, NC * C, D]  T R (erase modes)
   float* dSx;   // [BH, NC, D, D]   gradient of the state leaving each chunk
@@ -112,17 +111,16 @@ size_t slots(const BwdArgs& a) {
 size_t carve(const BwdArgs& a, BwdWs* ws) {
   const size_t ns = slots(a), D = a.d;
   const bool erase = mode_erase(a.mode);
-  const size_t n[9] = {ns * C,     erase ? ns * C * C : 0, ns * D * D, erase ? ns * C * D : 0,
-                       ns * D * D, erase ? ns * C * D : 0, ns * C * D, ns * D * D,
-                       erase ? ns * C * C : 0};
-  float* p[9];
+  const size_t n[8] = {ns * C,     ns * D * D, erase ? ns * C * D : 0, ns * D * D,
+                       erase ? ns * C * D : 0, ns * C * D, ns * D * D, erase ? ns * C * C : 0};
+  float* p[8];
   size_t off = 0;
   char* base = static_cast<char*>(a.workspace);
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 8; ++i) {
     p[i] = (base && n[i]) ? reinterpret_cast<float*>(base + off) : nullptr;
     off += align256(n[i] * sizeof(float));
   }
-  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], n[2], n[3], n[8]};
+  if (ws) *ws = BwdWs{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], n[1], n[2], n[7]};
   return off;
 }
 
@@ -379,13 +377,11 @@ __device__ __forceinline__ Frag<T> frag_kt(const T* Kt, int kb, int tj, int g, i
 // of the walk's double buffer.  Rows past the end of the sequence read as
 // zero.
 //
-// With TS (the reverse walk) T comes as T^T in SplitMat form: for bf16 its
-// hi and lo planes are staged as two bf16 [C][C + 8] tiles, the chain's
-// split operands as they are; for float as the float tile.
-//
-// With SPL (the forward walk, bf16) T comes as float rows and is split into
-// the same bf16 hi and lo planes on its way into LDS.
-template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X, bool TS, bool SPL, int NT_>
+// With TS, T (the forward walk) or T^T (the reverse walk) comes in SplitMat
+// form: for bf16 its hi and lo planes, as the prep kernel wrote them, are
+// staged as two bf16 [C][C + 8] tiles, the chain's split operands as they
+// are; for float as the float tile.
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X, bool TS, int NT_>
 struct ChunkStage {
   static constexpr int NT = NT_;
   static constexpr int PE = 16 / sizeof(T);
@@ -395,8 +391,7 @@ struct ChunkStage {
   static constexpr int IK = (NK + NT - 1) / NT;
   static constexpr int NTV = C * C / 4;          // 16-byte vectors of T (either form)
   static constexpr bool kTPlanes = TS && IsBf16<T>::value;
-  static constexpr bool kTSplit = SPL && IsBf16<T>::value;
-  static constexpr int LDTT = C + 8;              // row pitch of the bf16 T^T planes
+  static constexpr int LDTT = C + 8;              // row pitch of the bf16 T planes
   static constexpr int IT = ERASE ? (NTV + NT - 1) / NT : 1;
   static constexpr int VV = 16 / PE;              // 16-byte vectors per 16-column row
   static constexpr int NV = C * VV;
@@ -503,15 +498,6 @@ struct ChunkStage {
             const int pl = p / (NTV / 2), rem = p % (NTV / 2);
             T* dst = reinterpret_cast<T*>(Tb) + pl * C * LDTT + (rem / 8) * LDTT + 8 * (rem % 8);
             *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, tx[i]);
-          } else if constexpr (kTSplit) {
-            // row p / 16, four columns from 4 (p % 16): hi and lo parts
-            uint32_t h0, l0, h1, l1;
-            split_pair(tx[i][0], tx[i][1], h0, l0);
-            split_pair(tx[i][2], tx[i][3], h1, l1);
-            T* dst = reinterpret_cast<T*>(Tb) + (p / (C / 4)) * LDTT + 4 * (p % (C / 4));
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2*>(dst) = u32x2{h0, h1};
-            *reinterpret_cast<u32x2*>(dst + C * LDTT) = u32x2{l0, l1};
           } else {
             *reinterpret_cast<f32x4*>(Tb + (p / (C / 4)) * LDC + 4 * (p % (C / 4))) = tx[i];
           }
@@ -692,9 +678,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       }
       x[r] = s0 + s1;
     }
-#pragma unroll
-    for (int r = 0; r < C; ++r) ws.T[(cid * C + r) * C + lane] = x[r];
-    // row `lane` of T^T, in the operand form of the reverse walk
+    // row `lane` of T^T, in SplitMat form: the walks' T and T^T operands
     const SplitMat<T> Tt = SplitMat<T>::make(ws.TT, ws.nT);
 #pragma unroll
     for (int q8 = 0; q8 < C / 8; ++q8) {
@@ -761,7 +745,8 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   constexpr int NKT = D / 16, NKB = D / 32, NCT = D / 16;
   constexpr int HT = NKT / 2, HB = NKB / 2;      // of one chain half
 
-  // bf16: T as its bf16 hi and lo planes [C][C + 8]
+  // bf16: T^T as its bf16 hi and lo planes [C][C + 8] (the prep kernel's
+  // form; the chain reads T's rows as its columns)
   constexpr bool kTPlanes = IsBf16<T>::value;
   constexpr int LDTT = C + 8;
   constexpr int kTWords = kTPlanes ? C * LDTT : C * LDC;   // floats per buffer
@@ -792,14 +777,21 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   // during the step two before its use and land in LDS during the step
   // before it (the barriers wait for LDS traffic only, so the loads stay in
   // flight).
-  ChunkStage<T, D, kErase, true, false, false, true, kStatesStage> st;
+  ChunkStage<T, D, kErase, true, false, true, kStatesStage> st;
   const int ts = tid - kWalkChain;             // staging thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
     const size_t cid = si.slot0 + c;
-    st.load(k, v, beta, kErase ? ws.T + cid * C * C : nullptr, ws.g + cid * C, row0, nrows, col0,
-            ts);
+    const SplitMat<T> Tt = SplitMat<T>::make(ws.TT, ws.nT);
+    const T* th = nullptr;
+    const T* tl = nullptr;
+    if constexpr (kTPlanes && kErase) {
+      th = Tt.p + cid * C * C;
+      tl = Tt.p + Tt.plane + cid * C * C;
+    }
+    st.load(k, v, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr, ws.g + cid * C, row0,
+            nrows, col0, ts, nullptr, nullptr, th, tl);
   };
   auto store = [&](int b) {
     st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], ts);
@@ -901,13 +893,15 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             if (kb > ti / 2) continue;      // T is zero above the diagonal blocks
+            // row 16 ti + n of T, over columns 32 kb + kidx(g, j): a column of
+            // the T^T tile, read transposed (bf16 planes) or strided (float)
             Frag2<T> at;
             if constexpr (kTPlanes) {
-              const T* tp = reinterpret_cast<const T*>(Tb[b]) + (16 * ti + n) * LDTT + 32 * kb;
-              at.hi = frag_row(tp, g);
-              at.lo = frag_row(tp + C * LDTT, g);
+              const T* tp = reinterpret_cast<const T*>(Tb[b]);
+              at.hi = frag_kt<T, LDTT>(tp, kb, ti, g, n);
+              at.lo = frag_kt<T, LDTT>(tp + C * LDTT, kb, ti, g, n);
             } else {
-              at = frag2_rowx<T>(&Tb[b][(16 * ti + n) * LDC + 32 * kb], g);
+              at = frag2_col<T>(&Tb[b][32 * kb * LDC + 16 * ti + n], LDC, g);
             }
             mma_a2b2(at, bR[kb], U[ti]);
           }
@@ -1021,7 +1015,7 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
   // gates and the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO
   // (formed in parallel beforehand) -- two chunks ahead, as in the forward
   // walk.
-  ChunkStage<T, D, kErase, false, true, true, false, kRevStage> st;
+  ChunkStage<T, D, kErase, false, true, true, kRevStage> st;
   const int ts = tid - kWalkChain;             // staging thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);

@@ -454,8 +454,8 @@ int la_noncausal_workspace_bytes(int B, int H, int L, int dk, int dv,
  *                        last chunk may be partial)
  *   workspace       at least la_chunk_bwd_workspace_bytes() bytes, 16-byte
  *                   aligned: per chunk the entry state, the gradient of the
- *                   leaving state and Q^T diag(gam) dO (3 d^2 floats) and T
- *                   (C^2 floats); per token U, dR and P^T dO (3 d floats)
+ *                   leaving state and Q^T diag(gam) dO (3 d^2 floats) and
+ *                   T^T (C^2 floats); per token U, dR and P^T dO (3 d floats)
  *                   and g
  * Errors as la_chunk_fwd: missing required pointers LA_ERR_NULL; shapes
  * LA_ERR_SHAPE / LA_ERR_UNSUPPORTED (also LA_DTYPE_BF16_F32OUT); any overlap

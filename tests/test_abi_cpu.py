@@ -444,17 +444,17 @@ def bwd_ws_bytes(lib, B=1, H=1, L=64, d=64, mode=2, dtype=1):
 
 def expected_bwd_ws(B, H, L, d, erase):
     """Per chunk the entry state, the gradient of the leaving state and
-    Q^T diag(gam) dO (d^2 floats each); T (C^2) with erase; per padded token
-    g and P^T dO (d floats), and U and dR (d floats each) with erase; each
-    array 256-byte aligned."""
+    Q^T diag(gam) dO (d^2 floats each); T^T (C^2) with erase; per padded
+    token g and P^T dO (d floats), and U and dR (d floats each) with erase;
+    each array 256-byte aligned."""
     nc = -(-L // 64)
     pad = lambda n: -(-n * 4 // 256) * 256     # noqa: E731
     bh = B * H
     arrays = [bh * nc * 64, bh * nc * d * d, bh * nc * d * d, bh * nc * 64 * d, bh * nc * d * d]
     if erase:
-        arrays += [bh * nc * 64 * 64]             # T^T for the reverse walk
+        arrays += [bh * nc * 64 * 64]             # T^T, for both walks
     if erase:
-        arrays += [bh * nc * 64 * 64, bh * nc * 64 * d, bh * nc * 64 * d]
+        arrays += [bh * nc * 64 * d, bh * nc * 64 * d]
     return sum(pad(n) for n in arrays)
 
 
