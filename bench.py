@@ -37,8 +37,9 @@ CSRC = os.path.join(ROOT, "chunkwise_gated_delta_la_amd", "csrc")
 # Source files each kernel is built from: a traffic measurement is used
 # only while these are unchanged.
 KERNEL_SOURCES = {
-    "la_chunk": ["la_chunk.hip", "la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
-    "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_kernels.hpp"],
+    "la_chunk": ["la_chunk.hip", "la_chunk_pipe.hip", "la_device.hpp", "la_index.hpp",
+                 "la_kernels.hpp"],
+    "la_tsolve": ["la_chunk_pipe.hip", "la_device.hpp", "la_index.hpp", "la_kernels.hpp"],
     "la_decode": ["la_decode.hip", "la_device.hpp", "la_kernels.hpp"],
 }
 for _k in ("la_bwd_prep", "la_bwd_states", "la_bwd_rev", "la_bwd_grads"):
@@ -236,7 +237,8 @@ def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, com
         kernels[lib_name] = {
             "workload": workload[lib_name], "source_hash": source_hash(lib_name),
             "fetch_bytes_per_launch": round(f_b), "write_bytes_per_launch": round(w_b),
-            "hbm_bytes_per_launch": round(f_b + w_b), "dispatches": len(fv)}
+            "hbm_bytes_per_launch": round(f_b + w_b), "dispatches": len(fv),
+            "command": command}
     # kernels not in these runs keep their earlier records
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -245,7 +247,7 @@ def ingest_pmc(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, com
         old = {}
     old.update(kernels)
     rec = {"calibration": {"copy_bytes": 1 << 30, "fetch_scale": sf, "write_scale": sw},
-           "command": command, "kernels": old}
+           "kernels": old}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(rec, fh, indent=1)
@@ -633,7 +635,8 @@ def bwd_kernel_bytes(name, w):
     st = bh * nc * d * d * 4       # one state per chunk-head
     S = bh * d * d * 4             # one state per head
     return {
-        "la_bwd_prep": tok * (3 * d * esz + 8) + ptok * 4 + (2 * cc if erase else 0)
+        # T^T once, for both walks
+        "la_bwd_prep": tok * (3 * d * esz + 8) + ptok * 4 + (cc if erase else 0)
                        + ptok * d * 4 + st,
         "la_bwd_states": tok * (2 * d * esz + 8) + ptok * 4 + (cc if erase else 0) + S + st
                          + (ptok * d * 4 if erase else 0),
