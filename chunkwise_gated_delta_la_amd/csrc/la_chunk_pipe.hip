@@ -213,10 +213,13 @@ __device__ __forceinline__ void dma_tile(T16* dst, const T16* src_rows,
 // U_new = T R as a single bf16 (its rounding costs well under the
 // tolerance; R is split).
 
-// Diagonal blocks D_i = (I + A_ii)^-1: lane (g, n) solves column n of block
-// g by forward substitution; the block's rows are loaded first.
-__device__ __forceinline__ void t_diag(const float* Ab, float* Df, int g, int n) {
-  const float* A = Ab + bid(g, g) * 16 * LDB;
+// Diagonal blocks D_i = (I + A_ii)^-1, each written over A_ii: lane (g, n)
+// solves column n of block g by forward substitution.  The block's rows are
+// loaded first, by the one wave of the workgroup, so every read of A_ii
+// precedes every write of D_i, and nothing reads A_ii afterwards.
+__device__ __forceinline__ int dblk(int i) { return bid(i, i) * 16 * LDB; }
+__device__ __forceinline__ void t_diag(float* Ab, int g, int n) {
+  const float* A = Ab + dblk(g);
   f32x4 arow[16][4];
 #pragma unroll
   for (int r = 1; r < 16; ++r)
@@ -236,20 +239,21 @@ __device__ __forceinline__ void t_diag(const float* Ab, float* Df, int g, int n)
     x[r] = s0 + s1;
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) Df[g * 16 * LDB + r * LDB + n] = x[r];
+  for (int r = 0; r < 16; ++r) Ab[dblk(g) + r * LDB + n] = x[r];
 }
 
-// Blocks of T below the diagonal from the diagonal blocks D_i (Df) and A:
+// Blocks of T below the diagonal from the diagonal blocks D_i (in the
+// diagonal A blocks' place) and the A blocks below the diagonal:
 //   T10 = -D1 A10 D0,  T32 = -D3 A32 D2,
 //   [T20 T21; T30 T31] = -[[D2, 0], [T32, D3]] [A20 A21; A30 A31] [[D0, 0], [T10, D1]]
 // (block inverse of a 2 x 2 block lower-triangular matrix, applied twice),
 // four dependent product steps.  Products split both operands.  The six
 // blocks come back in accumulator layout: tb[0..5] = T10, T32, T20, T21,
 // T30, T31 (element (4 g + e, n) of each).
-__device__ __forceinline__ void t_col(const float* Ab, const float* Df, float* T32f,
-                                      f32x4 (&tb)[6], int g, int n) {
+__device__ __forceinline__ void t_col(const float* Ab, float* T32f, f32x4 (&tb)[6], int g,
+                                      int n) {
   auto blkA = [&](int i, int j) { return Ab + bid(i, j) * 16 * LDB; };
-  auto blkD = [&](int i) { return Df + i * 16 * LDB; };
+  auto blkD = [&](int i) { return Ab + dblk(i); };
   auto dacc = [&](int i) {     // D_i in accumulator layout
     f32x4 d;
 #pragma unroll
@@ -361,11 +365,12 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
                                                         ProIn pro) {
   constexpr int NKB = D / 32;
   __shared__ __attribute__((aligned(16))) float Ab[TS ? 10 * 16 * LDB : 1];
-  __shared__ __attribute__((aligned(16))) float Df[TS ? 4 * 16 * LDB : 1];
   __shared__ __attribute__((aligned(16))) float T32f[TS ? 16 * LDB : 1];
-  // The bf16 T tile that the record is gathered from takes the A blocks'
-  // place once they have been read for the last time: a third less LDS, so
-  // eight of these one-wave workgroups share a compute unit instead of five.
+  // The diagonal inverses take the diagonal A blocks' place, and the bf16 T
+  // tile that the record is gathered from the A blocks' place once they have
+  // been read for the last time: half the LDS of separate arrays (14.25
+  // KiB), so eleven of these one-wave workgroups share a compute unit
+  // instead of five.
   static_assert(!TS || C * LDT * sizeof(T16) <= sizeof(Ab), "T tile fits in the A blocks");
   T16* const Tb = reinterpret_cast<T16*>(Ab);
   __shared__ __attribute__((aligned(16))) float gsh[C];               // row exponents
@@ -478,18 +483,21 @@ __global__ __launch_bounds__(kWave) void t_solve_kernel(const T16* __restrict__ 
       }
     }
     __syncthreads();
-    t_diag(Ab, Df, g, n);
+    t_diag(Ab, g, n);
     __syncthreads();
     f32x4 tb[6];
-    t_col(Ab, Df, T32f, tb, g, n);
+    t_col(Ab, T32f, tb, g, n);
     __syncthreads();     // (the A blocks are read for the last time)
-    // T into its bf16 tile over the A blocks: the diagonal blocks from Df
-    // (lane (g, n): column n of block g), the six blocks below from t_col,
-    // and zeros for the upper blocks (0, 1) and (2, 3) that T's operand
-    // fragments span
+    // T into its bf16 tile over the A blocks: the diagonal blocks from the
+    // inverses (lane (g, n): column n of block g; the tile covers three of
+    // them, so all are read before the first write), the six blocks below
+    // from t_col, and zeros for the upper blocks (0, 1) and (2, 3) that T's
+    // operand fragments span
+    float dcol[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)Df[g * 16 * LDB + r * LDB + n];
+    for (int r = 0; r < 16; ++r) dcol[r] = Ab[dblk(g) + r * LDB + n];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tb[(16 * g + r) * LDT + 16 * g + n] = (T16)dcol[r];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e;
