@@ -282,7 +282,9 @@ __device__ __forceinline__ void mma_a2b(const Frag2<T>& a, const Frag<T>& b, f32
 // its staging waves through LDS, kept transposed ([16][R + 4]) so that a
 // chain lane writes its four rows of one accumulator tile with one 16-byte
 // write; the staging waves then store it to a workspace matrix (row pitch D,
-// the tile's 16 columns) in that matrix's form, 8 columns per thread.
+// the tile's 16 columns) in that matrix's form, 8 columns per thread (NT
+// threads, t < NT; a fixed trip count, so the compiler tracks the loads in
+// flight across it instead of waiting for them at a loop head).
 template <int R>
 __device__ __forceinline__ void tile_put(float* X, const f32x4* acc, int g, int n) {
 #pragma unroll
@@ -290,10 +292,14 @@ __device__ __forceinline__ void tile_put(float* X, const f32x4* acc, int g, int 
     *reinterpret_cast<f32x4*>(X + n * (R + 4) + 16 * t + 4 * g) = acc[t];
 }
 
-template <typename T, int D, int R>
+template <typename T, int D, int R, int NT>
 __device__ __forceinline__ void tile_flush(const float* X, const SplitMat<T>& M, size_t base,
-                                           int t, int nt) {
-  for (int p = t; p < 2 * R; p += nt) {
+                                           int t) {
+  __builtin_assume(t >= 0 && t < NT);
+#pragma unroll
+  for (int i = 0; i < (2 * R + NT - 1) / NT; ++i) {
+    const int p = t + i * NT;
+    if (p >= 2 * R) break;
     const int r = p / 2, c0 = 8 * (p % 2);
     float x[8];
 #pragma unroll
@@ -374,8 +380,10 @@ __device__ __forceinline__ Frag<T> frag_kt(const T* Kt, int kb, int tj, int g, i
 // V (forward walk), the decays (as exp(g) and exp(g_C - g)) and beta -- read
 // by the NT threads of the staging waves in one batch (every load issued,
 // at clamped indices, before the first LDS write), then written to one half
-// of the walk's double buffer.  Rows past the end of the sequence read as
-// zero.
+// of the walk's double buffer.  Rows past the end of the sequence are
+// written as zero: the mask is applied when the loaded values go to LDS, a
+// step after the loads, so no instruction touches a load's registers before
+// then (a select right after the load would wait for it there).
 //
 // With TS, T (the forward walk) or T^T (the reverse walk) comes in SplitMat
 // form: for bf16 its hi and lo planes, as the prep kernel wrote them, are
@@ -405,6 +413,7 @@ struct ChunkStage {
   u32x4 vx[IV];
   f32x4 x1[IX1], x2[IX2];
   float gx, gcx, bx;
+  int nr;                                          // valid rows of the loaded chunk
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
                                        const float* __restrict__ beta, const float* Tg,
@@ -412,7 +421,7 @@ struct ChunkStage {
                                        int t, const float* X1g = nullptr,
                                        const float* X2g = nullptr, const T* Th = nullptr,
                                        const T* Tl = nullptr) {
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    nr = nrows;
     if constexpr (WITH_X) {
       // 16 columns (col0 ..) of the chunk's X1 [C, D] and X2 [D, D]
 #pragma unroll
@@ -431,9 +440,7 @@ struct ChunkStage {
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int p = min(t + i * NT, NK - 1), r = p / VPR, cv = p % VPR;
-      const u32x4 x =
-          *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
-      kx[i] = r < nrows ? x : z;
+      kx[i] = *reinterpret_cast<const u32x4*>(k + (row0 + min(r, nrows - 1)) * D + cv * PE);
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -454,22 +461,22 @@ struct ChunkStage {
 #pragma unroll
       for (int i = 0; i < IV; ++i) {
         const int p = min(t + i * NT, NV - 1), r = p / VV, cv = p % VV;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(
-            v + (row0 + min(r, nrows - 1)) * D + col0 + cv * PE);
-        vx[i] = r < nrows ? x : z;
+        vx[i] = *reinterpret_cast<const u32x4*>(v + (row0 + min(r, nrows - 1)) * D + col0 +
+                                                cv * PE);
       }
     }
     const int tr = min(t, C - 1);
     gx = gg[tr];
     gcx = gg[C - 1];
-    float b = 0.f;
-    if constexpr (ERASE) b = beta[row0 + min(tr, nrows - 1)];
-    bx = tr < nrows ? b : 0.f;
+    bx = 0.f;
+    if constexpr (ERASE) bx = beta[row0 + min(tr, nrows - 1)];
   }
 
   __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* fsb,
                                         float* bsb, int t, float* X1b = nullptr,
                                         float* X2b = nullptr) const {
+    __builtin_assume(t >= 0 && t < NT);
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     if constexpr (WITH_X) {
 #pragma unroll
       for (int i = 0; i < IX1; ++i) {
@@ -487,7 +494,9 @@ struct ChunkStage {
 #pragma unroll
     for (int i = 0; i < IK; ++i) {
       const int p = t + i * NT;
-      if (p < NK) *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) = kx[i];
+      if (p < NK)
+        *reinterpret_cast<u32x4*>(Kb + (p / VPR) * LDK + (p % VPR) * PE) =
+            p / VPR < nr ? kx[i] : z;
     }
     if constexpr (ERASE) {
 #pragma unroll
@@ -510,12 +519,13 @@ struct ChunkStage {
         const int p = t + i * NT;
         if (p < NV) {
           float* dst = Vb + (p / VV) * LDX + (p % VV) * PE;
+          const u32x4 xv = p / VV < nr ? vx[i] : z;
           if constexpr (IsBf16<T>::value) {
-            const bf16x8 x = __builtin_bit_cast(bf16x8, vx[i]);
+            const bf16x8 x = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) dst[j] = (float)x[j];
           } else {
-            const f32x4 x = __builtin_bit_cast(f32x4, vx[i]);
+            const f32x4 x = __builtin_bit_cast(f32x4, xv);
 #pragma unroll
             for (int j = 0; j < 4; ++j) dst[j] = x[j];
           }
@@ -526,7 +536,7 @@ struct ChunkStage {
       // the decays the chain needs per row: gam = exp(g) and f = exp(g_C - g)
       gsb[t] = __expf(gx);
       fsb[t] = __expf(gcx - gx);
-      bsb[t] = bx;
+      bsb[t] = t < nr ? bx : 0.f;
     }
   }
 };
@@ -824,14 +834,20 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
     const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
     const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
     auto flush = [&](int c) {
-      tile_flush<T, D, D>(SxT[c % 3], Se, (si.slot0 + c) * D * D + col0, ts, kStatesStage);
+      tile_flush<T, D, D, kStatesStage>(SxT[c % 3], Se, (si.slot0 + c) * D * D + col0, ts);
       if constexpr (kErase)
-        tile_flush<T, D, C>(UxT[c & 1], Um, (si.slot0 + c) * C * D + col0, ts, kStatesStage);
+        tile_flush<T, D, C, kStatesStage>(UxT[c & 1], Um, (si.slot0 + c) * C * D + col0, ts);
     };
+    // per step: the LDS writes of the chunk loaded a step ago, the next
+    // loads, then the stores of the last step's results.  Loads and stores
+    // share one counter, and with both in flight a wait for a load is a wait
+    // for every store issued before it; in this order the LDS writes wait
+    // for loads and stores a step old, and nothing waits for a store just
+    // issued.
     for (int c = 0; c < NC; ++c) {
-      if (c >= 1) flush(c - 1);
       if (c + 1 < NC) store((c & 1) ^ 1);
       load(min(c + 2, NC - 1));
+      if (c >= 1) flush(c - 1);
       __syncthreads();
     }
     flush(NC - 1);
@@ -1063,14 +1079,17 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
     const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
     auto flush = [&](int s) {
       const int c = NC - 1 - s, b = s & 1;
-      tile_flush<T, D, D>(dSxT[s % 3], dSe, (si.slot0 + c) * D * D + col0, ts, kRevStage);
+      tile_flush<T, D, D, kRevStage>(dSxT[s % 3], dSe, (si.slot0 + c) * D * D + col0, ts);
       if constexpr (kErase)
-        tile_flush<T, D, C>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0, ts, kRevStage);
+        tile_flush<T, D, C, kRevStage>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0, ts);
       if constexpr (kDvTile) {
         // dv rows of the chunk (those inside the sequence), 8 columns a thread
         const int nrows = min(C, L - c * C);
         float* dvc = dv_out + (si.row0 + (size_t)c * C) * D + col0;
-        for (int p = ts; p < 2 * C; p += kRevStage) {
+#pragma unroll
+        for (int i = 0; i < (2 * C + kRevStage - 1) / kRevStage; ++i) {
+          const int p = ts + i * kRevStage;
+          if (p >= 2 * C) break;
           const int r = p / 2, c0 = 8 * (p % 2);
           if (r < nrows) {
             float x[8];
@@ -1083,10 +1102,10 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
         }
       }
     };
-    for (int s = 0; s < NC; ++s) {
-      if (s >= 1) flush(s - 1);
+    for (int s = 0; s < NC; ++s) {      // in the forward walk's order
       if (s + 1 < NC) store((s & 1) ^ 1);
       load(max(NC - 3 - s, 0));
+      if (s >= 1) flush(s - 1);
       __syncthreads();
     }
     flush(NC - 1);
