@@ -44,9 +44,11 @@
 //                of each chunk and dR, writing dv and dS0
 //   bwd_grads    per (b, h, chunk): dq, dk, dbeta, dlog_alpha
 // The walks keep their 16-column state (or state-gradient) tile in the MFMA
-// accumulators of wave 0; waves 1-3 stage the chain's operands two chunks
-// ahead into a double buffer and write out what the chain hands them
-// through LDS, so each chunk step has one barrier.
+// accumulators of waves 0 and 1, each holding half of its rows; waves 2
+// and 3 load the chain's operands two chunks ahead into registers and write
+// them into a double buffer in LDS the step before their use, and wave 4
+// writes out what the chain hands it through LDS, so each chunk step has
+// one barrier.
 //
 // A ragged last chunk is padded with rows that change nothing: q, k, v, dO
 // and beta read as zero and log alpha as zero, so the padded rows of T are
@@ -70,13 +72,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int LDC = C + 4;     // row pitch of float C x C tiles in LDS
 constexpr int LDX = 20;        // row pitch of float 16-column tiles in LDS
-// The walks: two chain waves (one per half of the state's rows) and the
-// staging waves
+// The walks: two chain waves (one per half of the state's rows), two waves
+// loading the chain's operands into LDS, and one wave storing what the
+// chain hands over (no wave has loads and stores in flight together: they
+// share one counter, and a wait for a load would wait for every store
+// issued before it).  The fifth wave shares a SIMD with a chain half; its
+// work per step is light.
 constexpr int kWalkChain = 2 * kWave;
-constexpr int kStatesStage = 128;              // staging threads of the forward walk
-constexpr int kRevStage = 128;                 // and of the reverse walk
-constexpr int kStatesThreads = kWalkChain + kStatesStage;
-constexpr int kRevThreads = kWalkChain + kRevStage;
+constexpr int kStatesLoad = 2 * kWave;         // loading threads of the forward walk
+constexpr int kRevLoad = 2 * kWave;            // and of the reverse walk
+constexpr int kStatesThreads = kWalkChain + kStatesLoad + kWave;
+constexpr int kRevThreads = kWalkChain + kRevLoad + kWave;
 
 // Per-chunk arrays are indexed by the chunk's slot: bh * NC + c for the
 // fixed-length layout, the forward's packed-batch slots (SeqMap) otherwise
@@ -279,9 +285,9 @@ __device__ __forceinline__ void mma_a2b(const Frag2<T>& a, const Frag<T>& b, f32
 }
 
 // A float tile of R rows x 16 columns handed from a walk's chain wave to
-// its staging waves through LDS, kept transposed ([16][R + 4]) so that a
+// its storing wave through LDS, kept transposed ([16][R + 4]) so that a
 // chain lane writes its four rows of one accumulator tile with one 16-byte
-// write; the staging waves then store it to a workspace matrix (row pitch D,
+// write; the storing wave then stores it to a workspace matrix (row pitch D,
 // the tile's 16 columns) in that matrix's form, 8 columns per thread (NT
 // threads, t < NT; a fixed trip count, so the compiler tracks the loads in
 // flight across it instead of waiting for them at a loop head).
@@ -378,7 +384,7 @@ __device__ __forceinline__ Frag<T> frag_kt(const T* Kt, int kb, int tj, int g, i
 
 // The chain operands of one chunk -- K rows, T (erase modes), 16 columns of
 // V (forward walk), the decays (as exp(g) and exp(g_C - g)) and beta -- read
-// by the NT threads of the staging waves in one batch (every load issued,
+// by the NT threads of the loading waves in one batch (every load issued,
 // at clamped indices, before the first LDS write), then written to one half
 // of the walk's double buffer.  Rows past the end of the sequence are
 // written as zero: the mask is applied when the loaded values go to LDS, a
@@ -741,9 +747,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 // Five waves, as in the reverse walk: waves 0 and 1 carry the state, each
 // on half of its rows (dk), and form the whole K S (the other half's rows
 // from the float tile of the state entering the chunk, which both hand to
-// the staging waves), R and U = T R (T lower triangular: row tiles 0 and 1
+// the storing wave), R and U = T R (T lower triangular: row tiles 0 and 1
 // skip the block above the diagonal, exact zeros), then update only their
-// rows; waves 2-4 stage the operands and store S and U.
+// rows; waves 2 and 3 stage the operands, wave 4 stores S and U.
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
@@ -783,12 +789,12 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   const int NC = (L + C - 1) / C;
   if (NC == 0) return;                         // nothing to store
 
-  // The staging waves stage the chain's operands: chunk c's loads go out
-  // during the step two before its use and land in LDS during the step
-  // before it (the barriers wait for LDS traffic only, so the loads stay in
-  // flight).
-  ChunkStage<T, D, kErase, true, false, true, kStatesStage> st;
-  const int ts = tid - kWalkChain;             // staging thread index
+  // Waves 2 and 3 stage the chain's operands: chunk c's loads go out during
+  // the step two before its use and land in LDS during the step before it
+  // (the barriers wait for LDS traffic only, so the loads stay in flight).
+  ChunkStage<T, D, kErase, true, false, true, kStatesLoad> st;
+  constexpr int kStore = 2 + kStatesLoad / kWave;   // the storing wave
+  const int tld = tid - kWalkChain;            // loading thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -801,10 +807,10 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
       tl = Tt.p + Tt.plane + cid * C * C;
     }
     st.load(k, v, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr, ws.g + cid * C, row0,
-            nrows, col0, ts, nullptr, nullptr, th, tl);
+            nrows, col0, tld, nullptr, nullptr, th, tl);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], ts);
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tld);
   };
 
   const int h = wave;                          // chain half (waves 0, 1)
@@ -819,34 +825,34 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
 #pragma unroll
     for (int j = 0; j < HT; ++j)
       *reinterpret_cast<f32x4*>(&SxT[0][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) = S[j];
-  } else {
+  } else if (wave < kStore) {
     load(0);
     store(0);
     load(min(1, NC - 1));
   }
   __syncthreads();
 
-  // each role runs its own loop (one barrier per chunk in both), so the
+  // each role runs its own loop (one barrier per chunk in all), so the
   // staging loads meet no other role's registers and are not waited for early
-  if (wave >= 2) {
+  if (wave >= 2 && wave < kStore) {
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) store((c & 1) ^ 1);
+      load(min(c + 2, NC - 1));
+      __syncthreads();
+    }
+    return;
+  }
+  if (wave == kStore) {
     // the state and U tiles of chunk c, handed over by the chain, go to the
     // workspace during the next step
     const SplitMat<T> Se = SplitMat<T>::make(ws.Sent, ws.nS);
     const SplitMat<T> Um = SplitMat<T>::make(ws.U, ws.nU);
     auto flush = [&](int c) {
-      tile_flush<T, D, D, kStatesStage>(SxT[c % 3], Se, (si.slot0 + c) * D * D + col0, ts);
+      tile_flush<T, D, D, kWave>(SxT[c % 3], Se, (si.slot0 + c) * D * D + col0, lane);
       if constexpr (kErase)
-        tile_flush<T, D, C, kStatesStage>(UxT[c & 1], Um, (si.slot0 + c) * C * D + col0, ts);
+        tile_flush<T, D, C, kWave>(UxT[c & 1], Um, (si.slot0 + c) * C * D + col0, lane);
     };
-    // per step: the LDS writes of the chunk loaded a step ago, the next
-    // loads, then the stores of the last step's results.  Loads and stores
-    // share one counter, and with both in flight a wait for a load is a wait
-    // for every store issued before it; in this order the LDS writes wait
-    // for loads and stores a step old, and nothing waits for a store just
-    // issued.
     for (int c = 0; c < NC; ++c) {
-      if (c + 1 < NC) store((c & 1) ^ 1);
-      load(min(c + 2, NC - 1));
       if (c >= 1) flush(c - 1);
       __syncthreads();
     }
@@ -964,10 +970,11 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
 
 // ------------------------------------------------------- reverse walk
 // Five waves: waves 0 and 1 carry the chain, each on half of the state
-// gradient's rows (dk); waves 2-4 stage the operands and store the results.
+// gradient's rows (dk); waves 2 and 3 stage the operands, wave 4 stores the
+// results.
 // Each chain half forms the whole dU = X1 + diag(f) K dS' and dR = T^T dU
 // (dS' from its own rows in registers and the other half's from the float
-// tile both hand to the staging waves) and updates only its rows of dS; the
+// tile both hand to the storing wave) and updates only its rows of dS; the
 // two never wait for each other inside a chunk.  T^T is upper triangular,
 // so its row tiles 2 and 3 skip the 32-deep block below the diagonal (exact
 // zeros: the sums are unchanged).
@@ -1027,12 +1034,13 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
     return;
   }
 
-  // The staging waves stage the chain's operands of each chunk -- K, T, the
+  // Waves 2 and 3 stage the chain's operands of each chunk -- K, T, the
   // gates and the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO
   // (formed in parallel beforehand) -- two chunks ahead, as in the forward
-  // walk.
-  ChunkStage<T, D, kErase, false, true, true, kRevStage> st;
-  const int ts = tid - kWalkChain;             // staging thread index
+  // walk; wave 4 stores the results.
+  ChunkStage<T, D, kErase, false, true, true, kRevLoad> st;
+  constexpr int kStore = 2 + kRevLoad / kWave;     // the storing wave
+  const int tld = tid - kWalkChain;            // loading thread index
   auto load = [&](int c) {
     const int nrows = min(C, L - c * C);
     const size_t row0 = si.row0 + (size_t)c * C;
@@ -1045,11 +1053,11 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
       tl = Tt.p + Tt.plane + cid * C * C;
     }
     st.load(k, nullptr, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr,
-            ws.g + cid * C, row0, nrows, col0, ts, ws.X1 + cid * C * D,
+            ws.g + cid * C, row0, nrows, col0, tld, ws.X1 + cid * C * D,
             ws.X2 + cid * D * D, th, tl);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], ts, X1[b], X2[b]);
+    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tld, X1[b], X2[b]);
   };
 
   const int h = wave;                          // chain half (waves 0, 1)
@@ -1066,29 +1074,37 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
 #pragma unroll
     for (int j = 0; j < HT; ++j)
       *reinterpret_cast<f32x4*>(&dSxT[0][n * (D + 4) + 16 * (h * HT + j) + 4 * g]) = dS[j];
-  } else {
+  } else if (wave < kStore) {
     load(NC - 1);
     store(0);
     load(max(NC - 2, 0));
   }
   __syncthreads();
-  if (wave >= 2) {
+  if (wave >= 2 && wave < kStore) {
+    for (int s = 0; s < NC; ++s) {
+      if (s + 1 < NC) store((s & 1) ^ 1);
+      load(max(NC - 3 - s, 0));
+      __syncthreads();
+    }
+    return;
+  }
+  if (wave == kStore) {
     // dS' and dR of the chunk of step s, handed over by the chain, go to the
     // workspace during step s + 1
     const SplitMat<T> dSe = SplitMat<T>::make(ws.dSx, ws.nS);
     const SplitMat<T> dRm = SplitMat<T>::make(ws.dR, ws.nU);
     auto flush = [&](int s) {
       const int c = NC - 1 - s, b = s & 1;
-      tile_flush<T, D, D, kRevStage>(dSxT[s % 3], dSe, (si.slot0 + c) * D * D + col0, ts);
+      tile_flush<T, D, D, kWave>(dSxT[s % 3], dSe, (si.slot0 + c) * D * D + col0, lane);
       if constexpr (kErase)
-        tile_flush<T, D, C, kRevStage>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0, ts);
+        tile_flush<T, D, C, kWave>(dRxT[b], dRm, (si.slot0 + c) * C * D + col0, lane);
       if constexpr (kDvTile) {
         // dv rows of the chunk (those inside the sequence), 8 columns a thread
         const int nrows = min(C, L - c * C);
         float* dvc = dv_out + (si.row0 + (size_t)c * C) * D + col0;
 #pragma unroll
-        for (int i = 0; i < (2 * C + kRevStage - 1) / kRevStage; ++i) {
-          const int p = ts + i * kRevStage;
+        for (int i = 0; i < 2 * C / kWave; ++i) {
+          const int p = lane + i * kWave;
           if (p >= 2 * C) break;
           const int r = p / 2, c0 = 8 * (p % 2);
           if (r < nrows) {
@@ -1102,9 +1118,7 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
         }
       }
     };
-    for (int s = 0; s < NC; ++s) {      // in the forward walk's order
-      if (s + 1 < NC) store((s & 1) ^ 1);
-      load(max(NC - 3 - s, 0));
+    for (int s = 0; s < NC; ++s) {
       if (s >= 1) flush(s - 1);
       __syncthreads();
     }
