@@ -438,24 +438,21 @@ int run_bwd(const la::BwdArgs& a, size_t n_x, size_t n_g, size_t n_s, int dtype,
   return LA_OK;
 }
 
-// Workspace of la_chunk_bwd_fused: the prologue's arrays (normalised q and
-// k in the input type, their inverse norms, the activated gates), each
-// 256-byte aligned, then the backward's own workspace.
+// Workspace of la_chunk_bwd_fused: the prologue's arrays (the inverse norms
+// of q and k, the activated gates), each 256-byte aligned, then the
+// backward's own workspace.
 struct ProWs {
-  size_t qn, kn, rq, rk, la, be, core;   // byte offsets
+  size_t rq, rk, la, be, core;           // byte offsets
   size_t bytes;                          // in all
 };
 
 ProWs pro_ws(const la::BwdArgs& a, int flags) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)a.B * a.H * a.L;
-  const size_t esz = a.in_bf16 ? 2 : 4;
   const bool norm = flags & LA_PRO_QK_L2NORM, gates = flags & LA_PRO_GATES;
   ProWs w{};
   size_t off = 0;
   auto take = [&](size_t n) { const size_t o = off; off += al(n); return o; };
-  w.qn = take(norm ? rows * a.d * esz : 0);
-  w.kn = take(norm ? rows * a.d * esz : 0);
   w.rq = take(norm ? rows * 4 : 0);
   w.rk = take(norm ? rows * 4 : 0);
   w.la = take(gates && la::mode_decay(a.mode) ? rows * 4 : 0);
@@ -665,7 +662,6 @@ int la_chunk_bwd_fused(const void* q, const void* k, const void* v, const float*
   const bool ga = (f.flags & LA_PRO_GATES) && gated, gb = (f.flags & LA_PRO_GATES) && erase;
   la::BwdProArgs p{};
   p.q = q; p.k = k; p.a_raw = a_raw; p.b_raw = b_raw;
-  p.qn = base + w.qn; p.kn = base + w.kn;
   p.rq = reinterpret_cast<float*>(base + w.rq); p.rk = reinterpret_cast<float*>(base + w.rk);
   p.la = reinterpret_cast<float*>(base + w.la); p.be = reinterpret_cast<float*>(base + w.be);
   p.dq = grad_q; p.dk = grad_k; p.da = grad_a; p.db = grad_b;
@@ -680,7 +676,9 @@ int la_chunk_bwd_fused(const void* q, const void* k, const void* v, const float*
     if (e != hipSuccess) return fail_hip("launching the backward prologue", e);
   }
   a.workspace = base + w.core;
-  a.q = norm ? p.qn : q; a.k = norm ? p.kn : k; a.v = v;
+  // the raw q and k, their inverse norms applied per row inside the products
+  a.q = q; a.k = k; a.v = v;
+  a.rq = norm ? p.rq : nullptr; a.rk = norm ? p.rk : nullptr;
   a.log_alpha = ga ? p.la : a_raw; a.beta = gb ? p.be : b_raw; a.S0 = S0;
   a.dout = grad_out; a.dS_final = grad_S_final;
   a.dq = grad_q; a.dk = grad_k; a.dv = grad_v; a.dlog_alpha = grad_a; a.dbeta = grad_b;

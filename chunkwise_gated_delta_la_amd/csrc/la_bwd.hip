@@ -395,7 +395,12 @@ __device__ __forceinline__ Frag<T> frag_kt(const T* Kt, int kb, int tj, int g, i
 // form: for bf16 its hi and lo planes, as the prep kernel wrote them, are
 // staged as two bf16 [C][C + 8] tiles, the chain's split operands as they
 // are; for float as the float tile.
-template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X, bool TS, int NT_>
+//
+// With NORM the K rows are the raw ones and each row's inverse norm goes
+// into both decay tables (every product of the walks that reads a K row
+// scales it by one of them); gam_C then comes from a slot of its own.
+template <typename T, int D, bool ERASE, bool WITH_V, bool WITH_X, bool TS, int NT_,
+          bool NORM = false>
 struct ChunkStage {
   static constexpr int NT = NT_;
   static constexpr int PE = 16 / sizeof(T);
@@ -418,7 +423,7 @@ struct ChunkStage {
   f32x4 tx[IT];
   u32x4 vx[IV];
   f32x4 x1[IX1], x2[IX2];
-  float gx, gcx, bx;
+  float gx, gcx, bx, rkx;
   int nr;                                          // valid rows of the loaded chunk
 
   __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
@@ -426,7 +431,7 @@ struct ChunkStage {
                                        const float* gg, size_t row0, int nrows, int col0,
                                        int t, const float* X1g = nullptr,
                                        const float* X2g = nullptr, const T* Th = nullptr,
-                                       const T* Tl = nullptr) {
+                                       const T* Tl = nullptr, const float* rk = nullptr) {
     nr = nrows;
     if constexpr (WITH_X) {
       // 16 columns (col0 ..) of the chunk's X1 [C, D] and X2 [D, D]
@@ -476,11 +481,12 @@ struct ChunkStage {
     gcx = gg[C - 1];
     bx = 0.f;
     if constexpr (ERASE) bx = beta[row0 + min(tr, nrows - 1)];
+    if constexpr (NORM) rkx = rk[row0 + min(tr, nrows - 1)];
   }
 
   __device__ __forceinline__ void store(T* Kb, float* Tb, float* Vb, float* gsb, float* fsb,
                                         float* bsb, int t, float* X1b = nullptr,
-                                        float* X2b = nullptr) const {
+                                        float* X2b = nullptr, float* gcb = nullptr) const {
     __builtin_assume(t >= 0 && t < NT);
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
     if constexpr (WITH_X) {
@@ -540,8 +546,14 @@ struct ChunkStage {
     }
     if (t < C) {
       // the decays the chain needs per row: gam = exp(g) and f = exp(g_C - g)
-      gsb[t] = __expf(gx);
-      fsb[t] = __expf(gcx - gx);
+      if constexpr (NORM) {
+        gsb[t] = __expf(gx) * rkx;
+        fsb[t] = __expf(gcx - gx) * rkx;
+        if (t == 0) *gcb = __expf(gcx);
+      } else {
+        gsb[t] = __expf(gx);
+        fsb[t] = __expf(gcx - gx);
+      }
       bsb[t] = t < nr ? bx : 0.f;
     }
   }
@@ -552,11 +564,14 @@ struct ChunkStage {
 // terms of the reverse walk that do not depend on the state gradient,
 // X1 = P^T dO [C, d] and X2 = Q^T diag(gam) dO [d, d].  P^T stays in LDS;
 // Q and dO are staged transposed so that every operand is read along its
-// contraction index.
-template <typename T, int D, int MODE>
+// contraction index.  With NORM, q and k are the raw rows and rq, rk their
+// inverse norms: the scores and A take them as row and column factors, X2
+// with gam.
+template <typename T, int D, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ dout,
-    const float* __restrict__ log_alpha, const float* __restrict__ beta, BwdWs ws, SeqMap sm) {
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const float* __restrict__ rq, const float* __restrict__ rk, BwdWs ws, SeqMap sm) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int NKB = D / 32;
@@ -577,6 +592,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) float gs[C];
   __shared__ __attribute__((aligned(16))) float gam[C];
   __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float rqs[NORM ? C : 1];
+  __shared__ __attribute__((aligned(16))) float rks[NORM ? C : 1];
   __shared__ __attribute__((aligned(16))) float Pt[C * LDC];
   __shared__ __attribute__((aligned(16))) float As[kErase ? C * LDC : 4];
   __shared__ __attribute__((aligned(16))) T QT[D * LDT];
@@ -620,6 +637,13 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     gs[lane] = gg;
     gam[lane] = kGated ? __expf(gg) : 1.f;
     bs[lane] = b;
+    if constexpr (NORM) {
+      // gam scales dO's rows for X2 = Q^T diag(gam) dO only: the q norms go with it
+      const float a = lane < nrows ? rq[row0 + lane] : 0.f;
+      rqs[lane] = a;
+      rks[lane] = lane < nrows ? rk[row0 + lane] : 0.f;
+      gam[lane] *= a;
+    }
     ws.g[cid * C + lane] = gg;
   }
   __syncthreads();
@@ -653,6 +677,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
       const int i = 16 * ti + 4 * g + e, r = 16 * tj + n;
       float x = 0.f;
       if (r >= i) x = acc[e] * (kGated ? __expf(gs[r] - gs[i]) : 1.f);
+      if constexpr (NORM) x *= rks[i] * rqs[r];
       Pt[i * LDC + r] = x;
     }
     if constexpr (kErase) {
@@ -667,6 +692,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
         const int r = 16 * ti + 4 * g + e, i = 16 * tj + n;
         float x = 0.f;
         if (r > i) x = bs[r] * a2[e] * (kGated ? __expf(gs[r] - gs[i]) : 1.f);
+        if constexpr (NORM) x *= rks[r] * rks[i];
         As[r * LDC + i] = x;
       }
     }
@@ -749,11 +775,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 // from the float tile of the state entering the chunk, which both hand to
 // the storing wave), R and U = T R (T lower triangular: row tiles 0 and 1
 // skip the block above the diagonal, exact zeros), then update only their
-// rows; waves 2 and 3 stage the operands, wave 4 stores S and U.
-template <typename T, int D, int MODE>
+// rows; waves 2 and 3 stage the operands, wave 4 stores S and U.  With
+// NORM, k is the raw rows and rk their inverse norms (in the decay tables).
+template <typename T, int D, int MODE, bool NORM>
 __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ beta,
-    const float* __restrict__ S0, BwdWs ws, SeqMap sm, int BH) {
+    const float* __restrict__ rk, const float* __restrict__ S0, BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int PE = 16 / sizeof(T);
@@ -777,6 +804,7 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
+  __shared__ float gcb[2];                                   // exp(g_C) (NORM)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -788,11 +816,12 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   const int L = si.len;                        // tokens of this sequence
   const int NC = (L + C - 1) / C;
   if (NC == 0) return;                         // nothing to store
+  constexpr bool kTab = kGated || NORM;        // the decay tables are not all ones
 
   // Waves 2 and 3 stage the chain's operands: chunk c's loads go out during
   // the step two before its use and land in LDS during the step before it
   // (the barriers wait for LDS traffic only, so the loads stay in flight).
-  ChunkStage<T, D, kErase, true, false, true, kStatesLoad> st;
+  ChunkStage<T, D, kErase, true, false, true, kStatesLoad, NORM> st;
   constexpr int kStore = 2 + kStatesLoad / kWave;   // the storing wave
   const int tld = tid - kWalkChain;            // loading thread index
   auto load = [&](int c) {
@@ -807,10 +836,11 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
       tl = Tt.p + Tt.plane + cid * C * C;
     }
     st.load(k, v, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr, ws.g + cid * C, row0,
-            nrows, col0, tld, nullptr, nullptr, th, tl);
+            nrows, col0, tld, nullptr, nullptr, th, tl, rk);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tld);
+    st.store(Kb[b], Tb[kErase ? b : 0], Vb[b], gsb[b], fsb[b], bsb[b], tld, nullptr, nullptr,
+             &gcb[b]);
   };
 
   const int h = wave;                          // chain half (waves 0, 1)
@@ -862,9 +892,9 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
   for (int c = 0; c < NC; ++c) {
     const int b = c & 1;
     {
-      const float* gmc = gsb[b];     // exp(g)
-      const float* fc = fsb[b];      // exp(g_C - g)
-      const float gamC = kGated ? gmc[C - 1] : 1.f;
+      const float* gmc = gsb[b];     // exp(g) (times the row's inverse norm with NORM)
+      const float* fc = fsb[b];      // exp(g_C - g) (the same)
+      const float gamC = kGated ? (NORM ? gcb[b] : gmc[C - 1]) : 1.f;
       // decay factors f of the rows 32 kb + 4 g + e (lo) and 32 kb + 16 + 4 g + e (hi)
       float flo[2][4], fhi[2][4];
 #pragma unroll
@@ -873,8 +903,8 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
         const f32x4 c2 = *reinterpret_cast<const f32x4*>(fc + 32 * kb + 16 + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          flo[kb][e] = kGated ? a[e] : 1.f;
-          fhi[kb][e] = kGated ? c2[e] : 1.f;
+          flo[kb][e] = kTab ? a[e] : 1.f;
+          fhi[kb][e] = kTab ? c2[e] : 1.f;
         }
       }
       Frag2<T> bX[2];
@@ -903,7 +933,7 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti + 4 * g + e;
-            const float gam = kGated ? gmc[r] : 1.f;
+            const float gam = kTab ? gmc[r] : 1.f;
             R[ti][e] = bsb[b][r] * (Vb[b][r * LDX + n] - gam * ks[e]);
           }
         }
@@ -977,11 +1007,13 @@ __global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(
 // tile both hand to the storing wave) and updates only its rows of dS; the
 // two never wait for each other inside a chunk.  T^T is upper triangular,
 // so its row tiles 2 and 3 skip the 32-deep block below the diagonal (exact
-// zeros: the sums are unchanged).
-template <typename T, int D, int MODE>
+// zeros: the sums are unchanged).  With NORM, k is the raw rows and rk
+// their inverse norms (in the decay tables).
+template <typename T, int D, int MODE, bool NORM>
 __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
-    const T* __restrict__ k, const float* __restrict__ beta, const float* __restrict__ dS_final,
-    float* __restrict__ dv_out, float* __restrict__ dS0, BwdWs ws, SeqMap sm, int BH) {
+    const T* __restrict__ k, const float* __restrict__ beta, const float* __restrict__ rk,
+    const float* __restrict__ dS_final, float* __restrict__ dv_out, float* __restrict__ dS0,
+    BwdWs ws, SeqMap sm, int BH) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr int PE = 16 / sizeof(T);
@@ -1009,6 +1041,8 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
   __shared__ __attribute__((aligned(16))) float gsb[2][C];   // exp(g)
   __shared__ __attribute__((aligned(16))) float fsb[2][C];   // exp(g_C - g)
   __shared__ __attribute__((aligned(16))) float bsb[2][C];
+  __shared__ float gcb[2];                                   // exp(g_C) (NORM)
+  constexpr bool kTab = kGated || NORM;        // the decay tables are not all ones
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -1038,7 +1072,7 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
   // gates and the tile's 16 columns of X1 = P^T dO and X2 = Q^T diag(gam) dO
   // (formed in parallel beforehand) -- two chunks ahead, as in the forward
   // walk; wave 4 stores the results.
-  ChunkStage<T, D, kErase, false, true, true, kRevLoad> st;
+  ChunkStage<T, D, kErase, false, true, true, kRevLoad, NORM> st;
   constexpr int kStore = 2 + kRevLoad / kWave;     // the storing wave
   const int tld = tid - kWalkChain;            // loading thread index
   auto load = [&](int c) {
@@ -1054,10 +1088,11 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
     }
     st.load(k, nullptr, beta, kErase && !kTPlanes ? ws.TT + cid * C * C : nullptr,
             ws.g + cid * C, row0, nrows, col0, tld, ws.X1 + cid * C * D,
-            ws.X2 + cid * D * D, th, tl);
+            ws.X2 + cid * D * D, th, tl, rk);
   };
   auto store = [&](int b) {
-    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tld, X1[b], X2[b]);
+    st.store(Kb[b], Tb[kErase ? b : 0], nullptr, gsb[b], fsb[b], bsb[b], tld, X1[b], X2[b],
+             &gcb[b]);
   };
 
   const int h = wave;                          // chain half (waves 0, 1)
@@ -1129,9 +1164,9 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
   for (int s = 0; s < NC; ++s) {
     const int c = NC - 1 - s, b = s & 1;
     {
-      const float* gmc = gsb[b];     // exp(g)
-      const float* fc = fsb[b];      // exp(g_C - g)
-      const float gamC = kGated ? gmc[C - 1] : 1.f;
+      const float* gmc = gsb[b];     // exp(g) (times the row's inverse norm with NORM)
+      const float* fc = fsb[b];      // exp(g_C - g) (the same)
+      const float gamC = kGated ? (NORM ? gcb[b] : gmc[C - 1]) : 1.f;
       const int nrows = min(C, L - c * C);
       const size_t row0 = si.row0 + (size_t)c * C;
       // dS' split over dk: this half's rows from registers, the other's from
@@ -1159,7 +1194,7 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(&X1[b][n * (C + 4) + 16 * ti + 4 * g]);
         const f32x4 fr = *reinterpret_cast<const f32x4*>(fc + 16 * ti + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dU[ti][e] = x1[e] + (kGated ? fr[e] : 1.f) * y[e];
+        for (int e = 0; e < 4; ++e) dU[ti][e] = x1[e] + (kTab ? fr[e] : 1.f) * y[e];
       }
       float* dvo = dv_out + row0 * D + col0 + n;
       // each half hands over (or stores) two of the four row tiles of dv and dR
@@ -1217,8 +1252,8 @@ __global__ __launch_bounds__(kRevThreads) void bwd_rev_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int rl = 32 * kb + 4 * g + e, rh = rl + 16;
-            slo[e] = -bsb[b][rl] * (kGated ? gmc[rl] : 1.f);
-            shi[e] = -bsb[b][rh] * (kGated ? gmc[rh] : 1.f);
+            slo[e] = -bsb[b][rl] * (kTab ? gmc[rl] : 1.f);
+            shi[e] = -bsb[b][rh] * (kTab ? gmc[rh] : 1.f);
           }
           bR[kb] = frag2_from_acc_scaled<T>(dR[2 * kb], dR[2 * kb + 1], slo, shi);
         }
@@ -1338,12 +1373,16 @@ struct ColStage {
   }
 };
 
-template <typename T, int D, int MODE>
+// With NORM, q and k are the raw rows and rq, rk their inverse norms: the
+// scores and K K^T take them as row and column factors, E, E^T and G as
+// factors over their contraction, the row dots as row factors; dq and dk
+// are the gradients of the normalised rows.
+template <typename T, int D, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ beta, const T* __restrict__ dout, float* __restrict__ dq,
-    float* __restrict__ dk, float* __restrict__ dla, float* __restrict__ dbeta, BwdWs ws,
-    SeqMap sm) {
+    const float* __restrict__ beta, const T* __restrict__ dout, const float* __restrict__ rq,
+    const float* __restrict__ rk, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dla, float* __restrict__ dbeta, BwdWs ws, SeqMap sm) {
   constexpr bool kErase = mode_erase(MODE);
   constexpr bool kGated = mode_decay(MODE);
   constexpr bool kSplit = IsBf16<T>::value;
@@ -1376,6 +1415,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   __shared__ __attribute__((aligned(16))) float gam[C];
   __shared__ __attribute__((aligned(16))) float fs[C];
   __shared__ __attribute__((aligned(16))) float bs[C];
+  __shared__ __attribute__((aligned(16))) float rqs[NORM ? C : 1];
+  __shared__ __attribute__((aligned(16))) float rks[NORM ? C : 1];
   // the C x C tiles E and H live until each wave holds its fragments of
   // them; the column-tile staging reuses their bytes after that
   constexpr int kEH = (kErase ? 2 : 1) * C * LDC * (int)sizeof(float);
@@ -1420,6 +1461,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
     gs[tid] = gg;
     gam[tid] = kGated ? __expf(gg) : 1.f;
     bs[tid] = (kErase && tid < nrows) ? beta[row0 + tid] : 0.f;
+    if constexpr (NORM) {
+      rqs[tid] = tid < nrows ? rq[row0 + tid] : 0.f;
+      rks[tid] = tid < nrows ? rk[row0 + tid] : 0.f;
+    }
   }
 #pragma unroll
   for (int i = 0; i < IK; ++i) {
@@ -1498,6 +1543,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ti + 4 * g + e, i = 16 * tj + n;
+      if constexpr (NORM) {
+        qk[e] *= rqs[r] * rks[i];
+        kk[e] *= rks[r] * rks[i];
+      }
       const float Gm = r >= i ? (kGated ? __expf(gs[r] - gs[i]) : 1.f) : 0.f;
       float gg = dp[e] * qk[e] * Gm;
       Em[r * LDC + i] = dp[e] * Gm;
@@ -1533,17 +1582,38 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
   Frag2<T> aE[2], aEt[2], aG[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    aE[kb] = frag2_rowx<T>(Em + ra * LDC + 32 * kb, g);
-    aEt[kb] = frag2_col<T>(Em + 32 * kb * LDC + ra, LDC, g);
+    if constexpr (NORM) {
+      // E K and G K read K's rows i, E^T Q Q's rows: their norms, per i
+      float xe[8], xt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * kb + kidx(g, j);
+        xe[j] = Em[ra * LDC + i] * rks[i];
+        xt[j] = Em[i * LDC + ra] * rqs[i];
+      }
+      aE[kb] = frag2_of<T>(xe);
+      aEt[kb] = frag2_of<T>(xt);
+    } else {
+      aE[kb] = frag2_rowx<T>(Em + ra * LDC + 32 * kb, g);
+      aEt[kb] = frag2_col<T>(Em + 32 * kb * LDC + ra, LDC, g);
+    }
     if constexpr (kErase) {
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 32 * kb + kidx(g, j);
         x[j] = Hm[ra * LDC + i] + Hm[i * LDC + ra];
+        if constexpr (NORM) x[j] *= rks[i];
       }
       aG[kb] = frag2_of<T>(x);
     }
+  }
+  // the row factors of the dots with this lane's Q and K rows
+  float rqr[4], rkr[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    rqr[e] = NORM ? rqs[16 * ti + 4 * g + e] : 1.f;
+    rkr[e] = NORM ? rks[16 * ti + 4 * g + e] : 1.f;
   }
   float dgc_part = 0.f;
   float rdg[4] = {0.f, 0.f, 0.f, 0.f}, rdf[4] = {0.f, 0.f, 0.f, 0.f},
@@ -1595,8 +1665,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * ti + 4 * g + e;
-      const float qv = to_f32(Qt[r * LQ + n]);
-      const float kv = to_f32(Kt[r * LQ + n]);
+      float qv = to_f32(Qt[r * LQ + n]);
+      float kv = to_f32(Kt[r * LQ + n]);
+      if constexpr (NORM) {
+        qv *= rqr[e];
+        kv *= rkr[e];
+      }
       float dQ = gam[r] * m1[e] + ek[e];
       float dK = fs[r] * m3[e] + etq[e];
       rdg[e] += qv * m1[e];
@@ -1647,8 +1721,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grads_kernel(
 
 // ------------------------------------------------------ fused prologue
 // The fused forward's prologue, for its backward: per token row, the op's
-// inputs from the raw ones -- q and k normalised, x r with r = (|x|^2 +
-// 1e-6)^(-1/2); beta = sigmoid(b); log alpha = -scale softplus(a) -- and,
+// inputs from the raw ones -- the inverse norms r = (|x|^2 + 1e-6)^(-1/2)
+// of q and k (the normalised rows x r are never formed: the backward takes
+// r as a row factor); beta = sigmoid(b); log alpha = -scale softplus(a) -- and,
 // after the backward proper, the chain rule back to the raw inputs:
 // dx = r (dx_hat - x_hat (x_hat . dx_hat)), db = dbeta sigmoid(b)(1 -
 // sigmoid(b)), da = -scale sigmoid(a) dlog_alpha.  d / 8 lanes per row.
@@ -1705,8 +1780,8 @@ __device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a_raw,
-    const float* __restrict__ b_raw, T* __restrict__ qn, T* __restrict__ kn,
-    float* __restrict__ rq, float* __restrict__ rk, float* __restrict__ la,
+    const float* __restrict__ b_raw, float* __restrict__ rq, float* __restrict__ rk,
+    float* __restrict__ la,
     float* __restrict__ be, size_t rows, int norm, int gates_a, int gates_b, float scale) {
   constexpr int W = pro_lanes<D>();
   const int sub = threadIdx.x % W;
@@ -1714,7 +1789,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
   if (row >= rows) return;
   if (norm) {
     const T* src[2] = {q, k};
-    T* dst[2] = {qn, kn};
     float* rr[2] = {rq, rk};
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -1724,9 +1798,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pro_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
       const float r = 1.f / sqrtf(sum_lanes<W>(ss) + kQKNormEps);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] *= r;
-      store8(dst[m] + row * D + 8 * sub, x);
       if (sub == 0) rr[m][row] = r;
     }
   }
@@ -1802,6 +1873,13 @@ hipError_t dispatch(const BwdArgs& a, F&& f) {
                    : by_mode(Type<float>{}, std::integral_constant<int, 128>{});
 }
 
+// f(std::bool_constant<NORM>): NORM when the call folds the q and k norms
+template <typename F>
+void by_norm(const BwdArgs& a, F&& f) {
+  if (a.rk) f(std::true_type{});
+  else f(std::false_type{});
+}
+
 }  // namespace
 
 size_t bwd_workspace_bytes(const BwdArgs& a) { return carve(a, nullptr); }
@@ -1813,10 +1891,13 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   const SeqMap sm = seq_map(a);
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
-    hipLaunchKernelGGL((bwd_prep_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
-                       dim3(kThreads), 0, st, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.dout), a.log_alpha,
-                       a.beta, ws, sm);
+    by_norm(a, [&](auto nm) {
+      hipLaunchKernelGGL(
+          (bwd_prep_kernel<T, decltype(d)::value, decltype(m)::value, decltype(nm)::value>),
+          dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+          static_cast<const T*>(a.k), static_cast<const T*>(a.dout), a.log_alpha, a.beta, a.rq,
+          a.rk, ws, sm);
+    });
     return hipGetLastError();
   });
 }
@@ -1828,9 +1909,12 @@ hipError_t launch_bwd_states(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)BH * (a.d / 16));
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
-    hipLaunchKernelGGL((bwd_states_kernel<T, decltype(d)::value, decltype(m)::value>),
-                       dim3(grid), dim3(kStatesThreads), 0, st, static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.beta, a.S0, ws, seq_map(a), BH);
+    by_norm(a, [&](auto nm) {
+      hipLaunchKernelGGL(
+          (bwd_states_kernel<T, decltype(d)::value, decltype(m)::value, decltype(nm)::value>),
+          dim3(grid), dim3(kStatesThreads), 0, st, static_cast<const T*>(a.k),
+          static_cast<const T*>(a.v), a.beta, a.rk, a.S0, ws, seq_map(a), BH);
+    });
     return hipGetLastError();
   });
 }
@@ -1842,9 +1926,12 @@ hipError_t launch_bwd_rev(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)BH * (a.d / 16));
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
-    hipLaunchKernelGGL((bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value>), dim3(grid),
-                       dim3(kRevThreads), 0, st, static_cast<const T*>(a.k), a.beta, a.dS_final,
-                       a.dv, a.dS0, ws, seq_map(a), BH);
+    by_norm(a, [&](auto nm) {
+      hipLaunchKernelGGL(
+          (bwd_rev_kernel<T, decltype(d)::value, decltype(m)::value, decltype(nm)::value>),
+          dim3(grid), dim3(kRevThreads), 0, st, static_cast<const T*>(a.k), a.beta, a.rk,
+          a.dS_final, a.dv, a.dS0, ws, seq_map(a), BH);
+    });
     return hipGetLastError();
   });
 }
@@ -1855,11 +1942,14 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)slots(a);
   return dispatch(a, [&](auto t, auto d, auto m) {
     using T = typename decltype(t)::type;
-    hipLaunchKernelGGL((bwd_grads_kernel<T, decltype(d)::value, decltype(m)::value>),
-                       dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.q),
-                       static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.beta,
-                       static_cast<const T*>(a.dout), a.dq, a.dk, a.dlog_alpha, a.dbeta, ws,
-                       seq_map(a));
+    by_norm(a, [&](auto nm) {
+      hipLaunchKernelGGL(
+          (bwd_grads_kernel<T, decltype(d)::value, decltype(m)::value, decltype(nm)::value>),
+          dim3(grid), dim3(kThreads), 0, st, static_cast<const T*>(a.q),
+          static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.beta,
+          static_cast<const T*>(a.dout), a.rq, a.rk, a.dq, a.dk, a.dlog_alpha, a.dbeta, ws,
+          seq_map(a));
+    });
     return hipGetLastError();
   });
 }
@@ -1874,8 +1964,7 @@ hipError_t launch_bwd_pro(const BwdProArgs& p, bool grad, hipStream_t st) {
     if (!grad)
       hipLaunchKernelGGL((bwd_pro_kernel<T, D>), dim3(grid), dim3(kThreads), 0, st,
                          static_cast<const T*>(p.q), static_cast<const T*>(p.k), p.a_raw,
-                         p.b_raw, static_cast<T*>(p.qn), static_cast<T*>(p.kn), p.rq, p.rk,
-                         p.la, p.be, p.rows, p.norm, p.gates_a, p.gates_b, p.scale);
+                         p.b_raw, p.rq, p.rk, p.la, p.be, p.rows, p.norm, p.gates_a, p.gates_b, p.scale);
     else
       hipLaunchKernelGGL((bwd_pro_grad_kernel<T, D>), dim3(grid), dim3(kThreads), 0, st,
                          static_cast<const T*>(p.q), static_cast<const T*>(p.k), p.a_raw,

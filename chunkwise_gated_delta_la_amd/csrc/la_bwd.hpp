@@ -34,6 +34,11 @@ struct BwdArgs {
   // [B, H, L, d].
   const int* cu = nullptr;
   bool packed = false;    // size the workspace for a packed batch (cu may be NULL then)
+  // Inverse norms of the q and k rows [rows, as the gates] (the fused
+  // prologue's normalisation): q and k are then the raw rows, and every
+  // product that reads them scales by these per row; NULL: q and k as given.
+  const float* rq = nullptr;
+  const float* rk = nullptr;
 };
 
 size_t bwd_workspace_bytes(const BwdArgs& a);
@@ -48,17 +53,16 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t st);
 
 
 // The fused prologue around the backward (la_chunk_bwd_fused): per token
-// row, normalised q and k with their inverse norms, and the activated
-// gates (grad = false); after the backward, the chain rule back to the raw
-// inputs, in place on the gradients (grad = true).
+// row, the inverse norms of q and k and the activated gates (grad = false;
+// the backward then reads the raw q and k with those norms, BwdArgs::rq,
+// rk); after the backward, the chain rule back to the raw inputs, in place
+// on the gradients (grad = true).
 struct BwdProArgs {
   const void* q;          // raw q, k [rows, d], the input type
   const void* k;
   const float* a_raw;     // raw gate scores [rows]
   const float* b_raw;
-  void* qn;               // normalised q, k [rows, d] (written)
-  void* kn;
-  float* rq;              // inverse norms [rows]
+  float* rq;              // inverse norms [rows] (written)
   float* rk;
   float* la;              // -scale softplus(a), sigmoid(b) [rows] (written)
   float* be;

@@ -511,15 +511,17 @@ int la_chunk_bwd_varlen_workspace_bytes(int N, int H, int T, int dk, int dv, int
  * their gradients (da = -gate_scale sigmoid(a) dlog_alpha, db = sigmoid(b)
  * (1 - sigmoid(b)) dbeta; for x_hat = x / sqrt(|x|^2 + 1e-6), dx = (dx_hat -
  * x_hat (x_hat . dx_hat)) / sqrt(|x|^2 + 1e-6)).  A prologue kernel writes the
- * prepared inputs into the workspace, la_chunk_bwd runs on them, and a last
- * kernel applies the chain rule in place.  Arguments, layouts and errors as
+ * inverse norms and the activated gates into the workspace, the backward's
+ * kernels read the raw q and k with the norms as per-row factors (the
+ * normalised rows are never rounded to bf16), and a last kernel applies the
+ * chain rule in place.  Arguments, layouts and errors as
  * la_chunk_bwd (a_raw, b_raw in place of log_alpha, beta; grad_a, grad_b in
  * place of their gradients); opts as la_chunk_fwd_fused, where the epilogue
  * flags (LA_EPI_DSKIP, LA_EPI_OUT_NORM) return LA_ERR_UNSUPPORTED: their
  * backward is not built.  NULL opts or flags = 0 is la_chunk_bwd.
  *   workspace  at least la_chunk_bwd_fused_workspace_bytes() bytes, 16-byte
- *              aligned: the prepared q, k (input type) and inverse norms,
- *              the activated gates, then la_chunk_bwd's workspace
+ *              aligned: the inverse norms of q and k, the activated
+ *              gates, then la_chunk_bwd's workspace
  */
 int la_chunk_bwd_fused(const void* q, const void* k, const void* v,
                        const float* a_raw, const float* b_raw, const float* S0,

@@ -544,9 +544,9 @@ _Opts = _lib.FusedOpts
 
 
 def test_bwd_fused_workspace_size():
-    """The prologue's arrays (normalised q, k in the input type, inverse
-    norms, activated gates), each 256-byte aligned, then the backward's
-    own workspace."""
+    """The prologue's arrays (the inverse norms of q and k, the activated
+    gates), each 256-byte aligned, then the backward's own workspace: the
+    normalised rows are never stored."""
     lib = _lib.get()
     pad = lambda n: -(-n // 256) * 256     # noqa: E731
     for mode in range(4):
@@ -556,10 +556,10 @@ def test_bwd_fused_workspace_size():
                 o = _Opts(flags, 0.0625, None, None, 0.0)
                 assert lib.la_chunk_bwd_fused_workspace_bytes(
                     B, H, L, d, d, 64, mode, dtype, ctypes.byref(o), ctypes.byref(n)) == OK
-                rows, esz = B * H * L, 2 if dtype == 1 else 4
+                rows = B * H * L
                 extra = 0
                 if flags & 2:
-                    extra += 2 * pad(rows * d * esz) + 2 * pad(rows * 4)
+                    extra += 2 * pad(rows * 4)
                 if flags & 1:
                     extra += pad(rows * 4) * ((mode in (2, 3)) + (mode in (1, 2)))
                 assert n.value == extra + expected_bwd_ws(B, H, L, d, mode in (1, 2))
@@ -584,8 +584,8 @@ def test_chunk_bwd_fused_rejects(flags, scale, eps, code):
 
 @pytest.mark.parametrize("arg", [2, 5, 6, 7])      # v, S0, grad_out, grad_S_final
 def test_chunk_bwd_fused_rejects_an_input_in_the_prologue_region(arg):
-    """The fused backward's prologue writes normalised q, k and the gates at
-    the start of the workspace before the backward proper reads v, grad_out,
+    """The fused backward's prologue writes the inverse norms of q and k and
+    the gates at the start of the workspace before the backward proper reads v, grad_out,
     S0 and grad_S_final: any of them inside that region must be rejected
     (it would be overwritten first), not only inside the backward's own
     part of the workspace."""
@@ -596,7 +596,7 @@ def test_chunk_bwd_fused_rejects_an_input_in_the_prologue_region(arg):
                                                   ctypes.byref(n)) == OK
     ws = 20 * P
     args = [fake(i) for i in range(14)]
-    args[arg] = ctypes.c_void_p(ws + 256)               # inside the normalised-q array
+    args[arg] = ctypes.c_void_p(ws + 256)               # inside the k norms (64 rows)
     rc = lib.la_chunk_bwd_fused(*args, 1, 1, 64, 64, 64, 64, 2, 1, ctypes.byref(o),
                                 ctypes.c_void_p(ws), n.value, None)
     assert rc == ALIAS, lib.la_last_error().decode()
