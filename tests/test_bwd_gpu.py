@@ -234,17 +234,12 @@ def test_chunk_bwd_deterministic(mode):
             assert torch.equal(a[n], b[n]), f"{n} differs between two calls"
 
 
-@pytest.mark.parametrize("flags", [1, 2, 3])
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
-@pytest.mark.parametrize("mode", MODES)
-def test_chunk_bwd_fused_prologue(mode, dtype, d, flags):
-    """The gradients of the fused forward's raw inputs (unnormalised q, k
-    with flag 2; raw gate scores with flag 1) against the oracle's backward
-    through prepare and the recurrence, every element."""
-    w = recipe(mode, dtype, B=2, H=1, L=131, d=d, s0_std=0.05, seed=111 + flags)
-    log(f"case chunk_bwd_fused {mode} {dtype} d{d} flags={flags} seed={w.seed}")
+def _fused_bwd_case(w, mode, flags, scale, checkpoint=None, heads=None):
+    """la_chunk_bwd_fused on the raw inputs of `w` against the oracle's
+    backward through prepare and the recurrence: (result, reference); with
+    `heads`, the oracle recomputes those heads only and the result is cut
+    to them (heads do not interact)."""
     r = workloads.make_raw_inputs(w)
-    scale = 1.0 / 16.0
     q, k, a, b = r["q"], r["k"], r["a_raw"], r["b_raw"]
     if not flags & 2:      # the op takes q, k as given: hand it normalised ones
         q = (q.float() / torch.linalg.vector_norm(q.float(), dim=-1, keepdim=True)).to(q.dtype)
@@ -260,14 +255,55 @@ def test_chunk_bwd_fused_prologue(mode, dtype, d, flags):
                        g["dout"], g["dS_final"], mode=mode, qk_l2norm=bool(flags & 2),
                        gate_act=bool(flags & 1), gate_scale=scale)
     torch.cuda.synchronize()
+    if heads is not None:
+        x = {n: t[:, heads].contiguous() for n, t in x.items()}
+        gr = {n: t[:, heads].contiguous() for n, t in gr.items()}
+        res = {n: (t[:, heads] if t is not None else None) for n, t in res.items()}
     y = workloads.to_f64(x)
     gy = workloads.to_f64(gr)
     qp, kp, lp, bp = oracle.prepare(y["q"], y["k"], y["log_alpha"], y["beta"], mode, flags,
                                     scale)
     ref = oracle.recurrent_bwd(qp, kp, y["v"], lp, bp, y["S0"], mode, gy["dout"],
-                               gy["dS_final"])
+                               gy["dS_final"], checkpoint=checkpoint)
     dq, dk_, da, db = oracle.prologue_bwd(y["q"], y["k"], y["log_alpha"], y["beta"], mode, flags,
                                           scale, ref["dq"], ref["dk"], ref["dlog_alpha"],
                                           ref["dbeta"])
-    ref = dict(ref, dq=dq, dk=dk_, dlog_alpha=da, dbeta=db)
+    return res, dict(ref, dq=dq, dk=dk_, dlog_alpha=da, dbeta=db)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_fused_prologue_long(mode):
+    """The fused backward over a long bf16 sequence at d = 128 (64 chunks, a
+    ragged last one), both prologue steps on: the walks take the k norms
+    inside their decay tables and the chunk's total decay from a slot of
+    its own at every step, the other kernels the q and k norms as row
+    factors; every gradient against the oracle's token backward through
+    prepare."""
+    w = recipe(mode, "bf16", B=1, H=2, L=4096 - 17, d=128, s0_std=0.05, seed=131)
+    log(f"case chunk_bwd_fused_long {mode} seed={w.seed}")
+    res, ref = _fused_bwd_case(w, mode, 3, 1.0 / 16.0, checkpoint=64)
+    compare(res, ref, mode, "bf16")
+
+
+def test_chunk_bwd_fused_full_size_sampled():
+    """The fused backward on the long-context workload at full size (B=1,
+    H=32, L=65536, d=128, bf16; raw q, k and gate scores, both prologue
+    steps), launched as the bench launches it; the float64 token backward
+    (checkpointed) through prepare recomputes two sampled heads."""
+    w = workloads.WORKLOADS[4]
+    log(f"case chunk_bwd_fused_full {w.name} seed={w.seed}")
+    res, ref = _fused_bwd_case(w, w.mode, 3, 1.0 / 16.0, checkpoint=64, heads=[0, w.H - 1])
+    compare(res, ref, w.mode, "bf16")
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_bwd_fused_prologue(mode, dtype, d, flags):
+    """The gradients of the fused forward's raw inputs (unnormalised q, k
+    with flag 2; raw gate scores with flag 1) against the oracle's backward
+    through prepare and the recurrence, every element."""
+    w = recipe(mode, dtype, B=2, H=1, L=131, d=d, s0_std=0.05, seed=111 + flags)
+    log(f"case chunk_bwd_fused {mode} {dtype} d{d} flags={flags} seed={w.seed}")
+    res, ref = _fused_bwd_case(w, mode, flags, 1.0 / 16.0)
     compare(res, ref, mode, dtype)
