@@ -1801,7 +1801,10 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(
 // per-row division and keeps its lanes' weights in registers; grid x walks
 // a sequence's rows.  Every lane moves 16 bytes (EPL elements) per access,
 // D / EPL adjacent lanes hold one row and reduce its sum of squares among
-// themselves, two row groups' loads are in flight per wave.
+// themselves, kOutNormU row groups' loads are in flight per wave (at eight
+// waves per SIMD, 128 KiB per compute unit: what HBM's latency asks for).
+constexpr int kOutNormU = 4;
+
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, int L, int H,
                                                        unsigned nseq, const float* __restrict__ w,
@@ -1829,18 +1832,18 @@ __global__ __launch_bounds__(256) void out_norm_kernel(TO* __restrict__ out, int
   const int groups = (L + RPW - 1) / RPW;
   const int nwaves = gridDim.x * (256 / kWave);
   for (int gi = blockIdx.x * (256 / kWave) + threadIdx.x / kWave; gi < groups;
-       gi += 2 * nwaves) {
-    int row[2];
-    bool live[2];
-    vec x[2];
+       gi += kOutNormU * nwaves) {
+    int row[kOutNormU];
+    bool live[kOutNormU];
+    vec x[kOutNormU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kOutNormU; ++u) {
       row[u] = (gi + u * nwaves) * RPW + lane / LPR;
       live[u] = gi + u * nwaves < groups && row[u] < L;
       x[u] = live[u] ? *reinterpret_cast<const vec*>(seq + (size_t)row[u] * D + c0) : vec{};
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kOutNormU; ++u) {
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < EPL; ++j) ss = fmaf((float)x[u][j], (float)x[u][j], ss);
@@ -2261,9 +2264,9 @@ hipError_t launch_tsolve(const ChunkArgs& a, hipStream_t st) {
 
 hipError_t launch_out_norm(const ChunkArgs& a, hipStream_t st) {
   const unsigned nseq = (unsigned)(a.cu ? a.H : a.B * a.H);
-  // rows per workgroup pass: 4 waves of kWave * EPL / D rows, two passes in
-  // flight; about 8 workgroups per compute unit in all
-  const int per = 8 * kWave * (a.out_bf16 ? 8 : 4) / a.d;
+  // rows per workgroup pass: 4 waves of kWave * EPL / D rows, kOutNormU
+  // passes in flight; about 8 workgroups per compute unit in all
+  const int per = 4 * kOutNormU * kWave * (a.out_bf16 ? 8 : 4) / a.d;
   const unsigned gx = (unsigned)std::max<long>(
       1, std::min<long>((a.L + per - 1) / per, (8L * kComputeUnits + nseq - 1) / nseq));
   const dim3 grid(gx, std::min(nseq, 65535u)), block(256);
