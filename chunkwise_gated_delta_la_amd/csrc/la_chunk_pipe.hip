@@ -2193,7 +2193,11 @@ size_t chunk_pipe_workspace_bytes(const ChunkArgs& a) {
 int plan_sum_segments(const ChunkArgs& a) {
   const long seqs = (long)a.B * a.H;
   const int nc = (a.L + C - 1) / C;
-  long P = (4L * kComputeUnits + seqs - 1) / seqs;
+  // one round of kv_kernel: two of its workgroups (64 KiB of LDS each) per
+  // compute unit.  More blocks add rounds, and each writes a d x d partial
+  // that seg_sum_kernel reads back (at B8 H16 L4096 d128, four blocks per
+  // sequence instead of eight: 68 + 11 instead of 73 + 18 us).
+  long P = (2L * kComputeUnits + seqs - 1) / seqs;
   P = std::max(1L, std::min({P, (long)nc, (long)kMaxSegments}));
   // the balanced block size, then the blocks it takes (none empty)
   const int per = (int)((nc + P - 1) / P);

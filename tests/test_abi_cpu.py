@@ -402,8 +402,8 @@ def test_noncausal_rejects(kw, code):
 def test_noncausal_workspace_size():
     """Three state blocks per token block of K^T V (the partial states, an
     unused block and S); the block count, a function of the sizes only,
-    gives about four workgroups per compute unit, at most one per chunk and
-    64 per sequence."""
+    gives about two workgroups per compute unit (one round), at most one per
+    chunk and 64 per sequence."""
     lib = _lib.get()
     def blocks(B, H, L, d):
         n = ctypes.c_size_t(0)
@@ -411,7 +411,7 @@ def test_noncausal_workspace_size():
         unit = 3 * B * H * d * d * 4
         assert n.value % unit == 0
         return n.value // unit
-    assert blocks(8, 16, 4096, 128) == 8
+    assert blocks(8, 16, 4096, 128) == 4
     assert blocks(1, 1, 65536, 128) == 64
     assert blocks(1, 2, 64, 64) == 1
     assert blocks(1, 1, 64 * 5 + 13, 128) == 6
